@@ -1,0 +1,410 @@
+"""Pins of the CPU oracle against things other than itself.
+
+Each ``check_*`` function raises AssertionError when the oracle disagrees with:
+hand-computed worked groups (``tests/golden/worked_groups.json``), bf16
+conversion by a library routine (torch), closed forms, algebraic invariants of
+the definitions, special cases, or a scalar brute-force restatement
+(``tests/scalar_reference.py``) on tiny inputs.  The checks are plain functions
+so that ``test_oracle_mutants.py`` can re-run them against planted mistakes.
+
+Definitions pinned: model card "rebuttal_w4g128_awq_w2" (details table rows
+"Scheme" and "Search"; the scale-rewrite paragraph; "Clipping granularity";
+the RTN note under the perplexity table); model card "Qwen3.6-27B-W4A16"
+(opening paragraph: symmetric int4 g128, activations 16-bit); benchmark record
+"AWQ INT4-g128 WikiText-2 perplexity delta vs fp16, Llama-2 7B" ("Methodology":
+group 128, alpha grid of 20).
+"""
+from __future__ import annotations
+
+import json
+import os
+
+import numpy as np
+
+from oracle import w4a16_oracle as O
+from tests import scalar_reference as S
+from workloads import round_to_bf16_bits, small_case
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "worked_groups.json")
+
+
+def _golden():
+    with open(GOLDEN) as f:
+        return json.load(f)
+
+
+def _group_values(g):
+    fill = g.get("fill", 0.0)
+    vals = np.full(128, fill, dtype=np.float32)
+    for k, v in g.get("listed", g.get("listed_all", {})).items():
+        vals[int(k)] = v
+    return vals
+
+
+def _bits(vals):
+    bits = round_to_bf16_bits(np.asarray(vals, dtype=np.float32))
+    assert np.array_equal((bits.astype(np.uint32) << 16).view(np.float32), vals), "fixture not bf16-exact"
+    return bits
+
+
+# ----------------------------------------------------------------------------- bf16
+
+def check_bf16_golden():
+    for src, dst in _golden()["bf16"]["cases"]:
+        x = np.array([int(src, 16)], dtype=np.uint32).view(np.float32)
+        assert int(O.f32_to_bf16(x)[0]) == int(dst, 16), (src, dst)
+
+
+def check_bf16_against_torch():
+    import torch
+    rng = np.random.default_rng(7)
+    x = rng.standard_normal(20000).astype(np.float32) * np.float32(3.0)
+    u = x.view(np.uint32)
+    u[:5000] = (u[:5000] & np.uint32(0xFFFF0000)) | np.uint32(0x8000)   # exact ties
+    x = u.view(np.float32)
+    want = torch.from_numpy(x.copy()).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(O.f32_to_bf16(x), want)
+    back = torch.from_numpy(want.view(np.int16).copy()).view(torch.bfloat16).float().numpy()
+    assert np.array_equal(O.bf16_to_f32(want), back)
+
+
+# ----------------------------------------------------------------------------- worked groups
+
+def check_worked_groups():
+    for g in _golden()["groups"]:
+        vals = _group_values(g)
+        W = _bits(vals)[None, :]
+        sym = g["symmetric"]
+        codes, scales, zeros = O.quantize_rtn(W, symmetric=sym)
+        assert int(scales[0, 0]) == int(g["scale_bits"], 16), (g["name"], hex(int(scales[0, 0])))
+        if not sym:
+            assert int(zeros[0, 0]) == g["zero"], g["name"]
+        want = np.full(128, g["code_unlisted"], dtype=np.int64)
+        for k, c in g["codes_listed"].items():
+            want[int(k)] = c
+        assert np.array_equal(codes[0].astype(np.int64), want), (g["name"], codes[0][:12])
+        qw, sc, qz = O.quantize_pack(W, symmetric=sym)
+        deq = O.dequantize(qw, sc, qz, 128, sym)
+        for k, d in g["dequant_listed"].items():
+            assert deq[0, int(k)] == np.float32(d), (g["name"], k, deq[0, int(k)], d)
+        for i, word in g.get("qweight_words", {}).items():
+            assert int(qw[0, int(i)]) == int(word, 16), (g["name"], i, hex(int(qw[0, int(i)])))
+        if "qzeros_word0" in g:
+            assert int(qz[0, 0]) == int(g["qzeros_word0"], 16)
+
+
+def check_pack_golden():
+    p = _golden()["pack"]
+    w = O.pack_nibbles(np.array([p["codes"]], dtype=np.uint8))
+    assert int(w[0, 0]) == int(p["word"], 16)
+
+
+# ----------------------------------------------------------------------------- invariants
+
+def _rand_w(N=24, K=512, seed=3, std=0.02):
+    _, W = small_case(1, K, N, seed, w_std=std)
+    return W
+
+
+def check_pack_roundtrip():
+    rng = np.random.default_rng(11)
+    for n in (8, 16, 24, 40, 136, 5):
+        c = rng.integers(0, 16, size=(7, n)).astype(np.uint8)
+        assert np.array_equal(O.unpack_nibbles(O.pack_nibbles(c), n), c)
+    # padding nibbles are zero
+    w = O.pack_nibbles(np.full((1, 5), 15, dtype=np.uint8))
+    assert int(w[0, 0]) == 0x000FFFFF
+
+
+def check_ranges_and_error_bound():
+    W = _rand_w()
+    for sym in (False, True):
+        codes, scales, zeros = O.quantize_rtn(W, symmetric=sym)
+        assert codes.max() <= 15
+        if zeros is not None:
+            assert zeros.max() <= 15
+        v = O.bf16_to_f32(W).reshape(W.shape[0], -1, 128)
+        sc = O.bf16_to_f32(scales)[..., None]
+        z = 8.0 if sym else zeros.astype(np.float64)[..., None]
+        deq = (codes.reshape(v.shape).astype(np.float64) - z) * sc
+        err = np.abs(deq - v)
+        c = codes.reshape(v.shape)
+        if sym:
+            # absmax / sc <= 7 (1 + 2^-8) < 7.5, so no code is clamped: every value is
+            # within half a step of its reconstruction, and |code| <= 7
+            assert np.all(err <= sc / 2 + 1e-12), float((err - sc / 2).max())
+            assert codes.min() >= 1
+        else:
+            # the bf16 scale can sit up to 2^-8 below (hi - lo)/15, so only the top code
+            # may be clamped, by at most 15 * 2^-8 of a step
+            top = c == 15
+            assert np.all(err[~top] <= np.broadcast_to(sc / 2 + 1e-12, err.shape)[~top])
+            assert np.all(err <= sc * (0.5 + 15 * 2.0 ** -8) + 1e-12)
+
+
+def check_asym_range_covers_group():
+    """Asymmetric: sc >= (hi - lo)/15 up to bf16 rounding, so 15 steps span the group."""
+    W = _rand_w(N=16, K=1024, seed=5)
+    codes, scales, zeros = O.quantize_rtn(W)
+    v = O.bf16_to_f32(W).astype(np.float64).reshape(16, -1, 128)
+    rng_ = v.max(-1) - v.min(-1)
+    sc = O.bf16_to_f32(scales).astype(np.float64)
+    assert np.all(np.abs(sc * 15 - rng_) <= rng_ * 2.0 ** -8 + 1e-12)
+    # the minimum of each group maps to a code <= 1 and the maximum to >= 14
+    c = codes.reshape(16, -1, 128)
+    idx_lo = v.argmin(-1)
+    idx_hi = v.argmax(-1)
+    clo = np.take_along_axis(c, idx_lo[..., None], -1)
+    chi = np.take_along_axis(c, idx_hi[..., None], -1)
+    assert clo.max() <= 1 and chi.min() >= 14
+
+
+def check_symmetric_oddness():
+    W = _rand_w(seed=9)
+    Wneg = W ^ np.uint16(0x8000)
+    qa, sa, _ = O.quantize_pack(W, symmetric=True)
+    qb, sb, _ = O.quantize_pack(Wneg, symmetric=True)
+    assert np.array_equal(sa, sb)
+    da = O.dequantize(qa, sa, None, W.shape[1], True)
+    db = O.dequantize(qb, sb, None, W.shape[1], True)
+    assert np.array_equal(da, -db)
+
+
+def check_power_of_two_equivariance():
+    W = _rand_w(seed=13)
+    for sym in (False, True):
+        for j in (-3, 2):
+            f = np.float32(2.0 ** j)
+            qa, sa, za = O.quantize_pack(W, symmetric=sym)
+            s = np.full(W.shape[1], f, dtype=np.float32)
+            qb, sb, zb = O.quantize_pack(W, s=s, symmetric=sym)
+            da = O.dequantize(qa, sa, za, W.shape[1], sym)
+            db = O.dequantize(qb, sb, zb, W.shape[1], sym)
+            assert np.array_equal(da * f, db), (sym, j)
+            assert np.array_equal(qa, qb)
+
+
+def check_scale_multiplies_input_channels():
+    """W diag(s): s_k scales column k (input channel) of every row, not row n."""
+    W = _rand_w(N=8, K=256, seed=21)
+    s = np.ones(256, dtype=np.float32)
+    s[:128] = 4.0                       # first group scaled by a power of two
+    qa, sa, za = O.quantize_pack(W)
+    qb, sb, zb = O.quantize_pack(W, s=s)
+    da = O.dequantize(qa, sa, za, 256, False)
+    db = O.dequantize(qb, sb, zb, 256, False)
+    assert np.array_equal(db[:, :128], 4 * da[:, :128])
+    assert np.array_equal(db[:, 128:], da[:, 128:])
+
+
+def check_clip_is_clamp():
+    """r < 1 clamps each group of W diag(s) at +-r*absmax; r = 1 is the identity."""
+    g = np.zeros(128, dtype=np.float32)
+    g[0], g[1], g[2] = -1.0, 2.0, 0.5
+    W = _bits(g)[None, :]
+    # r = 0.5: t = 1.0 -> group becomes {-1, 1, 0.5, 0...}: lo=-1, hi=1, sc = bf16(2/15)
+    codes, scales, zeros = O.quantize_rtn(W, clip_ratio=0.5)
+    sc = O.bf16_to_f32(scales)[0, 0]
+    assert sc == O.bf16_to_f32(O.f32_to_bf16(np.float32(2.0) / np.float32(15.0)))
+    d = O.dequantize(O.pack_nibbles(codes), scales, O.pack_nibbles(zeros), 128, False)[0]
+    assert abs(d[1] - 1.0) <= sc / 2 and abs(d[0] + 1.0) <= sc / 2
+    q1 = O.quantize_pack(W, clip_ratio=1.0)
+    q0 = O.quantize_pack(W)
+    assert all(np.array_equal(a, b) for a, b in zip(q1, q0))
+
+
+def check_dequant_exact():
+    W = _rand_w(seed=17)
+    qw, sc, qz = O.quantize_pack(W)
+    d = O.dequantize(qw, sc, qz, W.shape[1], False).astype(np.float64)
+    codes = O.unpack_nibbles(qw, W.shape[1]).astype(np.float64).reshape(W.shape[0], -1, 128)
+    z = O.unpack_nibbles(qz, W.shape[1] // 128).astype(np.float64)[..., None]
+    exact = ((codes - z) * O.bf16_to_f32(sc).astype(np.float64)[..., None]).reshape(W.shape)
+    assert np.array_equal(d, exact)
+
+
+# ----------------------------------------------------------------------------- contraction
+
+def check_linear_special_cases():
+    X, W = small_case(3, 256, 12, 23)
+    qw, sc, qz = O.quantize_pack(W)
+    What = O.dequantize(qw, sc, qz, 256, False)
+    # one-hot activations pick out one input channel of every row exactly
+    for k in (0, 127, 128, 255):
+        onehot = np.zeros((1, 256), dtype=np.uint16)
+        onehot[0, k] = 0x3F80          # 1.0 in bf16
+        y = O.linear(onehot, What)
+        assert np.array_equal(y[0], What[:, k].astype(np.float64))
+    assert not O.linear(np.zeros((2, 256), dtype=np.uint16), What).any()
+    # brute force on a tiny product
+    Xf = O.bf16_to_f32(X).astype(np.float64)
+    bf = [[sum(float(Xf[m, k]) * float(What[n, k]) for k in range(256)) for n in range(12)] for m in range(3)]
+    assert np.allclose(O.linear(X, What), np.array(bf), rtol=1e-13, atol=1e-13)
+
+
+# ----------------------------------------------------------------------------- AWQ search
+
+def check_grids():
+    a = O.alpha_grid()
+    assert a.size == 20 and a[0] == 0.0 and np.allclose(np.diff(a), 0.05) and a[-1] < 1.0
+    r = O.shrink_grid()
+    assert r.size == 10 and r[0] == 1.0 and r.min() >= 0.5 and np.all(np.diff(r) < 0)
+
+
+def check_act_stat_closed_form():
+    X = np.zeros((4, 256), dtype=np.float32)
+    X[:, :128] = [[1.0], [-1.0], [3.0], [-3.0]]       # mean |x| = 2 on the first 128 channels
+    X[:, 128:] = 0.5
+    m = O.act_mean_abs(round_to_bf16_bits(X))
+    assert np.all(m[:128] == 2.0) and np.all(m[128:] == 0.5)
+
+
+def check_scales_closed_form():
+    m = np.array([0.25, 1.0, 4.0, 16.0])
+    s1 = O.awq_scales(m, 1.0)                       # p = m; sqrt(16 * 0.25) = 2
+    assert np.array_equal(s1, np.array([0.125, 0.5, 2.0, 8.0], dtype=np.float32))
+    s0 = O.awq_scales(m, 0.0)
+    assert np.array_equal(s0, np.ones(4, dtype=np.float32))
+    s5 = O.awq_scales(m, 0.5)                       # p = sqrt(m) = .5,1,2,4; sqrt(4*.5) = sqrt 2
+    assert np.allclose(s5, np.array([0.5, 1, 2, 4]) / np.sqrt(2.0), rtol=1e-7)
+    # a zero statistic is floored at 1e-4 before normalising: p = (1e-4, 1), sqrt(1e-4) = 0.01
+    assert np.allclose(O.awq_scales(np.array([0.0, 1.0]), 0.5), [0.01, 100.0], rtol=1e-6)
+
+
+def check_rewrite_identity():
+    """X (Q(W diag s) diag(1/s))^T == (X diag(1/s)) Q(W diag s)^T; bit-exact for power-of-two s."""
+    X, W = small_case(6, 256, 8, 31)
+    rng = np.random.default_rng(3)
+    for pow2 in (True, False):
+        if pow2:
+            s = (2.0 ** rng.integers(-2, 3, size=256)).astype(np.float32)
+        else:
+            s = np.exp(rng.standard_normal(256) * 0.5).astype(np.float32)
+        qw, sc, qz = O.quantize_pack(W, s=s)
+        What = O.dequantize(qw, sc, qz, 256, False).astype(np.float64)
+        Xf = O.bf16_to_f32(X).astype(np.float64)
+        lhs = Xf @ (What / s.astype(np.float64)).T
+        rhs = (Xf / s.astype(np.float64)) @ What.T
+        if pow2:
+            assert np.array_equal(lhs, rhs)
+        else:
+            assert np.allclose(lhs, rhs, rtol=1e-12, atol=1e-14)
+        Yref = O.reference_output(X, W)
+        want = float(np.mean((rhs - Yref) ** 2))
+        got = O.candidate_loss(X, W, s, 1.0)
+        assert abs(got - want) <= 1e-12 * want, (got, want)
+
+
+def check_alpha_zero_is_rtn():
+    X, W = small_case(16, 256, 8, 37)
+    m = O.act_mean_abs(X)
+    s0 = O.awq_scales(m, 0.0)
+    assert np.array_equal(s0, np.ones(256, dtype=np.float32))
+    rtn = O.candidate_loss(X, W, s0, 1.0)
+    qw, sc, qz = O.quantize_pack(W)
+    What = O.dequantize(qw, sc, qz, 256, False)
+    d = O.linear(X, What) - O.reference_output(X, W)
+    assert O.candidate_loss(X, W, s0, 1.0) == float(np.mean(d * d)) == rtn
+    res = O.search(X, W)
+    assert res["alpha_losses"][0] == rtn
+    assert min(res["alpha_losses"]) <= rtn
+
+
+def check_loss_closed_form_reference():
+    """Y_ref is the bf16-rounded unquantized output; a weight with exact 4-bit
+    structure (every group already on its grid) has loss equal to the squared
+    bf16 rounding of the reference alone."""
+    rng = np.random.default_rng(41)
+    N, K = 4, 256
+    codes = rng.integers(0, 16, size=(N, K)).astype(np.float32)
+    codes[:, ::128] = 0.0
+    codes[:, 1::128] = 15.0                        # every group spans 0..15 exactly
+    Wf = (codes - 8.0) * np.float32(0.0625)        # sc = 15*0.0625/15, z = 8: exact on the grid
+    W = round_to_bf16_bits(Wf)
+    X = round_to_bf16_bits(rng.standard_normal((5, K)).astype(np.float32))
+    qw, sc, qz = O.quantize_pack(W)
+    assert np.array_equal(O.dequantize(qw, sc, qz, K, False), Wf)
+    y = O.linear(X, Wf.astype(np.float64))
+    yref = O.bf16_to_f32(O.f32_to_bf16(y.astype(np.float32))).astype(np.float64)
+    want = float(np.mean((y - yref) ** 2))
+    got = O.candidate_loss(X, W, np.ones(K, np.float32), 1.0)
+    assert abs(got - want) <= 1e-15 + 1e-12 * want
+
+
+def check_bruteforce_search():
+    """K=256, N=4, T=8, all 30 candidates: the scalar restatement agrees to 1e-10."""
+    X, W = small_case(8, 256, 4, 43)
+    rng = np.random.default_rng(43)
+    mag = np.exp(rng.standard_normal(256)).astype(np.float32)
+    X = round_to_bf16_bits(O.bf16_to_f32(X) * mag)
+    Xr = O.bf16_to_f32(X).astype(np.float64).tolist()
+    Wr = O.bf16_to_f32(W).astype(np.float64).tolist()
+    alphas = O.alpha_grid().tolist()
+    ratios = O.shrink_grid().tolist()
+    for sym in (False, True):
+        la, lr, ia, ir = S.search(Xr, Wr, alphas, ratios, sym)
+        res = O.search(X, W, symmetric=sym)
+        assert np.allclose(res["alpha_losses"], la, rtol=1e-10, atol=0), sym
+        assert np.allclose(res["ratio_losses"], lr, rtol=1e-10, atol=0), sym
+        assert res["alpha_index"] == ia and res["ratio_index"] == ir
+
+
+def check_bruteforce_quantizer_random():
+    """Scalar restatement vs vectorised quantizer, bit-exact, with s and clipping."""
+    rng = np.random.default_rng(47)
+    for sym in (False, True):
+        for r in (1.0, 0.85):
+            _, W = small_case(1, 256, 6, int(1000 * r) + sym)
+            s = np.exp(rng.standard_normal(256) * 0.7).astype(np.float32)
+            qw, sc, qz = O.quantize_pack(W, s=s, clip_ratio=r, symmetric=sym)
+            d = O.dequantize(qw, sc, qz, 256, sym).astype(np.float64)
+            ref = S.quantize_dequant(O.bf16_to_f32(W).astype(np.float64).tolist(),
+                                     s.astype(np.float64).tolist(), r, sym)
+            assert np.array_equal(d, np.array(ref)), (sym, r)
+
+
+def check_division_ties():
+    """Codes are rint of the IEEE fp32 quotient v / sc, ties to even.
+
+    Group 0 is {0, 1, t...}: sc = bf16(1/15) = 137/2048, z = 0.  Group 1 is
+    {0, 1.203125, t...}: sc = bf16(1.203125/15) = 164/2048, z = 0.  Each
+    t = (k + 1/2) sc is exact in fp32, so v / sc is exactly k + 1/2 and the code is
+    the even neighbour (for sc = 164/2048, multiplying by a rounded reciprocal
+    instead of dividing misses the ties at k = 3, 7 and 13).  The fp32 neighbours
+    of each tie are checked against the scalar restatement, which forms the
+    correctly rounded quotient independently.
+    """
+    s = np.ones(256, dtype=np.float32)
+    Wf = np.zeros(256, dtype=np.float32)
+    for g, (hi, num) in enumerate(((1.0, 137.0), (1.203125, 164.0))):
+        sc = num / 2048.0
+        ties = [(k + 0.5) * sc for k in range(14)]
+        below = [float(np.nextafter(np.float32(t), np.float32(0))) for t in ties]
+        above = [float(np.nextafter(np.float32(t), np.float32(2))) for t in ties]
+        vals = [0.0, hi] + ties + below + above
+        base = 128 * g
+        Wf[base + 1] = hi
+        Wf[base + 2: base + len(vals)] = 1.0          # v = 1.0 * s_k
+        s[base + 2: base + len(vals)] = np.array(vals[2:], dtype=np.float32)
+    W = round_to_bf16_bits(Wf)[None, :]
+    codes, scales, zeros = O.quantize_rtn(W, s=s)
+    assert int(scales[0, 0]) == 0x3D89 and int(scales[0, 1]) == 0x3DA4
+    assert int(zeros[0, 0]) == 0 and int(zeros[0, 1]) == 0
+    for g in range(2):
+        for k in range(14):
+            assert int(codes[0, 128 * g + 2 + k]) == (k if k % 2 == 0 else k + 1), (g, k)
+    ref = S.quantize_dequant([Wf.astype(np.float64).tolist()], s.astype(np.float64).tolist(), 1.0, False)
+    d = O.dequantize(O.pack_nibbles(codes), scales, O.pack_nibbles(zeros), 256, False)
+    assert np.array_equal(d[0].astype(np.float64), np.array(ref[0]))
+
+
+ALL_CHECKS = [
+    check_division_ties,
+    check_bf16_golden, check_bf16_against_torch, check_worked_groups, check_pack_golden,
+    check_pack_roundtrip, check_ranges_and_error_bound, check_asym_range_covers_group,
+    check_symmetric_oddness, check_power_of_two_equivariance, check_scale_multiplies_input_channels,
+    check_clip_is_clamp, check_dequant_exact, check_linear_special_cases, check_grids,
+    check_act_stat_closed_form, check_scales_closed_form, check_rewrite_identity,
+    check_alpha_zero_is_rtn, check_loss_closed_form_reference, check_bruteforce_search,
+    check_bruteforce_quantizer_random,
+]

@@ -1,0 +1,110 @@
+"""Pure-Python scalar restatement of the group-128 RTN quantizer and the AWQ
+candidate loss, for brute-force checks of the vectorised oracle on tiny inputs.
+
+It is written independently of ``oracle/``: one element at a time, Python
+floats (fp64) with every fp32 step rounded back to fp32 through ``struct``
+(rounding a correctly rounded fp64 sum, product or quotient of two fp32 values to
+fp32 gives the correctly rounded fp32 result, because 53 >= 2*24 + 2), bf16
+rounding by exponent/mantissa arithmetic (not bit tricks), and Python's
+``round`` (ties to even) as rint.  Definitions: model card
+"rebuttal_w4g128_awq_w2", details table rows "Scheme" and "Search", the
+scale-rewrite paragraph and "Clipping granularity"; model card
+"Qwen3.6-27B-W4A16", opening paragraph (symmetric form).
+"""
+from __future__ import annotations
+
+import math
+import struct
+
+
+def f32(x: float) -> float:
+    return struct.unpack("f", struct.pack("f", x))[0]
+
+
+def bf16_value(bits: int) -> float:
+    return struct.unpack(">f", struct.pack(">I", (bits & 0xFFFF) << 16))[0]
+
+
+def round_bf16(x: float) -> float:
+    """Nearest value with 8 significant bits, ties to even (finite, normal inputs)."""
+    if x == 0.0:
+        return 0.0
+    m, e = math.frexp(x)            # x = m * 2**e, 0.5 <= |m| < 1
+    scaled = m * 256.0              # 8 significant bits before the point
+    return math.ldexp(float(round(scaled)), e - 8)
+
+
+def quantize_group(v: list[float], symmetric: bool):
+    """One group of 128 fp32 values -> (codes 0..15, scale value, zero)."""
+    floor = f32(1e-5)
+    if symmetric:
+        amax = max(abs(x) for x in v)
+        sc = round_bf16(f32(max(amax, floor) / 7.0))
+        codes = [min(max(round(f32(x / sc)), -8), 7) + 8 for x in v]
+        return codes, sc, 8
+    lo, hi = min(v), max(v)
+    sc = round_bf16(f32(max(f32(hi - lo), floor) / 15.0))
+    z = min(max(round(f32(-lo / sc)), 0), 15)
+    codes = [min(max(round(f32(x / sc)) + z, 0), 15) for x in v]
+    return codes, sc, z
+
+
+def quantize_dequant(W_rows: list[list[float]], s: list[float] | None, r: float, symmetric: bool):
+    """Fake-quantized weights W_hat (list of rows) of Q(W diag(s)) with clip ratio r."""
+    out = []
+    r = f32(r)
+    for row in W_rows:
+        K = len(row)
+        v = [f32(row[k] * s[k]) if s is not None else row[k] for k in range(K)]
+        what = []
+        for g0 in range(0, K, 128):
+            grp = v[g0:g0 + 128]
+            if r < 1.0:
+                t = f32(r * max(abs(x) for x in grp))
+                grp = [min(max(x, -t), t) for x in grp]
+            codes, sc, z = quantize_group(grp, symmetric)
+            what.extend((c - z) * sc for c in codes)
+        out.append(what)
+    return out
+
+
+def mean_abs(X_rows):
+    T = len(X_rows)
+    K = len(X_rows[0])
+    return [sum(abs(X_rows[t][k]) for t in range(T)) / T for k in range(K)]
+
+
+def scales_for(m: list[float], alpha: float) -> list[float]:
+    p = [max(math.pow(x, alpha), 1e-4) for x in m]
+    d = math.sqrt(max(p) * min(p))
+    return [f32(x / d) for x in p]
+
+
+def loss(X_rows, W_rows, s, r, symmetric, Y_ref):
+    what = quantize_dequant(W_rows, s, r, symmetric)
+    T, N, K = len(X_rows), len(W_rows), len(W_rows[0])
+    acc = 0.0
+    for t in range(T):
+        for n in range(N):
+            y = 0.0
+            for k in range(K):
+                y += X_rows[t][k] * (what[n][k] / s[k])
+            d = y - Y_ref[t][n]
+            acc += d * d
+    return acc / (T * N)
+
+
+def reference(X_rows, W_rows):
+    """bf16(fp32(sum_k x w)) for every (t, n)."""
+    return [[round_bf16(f32(sum(x * w for x, w in zip(xr, wr)))) for wr in W_rows] for xr in X_rows]
+
+
+def search(X_rows, W_rows, alphas, ratios, symmetric=False):
+    m = mean_abs(X_rows)
+    Y_ref = reference(X_rows, W_rows)
+    la = [loss(X_rows, W_rows, scales_for(m, a), 1.0, symmetric, Y_ref) for a in alphas]
+    ia = min(range(len(la)), key=lambda i: (la[i], i))
+    s_star = scales_for(m, alphas[ia])
+    lr = [loss(X_rows, W_rows, s_star, r, symmetric, Y_ref) for r in ratios]
+    ir = min(range(len(lr)), key=lambda i: (lr[i], i))
+    return la, lr, ia, ir

@@ -1,0 +1,83 @@
+"""Plant plausible mistakes in a copy of the CPU oracle and require that at
+least one pin in ``tests/oracle_pins.py`` catches each of them.
+
+Each mutant is a source substitution applied to the oracle's text, executed as
+a fresh module on the CPU; the real oracle module's functions are then swapped
+for the mutant's while the pins run.  Nothing here touches a GPU.
+"""
+import importlib.util
+import inspect
+import types
+
+import pytest
+
+from oracle import w4a16_oracle as O
+from tests import oracle_pins as P
+
+MUTANTS = {
+    "rint_half_up": ("q = np.clip(np.rint(v / sc) + z, 0, ASYM_LEVELS)",
+                     "q = np.clip(np.floor(v / sc + np.float32(0.5)) + z, 0, ASYM_LEVELS)"),
+    "reciprocal_multiply": ("q = np.clip(np.rint(v / sc) + z, 0, ASYM_LEVELS)",
+                            "q = np.clip(np.rint(v * (np.float32(1.0) / sc)) + z, 0, ASYM_LEVELS)"),
+    "zero_sign": ("z = np.clip(np.rint(-lo / sc), 0, ASYM_LEVELS)",
+                  "z = np.clip(np.rint(lo / sc), 0, ASYM_LEVELS)"),
+    "zero_unclamped": ("z = np.clip(np.rint(-lo / sc), 0, ASYM_LEVELS)", "z = np.rint(-lo / sc)"),
+    "asym_levels_16": ("np.maximum(hi - lo, RANGE_FLOOR) / np.float32(ASYM_LEVELS)",
+                       "np.maximum(hi - lo, RANGE_FLOOR) / np.float32(16.0)"),
+    "sym_divisor_8": ("np.maximum(absmax, RANGE_FLOOR) / np.float32(SYM_MAX)",
+                      "np.maximum(absmax, RANGE_FLOOR) / np.float32(8.0)"),
+    "sym_no_offset": ("q = np.clip(np.rint(v / sc), -SYM_OFFSET, SYM_MAX) + SYM_OFFSET",
+                      "q = np.clip(np.rint(v / sc), -SYM_OFFSET, SYM_MAX) % 16"),
+    "scale_not_rounded": ("        sc = bf16_to_f32(sc_bits)\n        z = np.clip",
+                          "        sc = np.maximum(hi - lo, RANGE_FLOOR) / np.float32(ASYM_LEVELS)\n        z = np.clip"),
+    "clip_scales_instead_of_clamps": ("v = np.minimum(np.maximum(v, -t), t)", "v = v * r"),
+    "s_on_rows": ("v = v * np.asarray(s, dtype=np.float32)[None, :]",
+                  "v = v * np.asarray(s, dtype=np.float32)[:v.shape[0], None]"),
+    "nibbles_reversed": ("out |= padded[..., j] << np.uint32(4 * j)",
+                         "out |= padded[..., j] << np.uint32(4 * (7 - j))"),
+    "dequant_plus_zero": ("return ((codes.reshape(N, G, GROUP) - z) * sc).reshape(N, K)",
+                          "return ((codes.reshape(N, G, GROUP) + z - 2 * np.float32(SYM_OFFSET)) * sc).reshape(N, K)"),
+    "linear_transposed_weight": ("@ np.asarray(W_hat, dtype=np.float64).T",
+                                 "@ np.asarray(W_hat, dtype=np.float64).T[::-1]"),
+    "loss_multiplies_s": ("W_eff = W_hat / np.asarray(s", "W_eff = W_hat * np.asarray(s"),
+    "reference_unrounded": ("return bf16_to_f32(f32_to_bf16(y.astype(np.float32))).astype(np.float64)",
+                            "return y"),
+    "stat_without_abs": ("return np.abs(bf16_to_f32(X_bf16).astype(np.float64)).mean(axis=0)",
+                         "return bf16_to_f32(X_bf16).astype(np.float64).mean(axis=0)"),
+    "scales_unnormalised": ("return (p / np.sqrt(p.max() * p.min())).astype(np.float32)",
+                            "return p.astype(np.float32)"),
+    "alpha_linspace": ("return np.arange(n, dtype=np.float64) / n", "return np.linspace(0.0, 1.0, n)"),
+    "bf16_truncates": ("return ((u + np.uint64(0x7FFF) + lsb) >> np.uint64(16)).astype(np.uint16)",
+                       "return (u >> np.uint64(16)).astype(np.uint16)"),
+    "bf16_ties_away": ("return ((u + np.uint64(0x7FFF) + lsb) >> np.uint64(16)).astype(np.uint16)",
+                       "return ((u + np.uint64(0x8000)) >> np.uint64(16)).astype(np.uint16)"),
+    "clip_after_scale_choice": ("        absmax = np.abs(v).max(axis=2, keepdims=True)\n    if symmetric:",
+                                "    if symmetric:"),
+}
+
+
+def _mutant_module(old, new):
+    src = inspect.getsource(O)
+    assert src.count(old) >= 1, f"mutation anchor not found: {old!r}"
+    src = src.replace(old, new)
+    mod = types.ModuleType("oracle_mutant")
+    mod.__dict__["__name__"] = "oracle_mutant"
+    exec(compile(src, "oracle_mutant", "exec"), mod.__dict__)
+    return mod
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutant_is_caught(name, monkeypatch):
+    old, new = MUTANTS[name]
+    mod = _mutant_module(old, new)
+    for attr, val in vars(mod).items():
+        if callable(val) and getattr(val, "__module__", None) == "oracle_mutant":
+            monkeypatch.setattr(O, attr, val)
+    caught = []
+    for check in P.ALL_CHECKS:
+        try:
+            check()
+        except Exception as e:          # AssertionError or a shape error: the mistake is visible
+            caught.append((check.__name__, type(e).__name__))
+            break
+    assert caught, f"mutant {name} passed every pin"

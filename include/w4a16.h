@@ -1,0 +1,182 @@
+/*
+ * w4a16.h -- weight-only int4, group-128 quantized linear layers (W4A16) on
+ * AMD CDNA4 (MI355X, gfx950): quantize + pack, decode GEMV, prefill GEMM and the
+ * batched fake-quant loss of an AWQ scale-exponent / clip-shrink search.
+ *
+ * Sources for what is computed (web pages, cited by title and section):
+ *   [AWQ-W4 card]  model card "rebuttal_w4g128_awq_w2": details table rows
+ *                  "Scheme" (weight-only, 4-bit, group size 128, asymmetric zero
+ *                  point) and "Search" (20-point scale-exponent grid + 10-point
+ *                  global shrink grid); the scale-rewrite paragraph
+ *                  (prev_op /= s, W *= s  ==  Q(W diag(s)) diag(1/s)); the
+ *                  "Clipping granularity" paragraph; RTN note under the perplexity table.
+ *   [27B card]     model card "Qwen3.6-27B-W4A16": opening paragraph (int4, group
+ *                  128, symmetric, weight-only, 16-bit activations, data-free RTN).
+ *   [QSRT card]    model card "GLM-5.2-QSRT-Fruit-Instruct", "Reproducible runtime":
+ *                  decode-sized batches of at most 16 rows take a separate path
+ *                  from prefill; unsupported shapes fail closed.
+ *   [AWQ record]   benchmark record "AWQ INT4-g128 WikiText-2 perplexity delta vs
+ *                  fp16, Llama-2 7B", "Methodology": group 128, alpha grid of 20.
+ *
+ * Conventions for every entry point
+ *   - bf16 values are passed as uint16_t bit patterns.
+ *   - Array pointers are DEVICE pointers owned by the caller unless a parameter
+ *     says "host".  The library never frees caller memory and never allocates
+ *     device memory, except awq_search, which allocates its workspace itself
+ *     when the caller passes none (see there).
+ *   - `stream` is a hipStream_t (NULL = the default stream).  Work is enqueued
+ *     asynchronously on it; results are ready once the stream is synchronized.
+ *     awq_search is the one call that synchronizes (it reads losses on the host).
+ *   - Arguments are validated on the host before any HIP call; a failing check
+ *     returns a negative w4_status and enqueues nothing.  No call aborts or prints.
+ *   - Weight layout: W is [N][K] row-major (output channels x input channels,
+ *     input channels contiguous) -- the K x N weight of the linear, stored so that
+ *     W diag(s) scales input channels.  K must be a multiple of 128.
+ *   - Packed layout: qweight[n][i] (uint32, [N][K/8]) holds in nibble j (bits
+ *     4j..4j+3) the code of input channel k = 8i + j.  scales[n][g] (bf16,
+ *     [N][K/128]) is the scale of group g = k / 128.  qzeros[n][i] (uint32,
+ *     [N][ceil(K/1024)]) holds in nibble j the zero point of group 8i + j; unused
+ *     nibbles are 0.  Symmetric weights have no qzeros: the stored nibble is the
+ *     signed code + 8.
+ *   - Dequantized weight: W_hat[n][k] = (q - z) * scale, z = zero point
+ *     (asymmetric) or 8 (symmetric).
+ *   - Alignment: every array pointer must be 16-byte aligned (W4_ERR_ALIGN).
+ *   - Sizes are int; products are formed in 64-bit.
+ */
+#ifndef W4A16_H
+#define W4A16_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  W4_OK = 0,
+  W4_ERR_NULL = -1,         /* a required pointer is NULL (or a forbidden one is not)   */
+  W4_ERR_SHAPE = -2,        /* a size is out of range, or K is not a multiple of 128    */
+  W4_ERR_ALIGN = -3,        /* an array pointer is not 16-byte aligned                   */
+  W4_ERR_UNSUPPORTED = -4,  /* group_size != 128, gemv with M > 16, ...                  */
+  W4_ERR_WORKSPACE = -5,    /* workspace missing or smaller than the size query returns  */
+  W4_ERR_HIP = -6,          /* a HIP runtime call failed                                 */
+  W4_ERR_VALUE = -7         /* a scalar argument is out of range (clip ratio, grid size) */
+} w4_status;
+
+#define W4_GROUP_SIZE 128
+#define W4_GEMV_MAX_M 16
+
+/* Human-readable name of a status code (static storage; never NULL). */
+const char* w4_status_string(int status);
+
+/*
+ * awq_quantize_pack -- round-to-nearest group-128 quantization of v = W diag(s),
+ * with optional clipping, and nibble packing.  [AWQ-W4 card] "Scheme" and the
+ * scale-rewrite paragraph (the candidate weight Q(W diag(s))); "Clipping
+ * granularity" (one shrink ratio r for the whole linear); [27B card] opening
+ * paragraph (symmetric form).
+ *
+ * Per row n and group g, in IEEE fp32 with round-half-to-even rint:
+ *   v_k  = W[n][k] * s[k]                (s == NULL: v_k = W[n][k])
+ *   r<1: t = r * max|v|,  v_k = min(max(v_k, -t), t)
+ *   asymmetric: scale = bf16(max(max v - min v, 1e-5) / 15)
+ *               z = clamp(rint(-min v / scale), 0, 15)
+ *               q_k = clamp(rint(v_k / scale) + z, 0, 15)
+ *   symmetric : scale = bf16(max(max|v|, 1e-5) / 7)
+ *               q_k = clamp(rint(v_k / scale), -8, 7) + 8
+ * bf16() rounds to nearest even; "/" is IEEE division by the stored bf16 scale.
+ *
+ *   W          [N][K] bf16, device.           s        [K] fp32 or NULL.
+ *   clip_ratio in (0, 1]; 1 = no clipping.      symmetric 0 or 1.   group_size == 128.
+ *   qweight    [N][K/8] out.   scales [N][K/128] out.
+ *   qzeros     [N][ceil(K/1024)] out; must be NULL iff symmetric.
+ * Results are bit-identical to the definition above for every finite input.
+ */
+int awq_quantize_pack(const uint16_t* W, int N, int K, const float* s, float clip_ratio,
+                      int symmetric, int group_size, uint32_t* qweight, uint16_t* scales,
+                      uint32_t* qzeros, void* stream);
+
+/*
+ * w4a16_gemv -- decode contraction Y = X W_hat^T for 1 <= M <= 16 rows, bf16
+ * activations, int4 weights dequantized in registers; one wavefront reduction
+ * per output.  [QSRT card] "Reproducible runtime": decode batches of at most 16
+ * rows take their own path; [27B card] activations stay 16-bit.
+ *
+ *   X [M][K] bf16.  qweight/scales/qzeros as produced by awq_quantize_pack
+ *   (qzeros NULL iff symmetric).  Y [M][N] bf16 out: fp32 accumulation, each
+ *   128-group summed with exact integer weights (q - z) and scaled once, rounded
+ *   to nearest even at the store.
+ *   M > 16 returns W4_ERR_UNSUPPORTED (no silent fallback: use w4a16_gemm).
+ *   workspace / workspace_bytes: K-split partial sums for shapes whose
+ *   activations do not fit one workgroup's registers (size 0 for most shapes).
+ *   Size query: workspace == NULL with workspace_bytes != NULL writes the size
+ *   needed and returns W4_OK without enqueuing work.  To run a shape whose size
+ *   is 0, pass workspace == NULL and workspace_bytes == NULL.
+ */
+int w4a16_gemv(const uint16_t* X, int M, int K, int N, const uint32_t* qweight,
+               const uint16_t* scales, const uint32_t* qzeros, int symmetric, int group_size,
+               uint16_t* Y, void* workspace, size_t* workspace_bytes, void* stream);
+
+/*
+ * w4a16_gemm -- prefill contraction Y = X W_hat^T for any M >= 1 (intended for
+ * M >= 64), on MFMA bf16 matrix cores with LDS-staged activation tiles.
+ * [QSRT card] "Reproducible runtime": W4A16 serves prefill row counts.
+ * Same operands and rounding as w4a16_gemv.
+ *   workspace: per-row group sums of X (always needed, > 0 bytes).  Size query
+ *   as in w4a16_gemv.  The size depends only on (M, K, N).
+ */
+int w4a16_gemm(const uint16_t* X, int M, int K, int N, const uint32_t* qweight,
+               const uint16_t* scales, const uint32_t* qzeros, int symmetric, int group_size,
+               uint16_t* Y, void* workspace, size_t* workspace_bytes, void* stream);
+
+/*
+ * awq_grid_loss -- losses of C fake-quant candidates of one linear.
+ * [AWQ-W4 card] scale-rewrite paragraph: a candidate (s, r) is simulated by
+ * swapping the weight for Q(W diag(s)) diag(1/s), i.e. by feeding X diag(1/s)
+ * (rounded to bf16, the deployed prev_op /= s) to the int4 weight Q(W diag(s));
+ * "Search" and "Clipping granularity": s from the scale-exponent grid, one
+ * global shrink ratio r.
+ *   losses[c] = mean over T x N of (Y_hat_c - Y_ref)^2, Y_hat_c in fp32 and
+ *   Y_ref = bf16(X W^T).
+ *
+ *   X [T][K] bf16 calibration activations.  W [N][K] bf16 unquantized weight.
+ *   Yref [T][N] bf16, or NULL: then bf16(X W^T) is computed into the workspace.
+ *   S [C][K] fp32 (row c = s_c, every s_c[k] > 0).  ratios [C] fp32 in (0, 1].
+ *   losses [C] fp32 out (device).  Workspace size query as in w4a16_gemm; it
+ *   depends on (T, K, N, C) and on whether Yref is NULL.
+ * The per-tile partial sums are reduced in a fixed order: results are
+ * bit-identical from run to run.
+ */
+int awq_grid_loss(const uint16_t* X, int T, int K, int N, const uint16_t* W,
+                  const uint16_t* Yref, const float* S, const float* ratios, int C,
+                  int symmetric, int group_size, float* losses, void* workspace,
+                  size_t* workspace_bytes, void* stream);
+
+/*
+ * awq_search -- the two-phase search of [AWQ-W4 card] "Search": every alpha in
+ * `alphas` scored at r = 1, keep the first minimum alpha*; then every ratio in
+ * `ratios` scored at s(alpha*), keep the first minimum r*.
+ *   s(alpha)_k = max(m_k^alpha, 1e-4) / sqrt(max_j p_j * min_j p_j) with
+ *   m_k = mean_t |X[t][k]| (device, fp64, fixed order) and the rest in fp64 on
+ *   the host, stored fp32.
+ *
+ *   alphas [n_alpha], ratios [n_ratio]: host fp64 (1 <= n <= 64 each).
+ *   losses_out [n_alpha + n_ratio]: host fp32 out (alpha losses, then ratio losses).
+ *   alpha_index, ratio_index: host int out.   s_out [K] fp32 device out: s(alpha*).
+ *   workspace / workspace_bytes: as awq_grid_loss with C = max(n_alpha, n_ratio) plus
+ *   the statistic; workspace == NULL and workspace_bytes != NULL -> size query.
+ *   workspace == NULL and workspace_bytes == NULL -> the call allocates and frees
+ *   its own workspace.  Synchronizes `stream` (twice).
+ */
+int awq_search(const uint16_t* X, int T, int K, int N, const uint16_t* W,
+               const double* alphas, int n_alpha, const double* ratios, int n_ratio,
+               int symmetric, int group_size, float* losses_out, int* alpha_index,
+               int* ratio_index, float* s_out, void* workspace, size_t* workspace_bytes,
+               void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* W4A16_H */

@@ -1,0 +1,136 @@
+"""The C-ABI library on the host, no GPU: it loads, exports every function that
+include/w4a16.h declares, and rejects bad arguments before any HIP call."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import weight_only_int4_amd as w4
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "w4a16.h")
+P = ctypes.c_void_p
+A = P(0x10000)        # a 16-byte aligned fake device address (never dereferenced)
+MIS = P(0x10004)      # misaligned fake address
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return w4.load_library()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\*?\s+\**(\w+)\s*\(", text, flags=re.M)))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for n in ("awq_quantize_pack", "w4a16_gemv", "w4a16_gemm", "awq_grid_loss", "awq_search", "w4_status_string"):
+        assert n in names, names
+
+
+def test_every_declared_symbol_is_exported(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_status_strings(lib):
+    for code in range(0, -8, -1):
+        s = lib.w4_status_string(code).decode()
+        assert s.startswith("W4_"), s
+    assert lib.w4_status_string(-99).decode() == "W4_ERR_UNKNOWN"
+
+
+def q(lib, W=A, N=4, K=256, s=None, r=1.0, sym=0, gs=128, qw=A, sc=A, qz=A):
+    return lib.awq_quantize_pack(W, N, K, s, r, sym, gs, qw, sc, qz, None)
+
+
+def test_quantize_validation(lib):
+    assert q(lib, K=100) == -2
+    assert q(lib, K=0) == -2
+    assert q(lib, N=-1) == -2
+    assert q(lib, gs=64) == -4
+    assert q(lib, W=None) == -1
+    assert q(lib, qw=None) == -1
+    assert q(lib, sym=1) == -1                  # qzeros must be NULL when symmetric
+    assert q(lib, qz=None) == -1                # and set when asymmetric
+    assert q(lib, W=MIS) == -3
+    assert q(lib, s=MIS) == -3
+    assert q(lib, r=0.0) == -7
+    assert q(lib, r=1.5) == -7
+    assert q(lib, r=float("nan")) == -7
+    assert q(lib, sym=2, qz=None) == -7
+    assert q(lib, N=0) == 0                     # empty: nothing enqueued
+
+
+def test_gemv_validation_and_size_query(lib):
+    sz = ctypes.c_size_t(123)
+    f = lib.w4a16_gemv
+    assert f(A, 17, 256, 8, A, A, A, 0, 128, A, None, None, None) == -4
+    assert f(A, 1, 200, 8, A, A, A, 0, 128, A, None, None, None) == -2
+    assert f(A, 1, 256, 8, A, A, A, 0, 32, A, None, None, None) == -4
+    assert f(None, 1, 2048, 2048, None, None, None, 0, 128, None, None, ctypes.byref(sz), None) == 0
+    assert sz.value == 0
+    assert f(None, 16, 17408, 5120, None, None, None, 1, 128, None, None, ctypes.byref(sz), None) == 0
+    assert sz.value > 0
+    need = sz.value
+    small = ctypes.c_size_t(need - 4)
+    assert f(A, 16, 17408, 5120, A, A, None, 1, 128, A, A, ctypes.byref(small), None) == -5
+    assert f(A, 16, 17408, 5120, A, A, None, 1, 128, A, None, None, None) == -5
+    assert f(None, 1, 256, 8, A, A, A, 0, 128, A, None, None, None) == -1
+    assert f(A, 1, 256, 8, A, A, None, 0, 128, A, None, None, None) == -1
+    assert f(MIS, 1, 256, 8, A, A, A, 0, 128, A, None, None, None) == -3
+    assert f(A, 0, 256, 8, A, A, A, 0, 128, A, None, None, None) == 0      # M = 0: empty
+
+
+def test_gemm_size_query(lib):
+    sz = ctypes.c_size_t(0)
+    f = lib.w4a16_gemm
+    assert f(None, 2048, 2048, 6144, None, None, None, 0, 128, None, None, ctypes.byref(sz), None) == 0
+    assert sz.value == 16 * 2048 * 4            # group row sums, fp32 [K/128][M rounded to 128]
+    assert f(None, 200, 384, 8, None, None, None, 0, 128, None, None, ctypes.byref(sz), None) == 0
+    assert sz.value == 3 * 256 * 4
+    assert f(A, 200, 384, 8, A, A, A, 0, 128, A, None, None, None) == -5
+    small = ctypes.c_size_t(3 * 256 * 4 - 1)
+    assert f(A, 200, 384, 8, A, A, A, 0, 128, A, A, ctypes.byref(small), None) == -5
+    ok = ctypes.c_size_t(3 * 256 * 4)
+    assert f(A, 200, 384, 8, A, A, A, 0, 128, MIS, A, ctypes.byref(ok), None) == -3
+
+
+def test_grid_loss_validation(lib):
+    sz = ctypes.c_size_t(0)
+    f = lib.awq_grid_loss
+    assert f(None, 4096, 2048, 6144, None, None, None, None, 20, 0, 128, None, None, ctypes.byref(sz), None) == 0
+    with_ref = sz.value
+    assert f(None, 4096, 2048, 6144, None, A, None, None, 20, 0, 128, None, None, ctypes.byref(sz), None) == 0
+    assert with_ref - sz.value >= 4096 * 6144 * 2        # Y_ref buffer only when not given
+    assert f(A, 0, 2048, 64, A, None, A, A, 1, 0, 128, A, A, ctypes.byref(sz), None) == -2
+    assert f(A, 8, 2048, 64, A, None, A, A, -1, 0, 128, A, A, ctypes.byref(sz), None) == -2
+    assert f(A, 8, 2048, 64, A, None, A, A, 1, 3, 128, A, A, ctypes.byref(sz), None) == -7
+
+
+def test_search_validation(lib):
+    sz = ctypes.c_size_t(0)
+    f = lib.awq_search
+    D = ctypes.c_double
+    al = (D * 20)(*[i / 20 for i in range(20)])
+    ra = (D * 10)(*[1 - j / 20 for j in range(10)])
+    assert f(None, 4096, 2048, 6144, None, al, 20, ra, 10, 0, 128, None, None, None, None, None,
+             ctypes.byref(sz), None) == 0
+    assert sz.value > 20 * 6144 * 2048 // 2
+    assert f(A, 64, 256, 8, A, al, 0, ra, 10, 0, 128, None, None, None, None, None, ctypes.byref(sz), None) == -7
+    bad = (D * 1)(float("nan"))
+    assert f(A, 64, 256, 8, A, bad, 1, ra, 10, 0, 128, None, None, None, None, None, ctypes.byref(sz), None) == -7
+    badr = (D * 1)(0.0)
+    assert f(A, 64, 256, 8, A, al, 20, badr, 1, 0, 128, None, None, None, None, None, ctypes.byref(sz), None) == -7
+    assert f(A, 64, 256, 8, A, None, 20, ra, 10, 0, 128, None, None, None, None, None, ctypes.byref(sz), None) == -1
+
+
+def test_python_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(w4, "_LIB", None)
+    monkeypatch.setattr(w4, "_HERE", str(tmp_path))
+    with pytest.raises(RuntimeError, match="missing"):
+        w4.load_library()

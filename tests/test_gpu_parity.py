@@ -1,0 +1,362 @@
+"""GPU path (through the C ABI) against the CPU oracle, on the same seeded inputs.
+
+Bars:
+* quantize + pack: bit-exact (qweight, scales, qzeros).
+* GEMV / GEMM: relative Frobenius error <= 2e-3 against the fp64 oracle on the
+  same dequantized weights, and elementwise within half a bf16 ulp of the exact
+  value plus 1e-4 of the output RMS (the kernels keep every group sum exact in
+  integer weights and round once, at the store).
+* grid loss: every loss within 2e-3 relative of the oracle's; the chosen index
+  equals the oracle's or the oracle's losses at the two indices are within 2e-3.
+"""
+import numpy as np
+import pytest
+import torch
+
+import weight_only_int4_amd as w4
+import workloads as wl
+from oracle import w4a16_oracle as O
+from tests.gpu_util import (bf16_values, bits16, bits32, gpu_available, rel_fro, say, to_bf16, to_f32,
+                            to_i32)
+
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not gpu_available(), reason="needs an MI355X GPU")]
+
+FRO_TOL = 2e-3
+
+
+def _quant_gpu(W, s=None, r=1.0, sym=False):
+    qw, sc, qz = w4.awq_quantize_pack(to_bf16(W), None if s is None else to_f32(s), r, sym)
+    torch.cuda.synchronize()
+    return bits32(qw), bits16(sc), None if qz is None else bits32(qz)
+
+
+def _assert_quant_equal(W, s=None, r=1.0, sym=False):
+    gq, gs, gz = _quant_gpu(W, s, r, sym)
+    oq, os_, oz = O.quantize_pack(W, s, r, sym)
+    assert np.array_equal(gs, os_), f"scales differ at {np.argwhere(gs != os_)[:5]}"
+    if not sym:
+        assert np.array_equal(gz, oz), f"zeros differ at {np.argwhere(gz != oz)[:5]}"
+    assert np.array_equal(gq, oq), f"codes differ at {np.argwhere(gq != oq)[:5]}"
+
+
+def _fro_ok(y, ref):
+    """Relative Frobenius error <= 2e-3; for outputs so few that the bf16 rounding of
+    the exact result alone exceeds that, <= that rounding floor + 2e-4."""
+    floor = rel_fro(bf16_values(O.f32_to_bf16(np.asarray(ref, dtype=np.float32))), ref)
+    err = rel_fro(y, ref)
+    assert err <= max(FRO_TOL, floor + 2e-4), (err, floor)
+    return err, floor
+
+
+def _elementwise_ok(y_gpu, y_ref):
+    y_ref = np.asarray(y_ref, dtype=np.float64)
+    mag = np.abs(y_ref)
+    ulp = np.where(mag > 0, 2.0 ** (np.floor(np.log2(np.maximum(mag, 1e-300))) - 7), 0.0)
+    rms = np.sqrt(np.mean(y_ref ** 2)) if y_ref.size else 0.0
+    bound = 0.5 * ulp + 1e-4 * rms + 1e-30
+    bad = np.abs(y_gpu - y_ref) > bound
+    return int(bad.sum())
+
+
+# ----------------------------------------------------------------------------- quantize
+
+@pytest.mark.parametrize("sym", [False, True])
+@pytest.mark.parametrize("N,K", [(24, 512), (37, 384), (5, 128), (64, 1152), (3, 8320)])
+def test_quantize_small(sym, N, K):
+    say("quantize", N, K, sym)
+    _, W = wl.small_case(1, K, N, 1000 + N + K)
+    _assert_quant_equal(W, sym=sym)
+
+
+@pytest.mark.parametrize("sym", [False, True])
+@pytest.mark.parametrize("r", [1.0, 0.9, 0.55])
+def test_quantize_with_scales_and_clip(sym, r):
+    say("quantize s/clip", sym, r)
+    _, W = wl.small_case(1, 1024, 48, 77)
+    rng = np.random.default_rng(5)
+    s = np.exp(rng.standard_normal(1024) * 0.8).astype(np.float32)
+    _assert_quant_equal(W, s, r, sym)
+
+
+def test_quantize_golden_groups():
+    """The hand-computed worked groups go through the GPU quantizer unchanged."""
+    import json, os
+    g = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "worked_groups.json")))
+    for grp in g["groups"]:
+        vals = np.full(128, grp.get("fill", 0.0), dtype=np.float32)
+        for k, v in grp.get("listed", grp.get("listed_all", {})).items():
+            vals[int(k)] = v
+        W = wl.round_to_bf16_bits(vals)[None, :]
+        say("golden", grp["name"])
+        gq, gs, gz = _quant_gpu(W, sym=grp["symmetric"])
+        assert int(gs[0, 0]) == int(grp["scale_bits"], 16)
+        for i, word in grp.get("qweight_words", {}).items():
+            assert int(gq[0, int(i)]) == int(word, 16)
+        _assert_quant_equal(W, sym=grp["symmetric"])
+
+
+def test_quantize_division_ties():
+    """Exact half-integer quotients and their fp32 neighbours (IEEE division, ties to even)."""
+    sc = 164.0 / 2048.0
+    ties = [(k + 0.5) * sc for k in range(14)]
+    vals = ties + [float(np.nextafter(np.float32(t), np.float32(0))) for t in ties] + \
+        [float(np.nextafter(np.float32(t), np.float32(2))) for t in ties]
+    s = np.ones(128, dtype=np.float32)
+    s[2:2 + len(vals)] = vals
+    Wf = np.zeros(128, dtype=np.float32)
+    Wf[1] = 1.203125
+    Wf[2:2 + len(vals)] = 1.0
+    W = wl.round_to_bf16_bits(Wf)[None, :]
+    say("division ties")
+    _assert_quant_equal(W, s)
+
+
+def test_quantize_degenerate_groups():
+    """Constant and all-zero groups hit the 1e-5 range floor; a lone outlier clamps."""
+    W = np.zeros((4, 256), dtype=np.float32)
+    W[1, :] = 0.5
+    W[2, :128] = -3.0
+    W[3, 5] = 100.0
+    W = wl.round_to_bf16_bits(W)
+    say("degenerate groups")
+    for sym in (False, True):
+        for r in (1.0, 0.5):
+            _assert_quant_equal(W, None, r, sym)
+
+
+@pytest.mark.parametrize("shape", [0, 1])
+def test_quantize_full_size_large(shape):
+    """27B-shaped linears (symmetric): every row of a 1/16 sample, full rows."""
+    W = wl.large_weight(shape)
+    rows = np.arange(0, W.shape[0], 16)
+    say("quantize large", shape, W.shape)
+    gq, gs, _ = _quant_gpu(W, sym=True)
+    oq, os_, _ = O.quantize_pack(W[rows], None, 1.0, True)
+    assert np.array_equal(gs[rows], os_)
+    assert np.array_equal(gq[rows], oq)
+
+
+def test_quantize_full_size_decode_block():
+    """The seven linears of one hidden-2048 block, asymmetric, all rows."""
+    for layer in range(len(wl.BLOCK_LINEARS)):
+        W = wl.decode_weight(0, layer)
+        say("quantize block linear", layer, W.shape)
+        _assert_quant_equal(W)
+
+
+# ----------------------------------------------------------------------------- GEMV
+
+def _packed(W, sym, s=None):
+    qw, sc, qz = O.quantize_pack(W, s, 1.0, sym)
+    return qw, sc, qz
+
+
+def _gemv_case(X, W, sym):
+    qw, sc, qz = _packed(W, sym)
+    Y = w4.w4a16_gemv(to_bf16(X), to_i32(qw), to_bf16(sc), None if sym else to_i32(qz), sym)
+    torch.cuda.synchronize()
+    y = bf16_values(bits16(Y))
+    ref = O.linear(X, O.dequantize(qw, sc, qz, W.shape[1], sym))
+    return y, ref
+
+
+@pytest.mark.parametrize("M", list(range(1, 17)))
+@pytest.mark.parametrize("sym", [False, True])
+def test_gemv_all_m(M, sym):
+    say("gemv", M, sym)
+    X, W = wl.small_case(M, 2048, 300, 11 + M)
+    y, ref = _gemv_case(X, W, sym)
+    _fro_ok(y, ref)
+    assert _elementwise_ok(y, ref) == 0
+
+
+@pytest.mark.parametrize("M,K,N", [(1, 128, 1), (1, 384, 37), (3, 1152, 129), (8, 6144, 200), (16, 17408, 70),
+                                   (5, 5120, 64), (1, 17408, 33), (9, 8320, 17), (2, 16384, 8), (4, 24576, 5)])
+def test_gemv_ragged(M, K, N):
+    say("gemv ragged", M, K, N)
+    X, W = wl.small_case(M, K, N, 21)
+    for sym in (False, True):
+        y, ref = _gemv_case(X, W, sym)
+        _fro_ok(y, ref)
+        assert _elementwise_ok(y, ref) == 0
+
+
+def test_gemv_one_hot_and_zero():
+    """One-hot activations reproduce bf16 dequantized weights bit-exactly; X = 0 gives 0."""
+    _, W = wl.small_case(1, 512, 64, 3)
+    qw, sc, qz = _packed(W, False)
+    What = O.dequantize(qw, sc, qz, 512, False)
+    X = np.zeros((4, 512), dtype=np.uint16)
+    for i, k in enumerate((0, 127, 300, 511)):
+        X[i, k] = 0x3F80
+    say("gemv one-hot")
+    Y = w4.w4a16_gemv(to_bf16(X), to_i32(qw), to_bf16(sc), to_i32(qz), False)
+    torch.cuda.synchronize()
+    got = bits16(Y)
+    want = O.f32_to_bf16(What[:, [0, 127, 300, 511]].T.astype(np.float32))
+    assert np.array_equal(got, want)
+    Y0 = w4.w4a16_gemv(to_bf16(np.zeros((2, 512), np.uint16)), to_i32(qw), to_bf16(sc), to_i32(qz), False)
+    torch.cuda.synchronize()
+    assert not bf16_values(bits16(Y0)).any()
+
+
+def test_gemv_decode_block_full_size():
+    """All seven linears of block 0 at M in {1, 4, 16}, full size."""
+    for layer in range(len(wl.BLOCK_LINEARS)):
+        W = wl.decode_weight(0, layer)
+        for M in wl.DECODE_MS:
+            X = wl.decode_act(0, layer, M)
+            say("gemv block", layer, M)
+            y, ref = _gemv_case(X, W, False)
+            _fro_ok(y, ref)
+            assert _elementwise_ok(y, ref) == 0
+
+
+@pytest.mark.parametrize("shape", [0, 1])
+@pytest.mark.parametrize("M", [1, 8])
+def test_gemv_large_full_size(shape, M):
+    """27B-shaped symmetric linears at M in {1, 8}; oracle on a 1/8 sample of the rows of W."""
+    W = wl.large_weight(shape)
+    X = wl.large_act(shape, M)
+    qw, sc, _ = O.quantize_pack(W, None, 1.0, True)
+    say("gemv large", shape, M)
+    Y = w4.w4a16_gemv(to_bf16(X), to_i32(qw), to_bf16(sc), None, True)
+    torch.cuda.synchronize()
+    y = bf16_values(bits16(Y))
+    cols = np.arange(0, W.shape[0], 8)
+    ref = O.linear(X, O.dequantize(qw[cols], sc[cols], None, W.shape[1], True))
+    _fro_ok(y[:, cols], ref)
+    assert _elementwise_ok(y[:, cols], ref) == 0
+
+
+def test_gemv_rejects_m17():
+    _, W = wl.small_case(1, 256, 8, 1)
+    qw, sc, qz = _packed(W, False)
+    X = np.zeros((17, 256), dtype=np.uint16)
+    with pytest.raises(w4.W4Error):
+        w4.w4a16_gemv(to_bf16(X), to_i32(qw), to_bf16(sc), to_i32(qz), False)
+
+
+# ----------------------------------------------------------------------------- GEMM
+
+def _gemm_case(X, W, sym, rows=None):
+    qw, sc, qz = _packed(W, sym)
+    Y = w4.w4a16_gemm(to_bf16(X), to_i32(qw), to_bf16(sc), None if sym else to_i32(qz), sym)
+    torch.cuda.synchronize()
+    y = bf16_values(bits16(Y))
+    Xr = X if rows is None else X[rows]
+    ref = O.linear(Xr, O.dequantize(qw, sc, qz, W.shape[1], sym))
+    return (y if rows is None else y[rows]), ref
+
+
+@pytest.mark.parametrize("M,K,N", [(1, 128, 1), (64, 2048, 128), (200, 384, 200), (256, 1152, 1000),
+                                   (129, 2048, 257), (37, 5120, 64), (512, 256, 96), (130, 17408, 130)])
+@pytest.mark.parametrize("sym", [False, True])
+def test_gemm_shapes(M, K, N, sym):
+    say("gemm", M, K, N, sym)
+    X, W = wl.small_case(M, K, N, 31)
+    y, ref = _gemm_case(X, W, sym)
+    _fro_ok(y, ref)
+    assert _elementwise_ok(y, ref) == 0
+
+
+def test_gemm_one_hot_and_zero():
+    _, W = wl.small_case(1, 384, 160, 9)
+    qw, sc, qz = _packed(W, False)
+    What = O.dequantize(qw, sc, qz, 384, False)
+    X = np.zeros((130, 384), dtype=np.uint16)
+    ks = np.arange(130) * 3 % 384
+    X[np.arange(130), ks] = 0x3F80
+    say("gemm one-hot")
+    Y = w4.w4a16_gemm(to_bf16(X), to_i32(qw), to_bf16(sc), to_i32(qz), False)
+    torch.cuda.synchronize()
+    assert np.array_equal(bits16(Y), O.f32_to_bf16(What[:, ks].T.astype(np.float32)))
+
+
+@pytest.mark.parametrize("shape", [0, 1])
+def test_gemm_prefill_full_size(shape):
+    """M=2048 prefill shapes with x20 outlier channels, full size, all outputs."""
+    X, W = wl.prefill(shape)
+    say("gemm prefill", shape)
+    y, ref = _gemm_case(X, W, False)
+    _fro_ok(y, ref)
+    assert _elementwise_ok(y, ref) == 0
+
+
+@pytest.mark.parametrize("shape", [0, 1])
+@pytest.mark.parametrize("M", [64, 512])
+def test_gemm_large_full_size(shape, M):
+    W = wl.large_weight(shape)
+    X = wl.large_act(shape, M)
+    rows = np.arange(0, M, 8)
+    say("gemm large", shape, M)
+    y, ref = _gemm_case(X, W, True, rows)
+    _fro_ok(y, ref)
+    assert _elementwise_ok(y, ref) == 0
+
+
+def test_gemm_deterministic_and_overwrites():
+    X, W = wl.small_case(300, 1024, 300, 5)
+    qw, sc, qz = _packed(W, False)
+    args = (to_bf16(X), to_i32(qw), to_bf16(sc), to_i32(qz), False)
+    Y1 = torch.full((300, 300), float("nan"), dtype=torch.bfloat16, device="cuda")
+    w4.w4a16_gemm(*args, Y=Y1)
+    Y2 = w4.w4a16_gemm(*args)
+    torch.cuda.synchronize()
+    assert not torch.isnan(Y1.float()).any()
+    assert np.array_equal(bits16(Y1), bits16(Y2))
+
+
+# ----------------------------------------------------------------------------- grid loss
+
+def _grid_inputs(T, K, N, seed):
+    X, W = wl.awq_calibration(T, K, N, seed_block=seed)
+    m = O.act_mean_abs(X)
+    S = np.stack([O.awq_scales(m, a) for a in O.alpha_grid()])
+    return X, W, S
+
+
+@pytest.mark.parametrize("sym", [False, True])
+def test_grid_loss_small(sym):
+    X, W, S = _grid_inputs(256, 384, 200, 1)
+    S = np.concatenate([S, np.repeat(S[6:7], 10, axis=0)])          # 20 alphas + 10 ratios at alpha_6
+    ratios = np.concatenate([np.ones(20, np.float32), O.shrink_grid().astype(np.float32)])
+    say("grid loss small", sym)
+    L = w4.awq_grid_loss(to_bf16(X), to_bf16(W), to_f32(S), to_f32(ratios), sym)
+    L2 = w4.awq_grid_loss(to_bf16(X), to_bf16(W), to_f32(S), to_f32(ratios), sym)
+    torch.cuda.synchronize()
+    got = L.cpu().numpy().astype(np.float64)
+    assert np.array_equal(got, L2.cpu().numpy().astype(np.float64)), "grid loss not deterministic"
+    want = O.grid_loss(X, W, S, ratios, sym)
+    rel = np.abs(got - want) / want
+    assert rel.max() <= 2e-3, rel.max()
+
+
+def test_grid_loss_given_yref():
+    X, W, S = _grid_inputs(200, 256, 130, 2)
+    ratios = np.ones(S.shape[0], dtype=np.float32)
+    Yref = O.f32_to_bf16(O.linear(X, O.bf16_to_f32(W)).astype(np.float32))
+    say("grid loss yref")
+    L = w4.awq_grid_loss(to_bf16(X), to_bf16(W), to_f32(S), to_f32(ratios), False, Yref=to_bf16(Yref))
+    torch.cuda.synchronize()
+    want = O.grid_loss(X, W, S, ratios, False)
+    assert np.max(np.abs(L.cpu().numpy() - want) / want) <= 2e-3
+
+
+def _argmin_ok(i_gpu, i_or, losses_or):
+    return i_gpu == i_or or abs(losses_or[i_gpu] - losses_or[i_or]) <= 2e-3 * losses_or[i_or]
+
+
+def test_search_small():
+    X, W = wl.awq_calibration(512, 256, 192, seed_block=3)
+    say("search small")
+    res = w4.awq_search(to_bf16(X), to_bf16(W), O.alpha_grid(), O.shrink_grid())
+    ref = O.search(X, W)
+    la, lr = np.array(res["alpha_losses"]), np.array(res["ratio_losses"])
+    assert np.max(np.abs(la - ref["alpha_losses"]) / ref["alpha_losses"]) <= 2e-3
+    assert _argmin_ok(res["alpha_index"], ref["alpha_index"], ref["alpha_losses"])
+    if res["alpha_index"] == ref["alpha_index"]:
+        assert np.array_equal(res["s"].cpu().numpy(), ref["s"])
+        assert np.max(np.abs(lr - ref["ratio_losses"]) / ref["ratio_losses"]) <= 2e-3
+        assert _argmin_ok(res["ratio_index"], ref["ratio_index"], ref["ratio_losses"])

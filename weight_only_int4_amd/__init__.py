@@ -1,0 +1,236 @@
+"""Weight-only int4, group-128 linear layers (W4A16) on AMD MI355X (gfx950).
+
+Thin Python binding over the C-ABI library ``libw4a16.so`` (see
+``include/w4a16.h``).  The functions keep the C names; they check dtype,
+device and contiguity, allocate outputs with torch (device memory only),
+pass raw pointers and the current HIP stream, and raise ``W4Error`` on a
+non-zero status.  Every computation runs in the library's HIP kernels: there
+is no Python or CPU fallback, and a missing library is an error.
+
+Tensor conventions: bf16 data as ``torch.bfloat16``; packed uint32 words
+(qweight, qzeros) as ``torch.int32`` tensors holding the same bits.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+__all__ = [
+    "W4Error", "library_path", "load_library", "awq_quantize_pack", "w4a16_gemv", "w4a16_gemm",
+    "awq_grid_loss", "awq_search", "GROUP_SIZE", "GEMV_MAX_M",
+]
+
+GROUP_SIZE = 128
+GEMV_MAX_M = 16
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB = None
+
+_vp, _i, _f, _sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.POINTER(ctypes.c_size_t)
+_SIGNATURES = {
+    "w4_status_string": ([_i], ctypes.c_char_p),
+    "awq_quantize_pack": ([_vp, _i, _i, _vp, _f, _i, _i, _vp, _vp, _vp, _vp], _i),
+    "w4a16_gemv": ([_vp, _i, _i, _i, _vp, _vp, _vp, _i, _i, _vp, _vp, _sz, _vp], _i),
+    "w4a16_gemm": ([_vp, _i, _i, _i, _vp, _vp, _vp, _i, _i, _vp, _vp, _sz, _vp], _i),
+    "awq_grid_loss": ([_vp, _i, _i, _i, _vp, _vp, _vp, _vp, _i, _i, _i, _vp, _vp, _sz, _vp], _i),
+    "awq_search": ([_vp, _i, _i, _i, _vp, ctypes.POINTER(ctypes.c_double), _i,
+                    ctypes.POINTER(ctypes.c_double), _i, _i, _i, ctypes.POINTER(ctypes.c_float),
+                    ctypes.POINTER(ctypes.c_int), ctypes.POINTER(ctypes.c_int), _vp, _vp, _sz, _vp], _i),
+}
+
+
+class W4Error(RuntimeError):
+    """A W4A16 library call returned a non-zero status."""
+
+    def __init__(self, status: int, message: str):
+        super().__init__(message)
+        self.status = status
+
+
+def library_path() -> str:
+    return os.path.join(_HERE, "libw4a16.so")
+
+
+def load_library() -> ctypes.CDLL:
+    """Load libw4a16.so (built in-tree by ``python -m weight_only_int4_amd.build``)."""
+    global _LIB
+    if _LIB is None:
+        path = library_path()
+        if not os.path.exists(path):
+            raise RuntimeError(f"{path} is missing: build it with `python -m weight_only_int4_amd.build`")
+        lib = ctypes.CDLL(path)
+        for name, (args, res) in _SIGNATURES.items():
+            fn = getattr(lib, name)
+            fn.argtypes = args
+            fn.restype = res
+        _LIB = lib
+    return _LIB
+
+
+def _check(rc: int) -> None:
+    if rc != 0:
+        msg = load_library().w4_status_string(rc).decode()
+        raise W4Error(rc, msg)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _need(t, dtype, name, ndim=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims")
+
+
+def _workspace(query, device, workspace):
+    size = ctypes.c_size_t(0)
+    _check(query(ctypes.byref(size)))
+    if size.value == 0:
+        return None, None
+    if workspace is None or workspace.numel() < size.value:
+        workspace = torch.empty(size.value, dtype=torch.uint8, device=device)
+    return workspace, ctypes.c_size_t(workspace.numel())
+
+
+def awq_quantize_pack(W, s=None, clip_ratio: float = 1.0, symmetric: bool = False,
+                      qweight=None, scales=None, qzeros=None):
+    """Quantize W [N][K] bf16 (times diag(s), clipped at clip_ratio) to packed int4.
+
+    Returns (qweight int32 [N][K/8], scales bf16 [N][K/128], qzeros int32
+    [N][ceil(K/1024)] or None when symmetric).
+    """
+    lib = load_library()
+    _need(W, torch.bfloat16, "W", 2)
+    N, K = W.shape
+    dev = W.device
+    if s is not None:
+        _need(s, torch.float32, "s", 1)
+    G = K // GROUP_SIZE
+    if qweight is None:
+        qweight = torch.empty((N, K // 8), dtype=torch.int32, device=dev)
+    if scales is None:
+        scales = torch.empty((N, G), dtype=torch.bfloat16, device=dev)
+    if not symmetric and qzeros is None:
+        qzeros = torch.empty((N, (G + 7) // 8), dtype=torch.int32, device=dev)
+    if symmetric:
+        qzeros = None
+    _check(lib.awq_quantize_pack(_ptr(W), N, K, _ptr(s), float(clip_ratio), int(symmetric), GROUP_SIZE,
+                                 _ptr(qweight), _ptr(scales), _ptr(qzeros), _stream(dev)))
+    return qweight, scales, qzeros
+
+
+def _packed_shapes(X, qweight, scales, qzeros, symmetric):
+    _need(X, torch.bfloat16, "X", 2)
+    _need(qweight, torch.int32, "qweight", 2)
+    _need(scales, torch.bfloat16, "scales", 2)
+    if not symmetric:
+        _need(qzeros, torch.int32, "qzeros", 2)
+    M, K = X.shape
+    N = qweight.shape[0]
+    if qweight.shape[1] * 8 != K:
+        raise ValueError("qweight must be [N][K/8] for X [M][K]")
+    return M, K, N
+
+
+def w4a16_gemv(X, qweight, scales, qzeros=None, symmetric: bool = False, Y=None, workspace=None):
+    """Decode GEMV: Y [M][N] bf16 = X [M][K] (M <= 16) times the dequantized weight, transposed."""
+    lib = load_library()
+    M, K, N = _packed_shapes(X, qweight, scales, qzeros, symmetric)
+    dev = X.device
+    if Y is None:
+        Y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    qz = None if symmetric else qzeros
+
+    def q(sz):
+        return lib.w4a16_gemv(None, M, K, N, None, None, None, int(symmetric), GROUP_SIZE, None, None, sz, None)
+
+    ws, wsb = _workspace(q, dev, workspace)
+    _check(lib.w4a16_gemv(_ptr(X), M, K, N, _ptr(qweight), _ptr(scales), _ptr(qz), int(symmetric), GROUP_SIZE,
+                          _ptr(Y), _ptr(ws), None if wsb is None else ctypes.byref(wsb), _stream(dev)))
+    return Y
+
+
+def w4a16_gemm(X, qweight, scales, qzeros=None, symmetric: bool = False, Y=None, workspace=None):
+    """Prefill GEMM (MFMA): Y [M][N] bf16 = X [M][K] times the dequantized weight, transposed."""
+    lib = load_library()
+    M, K, N = _packed_shapes(X, qweight, scales, qzeros, symmetric)
+    dev = X.device
+    if Y is None:
+        Y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    qz = None if symmetric else qzeros
+
+    def q(sz):
+        return lib.w4a16_gemm(None, M, K, N, None, None, None, int(symmetric), GROUP_SIZE, None, None, sz, None)
+
+    ws, wsb = _workspace(q, dev, workspace)
+    _check(lib.w4a16_gemm(_ptr(X), M, K, N, _ptr(qweight), _ptr(scales), _ptr(qz), int(symmetric), GROUP_SIZE,
+                          _ptr(Y), _ptr(ws), None if wsb is None else ctypes.byref(wsb), _stream(dev)))
+    return Y
+
+
+def awq_grid_loss(X, W, S, ratios, symmetric: bool = False, Yref=None, losses=None, workspace=None):
+    """Losses [C] fp32 of the candidates (S[c], ratios[c]) against bf16(X W^T) (or Yref)."""
+    lib = load_library()
+    _need(X, torch.bfloat16, "X", 2)
+    _need(W, torch.bfloat16, "W", 2)
+    _need(S, torch.float32, "S", 2)
+    _need(ratios, torch.float32, "ratios", 1)
+    if Yref is not None:
+        _need(Yref, torch.bfloat16, "Yref", 2)
+    T, K = X.shape
+    N = W.shape[0]
+    C = S.shape[0]
+    dev = X.device
+    if losses is None:
+        losses = torch.empty(C, dtype=torch.float32, device=dev)
+
+    def q(sz):
+        return lib.awq_grid_loss(None, T, K, N, None, _ptr(Yref) if Yref is not None else None, None, None, C,
+                                 int(symmetric), GROUP_SIZE, None, None, sz, None)
+
+    ws, wsb = _workspace(q, dev, workspace)
+    _check(lib.awq_grid_loss(_ptr(X), T, K, N, _ptr(W), _ptr(Yref), _ptr(S), _ptr(ratios), C, int(symmetric),
+                             GROUP_SIZE, _ptr(losses), _ptr(ws), None if wsb is None else ctypes.byref(wsb),
+                             _stream(dev)))
+    return losses
+
+
+def awq_search(X, W, alphas, ratios, symmetric: bool = False, workspace=None):
+    """Two-phase AWQ search.  Returns dict(alpha_losses, ratio_losses, alpha_index,
+    ratio_index, s) with s = s(alpha*) as a fp32 GPU tensor.  Synchronizes."""
+    lib = load_library()
+    _need(X, torch.bfloat16, "X", 2)
+    _need(W, torch.bfloat16, "W", 2)
+    T, K = X.shape
+    N = W.shape[0]
+    dev = X.device
+    a = (ctypes.c_double * len(alphas))(*[float(x) for x in alphas])
+    r = (ctypes.c_double * len(ratios))(*[float(x) for x in ratios])
+    out = (ctypes.c_float * (len(alphas) + len(ratios)))()
+    ia, ir = ctypes.c_int(-1), ctypes.c_int(-1)
+    s_out = torch.empty(K, dtype=torch.float32, device=dev)
+
+    def q(sz):
+        return lib.awq_search(None, T, K, N, None, a, len(alphas), r, len(ratios), int(symmetric), GROUP_SIZE,
+                              None, None, None, None, None, sz, None)
+
+    ws, wsb = _workspace(q, dev, workspace)
+    _check(lib.awq_search(_ptr(X), T, K, N, _ptr(W), a, len(alphas), r, len(ratios), int(symmetric), GROUP_SIZE,
+                          out, ctypes.byref(ia), ctypes.byref(ir), _ptr(s_out), _ptr(ws),
+                          None if wsb is None else ctypes.byref(wsb), _stream(dev)))
+    vals = list(out)
+    return dict(alpha_losses=vals[: len(alphas)], ratio_losses=vals[len(alphas):], alpha_index=ia.value,
+                ratio_index=ir.value, s=s_out)

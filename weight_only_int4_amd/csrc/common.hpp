@@ -1,0 +1,67 @@
+// Shared device helpers for the W4A16 kernels (gfx950 / CDNA4, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/w4a16.h"
+
+namespace w4 {
+
+constexpr int kGroup = 128;          // input channels per quantization group
+constexpr int kWave = 64;            // CDNA wavefront width
+
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
+typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
+typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2;
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t bits16) {
+  return __uint_as_float(bits16 << 16);
+}
+
+// fp32 -> bf16 bits, round to nearest even (finite inputs).
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+// Two int4 codes of one packed word as a bf16 pair of exact integers 128 + q.
+// bf16 0x4300 is 128.0 with a mantissa step of 1, so OR-ing a nibble into the
+// low mantissa bits yields 128 + q exactly.  For word w, pair p (0..3) holds
+// (code of nibble p, code of nibble p + 4) = elements (p, p + 4) of the word's
+// 8-channel run.
+__device__ __forceinline__ uint32_t nibble_pair(uint32_t w, int p) {
+  return ((w >> (4 * p)) & 0x000F000Fu) | 0x43004300u;
+}
+
+// Reorder 8 consecutive bf16 activations (x0..x7 in 4 dwords) into the pairs
+// (x0,x4) (x1,x5) (x2,x6) (x3,x7) that match nibble_pair's element order.
+__device__ __forceinline__ void pair_activations(const uint32_t d[4], uint32_t e[4]) {
+  e[0] = (d[0] & 0xFFFFu) | (d[2] << 16);
+  e[1] = (d[0] >> 16) | (d[2] & 0xFFFF0000u);
+  e[2] = (d[1] & 0xFFFFu) | (d[3] << 16);
+  e[3] = (d[1] >> 16) | (d[3] & 0xFFFF0000u);
+}
+
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a),
+                                         __builtin_bit_cast(bf16x2, b), c, false);
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, kWave);
+  return v;
+}
+
+}  // namespace w4
+
+// Host-side launch-error helper: returns W4_ERR_HIP on a failed launch.
+#define W4_CHECK_LAUNCH()                                   \
+  do {                                                      \
+    if (hipPeekAtLastError() != hipSuccess) {               \
+      (void)hipGetLastError();                              \
+      return W4_ERR_HIP;                                    \
+    }                                                       \
+  } while (0)

@@ -1,0 +1,281 @@
+// Decode contraction Y = X W_hat^T for 1 <= M <= 16 rows (W4A16 GEMV).
+//
+// Model card "GLM-5.2-QSRT-Fruit-Instruct", "Reproducible runtime": decode
+// batches of at most 16 rows take their own path; model card
+// "Qwen3.6-27B-W4A16", opening paragraph: int4 weights, 16-bit activations.
+//
+// Design (CDNA4, wave64, VALU): a workgroup owns a contiguous slice of input
+// channels ("split") and a run of output rows.  Each lane keeps its WPL words
+// (8*WPL channels, inside one 128-group) of activations in registers as bf16
+// pairs, then streams the matching packed words of every row with one 16/8/4-byte
+// coalesced load, turns each word into four bf16 pairs of exact integers 128+q
+// with one shift and one AND-OR, and accumulates v_dot2_f32_bf16 products in fp32.
+// The zero point and scale are applied once per lane and row:
+//   sum_k x_k (q_k - z) sc = sc * (sum_k x_k (128 + q_k) - (128 + z) sum_k x_k).
+// Lane partials are reduced across the wavefront (transposing butterfly, one
+// value per lane at the end) and across waves through LDS, in a fixed order.
+#include "internal.hpp"
+
+namespace w4 {
+
+struct GemvArgs {
+  const uint16_t* X;
+  int K, N;
+  const uint32_t* qweight;
+  const uint16_t* scales;
+  const uint32_t* qzeros;
+  int symmetric;
+  uint16_t* Y;
+  float* partial;       // [splits][M][N] when splits > 1
+  int wps;              // packed words per split (multiple of WPL)
+  int rows_per_block;
+};
+
+// Butterfly reduction of V values per lane across the 64 lanes of a wave.
+// The first log2(V) steps halve the values each lane carries (each lane keeps
+// the half selected by its lane bit and adds its partner's copy); the rest are
+// plain xor sums.  Afterwards a[0] of every lane holds the wave total of value
+// index lane / (64 / V).
+template <int V, int O>
+struct WaveReduce {
+  __device__ static __forceinline__ void run(float* a, int lane) {
+    if constexpr (V > 1) {
+      constexpr int H = V / 2;
+      const bool upper = (lane & O) != 0;
+#pragma unroll
+      for (int i = 0; i < H; ++i) {
+        const float send = upper ? a[i] : a[i + H];
+        const float keep = upper ? a[i + H] : a[i];
+        a[i] = keep + __shfl_xor(send, O, kWave);
+      }
+      WaveReduce<H, O / 2>::run(a, lane);
+    } else if constexpr (O >= 1) {
+      a[0] += __shfl_xor(a[0], O, kWave);
+      WaveReduce<1, O / 2>::run(a, lane);
+    }
+  }
+};
+
+constexpr int pow2_ceil(int v) { return v <= 1 ? 1 : 2 * pow2_ceil((v + 1) / 2); }
+
+template <int WPL>
+struct WordVec;
+template <>
+struct WordVec<4> {
+  __device__ static __forceinline__ void load(const uint32_t* p, uint32_t* w) {
+    const uint4 v = *reinterpret_cast<const uint4*>(p);
+    w[0] = v.x; w[1] = v.y; w[2] = v.z; w[3] = v.w;
+  }
+};
+template <>
+struct WordVec<2> {
+  __device__ static __forceinline__ void load(const uint32_t* p, uint32_t* w) {
+    const uint2 v = *reinterpret_cast<const uint2*>(p);
+    w[0] = v.x; w[1] = v.y;
+  }
+};
+template <>
+struct WordVec<1> {
+  __device__ static __forceinline__ void load(const uint32_t* p, uint32_t* w) { w[0] = *p; }
+};
+
+template <int M, int WPL, int RB>
+__global__ __launch_bounds__(1024) void gemv_kernel(GemvArgs a) {
+  constexpr int V = RB * M;
+  constexpr int VP = pow2_ceil(V);
+  constexpr int SPREAD = kWave / VP;          // lanes per reduced value
+  __shared__ float red[16][VP];
+
+  const int t = threadIdx.x;
+  const int lane = t & (kWave - 1);
+  const int wave = t >> 6;
+  const int nw = blockDim.x >> 6;
+  const int words = a.K >> 3;
+  const int G = a.K >> 7;
+  const int GW = (G + 7) >> 3;
+  const int wb = blockIdx.y * a.wps + t * WPL;
+  const bool active = (t * WPL < a.wps) && (wb < words);
+  const int g = wb >> 4;
+
+  // this lane's activations as (x_j, x_j+4) bf16 pairs, and their fp32 sums
+  uint32_t xp[M][WPL][4];
+  float xs[M];
+#pragma unroll
+  for (int m = 0; m < M; ++m) {
+    xs[m] = 0.0f;
+#pragma unroll
+    for (int i = 0; i < WPL; ++i) {
+      uint32_t d[4] = {0u, 0u, 0u, 0u};
+      if (active) {
+        const uint4 v = *reinterpret_cast<const uint4*>(a.X + (size_t)m * a.K + (size_t)(wb + i) * 8);
+        d[0] = v.x; d[1] = v.y; d[2] = v.z; d[3] = v.w;
+      }
+      pair_activations(d, xp[m][i]);
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        xs[m] += __uint_as_float(d[q] << 16) + __uint_as_float(d[q] & 0xFFFF0000u);
+    }
+  }
+
+  const int row_begin = blockIdx.x * a.rows_per_block;
+  const int row_end = min(row_begin + a.rows_per_block, a.N);
+  const uint32_t zfix = a.symmetric ? 136u : 128u;
+
+  for (int r0 = row_begin; r0 < row_end; r0 += RB) {
+    uint32_t w[RB][WPL];
+    float sc[RB], zc[RB];
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      const int n = r0 + rb;
+#pragma unroll
+      for (int i = 0; i < WPL; ++i) w[rb][i] = 0u;
+      sc[rb] = 0.0f;
+      zc[rb] = 0.0f;
+      if (active && n < row_end) {
+        WordVec<WPL>::load(a.qweight + (size_t)n * words + wb, w[rb]);
+        sc[rb] = bf16_bits_to_f32(a.scales[(size_t)n * G + g]);
+        uint32_t z = zfix;
+        if (!a.symmetric) z = 128u + ((a.qzeros[(size_t)n * GW + (g >> 3)] >> (4 * (g & 7))) & 0xFu);
+        zc[rb] = (float)z;
+      }
+    }
+    float part[VP];
+#pragma unroll
+    for (int v = V; v < VP; ++v) part[v] = 0.0f;
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      uint32_t bp[WPL][4];
+#pragma unroll
+      for (int i = 0; i < WPL; ++i)
+#pragma unroll
+        for (int p = 0; p < 4; ++p) bp[i][p] = nibble_pair(w[rb][i], p);
+#pragma unroll
+      for (int m = 0; m < M; ++m) {
+        float acc = 0.0f;
+#pragma unroll
+        for (int i = 0; i < WPL; ++i)
+#pragma unroll
+          for (int p = 0; p < 4; ++p) acc = dot2_bf16(xp[m][i][p], bp[i][p], acc);
+        part[rb * M + m] = sc[rb] * (acc - zc[rb] * xs[m]);
+      }
+    }
+    WaveReduce<VP, 32>::run(part, lane);
+    const int idx = lane / SPREAD;
+    const bool writer = (lane % SPREAD) == 0 && idx < V;
+    const int rb = idx / M, m = idx % M;
+    const int n = r0 + rb;
+    if (nw == 1) {
+      if (writer && n < row_end) {
+        if (a.partial)
+          a.partial[((size_t)blockIdx.y * M + m) * a.N + n] = part[0];
+        else
+          a.Y[(size_t)m * a.N + n] = (uint16_t)f32_to_bf16_bits(part[0]);
+      }
+    } else {
+      if (writer) red[wave][idx] = part[0];
+      __syncthreads();
+      if (t < V) {
+        const int rbt = t / M, mt = t % M;
+        const int nt = r0 + rbt;
+        float sum = 0.0f;
+        for (int ww = 0; ww < nw; ++ww) sum += red[ww][t];
+        if (nt < row_end) {
+          if (a.partial)
+            a.partial[((size_t)blockIdx.y * M + mt) * a.N + nt] = sum;
+          else
+            a.Y[(size_t)mt * a.N + nt] = (uint16_t)f32_to_bf16_bits(sum);
+        }
+      }
+      __syncthreads();
+    }
+  }
+}
+
+// Y[m][n] = bf16(sum over splits of partial[s][m][n]), splits in order.
+__global__ __launch_bounds__(256) void gemv_split_reduce(const float* partial, int splits, size_t MN,
+                                                         uint16_t* Y) {
+  const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= MN) return;
+  float s = 0.0f;
+  for (int k = 0; k < splits; ++k) s += partial[(size_t)k * MN + i];
+  Y[i] = (uint16_t)f32_to_bf16_bits(s);
+}
+
+namespace {
+
+struct GemvPlan {
+  int wpl, rb, nw, splits, wps, rows_per_block;
+};
+
+constexpr int kTargetWaves = 256 * 16;   // 256 CUs x 16 resident waves at <= 128 VGPRs
+
+GemvPlan plan_gemv(int M, int K, int N) {
+  GemvPlan p;
+  p.wpl = M <= 4 ? 4 : (M <= 8 ? 2 : 1);
+  p.rb = M <= 2 ? 4 : 2;
+  const int words = K / 8;
+  const int max_wps = 16 * kWave * p.wpl;
+  p.splits = (words + max_wps - 1) / max_wps;
+  int wps = (words + p.splits - 1) / p.splits;
+  p.wps = (wps + p.wpl - 1) / p.wpl * p.wpl;
+  p.nw = (p.wps / p.wpl + kWave - 1) / kWave;
+  long long r = ((long long)N * p.splits * p.nw + kTargetWaves - 1) / kTargetWaves;
+  if (r < p.rb) r = p.rb;
+  r = (r + p.rb - 1) / p.rb * p.rb;
+  p.rows_per_block = (int)r;
+  return p;
+}
+
+template <int M>
+void launch_m(const GemvArgs& a, const GemvPlan& p, hipStream_t stream) {
+  constexpr int WPL = M <= 4 ? 4 : (M <= 8 ? 2 : 1);
+  constexpr int RB = M <= 2 ? 4 : 2;
+  dim3 grid((unsigned)((a.N + p.rows_per_block - 1) / p.rows_per_block), (unsigned)p.splits);
+  hipLaunchKernelGGL((gemv_kernel<M, WPL, RB>), grid, dim3(p.nw * kWave), 0, stream, a);
+}
+
+}  // namespace
+
+size_t gemv_workspace_bytes(int M, int K, int N) {
+  if (M <= 0 || N <= 0 || K <= 0) return 0;
+  const GemvPlan p = plan_gemv(M, K, N);
+  return p.splits > 1 ? (size_t)p.splits * M * N * sizeof(float) : 0;
+}
+
+int launch_gemv(const uint16_t* X, int M, int K, int N, const uint32_t* qweight,
+                const uint16_t* scales, const uint32_t* qzeros, int symmetric, uint16_t* Y,
+                void* workspace, hipStream_t stream) {
+  if (M == 0 || N == 0) return W4_OK;
+  const GemvPlan p = plan_gemv(M, K, N);
+  GemvArgs a{X, K, N, qweight, scales, qzeros, symmetric, Y,
+             p.splits > 1 ? static_cast<float*>(workspace) : nullptr, p.wps, p.rows_per_block};
+  switch (M) {
+    case 1: launch_m<1>(a, p, stream); break;
+    case 2: launch_m<2>(a, p, stream); break;
+    case 3: launch_m<3>(a, p, stream); break;
+    case 4: launch_m<4>(a, p, stream); break;
+    case 5: launch_m<5>(a, p, stream); break;
+    case 6: launch_m<6>(a, p, stream); break;
+    case 7: launch_m<7>(a, p, stream); break;
+    case 8: launch_m<8>(a, p, stream); break;
+    case 9: launch_m<9>(a, p, stream); break;
+    case 10: launch_m<10>(a, p, stream); break;
+    case 11: launch_m<11>(a, p, stream); break;
+    case 12: launch_m<12>(a, p, stream); break;
+    case 13: launch_m<13>(a, p, stream); break;
+    case 14: launch_m<14>(a, p, stream); break;
+    case 15: launch_m<15>(a, p, stream); break;
+    case 16: launch_m<16>(a, p, stream); break;
+    default: return W4_ERR_UNSUPPORTED;
+  }
+  W4_CHECK_LAUNCH();
+  if (p.splits > 1) {
+    const size_t MN = (size_t)M * N;
+    hipLaunchKernelGGL(gemv_split_reduce, dim3((unsigned)((MN + 255) / 256)), dim3(256), 0, stream,
+                       static_cast<const float*>(workspace), p.splits, MN, Y);
+    W4_CHECK_LAUNCH();
+  }
+  return W4_OK;
+}
+
+}  // namespace w4

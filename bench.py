@@ -1,0 +1,423 @@
+"""Benchmark of the W4A16 group-128 hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--step-only]
+
+One step is one decode sweep: the seven linears of a hidden-2048 decoder block
+(q 2048->2048, k/v 2048->1024, o 2048->2048, gate/up 2048->6144, down
+6144->2048) for 28 blocks, M = 1 bf16 activation row, asymmetric int4 group-128
+weights resident in HBM (734 MB of packed weights per sweep, more than the
+256 MB Infinity Cache, so every step streams them from HBM).  The step is
+replayed as one HIP graph of 196 GEMV launches.
+
+``value`` is the sweep's algorithmic bytes (packed weights + bf16 scales +
+packed zeros + X + Y) divided by the wall time per step (TB/s).  The same JSON
+line carries:
+  * ``roofline`` of the dominant kernel (the GEMV): algorithmic bytes per launch
+    over its average launch duration -- the event-timed graph replay (only GEMV
+    launches, back to back on one stream) divided by the launches -- against
+    the 8 TB/s HBM peak;
+  * ``rows``: every other step of the path measured in the same run (cold-cache
+    GEMV on the 27B-shaped linears, decode sweeps at M = 4 and 16, prefill GEMM
+    at M = 2048 and the 27B shapes, quantize + pack, the full 30-candidate AWQ
+    search), each with its own roofline fraction;
+  * ``cpu_baseline``: the CPU oracle on a bounded sample of the same sweep.
+All inputs are seeded synthetic tensors (``workloads``).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+GROUP = 128
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+# ----------------------------------------------------------------------------- helpers
+
+def packed_bytes(N, K, symmetric):
+    G = K // GROUP
+    b = N * K // 2 + N * G * 2
+    if not symmetric:
+        b += N * ((G + 7) // 8) * 4
+    return b
+
+
+def gemv_bytes(M, K, N, symmetric):
+    return packed_bytes(N, K, symmetric) + M * K * 2 + M * N * 2
+
+
+def to_dev_bf16(torch, u16):
+    return torch.from_numpy(np.ascontiguousarray(u16).view(np.int16)).view(torch.bfloat16).cuda()
+
+
+class Launch:
+    """One prepared GEMV/GEMM launch (operands preallocated, arguments validated once)."""
+
+    def __init__(self, launcher, nbytes, flops):
+        self.launcher, self.nbytes, self.flops = launcher, nbytes, flops
+
+    def __call__(self):
+        self.launcher()
+
+
+_SPACER = {}
+
+
+def spacer(torch, ms=20.0):
+    """Queue ~ms of GPU busy time so that every launch and event recorded after it
+    is already enqueued when the GPU reaches it (the host never sits inside a
+    timed interval).  torch.cuda._sleep spins a fixed number of cycles."""
+    if "cycles_per_ms" not in _SPACER:
+        torch.cuda._sleep(1000)
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        torch.cuda._sleep(2_000_000)
+        b.record()
+        b.synchronize()
+        _SPACER["cycles_per_ms"] = 2_000_000 / max(a.elapsed_time(b), 1e-3)
+    torch.cuda._sleep(int(_SPACER["cycles_per_ms"] * ms))
+
+
+def time_events(torch, fn, iters):
+    """Average ms per call of fn over iters calls bracketed by one pair of events."""
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    spacer(torch)
+    s.record()
+    for _ in range(iters):
+        fn()
+    e.record()
+    e.synchronize()
+    return s.elapsed_time(e) / iters
+
+
+# ----------------------------------------------------------------------------- workloads
+
+def pack_sweep(torch, w4, wl, blocks):
+    """Packed asymmetric weights of every linear of the sweep, in block order."""
+    packed = []
+    for b in range(blocks):
+        for layer, (_, K, N) in enumerate(wl.BLOCK_LINEARS):
+            W = to_dev_bf16(torch, wl.decode_weight(b, layer))
+            qw, sc, qz = w4.awq_quantize_pack(W)
+            del W
+            packed.append((b, layer, K, N, qw, sc, qz))
+    torch.cuda.synchronize()
+    return packed
+
+
+def sweep_launches(torch, w4, wl, packed, M):
+    launches = []
+    for b, layer, K, N, qw, sc, qz in packed:
+        X = to_dev_bf16(torch, wl.decode_act(b, layer, M))
+        Y = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+        launches.append(Launch(w4.gemv_launcher(X, qw, sc, qz, False, Y), gemv_bytes(M, K, N, False),
+                               2 * M * K * N))
+    torch.cuda.synchronize()
+    return launches
+
+
+def capture_graph(torch, launches):
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        for l in launches:          # warm the launch path outside capture
+            l()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        for l in launches:
+            l()
+    torch.cuda.synchronize()
+    return g
+
+
+def rotation_launches(torch, w4, X, qw, sc, qz, sym, min_bytes, make, M, K, N, flops_fn):
+    """Copies of one packed weight whose total exceeds min_bytes: launch i uses copy i."""
+    per = packed_bytes(N, K, sym)
+    copies = max(1, -(-min_bytes // per))
+    launches = []
+    for _ in range(copies):
+        q2, s2 = qw.clone(), sc.clone()
+        z2 = None if qz is None else qz.clone()
+        Y = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+        launches.append(Launch(make(X, q2, s2, z2, sym, Y), gemv_bytes(M, K, N, sym), flops_fn(M, K, N)))
+    return launches
+
+
+def measure_rotation(torch, launches, reps):
+    """Cold-cache average ms per launch: each rep runs every copy once in order."""
+    for l in launches:
+        l()
+    torch.cuda.synchronize()
+    ms = time_events(torch, lambda: [l() for l in launches], reps) / len(launches)
+    return ms
+
+
+# ----------------------------------------------------------------------------- rows
+
+def row_gemv(name, nbytes, ms, extra=None):
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    d = {"name": name, "bytes": int(nbytes), "us": round(ms * 1e3, 3), "GB/s": round(gbs, 1),
+         "bound": "hbm", "frac": round(gbs / HBM_PEAK_GBS, 4)}
+    if extra:
+        d.update(extra)
+    return d
+
+
+def row_gemm(name, flops, ms, extra=None):
+    tf = flops / (ms * 1e-3) / 1e12
+    d = {"name": name, "flops": int(flops), "us": round(ms * 1e3, 3), "TFLOP/s": round(tf, 1),
+         "bound": "mfma", "frac": round(tf / BF16_PEAK_TFLOPS, 4)}
+    if extra:
+        d.update(extra)
+    return d
+
+
+def rows_large(torch, w4, wl, reps):
+    rows = []
+    # 27B-shaped symmetric linears: cold-cache GEMV at M = 1, 8 and GEMM at M = 64, 512
+    for si, (K, N) in enumerate(wl.LARGE_SHAPES):
+        W = to_dev_bf16(torch, wl.large_weight(si))
+        # quantize + pack (HBM-bound read of bf16 W and write of the packed form)
+        qw, sc, _ = w4.awq_quantize_pack(W, symmetric=True)
+        ms = time_events(torch, lambda: w4.awq_quantize_pack(W, symmetric=True, qweight=qw, scales=sc), reps)
+        qbytes = N * K * 2 + packed_bytes(N, K, True)
+        rows.append(row_gemv(f"quantize_pack sym K={K} N={N}", qbytes, ms))
+        del W
+        for M in (1, 8):
+            X = to_dev_bf16(torch, wl.large_act(si, M))
+            ls = rotation_launches(torch, w4, X, qw, sc, None, True, 600 << 20, w4.gemv_launcher, M, K, N,
+                                   lambda m, k, n: 2 * m * k * n)
+            ms = measure_rotation(torch, ls, max(2, reps // 4))
+            rows.append(row_gemv(f"gemv cold M={M} K={K} N={N} sym", ls[0].nbytes, ms,
+                                 {"cache": f"cold ({len(ls)} rotating copies)"}))
+            del ls
+        for M in (64, 512):
+            X = to_dev_bf16(torch, wl.large_act(si, M))
+            Y = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+            ms = time_events(torch, w4.gemm_launcher(X, qw, sc, None, True, Y), reps)
+            rows.append(row_gemm(f"gemm M={M} K={K} N={N} sym", 2 * M * K * N, ms,
+                                 {"GB/s": round(gemv_bytes(M, K, N, True) / (ms * 1e-3) / 1e9, 1)}))
+        torch.cuda.synchronize()
+        del qw, sc
+    return rows
+
+
+def rows_prefill(torch, w4, wl, reps):
+    rows = []
+    # prefill GEMM, M = 2048, outlier channels
+    for si, (K, N) in enumerate(wl.PREFILL_SHAPES):
+        Xn, Wn = wl.prefill(si)
+        X, W = to_dev_bf16(torch, Xn), to_dev_bf16(torch, Wn)
+        qw, sc, qz = w4.awq_quantize_pack(W)
+        Y = torch.empty((wl.PREFILL_M, N), dtype=torch.bfloat16, device="cuda")
+        ms = time_events(torch, w4.gemm_launcher(X, qw, sc, qz, False, Y), reps)
+        rows.append(row_gemm(f"gemm prefill M=2048 K={K} N={N}", 2 * wl.PREFILL_M * K * N, ms))
+    return rows
+
+
+def rows_gemv2048(torch, w4, wl, reps):
+    rows = []
+    # single GEMV, M = 1, K = N = 2048: warm (cache-resident) and cold (rotation)
+    Xn, Wn = wl.gemv_2048()
+    X, W = to_dev_bf16(torch, Xn), to_dev_bf16(torch, Wn)
+    qw, sc, qz = w4.awq_quantize_pack(W)
+    Y = torch.empty((1, 2048), dtype=torch.bfloat16, device="cuda")
+    ms = time_events(torch, w4.gemv_launcher(X, qw, sc, qz, False, Y), reps * 10)
+    rows.append(row_gemv("gemv M=1 K=2048 N=2048 (cache-resident)", gemv_bytes(1, 2048, 2048, False), ms))
+    ls = rotation_launches(torch, w4, X, qw, sc, qz, False, 600 << 20, w4.gemv_launcher, 1, 2048, 2048,
+                           lambda m, k, n: 2 * m * k * n)
+    ms = measure_rotation(torch, ls, 3)
+    rows.append(row_gemv("gemv M=1 K=2048 N=2048 (cold)", gemv_bytes(1, 2048, 2048, False), ms,
+                         {"cache": f"cold ({len(ls)} rotating copies)"}))
+    del ls
+    return rows
+
+
+def rows_search(torch, w4, wl, reps):
+    rows = []
+    # full AWQ search: 20 alphas then 10 ratios, T=4096, K=2048, N=6144
+    Xn, Wn = wl.awq_calibration()
+    X, W = to_dev_bf16(torch, Xn), to_dev_bf16(torch, Wn)
+    alphas = [i / 20 for i in range(20)]
+    ratios = [1 - j / 20 for j in range(10)]
+    res = w4.awq_search(X, W, alphas, ratios)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    n = 2
+    for _ in range(n):
+        res = w4.awq_search(X, W, alphas, ratios)
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / n
+    flops = 31 * 2 * wl.AWQ_T * wl.AWQ_K * wl.AWQ_N
+    rows.append(row_gemm("awq_search T=4096 K=2048 N=6144 (20 alpha + 10 ratio + ref)", flops, ms,
+                         {"alpha_index": res["alpha_index"], "ratio_index": res["ratio_index"]}))
+    return rows
+
+
+# ----------------------------------------------------------------------------- CPU baseline
+
+def cpu_baseline(wl, budget_s=12.0):
+    """The oracle (dequantize + fp64 linear) over the sweep's linears in block order,
+    until budget_s of CPU time is spent; TB/s of algorithmic bytes."""
+    from oracle import w4a16_oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = 1
+    done_bytes, spent, n = 0, 0.0, 0
+    cache = {}
+    while spent < budget_s:
+        for b in range(2):
+            for layer, (_, K, N) in enumerate(wl.BLOCK_LINEARS):
+                if (b, layer) not in cache:
+                    W = wl.decode_weight(b, layer)
+                    cache[(b, layer)] = (wl.decode_act(b, layer, 1), O.quantize_pack(W))
+                X, (qw, sc, qz) = cache[(b, layer)]
+                t0 = time.perf_counter()
+                O.linear(X, O.dequantize(qw, sc, qz, K, False))
+                spent += time.perf_counter() - t0
+                done_bytes += gemv_bytes(1, K, N, False)
+                n += 1
+    return {"value": round(done_bytes / spent / 1e12, 6), "unit": "TB/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{n} GEMVs over the 14 linears of the first 2 blocks of the decode sweep (M=1), repeated: "
+                      f"oracle dequantize + fp64 linear, {spent:.1f} s of CPU time"}
+
+
+# ----------------------------------------------------------------------------- main
+
+def main(argv=None):
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
+    ap.add_argument("--step-only", action="store_true", help="measure only the decode-sweep step")
+    ap.add_argument("--only", default="", help="comma list of extra rows to measure "
+                    "(sweeps,large,prefill,gemv2048,search); default all")
+    ap.add_argument("--blocks", type=int, default=28)
+    ap.add_argument("--skip-step", action="store_true",
+                    help="profiling aid: skip the decode-sweep step (value is null) and run only --only rows")
+    args = ap.parse_args(argv)
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (the kernels shard by output rows "
+              "with no exchange; see the sharding notes). Run with --gpus 1.", file=sys.stderr)
+        return 2
+
+    import torch
+
+    import weight_only_int4_amd as w4
+    import workloads as wl
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 2
+    torch.cuda.set_device(0)
+    w4.load_library()
+
+    out = {
+        "metric": "W4A16 g128 GEMV achieved TB/s (M=1) + GEMM TFLOP/s (M=2048), % roofline",
+        "value": None,
+        "unit": "TB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": None,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16 x int4 (fp32 accumulate)",
+        "data": "synthetic (seeded; W ~ N(0,0.02) bf16, X ~ N(0,1) bf16)",
+        "config": {"workload": f"decode sweep: {args.blocks} blocks x 7 linears of a hidden-2048 decoder block "
+                               f"(q,k,v,o,gate,up,down), M=1, asymmetric int4 g128, HIP-graph replay"},
+    }
+    packed = []
+    if not args.skip_step:
+        log("packing decode-sweep weights")
+        packed = pack_sweep(torch, w4, wl, args.blocks)
+        sweep = sweep_launches(torch, w4, wl, packed, 1)
+        step_bytes = sum(l.nbytes for l in sweep)
+        graph = capture_graph(torch, sweep)
+
+        for _ in range(args.warmup):
+            graph.replay()
+        torch.cuda.synchronize()
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s.record()
+        for _ in range(args.steps):
+            graph.replay()
+        e.record()
+        torch.cuda.synchronize()
+        ms_step = s.elapsed_time(e) / args.steps
+        value = step_bytes / (ms_step * 1e-3) / 1e12
+        log(f"sweep: {ms_step * 1e3:.1f} us/step, {value:.3f} TB/s")
+
+        # dominant kernel: the step is a graph of GEMV launches only, so its event-timed
+        # duration over the timed region divided by the launches is the average launch
+        # duration on the launch stream (back-to-back, inter-kernel gaps included)
+        avg_launch_ms = ms_step / len(sweep)
+        avg_bytes = step_bytes / len(sweep)
+        achieved = avg_bytes / (avg_launch_ms * 1e-3) / 1e9
+        eager_ms = time_events(torch, lambda: [l() for l in sweep], max(2, args.steps // 4))
+        out["value"] = round(value, 4)
+        out["ms_per_step"] = round(ms_step, 5)
+        out["config"].update({"bytes_per_step": int(step_bytes), "launches_per_step": len(sweep),
+                              "eager_ms_per_step": round(eager_ms, 5)})
+        out["roofline"] = {"kernel": "gemv_kernel<M=1>", "bound": "hbm", "achieved": round(achieved, 1),
+                           "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                           "traffic": None, "avg_launch_us": round(avg_launch_ms * 1e3, 3),
+                           "bytes_per_launch": int(avg_bytes)}
+        del graph, sweep
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+
+    want = set(x for x in args.only.split(",") if x) or {"sweeps", "large", "prefill", "gemv2048", "search"}
+    if not args.step_only:
+        rows = []
+        for M in ((4, 16) if "sweeps" in want and packed else ()):
+            log(f"decode sweep M={M}")
+            sw = sweep_launches(torch, w4, wl, packed, M)
+            g = capture_graph(torch, sw)
+            ms = time_events(torch, g.replay, max(3, args.steps // 2))
+            rows.append(row_gemv(f"decode sweep M={M} (graph)", sum(l.nbytes for l in sw), ms))
+            del g, sw
+            torch.cuda.empty_cache()
+        del packed
+        torch.cuda.empty_cache()
+        reps = max(5, args.steps)
+        for name, fn in (("large", rows_large), ("prefill", rows_prefill), ("gemv2048", rows_gemv2048),
+                         ("search", rows_search)):
+            if name in want:
+                log(f"rows: {name}")
+                rows += fn(torch, w4, wl, reps)
+        out["rows"] = rows
+        pre = [r for r in rows if r["name"].startswith("gemm prefill")]
+        if pre:
+            out["prefill_gemm_tflops"] = [r["TFLOP/s"] for r in pre]
+            out["prefill_gemm_frac"] = [r["frac"] for r in pre]
+    if not args.no_cpu:
+        log("cpu baseline (oracle)")
+        out["cpu_baseline"] = cpu_baseline(wl)
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -175,6 +175,24 @@ int awq_search(const uint16_t* X, int T, int K, int N, const uint16_t* W,
                int* ratio_index, float* s_out, void* workspace, size_t* workspace_bytes,
                void* stream);
 
+/*
+ * Measurement helpers (not part of the method): the yardsticks the kernels
+ * above are measured against on the same device.
+ *
+ * w4_probe_stream_read -- read `bytes` (multiple of 16, 16-byte aligned) from
+ *   device buffer `buf` with a grid-stride loop of `blocks` x 256 threads, each
+ *   thread loading `unroll` (1, 2, 4 or 8) 16-byte chunks per iteration
+ *   (non-temporal loads if `nontemporal`), and write one uint32 XOR per thread
+ *   to `sink` (blocks * 256 uint32, device).  Its duration gives the bandwidth a
+ *   plain read reaches at that size, and its known traffic scales the hardware
+ *   fetch counters.
+ * w4_probe_empty -- launch a kernel that does nothing (one 64-thread block):
+ *   the launch-duration floor.
+ */
+int w4_probe_stream_read(const void* buf, size_t bytes, int unroll, int nontemporal, int blocks,
+                         uint32_t* sink, void* stream);
+int w4_probe_empty(void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -90,13 +90,16 @@ def test_gemm_size_query(lib):
     sz = ctypes.c_size_t(0)
     f = lib.w4a16_gemm
     assert f(None, 2048, 2048, 6144, None, None, None, 0, 128, None, None, ctypes.byref(sz), None) == 0
-    assert sz.value == 16 * 2048 * 4            # group row sums, fp32 [K/128][M rounded to 128]
+    # pair-arranged X [M][K] bf16, zero-point operands bf16 [M rounded to 128][16 ceil(G/3)]
+    # and [N][16 ceil(G/3)], each rounded up to 256 bytes
+    assert sz.value == 2048 * 2048 * 2 + 2048 * 96 * 2 + 6144 * 96 * 2
     assert f(None, 200, 384, 8, None, None, None, 0, 128, None, None, ctypes.byref(sz), None) == 0
-    assert sz.value == 3 * 256 * 4
+    need = 200 * 384 * 2 + 256 * 16 * 2 + 256
+    assert sz.value == need
     assert f(A, 200, 384, 8, A, A, A, 0, 128, A, None, None, None) == -5
-    small = ctypes.c_size_t(3 * 256 * 4 - 1)
+    small = ctypes.c_size_t(need - 1)
     assert f(A, 200, 384, 8, A, A, A, 0, 128, A, A, ctypes.byref(small), None) == -5
-    ok = ctypes.c_size_t(3 * 256 * 4)
+    ok = ctypes.c_size_t(need)
     assert f(A, 200, 384, 8, A, A, A, 0, 128, MIS, A, ctypes.byref(ok), None) == -3
 
 

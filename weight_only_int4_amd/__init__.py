@@ -19,7 +19,8 @@ import torch
 
 __all__ = [
     "W4Error", "library_path", "load_library", "awq_quantize_pack", "w4a16_gemv", "w4a16_gemm",
-    "awq_grid_loss", "awq_search", "GROUP_SIZE", "GEMV_MAX_M",
+    "awq_grid_loss", "awq_search", "GROUP_SIZE", "GEMV_MAX_M", "gemv_launcher", "gemm_launcher",
+    "probe_stream_read", "probe_empty",
 ]
 
 GROUP_SIZE = 128
@@ -34,6 +35,8 @@ _SIGNATURES = {
     "w4a16_gemv": ([_vp, _i, _i, _i, _vp, _vp, _vp, _i, _i, _vp, _vp, _sz, _vp], _i),
     "w4a16_gemm": ([_vp, _i, _i, _i, _vp, _vp, _vp, _i, _i, _vp, _vp, _sz, _vp], _i),
     "awq_grid_loss": ([_vp, _i, _i, _i, _vp, _vp, _vp, _vp, _i, _i, _i, _vp, _vp, _sz, _vp], _i),
+    "w4_probe_stream_read": ([_vp, ctypes.c_size_t, _i, _i, _i, _vp, _vp], _i),
+    "w4_probe_empty": ([_vp], _i),
     "awq_search": ([_vp, _i, _i, _i, _vp, ctypes.POINTER(ctypes.c_double), _i,
                     ctypes.POINTER(ctypes.c_double), _i, _i, _i, ctypes.POINTER(ctypes.c_float),
                     ctypes.POINTER(ctypes.c_int), ctypes.POINTER(ctypes.c_int), _vp, _vp, _sz, _vp], _i),
@@ -234,3 +237,60 @@ def awq_search(X, W, alphas, ratios, symmetric: bool = False, workspace=None):
     vals = list(out)
     return dict(alpha_losses=vals[: len(alphas)], ratio_losses=vals[len(alphas):], alpha_index=ia.value,
                 ratio_index=ir.value, s=s_out)
+
+
+def _launcher(cname, X, qweight, scales, qzeros, symmetric, Y, workspace):
+    lib = load_library()
+    M, K, N = _packed_shapes(X, qweight, scales, qzeros, symmetric)
+    _need(Y, torch.bfloat16, "Y", 2)
+    if tuple(Y.shape) != (M, N):
+        raise ValueError("Y must be [M][N]")
+    fn = getattr(lib, cname)
+    qz = None if symmetric else qzeros
+
+    def q(sz):
+        return fn(None, M, K, N, None, None, None, int(symmetric), GROUP_SIZE, None, None, sz, None)
+
+    ws, wsb = _workspace(q, X.device, workspace)
+    keep = (X, qweight, scales, qz, Y, ws)          # tensors stay alive while the launcher does
+    args = (_ptr(X), M, K, N, _ptr(qweight), _ptr(scales), _ptr(qz), int(symmetric), GROUP_SIZE, _ptr(Y),
+            _ptr(ws), None if wsb is None else ctypes.byref(wsb))
+    dev = X.device
+
+    def launch():
+        _check(fn(*args, _stream(dev)))
+
+    launch.tensors = keep
+    launch.workspace_size = wsb
+    return launch
+
+
+def gemv_launcher(X, qweight, scales, qzeros, symmetric: bool, Y, workspace=None):
+    """Validate once and return a zero-argument callable that enqueues the GEMV
+    Y = X W_hat^T on the current stream (for graph capture and timing loops)."""
+    return _launcher("w4a16_gemv", X, qweight, scales, qzeros, symmetric, Y, workspace)
+
+
+def gemm_launcher(X, qweight, scales, qzeros, symmetric: bool, Y, workspace=None):
+    """As gemv_launcher, for the MFMA GEMM."""
+    return _launcher("w4a16_gemm", X, qweight, scales, qzeros, symmetric, Y, workspace)
+
+
+def probe_stream_read(buf, unroll: int = 4, nontemporal: bool = False, blocks: int = 0, sink=None):
+    """Measurement helper: enqueue a plain streaming read of the whole tensor `buf`."""
+    lib = load_library()
+    if not buf.is_cuda or not buf.is_contiguous():
+        raise ValueError("buf must be a contiguous GPU tensor")
+    nbytes = buf.numel() * buf.element_size()
+    if blocks <= 0:
+        blocks = 256 * 8
+    if sink is None or sink.numel() < blocks * 256:
+        sink = torch.empty(blocks * 256, dtype=torch.int32, device=buf.device)
+    _check(lib.w4_probe_stream_read(_ptr(buf), nbytes, int(unroll), int(nontemporal), int(blocks), _ptr(sink),
+                                    _stream(buf.device)))
+    return sink
+
+
+def probe_empty(device="cuda"):
+    """Measurement helper: enqueue an empty kernel."""
+    _check(load_library().w4_probe_empty(_stream(torch.device(device))))

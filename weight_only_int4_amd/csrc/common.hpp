@@ -35,13 +35,26 @@ __device__ __forceinline__ uint32_t nibble_pair(uint32_t w, int p) {
   return ((w >> (4 * p)) & 0x000F000Fu) | 0x43004300u;
 }
 
+// Same, with the mask held in a register (see opaque_vgpr) so that the AND and
+// the OR fuse into one v_and_or_b32 (VOP3 cannot encode two literal constants).
+__device__ __forceinline__ uint32_t nibble_pair_m(uint32_t w, int p, uint32_t mask_vgpr) {
+  return ((w >> (4 * p)) & mask_vgpr) | 0x43004300u;
+}
+
+// A constant the compiler must keep in a VGPR instead of folding it into literals.
+__device__ __forceinline__ uint32_t opaque_vgpr(uint32_t v) {
+  asm volatile("" : "+v"(v));
+  return v;
+}
+
 // Reorder 8 consecutive bf16 activations (x0..x7 in 4 dwords) into the pairs
 // (x0,x4) (x1,x5) (x2,x6) (x3,x7) that match nibble_pair's element order.
 __device__ __forceinline__ void pair_activations(const uint32_t d[4], uint32_t e[4]) {
-  e[0] = (d[0] & 0xFFFFu) | (d[2] << 16);
-  e[1] = (d[0] >> 16) | (d[2] & 0xFFFF0000u);
-  e[2] = (d[1] & 0xFFFFu) | (d[3] << 16);
-  e[3] = (d[1] >> 16) | (d[3] & 0xFFFF0000u);
+  // v_perm_b32(hi, lo, sel): selector bytes 0-3 pick bytes of lo, 4-7 bytes of hi
+  e[0] = __builtin_amdgcn_perm(d[2], d[0], 0x05040100u);   // (lo16 d0, lo16 d2)
+  e[1] = __builtin_amdgcn_perm(d[2], d[0], 0x07060302u);   // (hi16 d0, hi16 d2)
+  e[2] = __builtin_amdgcn_perm(d[3], d[1], 0x05040100u);
+  e[3] = __builtin_amdgcn_perm(d[3], d[1], 0x07060302u);
 }
 
 __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {

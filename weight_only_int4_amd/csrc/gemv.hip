@@ -28,7 +28,6 @@ struct GemvArgs {
   uint16_t* Y;
   float* partial;       // [splits][M][N] when splits > 1
   int wps;              // packed words per split (multiple of WPL)
-  int rows_per_block;
 };
 
 // Butterfly reduction of V values per lane across the 64 lanes of a wave.
@@ -79,12 +78,41 @@ struct WordVec<1> {
   __device__ static __forceinline__ void load(const uint32_t* p, uint32_t* w) { w[0] = *p; }
 };
 
-template <int M, int WPL, int RB>
-__global__ __launch_bounds__(1024) void gemv_kernel(GemvArgs a) {
-  constexpr int V = RB * M;
+// A workgroup owns one K split and walks row batches b = blockIdx.x,
+// blockIdx.x + gridDim.x, ... (R rows each); the grid is sized to the number of
+// workgroups the device holds at once.  The lane's activations are loaded once.
+// The packed words, scales and zero words of the next batch are loaded (from
+// clamped, always-valid addresses, without branches around the loads) before
+// the current batch is computed, so every wave keeps a batch of loads in flight
+// while it computes and reduces.  Rows past N are computed on clamped data and
+// never stored; lanes past the end of K carry zero activations.
+template <int M, int WPL, int R>
+struct GemvBatch {
+  uint32_t w[R][WPL];
+  uint32_t scb[R], zw[R];
+};
+
+template <int M, int WPL, int R>
+__device__ __forceinline__ void gemv_load_batch(const GemvArgs& a, int b, int wb, int g, int words, int G, int GW,
+                                                GemvBatch<M, WPL, R>& B) {
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const int n = min(b * R + r, a.N - 1);
+    WordVec<WPL>::load(a.qweight + (size_t)n * words + wb, B.w[r]);
+    B.scb[r] = a.scales[(size_t)n * G + g];
+    B.zw[r] = a.symmetric ? 0u : a.qzeros[(size_t)n * GW + (g >> 3)];
+  }
+}
+
+// Up to 16 waves per workgroup for M <= 2 (128 VGPRs per lane), 8 above (256).
+constexpr int gemv_max_waves(int M) { return M <= 2 ? 16 : 8; }
+
+template <int M, int WPL, int R>
+__global__ __launch_bounds__(gemv_max_waves(M) * 64) void gemv_kernel(GemvArgs a) {
+  constexpr int V = R * M;
   constexpr int VP = pow2_ceil(V);
   constexpr int SPREAD = kWave / VP;          // lanes per reduced value
-  __shared__ float red[16][VP];
+  __shared__ float red[2][16][VP];
 
   const int t = threadIdx.x;
   const int lane = t & (kWave - 1);
@@ -93,9 +121,15 @@ __global__ __launch_bounds__(1024) void gemv_kernel(GemvArgs a) {
   const int words = a.K >> 3;
   const int G = a.K >> 7;
   const int GW = (G + 7) >> 3;
-  const int wb = blockIdx.y * a.wps + t * WPL;
-  const bool active = (t * WPL < a.wps) && (wb < words);
+  const int wb_raw = blockIdx.y * a.wps + t * WPL;
+  const bool active = (t * WPL < a.wps) && (wb_raw < words);
+  const int wb = active ? wb_raw : 0;
   const int g = wb >> 4;
+  const int nb = (a.N + R - 1) / R;
+  int b = blockIdx.x;
+
+  GemvBatch<M, WPL, R> B0, B1;
+  gemv_load_batch(a, b, wb, g, words, G, GW, B0);
 
   // this lane's activations as (x_j, x_j+4) bf16 pairs, and their fp32 sums
   uint32_t xp[M][WPL][4];
@@ -105,11 +139,10 @@ __global__ __launch_bounds__(1024) void gemv_kernel(GemvArgs a) {
     xs[m] = 0.0f;
 #pragma unroll
     for (int i = 0; i < WPL; ++i) {
-      uint32_t d[4] = {0u, 0u, 0u, 0u};
-      if (active) {
-        const uint4 v = *reinterpret_cast<const uint4*>(a.X + (size_t)m * a.K + (size_t)(wb + i) * 8);
-        d[0] = v.x; d[1] = v.y; d[2] = v.z; d[3] = v.w;
-      }
+      const uint4 v = *reinterpret_cast<const uint4*>(a.X + (size_t)m * a.K + (size_t)(wb + i) * 8);
+      uint32_t d[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int q = 0; q < 4; ++q) d[q] = active ? d[q] : 0u;
       pair_activations(d, xp[m][i]);
 #pragma unroll
       for (int q = 0; q < 4; ++q)
@@ -117,38 +150,20 @@ __global__ __launch_bounds__(1024) void gemv_kernel(GemvArgs a) {
     }
   }
 
-  const int row_begin = blockIdx.x * a.rows_per_block;
-  const int row_end = min(row_begin + a.rows_per_block, a.N);
-  const uint32_t zfix = a.symmetric ? 136u : 128u;
-
-  for (int r0 = row_begin; r0 < row_end; r0 += RB) {
-    uint32_t w[RB][WPL];
-    float sc[RB], zc[RB];
-#pragma unroll
-    for (int rb = 0; rb < RB; ++rb) {
-      const int n = r0 + rb;
-#pragma unroll
-      for (int i = 0; i < WPL; ++i) w[rb][i] = 0u;
-      sc[rb] = 0.0f;
-      zc[rb] = 0.0f;
-      if (active && n < row_end) {
-        WordVec<WPL>::load(a.qweight + (size_t)n * words + wb, w[rb]);
-        sc[rb] = bf16_bits_to_f32(a.scales[(size_t)n * G + g]);
-        uint32_t z = zfix;
-        if (!a.symmetric) z = 128u + ((a.qzeros[(size_t)n * GW + (g >> 3)] >> (4 * (g & 7))) & 0xFu);
-        zc[rb] = (float)z;
-      }
-    }
+  // compute batch `bb` from registers `B`, reduce and store; `par` selects the LDS buffer
+  auto process = [&](const GemvBatch<M, WPL, R>& Bc, int bb, int par) {
     float part[VP];
 #pragma unroll
     for (int v = V; v < VP; ++v) part[v] = 0.0f;
 #pragma unroll
-    for (int rb = 0; rb < RB; ++rb) {
+    for (int r = 0; r < R; ++r) {
+      const float sc = bf16_bits_to_f32(Bc.scb[r]);
+      const float zc = a.symmetric ? 136.0f : (float)(128u + ((Bc.zw[r] >> (4 * (g & 7))) & 0xFu));
       uint32_t bp[WPL][4];
 #pragma unroll
       for (int i = 0; i < WPL; ++i)
 #pragma unroll
-        for (int p = 0; p < 4; ++p) bp[i][p] = nibble_pair(w[rb][i], p);
+        for (int p = 0; p < 4; ++p) bp[i][p] = nibble_pair(Bc.w[r][i], p);
 #pragma unroll
       for (int m = 0; m < M; ++m) {
         float acc = 0.0f;
@@ -156,38 +171,48 @@ __global__ __launch_bounds__(1024) void gemv_kernel(GemvArgs a) {
         for (int i = 0; i < WPL; ++i)
 #pragma unroll
           for (int p = 0; p < 4; ++p) acc = dot2_bf16(xp[m][i][p], bp[i][p], acc);
-        part[rb * M + m] = sc[rb] * (acc - zc[rb] * xs[m]);
+        part[r * M + m] = sc * (acc - zc * xs[m]);
       }
     }
     WaveReduce<VP, 32>::run(part, lane);
     const int idx = lane / SPREAD;
     const bool writer = (lane % SPREAD) == 0 && idx < V;
-    const int rb = idx / M, m = idx % M;
-    const int n = r0 + rb;
+    const int n0 = bb * R;
     if (nw == 1) {
-      if (writer && n < row_end) {
+      const int n = n0 + idx / M, m = idx % M;
+      if (writer && n < a.N) {
         if (a.partial)
           a.partial[((size_t)blockIdx.y * M + m) * a.N + n] = part[0];
         else
           a.Y[(size_t)m * a.N + n] = (uint16_t)f32_to_bf16_bits(part[0]);
       }
     } else {
-      if (writer) red[wave][idx] = part[0];
+      // two LDS buffers alternate between batches, so one barrier per batch suffices
+      if (writer) red[par][wave][idx] = part[0];
       __syncthreads();
       if (t < V) {
-        const int rbt = t / M, mt = t % M;
-        const int nt = r0 + rbt;
+        const int n = n0 + t / M, m = t % M;
         float sum = 0.0f;
-        for (int ww = 0; ww < nw; ++ww) sum += red[ww][t];
-        if (nt < row_end) {
+        for (int ww = 0; ww < nw; ++ww) sum += red[par][ww][t];
+        if (n < a.N) {
           if (a.partial)
-            a.partial[((size_t)blockIdx.y * M + mt) * a.N + nt] = sum;
+            a.partial[((size_t)blockIdx.y * M + m) * a.N + n] = sum;
           else
-            a.Y[(size_t)mt * a.N + nt] = (uint16_t)f32_to_bf16_bits(sum);
+            a.Y[(size_t)m * a.N + n] = (uint16_t)f32_to_bf16_bits(sum);
         }
       }
-      __syncthreads();
     }
+  };
+
+  const int step = gridDim.x;
+  while (b < nb) {
+    if (b + step < nb) gemv_load_batch(a, b + step, wb, g, words, G, GW, B1);
+    process(B0, b, 0);
+    b += step;
+    if (b >= nb) break;
+    if (b + step < nb) gemv_load_batch(a, b + step, wb, g, words, G, GW, B0);
+    process(B1, b, 1);
+    b += step;
   }
 }
 
@@ -204,34 +229,64 @@ __global__ __launch_bounds__(256) void gemv_split_reduce(const float* partial, i
 namespace {
 
 struct GemvPlan {
-  int wpl, rb, nw, splits, wps, rows_per_block;
+  int wpl, nw, splits, wps;
 };
 
-constexpr int kTargetWaves = 256 * 16;   // 256 CUs x 16 resident waves at <= 128 VGPRs
+// words per lane and rows per workgroup for M activation rows
+constexpr int gemv_wpl(int M) { return M <= 4 ? 4 : (M <= 8 ? 2 : 1); }
+constexpr int gemv_rows(int M) { return M == 1 ? 4 : (M <= 8 ? 2 : 1); }
 
 GemvPlan plan_gemv(int M, int K, int N) {
+  (void)N;
   GemvPlan p;
-  p.wpl = M <= 4 ? 4 : (M <= 8 ? 2 : 1);
-  p.rb = M <= 2 ? 4 : 2;
+  p.wpl = gemv_wpl(M);
   const int words = K / 8;
-  const int max_wps = 16 * kWave * p.wpl;
+  const int max_wps = gemv_max_waves(M) * kWave * p.wpl;
   p.splits = (words + max_wps - 1) / max_wps;
   int wps = (words + p.splits - 1) / p.splits;
   p.wps = (wps + p.wpl - 1) / p.wpl * p.wpl;
   p.nw = (p.wps / p.wpl + kWave - 1) / kWave;
-  long long r = ((long long)N * p.splits * p.nw + kTargetWaves - 1) / kTargetWaves;
-  if (r < p.rb) r = p.rb;
-  r = (r + p.rb - 1) / p.rb * p.rb;
-  p.rows_per_block = (int)r;
   return p;
+}
+
+// Resident workgroups per CU of one gemv instantiation at a block size (cached).
+template <int M>
+int gemv_blocks_per_cu(int threads) {
+  static int cache[17] = {0};
+  const int slot = threads / kWave;
+  if (cache[slot] == 0) {
+    int nblk = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nblk, gemv_kernel<M, gemv_wpl(M), gemv_rows(M)>, threads,
+                                                     0) != hipSuccess ||
+        nblk < 1)
+      nblk = 1;
+    cache[slot] = nblk;
+  }
+  return cache[slot];
+}
+
+int device_cus() {
+  static int cus[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cus[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 1) n = 256;
+    cus[dev] = n;
+  }
+  return cus[dev];
 }
 
 template <int M>
 void launch_m(const GemvArgs& a, const GemvPlan& p, hipStream_t stream) {
-  constexpr int WPL = M <= 4 ? 4 : (M <= 8 ? 2 : 1);
-  constexpr int RB = M <= 2 ? 4 : 2;
-  dim3 grid((unsigned)((a.N + p.rows_per_block - 1) / p.rows_per_block), (unsigned)p.splits);
-  hipLaunchKernelGGL((gemv_kernel<M, WPL, RB>), grid, dim3(p.nw * kWave), 0, stream, a);
+  constexpr int WPL = gemv_wpl(M);
+  constexpr int R = gemv_rows(M);
+  const int threads = p.nw * kWave;
+  const long long nb = (a.N + R - 1) / R;
+  const long long resident = (long long)device_cus() * gemv_blocks_per_cu<M>(threads);
+  const long long per_split = (resident + p.splits - 1) / p.splits;
+  const unsigned gx = (unsigned)(nb < per_split ? nb : per_split);
+  hipLaunchKernelGGL((gemv_kernel<M, WPL, R>), dim3(gx, (unsigned)p.splits), dim3(threads), 0, stream, a);
 }
 
 }  // namespace
@@ -248,7 +303,7 @@ int launch_gemv(const uint16_t* X, int M, int K, int N, const uint32_t* qweight,
   if (M == 0 || N == 0) return W4_OK;
   const GemvPlan p = plan_gemv(M, K, N);
   GemvArgs a{X, K, N, qweight, scales, qzeros, symmetric, Y,
-             p.splits > 1 ? static_cast<float*>(workspace) : nullptr, p.wps, p.rows_per_block};
+             p.splits > 1 ? static_cast<float*>(workspace) : nullptr, p.wps};
   switch (M) {
     case 1: launch_m<1>(a, p, stream); break;
     case 2: launch_m<2>(a, p, stream); break;

@@ -21,8 +21,8 @@ namespace w4 {
 namespace {
 
 struct LossLayout {
-  size_t yref, qw, sc, qz, xs, rs, part, total;
-  int mpad, G, GW, tiles;
+  size_t yref, qw, sc, qz, xs, rsx, cz, part, total;
+  int mpad, G, GW, kz, tiles;
 };
 
 LossLayout loss_layout(int T, int K, int N, int C, bool need_yref) {
@@ -30,6 +30,7 @@ LossLayout loss_layout(int T, int K, int N, int C, bool need_yref) {
   L.G = K / kGroup;
   L.GW = (L.G + 7) / 8;
   L.mpad = (int)align_up((size_t)T, kBM);
+  L.kz = zterm_kz(K);
   L.tiles = ((N + kBN - 1) / kBN) * ((T + kBM - 1) / kBM);
   size_t off = 0;
   auto take = [&](size_t bytes) {
@@ -42,14 +43,16 @@ LossLayout loss_layout(int T, int K, int N, int C, bool need_yref) {
   L.sc = take((size_t)C * N * L.G * 2);
   L.qz = take((size_t)C * N * L.GW * 4);
   L.xs = take((size_t)C * T * K * 2);
-  L.rs = take((size_t)C * L.G * L.mpad * 4);
+  L.rsx = take((size_t)C * L.mpad * L.kz * 2);
+  L.cz = take((size_t)C * N * L.kz * 2);
   L.part = take((size_t)C * L.tiles * 4);
   L.total = off;
   return L;
 }
 
-// Xs[c][t][k] = bf16(X[t][k] / S[c][k]) (IEEE division, round to nearest even).
-// Each thread handles 8 consecutive channels of one row.
+// Xs[c][t][k] = bf16(X[t][k] / S[c][k]) (IEEE division, round to nearest even),
+// stored pair-arranged for the int4 MFMA path: each 8-channel run as
+// (x0,x4)(x1,x5)(x2,x6)(x3,x7).  Each thread handles 8 consecutive channels of one row.
 __global__ __launch_bounds__(256) void scale_activations_kernel(const uint16_t* X, int T, int K,
                                                                 const float* S, uint16_t* Xs) {
   const int c = blockIdx.z;
@@ -70,7 +73,9 @@ __global__ __launch_bounds__(256) void scale_activations_kernel(const uint16_t* 
     const float hi = __uint_as_float(d[q] & 0xFFFF0000u) / s[2 * q + 1];
     o[q] = f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
   }
-  *reinterpret_cast<uint4*>(Xs + (size_t)c * T * K + t * K + k0) = make_uint4(o[0], o[1], o[2], o[3]);
+  uint32_t e[4];
+  pair_activations(o, e);
+  *reinterpret_cast<uint4*>(Xs + (size_t)c * T * K + t * K + k0) = make_uint4(e[0], e[1], e[2], e[3]);
 }
 
 // losses[c] = sum_tiles partials[c][tile] (fp64, tile order) / (T N); one wave per c,
@@ -118,10 +123,11 @@ int launch_grid_loss(const uint16_t* X, int T, int K, int N, const uint16_t* W, 
                      const float* S, const float* ratios, int C, int symmetric, float* losses,
                      void* workspace, hipStream_t stream) {
   if (C == 0) return W4_OK;
+  if ((long long)T * K >= (1LL << 31)) return W4_ERR_SHAPE;   // 32-bit element offsets in the MFMA core
   const LossLayout L = loss_layout(T, K, N, C, Yref == nullptr);
   char* ws = static_cast<char*>(workspace);
-  const dim3 tile_grid((unsigned)((N + kBN - 1) / kBN), (unsigned)((T + kBM - 1) / kBM), 1);
-  if (tile_grid.y > 65535 || C > 65535) return W4_ERR_SHAPE;
+  const dim3 tile_grid((unsigned)L.tiles, 1, 1);
+  if (C > 65535) return W4_ERR_SHAPE;
 
   if (Yref == nullptr) {
     uint16_t* yref = reinterpret_cast<uint16_t*>(ws + L.yref);
@@ -134,7 +140,8 @@ int launch_grid_loss(const uint16_t* X, int T, int K, int N, const uint16_t* W, 
   uint16_t* sc = reinterpret_cast<uint16_t*>(ws + L.sc);
   uint32_t* qz = reinterpret_cast<uint32_t*>(ws + L.qz);
   uint16_t* xs = reinterpret_cast<uint16_t*>(ws + L.xs);
-  float* rs = reinterpret_cast<float*>(ws + L.rs);
+  uint16_t* rsx = reinterpret_cast<uint16_t*>(ws + L.rsx);
+  uint16_t* cz = reinterpret_cast<uint16_t*>(ws + L.cz);
   float* part = reinterpret_cast<float*>(ws + L.part);
 
   QuantArgs q{};
@@ -159,7 +166,8 @@ int launch_grid_loss(const uint16_t* X, int T, int K, int N, const uint16_t* W, 
   hipLaunchKernelGGL(scale_activations_kernel, dim3((unsigned)((chunks + 255) / 256), 1, (unsigned)C), dim3(256), 0,
                      stream, X, T, K, S, xs);
   W4_CHECK_LAUNCH();
-  st = launch_group_rowsum(xs, (size_t)T * K, T, K, L.mpad, rs, (size_t)L.G * L.mpad, C, stream);
+  st = launch_zterm_prep(xs, (size_t)T * K, T, K, L.mpad, sc, q.sc_stride, symmetric ? nullptr : qz, q.qz_stride,
+                         symmetric, N, rsx, (size_t)L.mpad * L.kz, cz, (size_t)N * L.kz, nullptr, C, stream);
   if (st != W4_OK) return st;
 
   GemmCoreArgs a{};
@@ -172,12 +180,11 @@ int launch_grid_loss(const uint16_t* X, int T, int K, int N, const uint16_t* W, 
   a.qw_stride = q.qw_stride;
   a.scales = sc;
   a.sc_stride = q.sc_stride;
-  a.qzeros = symmetric ? nullptr : qz;
-  a.qz_stride = q.qz_stride;
-  a.symmetric = symmetric;
-  a.rs = rs;
-  a.rs_stride = (size_t)L.G * L.mpad;
-  a.mpad = L.mpad;
+  a.rsx = rsx;
+  a.rsx_stride = (size_t)L.mpad * L.kz;
+  a.cz = cz;
+  a.cz_stride = (size_t)N * L.kz;
+  a.kz = L.kz;
   a.Yref = Yref;
   a.partials = part;
   dim3 grid = tile_grid;
@@ -193,6 +200,7 @@ int launch_grid_loss(const uint16_t* X, int T, int K, int N, const uint16_t* W, 
 
 int launch_reference_gemm(const uint16_t* X, int M, int K, int N, const uint16_t* W, uint16_t* Y,
                           hipStream_t stream) {
+  if ((long long)M * K >= (1LL << 31)) return W4_ERR_SHAPE;   // 32-bit element offsets in the MFMA core
   GemmCoreArgs r{};
   r.X = X;
   r.M = M;
@@ -200,9 +208,9 @@ int launch_reference_gemm(const uint16_t* X, int M, int K, int N, const uint16_t
   r.N = N;
   r.W = W;
   r.Y = Y;
-  const dim3 grid((unsigned)((N + kBN - 1) / kBN), (unsigned)((M + kBM - 1) / kBM), 1);
-  if (grid.y > 65535) return W4_ERR_SHAPE;
-  hipLaunchKernelGGL((gemm_core_kernel<false, EPI_STORE>), grid, dim3(256), 0, stream, r);
+  const long long tiles = (long long)((N + kBN - 1) / kBN) * ((M + kBM - 1) / kBM);
+  if (tiles > 0x7FFFFFFFLL) return W4_ERR_SHAPE;
+  hipLaunchKernelGGL((gemm_core_kernel<false, EPI_STORE>), dim3((unsigned)tiles), dim3(256), 0, stream, r);
   W4_CHECK_LAUNCH();
   return W4_OK;
 }

@@ -19,13 +19,14 @@ __device__ __forceinline__ void split3(float v, uint32_t& hi, uint32_t& mid, uin
 //  * blocks [0, rsx_blocks): one wave per (row m < mpad, triple t): lanes 0..47
 //    each sum 8 consecutive bf16 of the triple's 384 channels (fp32, fixed order),
 //    16-lane xor trees give the three group sums, lane 0 writes the 16 slots;
-//  * the remaining blocks: one thread per (column n, triple t) writes the 16
-//    slots of -sc (128 + z).
+//  * the remaining blocks: one thread per (triple t, column n < npad) writes the
+//    16 slots of -sc (128 + z) and the triple's scales group-major (0 past N).
 __global__ __launch_bounds__(256) void zterm_prep_kernel(const uint16_t* X, size_t x_stride, int M, int K,
                                                          int mpad, const uint16_t* scales, size_t sc_stride,
                                                          const uint32_t* qzeros, size_t qz_stride, int symmetric,
                                                          int N, uint16_t* rsx, size_t rsx_stride, uint16_t* cz,
-                                                         size_t cz_stride, uint16_t* xp, int rsx_blocks) {
+                                                         size_t cz_stride, uint16_t* sct, size_t sct_stride,
+                                                         uint16_t* xp, int rsx_blocks) {
 #pragma clang fp contract(off)
   const int G = K >> 7;
   const int T3 = (G + 2) / 3;
@@ -74,10 +75,17 @@ __global__ __launch_bounds__(256) void zterm_prep_kernel(const uint16_t* X, size
       dst[1] = make_uint4(sl[8] | sl[9] << 16, sl[10] | sl[11] << 16, sl[12] | sl[13] << 16, sl[14] | sl[15] << 16);
     }
   } else {
+    const int npad = (N + 127) & ~127;
     const long long item = (long long)(blockIdx.x - rsx_blocks) * 256 + threadIdx.x;
-    if (item >= (long long)N * T3) return;
-    const int n = (int)(item / T3);
-    const int t = (int)(item % T3);
+    if (item >= (long long)npad * T3) return;
+    const int t = (int)(item / npad);
+    const int n = (int)(item % npad);
+    uint16_t* sct_c = sct + (size_t)c * sct_stride;
+    if (n >= N) {                                          // padding columns: scale 0
+      for (int jj = 0; jj < 3; ++jj)
+        if (3 * t + jj < G) sct_c[(size_t)(3 * t + jj) * npad + n] = 0;
+      return;
+    }
     const int GW = (G + 7) >> 3;
     uint32_t sl[16];
 #pragma unroll
@@ -85,7 +93,9 @@ __global__ __launch_bounds__(256) void zterm_prep_kernel(const uint16_t* X, size
       const int g = 3 * t + jj;
       uint32_t hi = 0, lo = 0;
       if (g < G) {
-        const float sc = bf16_bits_to_f32(scales[(size_t)c * sc_stride + (size_t)n * G + g]);
+        const uint16_t scb = scales[(size_t)c * sc_stride + (size_t)n * G + g];
+        sct_c[(size_t)g * npad + n] = scb;
+        const float sc = bf16_bits_to_f32(scb);
         uint32_t z = 8;
         if (!symmetric) z = (qzeros[(size_t)c * qz_stride + (size_t)n * GW + (g >> 3)] >> (4 * (g & 7))) & 0xFu;
         const float cv = -(sc * (float)(128u + z));          // exact: at most 16 significant bits
@@ -107,27 +117,29 @@ __global__ __launch_bounds__(256) void zterm_prep_kernel(const uint16_t* X, size
 
 int launch_zterm_prep(const uint16_t* X, size_t x_stride, int M, int K, int mpad, const uint16_t* scales,
                       size_t sc_stride, const uint32_t* qzeros, size_t qz_stride, int symmetric, int N,
-                      uint16_t* rsx, size_t rsx_stride, uint16_t* cz, size_t cz_stride, uint16_t* xp, int C,
-                      hipStream_t stream) {
+                      uint16_t* rsx, size_t rsx_stride, uint16_t* cz, size_t cz_stride, uint16_t* sct,
+                      size_t sct_stride, uint16_t* xp, int C, hipStream_t stream) {
   const int T3 = ((K >> 7) + 2) / 3;
   const long long rsx_blocks = ((long long)mpad * T3 + 3) / 4;
-  const long long cz_blocks = ((long long)N * T3 + 255) / 256;
+  const long long cz_blocks = ((long long)gemm_npad(N) * T3 + 255) / 256;
   if (rsx_blocks + cz_blocks == 0) return W4_OK;
   if (rsx_blocks + cz_blocks > 0x7FFFFFFFLL || C > 65535) return W4_ERR_SHAPE;
   hipLaunchKernelGGL(zterm_prep_kernel, dim3((unsigned)(rsx_blocks + cz_blocks), 1, (unsigned)C), dim3(256), 0,
                      stream, X, x_stride, M, K, mpad, scales, sc_stride, symmetric ? nullptr : qzeros, qz_stride,
-                     symmetric, N, rsx, rsx_stride, cz, cz_stride, xp, (int)rsx_blocks);
+                     symmetric, N, rsx, rsx_stride, cz, cz_stride, sct, sct_stride, xp, (int)rsx_blocks);
   W4_CHECK_LAUNCH();
   return W4_OK;
 }
 
 
-// workspace: pair-arranged X [M][K] bf16, rsx [mpad][kz] bf16, cz [N][kz] bf16
+// workspace: pair-arranged X [M][K] bf16, rsx [mpad][kz] bf16, cz [N][kz] bf16,
+// sct [K/128][npad] bf16
 size_t gemm_workspace_bytes(int M, int K, int N) {
   if (M <= 0 || K <= 0 || N <= 0) return 0;
   const size_t mpad = align_up((size_t)M, kBM);
   const size_t kz = (size_t)zterm_kz(K);
-  return align_up((size_t)M * K * 2, 256) + align_up(mpad * kz * 2, 256) + align_up((size_t)N * kz * 2, 256);
+  return align_up((size_t)M * K * 2, 256) + align_up(mpad * kz * 2, 256) + align_up((size_t)N * kz * 2, 256) +
+         align_up((size_t)(K / kGroup) * gemm_npad(N) * 2, 256);
 }
 
 int launch_gemm(const uint16_t* X, int M, int K, int N, const uint32_t* qweight,
@@ -141,8 +153,12 @@ int launch_gemm(const uint16_t* X, int M, int K, int N, const uint32_t* qweight,
   uint16_t* xp = reinterpret_cast<uint16_t*>(ws);
   ws += align_up((size_t)M * K * 2, 256);
   uint16_t* rsx = reinterpret_cast<uint16_t*>(ws);
-  uint16_t* cz = reinterpret_cast<uint16_t*>(ws + align_up((size_t)mpad * kz * 2, 256));
-  int st = launch_zterm_prep(X, 0, M, K, mpad, scales, 0, qzeros, 0, symmetric, N, rsx, 0, cz, 0, xp, 1, stream);
+  ws += align_up((size_t)mpad * kz * 2, 256);
+  uint16_t* cz = reinterpret_cast<uint16_t*>(ws);
+  ws += align_up((size_t)N * kz * 2, 256);
+  uint16_t* sct = reinterpret_cast<uint16_t*>(ws);
+  int st = launch_zterm_prep(X, 0, M, K, mpad, scales, 0, qzeros, 0, symmetric, N, rsx, 0, cz, 0, sct, 0, xp, 1,
+                             stream);
   if (st != W4_OK) return st;
   GemmCoreArgs a{};
   a.X = xp;
@@ -150,7 +166,8 @@ int launch_gemm(const uint16_t* X, int M, int K, int N, const uint32_t* qweight,
   a.K = K;
   a.N = N;
   a.qweight = qweight;
-  a.scales = scales;
+  a.sct = sct;
+  a.npad = gemm_npad(N);
   a.rsx = rsx;
   a.cz = cz;
   a.kz = kz;

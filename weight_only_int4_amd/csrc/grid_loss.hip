@@ -21,8 +21,8 @@ namespace w4 {
 namespace {
 
 struct LossLayout {
-  size_t yref, qw, sc, qz, xs, rsx, cz, part, total;
-  int mpad, G, GW, kz, tiles;
+  size_t yref, qw, sc, qz, xs, rsx, cz, sct, part, total;
+  int mpad, npad, G, GW, kz, tiles;
 };
 
 LossLayout loss_layout(int T, int K, int N, int C, bool need_yref) {
@@ -30,6 +30,7 @@ LossLayout loss_layout(int T, int K, int N, int C, bool need_yref) {
   L.G = K / kGroup;
   L.GW = (L.G + 7) / 8;
   L.mpad = (int)align_up((size_t)T, kBM);
+  L.npad = gemm_npad(N);
   L.kz = zterm_kz(K);
   L.tiles = ((N + kBN - 1) / kBN) * ((T + kBM - 1) / kBM);
   size_t off = 0;
@@ -45,6 +46,7 @@ LossLayout loss_layout(int T, int K, int N, int C, bool need_yref) {
   L.xs = take((size_t)C * T * K * 2);
   L.rsx = take((size_t)C * L.mpad * L.kz * 2);
   L.cz = take((size_t)C * N * L.kz * 2);
+  L.sct = take((size_t)C * L.G * L.npad * 2);
   L.part = take((size_t)C * L.tiles * 4);
   L.total = off;
   return L;
@@ -142,6 +144,7 @@ int launch_grid_loss(const uint16_t* X, int T, int K, int N, const uint16_t* W, 
   uint16_t* xs = reinterpret_cast<uint16_t*>(ws + L.xs);
   uint16_t* rsx = reinterpret_cast<uint16_t*>(ws + L.rsx);
   uint16_t* cz = reinterpret_cast<uint16_t*>(ws + L.cz);
+  uint16_t* sct = reinterpret_cast<uint16_t*>(ws + L.sct);
   float* part = reinterpret_cast<float*>(ws + L.part);
 
   QuantArgs q{};
@@ -167,7 +170,8 @@ int launch_grid_loss(const uint16_t* X, int T, int K, int N, const uint16_t* W, 
                      stream, X, T, K, S, xs);
   W4_CHECK_LAUNCH();
   st = launch_zterm_prep(xs, (size_t)T * K, T, K, L.mpad, sc, q.sc_stride, symmetric ? nullptr : qz, q.qz_stride,
-                         symmetric, N, rsx, (size_t)L.mpad * L.kz, cz, (size_t)N * L.kz, nullptr, C, stream);
+                         symmetric, N, rsx, (size_t)L.mpad * L.kz, cz, (size_t)N * L.kz, sct,
+                         (size_t)L.G * L.npad, nullptr, C, stream);
   if (st != W4_OK) return st;
 
   GemmCoreArgs a{};
@@ -178,8 +182,9 @@ int launch_grid_loss(const uint16_t* X, int T, int K, int N, const uint16_t* W, 
   a.N = N;
   a.qweight = qw;
   a.qw_stride = q.qw_stride;
-  a.scales = sc;
-  a.sc_stride = q.sc_stride;
+  a.sct = sct;
+  a.sct_stride = (size_t)L.G * L.npad;
+  a.npad = L.npad;
   a.rsx = rsx;
   a.rsx_stride = (size_t)L.mpad * L.kz;
   a.cz = cz;

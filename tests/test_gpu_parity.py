@@ -251,7 +251,8 @@ def _gemm_case(X, W, sym, rows=None):
 
 
 @pytest.mark.parametrize("M,K,N", [(1, 128, 1), (64, 2048, 128), (200, 384, 200), (256, 1152, 1000),
-                                   (129, 2048, 257), (37, 5120, 64), (512, 256, 96), (130, 17408, 130)])
+                                   (129, 2048, 257), (37, 5120, 64), (512, 256, 96), (130, 17408, 130),
+                                   (70, 640, 90)])
 @pytest.mark.parametrize("sym", [False, True])
 def test_gemm_shapes(M, K, N, sym):
     say("gemm", M, K, N, sym)

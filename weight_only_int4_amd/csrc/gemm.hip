@@ -146,7 +146,8 @@ int launch_gemm(const uint16_t* X, int M, int K, int N, const uint32_t* qweight,
                 const uint16_t* scales, const uint32_t* qzeros, int symmetric, uint16_t* Y,
                 void* workspace, hipStream_t stream) {
   if (M == 0 || N == 0) return W4_OK;
-  if ((long long)M * K >= (1LL << 31)) return W4_ERR_SHAPE;   // 32-bit element offsets in the kernel
+  // 32-bit per-lane byte offsets in the kernel: 2 M K and N K / 2 below 2^32
+  if ((long long)M * K >= (1LL << 31) || (long long)N * K >= (1LL << 33)) return W4_ERR_SHAPE;
   const int mpad = (int)align_up((size_t)M, kBM);
   const int kz = zterm_kz(K);
   char* ws = static_cast<char*>(workspace);

@@ -2,9 +2,10 @@
 // grid loss.  Y = X W_hat^T with X bf16 [M][K] and W_hat given either as packed
 // int4 groups (q - z) * sc or, for the unquantized reference, as bf16 [N][K].
 //
-// Workgroup tile 128 x 128, 4 waves in a 2 x 2 grid, wave tile 64 x 64 made of
-// 2 x 2 v_mfma_f32_32x32x16_bf16 blocks.  One main-loop step covers one
-// 128-channel quantization group.
+// Workgroup tile 128 x 128, 4 waves side by side: wave w computes all 128 rows
+// of columns 32 w .. 32 w + 31 as 4 v_mfma_f32_32x32x16_bf16 blocks, so every
+// packed weight word is expanded by exactly one wave.  One main-loop step covers
+// one 128-channel quantization group.
 //
 // Every operand of a group travels from global memory straight into LDS
 // (global_load_lds: no registers), STAGES groups deep.  These copies are issued
@@ -100,15 +101,16 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
-// Global -> LDS copies: lane l writes 16 (or 4) bytes at LDS byte address
-// m0 + 16 l (4 l).  M0 is set by the compiler from the "{m0}" operand; the
-// s_nop covers the one wait state the hardware needs between an M0 write and an
-// LDS copy.  The source address is a per-lane 64-bit VGPR pair.
-__device__ __forceinline__ void lds_copy16(const void* src, uint32_t lds) {
-  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "{m0}"(lds) : "memory");
+// Global -> LDS copies: lane l reads 16 (or 4) bytes at base + off (base a
+// wave-uniform 64-bit address held in SGPRs, off a per-lane unsigned 32-bit byte
+// offset) and writes them at LDS byte address m0 + 16 l (4 l).  M0 is set by the
+// compiler from the "{m0}" operand; the s_nop covers the one wait state the
+// hardware needs between an M0 write and an LDS copy.
+__device__ __forceinline__ void lds_copy16(uint32_t off, const void* base, uint32_t lds) {
+  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(base), "{m0}"(lds) : "memory");
 }
-__device__ __forceinline__ void lds_copy4(const void* src, uint32_t lds) {
-  asm volatile("s_nop 0\n\tglobal_load_lds_dword %0, off" ::"v"(src), "{m0}"(lds) : "memory");
+__device__ __forceinline__ void lds_copy4(uint32_t off, const void* base, uint32_t lds) {
+  asm volatile("s_nop 0\n\tglobal_load_lds_dword %0, %1" ::"v"(off), "s"(base), "{m0}"(lds) : "memory");
 }
 
 // Workgroup barrier without a memory fence.  LDS reads are complete (lgkmcnt);
@@ -142,8 +144,7 @@ __global__ __launch_bounds__(256, 1) void gemm_core_kernel(GemmCoreArgs a) {
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // column block of the tile
   const int h = lane >> 5, l32 = lane & 31;
   int tm, tn;
   tile_coords(blockIdx.x, (a.M + kBM - 1) / kBM, (a.N + kBN - 1) / kBN, tm, tn);
@@ -153,81 +154,108 @@ __global__ __launch_bounds__(256, 1) void gemm_core_kernel(GemmCoreArgs a) {
   const int T3 = (G + 2) / 3;
   const uint32_t smem_base = (uint32_t)(uintptr_t)smem;   // LDS byte address (low half of the generic one)
 
-  // ---- copy sources, per lane, without the group term ----
+  // ---- copy sources: wave-uniform bases (without the group term) and per-lane byte offsets ----
   // activations: copy i of wave w fills rows 4 (8 w + i) .. +3; lane -> row
   // 4 (8 w + i) + lane / 16, stored chunk lane % 16, which holds logical chunk
   // (lane % 16) ^ (row & 15).  Rows past M read row M-1 (always valid): their
-  // finite results are never stored or scored.
-  const uint16_t* X = a.X + (size_t)zc_idx * a.x_stride;
-  const uint16_t* asrc[8];
+  // finite results are never stored or scored.  Offsets < 2 M K < 2^32.
+  const unsigned char* abase = reinterpret_cast<const unsigned char*>(a.X + (size_t)zc_idx * a.x_stride);
+  uint32_t aoff[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     const int row = 4 * (8 * wave + i) + (lane >> 4);
-    const int grow = min(m0 + row, a.M - 1);
-    asrc[i] = X + (size_t)grow * a.K + (((lane & 15) ^ (row & 15)) * 8);
+    const uint32_t grow = (uint32_t)min(m0 + row, a.M - 1);
+    aoff[i] = (grow * (uint32_t)a.K + (uint32_t)(((lane & 15) ^ (row & 15)) * 8)) * 2u;
   }
   // weights.  int4: copy i (of 8, wave w issues 2w, 2w+1) fills LDS chunks 64 i + lane:
-  // column (64 i + lane) / 4, stored chunk lane % 4, logical chunk (lane % 4) ^ ((col >> 2) & 3).
+  // column (64 i + lane) / 4, stored chunk lane % 4, logical chunk (lane % 4) ^ ((col >> 2) & 3)
   // (LDS serves a 16-byte read 16 lanes at a time over 64 banks: 16 consecutive
-  // columns then hit 16 distinct 16-byte bank groups.)
-  // bf16: like the activations, rows = columns n.  Columns past N read column N-1.
-  const unsigned char* wsrc[INT4 ? 2 : 8];
+  // columns then hit 16 distinct 16-byte bank groups); offsets < N K / 2.
+  // bf16: like the activations, rows = columns n; offsets < 2 N K.  Columns past N
+  // read column N-1.
+  const unsigned char* wbase;
+  uint32_t woff[INT4 ? 2 : 8];
   if constexpr (INT4) {
-    const uint32_t* qw = a.qweight + (size_t)zc_idx * a.qw_stride;
-    const int words = a.K >> 3;
+    wbase = reinterpret_cast<const unsigned char*>(a.qweight + (size_t)zc_idx * a.qw_stride);
+    const uint32_t words = (uint32_t)(a.K >> 3);
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
       const int p = 64 * (2 * wave + u) + lane;
       const int col = p >> 2;
       const int chunk = (p & 3) ^ ((col >> 2) & 3);
-      wsrc[u] = reinterpret_cast<const unsigned char*>(qw + (size_t)min(n0 + col, a.N - 1) * words + chunk * 4);
+      woff[u] = (uint32_t)min(n0 + col, a.N - 1) * words * 4u + (uint32_t)chunk * 16u;
     }
   } else {
+    wbase = reinterpret_cast<const unsigned char*>(a.W);
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const int row = 4 * (8 * wave + i) + (lane >> 4);
-      wsrc[i] = reinterpret_cast<const unsigned char*>(a.W + (size_t)min(n0 + row, a.N - 1) * a.K +
-                                                       (((lane & 15) ^ (row & 15)) * 8));
+      woff[i] = ((uint32_t)min(n0 + row, a.N - 1) * (uint32_t)a.K + (uint32_t)(((lane & 15) ^ (row & 15)) * 8)) * 2u;
     }
   }
   // zero-point operands: copy i (of 8, wave w issues 2w, 2w+1) fills Z bytes
-  // 1024 i + 16 lane; i < 4: row parts of tile rows 32 i .. +31, i >= 4: column
-  // parts of tile columns 32 (i-4) .. +31; lane -> entry 32 (i % 4) + lane / 2,
-  // stored half lane % 2 holding logical half (lane % 2) ^ ((entry >> 3) & 1)
-  const uint16_t* zsrc[2] = {nullptr, nullptr};
-  const uint16_t* ssrc = nullptr;
+  // 1024 i + 16 lane; i < 4: row parts of tile rows 32 i .. +31 (waves 0, 1),
+  // i >= 4: column parts of tile columns 32 (i-4) .. +31 (waves 2, 3); lane ->
+  // entry 32 (i % 4) + lane / 2, stored half lane % 2 holding logical half
+  // (lane % 2) ^ ((entry >> 3) & 1)
+  const unsigned char* zbase = nullptr;
+  uint32_t zoff[2] = {0u, 0u};
+  const unsigned char* sbase = nullptr;
   if constexpr (INT4) {
+    zbase = wave < 2 ? reinterpret_cast<const unsigned char*>(a.rsx + (size_t)zc_idx * a.rsx_stride)
+                     : reinterpret_cast<const unsigned char*>(a.cz + (size_t)zc_idx * a.cz_stride);
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
       const int i = 2 * wave + u;
       const int e = 32 * (i & 3) + (lane >> 1);
       const int half = (lane & 1) ^ ((e >> 3) & 1);
-      if (i < 4)
-        zsrc[u] = a.rsx + (size_t)zc_idx * a.rsx_stride + (size_t)(m0 + e) * a.kz + half * 8;
-      else
-        zsrc[u] = a.cz + (size_t)zc_idx * a.cz_stride + (size_t)min(n0 + e, a.N - 1) * a.kz + half * 8;
+      const uint32_t ent = (uint32_t)(i < 4 ? m0 + e : min(n0 + e, a.N - 1));
+      zoff[u] = (ent * (uint32_t)a.kz + (uint32_t)half * 8u) * 2u;
     }
     // scales: 128 bf16 of the tile's columns, 4 bytes per lane
-    ssrc = a.sct + (size_t)zc_idx * a.sct_stride + n0 + 2 * lane;
+    sbase = reinterpret_cast<const unsigned char*>(a.sct + (size_t)zc_idx * a.sct_stride + n0);
   }
 
-  auto load_stage = [&](int g, int s) {
-    const uint32_t st = smem_base + s * SM::kStage;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) lds_copy16(asrc[i] + g * 128, st + SM::kA + (8 * wave + i) * 1024);
-    if constexpr (INT4) {
-#pragma unroll
-      for (int u = 0; u < 2; ++u) lds_copy16(wsrc[u] + g * 64, st + SM::kB + (2 * wave + u) * 1024);
-      // zero-point step t = g (a repeat of step 0 for g >= ceil(G/3), so every
-      // stage issues the same copies; it is not used)
-      const int t = g < T3 ? g : 0;
-#pragma unroll
-      for (int u = 0; u < 2; ++u) lds_copy16(zsrc[u] + t * 16, st + SM::kZ + (2 * wave + u) * 1024);
-      lds_copy4(ssrc + (size_t)g * a.npad, st + SM::kS + wave * 256);
+  // Sources of one group's copies: wave-uniform base addresses.
+  struct GroupSrc {
+    const unsigned char* a;   // activations
+    const unsigned char* w;   // packed words (int4) / weights (bf16)
+    const unsigned char* z;   // zero-point operands (int4)
+    const unsigned char* s;   // scales (int4)
+  };
+  auto group_src = [&](int g) {
+    GroupSrc r;
+    r.a = abase + (size_t)g * 256;
+    r.w = wbase + (size_t)g * (INT4 ? 64 : 256);
+    // zero-point step t = g (a repeat of step 0 for g >= ceil(G/3), so every
+    // stage issues the same copies; it is not used)
+    r.z = INT4 ? zbase + (size_t)(g < T3 ? g : 0) * 32 : nullptr;
+    r.s = INT4 ? sbase + (size_t)g * a.npad * 2 : nullptr;
+    return r;
+  };
+  // copy k (0 .. L-1) of a group into the stage at LDS byte address st.  int4: 0-7
+  // activations, 8-9 packed words, 10-11 zero-point operands, 12 scales; bf16:
+  // 0-7 activations, 8-15 weights.
+  auto copy_piece = [&](auto kidx, const GroupSrc& src, uint32_t st) {
+    constexpr int k = decltype(kidx)::value;
+    if constexpr (k < 8) {
+      lds_copy16(aoff[k], src.a, st + SM::kA + (8 * wave + k) * 1024);
+    } else if constexpr (INT4) {
+      if constexpr (k < 10)
+        lds_copy16(woff[k - 8], src.w, st + SM::kB + (2 * wave + k - 8) * 1024);
+      else if constexpr (k < 12)
+        lds_copy16(zoff[k - 10], src.z, st + SM::kZ + (2 * wave + k - 10) * 1024);
+      else
+        lds_copy4(4u * (uint32_t)lane, src.s, st + SM::kS + wave * 256);
     } else {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) lds_copy16(wsrc[i] + g * 256, st + SM::kB + (8 * wave + i) * 1024);
+      lds_copy16(woff[k - 8], src.w, st + SM::kB + (8 * wave + k - 8) * 1024);
     }
+  };
+  // the copies that go with MFMA step j of the group being computed
+  auto copies_of_step = [&](auto jidx, const GroupSrc& src, uint32_t st) {
+    constexpr int j = decltype(jidx)::value;
+    copy_piece(std::integral_constant<int, j>{}, src, st);
+    if constexpr (8 + j < L) copy_piece(std::integral_constant<int, 8 + j>{}, src, st);
   };
 
   // fragment reads of a 256-byte-row tile (activations; bf16 weights): row r,
@@ -236,174 +264,177 @@ __global__ __launch_bounds__(256, 1) void gemm_core_kernel(GemmCoreArgs a) {
   auto frag = [&](const unsigned char* tile, int row, int j) {
     return *reinterpret_cast<const bf16x8*>(tile + row * 256 + (((8 * h + j) ^ sw) * 16));
   };
+  const int col = 32 * wave + l32;         // this lane's output column within the tile
 
-  f32x16 acc[2][2];
+  f32x16 acc[4];
 #pragma unroll
-  for (int bm = 0; bm < 2; ++bm)
+  for (int bm = 0; bm < 4; ++bm)
 #pragma unroll
-    for (int bn = 0; bn < 2; ++bn)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[bm][bn][r] = 0.0f;
+    for (int r = 0; r < 16; ++r) acc[bm][r] = 0.0f;
 
   const uint32_t nib_mask = opaque_vgpr(0x000F000Fu);
-  auto compute = [&](int s, bool zstep) {
+  // Computes the group in stage s; between its MFMA steps it issues the copies of
+  // group gn into stage sn.  The activation fragments of step j+1 are read before
+  // the MFMAs of step j.
+  auto compute = [&](int s, bool zstep, const GroupSrc& nsrc, uint32_t nst) {
     const unsigned char* st = smem + s * SM::kStage;
     const unsigned char* sa = st + SM::kA;
     const unsigned char* sb = st + SM::kB;
+    bf16x8 af[2][4];
+#pragma unroll
+    for (int bm = 0; bm < 4; ++bm) af[0][bm] = frag(sa, bm * 32 + l32, 0);
     if constexpr (INT4) {
-      // this lane's 8 words of each of its two columns
-      uint4 wv[2][2];
+      // this lane's 8 words of its column
+      uint4 wv[2];
 #pragma unroll
-      for (int bn = 0; bn < 2; ++bn) {
-        const int col = wn * 64 + bn * 32 + l32;
+      for (int c = 0; c < 2; ++c)
+        wv[c] = *reinterpret_cast<const uint4*>(sb + col * 64 + (((2 * h + c) ^ ((col >> 2) & 3)) * 16));
+      f32x16 tmp[4];
+      auto step = [&](auto jidx) {
+        constexpr int j = decltype(jidx)::value;
+        if constexpr (j < 7) {
 #pragma unroll
-        for (int c = 0; c < 2; ++c)
-          wv[bn][c] = *reinterpret_cast<const uint4*>(sb + col * 64 + (((2 * h + c) ^ ((col >> 2) & 3)) * 16));
-      }
-      f32x16 tmp[2][2];
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        bf16x8 af[2], bf[2];
-#pragma unroll
-        for (int bm = 0; bm < 2; ++bm) af[bm] = frag(sa, wm * 64 + bm * 32 + l32, j);
-#pragma unroll
-        for (int bn = 0; bn < 2; ++bn) {
-          const uint4 w4v = wv[bn][j >> 2];
-          const uint32_t word = (j & 3) == 0 ? w4v.x : (j & 3) == 1 ? w4v.y : (j & 3) == 2 ? w4v.z : w4v.w;
-          const uint4 pr = make_uint4(nibble_pair_m(word, 0, nib_mask), nibble_pair_m(word, 1, nib_mask),
-                                      nibble_pair_m(word, 2, nib_mask), nibble_pair_m(word, 3, nib_mask));
-          bf[bn] = __builtin_bit_cast(bf16x8, pr);
+          for (int bm = 0; bm < 4; ++bm) af[(j + 1) & 1][bm] = frag(sa, bm * 32 + l32, j + 1);
         }
+        copies_of_step(jidx, nsrc, nst);
+        const uint4 w4v = wv[j >> 2];
+        const uint32_t word = (j & 3) == 0 ? w4v.x : (j & 3) == 1 ? w4v.y : (j & 3) == 2 ? w4v.z : w4v.w;
+        const bf16x8 bf = __builtin_bit_cast(
+            bf16x8, make_uint4(nibble_pair_m(word, 0, nib_mask), nibble_pair_m(word, 1, nib_mask),
+                               nibble_pair_m(word, 2, nib_mask), nibble_pair_m(word, 3, nib_mask)));
 #pragma unroll
-        for (int bm = 0; bm < 2; ++bm)
-#pragma unroll
-          for (int bn = 0; bn < 2; ++bn) {
-            if (j == 0)
-              tmp[bm][bn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[bm], bf[bn], f32x16{}, 0, 0, 0);
-            else
-              tmp[bm][bn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[bm], bf[bn], tmp[bm][bn], 0, 0, 0);
-          }
-      }
+        for (int bm = 0; bm < 4; ++bm) {
+          if constexpr (j == 0)
+            tmp[bm] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[0][bm], bf, f32x16{}, 0, 0, 0);
+          else
+            tmp[bm] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[j & 1][bm], bf, tmp[bm], 0, 0, 0);
+        }
+      };
+      step(std::integral_constant<int, 0>{});
+      step(std::integral_constant<int, 1>{});
+      step(std::integral_constant<int, 2>{});
+      step(std::integral_constant<int, 3>{});
+      step(std::integral_constant<int, 4>{});
+      step(std::integral_constant<int, 5>{});
+      step(std::integral_constant<int, 6>{});
+      step(std::integral_constant<int, 7>{});
       // zero-point step (accumulates straight into acc)
       if (zstep) {
         const unsigned char* sz = st + SM::kZ;
-        bf16x8 za[2], zb[2];
+        const bf16x8 zb = *reinterpret_cast<const bf16x8*>(sz + 4096 + col * 32 + ((h ^ ((col >> 3) & 1)) * 16));
 #pragma unroll
-        for (int bm = 0; bm < 2; ++bm) {
-          const int e = wm * 64 + bm * 32 + l32;
-          za[bm] = *reinterpret_cast<const bf16x8*>(sz + e * 32 + ((h ^ ((e >> 3) & 1)) * 16));
+        for (int bm = 0; bm < 4; ++bm) {
+          const int e = bm * 32 + l32;
+          const bf16x8 za = *reinterpret_cast<const bf16x8*>(sz + e * 32 + ((h ^ ((e >> 3) & 1)) * 16));
+          acc[bm] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(za, zb, acc[bm], 0, 0, 0);
         }
-#pragma unroll
-        for (int bn = 0; bn < 2; ++bn) {
-          const int e = wn * 64 + bn * 32 + l32;
-          zb[bn] = *reinterpret_cast<const bf16x8*>(sz + 4096 + e * 32 + ((h ^ ((e >> 3) & 1)) * 16));
-        }
-#pragma unroll
-        for (int bm = 0; bm < 2; ++bm)
-#pragma unroll
-          for (int bn = 0; bn < 2; ++bn)
-            acc[bm][bn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(za[bm], zb[bn], acc[bm][bn], 0, 0, 0);
       }
       // fold: acc += sc * tmp (scales of columns past N are 0)
-      const uint16_t* ss = reinterpret_cast<const uint16_t*>(st + SM::kS + wave * 256);
-      float sc[2];
+      const float sc = bf16_bits_to_f32(reinterpret_cast<const uint16_t*>(st + SM::kS + wave * 256)[col]);
 #pragma unroll
-      for (int bn = 0; bn < 2; ++bn) sc[bn] = bf16_bits_to_f32(ss[wn * 64 + bn * 32 + l32]);
+      for (int bm = 0; bm < 4; ++bm)
 #pragma unroll
-      for (int bm = 0; bm < 2; ++bm)
-#pragma unroll
-        for (int bn = 0; bn < 2; ++bn)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) acc[bm][bn][r] = fmaf(sc[bn], tmp[bm][bn][r], acc[bm][bn][r]);
+        for (int r = 0; r < 16; ++r) acc[bm][r] = fmaf(sc, tmp[bm][r], acc[bm][r]);
     } else {
       (void)zstep;
+      auto step = [&](auto jidx) {
+        constexpr int j = decltype(jidx)::value;
+        if constexpr (j < 7) {
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        bf16x8 af[2], bf[2];
+          for (int bm = 0; bm < 4; ++bm) af[(j + 1) & 1][bm] = frag(sa, bm * 32 + l32, j + 1);
+        }
+        const bf16x8 bf = frag(sb, col, j);
+        copies_of_step(jidx, nsrc, nst);
 #pragma unroll
-        for (int bm = 0; bm < 2; ++bm) af[bm] = frag(sa, wm * 64 + bm * 32 + l32, j);
-#pragma unroll
-        for (int bn = 0; bn < 2; ++bn) bf[bn] = frag(sb, wn * 64 + bn * 32 + l32, j);
-#pragma unroll
-        for (int bm = 0; bm < 2; ++bm)
-#pragma unroll
-          for (int bn = 0; bn < 2; ++bn)
-            acc[bm][bn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[bm], bf[bn], acc[bm][bn], 0, 0, 0);
-      }
+        for (int bm = 0; bm < 4; ++bm)
+          acc[bm] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[j & 1][bm], bf, acc[bm], 0, 0, 0);
+      };
+      step(std::integral_constant<int, 0>{});
+      step(std::integral_constant<int, 1>{});
+      step(std::integral_constant<int, 2>{});
+      step(std::integral_constant<int, 3>{});
+      step(std::integral_constant<int, 4>{});
+      step(std::integral_constant<int, 5>{});
+      step(std::integral_constant<int, 6>{});
+      step(std::integral_constant<int, 7>{});
     }
   };
 
   // Pipeline.  Stage s holds group g with g % S == s.  Iteration g waits until
-  // this wave's copies of group g are complete (groups g+1 .. g+D-1 may stay in
-  // flight), barriers -- after which every wave's group-g copies are in LDS and
-  // every wave has finished reading group g-1 -- then issues the copies of group
-  // g + D into the stage group g-1 used, and computes group g.
+  // this wave's copies of group g are complete (with 3 stages those of group
+  // g+1, issued during iteration g-1, may stay in flight), barriers -- after which every
+  // wave's group-g copies are in LDS and every wave has finished reading group
+  // g-1 -- then computes group g while issuing the copies of group g + D into the
+  // stage group g-1 used.  Past the last group the copies repeat group G-1 into
+  // that stage, which nothing reads again: every stage issues the same L copies,
+  // so the wait count is the same in every iteration.
+  static_assert(D == 1 || D == 2, "at most one stage in flight at each wait");
 #pragma unroll
-  for (int p = 0; p < D; ++p)
-    if (p < G) load_stage(p, p);
+  for (int p = 0; p < D; ++p) {
+    const GroupSrc src = group_src(min(p, G - 1));
+    const uint32_t st = smem_base + p * SM::kStage;
+    copies_of_step(std::integral_constant<int, 0>{}, src, st);
+    copies_of_step(std::integral_constant<int, 1>{}, src, st);
+    copies_of_step(std::integral_constant<int, 2>{}, src, st);
+    copies_of_step(std::integral_constant<int, 3>{}, src, st);
+    copies_of_step(std::integral_constant<int, 4>{}, src, st);
+    copies_of_step(std::integral_constant<int, 5>{}, src, st);
+    copies_of_step(std::integral_constant<int, 6>{}, src, st);
+    copies_of_step(std::integral_constant<int, 7>{}, src, st);
+  }
 
   auto iteration = [&](auto sidx, int g) {
     constexpr int s = decltype(sidx)::value;
-    const int ahead = min(D - 1, G - 1 - g);   // groups after g already issued
-    static_assert(D <= 2, "waits below cover at most one stage in flight");
-    if (ahead >= 1) wait_vmcnt<L>();
-    else wait_vmcnt<0>();
+    wait_vmcnt<(D - 1) * L>();
     lds_barrier();
-    if (g + D < G) load_stage(g + D, (s + D) % S);
-    compute(s, INT4 && g < T3);
+    const GroupSrc nsrc = group_src(min(g + D, G - 1));
+    compute(s, INT4 && g < T3, nsrc, smem_base + ((s + D) % S) * SM::kStage);
   };
 
   for (int g = 0; g < G; g += S) {
     iteration(std::integral_constant<int, 0>{}, g);
     if (g + 1 >= G) break;
     iteration(std::integral_constant<int, 1>{}, g + 1);
-    if constexpr (S >= 3) {
+    if constexpr (S == 3) {
       if (g + 2 >= G) break;
       iteration(std::integral_constant<int, 2>{}, g + 2);
     }
   }
+  // the repeated copies of the last iterations must land before LDS is reused or released
+  wait_vmcnt<0>();
 
   // epilogue.  Output layout of a 32x32 block: lane holds column l32 and rows
   // 8*i + 4*h + j for register 4*i + j.
-  bool nok[2];
-  int ncol[2];
-#pragma unroll
-  for (int bn = 0; bn < 2; ++bn) {
-    ncol[bn] = n0 + wn * 64 + bn * 32 + l32;
-    nok[bn] = ncol[bn] < a.N;
-  }
+  const int ncol = n0 + col;
+  const bool nok = ncol < a.N;
   if constexpr (EPI == EPI_STORE) {
+    if (nok) {
 #pragma unroll
-    for (int bm = 0; bm < 2; ++bm)
-#pragma unroll
-      for (int bn = 0; bn < 2; ++bn) {
-        if (!nok[bn]) continue;
+      for (int bm = 0; bm < 4; ++bm)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int row = m0 + wm * 64 + bm * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
-          if (row < a.M) a.Y[(size_t)row * a.N + ncol[bn]] = (uint16_t)f32_to_bf16_bits(acc[bm][bn][r]);
+          const int row = m0 + bm * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
+          if (row < a.M) a.Y[(size_t)row * a.N + ncol] = (uint16_t)f32_to_bf16_bits(acc[bm][r]);
         }
-      }
+    }
   } else {
     const uint16_t* Yref = a.Yref;
     float s = 0.0f;
+    if (nok) {
 #pragma unroll
-    for (int bm = 0; bm < 2; ++bm)
-#pragma unroll
-      for (int bn = 0; bn < 2; ++bn) {
-        if (!nok[bn]) continue;
+      for (int bm = 0; bm < 4; ++bm)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int row = m0 + wm * 64 + bm * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
+          const int row = m0 + bm * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
           if (row < a.M) {
-            const float d = acc[bm][bn][r] - bf16_bits_to_f32(Yref[(size_t)row * a.N + ncol[bn]]);
+            const float d = acc[bm][r] - bf16_bits_to_f32(Yref[(size_t)row * a.N + ncol]);
             s = fmaf(d, d, s);
           }
         }
-      }
+    }
     s = wave_sum(s);
-    // all copies have completed (the last iteration waited for vmcnt 0) and every
-    // wave is past its last LDS read after this barrier: stage 0 is free
+    // all copies have completed (vmcnt 0 above) and every wave is past its last
+    // LDS read after this barrier: stage 0 is free
     float* sRed = reinterpret_cast<float*>(smem);
     lds_barrier();
     if (lane == 0) sRed[wave] = s;

@@ -125,7 +125,8 @@ int launch_grid_loss(const uint16_t* X, int T, int K, int N, const uint16_t* W, 
                      const float* S, const float* ratios, int C, int symmetric, float* losses,
                      void* workspace, hipStream_t stream) {
   if (C == 0) return W4_OK;
-  if ((long long)T * K >= (1LL << 31)) return W4_ERR_SHAPE;   // 32-bit element offsets in the MFMA core
+  // 32-bit per-lane byte offsets in the MFMA core: 2 T K and 2 N K (bf16 reference weights) below 2^32
+  if ((long long)T * K >= (1LL << 31) || (long long)N * K >= (1LL << 31)) return W4_ERR_SHAPE;
   const LossLayout L = loss_layout(T, K, N, C, Yref == nullptr);
   char* ws = static_cast<char*>(workspace);
   const dim3 tile_grid((unsigned)L.tiles, 1, 1);
@@ -205,7 +206,8 @@ int launch_grid_loss(const uint16_t* X, int T, int K, int N, const uint16_t* W, 
 
 int launch_reference_gemm(const uint16_t* X, int M, int K, int N, const uint16_t* W, uint16_t* Y,
                           hipStream_t stream) {
-  if ((long long)M * K >= (1LL << 31)) return W4_ERR_SHAPE;   // 32-bit element offsets in the MFMA core
+  // 32-bit per-lane byte offsets in the MFMA core: 2 M K and 2 N K below 2^32
+  if ((long long)M * K >= (1LL << 31) || (long long)N * K >= (1LL << 31)) return W4_ERR_SHAPE;
   GemmCoreArgs r{};
   r.X = X;
   r.M = M;

@@ -52,6 +52,9 @@ __global__ __launch_bounds__(256) void zterm_prep_kernel(const uint16_t* X, size
         pair_activations(d, e);
         *reinterpret_cast<uint4*>(xp + off) = make_uint4(e[0], e[1], e[2], e[3]);
       }
+    } else if (xp && m >= M && j < 3 && g < G) {      // padding rows of xp
+      const size_t off = (size_t)c * x_stride + (size_t)m * K + (size_t)g * kGroup + (lane & 15) * 8;
+      *reinterpret_cast<uint4*>(xp + off) = make_uint4(0u, 0u, 0u, 0u);
     }
 #pragma unroll
     for (int off = 1; off < 16; off <<= 1) s += __shfl_xor(s, off, kWave);
@@ -132,13 +135,13 @@ int launch_zterm_prep(const uint16_t* X, size_t x_stride, int M, int K, int mpad
 }
 
 
-// workspace: pair-arranged X [M][K] bf16, rsx [mpad][kz] bf16, cz [N][kz] bf16,
-// sct [K/128][npad] bf16
+// workspace: pair-arranged X [mpad][K] bf16 (rows >= M zero), rsx [mpad][kz] bf16,
+// cz [N][kz] bf16, sct [K/128][npad] bf16
 size_t gemm_workspace_bytes(int M, int K, int N) {
   if (M <= 0 || K <= 0 || N <= 0) return 0;
   const size_t mpad = align_up((size_t)M, kBM);
   const size_t kz = (size_t)zterm_kz(K);
-  return align_up((size_t)M * K * 2, 256) + align_up(mpad * kz * 2, 256) + align_up((size_t)N * kz * 2, 256) +
+  return align_up(mpad * K * 2, 256) + align_up(mpad * kz * 2, 256) + align_up((size_t)N * kz * 2, 256) +
          align_up((size_t)(K / kGroup) * gemm_npad(N) * 2, 256);
 }
 
@@ -146,13 +149,13 @@ int launch_gemm(const uint16_t* X, int M, int K, int N, const uint32_t* qweight,
                 const uint16_t* scales, const uint32_t* qzeros, int symmetric, uint16_t* Y,
                 void* workspace, hipStream_t stream) {
   if (M == 0 || N == 0) return W4_OK;
-  // 32-bit per-lane byte offsets in the kernel: 2 M K and N K / 2 below 2^32
-  if ((long long)M * K >= (1LL << 31) || (long long)N * K >= (1LL << 33)) return W4_ERR_SHAPE;
+  // 32-bit per-lane byte offsets in the kernel: 2 mpad K and N K / 2 below 2^32
+  if (((long long)M + kBM) * K >= (1LL << 31) || (long long)N * K >= (1LL << 33)) return W4_ERR_SHAPE;
   const int mpad = (int)align_up((size_t)M, kBM);
   const int kz = zterm_kz(K);
   char* ws = static_cast<char*>(workspace);
   uint16_t* xp = reinterpret_cast<uint16_t*>(ws);
-  ws += align_up((size_t)M * K * 2, 256);
+  ws += align_up((size_t)mpad * K * 2, 256);
   uint16_t* rsx = reinterpret_cast<uint16_t*>(ws);
   ws += align_up((size_t)mpad * kz * 2, 256);
   uint16_t* cz = reinterpret_cast<uint16_t*>(ws);

@@ -23,19 +23,20 @@
 //     prologue kernel);
 //   * packed words: 128 columns x 16 words (8 KB); inside a column's 64 bytes the
 //     16-byte chunk c is stored at position c ^ ((col >> 2) & 3);
-//   * zero-point operands of one K=16 step (8 KB, see below);
 //   * scales of the group: 128 bf16, one copy per wave (the prologue writes them
 //     group-major, zero past N).
 // Each lane's weight operand for one MFMA is one packed uint32 word (8
 // consecutive channels of its output column), expanded in registers to bf16
 // integers 128 + q.  The 8 MFMAs of a group accumulate exact integer-weight
 // products sum_k x (128 + q) into a per-group fp32 tile, folded into the output
-// accumulator with one FMA: acc += sc * tmp.  The zero-point term
+// accumulator with one FMA, acc += sc * tmp, block by block between the first
+// MFMAs of the next group (so the matrix cores do not drain at group
+// boundaries).  The zero-point term
 // -sum_g rowsum_g(X)[m] * sc[n,g] (128 + z[n,g]) is a small contraction over
-// groups, also done on the MFMA: the prologue writes rowsum_g(X) as three bf16
-// parts (hi + mid + lo, exact) and -sc (128 + z) as two (exact: it has at most
-// 16 significant bits) into 16-slot rows, 5 products per group, 3 groups per
-// K=16 step; one such step per three groups accumulates straight into acc.
+// groups, also done on the MFMA, once per tile after the main loop: the prologue
+// writes rowsum_g(X) as three bf16 parts (hi + mid + lo, exact) and -sc (128 + z)
+// as two (exact: it has at most 16 significant bits) into 16-slot rows, 5
+// products per group, 3 groups per K=16 step.
 // The k-slots of the MFMA are assigned so that lane half h, step j covers
 // channels 64h + 8j .. 64h + 8j + 7 of the group: each lane's 8 words of a group
 // are contiguous.
@@ -53,7 +54,8 @@ constexpr int kBN = 128;
 enum { EPI_STORE = 0, EPI_SQDIFF = 1 };
 
 struct GemmCoreArgs {
-  const uint16_t* X;       // [M][K] bf16 (+ z * x_stride); pair-arranged for int4 weights
+  const uint16_t* X;       // [M][K] bf16 (+ z * x_stride); int4 weights: pair-arranged, rows up to M
+                           // rounded to 128 readable
   size_t x_stride;
   int M, K, N;
   // int4 weights
@@ -124,13 +126,12 @@ template <bool INT4>
 struct GemmSmem {
   static constexpr int kA = 0;                                   // activations, 32 KB
   static constexpr int kB = kBM * 256;                           // int4: packed words 8 KB; bf16: weights 32 KB
-  static constexpr int kZ = kB + (INT4 ? kBN * 64 : kBN * 256);  // int4: zero-point operands 8 KB
-  static constexpr int kS = kZ + (INT4 ? 8192 : 0);              // int4: scales, 4 waves x 256 B
+  static constexpr int kS = kB + (INT4 ? kBN * 64 : kBN * 256);  // int4: scales, 4 waves x 256 B
   static constexpr int kStage = kS + (INT4 ? 1024 : 0);
   static constexpr int kStages = INT4 ? 3 : 2;
-  // copies issued per stage and wave: activations 8 (+ int4: words 2, zero-point 2,
-  // scales 1; bf16: weights 8)
-  static constexpr int kCopies = INT4 ? 13 : 16;
+  // copies issued per stage and wave: activations 8 (+ int4: words 2, scales 1;
+  // bf16: weights 8)
+  static constexpr int kCopies = INT4 ? 11 : 16;
   static_assert(kStage * kStages <= 160 * 1024, "LDS");
 };
 
@@ -155,17 +156,23 @@ __global__ __launch_bounds__(256, 1) void gemm_core_kernel(GemmCoreArgs a) {
   const uint32_t smem_base = (uint32_t)(uintptr_t)smem;   // LDS byte address (low half of the generic one)
 
   // ---- copy sources: wave-uniform bases (without the group term) and per-lane byte offsets ----
-  // activations: copy i of wave w fills rows 4 (8 w + i) .. +3; lane -> row
-  // 4 (8 w + i) + lane / 16, stored chunk lane % 16, which holds logical chunk
-  // (lane % 16) ^ (row & 15).  Rows past M read row M-1 (always valid): their
-  // finite results are never stored or scored.  Offsets < 2 M K < 2^32.
+  // activations: copy i of wave w fills rows 4 (w + 4 i) .. +3; lane -> row
+  // 4 (w + 4 i) + lane / 16, stored chunk lane % 16, which holds logical chunk
+  // (lane % 16) ^ (row & 15); row & 15 = 4 w + lane / 16 for every i.
+  // int4: X has rows up to M rounded to 128 (the prologue pads them), so copy i
+  // is copy 0 moved by 16 rows and one offset serves all eight (< 2 mpad K).
+  // bf16: rows past M read row M-1 (always valid): their finite results are
+  // never stored or scored.
   const unsigned char* abase = reinterpret_cast<const unsigned char*>(a.X + (size_t)zc_idx * a.x_stride);
-  uint32_t aoff[8];
+  const int arow = 4 * wave + (lane >> 4);
+  const uint32_t achunk = (uint32_t)(((lane & 15) ^ (arow & 15)) * 8);
+  uint32_t aoff[INT4 ? 1 : 8];
+  if constexpr (INT4) {
+    aoff[0] = ((uint32_t)(m0 + arow) * (uint32_t)a.K + achunk) * 2u;
+  } else {
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int row = 4 * (8 * wave + i) + (lane >> 4);
-    const uint32_t grow = (uint32_t)min(m0 + row, a.M - 1);
-    aoff[i] = (grow * (uint32_t)a.K + (uint32_t)(((lane & 15) ^ (row & 15)) * 8)) * 2u;
+    for (int i = 0; i < 8; ++i)
+      aoff[i] = ((uint32_t)min(m0 + arow + 16 * i, a.M - 1) * (uint32_t)a.K + achunk) * 2u;
   }
   // weights.  int4: copy i (of 8, wave w issues 2w, 2w+1) fills LDS chunks 64 i + lane:
   // column (64 i + lane) / 4, stored chunk lane % 4, logical chunk (lane % 4) ^ ((col >> 2) & 3)
@@ -188,30 +195,11 @@ __global__ __launch_bounds__(256, 1) void gemm_core_kernel(GemmCoreArgs a) {
   } else {
     wbase = reinterpret_cast<const unsigned char*>(a.W);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int row = 4 * (8 * wave + i) + (lane >> 4);
-      woff[i] = ((uint32_t)min(n0 + row, a.N - 1) * (uint32_t)a.K + (uint32_t)(((lane & 15) ^ (row & 15)) * 8)) * 2u;
-    }
+    for (int i = 0; i < 8; ++i)
+      woff[i] = ((uint32_t)min(n0 + arow + 16 * i, a.N - 1) * (uint32_t)a.K + achunk) * 2u;
   }
-  // zero-point operands: copy i (of 8, wave w issues 2w, 2w+1) fills Z bytes
-  // 1024 i + 16 lane; i < 4: row parts of tile rows 32 i .. +31 (waves 0, 1),
-  // i >= 4: column parts of tile columns 32 (i-4) .. +31 (waves 2, 3); lane ->
-  // entry 32 (i % 4) + lane / 2, stored half lane % 2 holding logical half
-  // (lane % 2) ^ ((entry >> 3) & 1)
-  const unsigned char* zbase = nullptr;
-  uint32_t zoff[2] = {0u, 0u};
   const unsigned char* sbase = nullptr;
   if constexpr (INT4) {
-    zbase = wave < 2 ? reinterpret_cast<const unsigned char*>(a.rsx + (size_t)zc_idx * a.rsx_stride)
-                     : reinterpret_cast<const unsigned char*>(a.cz + (size_t)zc_idx * a.cz_stride);
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const int i = 2 * wave + u;
-      const int e = 32 * (i & 3) + (lane >> 1);
-      const int half = (lane & 1) ^ ((e >> 3) & 1);
-      const uint32_t ent = (uint32_t)(i < 4 ? m0 + e : min(n0 + e, a.N - 1));
-      zoff[u] = (ent * (uint32_t)a.kz + (uint32_t)half * 8u) * 2u;
-    }
     // scales: 128 bf16 of the tile's columns, 4 bytes per lane
     sbase = reinterpret_cast<const unsigned char*>(a.sct + (size_t)zc_idx * a.sct_stride + n0);
   }
@@ -220,35 +208,31 @@ __global__ __launch_bounds__(256, 1) void gemm_core_kernel(GemmCoreArgs a) {
   struct GroupSrc {
     const unsigned char* a;   // activations
     const unsigned char* w;   // packed words (int4) / weights (bf16)
-    const unsigned char* z;   // zero-point operands (int4)
     const unsigned char* s;   // scales (int4)
   };
   auto group_src = [&](int g) {
     GroupSrc r;
     r.a = abase + (size_t)g * 256;
     r.w = wbase + (size_t)g * (INT4 ? 64 : 256);
-    // zero-point step t = g (a repeat of step 0 for g >= ceil(G/3), so every
-    // stage issues the same copies; it is not used)
-    r.z = INT4 ? zbase + (size_t)(g < T3 ? g : 0) * 32 : nullptr;
     r.s = INT4 ? sbase + (size_t)g * a.npad * 2 : nullptr;
     return r;
   };
   // copy k (0 .. L-1) of a group into the stage at LDS byte address st.  int4: 0-7
-  // activations, 8-9 packed words, 10-11 zero-point operands, 12 scales; bf16:
-  // 0-7 activations, 8-15 weights.
+  // activations, 8-9 packed words, 10 scales; bf16: 0-7 activations, 8-15 weights.
   auto copy_piece = [&](auto kidx, const GroupSrc& src, uint32_t st) {
     constexpr int k = decltype(kidx)::value;
     if constexpr (k < 8) {
-      lds_copy16(aoff[k], src.a, st + SM::kA + (8 * wave + k) * 1024);
+      if constexpr (INT4)
+        lds_copy16(aoff[0], src.a + (size_t)k * 32 * a.K, st + SM::kA + (wave + 4 * k) * 1024);
+      else
+        lds_copy16(aoff[k], src.a, st + SM::kA + (wave + 4 * k) * 1024);
     } else if constexpr (INT4) {
       if constexpr (k < 10)
         lds_copy16(woff[k - 8], src.w, st + SM::kB + (2 * wave + k - 8) * 1024);
-      else if constexpr (k < 12)
-        lds_copy16(zoff[k - 10], src.z, st + SM::kZ + (2 * wave + k - 10) * 1024);
       else
         lds_copy4(4u * (uint32_t)lane, src.s, st + SM::kS + wave * 256);
     } else {
-      lds_copy16(woff[k - 8], src.w, st + SM::kB + (8 * wave + k - 8) * 1024);
+      lds_copy16(woff[k - 8], src.w, st + SM::kB + (wave + 4 * (k - 8)) * 1024);
     }
   };
   // the copies that go with MFMA step j of the group being computed
@@ -258,11 +242,14 @@ __global__ __launch_bounds__(256, 1) void gemm_core_kernel(GemmCoreArgs a) {
     if constexpr (8 + j < L) copy_piece(std::integral_constant<int, 8 + j>{}, src, st);
   };
 
-  // fragment reads of a 256-byte-row tile (activations; bf16 weights): row r,
-  // logical chunk 8h + j at stored chunk (8h + j) ^ (r & 15); r & 15 = l32 & 15
-  const int sw = l32 & 15;
-  auto frag = [&](const unsigned char* tile, int row, int j) {
-    return *reinterpret_cast<const bf16x8*>(tile + row * 256 + (((8 * h + j) ^ sw) * 16));
+  // fragment reads of a 256-byte-row tile (activations; bf16 weights): row
+  // 32 bm + l32, logical chunk 8h + j at stored chunk (8h + j) ^ (l32 & 15), i.e.
+  // byte (l32 * 256 + ((8h ^ (l32 & 15)) * 16)) ^ (16 j) + 8192 bm: one XOR per
+  // step, the rest immediate offsets
+  const uint32_t fbase = (uint32_t)(l32 * 256 + (((8 * h) ^ (l32 & 15)) * 16));
+  uint32_t fb = fbase;
+  auto frag = [&](const unsigned char* tile, int bm, int j) {
+    return *reinterpret_cast<const bf16x8*>(tile + ((fb ^ (uint32_t)(16 * j)) + 8192u * bm));
   };
   const int col = 32 * wave + l32;         // this lane's output column within the tile
 
@@ -272,30 +259,45 @@ __global__ __launch_bounds__(256, 1) void gemm_core_kernel(GemmCoreArgs a) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[bm][r] = 0.0f;
 
+  // int4: per-group products of the last group computed and its scale, folded
+  // into acc at the start of the next group (0 * 0 before the first)
+  f32x16 tmp[4];
+#pragma unroll
+  for (int bm = 0; bm < 4; ++bm)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) tmp[bm][r] = 0.0f;
+  float sc_prev = 0.0f;
+
   const uint32_t nib_mask = opaque_vgpr(0x000F000Fu);
   // Computes the group in stage s; between its MFMA steps it issues the copies of
   // group gn into stage sn.  The activation fragments of step j+1 are read before
   // the MFMAs of step j.
-  auto compute = [&](int s, bool zstep, const GroupSrc& nsrc, uint32_t nst) {
+  auto compute = [&](int s, const GroupSrc& nsrc, uint32_t nst) {
     const unsigned char* st = smem + s * SM::kStage;
     const unsigned char* sa = st + SM::kA;
     const unsigned char* sb = st + SM::kB;
+    // recomputed per group: hoisted out of the loop, the eight per-step
+    // addresses would stay live in registers for the whole kernel
+    fb = opaque_vgpr(fbase);
     bf16x8 af[2][4];
 #pragma unroll
-    for (int bm = 0; bm < 4; ++bm) af[0][bm] = frag(sa, bm * 32 + l32, 0);
+    for (int bm = 0; bm < 4; ++bm) af[0][bm] = frag(sa, bm, 0);
     if constexpr (INT4) {
       // this lane's 8 words of its column
       uint4 wv[2];
 #pragma unroll
       for (int c = 0; c < 2; ++c)
         wv[c] = *reinterpret_cast<const uint4*>(sb + col * 64 + (((2 * h + c) ^ ((col >> 2) & 3)) * 16));
-      f32x16 tmp[4];
+      __builtin_amdgcn_sched_barrier(0);
       auto step = [&](auto jidx) {
         constexpr int j = decltype(jidx)::value;
         if constexpr (j < 7) {
 #pragma unroll
-          for (int bm = 0; bm < 4; ++bm) af[(j + 1) & 1][bm] = frag(sa, bm * 32 + l32, j + 1);
+          for (int bm = 0; bm < 4; ++bm) af[(j + 1) & 1][bm] = frag(sa, bm, j + 1);
         }
+        // keep the reads of step j+1 ahead of the MFMAs of step j (the scheduler
+        // would otherwise sink each read next to its use and expose LDS latency)
+        __builtin_amdgcn_sched_barrier(0);
         copies_of_step(jidx, nsrc, nst);
         const uint4 w4v = wv[j >> 2];
         const uint32_t word = (j & 3) == 0 ? w4v.x : (j & 3) == 1 ? w4v.y : (j & 3) == 2 ? w4v.z : w4v.w;
@@ -304,11 +306,17 @@ __global__ __launch_bounds__(256, 1) void gemm_core_kernel(GemmCoreArgs a) {
                                nibble_pair_m(word, 2, nib_mask), nibble_pair_m(word, 3, nib_mask)));
 #pragma unroll
         for (int bm = 0; bm < 4; ++bm) {
-          if constexpr (j == 0)
+          if constexpr (j == 0) {
+            // fold the previous group's block first: acc += sc_prev * tmp (fenced
+            // from the MFMA that overwrites tmp, so both never need registers at once)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[bm][r] = fmaf(sc_prev, tmp[bm][r], acc[bm][r]);
+            __builtin_amdgcn_sched_barrier(0);
             tmp[bm] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[0][bm], bf, f32x16{}, 0, 0, 0);
-          else
+          } else
             tmp[bm] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[j & 1][bm], bf, tmp[bm], 0, 0, 0);
         }
+        __builtin_amdgcn_sched_barrier(0);
       };
       step(std::integral_constant<int, 0>{});
       step(std::integral_constant<int, 1>{});
@@ -318,36 +326,27 @@ __global__ __launch_bounds__(256, 1) void gemm_core_kernel(GemmCoreArgs a) {
       step(std::integral_constant<int, 5>{});
       step(std::integral_constant<int, 6>{});
       step(std::integral_constant<int, 7>{});
-      // zero-point step (accumulates straight into acc)
-      if (zstep) {
-        const unsigned char* sz = st + SM::kZ;
-        const bf16x8 zb = *reinterpret_cast<const bf16x8*>(sz + 4096 + col * 32 + ((h ^ ((col >> 3) & 1)) * 16));
-#pragma unroll
-        for (int bm = 0; bm < 4; ++bm) {
-          const int e = bm * 32 + l32;
-          const bf16x8 za = *reinterpret_cast<const bf16x8*>(sz + e * 32 + ((h ^ ((e >> 3) & 1)) * 16));
-          acc[bm] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(za, zb, acc[bm], 0, 0, 0);
-        }
-      }
-      // fold: acc += sc * tmp (scales of columns past N are 0)
-      const float sc = bf16_bits_to_f32(reinterpret_cast<const uint16_t*>(st + SM::kS + wave * 256)[col]);
-#pragma unroll
-      for (int bm = 0; bm < 4; ++bm)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) acc[bm][r] = fmaf(sc, tmp[bm][r], acc[bm][r]);
+      // this group's scale (columns past N have 0), read before the stage can be
+      // overwritten; its fold happens in step 0 of the next group (or after the loop)
+      sc_prev = bf16_bits_to_f32(reinterpret_cast<const uint16_t*>(st + SM::kS + wave * 256)[col]);
     } else {
-      (void)zstep;
+      bf16x8 bfc = frag(sb, wave, 0), bfn = bfc;
+      __builtin_amdgcn_sched_barrier(0);
       auto step = [&](auto jidx) {
         constexpr int j = decltype(jidx)::value;
         if constexpr (j < 7) {
 #pragma unroll
-          for (int bm = 0; bm < 4; ++bm) af[(j + 1) & 1][bm] = frag(sa, bm * 32 + l32, j + 1);
+          for (int bm = 0; bm < 4; ++bm) af[(j + 1) & 1][bm] = frag(sa, bm, j + 1);
+          bfn = frag(sb, wave, j + 1);
         }
-        const bf16x8 bf = frag(sb, col, j);
+        __builtin_amdgcn_sched_barrier(0);
+        const bf16x8 bf = bfc;
         copies_of_step(jidx, nsrc, nst);
 #pragma unroll
         for (int bm = 0; bm < 4; ++bm)
           acc[bm] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[j & 1][bm], bf, acc[bm], 0, 0, 0);
+        bfc = bfn;
+        __builtin_amdgcn_sched_barrier(0);
       };
       step(std::integral_constant<int, 0>{});
       step(std::integral_constant<int, 1>{});
@@ -388,7 +387,7 @@ __global__ __launch_bounds__(256, 1) void gemm_core_kernel(GemmCoreArgs a) {
     wait_vmcnt<(D - 1) * L>();
     lds_barrier();
     const GroupSrc nsrc = group_src(min(g + D, G - 1));
-    compute(s, INT4 && g < T3, nsrc, smem_base + ((s + D) % S) * SM::kStage);
+    compute(s, nsrc, smem_base + ((s + D) % S) * SM::kStage);
   };
 
   for (int g = 0; g < G; g += S) {
@@ -402,6 +401,42 @@ __global__ __launch_bounds__(256, 1) void gemm_core_kernel(GemmCoreArgs a) {
   }
   // the repeated copies of the last iterations must land before LDS is reused or released
   wait_vmcnt<0>();
+  if constexpr (INT4) {
+#pragma unroll
+    for (int bm = 0; bm < 4; ++bm)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[bm][r] = fmaf(sc_prev, tmp[bm][r], acc[bm][r]);
+
+    // zero-point term: ceil(G/3) K=16 steps over the split operands, read straight
+    // from global memory one step ahead, accumulated in tmp (free now), then added
+    const uint16_t* zr = a.rsx + (size_t)zc_idx * a.rsx_stride + (size_t)(m0 + l32) * a.kz + 8 * h;
+    const uint16_t* zcl = a.cz + (size_t)zc_idx * a.cz_stride + (size_t)min(n0 + col, a.N - 1) * a.kz + 8 * h;
+    const size_t zrow32 = (size_t)32 * a.kz;
+    bf16x8 za[2][4], zb[2];
+    auto zload = [&](int t, int b) {
+      zb[b] = *reinterpret_cast<const bf16x8*>(zcl + 16 * t);
+#pragma unroll
+      for (int bm = 0; bm < 4; ++bm) za[b][bm] = *reinterpret_cast<const bf16x8*>(zr + bm * zrow32 + 16 * t);
+    };
+    auto zstep = [&](int b, bool first) {
+#pragma unroll
+      for (int bm = 0; bm < 4; ++bm)
+        tmp[bm] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(za[b][bm], zb[b], first ? f32x16{} : tmp[bm], 0, 0, 0);
+    };
+    zload(0, 0);
+    for (int t = 0; t < T3; t += 2) {
+      if (t + 1 < T3) zload(t + 1, 1);
+      zstep(0, t == 0);
+      if (t + 1 < T3) {
+        if (t + 2 < T3) zload(t + 2, 0);
+        zstep(1, false);
+      }
+    }
+#pragma unroll
+    for (int bm = 0; bm < 4; ++bm)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[bm][r] += tmp[bm][r];
+  }
 
   // epilogue.  Output layout of a 32x32 block: lane holds column l32 and rows
   // 8*i + 4*h + j for register 4*i + j.
@@ -418,25 +453,53 @@ __global__ __launch_bounds__(256, 1) void gemm_core_kernel(GemmCoreArgs a) {
         }
     }
   } else {
-    const uint16_t* Yref = a.Yref;
+    // Squared differences against Yref.  The fp32 tile goes through LDS (rows of
+    // 136 floats: the two lane halves, 4 rows apart, then hit different banks),
+    // then each thread scores half a row with 16-byte reads of the tile and of
+    // Yref.  The values are handed over as opaque bits: consumed as floats
+    // right here, the optimizer reshapes the loop's accumulator into scalars
+    // and the register allocator starts copying it through AGPRs every group.
+    constexpr int kTS = 136;
+    static_assert(128 * kTS * 4 + 16 <= S * SM::kStage, "score tile fits in the stage buffers");
+    uint32_t* tile = reinterpret_cast<uint32_t*>(smem);
+    lds_barrier();        // all copies have landed (vmcnt 0 above), every wave is past its last read
+#pragma unroll
+    for (int bm = 0; bm < 4; ++bm)
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        tile[(bm * 32 + 8 * (r >> 2) + 4 * h + (r & 3)) * kTS + col] = opaque_vgpr(__float_as_uint(acc[bm][r]));
+    __syncthreads();
+    const int trow = tid >> 1;                 // tile row scored by this thread
+    const int tc0 = (tid & 1) * 64;            // first of its 64 tile columns
     float s = 0.0f;
-    if (nok) {
+    if (m0 + trow < a.M) {
+      const uint16_t* yr = a.Yref + (size_t)(m0 + trow) * a.N + n0 + tc0;
+      const float* tr = reinterpret_cast<const float*>(tile) + trow * kTS + tc0;
+      const int ncols = min(64, a.N - n0 - tc0);     // may be <= 0
+      if (ncols == 64 && (a.N & 7) == 0 && (reinterpret_cast<uintptr_t>(a.Yref) & 15) == 0) {
 #pragma unroll
-      for (int bm = 0; bm < 4; ++bm)
+        for (int c8 = 0; c8 < 8; ++c8) {
+          const uint4 yv = *reinterpret_cast<const uint4*>(yr + 8 * c8);
+          const float4 t0 = *reinterpret_cast<const float4*>(tr + 8 * c8);
+          const float4 t1 = *reinterpret_cast<const float4*>(tr + 8 * c8 + 4);
+          const float tv[8] = {t0.x, t0.y, t0.z, t0.w, t1.x, t1.y, t1.z, t1.w};
+          const uint32_t yw[4] = {yv.x, yv.y, yv.z, yv.w};
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int row = m0 + bm * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
-          if (row < a.M) {
-            const float d = acc[bm][r] - bf16_bits_to_f32(Yref[(size_t)row * a.N + ncol]);
+          for (int e = 0; e < 8; ++e) {
+            const float yf = __uint_as_float((e & 1) ? (yw[e >> 1] & 0xFFFF0000u) : (yw[e >> 1] << 16));
+            const float d = tv[e] - yf;
             s = fmaf(d, d, s);
           }
         }
+      } else {
+        for (int c = 0; c < ncols; ++c) {
+          const float d = tr[c] - bf16_bits_to_f32(yr[c]);
+          s = fmaf(d, d, s);
+        }
+      }
     }
     s = wave_sum(s);
-    // all copies have completed (vmcnt 0 above) and every wave is past its last
-    // LDS read after this barrier: stage 0 is free
-    float* sRed = reinterpret_cast<float*>(smem);
-    lds_barrier();
+    float* sRed = reinterpret_cast<float*>(smem) + 128 * kTS;
     if (lane == 0) sRed[wave] = s;
     __syncthreads();
     if (tid == 0) {
@@ -453,7 +516,8 @@ __global__ __launch_bounds__(256, 1) void gemm_core_kernel(GemmCoreArgs a) {
 //   c parts (hi, lo, hi, lo, hi); slot 15 and slots of groups >= G are 0;
 //   sct[c][g][n] (n < npad): the scales group-major, 0 for n >= N.
 // When xp is not NULL it also writes X[c] pair-arranged (every 8-channel run as
-// (x0,x4)(x1,x5)(x2,x6)(x3,x7)) into xp[c] ([M][K], same strides as X).
+// (x0,x4)(x1,x5)(x2,x6)(x3,x7)) into xp[c] ([mpad][K], same strides as X; rows
+// M .. mpad-1 zero).
 inline int zterm_kz(int K) { return 16 * (((K >> 7) + 2) / 3); }
 inline int gemm_npad(int N) { return (N + kBN - 1) / kBN * kBN; }
 int launch_zterm_prep(const uint16_t* X, size_t x_stride, int M, int K, int mpad, const uint16_t* scales,

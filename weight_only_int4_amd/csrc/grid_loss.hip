@@ -43,7 +43,7 @@ LossLayout loss_layout(int T, int K, int N, int C, bool need_yref) {
   L.qw = take((size_t)C * N * (K / 8) * 4);
   L.sc = take((size_t)C * N * L.G * 2);
   L.qz = take((size_t)C * N * L.GW * 4);
-  L.xs = take((size_t)C * T * K * 2);
+  L.xs = take((size_t)C * L.mpad * K * 2);
   L.rsx = take((size_t)C * L.mpad * L.kz * 2);
   L.cz = take((size_t)C * N * L.kz * 2);
   L.sct = take((size_t)C * L.G * L.npad * 2);
@@ -54,15 +54,21 @@ LossLayout loss_layout(int T, int K, int N, int C, bool need_yref) {
 
 // Xs[c][t][k] = bf16(X[t][k] / S[c][k]) (IEEE division, round to nearest even),
 // stored pair-arranged for the int4 MFMA path: each 8-channel run as
-// (x0,x4)(x1,x5)(x2,x6)(x3,x7).  Each thread handles 8 consecutive channels of one row.
-__global__ __launch_bounds__(256) void scale_activations_kernel(const uint16_t* X, int T, int K,
+// (x0,x4)(x1,x5)(x2,x6)(x3,x7); Xs[c] has tpad rows, rows T .. tpad-1 zero.
+// Each thread handles 8 consecutive channels of one row.
+__global__ __launch_bounds__(256) void scale_activations_kernel(const uint16_t* X, int T, int tpad, int K,
                                                                 const float* S, uint16_t* Xs) {
   const int c = blockIdx.z;
-  const size_t chunks = (size_t)T * (K / 8);
+  const size_t chunks = (size_t)tpad * (K / 8);
   const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
   if (i >= chunks) return;
   const size_t t = i / (K / 8);
   const int k0 = (int)(i % (K / 8)) * 8;
+  uint4* dst = reinterpret_cast<uint4*>(Xs + (size_t)c * tpad * K + t * K + k0);
+  if ((int)t >= T) {
+    *dst = make_uint4(0u, 0u, 0u, 0u);
+    return;
+  }
   const uint4 v = *reinterpret_cast<const uint4*>(X + t * K + k0);
   const float4 s0 = *reinterpret_cast<const float4*>(S + (size_t)c * K + k0);
   const float4 s1 = *reinterpret_cast<const float4*>(S + (size_t)c * K + k0 + 4);
@@ -77,7 +83,7 @@ __global__ __launch_bounds__(256) void scale_activations_kernel(const uint16_t* 
   }
   uint32_t e[4];
   pair_activations(o, e);
-  *reinterpret_cast<uint4*>(Xs + (size_t)c * T * K + t * K + k0) = make_uint4(e[0], e[1], e[2], e[3]);
+  *dst = make_uint4(e[0], e[1], e[2], e[3]);
 }
 
 // losses[c] = sum_tiles partials[c][tile] (fp64, tile order) / (T N); one wave per c,
@@ -125,8 +131,8 @@ int launch_grid_loss(const uint16_t* X, int T, int K, int N, const uint16_t* W, 
                      const float* S, const float* ratios, int C, int symmetric, float* losses,
                      void* workspace, hipStream_t stream) {
   if (C == 0) return W4_OK;
-  // 32-bit per-lane byte offsets in the MFMA core: 2 T K and 2 N K (bf16 reference weights) below 2^32
-  if ((long long)T * K >= (1LL << 31) || (long long)N * K >= (1LL << 31)) return W4_ERR_SHAPE;
+  // 32-bit per-lane byte offsets in the MFMA core: 2 tpad K and 2 N K (bf16 reference weights) below 2^32
+  if (((long long)T + kBM) * K >= (1LL << 31) || (long long)N * K >= (1LL << 31)) return W4_ERR_SHAPE;
   const LossLayout L = loss_layout(T, K, N, C, Yref == nullptr);
   char* ws = static_cast<char*>(workspace);
   const dim3 tile_grid((unsigned)L.tiles, 1, 1);
@@ -166,18 +172,18 @@ int launch_grid_loss(const uint16_t* X, int T, int K, int N, const uint16_t* W, 
   int st = launch_quantize_pack(q, C, stream);
   if (st != W4_OK) return st;
 
-  const size_t chunks = (size_t)T * (K / 8);
+  const size_t chunks = (size_t)L.mpad * (K / 8);
   hipLaunchKernelGGL(scale_activations_kernel, dim3((unsigned)((chunks + 255) / 256), 1, (unsigned)C), dim3(256), 0,
-                     stream, X, T, K, S, xs);
+                     stream, X, T, L.mpad, K, S, xs);
   W4_CHECK_LAUNCH();
-  st = launch_zterm_prep(xs, (size_t)T * K, T, K, L.mpad, sc, q.sc_stride, symmetric ? nullptr : qz, q.qz_stride,
+  st = launch_zterm_prep(xs, (size_t)L.mpad * K, T, K, L.mpad, sc, q.sc_stride, symmetric ? nullptr : qz, q.qz_stride,
                          symmetric, N, rsx, (size_t)L.mpad * L.kz, cz, (size_t)N * L.kz, sct,
                          (size_t)L.G * L.npad, nullptr, C, stream);
   if (st != W4_OK) return st;
 
   GemmCoreArgs a{};
   a.X = xs;
-  a.x_stride = (size_t)T * K;
+  a.x_stride = (size_t)L.mpad * K;
   a.M = T;
   a.K = K;
   a.N = N;

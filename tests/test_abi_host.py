@@ -90,12 +90,11 @@ def test_gemm_size_query(lib):
     sz = ctypes.c_size_t(0)
     f = lib.w4a16_gemm
     assert f(None, 2048, 2048, 6144, None, None, None, 0, 128, None, None, ctypes.byref(sz), None) == 0
-    # pair-arranged X [M rounded to 128][K] bf16, zero-point operands bf16 [M rounded to
-    # 128][16 ceil(G/3)] and [N][16 ceil(G/3)], scales bf16 [G][N rounded to 128], each
-    # rounded up to 256 bytes
-    assert sz.value == 2048 * 2048 * 2 + 2048 * 96 * 2 + 6144 * 96 * 2 + 16 * 6144 * 2
+    # pair-arranged X [M rounded to 128][K] bf16, per-group row sums bf16 [G][M rounded to
+    # 128][4] and per-group column words u32 [G][N rounded to 128], each rounded up to 256 bytes
+    assert sz.value == 2048 * 2048 * 2 + 16 * 2048 * 8 + 16 * 6144 * 4
     assert f(None, 200, 384, 8, None, None, None, 0, 128, None, None, ctypes.byref(sz), None) == 0
-    need = 256 * 384 * 2 + 256 * 16 * 2 + 256 + 3 * 128 * 2
+    need = 256 * 384 * 2 + 3 * 256 * 8 + 3 * 128 * 4
     assert sz.value == need
     assert f(A, 200, 384, 8, A, A, A, 0, 128, A, None, None, None) == -5
     small = ctypes.c_size_t(need - 1)

@@ -23,20 +23,19 @@
 //     prologue kernel);
 //   * packed words: 128 columns x 16 words (8 KB); inside a column's 64 bytes the
 //     16-byte chunk c is stored at position c ^ ((col >> 2) & 3);
-//   * scales of the group: 128 bf16, one copy per wave (the prologue writes them
-//     group-major, zero past N).
+//   * per column of the group: scale bits | bf16(128 + z) << 16 (the prologue
+//     writes them group-major, zero past N), each wave its own 32 columns;
+//   * per row of the group: the negated row sum of the group's activations as
+//     three bf16 parts (hi, mid, lo, exact) and a zero.
 // Each lane's weight operand for one MFMA is one packed uint32 word (8
 // consecutive channels of its output column), expanded in registers to bf16
-// integers 128 + q.  The 8 MFMAs of a group accumulate exact integer-weight
-// products sum_k x (128 + q) into a per-group fp32 tile, folded into the output
-// accumulator with one FMA, acc += sc * tmp, block by block between the first
-// MFMAs of the next group (so the matrix cores do not drain at group
-// boundaries).  The zero-point term
-// -sum_g rowsum_g(X)[m] * sc[n,g] (128 + z[n,g]) is a small contraction over
-// groups, also done on the MFMA, once per tile after the main loop: the prologue
-// writes rowsum_g(X) as three bf16 parts (hi + mid + lo, exact) and -sc (128 + z)
-// as two (exact: it has at most 16 significant bits) into 16-slot rows, 5
-// products per group, 3 groups per K=16 step.
+// integers 128 + q.  Per group the MFMAs first put the zero-point term
+// -rowsum_g(X)[m] (128 + z[n,g]) into a per-group fp32 tile (one K=16 step with 3
+// live k-slots: hi, mid, lo times 128 + z, all products exact), then accumulate
+// the exact integer-weight products sum_k x (128 + q) on top: the tile holds
+// sum_k x (q - z).  It is folded into the output accumulator with one FMA,
+// acc += sc * tmp, block by block between the first MFMAs of the next group (so
+// the matrix cores do not drain at group boundaries).
 // The k-slots of the MFMA are assigned so that lane half h, step j covers
 // channels 64h + 8j .. 64h + 8j + 7 of the group: each lane's 8 words of a group
 // are contiguous.
@@ -61,14 +60,11 @@ struct GemmCoreArgs {
   // int4 weights
   const uint32_t* qweight; // [N][K/8] (+ z * qw_stride)
   size_t qw_stride;
-  const uint16_t* sct;     // [K/128][npad] bf16 scales, group-major, 0 for columns >= N (+ z * sct_stride)
-  size_t sct_stride;
-  int npad;                // N rounded up to 128
-  const uint16_t* rsx;     // [mpad][kz] bf16 split group row sums of X (+ z * rsx_stride)
-  size_t rsx_stride;
-  const uint16_t* cz;      // [N][kz] bf16 split -sc (128 + z) (+ z * cz_stride)
-  size_t cz_stride;
-  int kz;                  // 16 * ceil(G / 3)
+  const uint16_t* rsq;     // [K/128][mpad][4] bf16: -(group row sum of X) as hi, mid, lo, 0 (+ z * rsq_stride)
+  size_t rsq_stride;
+  const uint32_t* szq;     // [K/128][npad]: scale bits | bf16(128 + z) << 16, 0 for columns >= N (+ z * szq_stride)
+  size_t szq_stride;
+  int mpad, npad;          // M and N rounded up to 128
   // bf16 weights (reference path)
   const uint16_t* W;       // [N][K]
   // epilogue
@@ -126,12 +122,13 @@ template <bool INT4>
 struct GemmSmem {
   static constexpr int kA = 0;                                   // activations, 32 KB
   static constexpr int kB = kBM * 256;                           // int4: packed words 8 KB; bf16: weights 32 KB
-  static constexpr int kS = kB + (INT4 ? kBN * 64 : kBN * 256);  // int4: scales, 4 waves x 256 B
-  static constexpr int kStage = kS + (INT4 ? 1024 : 0);
+  static constexpr int kS = kB + (INT4 ? kBN * 64 : kBN * 256);  // int4: column words, 4 waves x 256 B
+  static constexpr int kR = kS + (INT4 ? 1024 : 0);               // int4: row sums, 128 x 8 B
+  static constexpr int kStage = kR + (INT4 ? 1024 : 0);
   static constexpr int kStages = INT4 ? 3 : 2;
-  // copies issued per stage and wave: activations 8 (+ int4: words 2, scales 1;
-  // bf16: weights 8)
-  static constexpr int kCopies = INT4 ? 11 : 16;
+  // copies issued per stage and wave: activations 8 (+ int4: words 2, column
+  // words 1, row sums 1; bf16: weights 8)
+  static constexpr int kCopies = INT4 ? 12 : 16;
   static_assert(kStage * kStages <= 160 * 1024, "LDS");
 };
 
@@ -152,7 +149,6 @@ __global__ __launch_bounds__(256, 1) void gemm_core_kernel(GemmCoreArgs a) {
   const int m0 = tm * kBM, n0 = tn * kBN;
   const int zc_idx = blockIdx.z;
   const int G = a.K >> 7;
-  const int T3 = (G + 2) / 3;
   const uint32_t smem_base = (uint32_t)(uintptr_t)smem;   // LDS byte address (low half of the generic one)
 
   // ---- copy sources: wave-uniform bases (without the group term) and per-lane byte offsets ----
@@ -198,27 +194,35 @@ __global__ __launch_bounds__(256, 1) void gemm_core_kernel(GemmCoreArgs a) {
     for (int i = 0; i < 8; ++i)
       woff[i] = ((uint32_t)min(n0 + arow + 16 * i, a.N - 1) * (uint32_t)a.K + achunk) * 2u;
   }
-  const unsigned char* sbase = nullptr;
+  // column words: wave w copies those of its columns 32 w .. +31 (lanes 32-63
+  // repeat lanes 0-31) into its own 256-byte slot; row sums: wave w copies rows
+  // 32 w .. +31 (8 bytes each, 4 per lane)
+  const unsigned char* szbase = nullptr;
+  const unsigned char* rsbase = nullptr;
   if constexpr (INT4) {
-    // scales: 128 bf16 of the tile's columns, 4 bytes per lane
-    sbase = reinterpret_cast<const unsigned char*>(a.sct + (size_t)zc_idx * a.sct_stride + n0);
+    szbase = reinterpret_cast<const unsigned char*>(a.szq + (size_t)zc_idx * a.szq_stride + n0 + 32 * wave);
+    rsbase = reinterpret_cast<const unsigned char*>(a.rsq + (size_t)zc_idx * a.rsq_stride + (size_t)(m0 + 32 * wave) * 4);
   }
+  const uint32_t szoff = 4u * (uint32_t)(lane & 31);
 
   // Sources of one group's copies: wave-uniform base addresses.
   struct GroupSrc {
     const unsigned char* a;   // activations
     const unsigned char* w;   // packed words (int4) / weights (bf16)
-    const unsigned char* s;   // scales (int4)
+    const unsigned char* sz;  // column words (int4)
+    const unsigned char* rs;  // row sums (int4)
   };
   auto group_src = [&](int g) {
     GroupSrc r;
     r.a = abase + (size_t)g * 256;
     r.w = wbase + (size_t)g * (INT4 ? 64 : 256);
-    r.s = INT4 ? sbase + (size_t)g * a.npad * 2 : nullptr;
+    r.sz = INT4 ? szbase + (size_t)g * a.npad * 4 : nullptr;
+    r.rs = INT4 ? rsbase + (size_t)g * a.mpad * 8 : nullptr;
     return r;
   };
   // copy k (0 .. L-1) of a group into the stage at LDS byte address st.  int4: 0-7
-  // activations, 8-9 packed words, 10 scales; bf16: 0-7 activations, 8-15 weights.
+  // activations, 8-9 packed words, 10 column words, 11 row sums; bf16: 0-7
+  // activations, 8-15 weights.
   auto copy_piece = [&](auto kidx, const GroupSrc& src, uint32_t st) {
     constexpr int k = decltype(kidx)::value;
     if constexpr (k < 8) {
@@ -229,8 +233,10 @@ __global__ __launch_bounds__(256, 1) void gemm_core_kernel(GemmCoreArgs a) {
     } else if constexpr (INT4) {
       if constexpr (k < 10)
         lds_copy16(woff[k - 8], src.w, st + SM::kB + (2 * wave + k - 8) * 1024);
+      else if constexpr (k == 10)
+        lds_copy4(szoff, src.sz, st + SM::kS + wave * 256);
       else
-        lds_copy4(4u * (uint32_t)lane, src.s, st + SM::kS + wave * 256);
+        lds_copy4(4u * (uint32_t)lane, src.rs, st + SM::kR + wave * 256);
     } else {
       lds_copy16(woff[k - 8], src.w, st + SM::kB + (wave + 4 * (k - 8)) * 1024);
     }
@@ -288,6 +294,18 @@ __global__ __launch_bounds__(256, 1) void gemm_core_kernel(GemmCoreArgs a) {
 #pragma unroll
       for (int c = 0; c < 2; ++c)
         wv[c] = *reinterpret_cast<const uint4*>(sb + col * 64 + (((2 * h + c) ^ ((col >> 2) & 3)) * 16));
+      // zero-point step operands: k-slots 0..2 (lane half 0) hold the row sum parts
+      // against 128 + z three times; every other slot is 0
+      const uint32_t szw = reinterpret_cast<const uint32_t*>(st + SM::kS + wave * 256)[l32];
+      const float sc_cur = __uint_as_float(szw << 16);
+      const uint32_t zbf = szw >> 16;
+      const bf16x8 zb = __builtin_bit_cast(bf16x8, make_uint4(h ? 0u : zbf * 0x10001u, h ? 0u : zbf, 0u, 0u));
+      bf16x8 za[4];
+#pragma unroll
+      for (int bm = 0; bm < 4; ++bm) {
+        const uint2 rv = *reinterpret_cast<const uint2*>(st + SM::kR + (bm * 32 + l32) * 8);
+        za[bm] = __builtin_bit_cast(bf16x8, make_uint4(h ? 0u : rv.x, h ? 0u : rv.y, 0u, 0u));
+      }
       __builtin_amdgcn_sched_barrier(0);
       auto step = [&](auto jidx) {
         constexpr int j = decltype(jidx)::value;
@@ -304,18 +322,21 @@ __global__ __launch_bounds__(256, 1) void gemm_core_kernel(GemmCoreArgs a) {
         const bf16x8 bf = __builtin_bit_cast(
             bf16x8, make_uint4(nibble_pair_m(word, 0, nib_mask), nibble_pair_m(word, 1, nib_mask),
                                nibble_pair_m(word, 2, nib_mask), nibble_pair_m(word, 3, nib_mask)));
+        if constexpr (j == 0) {
 #pragma unroll
-        for (int bm = 0; bm < 4; ++bm) {
-          if constexpr (j == 0) {
+          for (int bm = 0; bm < 4; ++bm) {
             // fold the previous group's block first: acc += sc_prev * tmp (fenced
-            // from the MFMA that overwrites tmp, so both never need registers at once)
+            // from the MFMA that overwrites tmp, so both never need registers at
+            // once), then start this group's block with its zero-point term
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[bm][r] = fmaf(sc_prev, tmp[bm][r], acc[bm][r]);
             __builtin_amdgcn_sched_barrier(0);
-            tmp[bm] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[0][bm], bf, f32x16{}, 0, 0, 0);
-          } else
-            tmp[bm] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[j & 1][bm], bf, tmp[bm], 0, 0, 0);
+            tmp[bm] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(za[bm], zb, f32x16{}, 0, 0, 0);
+          }
         }
+#pragma unroll
+        for (int bm = 0; bm < 4; ++bm)
+          tmp[bm] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[j & 1][bm], bf, tmp[bm], 0, 0, 0);
         __builtin_amdgcn_sched_barrier(0);
       };
       step(std::integral_constant<int, 0>{});
@@ -326,9 +347,9 @@ __global__ __launch_bounds__(256, 1) void gemm_core_kernel(GemmCoreArgs a) {
       step(std::integral_constant<int, 5>{});
       step(std::integral_constant<int, 6>{});
       step(std::integral_constant<int, 7>{});
-      // this group's scale (columns past N have 0), read before the stage can be
-      // overwritten; its fold happens in step 0 of the next group (or after the loop)
-      sc_prev = bf16_bits_to_f32(reinterpret_cast<const uint16_t*>(st + SM::kS + wave * 256)[col]);
+      // this group's scale (columns past N have 0); its fold happens in step 0 of
+      // the next group (or after the loop)
+      sc_prev = sc_cur;
     } else {
       bf16x8 bfc = frag(sb, wave, 0), bfn = bfc;
       __builtin_amdgcn_sched_barrier(0);
@@ -406,36 +427,6 @@ __global__ __launch_bounds__(256, 1) void gemm_core_kernel(GemmCoreArgs a) {
     for (int bm = 0; bm < 4; ++bm)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[bm][r] = fmaf(sc_prev, tmp[bm][r], acc[bm][r]);
-
-    // zero-point term: ceil(G/3) K=16 steps over the split operands, read straight
-    // from global memory one step ahead, accumulated in tmp (free now), then added
-    const uint16_t* zr = a.rsx + (size_t)zc_idx * a.rsx_stride + (size_t)(m0 + l32) * a.kz + 8 * h;
-    const uint16_t* zcl = a.cz + (size_t)zc_idx * a.cz_stride + (size_t)min(n0 + col, a.N - 1) * a.kz + 8 * h;
-    const size_t zrow32 = (size_t)32 * a.kz;
-    bf16x8 za[2][4], zb[2];
-    auto zload = [&](int t, int b) {
-      zb[b] = *reinterpret_cast<const bf16x8*>(zcl + 16 * t);
-#pragma unroll
-      for (int bm = 0; bm < 4; ++bm) za[b][bm] = *reinterpret_cast<const bf16x8*>(zr + bm * zrow32 + 16 * t);
-    };
-    auto zstep = [&](int b, bool first) {
-#pragma unroll
-      for (int bm = 0; bm < 4; ++bm)
-        tmp[bm] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(za[b][bm], zb[b], first ? f32x16{} : tmp[bm], 0, 0, 0);
-    };
-    zload(0, 0);
-    for (int t = 0; t < T3; t += 2) {
-      if (t + 1 < T3) zload(t + 1, 1);
-      zstep(0, t == 0);
-      if (t + 1 < T3) {
-        if (t + 2 < T3) zload(t + 2, 0);
-        zstep(1, false);
-      }
-    }
-#pragma unroll
-    for (int bm = 0; bm < 4; ++bm)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[bm][r] += tmp[bm][r];
   }
 
   // epilogue.  Output layout of a 32x32 block: lane holds column l32 and rows
@@ -509,20 +500,19 @@ __global__ __launch_bounds__(256, 1) void gemm_core_kernel(GemmCoreArgs a) {
   }
 }
 
-// Operands written by the prologue kernel (defined in gemm.hip), for C problems:
-//   rsx[c][m][16t + s] (m < mpad; rows >= M are 0): group row sums of X[c] split
-//   into bf16 parts, cz[c][n][16t + s]: -sc (128 + z) split into bf16 parts, with
-//   slot s = 5j + u for group 3t + j: rs parts (hi, hi, mid, mid, lo) against
-//   c parts (hi, lo, hi, lo, hi); slot 15 and slots of groups >= G are 0;
-//   sct[c][g][n] (n < npad): the scales group-major, 0 for n >= N.
+// Operands written by the prologue kernel (defined in gemm.hip), for C problems
+// (c = blockIdx.z of the core):
+//   rsq[c][g][m][0..3] (m < mpad): -(sum of X[c][m][128 g .. 128 g + 127]) as the
+//   bf16 parts hi, mid, lo (exact) and 0; 0 for rows >= M;
+//   szq[c][g][n] (n < npad): scale bits | bf16(128 + z) << 16 (z = 8 when
+//   symmetric); 0 for columns >= N.
 // When xp is not NULL it also writes X[c] pair-arranged (every 8-channel run as
 // (x0,x4)(x1,x5)(x2,x6)(x3,x7)) into xp[c] ([mpad][K], same strides as X; rows
 // M .. mpad-1 zero).
-inline int zterm_kz(int K) { return 16 * (((K >> 7) + 2) / 3); }
-inline int gemm_npad(int N) { return (N + kBN - 1) / kBN * kBN; }
-int launch_zterm_prep(const uint16_t* X, size_t x_stride, int M, int K, int mpad, const uint16_t* scales,
-                      size_t sc_stride, const uint32_t* qzeros, size_t qz_stride, int symmetric, int N,
-                      uint16_t* rsx, size_t rsx_stride, uint16_t* cz, size_t cz_stride, uint16_t* sct,
-                      size_t sct_stride, uint16_t* xp, int C, hipStream_t stream);
+__host__ __device__ inline int gemm_npad(int N) { return (N + kBN - 1) / kBN * kBN; }
+int launch_gemm_prep(const uint16_t* X, size_t x_stride, int M, int K, int mpad, const uint16_t* scales,
+                     size_t sc_stride, const uint32_t* qzeros, size_t qz_stride, int symmetric, int N,
+                     uint16_t* rsq, size_t rsq_stride, uint32_t* szq, size_t szq_stride, uint16_t* xp, int C,
+                     hipStream_t stream);
 
 }  // namespace w4

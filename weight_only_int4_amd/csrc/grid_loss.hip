@@ -21,8 +21,8 @@ namespace w4 {
 namespace {
 
 struct LossLayout {
-  size_t yref, qw, sc, qz, xs, rsx, cz, sct, part, total;
-  int mpad, npad, G, GW, kz, tiles;
+  size_t yref, qw, sc, qz, xs, rsq, szq, part, total;
+  int mpad, npad, G, GW, tiles;
 };
 
 LossLayout loss_layout(int T, int K, int N, int C, bool need_yref) {
@@ -31,7 +31,6 @@ LossLayout loss_layout(int T, int K, int N, int C, bool need_yref) {
   L.GW = (L.G + 7) / 8;
   L.mpad = (int)align_up((size_t)T, kBM);
   L.npad = gemm_npad(N);
-  L.kz = zterm_kz(K);
   L.tiles = ((N + kBN - 1) / kBN) * ((T + kBM - 1) / kBM);
   size_t off = 0;
   auto take = [&](size_t bytes) {
@@ -44,9 +43,8 @@ LossLayout loss_layout(int T, int K, int N, int C, bool need_yref) {
   L.sc = take((size_t)C * N * L.G * 2);
   L.qz = take((size_t)C * N * L.GW * 4);
   L.xs = take((size_t)C * L.mpad * K * 2);
-  L.rsx = take((size_t)C * L.mpad * L.kz * 2);
-  L.cz = take((size_t)C * N * L.kz * 2);
-  L.sct = take((size_t)C * L.G * L.npad * 2);
+  L.rsq = take((size_t)C * L.G * L.mpad * 8);
+  L.szq = take((size_t)C * L.G * L.npad * 4);
   L.part = take((size_t)C * L.tiles * 4);
   L.total = off;
   return L;
@@ -149,9 +147,8 @@ int launch_grid_loss(const uint16_t* X, int T, int K, int N, const uint16_t* W, 
   uint16_t* sc = reinterpret_cast<uint16_t*>(ws + L.sc);
   uint32_t* qz = reinterpret_cast<uint32_t*>(ws + L.qz);
   uint16_t* xs = reinterpret_cast<uint16_t*>(ws + L.xs);
-  uint16_t* rsx = reinterpret_cast<uint16_t*>(ws + L.rsx);
-  uint16_t* cz = reinterpret_cast<uint16_t*>(ws + L.cz);
-  uint16_t* sct = reinterpret_cast<uint16_t*>(ws + L.sct);
+  uint16_t* rsq = reinterpret_cast<uint16_t*>(ws + L.rsq);
+  uint32_t* szq = reinterpret_cast<uint32_t*>(ws + L.szq);
   float* part = reinterpret_cast<float*>(ws + L.part);
 
   QuantArgs q{};
@@ -176,9 +173,9 @@ int launch_grid_loss(const uint16_t* X, int T, int K, int N, const uint16_t* W, 
   hipLaunchKernelGGL(scale_activations_kernel, dim3((unsigned)((chunks + 255) / 256), 1, (unsigned)C), dim3(256), 0,
                      stream, X, T, L.mpad, K, S, xs);
   W4_CHECK_LAUNCH();
-  st = launch_zterm_prep(xs, (size_t)L.mpad * K, T, K, L.mpad, sc, q.sc_stride, symmetric ? nullptr : qz, q.qz_stride,
-                         symmetric, N, rsx, (size_t)L.mpad * L.kz, cz, (size_t)N * L.kz, sct,
-                         (size_t)L.G * L.npad, nullptr, C, stream);
+  st = launch_gemm_prep(xs, (size_t)L.mpad * K, T, K, L.mpad, sc, q.sc_stride, symmetric ? nullptr : qz,
+                        q.qz_stride, symmetric, N, rsq, (size_t)L.G * L.mpad * 4, szq, (size_t)L.G * L.npad, nullptr,
+                        C, stream);
   if (st != W4_OK) return st;
 
   GemmCoreArgs a{};
@@ -189,14 +186,12 @@ int launch_grid_loss(const uint16_t* X, int T, int K, int N, const uint16_t* W, 
   a.N = N;
   a.qweight = qw;
   a.qw_stride = q.qw_stride;
-  a.sct = sct;
-  a.sct_stride = (size_t)L.G * L.npad;
+  a.rsq = rsq;
+  a.rsq_stride = (size_t)L.G * L.mpad * 4;
+  a.szq = szq;
+  a.szq_stride = (size_t)L.G * L.npad;
+  a.mpad = L.mpad;
   a.npad = L.npad;
-  a.rsx = rsx;
-  a.rsx_stride = (size_t)L.mpad * L.kz;
-  a.cz = cz;
-  a.cz_stride = (size_t)N * L.kz;
-  a.kz = L.kz;
   a.Yref = Yref;
   a.partials = part;
   dim3 grid = tile_grid;

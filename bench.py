@@ -26,8 +26,10 @@ All inputs are seeded synthetic tensors (``workloads``).
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -103,6 +105,24 @@ def time_events(torch, fn, iters):
     e.record()
     e.synchronize()
     return s.elapsed_time(e) / iters
+
+
+def profiled_traffic():
+    """HBM bytes per GEMV launch of the decode sweep as measured by rocprofv3 (FETCH_SIZE and
+    WRITE_SIZE, scaled by a plain-copy calibration) in profiles/gemv_decode_sweep_M1.md, or
+    None when the GEMV sources have changed since that profile was taken."""
+    try:
+        text = open(os.path.join(ROOT, "profiles", "gemv_decode_sweep_M1.md")).read()
+        vals = dict(re.findall(r"^(\w+): (\S+)$", text, flags=re.M))
+        h = hashlib.sha256()
+        for f in ("gemv.hip", "common.hpp", "internal.hpp"):
+            with open(os.path.join(ROOT, "weight_only_int4_amd", "csrc", f), "rb") as fh:
+                h.update(fh.read())
+        if vals.get("gemv_source_sha256_16") != h.hexdigest()[:16]:
+            return None
+        return int(vals["traffic_bytes_per_launch"])
+    except (OSError, KeyError, ValueError):
+        return None
 
 
 # ----------------------------------------------------------------------------- workloads
@@ -315,6 +335,8 @@ def main(argv=None):
     ap.add_argument("--blocks", type=int, default=28)
     ap.add_argument("--skip-step", action="store_true",
                     help="profiling aid: skip the decode-sweep step (value is null) and run only --only rows")
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
+                    help="counter calibration: run only a plain device copy of MIB MiB ten times and exit")
     args = ap.parse_args(argv)
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (the kernels shard by output rows "
@@ -330,6 +352,16 @@ def main(argv=None):
         print("bench.py needs a GPU", file=sys.stderr)
         return 2
     torch.cuda.set_device(0)
+    if args.copy_probe:
+        # a plain copy of known size: reads and writes copy_probe MiB per dispatch, so
+        # the HBM counters of a profiler run over it calibrate FETCH_SIZE / WRITE_SIZE
+        src = torch.ones(args.copy_probe << 18, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(10):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_probe_bytes": src.numel() * 4, "dispatches": 10}), flush=True)
+        return 0
     w4.load_library()
 
     out = {
@@ -382,7 +414,7 @@ def main(argv=None):
                               "eager_ms_per_step": round(eager_ms, 5)})
         out["roofline"] = {"kernel": "gemv_kernel<M=1>", "bound": "hbm", "achieved": round(achieved, 1),
                            "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                           "traffic": None, "avg_launch_us": round(avg_launch_ms * 1e3, 3),
+                           "traffic": profiled_traffic(), "avg_launch_us": round(avg_launch_ms * 1e3, 3),
                            "bytes_per_launch": int(avg_bytes)}
         del graph, sweep
         torch.cuda.synchronize()

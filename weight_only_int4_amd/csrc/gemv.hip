@@ -89,7 +89,8 @@ struct WordVec<1> {
 template <int M, int WPL, int R>
 struct GemvBatch {
   uint32_t w[R][WPL];
-  uint32_t scb[R], zw[R];
+  uint16_t scb[R];      // kept 16-bit: widening at the load would wait for it right there
+  uint32_t zw[R];
 };
 
 template <int M, int WPL, int R>
@@ -100,7 +101,11 @@ __device__ __forceinline__ void gemv_load_batch(const GemvArgs& a, int b, int wb
     const int n = min(b * R + r, a.N - 1);
     WordVec<WPL>::load(a.qweight + (size_t)n * words + wb, B.w[r]);
     B.scb[r] = a.scales[(size_t)n * G + g];
-    B.zw[r] = a.symmetric ? 0u : a.qzeros[(size_t)n * GW + (g >> 3)];
+    // branch-free: symmetric weights read (and ignore) the first scale word, so
+    // every batch issues the same loads and the waits on them stay exact
+    const uint32_t* zp = a.symmetric ? reinterpret_cast<const uint32_t*>(a.scales)
+                                     : a.qzeros + (size_t)n * GW + (g >> 3);
+    B.zw[r] = *zp;
   }
 }
 
@@ -128,8 +133,19 @@ __global__ __launch_bounds__(gemv_max_waves(M) * 64) void gemv_kernel(GemvArgs a
   const int nb = (a.N + R - 1) / R;
   int b = blockIdx.x;
 
+  // Every load of the prologue -- this lane's activations, then the first batch --
+  // is issued before anything waits for one (the scheduling fence keeps the
+  // compiler from sinking each load next to its use, which would cost one memory
+  // round trip per load).
+  uint4 xr[M][WPL];
+#pragma unroll
+  for (int m = 0; m < M; ++m)
+#pragma unroll
+    for (int i = 0; i < WPL; ++i)
+      xr[m][i] = *reinterpret_cast<const uint4*>(a.X + (size_t)m * a.K + (size_t)(wb + i) * 8);
   GemvBatch<M, WPL, R> B0, B1;
   gemv_load_batch(a, b, wb, g, words, G, GW, B0);
+  __builtin_amdgcn_sched_barrier(0);
 
   // this lane's activations as (x_j, x_j+4) bf16 pairs, and their fp32 sums
   uint32_t xp[M][WPL][4];
@@ -139,7 +155,7 @@ __global__ __launch_bounds__(gemv_max_waves(M) * 64) void gemv_kernel(GemvArgs a
     xs[m] = 0.0f;
 #pragma unroll
     for (int i = 0; i < WPL; ++i) {
-      const uint4 v = *reinterpret_cast<const uint4*>(a.X + (size_t)m * a.K + (size_t)(wb + i) * 8);
+      const uint4 v = xr[m][i];
       uint32_t d[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
       for (int q = 0; q < 4; ++q) d[q] = active ? d[q] : 0u;
@@ -205,12 +221,18 @@ __global__ __launch_bounds__(gemv_max_waves(M) * 64) void gemv_kernel(GemvArgs a
   };
 
   const int step = gridDim.x;
+  // The next batch's loads are issued (and fenced) before the current batch is
+  // computed.  They are issued unconditionally (past the last batch they repeat
+  // it): with a branch around them the compiler can no longer count which loads
+  // are outstanding and waits for all of them before computing.
   while (b < nb) {
-    if (b + step < nb) gemv_load_batch(a, b + step, wb, g, words, G, GW, B1);
+    gemv_load_batch(a, min(b + step, nb - 1), wb, g, words, G, GW, B1);
+    __builtin_amdgcn_sched_barrier(0);
     process(B0, b, 0);
     b += step;
     if (b >= nb) break;
-    if (b + step < nb) gemv_load_batch(a, b + step, wb, g, words, G, GW, B0);
+    gemv_load_batch(a, min(b + step, nb - 1), wb, g, words, G, GW, B0);
+    __builtin_amdgcn_sched_barrier(0);
     process(B1, b, 1);
     b += step;
   }

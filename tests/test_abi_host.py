@@ -90,8 +90,8 @@ def test_gemm_size_query(lib):
     sz = ctypes.c_size_t(0)
     f = lib.w4a16_gemm
     assert f(None, 2048, 2048, 6144, None, None, None, 0, 128, None, None, ctypes.byref(sz), None) == 0
-    # pair-arranged X [M rounded to 128][K] bf16, per-group row sums bf16 [G][M rounded to
-    # 128][4] and per-group column words u32 [G][N rounded to 128], each rounded up to 256 bytes
+    # pair-arranged X [M rounded to 64][K] bf16, per-group row sums bf16 [G][M rounded to
+    # 64][4] and per-group column words u32 [G][N rounded to 128], each rounded up to 256 bytes
     assert sz.value == 2048 * 2048 * 2 + 16 * 2048 * 8 + 16 * 6144 * 4
     assert f(None, 200, 384, 8, None, None, None, 0, 128, None, None, ctypes.byref(sz), None) == 0
     need = 256 * 384 * 2 + 3 * 256 * 8 + 3 * 128 * 4

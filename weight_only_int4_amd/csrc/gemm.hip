@@ -151,7 +151,7 @@ int launch_gemm(const uint16_t* X, int M, int K, int N, const uint32_t* qweight,
   const long long tiles = (long long)((N + kBN - 1) / kBN) * ((M + kBM - 1) / kBM);
   if (tiles > 0x7FFFFFFFLL) return W4_ERR_SHAPE;
   const dim3 grid((unsigned)tiles, 1, 1);
-  hipLaunchKernelGGL((gemm_core_kernel<true, EPI_STORE>), grid, dim3(256), 0, stream, a);
+  hipLaunchKernelGGL((gemm_core_kernel<true, EPI_STORE>), grid, dim3(kGemmWaves * 64), 0, stream, a);
   W4_CHECK_LAUNCH();
   return W4_OK;
 }

@@ -2,10 +2,11 @@
 // grid loss.  Y = X W_hat^T with X bf16 [M][K] and W_hat given either as packed
 // int4 groups (q - z) * sc or, for the unquantized reference, as bf16 [N][K].
 //
-// Workgroup tile 128 x 128, 4 waves side by side: wave w computes all 128 rows
-// of columns 32 w .. 32 w + 31 as 4 v_mfma_f32_32x32x16_bf16 blocks, so every
-// packed weight word is expanded by exactly one wave.  One main-loop step covers
-// one 128-channel quantization group.
+// Workgroup tile 64 x 128, 4 waves: wave w computes all 64 rows of columns
+// 32 w .. +31 as 2 v_mfma_f32_32x32x16_bf16 blocks, so every packed weight word is
+// expanded once per tile.  Two workgroups share a CU (75 KB of LDS each): while
+// one waits at its per-group barrier the other keeps the matrix cores busy.  One
+// main-loop step covers one 128-channel quantization group.
 //
 // Every operand of a group travels from global memory straight into LDS
 // (global_load_lds: no registers), STAGES groups deep.  These copies are issued
@@ -16,7 +17,7 @@
 // issue order), then synchronises the workgroup with a bare s_barrier.
 //
 // Per stage (int4 weights):
-//   * activations: 128 rows x 128 channels bf16 (32 KB); inside a 256-byte row
+//   * activations: 64 rows x 128 channels bf16 (16 KB); inside a 256-byte row
 //     the 16-byte chunk c is stored at position c ^ (row & 15).  They arrive
 //     pre-arranged: every 8-channel run holds the pairs (x0,x4)(x1,x5)(x2,x6)
 //     (x3,x7), the order in which one packed word expands (written so by the
@@ -24,7 +25,7 @@
 //   * packed words: 128 columns x 16 words (8 KB); inside a column's 64 bytes the
 //     16-byte chunk c is stored at position c ^ ((col >> 2) & 3);
 //   * per column of the group: scale bits | bf16(128 + z) << 16 (the prologue
-//     writes them group-major, zero past N), each wave its own 32 columns;
+//     writes them group-major, zero past N);
 //   * per row of the group: the negated row sum of the group's activations as
 //     three bf16 parts (hi, mid, lo, exact) and a zero.
 // Each lane's weight operand for one MFMA is one packed uint32 word (8
@@ -47,7 +48,7 @@
 
 namespace w4 {
 
-constexpr int kBM = 128;
+constexpr int kBM = 64;
 constexpr int kBN = 128;
 
 enum { EPI_STORE = 0, EPI_SQDIFF = 1 };
@@ -120,20 +121,24 @@ __device__ __forceinline__ void lds_barrier() {
 // LDS byte layout of one pipeline stage.
 template <bool INT4>
 struct GemmSmem {
-  static constexpr int kA = 0;                                   // activations, 32 KB
+  static constexpr int kA = 0;                                   // activations, 16 KB
   static constexpr int kB = kBM * 256;                           // int4: packed words 8 KB; bf16: weights 32 KB
-  static constexpr int kS = kB + (INT4 ? kBN * 64 : kBN * 256);  // int4: column words, 4 waves x 256 B
-  static constexpr int kR = kS + (INT4 ? 1024 : 0);               // int4: row sums, 128 x 8 B
-  static constexpr int kStage = kR + (INT4 ? 1024 : 0);
+  static constexpr int kS = kB + (INT4 ? kBN * 64 : kBN * 256);  // int4: column words, 128 x 4 B
+  static constexpr int kR = kS + (INT4 ? 512 : 0);                // int4: row sums, 64 x 8 B
+  static constexpr int kStage = kR + (INT4 ? 512 : 0);
   static constexpr int kStages = INT4 ? 3 : 2;
-  // copies issued per stage and wave: activations 8 (+ int4: words 2, column
-  // words 1, row sums 1; bf16: weights 8)
-  static constexpr int kCopies = INT4 ? 12 : 16;
-  static_assert(kStage * kStages <= 160 * 1024, "LDS");
+  static constexpr int kBlocksPerCU = INT4 ? 2 : 1;
+  // copies issued per stage and wave (each moves 1 KB, or 256 B for the 4-byte
+  // one): activations 4 + int4: packed words 2, column words or row sums 1;
+  // bf16: weights 8
+  static constexpr int kCopies = INT4 ? 7 : 12;
+  static_assert(kStage * kStages * kBlocksPerCU <= 160 * 1024, "LDS");
 };
 
+constexpr int kGemmWaves = 4;
+
 template <bool INT4, int EPI>
-__global__ __launch_bounds__(256, 1) void gemm_core_kernel(GemmCoreArgs a) {
+__global__ __launch_bounds__(kGemmWaves * 64, GemmSmem<INT4>::kBlocksPerCU) void gemm_core_kernel(GemmCoreArgs a) {
   using SM = GemmSmem<INT4>;
   constexpr int S = SM::kStages;
   constexpr int D = S - 1;                 // prefetch distance in groups
@@ -152,29 +157,30 @@ __global__ __launch_bounds__(256, 1) void gemm_core_kernel(GemmCoreArgs a) {
   const uint32_t smem_base = (uint32_t)(uintptr_t)smem;   // LDS byte address (low half of the generic one)
 
   // ---- copy sources: wave-uniform bases (without the group term) and per-lane byte offsets ----
-  // activations: copy i of wave w fills rows 4 (w + 4 i) .. +3; lane -> row
-  // 4 (w + 4 i) + lane / 16, stored chunk lane % 16, which holds logical chunk
-  // (lane % 16) ^ (row & 15); row & 15 = 4 w + lane / 16 for every i.
-  // int4: X has rows up to M rounded to 128 (the prologue pads them), so copy i
-  // is copy 0 moved by 16 rows and one offset serves all eight (< 2 mpad K).
-  // bf16: rows past M read row M-1 (always valid): their finite results are
-  // never stored or scored.
+  // 256-byte-row tiles (activations; bf16 weights): copy i of wave w fills rows
+  // 4 u .. 4 u + 3 with u = w + 4 i; lane -> row 4 u + lane / 16, stored chunk
+  // lane % 16 holding logical chunk (lane % 16) ^ (row & 15), and row & 15 =
+  // 4 w + lane / 16 for every i.  int4: X has rows up to M rounded to 64 (the
+  // prologue pads them), so copy i is copy 0 moved by 16 rows and one offset
+  // serves all four (< 2 mpad K).  bf16: rows past M (columns past N) read the
+  // last valid one: their finite results are never stored or scored.
   const unsigned char* abase = reinterpret_cast<const unsigned char*>(a.X + (size_t)zc_idx * a.x_stride);
   const int arow = 4 * wave + (lane >> 4);
   const uint32_t achunk = (uint32_t)(((lane & 15) ^ (arow & 15)) * 8);
-  uint32_t aoff[INT4 ? 1 : 8];
+  uint32_t aoff[INT4 ? 1 : 4];
   if constexpr (INT4) {
     aoff[0] = ((uint32_t)(m0 + arow) * (uint32_t)a.K + achunk) * 2u;
   } else {
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
+    for (int i = 0; i < 4; ++i)
       aoff[i] = ((uint32_t)min(m0 + arow + 16 * i, a.M - 1) * (uint32_t)a.K + achunk) * 2u;
   }
-  // weights.  int4: copy i (of 8, wave w issues 2w, 2w+1) fills LDS chunks 64 i + lane:
-  // column (64 i + lane) / 4, stored chunk lane % 4, logical chunk (lane % 4) ^ ((col >> 2) & 3)
-  // (LDS serves a 16-byte read 16 lanes at a time over 64 banks: 16 consecutive
-  // columns then hit 16 distinct 16-byte bank groups); offsets < N K / 2.
-  // bf16: like the activations, rows = columns n; offsets < 2 N K.  Columns past N
+  // weights.  int4: copy u (of 2) of wave w fills LDS chunks 64 (2 w + u) + lane:
+  // column (64 (2 w + u) + lane) / 4, stored chunk lane % 4 holding logical chunk
+  // (lane % 4) ^ ((col >> 2) & 3) (LDS serves a 16-byte read 16 lanes at a time
+  // over 64 banks: 16 consecutive columns then hit 16 distinct 16-byte bank
+  // groups); offsets < N K / 2.  bf16: like the activations, 128 rows = columns
+  // n, 8 copies per wave (rows 4 (w + 4 i) ..); offsets < 2 N K.  Columns past N
   // read column N-1.
   const unsigned char* wbase;
   uint32_t woff[INT4 ? 2 : 8];
@@ -194,90 +200,90 @@ __global__ __launch_bounds__(256, 1) void gemm_core_kernel(GemmCoreArgs a) {
     for (int i = 0; i < 8; ++i)
       woff[i] = ((uint32_t)min(n0 + arow + 16 * i, a.N - 1) * (uint32_t)a.K + achunk) * 2u;
   }
-  // column words: wave w copies those of its columns 32 w .. +31 (lanes 32-63
-  // repeat lanes 0-31) into its own 256-byte slot; row sums: wave w copies rows
-  // 32 w .. +31 (8 bytes each, 4 per lane)
-  const unsigned char* szbase = nullptr;
-  const unsigned char* rsbase = nullptr;
+  // int4, 4-byte copies: waves 0, 1 copy the column words of columns 64 w .. +63;
+  // waves 2, 3 copy the row sums of rows 32 (w - 2) .. +31 (8 bytes each, 4 per lane)
+  const unsigned char* mbase = nullptr;
+  uint32_t mdst = 0;
   if constexpr (INT4) {
-    szbase = reinterpret_cast<const unsigned char*>(a.szq + (size_t)zc_idx * a.szq_stride + n0 + 32 * wave);
-    rsbase = reinterpret_cast<const unsigned char*>(a.rsq + (size_t)zc_idx * a.rsq_stride + (size_t)(m0 + 32 * wave) * 4);
+    if (wave < 2) {
+      mbase = reinterpret_cast<const unsigned char*>(a.szq + (size_t)zc_idx * a.szq_stride + n0 + 64 * wave);
+      mdst = SM::kS + wave * 256;
+    } else {
+      mbase = reinterpret_cast<const unsigned char*>(a.rsq + (size_t)zc_idx * a.rsq_stride +
+                                                     (size_t)(m0 + 32 * (wave - 2)) * 4);
+      mdst = SM::kR + (wave - 2) * 256;
+    }
   }
-  const uint32_t szoff = 4u * (uint32_t)(lane & 31);
 
   // Sources of one group's copies: wave-uniform base addresses.
   struct GroupSrc {
     const unsigned char* a;   // activations
     const unsigned char* w;   // packed words (int4) / weights (bf16)
-    const unsigned char* sz;  // column words (int4)
-    const unsigned char* rs;  // row sums (int4)
+    const unsigned char* m;   // row sums or column words (int4)
   };
   auto group_src = [&](int g) {
     GroupSrc r;
     r.a = abase + (size_t)g * 256;
     r.w = wbase + (size_t)g * (INT4 ? 64 : 256);
-    r.sz = INT4 ? szbase + (size_t)g * a.npad * 4 : nullptr;
-    r.rs = INT4 ? rsbase + (size_t)g * a.mpad * 8 : nullptr;
+    r.m = INT4 ? mbase + (size_t)g * (wave < 2 ? (size_t)a.npad * 4 : (size_t)a.mpad * 8) : nullptr;
     return r;
   };
-  // copy k (0 .. L-1) of a group into the stage at LDS byte address st.  int4: 0-7
-  // activations, 8-9 packed words, 10 column words, 11 row sums; bf16: 0-7
-  // activations, 8-15 weights.
+  // copy k (0 .. L-1) of a group into the stage at LDS byte address st.  int4: 0-3
+  // activations, 4-5 packed words, 6 column words / row sums; bf16: 0-3
+  // activations, 4-11 weights.
   auto copy_piece = [&](auto kidx, const GroupSrc& src, uint32_t st) {
     constexpr int k = decltype(kidx)::value;
-    if constexpr (k < 8) {
+    if constexpr (k < 4) {
       if constexpr (INT4)
         lds_copy16(aoff[0], src.a + (size_t)k * 32 * a.K, st + SM::kA + (wave + 4 * k) * 1024);
       else
         lds_copy16(aoff[k], src.a, st + SM::kA + (wave + 4 * k) * 1024);
     } else if constexpr (INT4) {
-      if constexpr (k < 10)
-        lds_copy16(woff[k - 8], src.w, st + SM::kB + (2 * wave + k - 8) * 1024);
-      else if constexpr (k == 10)
-        lds_copy4(szoff, src.sz, st + SM::kS + wave * 256);
+      if constexpr (k < 6)
+        lds_copy16(woff[k - 4], src.w, st + SM::kB + (2 * wave + k - 4) * 1024);
       else
-        lds_copy4(4u * (uint32_t)lane, src.rs, st + SM::kR + wave * 256);
+        lds_copy4(4u * (uint32_t)lane, src.m, st + mdst);
     } else {
-      lds_copy16(woff[k - 8], src.w, st + SM::kB + (wave + 4 * (k - 8)) * 1024);
+      lds_copy16(woff[k - 4], src.w, st + SM::kB + (wave + 4 * (k - 4)) * 1024);
     }
   };
-  // the copies that go with MFMA step j of the group being computed
+  // the copies that go with MFMA step j of the group being computed (bf16: two
+  // per step from step 4 on)
   auto copies_of_step = [&](auto jidx, const GroupSrc& src, uint32_t st) {
     constexpr int j = decltype(jidx)::value;
-    copy_piece(std::integral_constant<int, j>{}, src, st);
-    if constexpr (8 + j < L) copy_piece(std::integral_constant<int, 8 + j>{}, src, st);
+    if constexpr (j < L) copy_piece(std::integral_constant<int, j>{}, src, st);
+    if constexpr (j >= 4 && j + 4 < L) copy_piece(std::integral_constant<int, j + 4>{}, src, st);
   };
 
   // fragment reads of a 256-byte-row tile (activations; bf16 weights): row
-  // 32 bm + l32, logical chunk 8h + j at stored chunk (8h + j) ^ (l32 & 15), i.e.
-  // byte (l32 * 256 + ((8h ^ (l32 & 15)) * 16)) ^ (16 j) + 8192 bm: one XOR per
-  // step, the rest immediate offsets
+  // 32 rb + l32 (rb = 32-row block), logical chunk 8h + j at stored chunk
+  // (8h + j) ^ (l32 & 15), i.e. byte (l32 * 256 + ((8h ^ (l32 & 15)) * 16)) ^ (16 j)
+  // + 8192 rb: one XOR per step, the rest immediate offsets
   const uint32_t fbase = (uint32_t)(l32 * 256 + (((8 * h) ^ (l32 & 15)) * 16));
   uint32_t fb = fbase;
-  auto frag = [&](const unsigned char* tile, int bm, int j) {
-    return *reinterpret_cast<const bf16x8*>(tile + ((fb ^ (uint32_t)(16 * j)) + 8192u * bm));
+  auto frag = [&](const unsigned char* tile, int rb, int j) {
+    return *reinterpret_cast<const bf16x8*>(tile + ((fb ^ (uint32_t)(16 * j)) + 8192u * rb));
   };
   const int col = 32 * wave + l32;         // this lane's output column within the tile
 
-  f32x16 acc[4];
+  f32x16 acc[2];
 #pragma unroll
-  for (int bm = 0; bm < 4; ++bm)
+  for (int bm = 0; bm < 2; ++bm)
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[bm][r] = 0.0f;
-
   // int4: per-group products of the last group computed and its scale, folded
   // into acc at the start of the next group (0 * 0 before the first)
-  f32x16 tmp[4];
+  f32x16 tmp[2];
 #pragma unroll
-  for (int bm = 0; bm < 4; ++bm)
+  for (int bm = 0; bm < 2; ++bm)
 #pragma unroll
     for (int r = 0; r < 16; ++r) tmp[bm][r] = 0.0f;
   float sc_prev = 0.0f;
 
   const uint32_t nib_mask = opaque_vgpr(0x000F000Fu);
   // Computes the group in stage s; between its MFMA steps it issues the copies of
-  // group gn into stage sn.  The activation fragments of step j+1 are read before
-  // the MFMAs of step j.
+  // the group described by nsrc into the stage at LDS byte address nst.  The
+  // activation fragments of step j+1 are read before the MFMAs of step j.
   auto compute = [&](int s, const GroupSrc& nsrc, uint32_t nst) {
     const unsigned char* st = smem + s * SM::kStage;
     const unsigned char* sa = st + SM::kA;
@@ -285,9 +291,9 @@ __global__ __launch_bounds__(256, 1) void gemm_core_kernel(GemmCoreArgs a) {
     // recomputed per group: hoisted out of the loop, the eight per-step
     // addresses would stay live in registers for the whole kernel
     fb = opaque_vgpr(fbase);
-    bf16x8 af[2][4];
+    bf16x8 af[2][2];
 #pragma unroll
-    for (int bm = 0; bm < 4; ++bm) af[0][bm] = frag(sa, bm, 0);
+    for (int bm = 0; bm < 2; ++bm) af[0][bm] = frag(sa, bm, 0);
     if constexpr (INT4) {
       // this lane's 8 words of its column
       uint4 wv[2];
@@ -296,14 +302,14 @@ __global__ __launch_bounds__(256, 1) void gemm_core_kernel(GemmCoreArgs a) {
         wv[c] = *reinterpret_cast<const uint4*>(sb + col * 64 + (((2 * h + c) ^ ((col >> 2) & 3)) * 16));
       // zero-point step operands: k-slots 0..2 (lane half 0) hold the row sum parts
       // against 128 + z three times; every other slot is 0
-      const uint32_t szw = reinterpret_cast<const uint32_t*>(st + SM::kS + wave * 256)[l32];
+      const uint32_t szw = reinterpret_cast<const uint32_t*>(st + SM::kS)[col];
       const float sc_cur = __uint_as_float(szw << 16);
       const uint32_t zbf = szw >> 16;
       const bf16x8 zb = __builtin_bit_cast(bf16x8, make_uint4(h ? 0u : zbf * 0x10001u, h ? 0u : zbf, 0u, 0u));
-      bf16x8 za[4];
+      bf16x8 za[2];
 #pragma unroll
-      for (int bm = 0; bm < 4; ++bm) {
-        const uint2 rv = *reinterpret_cast<const uint2*>(st + SM::kR + (bm * 32 + l32) * 8);
+      for (int bm = 0; bm < 2; ++bm) {
+        const uint2 rv = *reinterpret_cast<const uint2*>(st + SM::kR + (32 * bm + l32) * 8);
         za[bm] = __builtin_bit_cast(bf16x8, make_uint4(h ? 0u : rv.x, h ? 0u : rv.y, 0u, 0u));
       }
       __builtin_amdgcn_sched_barrier(0);
@@ -311,7 +317,7 @@ __global__ __launch_bounds__(256, 1) void gemm_core_kernel(GemmCoreArgs a) {
         constexpr int j = decltype(jidx)::value;
         if constexpr (j < 7) {
 #pragma unroll
-          for (int bm = 0; bm < 4; ++bm) af[(j + 1) & 1][bm] = frag(sa, bm, j + 1);
+          for (int bm = 0; bm < 2; ++bm) af[(j + 1) & 1][bm] = frag(sa, bm, j + 1);
         }
         // keep the reads of step j+1 ahead of the MFMAs of step j (the scheduler
         // would otherwise sink each read next to its use and expose LDS latency)
@@ -324,7 +330,7 @@ __global__ __launch_bounds__(256, 1) void gemm_core_kernel(GemmCoreArgs a) {
                                nibble_pair_m(word, 2, nib_mask), nibble_pair_m(word, 3, nib_mask)));
         if constexpr (j == 0) {
 #pragma unroll
-          for (int bm = 0; bm < 4; ++bm) {
+          for (int bm = 0; bm < 2; ++bm) {
             // fold the previous group's block first: acc += sc_prev * tmp (fenced
             // from the MFMA that overwrites tmp, so both never need registers at
             // once), then start this group's block with its zero-point term
@@ -335,7 +341,7 @@ __global__ __launch_bounds__(256, 1) void gemm_core_kernel(GemmCoreArgs a) {
           }
         }
 #pragma unroll
-        for (int bm = 0; bm < 4; ++bm)
+        for (int bm = 0; bm < 2; ++bm)
           tmp[bm] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[j & 1][bm], bf, tmp[bm], 0, 0, 0);
         __builtin_amdgcn_sched_barrier(0);
       };
@@ -357,14 +363,14 @@ __global__ __launch_bounds__(256, 1) void gemm_core_kernel(GemmCoreArgs a) {
         constexpr int j = decltype(jidx)::value;
         if constexpr (j < 7) {
 #pragma unroll
-          for (int bm = 0; bm < 4; ++bm) af[(j + 1) & 1][bm] = frag(sa, bm, j + 1);
+          for (int bm = 0; bm < 2; ++bm) af[(j + 1) & 1][bm] = frag(sa, bm, j + 1);
           bfn = frag(sb, wave, j + 1);
         }
         __builtin_amdgcn_sched_barrier(0);
         const bf16x8 bf = bfc;
         copies_of_step(jidx, nsrc, nst);
 #pragma unroll
-        for (int bm = 0; bm < 4; ++bm)
+        for (int bm = 0; bm < 2; ++bm)
           acc[bm] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[j & 1][bm], bf, acc[bm], 0, 0, 0);
         bfc = bfn;
         __builtin_amdgcn_sched_barrier(0);
@@ -424,7 +430,7 @@ __global__ __launch_bounds__(256, 1) void gemm_core_kernel(GemmCoreArgs a) {
   wait_vmcnt<0>();
   if constexpr (INT4) {
 #pragma unroll
-    for (int bm = 0; bm < 4; ++bm)
+    for (int bm = 0; bm < 2; ++bm)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[bm][r] = fmaf(sc_prev, tmp[bm][r], acc[bm][r]);
   }
@@ -436,40 +442,41 @@ __global__ __launch_bounds__(256, 1) void gemm_core_kernel(GemmCoreArgs a) {
   if constexpr (EPI == EPI_STORE) {
     if (nok) {
 #pragma unroll
-      for (int bm = 0; bm < 4; ++bm)
+      for (int bm = 0; bm < 2; ++bm)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int row = m0 + bm * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
+          const int row = m0 + 32 * bm + 8 * (r >> 2) + 4 * h + (r & 3);
           if (row < a.M) a.Y[(size_t)row * a.N + ncol] = (uint16_t)f32_to_bf16_bits(acc[bm][r]);
         }
     }
   } else {
     // Squared differences against Yref.  The fp32 tile goes through LDS (rows of
     // 136 floats: the two lane halves, 4 rows apart, then hit different banks),
-    // then each thread scores half a row with 16-byte reads of the tile and of
-    // Yref.  The values are handed over as opaque bits: consumed as floats
-    // right here, the optimizer reshapes the loop's accumulator into scalars
-    // and the register allocator starts copying it through AGPRs every group.
+    // then each thread scores a quarter row with 16-byte reads of the tile and of
+    // Yref.  The values are handed over as opaque bits: consumed as floats right
+    // here, the optimizer may reshape the loop's accumulator into scalars and the
+    // register allocator start copying it through AGPRs every group.
     constexpr int kTS = 136;
-    static_assert(128 * kTS * 4 + 16 <= S * SM::kStage, "score tile fits in the stage buffers");
+    static_assert(kBM * kTS * 4 + 4 * kGemmWaves <= S * SM::kStage, "score tile fits in the stage buffers");
     uint32_t* tile = reinterpret_cast<uint32_t*>(smem);
     lds_barrier();        // all copies have landed (vmcnt 0 above), every wave is past its last read
 #pragma unroll
-    for (int bm = 0; bm < 4; ++bm)
+    for (int bm = 0; bm < 2; ++bm)
 #pragma unroll
       for (int r = 0; r < 16; ++r)
-        tile[(bm * 32 + 8 * (r >> 2) + 4 * h + (r & 3)) * kTS + col] = opaque_vgpr(__float_as_uint(acc[bm][r]));
+        tile[(32 * bm + 8 * (r >> 2) + 4 * h + (r & 3)) * kTS + col] =
+            opaque_vgpr(__float_as_uint(acc[bm][r]));
     __syncthreads();
-    const int trow = tid >> 1;                 // tile row scored by this thread
-    const int tc0 = (tid & 1) * 64;            // first of its 64 tile columns
+    const int trow = tid >> 2;                 // tile row scored by this thread
+    const int tc0 = (tid & 3) * 32;            // first of its 32 tile columns
     float s = 0.0f;
     if (m0 + trow < a.M) {
       const uint16_t* yr = a.Yref + (size_t)(m0 + trow) * a.N + n0 + tc0;
       const float* tr = reinterpret_cast<const float*>(tile) + trow * kTS + tc0;
-      const int ncols = min(64, a.N - n0 - tc0);     // may be <= 0
-      if (ncols == 64 && (a.N & 7) == 0 && (reinterpret_cast<uintptr_t>(a.Yref) & 15) == 0) {
+      const int ncols = min(32, a.N - n0 - tc0);     // may be <= 0
+      if (ncols == 32 && (a.N & 7) == 0 && (reinterpret_cast<uintptr_t>(a.Yref) & 15) == 0) {
 #pragma unroll
-        for (int c8 = 0; c8 < 8; ++c8) {
+        for (int c8 = 0; c8 < 4; ++c8) {
           const uint4 yv = *reinterpret_cast<const uint4*>(yr + 8 * c8);
           const float4 t0 = *reinterpret_cast<const float4*>(tr + 8 * c8);
           const float4 t1 = *reinterpret_cast<const float4*>(tr + 8 * c8 + 4);
@@ -490,11 +497,13 @@ __global__ __launch_bounds__(256, 1) void gemm_core_kernel(GemmCoreArgs a) {
       }
     }
     s = wave_sum(s);
-    float* sRed = reinterpret_cast<float*>(smem) + 128 * kTS;
+    float* sRed = reinterpret_cast<float*>(smem) + kBM * kTS;
     if (lane == 0) sRed[wave] = s;
     __syncthreads();
     if (tid == 0) {
-      const float tot = (sRed[0] + sRed[1]) + (sRed[2] + sRed[3]);
+      float tot = 0.0f;
+#pragma unroll
+      for (int w = 0; w < kGemmWaves; ++w) tot += sRed[w];
       a.partials[(size_t)zc_idx * gridDim.x + blockIdx.x] = tot;
     }
   }

@@ -196,7 +196,7 @@ int launch_grid_loss(const uint16_t* X, int T, int K, int N, const uint16_t* W, 
   a.partials = part;
   dim3 grid = tile_grid;
   grid.z = (unsigned)C;
-  hipLaunchKernelGGL((gemm_core_kernel<true, EPI_SQDIFF>), grid, dim3(256), 0, stream, a);
+  hipLaunchKernelGGL((gemm_core_kernel<true, EPI_SQDIFF>), grid, dim3(kGemmWaves * 64), 0, stream, a);
   W4_CHECK_LAUNCH();
 
   hipLaunchKernelGGL(loss_reduce_kernel, dim3((unsigned)C), dim3(64), 0, stream, part, L.tiles,
@@ -218,7 +218,7 @@ int launch_reference_gemm(const uint16_t* X, int M, int K, int N, const uint16_t
   r.Y = Y;
   const long long tiles = (long long)((N + kBN - 1) / kBN) * ((M + kBM - 1) / kBM);
   if (tiles > 0x7FFFFFFFLL) return W4_ERR_SHAPE;
-  hipLaunchKernelGGL((gemm_core_kernel<false, EPI_STORE>), dim3((unsigned)tiles), dim3(256), 0, stream, r);
+  hipLaunchKernelGGL((gemm_core_kernel<false, EPI_STORE>), dim3((unsigned)tiles), dim3(kGemmWaves * 64), 0, stream, r);
   W4_CHECK_LAUNCH();
   return W4_OK;
 }

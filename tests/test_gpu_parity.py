@@ -172,7 +172,8 @@ def test_gemv_all_m(M, sym):
 
 
 @pytest.mark.parametrize("M,K,N", [(1, 128, 1), (1, 384, 37), (3, 1152, 129), (8, 6144, 200), (16, 17408, 70),
-                                   (5, 5120, 64), (1, 17408, 33), (9, 8320, 17), (2, 16384, 8), (4, 24576, 5)])
+                                   (5, 5120, 64), (1, 17408, 33), (9, 8320, 17), (2, 16384, 8), (4, 24576, 5),
+                                   (1, 4096, 77), (1, 5120, 65), (1, 8192, 9), (1, 9216, 40), (1, 33792, 12)])
 def test_gemv_ragged(M, K, N):
     say("gemv ragged", M, K, N)
     X, W = wl.small_case(M, K, N, 21)
@@ -228,6 +229,29 @@ def test_gemv_large_full_size(shape, M):
     ref = O.linear(X, O.dequantize(qw[cols], sc[cols], None, W.shape[1], True))
     _fro_ok(y[:, cols], ref)
     assert _elementwise_ok(y[:, cols], ref) == 0
+
+
+@pytest.mark.parametrize("M,N", [(1, 40000), (2, 40000), (4, 36000), (16, 30000)])
+def test_gemv_tall_random_codes(M, N):
+    """Tall K = 2048 linears: enough rows that every workgroup gets several row
+    batches (and, for the larger M, several rounds of workgroups).  The packed
+    operands are drawn directly (random codes, scales and zero words); oracle on
+    every 16th row."""
+    rng = np.random.default_rng(1000 + M)
+    K = 2048
+    qw = rng.integers(0, 2 ** 32, size=(N, K // 8), dtype=np.uint64).astype(np.uint32)
+    sc = O.f32_to_bf16((np.abs(rng.standard_normal((N, K // 128))) * 2e-3 + 1e-4).astype(np.float32))
+    qz = rng.integers(0, 2 ** 32, size=(N, (K // 128 + 7) // 8), dtype=np.uint64).astype(np.uint32)
+    X = O.f32_to_bf16(rng.standard_normal((M, K)).astype(np.float32))
+    rows = np.arange(0, N, 16)
+    for sym in (False, True):
+        say("gemv tall", M, N, sym)
+        Y = w4.w4a16_gemv(to_bf16(X), to_i32(qw), to_bf16(sc), None if sym else to_i32(qz), sym)
+        torch.cuda.synchronize()
+        y = bf16_values(bits16(Y))[:, rows]
+        ref = O.linear(X, O.dequantize(qw[rows], sc[rows], None if sym else qz[rows], K, sym))
+        _fro_ok(y, ref)
+        assert _elementwise_ok(y, ref) == 0
 
 
 def test_gemv_rejects_m17():

@@ -4,16 +4,30 @@
 // batches of at most 16 rows take their own path; model card
 // "Qwen3.6-27B-W4A16", opening paragraph: int4 weights, 16-bit activations.
 //
-// Design (CDNA4, wave64, VALU): a workgroup owns a contiguous slice of input
-// channels ("split") and a run of output rows.  Each lane keeps its WPL words
-// (8*WPL channels, inside one 128-group) of activations in registers as bf16
-// pairs, then streams the matching packed words of every row with one 16/8/4-byte
-// coalesced load, turns each word into four bf16 pairs of exact integers 128+q
-// with one shift and one AND-OR, and accumulates v_dot2_f32_bf16 products in fp32.
-// The zero point and scale are applied once per lane and row:
-//   sum_k x_k (q_k - z) sc = sc * (sum_k x_k (128 + q_k) - (128 + z) sum_k x_k).
-// Lane partials are reduced across the wavefront (transposing butterfly, one
-// value per lane at the end) and across waves through LDS, in a fixed order.
+// Design (CDNA4, wave64, VALU):
+//  * A workgroup owns a contiguous slab of output rows (BPW batches of R rows)
+//    and a range of input channels (all of K unless K is split over
+//    grid.y).  Its waves split the channel range: every lane holds WPL packed
+//    words (8 WPL channels inside one 128-group) at a fixed position, with the
+//    matching activations in registers as bf16 pairs (x_j, x_j+4) and their fp32
+//    sum.
+//  * Each wave streams its slice of every row of the slab: per row and lane one
+//    16/8/4-byte load of packed words, one 2-byte scale load and (asymmetric) one
+//    4-byte zero-word load.  These are buffer loads: an offset past the end of
+//    the buffer returns 0 without a memory access, so lanes past the channel
+//    range and rows past N need neither branches nor clamped re-reads.  The
+//    batch loop is unrolled (BPW is a template parameter): straight-line code in
+//    which NB batches are in flight (a buffer is refilled as soon as its batch
+//    is computed) and every wait is for exactly the loads it needs.
+//  * A word expands into four pairs of exact bf16 integers 128+q (shift, AND-OR);
+//    v_dot2_f32_bf16 accumulates in fp32, and the zero point and scale are applied
+//    once per lane and row:
+//      sum_k x_k (q_k - z) sc = sc * (sum_k x_k (128 + q_k) - (128 + z) sum_k x_k).
+//  * The R*M partials of a batch are reduced across the wave by a transposing
+//    butterfly of lane swaps (permlane 32/16) and DPP permutations: no LDS.  With
+//    one wave per row the results are stored at once; otherwise every wave parks
+//    its per-row sums in LDS and the workgroup adds them in wave order after the
+//    last batch (one barrier per workgroup).
 #include "internal.hpp"
 
 namespace w4 {
@@ -24,100 +38,109 @@ struct GemvArgs {
   const uint32_t* qweight;
   const uint16_t* scales;
   const uint32_t* qzeros;
-  int symmetric;
   uint16_t* Y;
   float* partial;       // [splits][M][N] when splits > 1
   int wps;              // packed words per split (multiple of WPL)
 };
 
-// Butterfly reduction of V values per lane across the 64 lanes of a wave.
-// The first log2(V) steps halve the values each lane carries (each lane keeps
-// the half selected by its lane bit and adds its partner's copy); the rest are
-// plain xor sums.  Afterwards a[0] of every lane holds the wave total of value
-// index lane / (64 / V).
-template <int V, int O>
+// Raw buffer resource over [base, base + bytes) (gfx9 word 3: untyped, range
+// checked).  A load whose byte offset is >= bytes returns 0 and touches no memory.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+// Lane offset that keeps every load out of range: all buffers here are smaller than
+// 2^31 bytes, so row offset + kOob neither wraps nor lands in range.
+constexpr uint32_t kOob = 0x80000000u;
+
+template <int WPL>
+__device__ __forceinline__ void load_words(__amdgpu_buffer_rsrc_t r, uint32_t off, uint32_t* w) {
+  if constexpr (WPL == 4) {
+    const auto v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+    w[0] = v[0]; w[1] = v[1]; w[2] = v[2]; w[3] = v[3];
+  } else if constexpr (WPL == 2) {
+    const auto v = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
+    w[0] = v[0]; w[1] = v[1];
+  } else {
+    w[0] = __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
+  }
+}
+
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, true));
+}
+// permlane32 swap of (x, y): lanes 0-31 end up with (x, x of lane + 32), lanes 32-63
+// with (y of lane - 32, y); the sum of the pair is x summed over lanes l, l + 32 in
+// the lower half and y summed over them in the upper half.  permlane16 likewise
+// for lanes 16 apart (even 16-lane rows keep x, odd rows y).
+__device__ __forceinline__ float swap_sum32(float x, float y) {
+  const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(y), false, false);
+  return __uint_as_float(p[0]) + __uint_as_float(p[1]);
+}
+__device__ __forceinline__ float swap_sum16(float x, float y) {
+  const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(y), false, false);
+  return __uint_as_float(p[0]) + __uint_as_float(p[1]);
+}
+
+// keep + the partner's `send`, partners paired by lane bit B:
+//   B = 3, 2: the mirrors l <-> 15 - l, l <-> 7 - l inside each 16-lane row;
+//   B = 1, 0: l ^ 2, l ^ 1 (quad permutations).
+template <int B>
+__device__ __forceinline__ float pair_sum(float keep, float send) {
+  if constexpr (B == 3) return keep + dpp<0x140>(send);        // row_mirror
+  else if constexpr (B == 2) return keep + dpp<0x141>(send);   // row_half_mirror
+  else if constexpr (B == 1) return keep + dpp<0x4E>(send);    // quad_perm [2,3,0,1]
+  else return keep + dpp<0xB1>(send);                          // quad_perm [1,0,3,2]
+}
+
+// Transposing butterfly over the 64 lanes for V (power of two) values per lane,
+// one stage per lane bit B = 5 .. 0 (partners 32 apart, 16 apart, then the
+// in-row pairings of pair_sum).  The pairing masks (32, 16, 15, 7, 2, 1) span the
+// 6 lane bits and each flips the bit its stage splits on.  While more than one
+// value remains, a lane keeps the half selected by its bit B (the upper half when
+// set) and adds the partner's copy of that half; then plain sums.  Afterwards
+// value index lane >> (6 - log2 V), summed over all lanes, is in every lane.
+template <int V, int B>
 struct WaveReduce {
   __device__ static __forceinline__ void run(float* a, int lane) {
-    if constexpr (V > 1) {
-      constexpr int H = V / 2;
-      const bool upper = (lane & O) != 0;
+    if constexpr (B >= 0) {
+      if constexpr (V > 1) {
+        constexpr int H = V / 2;
+        if constexpr (B >= 4) {
 #pragma unroll
-      for (int i = 0; i < H; ++i) {
-        const float send = upper ? a[i] : a[i + H];
-        const float keep = upper ? a[i + H] : a[i];
-        a[i] = keep + __shfl_xor(send, O, kWave);
+          for (int i = 0; i < H; ++i) a[i] = B == 5 ? swap_sum32(a[i], a[i + H]) : swap_sum16(a[i], a[i + H]);
+        } else {
+          const bool upper = (lane >> B) & 1;
+#pragma unroll
+          for (int i = 0; i < H; ++i) {
+            const float send = upper ? a[i] : a[i + H];
+            const float keep = upper ? a[i + H] : a[i];
+            a[i] = pair_sum<B>(keep, send);
+          }
+        }
+        WaveReduce<H, B - 1>::run(a, lane);
+      } else {
+        if constexpr (B == 5) a[0] = swap_sum32(a[0], a[0]);
+        else if constexpr (B == 4) a[0] = swap_sum16(a[0], a[0]);
+        else a[0] = pair_sum<B>(a[0], a[0]);
+        WaveReduce<1, B - 1>::run(a, lane);
       }
-      WaveReduce<H, O / 2>::run(a, lane);
-    } else if constexpr (O >= 1) {
-      a[0] += __shfl_xor(a[0], O, kWave);
-      WaveReduce<1, O / 2>::run(a, lane);
     }
   }
 };
 
 constexpr int pow2_ceil(int v) { return v <= 1 ? 1 : 2 * pow2_ceil((v + 1) / 2); }
-
-template <int WPL>
-struct WordVec;
-template <>
-struct WordVec<4> {
-  __device__ static __forceinline__ void load(const uint32_t* p, uint32_t* w) {
-    const uint4 v = *reinterpret_cast<const uint4*>(p);
-    w[0] = v.x; w[1] = v.y; w[2] = v.z; w[3] = v.w;
-  }
-};
-template <>
-struct WordVec<2> {
-  __device__ static __forceinline__ void load(const uint32_t* p, uint32_t* w) {
-    const uint2 v = *reinterpret_cast<const uint2*>(p);
-    w[0] = v.x; w[1] = v.y;
-  }
-};
-template <>
-struct WordVec<1> {
-  __device__ static __forceinline__ void load(const uint32_t* p, uint32_t* w) { w[0] = *p; }
-};
-
-// A workgroup owns one K split and walks row batches b = blockIdx.x,
-// blockIdx.x + gridDim.x, ... (R rows each); the grid is sized to the number of
-// workgroups the device holds at once.  The lane's activations are loaded once.
-// The packed words, scales and zero words of the next batch are loaded (from
-// clamped, always-valid addresses, without branches around the loads) before
-// the current batch is computed, so every wave keeps a batch of loads in flight
-// while it computes and reduces.  Rows past N are computed on clamped data and
-// never stored; lanes past the end of K carry zero activations.
-template <int M, int WPL, int R>
-struct GemvBatch {
-  uint32_t w[R][WPL];
-  uint16_t scb[R];      // kept 16-bit: widening at the load would wait for it right there
-  uint32_t zw[R];
-};
-
-template <int M, int WPL, int R>
-__device__ __forceinline__ void gemv_load_batch(const GemvArgs& a, int b, int wb, int g, int words, int G, int GW,
-                                                GemvBatch<M, WPL, R>& B) {
-#pragma unroll
-  for (int r = 0; r < R; ++r) {
-    const int n = min(b * R + r, a.N - 1);
-    WordVec<WPL>::load(a.qweight + (size_t)n * words + wb, B.w[r]);
-    B.scb[r] = a.scales[(size_t)n * G + g];
-    // branch-free: symmetric weights read (and ignore) the first scale word, so
-    // every batch issues the same loads and the waits on them stay exact
-    const uint32_t* zp = a.symmetric ? reinterpret_cast<const uint32_t*>(a.scales)
-                                     : a.qzeros + (size_t)n * GW + (g >> 3);
-    B.zw[r] = *zp;
-  }
-}
+constexpr int ilog2(int v) { return v <= 1 ? 0 : 1 + ilog2(v / 2); }
 
 // Up to 16 waves per workgroup for M <= 2 (128 VGPRs per lane), 8 above (256).
 constexpr int gemv_max_waves(int M) { return M <= 2 ? 16 : 8; }
 
-template <int M, int WPL, int R>
+template <int M, int WPL, int R, int BPW, int NB, bool SYM>
 __global__ __launch_bounds__(gemv_max_waves(M) * 64) void gemv_kernel(GemvArgs a) {
   constexpr int V = R * M;
   constexpr int VP = pow2_ceil(V);
-  constexpr int SPREAD = kWave / VP;          // lanes per reduced value
-  __shared__ float red[2][16][VP];
+  constexpr int LOGV = ilog2(VP);
+  __shared__ float red[BPW * R * M][16];    // per-row sums of every wave when nw > 1
 
   const int t = threadIdx.x;
   const int lane = t & (kWave - 1);
@@ -126,28 +149,57 @@ __global__ __launch_bounds__(gemv_max_waves(M) * 64) void gemv_kernel(GemvArgs a
   const int words = a.K >> 3;
   const int G = a.K >> 7;
   const int GW = (G + 7) >> 3;
-  const int wb_raw = blockIdx.y * a.wps + t * WPL;
-  const bool active = (t * WPL < a.wps) && (wb_raw < words);
-  const int wb = active ? wb_raw : 0;
-  const int g = wb >> 4;
-  const int nb = (a.N + R - 1) / R;
-  int b = blockIdx.x;
+  // this lane's WPL words start at word t WPL of the split; byte offsets inside
+  // one row of each array, out of range when they lie past the split or past K
+  const int wl = blockIdx.y * a.wps + t * WPL;
+  const bool active = (t * WPL < a.wps) && (wl < words);
+  const int g = active ? wl >> 4 : 0;
+  const int zsh = 4 * (g & 7);
+  const uint32_t kw = active ? (uint32_t)wl * 4u : kOob;
+  const uint32_t ks = active ? (uint32_t)g * 2u : kOob;
+  const uint32_t kz = active ? (uint32_t)(g >> 3) * 4u : kOob;
+  const uint32_t kx = active ? (uint32_t)wl * 16u : kOob;
+  const uint32_t wrow = (uint32_t)words * 4u, srow = (uint32_t)G * 2u, zrow = (uint32_t)GW * 4u;
+  const auto rw = make_rsrc(a.qweight, (uint32_t)a.N * wrow);
+  const auto rs = make_rsrc(a.scales, (uint32_t)a.N * srow);
+  const auto rz = make_rsrc(SYM ? static_cast<const void*>(a.scales) : a.qzeros, SYM ? 0u : (uint32_t)a.N * zrow);
+  const auto rx = make_rsrc(a.X, (uint32_t)(M * a.K) * 2u);
+  const int n_first = blockIdx.x * BPW * R;   // first row of the slab
 
-  // Every load of the prologue -- this lane's activations, then the first batch --
-  // is issued before anything waits for one (the scheduling fence keeps the
-  // compiler from sinking each load next to its use, which would cost one memory
-  // round trip per load).
-  uint4 xr[M][WPL];
+  struct Batch {
+    uint32_t w[R][WPL];
+    uint16_t sc[R];     // kept 16-bit: widening at the load would wait for it right there
+    uint32_t z[R];
+  };
+  // batch i of the slab; rows past N read nothing
+  auto load = [&](int i, Batch& B) {
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const uint32_t row = (uint32_t)min(n_first + i * R + r, a.N);
+      load_words<WPL>(rw, row * wrow + kw, B.w[r]);
+      B.sc[r] = __builtin_amdgcn_raw_buffer_load_b16(rs, row * srow + ks, 0, 0);
+      if constexpr (!SYM) B.z[r] = __builtin_amdgcn_raw_buffer_load_b32(rz, row * zrow + kz, 0, 0);
+    }
+  };
+
+  // Prologue: every load -- this lane's activations, then the first NB batches --
+  // is issued before anything waits for one (the scheduling fence keeps the compiler
+  // from sinking each load next to its use, one memory round trip per load).
+  uint32_t xr[M][WPL][4];
 #pragma unroll
   for (int m = 0; m < M; ++m)
 #pragma unroll
-    for (int i = 0; i < WPL; ++i)
-      xr[m][i] = *reinterpret_cast<const uint4*>(a.X + (size_t)m * a.K + (size_t)(wb + i) * 8);
-  GemvBatch<M, WPL, R> B0, B1;
-  gemv_load_batch(a, b, wb, g, words, G, GW, B0);
+    for (int i = 0; i < WPL; ++i) {
+      const auto v = __builtin_amdgcn_raw_buffer_load_b128(rx, (uint32_t)(m * a.K) * 2u + kx + 16u * i, 0, 0);
+      xr[m][i][0] = v[0]; xr[m][i][1] = v[1]; xr[m][i][2] = v[2]; xr[m][i][3] = v[3];
+    }
+  __builtin_amdgcn_sched_barrier(0);
+  Batch B[NB];
+#pragma unroll
+  for (int i = 0; i < NB; ++i)
+    if (i < BPW) load(i, B[i]);
   __builtin_amdgcn_sched_barrier(0);
 
-  // this lane's activations as (x_j, x_j+4) bf16 pairs, and their fp32 sums
   uint32_t xp[M][WPL][4];
   float xs[M];
 #pragma unroll
@@ -155,86 +207,75 @@ __global__ __launch_bounds__(gemv_max_waves(M) * 64) void gemv_kernel(GemvArgs a
     xs[m] = 0.0f;
 #pragma unroll
     for (int i = 0; i < WPL; ++i) {
-      const uint4 v = xr[m][i];
-      uint32_t d[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-      for (int q = 0; q < 4; ++q) d[q] = active ? d[q] : 0u;
-      pair_activations(d, xp[m][i]);
+      pair_activations(xr[m][i], xp[m][i]);
 #pragma unroll
       for (int q = 0; q < 4; ++q)
-        xs[m] += __uint_as_float(d[q] << 16) + __uint_as_float(d[q] & 0xFFFF0000u);
+        xs[m] += __uint_as_float(xr[m][i][q] << 16) + __uint_as_float(xr[m][i][q] & 0xFFFF0000u);
     }
   }
+  // the nibble mask stays in a register, so AND and OR fuse into one v_and_or_b32
+  const uint32_t nib_mask = opaque_vgpr(0x000F000Fu);
 
-  // compute batch `bb` from registers `B`, reduce and store; `par` selects the LDS buffer
-  auto process = [&](const GemvBatch<M, WPL, R>& Bc, int bb, int par) {
+  auto store = [&](int m, int n, float v) {
+    if (a.partial)
+      a.partial[((size_t)blockIdx.y * M + m) * a.N + n] = v;
+    else
+      a.Y[(size_t)m * a.N + n] = (uint16_t)f32_to_bf16_bits(v);
+  };
+
+  auto process = [&](const Batch& Bc, int i) {
     float part[VP];
 #pragma unroll
     for (int v = V; v < VP; ++v) part[v] = 0.0f;
 #pragma unroll
     for (int r = 0; r < R; ++r) {
-      const float sc = bf16_bits_to_f32(Bc.scb[r]);
-      const float zc = a.symmetric ? 136.0f : (float)(128u + ((Bc.zw[r] >> (4 * (g & 7))) & 0xFu));
+      const float sc = bf16_bits_to_f32(Bc.sc[r]);
+      const float zc = SYM ? 136.0f : (float)(128u + ((Bc.z[r] >> zsh) & 0xFu));
       uint32_t bp[WPL][4];
 #pragma unroll
-      for (int i = 0; i < WPL; ++i)
+      for (int w = 0; w < WPL; ++w)
 #pragma unroll
-        for (int p = 0; p < 4; ++p) bp[i][p] = nibble_pair(Bc.w[r][i], p);
+        for (int p = 0; p < 4; ++p) bp[w][p] = nibble_pair_m(Bc.w[r][w], p, nib_mask);
 #pragma unroll
       for (int m = 0; m < M; ++m) {
         float acc = 0.0f;
 #pragma unroll
-        for (int i = 0; i < WPL; ++i)
+        for (int w = 0; w < WPL; ++w)
 #pragma unroll
-          for (int p = 0; p < 4; ++p) acc = dot2_bf16(xp[m][i][p], bp[i][p], acc);
+          for (int p = 0; p < 4; ++p) acc = dot2_bf16(xp[m][w][p], bp[w][p], acc);
         part[r * M + m] = sc * (acc - zc * xs[m]);
       }
     }
-    WaveReduce<VP, 32>::run(part, lane);
-    const int idx = lane / SPREAD;
-    const bool writer = (lane % SPREAD) == 0 && idx < V;
-    const int n0 = bb * R;
+    WaveReduce<VP, 5>::run(part, lane);
+    const int idx = lane >> (6 - LOGV);
+    const bool writer = (lane & ((kWave >> LOGV) - 1)) == 0 && idx < V;
+    const int rloc = i * R + idx / M;
+    const int m = idx % M;
     if (nw == 1) {
-      const int n = n0 + idx / M, m = idx % M;
-      if (writer && n < a.N) {
-        if (a.partial)
-          a.partial[((size_t)blockIdx.y * M + m) * a.N + n] = part[0];
-        else
-          a.Y[(size_t)m * a.N + n] = (uint16_t)f32_to_bf16_bits(part[0]);
-      }
-    } else {
-      // two LDS buffers alternate between batches, so one barrier per batch suffices
-      if (writer) red[par][wave][idx] = part[0];
-      __syncthreads();
-      if (t < V) {
-        const int n = n0 + t / M, m = t % M;
-        float sum = 0.0f;
-        for (int ww = 0; ww < nw; ++ww) sum += red[par][ww][t];
-        if (n < a.N) {
-          if (a.partial)
-            a.partial[((size_t)blockIdx.y * M + m) * a.N + n] = sum;
-          else
-            a.Y[(size_t)m * a.N + n] = (uint16_t)f32_to_bf16_bits(sum);
-        }
-      }
+      const int n = n_first + rloc;
+      if (writer && n < a.N) store(m, n, part[0]);
+    } else if (writer) {
+      red[rloc * M + m][wave] = part[0];
     }
   };
 
-  const int step = gridDim.x;
-  // The next batch's loads are issued (and fenced) before the current batch is
-  // computed.  They are issued unconditionally (past the last batch they repeat
-  // it): with a branch around them the compiler can no longer count which loads
-  // are outstanding and waits for all of them before computing.
-  while (b < nb) {
-    gemv_load_batch(a, min(b + step, nb - 1), wb, g, words, G, GW, B1);
+#pragma unroll
+  for (int i = 0; i < BPW; ++i) {
+    process(B[i % NB], i);
+    if (i + NB < BPW) load(i + NB, B[i % NB]);
     __builtin_amdgcn_sched_barrier(0);
-    process(B0, b, 0);
-    b += step;
-    if (b >= nb) break;
-    gemv_load_batch(a, min(b + step, nb - 1), wb, g, words, G, GW, B0);
-    __builtin_amdgcn_sched_barrier(0);
-    process(B1, b, 1);
-    b += step;
+  }
+
+  if (nw > 1) {
+    __syncthreads();
+    for (int e = t; e < BPW * R * M; e += blockDim.x) {
+      const int n = n_first + e / M;
+      if (n < a.N) {
+        float s = 0.0f;
+        for (int w = 0; w < nw; ++w) s += red[e][w];
+        store(e % M, n, s);
+      }
+    }
   }
 }
 
@@ -250,41 +291,27 @@ __global__ __launch_bounds__(256) void gemv_split_reduce(const float* partial, i
 
 namespace {
 
+// Words per lane, rows per batch and batches in flight for M activation rows
+// (the activations of one lane take 16 M WPL registers: 16 to 64).
+constexpr int gemv_wpl(int M) { return M <= 4 ? 4 : (M <= 8 ? 2 : 1); }
+constexpr int gemv_rows(int M) { return M <= 8 ? 2 : 1; }
+constexpr int gemv_nb(int M) { return 2; }
+
 struct GemvPlan {
   int wpl, nw, splits, wps;
 };
 
-// words per lane and rows per workgroup for M activation rows
-constexpr int gemv_wpl(int M) { return M <= 4 ? 4 : (M <= 8 ? 2 : 1); }
-constexpr int gemv_rows(int M) { return M == 1 ? 4 : (M <= 8 ? 2 : 1); }
-
-GemvPlan plan_gemv(int M, int K, int N) {
-  (void)N;
+// K split into `splits` ranges of wps words, each covered by nw waves.
+GemvPlan plan_gemv(int M, int K) {
   GemvPlan p;
   p.wpl = gemv_wpl(M);
   const int words = K / 8;
   const int max_wps = gemv_max_waves(M) * kWave * p.wpl;
   p.splits = (words + max_wps - 1) / max_wps;
-  int wps = (words + p.splits - 1) / p.splits;
+  const int wps = (words + p.splits - 1) / p.splits;
   p.wps = (wps + p.wpl - 1) / p.wpl * p.wpl;
   p.nw = (p.wps / p.wpl + kWave - 1) / kWave;
   return p;
-}
-
-// Resident workgroups per CU of one gemv instantiation at a block size (cached).
-template <int M>
-int gemv_blocks_per_cu(int threads) {
-  static int cache[17] = {0};
-  const int slot = threads / kWave;
-  if (cache[slot] == 0) {
-    int nblk = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nblk, gemv_kernel<M, gemv_wpl(M), gemv_rows(M)>, threads,
-                                                     0) != hipSuccess ||
-        nblk < 1)
-      nblk = 1;
-    cache[slot] = nblk;
-  }
-  return cache[slot];
 }
 
 int device_cus() {
@@ -299,23 +326,62 @@ int device_cus() {
   return cus[dev];
 }
 
-template <int M>
+template <int M, int BPW, bool SYM>
+constexpr auto gemv_instance() {
+  return gemv_kernel<M, gemv_wpl(M), gemv_rows(M), BPW, gemv_nb(M), SYM>;
+}
+
+// Resident workgroups per CU of one instantiation at a block size (cached).
+template <int M, int BPW, bool SYM>
+int gemv_blocks_per_cu(int threads) {
+  static int cache[17] = {0};
+  const int slot = threads / kWave;
+  if (cache[slot] == 0) {
+    int nblk = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nblk, gemv_instance<M, BPW, SYM>(), threads, 0) != hipSuccess ||
+        nblk < 1)
+      nblk = 1;
+    cache[slot] = nblk;
+  }
+  return cache[slot];
+}
+
+// Batches per workgroup: the fewest (1, 2, 4 or 8) with which one round of
+// resident workgroups covers all rows, else 8 (then several rounds).
+template <int M, bool SYM>
 void launch_m(const GemvArgs& a, const GemvPlan& p, hipStream_t stream) {
-  constexpr int WPL = gemv_wpl(M);
   constexpr int R = gemv_rows(M);
   const int threads = p.nw * kWave;
   const long long nb = (a.N + R - 1) / R;
-  const long long resident = (long long)device_cus() * gemv_blocks_per_cu<M>(threads);
-  const long long per_split = (resident + p.splits - 1) / p.splits;
-  const unsigned gx = (unsigned)(nb < per_split ? nb : per_split);
-  hipLaunchKernelGGL((gemv_kernel<M, WPL, R>), dim3(gx, (unsigned)p.splits), dim3(threads), 0, stream, a);
+  const long long cus = device_cus();
+  auto go = [&](auto kernel, int bpw) {
+    const unsigned gx = (unsigned)((nb + bpw - 1) / bpw);
+    hipLaunchKernelGGL(kernel, dim3(gx, (unsigned)p.splits), dim3(threads), 0, stream, a);
+  };
+  auto fits = [&](int bpw, int per_cu) { return (nb + bpw - 1) / bpw * p.splits <= cus * per_cu; };
+  if (fits(1, gemv_blocks_per_cu<M, 1, SYM>(threads)))
+    go(gemv_instance<M, 1, SYM>(), 1);
+  else if (fits(2, gemv_blocks_per_cu<M, 2, SYM>(threads)))
+    go(gemv_instance<M, 2, SYM>(), 2);
+  else if (fits(4, gemv_blocks_per_cu<M, 4, SYM>(threads)))
+    go(gemv_instance<M, 4, SYM>(), 4);
+  else
+    go(gemv_instance<M, 8, SYM>(), 8);
+}
+
+template <int M>
+void launch_sym(const GemvArgs& a, const GemvPlan& p, bool symmetric, hipStream_t stream) {
+  if (symmetric)
+    launch_m<M, true>(a, p, stream);
+  else
+    launch_m<M, false>(a, p, stream);
 }
 
 }  // namespace
 
 size_t gemv_workspace_bytes(int M, int K, int N) {
   if (M <= 0 || N <= 0 || K <= 0) return 0;
-  const GemvPlan p = plan_gemv(M, K, N);
+  const GemvPlan p = plan_gemv(M, K);
   return p.splits > 1 ? (size_t)p.splits * M * N * sizeof(float) : 0;
 }
 
@@ -323,26 +389,29 @@ int launch_gemv(const uint16_t* X, int M, int K, int N, const uint32_t* qweight,
                 const uint16_t* scales, const uint32_t* qzeros, int symmetric, uint16_t* Y,
                 void* workspace, hipStream_t stream) {
   if (M == 0 || N == 0) return W4_OK;
-  const GemvPlan p = plan_gemv(M, K, N);
-  GemvArgs a{X, K, N, qweight, scales, qzeros, symmetric, Y,
-             p.splits > 1 ? static_cast<float*>(workspace) : nullptr, p.wps};
+  // buffer loads take 32-bit byte offsets: every operand below 2^31 bytes
+  // (packed words N K / 2, activations 2 M K)
+  if ((long long)N * K / 2 >= (1LL << 31) || 2LL * M * K >= (1LL << 31)) return W4_ERR_SHAPE;
+  const GemvPlan p = plan_gemv(M, K);
+  GemvArgs a{X, K, N, qweight, scales, qzeros, Y, p.splits > 1 ? static_cast<float*>(workspace) : nullptr, p.wps};
+  const bool sym = symmetric != 0;
   switch (M) {
-    case 1: launch_m<1>(a, p, stream); break;
-    case 2: launch_m<2>(a, p, stream); break;
-    case 3: launch_m<3>(a, p, stream); break;
-    case 4: launch_m<4>(a, p, stream); break;
-    case 5: launch_m<5>(a, p, stream); break;
-    case 6: launch_m<6>(a, p, stream); break;
-    case 7: launch_m<7>(a, p, stream); break;
-    case 8: launch_m<8>(a, p, stream); break;
-    case 9: launch_m<9>(a, p, stream); break;
-    case 10: launch_m<10>(a, p, stream); break;
-    case 11: launch_m<11>(a, p, stream); break;
-    case 12: launch_m<12>(a, p, stream); break;
-    case 13: launch_m<13>(a, p, stream); break;
-    case 14: launch_m<14>(a, p, stream); break;
-    case 15: launch_m<15>(a, p, stream); break;
-    case 16: launch_m<16>(a, p, stream); break;
+    case 1: launch_sym<1>(a, p, sym, stream); break;
+    case 2: launch_sym<2>(a, p, sym, stream); break;
+    case 3: launch_sym<3>(a, p, sym, stream); break;
+    case 4: launch_sym<4>(a, p, sym, stream); break;
+    case 5: launch_sym<5>(a, p, sym, stream); break;
+    case 6: launch_sym<6>(a, p, sym, stream); break;
+    case 7: launch_sym<7>(a, p, sym, stream); break;
+    case 8: launch_sym<8>(a, p, sym, stream); break;
+    case 9: launch_sym<9>(a, p, sym, stream); break;
+    case 10: launch_sym<10>(a, p, sym, stream); break;
+    case 11: launch_sym<11>(a, p, sym, stream); break;
+    case 12: launch_sym<12>(a, p, sym, stream); break;
+    case 13: launch_sym<13>(a, p, sym, stream); break;
+    case 14: launch_sym<14>(a, p, sym, stream); break;
+    case 15: launch_sym<15>(a, p, sym, stream); break;
+    case 16: launch_sym<16>(a, p, sym, stream); break;
     default: return W4_ERR_UNSUPPORTED;
   }
   W4_CHECK_LAUNCH();

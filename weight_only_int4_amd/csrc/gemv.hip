@@ -22,7 +22,7 @@
 //  * A word expands into four pairs of exact bf16 integers 128+q (shift, AND-OR);
 //    v_dot2_f32_bf16 accumulates in fp32, and the zero point and scale are applied
 //    once per lane and row:
-//      sum_k x_k (q_k - z) sc = sc * (sum_k x_k (128 + q_k) - (128 + z) sum_k x_k).
+//      sum_k x_k (q_k - z) sc = sc * (-(128 + z) sum_k x_k + sum_k x_k (128 + q_k)).
 //  * The R*M partials of a batch are reduced across the wave by a transposing
 //    butterfly of lane swaps (permlane 32/16) and DPP permutations: no LDS.  With
 //    one wave per row the results are stored at once; otherwise every wave parks
@@ -213,6 +213,10 @@ __global__ __launch_bounds__(gemv_max_waves(M) * 64) void gemv_kernel(GemvArgs a
         xs[m] += __uint_as_float(xr[m][i][q] << 16) + __uint_as_float(xr[m][i][q] & 0xFFFF0000u);
     }
   }
+  // symmetric: the zero-point term -(128 + 8) sum_k x_k is the same for every row
+  float zx[M];
+#pragma unroll
+  for (int m = 0; m < M; ++m) zx[m] = -136.0f * xs[m];
   // the nibble mask stays in a register, so AND and OR fuse into one v_and_or_b32
   const uint32_t nib_mask = opaque_vgpr(0x000F000Fu);
 
@@ -230,7 +234,7 @@ __global__ __launch_bounds__(gemv_max_waves(M) * 64) void gemv_kernel(GemvArgs a
 #pragma unroll
     for (int r = 0; r < R; ++r) {
       const float sc = bf16_bits_to_f32(Bc.sc[r]);
-      const float zc = SYM ? 136.0f : (float)(128u + ((Bc.z[r] >> zsh) & 0xFu));
+      const float zc = SYM ? 0.0f : (float)(128u + ((Bc.z[r] >> zsh) & 0xFu));
       uint32_t bp[WPL][4];
 #pragma unroll
       for (int w = 0; w < WPL; ++w)
@@ -238,12 +242,12 @@ __global__ __launch_bounds__(gemv_max_waves(M) * 64) void gemv_kernel(GemvArgs a
         for (int p = 0; p < 4; ++p) bp[w][p] = nibble_pair_m(Bc.w[r][w], p, nib_mask);
 #pragma unroll
       for (int m = 0; m < M; ++m) {
-        float acc = 0.0f;
+        float acc = SYM ? zx[m] : -zc * xs[m];
 #pragma unroll
         for (int w = 0; w < WPL; ++w)
 #pragma unroll
           for (int p = 0; p < 4; ++p) acc = dot2_bf16(xp[m][w][p], bp[w][p], acc);
-        part[r * M + m] = sc * (acc - zc * xs[m]);
+        part[r * M + m] = sc * acc;
       }
     }
     WaveReduce<VP, 5>::run(part, lane);
@@ -292,8 +296,8 @@ __global__ __launch_bounds__(256) void gemv_split_reduce(const float* partial, i
 namespace {
 
 // Words per lane, rows per batch and batches in flight for M activation rows
-// (the activations of one lane take 16 M WPL registers: 16 to 64).
-constexpr int gemv_wpl(int M) { return M <= 4 ? 4 : (M <= 8 ? 2 : 1); }
+// (the activations of one lane take 4 M WPL registers: 16 to 128).
+constexpr int gemv_wpl(int M) { return M <= 4 ? 4 : 2; }
 constexpr int gemv_rows(int M) { return M <= 8 ? 2 : 1; }
 constexpr int gemv_nb(int M) { return 2; }
 
@@ -346,8 +350,8 @@ int gemv_blocks_per_cu(int threads) {
   return cache[slot];
 }
 
-// Batches per workgroup: the fewest (1, 2, 4 or 8) with which one round of
-// resident workgroups covers all rows, else 8 (then several rounds).
+// Batches per workgroup: the fewest (1, 2, 4, 8 or 16) with which one round of
+// resident workgroups covers all rows, else 16 (then several rounds).
 template <int M, bool SYM>
 void launch_m(const GemvArgs& a, const GemvPlan& p, hipStream_t stream) {
   constexpr int R = gemv_rows(M);
@@ -365,8 +369,10 @@ void launch_m(const GemvArgs& a, const GemvPlan& p, hipStream_t stream) {
     go(gemv_instance<M, 2, SYM>(), 2);
   else if (fits(4, gemv_blocks_per_cu<M, 4, SYM>(threads)))
     go(gemv_instance<M, 4, SYM>(), 4);
-  else
+  else if (fits(8, gemv_blocks_per_cu<M, 8, SYM>(threads)))
     go(gemv_instance<M, 8, SYM>(), 8);
+  else
+    go(gemv_instance<M, 16, SYM>(), 16);
 }
 
 template <int M>

@@ -1,6 +1,8 @@
 // Prefill contraction Y = X W_hat^T on MFMA (model card
 // "GLM-5.2-QSRT-Fruit-Instruct", "Reproducible runtime": W4A16 serves prefill row
 // counts; model card "Qwen3.6-27B-W4A16": int4 weights, 16-bit activations).
+#include <type_traits>
+
 #include "gemm_core.hpp"
 
 namespace w4 {
@@ -15,15 +17,30 @@ __device__ __forceinline__ void split3(float v, uint32_t& hi, uint32_t& mid, uin
   lo = f32_to_bf16_bits(r2);
 }
 
+// Sum over the 16 lanes of each 16-lane row of the wave (DPP: mirror inside the
+// row, mirror inside each half, then the quad permutations), in every lane.
+__device__ __forceinline__ float row16_sum(float v) {
+  auto step = [](float x, auto ctrl) {
+    return x + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), decltype(ctrl)::value, 0xF, 0xF, true));
+  };
+  v = step(v, std::integral_constant<int, 0x140>{});   // row_mirror
+  v = step(v, std::integral_constant<int, 0x141>{});   // row_half_mirror
+  v = step(v, std::integral_constant<int, 0x4E>{});    // quad_perm [2,3,0,1]
+  v = step(v, std::integral_constant<int, 0xB1>{});    // quad_perm [1,0,3,2]
+  return v;
+}
+
 // One launch, two jobs (grid.z = problem c):
-//  * blocks [0, rs_blocks): one wave per (row m < mpad, triple of groups t):
-//    lanes 0..47 each sum 8 consecutive bf16 of the triple's 384 channels (fp32,
-//    fixed order), 16-lane xor trees give the three group sums; lane 0 writes
-//    rsq[g][m] = the negated sum split into three bf16 parts (exact) and a zero
-//    (rows >= M: zeros), and, when xp is set, every lane writes its 8 channels
-//    of X pair-arranged into xp (rows >= M: zeros);
-//  * the remaining blocks: one thread per (triple t, column n < npad) writes
-//    szq[g][n] = scale bits | bf16(128 + z) << 16 (0 for n >= N).
+//  * blocks [0, rs_blocks): one wave per row m < mpad.  Pass i covers channels
+//    512 i .. 512 i + 511: lane l loads 8 consecutive bf16 (16 bytes) at
+//    512 i + 8 l, so the 16 lanes of row r of the wave hold group 4 i + r; each
+//    lane sums its 8 values in fp32 (fixed order), the row adds its 16 lanes, and
+//    lane 16 r writes rsq[g][m] = the negated group sum split into three bf16
+//    parts (exact) and a zero (rows >= M: zeros).  When xp is set every lane also
+//    writes its 8 channels pair-arranged into xp (rows >= M: zeros).  All passes'
+//    loads are issued before the first sum.
+//  * the remaining blocks: one thread per (triple of groups t, column n < npad)
+//    writes szq[g][n] = scale bits | bf16(128 + z) << 16 (0 for n >= N).
 __global__ __launch_bounds__(256) void gemm_prep_kernel(const uint16_t* X, size_t x_stride, int M, int K, int mpad,
                                                         const uint16_t* scales, size_t sc_stride,
                                                         const uint32_t* qzeros, size_t qz_stride, int symmetric,
@@ -31,49 +48,49 @@ __global__ __launch_bounds__(256) void gemm_prep_kernel(const uint16_t* X, size_
                                                         size_t szq_stride, uint16_t* xp, int rs_blocks) {
 #pragma clang fp contract(off)
   const int G = K >> 7;
-  const int T3 = (G + 2) / 3;
   const int c = blockIdx.z;
   if ((int)blockIdx.x < rs_blocks) {
     const int lane = threadIdx.x & 63;
-    const long long item = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (item >= (long long)mpad * T3) return;            // uniform per wave
-    const int m = (int)(item / T3);
-    const int t = (int)(item % T3);
-    const int j = lane >> 4;
-    const int g = 3 * t + j;
-    float s = 0.0f;
-    if (j < 3 && g < G) {
-      const size_t off = (size_t)c * x_stride + (size_t)m * K + (size_t)g * kGroup + (lane & 15) * 8;
-      if (m < M) {
-        const uint4 v = *reinterpret_cast<const uint4*>(X + off);
-        const uint32_t d[4] = {v.x, v.y, v.z, v.w};
+    const int m = blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (m >= mpad) return;                                // uniform per wave
+    const int passes = (K + 511) >> 9;
+    const uint16_t* xrow = X + (size_t)c * x_stride + (size_t)m * K;
+    uint16_t* prow = xp ? xp + (size_t)c * x_stride + (size_t)m * K : nullptr;
+    constexpr int kMaxPasses = 8;                         // 4096 channels per batch of passes
+    for (int i0 = 0; i0 < passes; i0 += kMaxPasses) {
+      uint4 v[kMaxPasses];
+#pragma unroll
+      for (int j = 0; j < kMaxPasses; ++j) {
+        const int k = (i0 + j) * 512 + lane * 8;
+        v[j] = (i0 + j < passes && k < K && m < M) ? *reinterpret_cast<const uint4*>(xrow + k)
+                                                     : make_uint4(0u, 0u, 0u, 0u);
+      }
+#pragma unroll
+      for (int j = 0; j < kMaxPasses; ++j) {
+        const int i = i0 + j;
+        if (i >= passes) break;                           // uniform
+        const int k = i * 512 + lane * 8;
+        const uint32_t d[4] = {v[j].x, v[j].y, v[j].z, v[j].w};
+        float s = 0.0f;
 #pragma unroll
         for (int q = 0; q < 4; ++q) s += __uint_as_float(d[q] << 16) + __uint_as_float(d[q] & 0xFFFF0000u);
-        if (xp) {
+        if (prow && k < K) {
           uint32_t e[4];
           pair_activations(d, e);
-          *reinterpret_cast<uint4*>(xp + off) = make_uint4(e[0], e[1], e[2], e[3]);
+          *reinterpret_cast<uint4*>(prow + k) = make_uint4(e[0], e[1], e[2], e[3]);
         }
-      } else if (xp) {
-        *reinterpret_cast<uint4*>(xp + off) = make_uint4(0u, 0u, 0u, 0u);
-      }
-    }
-#pragma unroll
-    for (int off = 1; off < 16; off <<= 1) s += __shfl_xor(s, off, kWave);
-    const float r0 = __shfl(s, 0, kWave), r1 = __shfl(s, 16, kWave), r2 = __shfl(s, 32, kWave);
-    if (lane == 0) {
-      const float rr[3] = {r0, r1, r2};
-#pragma unroll
-      for (int jj = 0; jj < 3; ++jj) {
-        const int gg = 3 * t + jj;
-        if (gg >= G) break;
-        uint32_t hi, mid, lo;
-        split3(-rr[jj], hi, mid, lo);
-        *reinterpret_cast<uint2*>(rsq + (size_t)c * rsq_stride + ((size_t)gg * mpad + m) * 4) =
-            make_uint2(hi | (mid << 16), lo);
+        s = row16_sum(s);
+        const int g = 4 * i + (lane >> 4);
+        if ((lane & 15) == 0 && g < G) {
+          uint32_t hi, mid, lo;
+          split3(-s, hi, mid, lo);
+          *reinterpret_cast<uint2*>(rsq + (size_t)c * rsq_stride + ((size_t)g * mpad + m) * 4) =
+              make_uint2(hi | (mid << 16), lo);
+        }
       }
     }
   } else {
+    const int T3 = (G + 2) / 3;
     const int npad = gemm_npad(N);
     const long long item = (long long)(blockIdx.x - rs_blocks) * 256 + threadIdx.x;
     if (item >= (long long)npad * T3) return;
@@ -100,7 +117,7 @@ int launch_gemm_prep(const uint16_t* X, size_t x_stride, int M, int K, int mpad,
                      uint16_t* rsq, size_t rsq_stride, uint32_t* szq, size_t szq_stride, uint16_t* xp, int C,
                      hipStream_t stream) {
   const int T3 = ((K >> 7) + 2) / 3;
-  const long long rs_blocks = ((long long)mpad * T3 + 3) / 4;
+  const long long rs_blocks = ((long long)mpad + 3) / 4;
   const long long sz_blocks = ((long long)gemm_npad(N) * T3 + 255) / 256;
   if (rs_blocks + sz_blocks == 0) return W4_OK;
   if (rs_blocks + sz_blocks > 0x7FFFFFFFLL || C > 65535) return W4_ERR_SHAPE;

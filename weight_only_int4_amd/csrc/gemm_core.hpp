@@ -247,12 +247,18 @@ __global__ __launch_bounds__(kGemmWaves * 64, GemmSmem<INT4>::kBlocksPerCU) void
       lds_copy16(woff[k - 4], src.w, st + SM::kB + (wave + 4 * (k - 4)) * 1024);
     }
   };
-  // the copies that go with MFMA step j of the group being computed (bf16: two
-  // per step from step 4 on)
+  // the copies that go with MFMA step j of the group being computed.  int4: the
+  // packed words and the column words / row sums first (steps 0-2), so that they
+  // can be waited for one group earlier than the activations (steps 3-6); bf16:
+  // two per step from step 4 on
   auto copies_of_step = [&](auto jidx, const GroupSrc& src, uint32_t st) {
     constexpr int j = decltype(jidx)::value;
-    if constexpr (j < L) copy_piece(std::integral_constant<int, j>{}, src, st);
-    if constexpr (j >= 4 && j + 4 < L) copy_piece(std::integral_constant<int, j + 4>{}, src, st);
+    if constexpr (INT4) {
+      if constexpr (j < L) copy_piece(std::integral_constant<int, j < 3 ? j + 4 : j - 3>{}, src, st);
+    } else {
+      if constexpr (j < L) copy_piece(std::integral_constant<int, j>{}, src, st);
+      if constexpr (j >= 4 && j + 4 < L) copy_piece(std::integral_constant<int, j + 4>{}, src, st);
+    }
   };
 
   // fragment reads of a 256-byte-row tile (activations; bf16 weights): row
@@ -281,9 +287,28 @@ __global__ __launch_bounds__(kGemmWaves * 64, GemmSmem<INT4>::kBlocksPerCU) void
   float sc_prev = 0.0f;
 
   const uint32_t nib_mask = opaque_vgpr(0x000F000Fu);
+  // int4: what a lane needs of a group besides the activations -- its 8 packed
+  // words, its column word and the row sums of its two row blocks.  Read one group
+  // ahead (see the pipeline below), so no group starts on an LDS round trip.
+  struct GroupMisc {
+    uint4 wv[2];
+    uint32_t szw;
+    uint2 rv[2];
+  };
+  auto read_misc = [&](const unsigned char* st, GroupMisc& gm) {
+#pragma unroll
+    for (int c = 0; c < 2; ++c)
+      gm.wv[c] = *reinterpret_cast<const uint4*>(st + SM::kB + col * 64 + (((2 * h + c) ^ ((col >> 2) & 3)) * 16));
+    gm.szw = reinterpret_cast<const uint32_t*>(st + SM::kS)[col];
+#pragma unroll
+    for (int bm = 0; bm < 2; ++bm) gm.rv[bm] = *reinterpret_cast<const uint2*>(st + SM::kR + (32 * bm + l32) * 8);
+  };
+  GroupMisc gcur{}, gnext{};
   // Computes the group in stage s; between its MFMA steps it issues the copies of
   // the group described by nsrc into the stage at LDS byte address nst.  The
-  // activation fragments of step j+1 are read before the MFMAs of step j.
+  // activation fragments of step j+1 are read before the MFMAs of step j.  int4:
+  // uses gcur and, during step 4, reads the next group's GroupMisc (stage s+1)
+  // into gnext.
   auto compute = [&](int s, const GroupSrc& nsrc, uint32_t nst) {
     const unsigned char* st = smem + s * SM::kStage;
     const unsigned char* sa = st + SM::kA;
@@ -295,23 +320,18 @@ __global__ __launch_bounds__(kGemmWaves * 64, GemmSmem<INT4>::kBlocksPerCU) void
 #pragma unroll
     for (int bm = 0; bm < 2; ++bm) af[0][bm] = frag(sa, bm, 0);
     if constexpr (INT4) {
-      // this lane's 8 words of its column
-      uint4 wv[2];
-#pragma unroll
-      for (int c = 0; c < 2; ++c)
-        wv[c] = *reinterpret_cast<const uint4*>(sb + col * 64 + (((2 * h + c) ^ ((col >> 2) & 3)) * 16));
+      (void)sb;
+      const uint4* wv = gcur.wv;
       // zero-point step operands: k-slots 0..2 (lane half 0) hold the row sum parts
       // against 128 + z three times; every other slot is 0
-      const uint32_t szw = reinterpret_cast<const uint32_t*>(st + SM::kS)[col];
-      const float sc_cur = __uint_as_float(szw << 16);
-      const uint32_t zbf = szw >> 16;
+      const float sc_cur = __uint_as_float(gcur.szw << 16);
+      const uint32_t zbf = gcur.szw >> 16;
       const bf16x8 zb = __builtin_bit_cast(bf16x8, make_uint4(h ? 0u : zbf * 0x10001u, h ? 0u : zbf, 0u, 0u));
       bf16x8 za[2];
 #pragma unroll
-      for (int bm = 0; bm < 2; ++bm) {
-        const uint2 rv = *reinterpret_cast<const uint2*>(st + SM::kR + (32 * bm + l32) * 8);
-        za[bm] = __builtin_bit_cast(bf16x8, make_uint4(h ? 0u : rv.x, h ? 0u : rv.y, 0u, 0u));
-      }
+      for (int bm = 0; bm < 2; ++bm)
+        za[bm] = __builtin_bit_cast(bf16x8, make_uint4(h ? 0u : gcur.rv[bm].x, h ? 0u : gcur.rv[bm].y, 0u, 0u));
+      const unsigned char* st_next = smem + ((s + 1) % S) * SM::kStage;
       __builtin_amdgcn_sched_barrier(0);
       auto step = [&](auto jidx) {
         constexpr int j = decltype(jidx)::value;
@@ -319,6 +339,7 @@ __global__ __launch_bounds__(kGemmWaves * 64, GemmSmem<INT4>::kBlocksPerCU) void
 #pragma unroll
           for (int bm = 0; bm < 2; ++bm) af[(j + 1) & 1][bm] = frag(sa, bm, j + 1);
         }
+        if constexpr (j == 4) read_misc(st_next, gnext);
         // keep the reads of step j+1 ahead of the MFMAs of step j (the scheduler
         // would otherwise sink each read next to its use and expose LDS latency)
         __builtin_amdgcn_sched_barrier(0);
@@ -356,6 +377,7 @@ __global__ __launch_bounds__(kGemmWaves * 64, GemmSmem<INT4>::kBlocksPerCU) void
       // this group's scale (columns past N have 0); its fold happens in step 0 of
       // the next group (or after the loop)
       sc_prev = sc_cur;
+      gcur = gnext;
     } else {
       bf16x8 bfc = frag(sb, wave, 0), bfn = bfc;
       __builtin_amdgcn_sched_barrier(0);
@@ -409,9 +431,18 @@ __global__ __launch_bounds__(kGemmWaves * 64, GemmSmem<INT4>::kBlocksPerCU) void
     copies_of_step(std::integral_constant<int, 7>{}, src, st);
   }
 
+  // int4: at the barrier of group g the copies still in flight are the
+  // activation copies of group g+1 (its other copies, issued first, are complete:
+  // every wave may read group g+1's GroupMisc during group g)
+  constexpr int kInFlight = INT4 ? 4 : (D - 1) * L;
+  if constexpr (INT4) {
+    wait_vmcnt<kInFlight>();
+    lds_barrier();
+    read_misc(smem, gcur);
+  }
   auto iteration = [&](auto sidx, int g) {
     constexpr int s = decltype(sidx)::value;
-    wait_vmcnt<(D - 1) * L>();
+    wait_vmcnt<kInFlight>();
     lds_barrier();
     const GroupSrc nsrc = group_src(min(g + D, G - 1));
     compute(s, nsrc, smem_base + ((s + D) % S) * SM::kStage);

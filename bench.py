@@ -181,12 +181,39 @@ def rotation_launches(torch, w4, X, qw, sc, qz, sym, min_bytes, make, M, K, N, f
 
 
 def measure_rotation(torch, launches, reps):
-    """Cold-cache average ms per launch: each rep runs every copy once in order."""
-    for l in launches:
-        l()
+    """Cold-cache average ms per launch: the launches over every copy, in order, are
+    captured in one HIP graph; each rep replays it once (no host launch cost)."""
+    g = capture_graph(torch, launches)
+    g.replay()
     torch.cuda.synchronize()
-    ms = time_events(torch, lambda: [l() for l in launches], reps) / len(launches)
+    ms = time_events(torch, g.replay, reps) / len(launches)
+    del g
     return ms
+
+
+def fused_sweep_launches(torch, w4, wl, packed, M):
+    """Variant of the sweep with the shared-input linears of a block launched as one
+    GEMV each: q|k|v (N = 4096) and gate|up (N = 12288), their packed rows
+    concatenated along N (contiguous in the N-major layout).  Four launches per
+    block: q|k|v, o, gate|up, down."""
+    by_block = {}
+    for b, layer, K, N, qw, sc, qz in packed:
+        by_block.setdefault(b, {})[layer] = (K, N, qw, sc, qz)
+    launches = []
+    for b in sorted(by_block):
+        L = by_block[b]
+        for group in ((0, 1, 2), (3,), (4, 5), (6,)):
+            K = L[group[0]][0]
+            N = sum(L[i][1] for i in group)
+            qw = torch.cat([L[i][2] for i in group], 0)
+            sc = torch.cat([L[i][3] for i in group], 0)
+            qz = torch.cat([L[i][4] for i in group], 0)
+            X = to_dev_bf16(torch, wl.decode_act(b, group[0], M))
+            Y = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+            launches.append(Launch(w4.gemv_launcher(X, qw, sc, qz, False, Y), gemv_bytes(M, K, N, False),
+                                   2 * M * K * N))
+    torch.cuda.synchronize()
+    return launches
 
 
 # ----------------------------------------------------------------------------- rows
@@ -259,8 +286,12 @@ def rows_gemv2048(torch, w4, wl, reps):
     X, W = to_dev_bf16(torch, Xn), to_dev_bf16(torch, Wn)
     qw, sc, qz = w4.awq_quantize_pack(W)
     Y = torch.empty((1, 2048), dtype=torch.bfloat16, device="cuda")
-    ms = time_events(torch, w4.gemv_launcher(X, qw, sc, qz, False, Y), reps * 10)
-    rows.append(row_gemv("gemv M=1 K=2048 N=2048 (cache-resident)", gemv_bytes(1, 2048, 2048, False), ms))
+    same = [w4.gemv_launcher(X, qw, sc, qz, False, Y)] * 100
+    g = capture_graph(torch, same)
+    ms = time_events(torch, g.replay, max(3, reps // 4)) / len(same)
+    del g
+    rows.append(row_gemv("gemv M=1 K=2048 N=2048 (cache-resident, graph of 100)", gemv_bytes(1, 2048, 2048, False),
+                         ms))
     ls = rotation_launches(torch, w4, X, qw, sc, qz, False, 600 << 20, w4.gemv_launcher, 1, 2048, 2048,
                            lambda m, k, n: 2 * m * k * n)
     ms = measure_rotation(torch, ls, 3)
@@ -423,6 +454,15 @@ def main(argv=None):
     want = set(x for x in args.only.split(",") if x) or {"sweeps", "large", "prefill", "gemv2048", "search"}
     if not args.step_only:
         rows = []
+        if "sweeps" in want and packed:
+            log("decode sweep M=1, fused shared-input linears")
+            fs = fused_sweep_launches(torch, w4, wl, packed, 1)
+            g = capture_graph(torch, fs)
+            ms = time_events(torch, g.replay, max(3, args.steps // 2))
+            rows.append(row_gemv("decode sweep M=1 fused q|k|v and gate|up (graph, variant)",
+                                 sum(l.nbytes for l in fs), ms, {"launches": len(fs)}))
+            del g, fs
+            torch.cuda.empty_cache()
         for M in ((4, 16) if "sweeps" in want and packed else ()):
             log(f"decode sweep M={M}")
             sw = sweep_launches(torch, w4, wl, packed, M)

@@ -124,9 +124,10 @@ int w4a16_gemv(const uint16_t* X, int M, int K, int N, const uint32_t* qweight,
  * [QSRT card] "Reproducible runtime": W4A16 serves prefill row counts.
  * Same operands and rounding as w4a16_gemv.
  *   workspace (always needed, > 0 bytes): X with every 8-channel run reordered
- *   for the packed-word expansion, the zero-point operands (split group row
- *   sums of X, split -sc (128 + z)) and the scales group-major.  Size query as
- *   in w4a16_gemv.  The size depends only on (M, K, N); about 2 M K bytes.
+ *   for the packed-word expansion, the negated group row sums of X (each as
+ *   three exact bf16 parts) and, per group and column, the scale with
+ *   bf16(128 + z).  Size query as in w4a16_gemv.  The size depends only on
+ *   (M, K, N); about 2 M K bytes.
  */
 int w4a16_gemm(const uint16_t* X, int M, int K, int N, const uint32_t* qweight,
                const uint16_t* scales, const uint32_t* qzeros, int symmetric, int group_size,

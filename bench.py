@@ -322,6 +322,32 @@ def rows_search(torch, w4, wl, reps):
     return rows
 
 
+def rows_convert(torch, w4, wl, reps):
+    """Streaming data-free symmetric conversion of a synthetic 3-shard checkpoint
+    (8 hidden-2048 blocks, 0.87 GB of bf16) written to a temporary directory."""
+    import shutil
+    import tempfile
+    from weight_only_int4_amd import convert as C
+    rows = []
+    tmp = tempfile.mkdtemp(prefix="w4ckpt_")
+    try:
+        src, dst = os.path.join(tmp, "src"), os.path.join(tmp, "dst")
+        wl.write_checkpoint(src, blocks=8, shards=3)
+        C.convert_checkpoint(src, dst)                  # warm: library, staging buffer, page cache
+        st = C.convert_checkpoint(src, dst)
+        n_w = st["bytes_converted"] // 2
+        alg = n_w * 2 + packed_bytes(1, GROUP, True) * n_w // GROUP     # bf16 read + packed written
+        rows.append({"name": "streaming symmetric conversion, 3 shards, 8 blocks (end to end, files on host)",
+                     "bytes": int(st["bytes_converted"]), "us": round(st["wall_s"] * 1e6, 1),
+                     "GB/s": round(st["bytes_converted"] / st["wall_s"] / 1e9, 2), "bound": "host IO",
+                     "tensors": st["converted"], "written_bytes": int(st["bytes_written"])})
+        rows.append(row_gemv("streaming symmetric conversion: quantize kernel only (sum over tensors)", alg,
+                             st["kernel_s"] * 1e3, {"weights": int(n_w)}))
+    finally:
+        shutil.rmtree(tmp, ignore_errors=True)
+    return rows
+
+
 # ----------------------------------------------------------------------------- CPU baseline
 
 def cpu_baseline(wl, budget_s=12.0):
@@ -362,7 +388,7 @@ def main(argv=None):
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
     ap.add_argument("--step-only", action="store_true", help="measure only the decode-sweep step")
     ap.add_argument("--only", default="", help="comma list of extra rows to measure "
-                    "(sweeps,large,prefill,gemv2048,search); default all")
+                    "(sweeps,large,prefill,gemv2048,search,convert); default all")
     ap.add_argument("--blocks", type=int, default=28)
     ap.add_argument("--skip-step", action="store_true",
                     help="profiling aid: skip the decode-sweep step (value is null) and run only --only rows")
@@ -451,7 +477,8 @@ def main(argv=None):
         torch.cuda.synchronize()
         torch.cuda.empty_cache()
 
-    want = set(x for x in args.only.split(",") if x) or {"sweeps", "large", "prefill", "gemv2048", "search"}
+    want = set(x for x in args.only.split(",") if x) or {"sweeps", "large", "prefill", "gemv2048", "search",
+                                                         "convert"}
     if not args.step_only:
         rows = []
         if "sweeps" in want and packed:
@@ -475,7 +502,7 @@ def main(argv=None):
         torch.cuda.empty_cache()
         reps = max(5, args.steps)
         for name, fn in (("large", rows_large), ("prefill", rows_prefill), ("gemv2048", rows_gemv2048),
-                         ("search", rows_search)):
+                         ("search", rows_search), ("convert", rows_convert)):
             if name in want:
                 log(f"rows: {name}")
                 rows += fn(torch, w4, wl, reps)

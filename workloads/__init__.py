@@ -23,6 +23,10 @@ Shapes and distributions follow the five workloads the method is measured on:
   magnitudes m_k = exp(N(0,1)) (LogNormal(0,1)), X[t,k] = m_k * N(0,1),
   W ~ N(0, 0.02).  These stand in for the calibration text of the pages
   (OpenR1-CMA rows, the Pile), which are not available.
+* ``checkpoint``  -- a sharded bf16 checkpoint of a decoder-only model with
+  hidden-2048 blocks (the seven linears above, two norm vectors per block),
+  token embedding and output head, for the streaming data-free conversion:
+  linears ~ N(0, 0.015), embedding / head ~ N(0, 0.02), norms ~ 1 + N(0, 0.05).
 
 Every tensor has its own ``numpy.random.SeedSequence`` entropy
 ``[0, workload_id, block, tensor_id]`` so any one can be regenerated alone.
@@ -33,7 +37,7 @@ from __future__ import annotations
 import numpy as np
 
 # workload ids used in the seed entropy
-GEMV_2048, DECODE_SWEEP, PREFILL, LARGE_SYM, AWQ_SEARCH = 1, 2, 3, 4, 5
+GEMV_2048, DECODE_SWEEP, PREFILL, LARGE_SYM, AWQ_SEARCH, CHECKPOINT = 1, 2, 3, 4, 5, 6
 
 # (name, K, N) of one hidden-2048 decoder block, in execution order
 BLOCK_LINEARS = (
@@ -137,3 +141,65 @@ def small_case(M: int, K: int, N: int, seed: int, w_std: float = 0.02, x_std: fl
     W = normal_bf16(rng, (N, K), w_std)
     X = normal_bf16(rng, (M, K), x_std)
     return X, W
+
+
+# ----------------------------------------------------------------------------- sharded checkpoint
+
+_CKPT_LINEARS = (("self_attn.q_proj", 0), ("self_attn.k_proj", 1), ("self_attn.v_proj", 2),
+                 ("self_attn.o_proj", 3), ("mlp.gate_proj", 4), ("mlp.up_proj", 5), ("mlp.down_proj", 6))
+
+
+def checkpoint_tensor_list(blocks: int, vocab: int = 8192, hidden: int = 2048):
+    """(name, shape) of every tensor of the synthetic checkpoint, in storage order.
+    Linear shapes are [N][K] (out x in); at hidden = 2048 they are BLOCK_LINEARS."""
+    scale = hidden / 2048
+    out = [("model.embed_tokens.weight", (vocab, hidden))]
+    for b in range(blocks):
+        out.append((f"model.layers.{b}.input_layernorm.weight", (hidden,)))
+        for name, li in _CKPT_LINEARS:
+            _, K, N = BLOCK_LINEARS[li]
+            out.append((f"model.layers.{b}.{name}.weight", (int(N * scale), int(K * scale))))
+        out.append((f"model.layers.{b}.post_attention_layernorm.weight", (hidden,)))
+    out.append(("model.norm.weight", (hidden,)))
+    out.append(("lm_head.weight", (vocab, hidden)))
+    return out
+
+
+def checkpoint_tensor(index: int, name: str, shape) -> np.ndarray:
+    """bf16 bits of tensor ``index`` of checkpoint_tensor_list (seeded by its index)."""
+    rng = _rng(CHECKPOINT, 0, index)
+    if len(shape) == 1:
+        return round_to_bf16_bits(1.0 + 0.05 * rng.standard_normal(size=shape, dtype=np.float32))
+    std = 0.02 if ("embed" in name or "lm_head" in name) else 0.015
+    return normal_bf16(rng, shape, std)
+
+
+def write_checkpoint(directory: str, blocks: int, shards: int, vocab: int = 8192, hidden: int = 2048):
+    """Write the synthetic checkpoint as ``shards`` safetensors files of about equal
+    size (tensors in storage order, never split), named model-0000i-of-0000n.
+    Returns the list of file paths."""
+    import os
+    import torch
+    from safetensors.torch import save_file
+    tensors = checkpoint_tensor_list(blocks, vocab, hidden)
+    total = sum(int(np.prod(s)) * 2 for _, s in tensors)
+    target = total / shards
+    os.makedirs(directory, exist_ok=True)
+    paths, cur, cur_bytes = [], {}, 0
+
+    def flush():
+        nonlocal cur, cur_bytes
+        path = os.path.join(directory, f"model-{len(paths) + 1:05d}-of-{shards:05d}.safetensors")
+        save_file(cur, path, metadata={"format": "pt"})
+        paths.append(path)
+        cur, cur_bytes = {}, 0
+
+    for i, (name, shape) in enumerate(tensors):
+        u16 = checkpoint_tensor(i, name, shape)
+        cur[name] = torch.from_numpy(np.ascontiguousarray(u16).view(np.int16)).view(torch.bfloat16)
+        cur_bytes += u16.nbytes
+        if cur_bytes >= target and len(paths) < shards - 1:
+            flush()
+    if cur:
+        flush()
+    return paths

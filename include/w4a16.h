@@ -119,6 +119,37 @@ int w4a16_gemv(const uint16_t* X, int M, int K, int N, const uint32_t* qweight,
                uint16_t* Y, void* workspace, size_t* workspace_bytes, void* stream);
 
 /*
+ * w4a8_quantize_activations -- per-row symmetric int8 quantization of decode
+ * activations for w4a8_gemv.  [QSRT card] "What is included" and "Size and
+ * memory": a W4A8 decode path over the same stored int4 weights; the pages do
+ * not define the 8-bit activation format, the reading used here is per row:
+ *   sx[m] = max_k |X[m][k]| / 127 (fp32 IEEE division; 1 for an all-zero row),
+ *   Xq[m][k] = clamp(rint(X[m][k] / sx[m]), -127, 127) (IEEE division, ties to even),
+ *   xsum[m][g] = sum of Xq[m][k] over group g (exact int32).
+ *   X [M][K] bf16 in, 1 <= M <= 16 (M > 16: W4_ERR_UNSUPPORTED; M = 0: no-op).
+ *   Xq [M][K] int8, sx [M] fp32, xsum [M][K/128] int32 out (device).
+ */
+int w4a8_quantize_activations(const uint16_t* X, int M, int K, int8_t* Xq, float* sx, int32_t* xsum,
+                              void* stream);
+
+/*
+ * w4a8_gemv -- W4A8 decode contraction for 1 <= M <= 16 rows on int8 matrix
+ * cores.  [QSRT card] "Reproducible runtime": decode batches of at most 16 rows
+ * take the W4A8 path, W4A16 serves everything above.
+ *   Y[m][n] = bf16( sx[m] * sum_g scales[n][g] * (sum_{k in g} Xq[m][k] q[n][k]
+ *                                                 - z[n][g] xsum[m][g]) )
+ *   with q the stored nibble, z the zero point (8 when symmetric); the group
+ *   sums are exact int32, the scaling fp32.  Xq, sx, xsum as written by
+ *   w4a8_quantize_activations; qweight/scales/qzeros as for w4a16_gemv.
+ *   M > 16: W4_ERR_UNSUPPORTED; K above 50,944 channels (398 groups: the
+ *   per-workgroup staging of scales and sums would exceed 64 KB of LDS):
+ *   W4_ERR_UNSUPPORTED.
+ */
+int w4a8_gemv(const int8_t* Xq, const float* sx, const int32_t* xsum, int M, int K, int N,
+              const uint32_t* qweight, const uint16_t* scales, const uint32_t* qzeros, int symmetric,
+              int group_size, uint16_t* Y, void* stream);
+
+/*
  * w4a16_gemm -- prefill contraction Y = X W_hat^T for any M >= 1 (intended for
  * M >= 64), on MFMA bf16 matrix cores with LDS-staged activation tiles.
  * [QSRT card] "Reproducible runtime": W4A16 serves prefill row counts.

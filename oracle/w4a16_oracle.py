@@ -176,6 +176,50 @@ def linear(X_bf16: np.ndarray, W_hat: np.ndarray) -> np.ndarray:
     return bf16_to_f32(X_bf16).astype(np.float64) @ np.asarray(W_hat, dtype=np.float64).T
 
 
+# --------------------------------------------------------------------------- W4A8 decode
+
+INT8_MAX = 127       # symmetric int8 activation codes in [-127, 127] (reading)
+
+
+def quantize_activations_int8(X_bf16: np.ndarray):
+    """Per-row symmetric int8 activations for the W4A8 decode path.
+
+    [QSRT card] "What is included" / "Size and memory": W4A8 decode runs on the
+    same stored int4 weights; the pages do not define the 8-bit activation format.
+    Reading: per row m, sx = max_k |x| / 127 in fp32 (IEEE division; 1 for an
+    all-zero row), xq = clamp(rint(x / sx), -127, 127) with the IEEE fp32 quotient,
+    ties to even.  Returns (Xq int8 [M][K], sx fp32 [M], xsum int64 [M][K/128]:
+    the code sum of every group).
+    """
+    x = bf16_to_f32(X_bf16)
+    M, K = x.shape
+    amax = np.abs(x).max(axis=1)
+    sx = np.where(amax > 0, amax / np.float32(INT8_MAX), np.float32(1.0)).astype(np.float32)
+    q = np.rint(x / sx[:, None])
+    xq = np.clip(q, -INT8_MAX, INT8_MAX).astype(np.int8)
+    xsum = xq.astype(np.int64).reshape(M, K // GROUP, GROUP).sum(axis=2)
+    return xq, sx, xsum
+
+
+def w4a8_linear(Xq, sx, qweight, scales, qzeros, K: int, symmetric: bool) -> np.ndarray:
+    """Y[m][n] = sx[m] * sum_g sc[n][g] * sum_{k in g} xq[m][k] (q[n][k] - z[n][g]).
+
+    [QSRT card] "Reproducible runtime": the W4A8 decode contraction.  The group
+    sums are exact integers; the scaling and the sum over groups are fp64.
+    """
+    codes = unpack_nibbles(qweight, K).astype(np.int64)
+    N = codes.shape[0]
+    G = K // GROUP
+    z = (np.full((N, G), SYM_OFFSET, dtype=np.int64) if symmetric
+         else unpack_nibbles(qzeros, G).astype(np.int64))
+    d = codes.reshape(N, G, GROUP) - z[:, :, None]                                # q - z
+    xq = np.asarray(Xq, dtype=np.int64).reshape(-1, G, GROUP)
+    isum = np.einsum("mgk,ngk->mng", xq, d)                                       # exact int64
+    sc = bf16_to_f32(scales).astype(np.float64)                                   # [N][G]
+    y = (isum.astype(np.float64) * sc[None, :, :]).sum(axis=2)
+    return y * np.asarray(sx, dtype=np.float64)[:, None]
+
+
 # --------------------------------------------------------------------------- AWQ search
 
 def act_mean_abs(X_bf16: np.ndarray) -> np.ndarray:

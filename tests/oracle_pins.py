@@ -398,7 +398,63 @@ def check_division_ties():
     assert np.array_equal(d[0].astype(np.float64), np.array(ref[0]))
 
 
+def check_w4a8_activation_codes():
+    """Per-row int8 activations: codes in [-127, 127], the absmax element of every
+    nonzero row maps to +-127 exactly, an all-zero row gives scale 1 and codes 0,
+    integer rows containing +-127 come back unchanged (scale 1), quotients at
+    k + 1/2 round to the even neighbour, and xsum is the per-group code sum
+    (pure-Python loop)."""
+    rng = np.random.default_rng(7)
+    X = round_to_bf16_bits(rng.standard_normal((5, 384)).astype(np.float32) * 3)
+    X[3] = 0
+    xq, sx, xs = O.quantize_activations_int8(X)
+    assert xq.dtype == np.int8 and xq.min() >= -127 and xq.max() <= 127
+    x = O.bf16_to_f32(X)
+    for m in (0, 1, 2, 4):
+        j = int(np.argmax(np.abs(x[m])))
+        assert abs(int(xq[m, j])) == 127 and np.sign(xq[m, j]) == np.sign(x[m, j])
+        assert sx[m] == np.float32(np.abs(x[m]).max()) / np.float32(127)
+    assert sx[3] == 1.0 and not xq[3].any()
+    ints = np.array([[127, -3, 5, 0] * 32, [-127, 126, 1, -1] * 32], dtype=np.float32)
+    q2, s2, _ = O.quantize_activations_int8(round_to_bf16_bits(ints))
+    assert np.all(s2 == 1.0) and np.array_equal(q2.astype(np.float32), ints)
+    # ties: row absmax 127 * 2 -> sx = 2, values 2k + 1 divide to k + 1/2 exactly
+    half = np.array([[254.0] + [2 * k + 1.0 for k in range(127)]], dtype=np.float32)
+    q3, s3, _ = O.quantize_activations_int8(round_to_bf16_bits(half))
+    assert s3[0] == 2.0
+    for k in range(127):
+        want = k if k % 2 == 0 else k + 1
+        assert int(q3[0, 1 + k]) == min(want, 127), k
+    for m in range(5):
+        for g in range(3):
+            tot = 0
+            for k in range(128 * g, 128 * g + 128):
+                tot += int(xq[m, k])
+            assert xs[m, g] == tot
+
+
+def check_w4a8_linear_reduces_to_dequant_matmul():
+    """The W4A8 contraction equals a library fp64 matmul of the dequantized codes:
+    Y = diag(sx) (Xq W_hat^T) with W_hat the W4A16 dequantization, asymmetric and
+    symmetric, and a one-hot code row picks sx * W_hat[n][k] * 127."""
+    W = _rand_w(N=9, K=384, seed=11)
+    rng = np.random.default_rng(12)
+    X = round_to_bf16_bits(rng.standard_normal((3, 384)).astype(np.float32))
+    xq, sx, _ = O.quantize_activations_int8(X)
+    for sym in (False, True):
+        qw, sc, qz = O.quantize_pack(W, None, 1.0, sym)
+        Wh = O.dequantize(qw, sc, qz, 384, sym).astype(np.float64)
+        y = O.w4a8_linear(xq, sx, qw, sc, qz, 384, sym)
+        ref = sx.astype(np.float64)[:, None] * (xq.astype(np.float64) @ Wh.T)
+        assert np.allclose(y, ref, rtol=1e-12, atol=1e-12), sym
+        onehot = np.zeros((1, 384), dtype=np.int8)
+        onehot[0, 200] = 127
+        y1 = O.w4a8_linear(onehot, np.array([0.5], np.float32), qw, sc, qz, 384, sym)
+        assert np.array_equal(y1[0], 0.5 * 127 * Wh[:, 200])
+
+
 ALL_CHECKS = [
+    check_w4a8_activation_codes, check_w4a8_linear_reduces_to_dequant_matmul,
     check_division_ties,
     check_bf16_golden, check_bf16_against_torch, check_worked_groups, check_pack_golden,
     check_pack_roundtrip, check_ranges_and_error_bound, check_asym_range_covers_group,

@@ -86,6 +86,28 @@ def test_gemv_validation_and_size_query(lib):
     assert f(A, 0, 256, 8, A, A, A, 0, 128, A, None, None, None) == 0      # M = 0: empty
 
 
+def test_w4a8_validation(lib):
+    f = lib.w4a8_quantize_activations
+    assert f(A, 17, 256, A, A, A, None) == -4
+    assert f(A, 1, 200, A, A, A, None) == -2
+    assert f(A, -1, 256, A, A, A, None) == -2
+    assert f(None, 1, 256, A, A, A, None) == -1
+    assert f(A, 1, 256, A, None, A, None) == -1
+    assert f(MIS, 1, 256, A, A, A, None) == -3
+    assert f(A, 0, 256, A, A, A, None) == 0                         # M = 0: empty
+    g = lib.w4a8_gemv
+    assert g(A, A, A, 17, 256, 8, A, A, A, 0, 128, A, None) == -4
+    assert g(A, A, A, 1, 200, 8, A, A, A, 0, 128, A, None) == -2
+    assert g(A, A, A, 1, 256, 8, A, A, A, 0, 64, A, None) == -4
+    assert g(A, A, A, 1, 51072, 8, A, A, A, 0, 128, A, None) == -4   # 399 groups: LDS staging too large
+    assert g(None, A, A, 1, 256, 8, A, A, A, 0, 128, A, None) == -1
+    assert g(A, A, None, 1, 256, 8, A, A, A, 0, 128, A, None) == -1
+    assert g(A, A, A, 1, 256, 8, A, A, None, 0, 128, A, None) == -1  # asymmetric needs qzeros
+    assert g(A, A, A, 1, 256, 8, A, A, A, 1, 128, A, None) == -1     # symmetric forbids them
+    assert g(MIS, A, A, 1, 256, 8, A, A, A, 0, 128, A, None) == -3
+    assert g(A, A, A, 0, 256, 8, A, A, A, 0, 128, A, None) == 0
+
+
 def test_gemm_size_query(lib):
     sz = ctypes.c_size_t(0)
     f = lib.w4a16_gemm

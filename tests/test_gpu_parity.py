@@ -385,3 +385,71 @@ def test_search_small():
         assert np.array_equal(res["s"].cpu().numpy(), ref["s"])
         assert np.max(np.abs(lr - ref["ratio_losses"]) / ref["ratio_losses"]) <= 2e-3
         assert _argmin_ok(res["ratio_index"], ref["ratio_index"], ref["ratio_losses"])
+
+
+# ----------------------------------------------------------------------------- W4A8 decode
+
+def _w4a8_inputs(X):
+    xq, sx, xs = O.quantize_activations_int8(X)
+    return (torch.from_numpy(xq).cuda(), torch.from_numpy(sx).cuda(),
+            torch.from_numpy(xs.astype(np.int32)).cuda(), xq, sx, xs)
+
+
+@pytest.mark.parametrize("M,K", [(1, 128), (5, 2048), (16, 5120), (3, 17408)])
+def test_w4a8_quantize_activations_bit_exact(M, K):
+    say("w4a8 quantize", M, K)
+    X, _ = wl.small_case(M, K, 1, 31)
+    X[M - 1, : K // 2] = 0                                  # a half-zero row
+    if M > 1:
+        X[0] = 0                                            # an all-zero row
+    Xq, sx, xs = w4.w4a8_quantize_activations(to_bf16(X))
+    torch.cuda.synchronize()
+    oq, osx, oxs = O.quantize_activations_int8(X)
+    assert np.array_equal(Xq.cpu().numpy(), oq)
+    assert np.array_equal(sx.cpu().numpy().view(np.uint32), osx.view(np.uint32))
+    assert np.array_equal(xs.cpu().numpy(), oxs.astype(np.int32))
+
+
+@pytest.mark.parametrize("M,K,N", [(1, 2048, 300), (4, 2048, 129), (16, 2048, 64), (7, 128, 33), (2, 6144, 17),
+                                   (16, 17408, 40), (1, 5120, 1000), (9, 4224, 31)])
+@pytest.mark.parametrize("sym", [False, True])
+def test_w4a8_gemv(M, K, N, sym):
+    say("w4a8 gemv", M, K, N, sym)
+    X, W = wl.small_case(M, K, N, 41)
+    qw, sc, qz = _packed(W, sym)
+    gq, gsx, gxs, xq, sx, _ = _w4a8_inputs(X)
+    Y = w4.w4a8_gemv(gq, gsx, gxs, to_i32(qw), to_bf16(sc), None if sym else to_i32(qz), sym)
+    torch.cuda.synchronize()
+    y = bf16_values(bits16(Y))
+    ref = O.w4a8_linear(xq, sx, qw, sc, qz, K, sym)
+    _fro_ok(y, ref)
+    assert _elementwise_ok(y, ref) == 0
+
+
+@pytest.mark.parametrize("shape", [0, 1])
+@pytest.mark.parametrize("M", [1, 16])
+def test_w4a8_gemv_large_full_size(shape, M):
+    """27B-shaped symmetric linears; activations quantized on the GPU (bit-exact
+    with the oracle's); oracle on every 8th output channel."""
+    W = wl.large_weight(shape)
+    X = wl.large_act(shape, M)
+    qw, sc, _ = O.quantize_pack(W, None, 1.0, True)
+    say("w4a8 large", shape, M)
+    Xq, sx, xs = w4.w4a8_quantize_activations(to_bf16(X))
+    Y = w4.w4a8_gemv(Xq, sx, xs, to_i32(qw), to_bf16(sc), None, True)
+    torch.cuda.synchronize()
+    oq, osx, _ = O.quantize_activations_int8(X)
+    assert np.array_equal(Xq.cpu().numpy(), oq)
+    y = bf16_values(bits16(Y))
+    cols = np.arange(0, W.shape[0], 8)
+    ref = O.w4a8_linear(oq, osx, qw[cols], sc[cols], None, W.shape[1], True)
+    _fro_ok(y[:, cols], ref)
+    assert _elementwise_ok(y[:, cols], ref) == 0
+
+
+def test_w4a8_rejects_m17():
+    _, W = wl.small_case(1, 256, 8, 1)
+    qw, sc, qz = _packed(W, False)
+    X = np.zeros((17, 256), dtype=np.uint16)
+    with pytest.raises(w4.W4Error):
+        w4.w4a8_quantize_activations(to_bf16(X))

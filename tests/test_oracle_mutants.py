@@ -51,6 +51,13 @@ MUTANTS = {
                        "return (u >> np.uint64(16)).astype(np.uint16)"),
     "bf16_ties_away": ("return ((u + np.uint64(0x7FFF) + lsb) >> np.uint64(16)).astype(np.uint16)",
                        "return ((u + np.uint64(0x8000)) >> np.uint64(16)).astype(np.uint16)"),
+    "w4a8_scale_128": ("amax / np.float32(INT8_MAX)", "amax / np.float32(128.0)"),
+    "w4a8_floor": ("q = np.rint(x / sx[:, None])", "q = np.floor(x / sx[:, None])"),
+    "w4a8_half_up": ("q = np.rint(x / sx[:, None])", "q = np.floor(x / sx[:, None] + np.float32(0.5))"),
+    "w4a8_zero_ignored": ("d = codes.reshape(N, G, GROUP) - z[:, :, None]", "d = codes.reshape(N, G, GROUP) - 8"),
+    "w4a8_no_act_scale": ("return y * np.asarray(sx, dtype=np.float64)[:, None]", "return y"),
+    "w4a8_group_sum_shifted": ("xsum = xq.astype(np.int64).reshape(M, K // GROUP, GROUP).sum(axis=2)",
+                               "xsum = np.roll(xq.astype(np.int64), 1, axis=1).reshape(M, K // GROUP, GROUP).sum(axis=2)"),
     "clip_after_scale_choice": ("        absmax = np.abs(v).max(axis=2, keepdims=True)\n    if symmetric:",
                                 "    if symmetric:"),
 }

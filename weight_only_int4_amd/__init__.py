@@ -20,7 +20,7 @@ import torch
 __all__ = [
     "W4Error", "library_path", "load_library", "awq_quantize_pack", "w4a16_gemv", "w4a16_gemm",
     "awq_grid_loss", "awq_search", "GROUP_SIZE", "GEMV_MAX_M", "gemv_launcher", "gemm_launcher",
-    "probe_stream_read", "probe_empty",
+    "w4a8_quantize_activations", "w4a8_gemv", "w4a8_gemv_launcher", "probe_stream_read", "probe_empty",
 ]
 
 GROUP_SIZE = 128
@@ -37,6 +37,8 @@ _SIGNATURES = {
     "awq_grid_loss": ([_vp, _i, _i, _i, _vp, _vp, _vp, _vp, _i, _i, _i, _vp, _vp, _sz, _vp], _i),
     "w4_probe_stream_read": ([_vp, ctypes.c_size_t, _i, _i, _i, _vp, _vp], _i),
     "w4_probe_empty": ([_vp], _i),
+    "w4a8_quantize_activations": ([_vp, _i, _i, _vp, _vp, _vp, _vp], _i),
+    "w4a8_gemv": ([_vp, _vp, _vp, _i, _i, _i, _vp, _vp, _vp, _i, _i, _vp, _vp], _i),
     "awq_search": ([_vp, _i, _i, _i, _vp, ctypes.POINTER(ctypes.c_double), _i,
                     ctypes.POINTER(ctypes.c_double), _i, _i, _i, ctypes.POINTER(ctypes.c_float),
                     ctypes.POINTER(ctypes.c_int), ctypes.POINTER(ctypes.c_int), _vp, _vp, _sz, _vp], _i),
@@ -164,6 +166,66 @@ def w4a16_gemv(X, qweight, scales, qzeros=None, symmetric: bool = False, Y=None,
     _check(lib.w4a16_gemv(_ptr(X), M, K, N, _ptr(qweight), _ptr(scales), _ptr(qz), int(symmetric), GROUP_SIZE,
                           _ptr(Y), _ptr(ws), None if wsb is None else ctypes.byref(wsb), _stream(dev)))
     return Y
+
+
+def w4a8_quantize_activations(X, Xq=None, sx=None, xsum=None):
+    """Per-row int8 activations for the W4A8 decode path: returns (Xq int8 [M][K],
+    sx fp32 [M], xsum int32 [M][K/128])."""
+    lib = load_library()
+    _need(X, torch.bfloat16, "X", 2)
+    M, K = X.shape
+    dev = X.device
+    Xq = torch.empty((M, K), dtype=torch.int8, device=dev) if Xq is None else Xq
+    sx = torch.empty(M, dtype=torch.float32, device=dev) if sx is None else sx
+    xsum = torch.empty((M, K // GROUP_SIZE), dtype=torch.int32, device=dev) if xsum is None else xsum
+    _check(lib.w4a8_quantize_activations(_ptr(X), M, K, _ptr(Xq), _ptr(sx), _ptr(xsum), _stream(dev)))
+    return Xq, sx, xsum
+
+
+def _w4a8_args(Xq, sx, xsum, qweight, scales, qzeros, symmetric):
+    _need(Xq, torch.int8, "Xq", 2)
+    _need(sx, torch.float32, "sx", 1)
+    _need(xsum, torch.int32, "xsum", 2)
+    _need(qweight, torch.int32, "qweight", 2)
+    _need(scales, torch.bfloat16, "scales", 2)
+    if not symmetric:
+        _need(qzeros, torch.int32, "qzeros", 2)
+    M, K = Xq.shape
+    N = qweight.shape[0]
+    if qweight.shape[1] * 8 != K or sx.shape[0] != M or tuple(xsum.shape) != (M, K // GROUP_SIZE):
+        raise ValueError("shapes of Xq [M][K], sx [M], xsum [M][K/128], qweight [N][K/8] disagree")
+    return M, K, N
+
+
+def w4a8_gemv(Xq, sx, xsum, qweight, scales, qzeros=None, symmetric: bool = False, Y=None):
+    """W4A8 decode GEMV: Y [M][N] bf16 from int8 activations (w4a8_quantize_activations)."""
+    lib = load_library()
+    M, K, N = _w4a8_args(Xq, sx, xsum, qweight, scales, qzeros, symmetric)
+    dev = Xq.device
+    if Y is None:
+        Y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    _check(lib.w4a8_gemv(_ptr(Xq), _ptr(sx), _ptr(xsum), M, K, N, _ptr(qweight), _ptr(scales),
+                         _ptr(None if symmetric else qzeros), int(symmetric), GROUP_SIZE, _ptr(Y), _stream(dev)))
+    return Y
+
+
+def w4a8_gemv_launcher(Xq, sx, xsum, qweight, scales, qzeros, symmetric: bool, Y):
+    """As gemv_launcher, for w4a8_gemv."""
+    lib = load_library()
+    M, K, N = _w4a8_args(Xq, sx, xsum, qweight, scales, qzeros, symmetric)
+    _need(Y, torch.bfloat16, "Y", 2)
+    if tuple(Y.shape) != (M, N):
+        raise ValueError("Y must be [M][N]")
+    qz = None if symmetric else qzeros
+    args = (_ptr(Xq), _ptr(sx), _ptr(xsum), M, K, N, _ptr(qweight), _ptr(scales), _ptr(qz), int(symmetric),
+            GROUP_SIZE, _ptr(Y))
+    dev = Xq.device
+
+    def launch():
+        _check(lib.w4a8_gemv(*args, _stream(dev)))
+
+    launch.tensors = (Xq, sx, xsum, qweight, scales, qz, Y)
+    return launch
 
 
 def w4a16_gemm(X, qweight, scales, qzeros=None, symmetric: bool = False, Y=None, workspace=None):

@@ -33,6 +33,14 @@ int launch_gemv(const uint16_t* X, int M, int K, int N, const uint32_t* qweight,
                 const uint16_t* scales, const uint32_t* qzeros, int symmetric, uint16_t* Y,
                 void* workspace, hipStream_t stream);
 
+// ---------------------------------------------------------------- W4A8 decode (M <= 16)
+int launch_w4a8_quantize(const uint16_t* X, int M, int K, int8_t* Xq, float* sx, int32_t* xsum,
+                         hipStream_t stream);
+size_t w4a8_gemv_lds_bytes(int K, int waves);
+int launch_w4a8_gemv(const int8_t* Xq, const float* sx, const int32_t* xsum, int M, int K, int N,
+                     const uint32_t* qweight, const uint16_t* scales, const uint32_t* qzeros, int symmetric,
+                     uint16_t* Y, hipStream_t stream);
+
 // ---------------------------------------------------------------- GEMM (MFMA)
 size_t gemm_workspace_bytes(int M, int K, int N);
 int launch_gemm(const uint16_t* X, int M, int K, int N, const uint32_t* qweight,

@@ -91,6 +91,33 @@ int w4a16_gemv(const uint16_t* X, int M, int K, int N, const uint32_t* qweight, 
                      static_cast<hipStream_t>(stream));
 }
 
+int w4a8_quantize_activations(const uint16_t* X, int M, int K, int8_t* Xq, float* sx, int32_t* xsum,
+                              void* stream) {
+  if (M < 0 || K <= 0 || K % kGroup != 0) return W4_ERR_SHAPE;
+  if (M > W4_GEMV_MAX_M) return W4_ERR_UNSUPPORTED;
+  if (M == 0) return W4_OK;
+  if (!X || !Xq || !sx || !xsum) return W4_ERR_NULL;
+  if (misaligned(X) || misaligned(Xq)) return W4_ERR_ALIGN;
+  return launch_w4a8_quantize(X, M, K, Xq, sx, xsum, static_cast<hipStream_t>(stream));
+}
+
+int w4a8_gemv(const int8_t* Xq, const float* sx, const int32_t* xsum, int M, int K, int N,
+              const uint32_t* qweight, const uint16_t* scales, const uint32_t* qzeros, int symmetric,
+              int group_size, uint16_t* Y, void* stream) {
+  int st = check_weight_shape(N, K, group_size);
+  if (st) return st;
+  if (M < 0) return W4_ERR_SHAPE;
+  if (M > W4_GEMV_MAX_M) return W4_ERR_UNSUPPORTED;
+  if (w4a8_gemv_lds_bytes(K, 8) > 64 * 1024) return W4_ERR_UNSUPPORTED;
+  if (M == 0 || N == 0) return W4_OK;
+  if (!Xq || !sx || !xsum || !Y) return W4_ERR_NULL;
+  st = check_packed(qweight, scales, qzeros, symmetric);
+  if (st) return st;
+  if (misaligned(Xq) || misaligned(Y)) return W4_ERR_ALIGN;
+  return launch_w4a8_gemv(Xq, sx, xsum, M, K, N, qweight, scales, qzeros, symmetric, Y,
+                          static_cast<hipStream_t>(stream));
+}
+
 int w4a16_gemm(const uint16_t* X, int M, int K, int N, const uint32_t* qweight, const uint16_t* scales,
                const uint32_t* qzeros, int symmetric, int group_size, uint16_t* Y, void* workspace,
                size_t* workspace_bytes, void* stream) {

@@ -151,6 +151,21 @@ def sweep_launches(torch, w4, wl, packed, M):
     return launches
 
 
+def w4a8_sweep_launches(torch, w4, wl, packed, M):
+    """The decode sweep on the W4A8 path: activations quantized once up front (in a
+    real decoder the previous op emits them), one w4a8_gemv per linear."""
+    launches = []
+    for b, layer, K, N, qw, sc, qz in packed:
+        X = to_dev_bf16(torch, wl.decode_act(b, layer, M))
+        Xq, sx, xs = w4.w4a8_quantize_activations(X)
+        Y = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+        launches.append(Launch(w4.w4a8_gemv_launcher(Xq, sx, xs, qw, sc, qz, False, Y),
+                               packed_bytes(N, K, False) + M * K + M * 4 + M * (K // GROUP) * 4 + M * N * 2,
+                               2 * M * K * N))
+    torch.cuda.synchronize()
+    return launches
+
+
 def capture_graph(torch, launches):
     g = torch.cuda.CUDAGraph()
     s = torch.cuda.Stream()
@@ -253,6 +268,19 @@ def rows_large(torch, w4, wl, reps):
                                    lambda m, k, n: 2 * m * k * n)
             ms = measure_rotation(torch, ls, max(2, reps // 4))
             rows.append(row_gemv(f"gemv cold M={M} K={K} N={N} sym", ls[0].nbytes, ms,
+                                 {"cache": f"cold ({len(ls)} rotating copies)"}))
+            del ls
+        for M in (1, 16):
+            X = to_dev_bf16(torch, wl.large_act(si, M))
+            Xq, sx, xs = w4.w4a8_quantize_activations(X)
+            nbytes = packed_bytes(N, K, True) + M * K + M * 4 + M * (K // GROUP) * 4 + M * N * 2
+            ls = rotation_launches(torch, w4, None, qw, sc, None, True, 600 << 20,
+                                   lambda _x, q2, s2, z2, sym, Y: w4.w4a8_gemv_launcher(Xq, sx, xs, q2, s2, z2, sym, Y),
+                                   M, K, N, lambda m, k, n: 2 * m * k * n)
+            for l in ls:
+                l.nbytes = nbytes
+            ms = measure_rotation(torch, ls, max(2, reps // 4))
+            rows.append(row_gemv(f"W4A8 gemv cold M={M} K={K} N={N} sym", nbytes, ms,
                                  {"cache": f"cold ({len(ls)} rotating copies)"}))
             del ls
         for M in (64, 512):
@@ -388,7 +416,7 @@ def main(argv=None):
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
     ap.add_argument("--step-only", action="store_true", help="measure only the decode-sweep step")
     ap.add_argument("--only", default="", help="comma list of extra rows to measure "
-                    "(sweeps,large,prefill,gemv2048,search,convert); default all")
+                    "(sweeps,w4a8,large,prefill,gemv2048,search,convert); default all")
     ap.add_argument("--blocks", type=int, default=28)
     ap.add_argument("--skip-step", action="store_true",
                     help="profiling aid: skip the decode-sweep step (value is null) and run only --only rows")
@@ -477,8 +505,8 @@ def main(argv=None):
         torch.cuda.synchronize()
         torch.cuda.empty_cache()
 
-    want = set(x for x in args.only.split(",") if x) or {"sweeps", "large", "prefill", "gemv2048", "search",
-                                                         "convert"}
+    want = set(x for x in args.only.split(",") if x) or {"sweeps", "w4a8", "large", "prefill", "gemv2048",
+                                                         "search", "convert"}
     if not args.step_only:
         rows = []
         if "sweeps" in want and packed:
@@ -489,6 +517,14 @@ def main(argv=None):
             rows.append(row_gemv("decode sweep M=1 fused q|k|v and gate|up (graph, variant)",
                                  sum(l.nbytes for l in fs), ms, {"launches": len(fs)}))
             del g, fs
+            torch.cuda.empty_cache()
+        for M in ((1, 4, 16) if "w4a8" in want and packed else ()):
+            log(f"W4A8 decode sweep M={M}")
+            sw = w4a8_sweep_launches(torch, w4, wl, packed, M)
+            g = capture_graph(torch, sw)
+            ms = time_events(torch, g.replay, max(3, args.steps // 2))
+            rows.append(row_gemv(f"W4A8 decode sweep M={M} (graph)", sum(l.nbytes for l in sw), ms))
+            del g, sw
             torch.cuda.empty_cache()
         for M in ((4, 16) if "sweeps" in want and packed else ()):
             log(f"decode sweep M={M}")

@@ -141,9 +141,8 @@ int w4a8_quantize_activations(const uint16_t* X, int M, int K, int8_t* Xq, float
  *   with q the stored nibble, z the zero point (8 when symmetric); the group
  *   sums are exact int32, the scaling fp32.  Xq, sx, xsum as written by
  *   w4a8_quantize_activations; qweight/scales/qzeros as for w4a16_gemv.
- *   M > 16: W4_ERR_UNSUPPORTED; K above 50,944 channels (398 groups: the
- *   per-workgroup staging of scales and sums would exceed 64 KB of LDS):
- *   W4_ERR_UNSUPPORTED.
+ *   M > 16: W4_ERR_UNSUPPORTED; K above 51,200 channels (400 groups, 25 per
+ *   wave of a 16-wave workgroup): W4_ERR_UNSUPPORTED.
  */
 int w4a8_gemv(const int8_t* Xq, const float* sx, const int32_t* xsum, int M, int K, int N,
               const uint32_t* qweight, const uint16_t* scales, const uint32_t* qzeros, int symmetric,

@@ -99,7 +99,7 @@ def test_w4a8_validation(lib):
     assert g(A, A, A, 17, 256, 8, A, A, A, 0, 128, A, None) == -4
     assert g(A, A, A, 1, 200, 8, A, A, A, 0, 128, A, None) == -2
     assert g(A, A, A, 1, 256, 8, A, A, A, 0, 64, A, None) == -4
-    assert g(A, A, A, 1, 51072, 8, A, A, A, 0, 128, A, None) == -4   # 399 groups: LDS staging too large
+    assert g(A, A, A, 1, 51328, 8, A, A, A, 0, 128, A, None) == -4   # 401 groups: beyond the unrolled kernels
     assert g(None, A, A, 1, 256, 8, A, A, A, 0, 128, A, None) == -1
     assert g(A, A, None, 1, 256, 8, A, A, A, 0, 128, A, None) == -1
     assert g(A, A, A, 1, 256, 8, A, A, None, 0, 128, A, None) == -1  # asymmetric needs qzeros

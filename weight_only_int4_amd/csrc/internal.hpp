@@ -36,7 +36,7 @@ int launch_gemv(const uint16_t* X, int M, int K, int N, const uint32_t* qweight,
 // ---------------------------------------------------------------- W4A8 decode (M <= 16)
 int launch_w4a8_quantize(const uint16_t* X, int M, int K, int8_t* Xq, float* sx, int32_t* xsum,
                          hipStream_t stream);
-size_t w4a8_gemv_lds_bytes(int K, int waves);
+int w4a8_plan(int K, int N, int cus, int* ni, int* waves, size_t* lds);   // W4_ERR_UNSUPPORTED when K is too long
 int launch_w4a8_gemv(const int8_t* Xq, const float* sx, const int32_t* xsum, int M, int K, int N,
                      const uint32_t* qweight, const uint16_t* scales, const uint32_t* qzeros, int symmetric,
                      uint16_t* Y, hipStream_t stream);

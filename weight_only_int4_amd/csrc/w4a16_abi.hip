@@ -108,7 +108,7 @@ int w4a8_gemv(const int8_t* Xq, const float* sx, const int32_t* xsum, int M, int
   if (st) return st;
   if (M < 0) return W4_ERR_SHAPE;
   if (M > W4_GEMV_MAX_M) return W4_ERR_UNSUPPORTED;
-  if (w4a8_gemv_lds_bytes(K, 8) > 64 * 1024) return W4_ERR_UNSUPPORTED;
+  if (w4a8_plan(K, N, 256, nullptr, nullptr, nullptr) != W4_OK) return W4_ERR_UNSUPPORTED;
   if (M == 0 || N == 0) return W4_OK;
   if (!Xq || !sx || !xsum || !Y) return W4_ERR_NULL;
   st = check_packed(qweight, scales, qzeros, symmetric);

@@ -10,6 +10,9 @@
 // (IEEE fp32 division, round half to even), and
 //   Y[m][n] = sx[m] * sum_g sc[n][g] * (sum_{k in g} xq[m][k] q[n][k] - z[n][g] sum_{k in g} xq[m][k])
 // with the group sums exact in int32 and the rest in fp32.
+#include <algorithm>
+#include <utility>
+
 #include "internal.hpp"
 
 namespace w4 {
@@ -87,101 +90,150 @@ __global__ __launch_bounds__(64) void w4a8_quant_act_kernel(const uint16_t* X, i
 }
 
 // Workgroup: 16 output channels n0 .. n0+15 and all of K; its W waves take the
-// groups g = w, w + W, ... in turn.  Per group, lane l (n = l % 16, quarter
-// q = l / 16) holds the 32 codes of row n0 + n at channels 128 g + 32 q .. +31
-// (one 16-byte load) and, for activation row m = l % 16, the matching 32 int8
-// activations (two 16-byte loads); two v_mfma_i32_16x16x64_i8 give the group's
-// exact integer sums C[n][m] (lane l: rows n = 4 (l / 16) + r, column m = l % 16).
-// Codes expand to bytes with one AND (even nibbles) and one shift + AND (odd
-// nibbles) per word; the activations are permuted to the same byte order.  The
-// zero-point and scale fold per group reads the group's scales, zeros and
-// activation code sums from LDS (staged once per workgroup); the W waves' fp32
-// sums meet in LDS at the end, are added in wave order and scaled by sx[m].
-template <int W>
-__global__ __launch_bounds__(W * 64) void w4a8_gemv_kernel(const int8_t* Xq, const float* sx, const int32_t* xsum,
-                                                           int M, int K, int N, const uint32_t* qweight,
-                                                           const uint16_t* scales, const uint32_t* qzeros,
-                                                           int symmetric, uint16_t* Y) {
+// groups g = w, w + W, ..., w + (NI - 1) W in turn.  Per group, lane l (row index
+// l % 16, quarter q = l / 16) holds the 32 int8 activations of row m = l % 16 at
+// channels 128 g + 32 q .. +31 (two 16-byte loads) and the 32 codes of output
+// channel n0 + l % 16 at the same channels (one 16-byte load), plus that
+// channel's scale and zero word of group g; two v_mfma_i32_16x16x64_i8
+// (activations as A, codes as B) give the group's exact integer sums C[m][n]
+// (lane l: rows m = 4 (l / 16) + r, column n = l % 16).  Codes expand to bytes
+// with one AND (even nibbles) and one shift + AND (odd nibbles) per word; the
+// activations are permuted to the same byte order.  All of a wave's groups are
+// unrolled with four in flight.  The activation code sums of every group are
+// staged in LDS once per workgroup; the zero-point and scale fold is one
+// subtract-multiply-add per output per group; the W waves' fp32 sums meet in
+// LDS at the end, are added in wave order and scaled by sx[m].
+template <int NI>
+__global__ __launch_bounds__(1024) void w4a8_gemv_kernel(const int8_t* Xq, const float* sx, const int32_t* xsum,
+                                                         int M, int K, int N, const uint32_t* qweight,
+                                                         const uint16_t* scales, const uint32_t* qzeros,
+                                                         int symmetric, uint16_t* Y) {
 #pragma clang fp contract(off)
   extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
   const int G = K >> 7;
   const int GW = (G + 7) >> 3;
   const int t = threadIdx.x;
   const int lane = t & 63;
-  const int wave = t >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+  const int W = blockDim.x >> 6;          // waves: group g = wave + i W, i < NI
   const int n0 = blockIdx.x * 16;
-  float* s_sc = reinterpret_cast<float*>(lds);                              // [G][16]
-  int32_t* s_xs = reinterpret_cast<int32_t*>(lds + (size_t)G * 64);         // [G][16]
-  uint8_t* s_z = lds + (size_t)G * 128;                                     // [G][16]
-  float* s_red = reinterpret_cast<float*>(lds + (size_t)G * 144);           // [W][16][16]
-
-  for (int e = t; e < G * 16; e += W * 64) {
-    const int g = e >> 4, r = e & 15;
-    const int n = n0 + r;
-    float sc = 0.0f;
-    uint32_t z = 8;
-    if (n < N) {
-      sc = bf16_bits_to_f32(scales[(size_t)n * G + g]);
-      if (!symmetric) z = (qzeros[(size_t)n * GW + (g >> 3)] >> (4 * (g & 7))) & 0xFu;
-    }
-    s_sc[e] = sc;
-    s_z[e] = (uint8_t)z;
-    s_xs[e] = r < M ? xsum[(size_t)r * G + g] : 0;
-  }
-  __syncthreads();
+  int32_t* s_xs = reinterpret_cast<int32_t*>(lds);                          // [G][16]
+  float* s_red = reinterpret_cast<float*>(lds + (size_t)G * 64);            // [W][16][16]
 
   const int ln = lane & 15, q = lane >> 4;
   const uint32_t words = (uint32_t)(K >> 3);
   const auto rw = rsrc(qweight, (uint32_t)N * words * 4u);
   const auto rx = rsrc(Xq, (uint32_t)M * (uint32_t)K);
-  // byte offsets of this lane's slice of group 0 (out of range past N / past M)
-  const uint32_t wbase = (n0 + ln < N) ? ((uint32_t)(n0 + ln) * words + 4u * q) * 4u : kFar;
+  const auto rs = rsrc(scales, (uint32_t)N * (uint32_t)G * 2u);
+  const auto rz = rsrc(symmetric ? static_cast<const void*>(scales) : qzeros,
+                       symmetric ? 0u : (uint32_t)N * (uint32_t)GW * 4u);
+  // byte offsets of this lane's slice of group 0 (out of range past N / past M,
+  // whatever the group offset added to them)
+  const bool nok = n0 + ln < N;
+  const uint32_t wbase = nok ? ((uint32_t)(n0 + ln) * words + 4u * q) * 4u : kFar;
+  const uint32_t sbase = nok ? (uint32_t)(n0 + ln) * (uint32_t)G * 2u : kFar;
+  const uint32_t zbase = nok ? (uint32_t)(n0 + ln) * (uint32_t)GW * 4u : kFar;
   const uint32_t xbase = (ln < M) ? (uint32_t)ln * (uint32_t)K + 32u * q : kFar;
+  struct Slice {
+    i32x4 w, x0, x1;
+    uint16_t sc;
+    uint32_t z;
+  };
+  // this lane's codes, activations, scale and zero word of group g: the lane part
+  // of every offset is fixed, the group part is wave-uniform and goes in the
+  // scalar offset; groups past G (the unrolled tail) re-read group G-1
+  auto load = [&](int g, Slice& L) {
+    const int gc = min(g, G - 1);
+    L.w = __builtin_bit_cast(i32x4, __builtin_amdgcn_raw_buffer_load_b128(rw, wbase, gc * 64, 0));
+    L.x0 = __builtin_bit_cast(i32x4, __builtin_amdgcn_raw_buffer_load_b128(rx, xbase, gc * 128, 0));
+    L.x1 = __builtin_bit_cast(i32x4, __builtin_amdgcn_raw_buffer_load_b128(rx, xbase + 16u, gc * 128, 0));
+    L.sc = __builtin_amdgcn_raw_buffer_load_b16(rs, sbase, gc * 2, 0);
+    L.z = symmetric ? 0u : __builtin_amdgcn_raw_buffer_load_b32(rz, zbase, (gc >> 3) * 4, 0);
+  };
+  // the first P groups' loads go out before the staging below
+  constexpr int P = NI < 4 ? NI : 4;
+  Slice Ls[P];
+#pragma unroll
+  for (int i = 0; i < P; ++i) load(wave + i * W, Ls[i]);
+  __builtin_amdgcn_sched_barrier(0);
+
+  for (int e = t; e < G * 16; e += blockDim.x) {
+    const int g = e >> 4, m = e & 15;
+    s_xs[e] = m < M ? xsum[(size_t)m * G + g] : 0;
+  }
+  __syncthreads();
 
   float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-  for (int g = wave; g < G; g += W) {
-    const auto wv = __builtin_amdgcn_raw_buffer_load_b128(rw, wbase + (uint32_t)g * 64u, 0, 0);
-    const auto x0 = __builtin_amdgcn_raw_buffer_load_b128(rx, xbase + (uint32_t)g * 128u, 0, 0);
-    const auto x1 = __builtin_amdgcn_raw_buffer_load_b128(rx, xbase + (uint32_t)g * 128u + 16u, 0, 0);
-    const uint32_t w4[4] = {(uint32_t)wv[0], (uint32_t)wv[1], (uint32_t)wv[2], (uint32_t)wv[3]};
-    const uint32_t xd[8] = {(uint32_t)x0[0], (uint32_t)x0[1], (uint32_t)x0[2], (uint32_t)x0[3],
-                            (uint32_t)x1[0], (uint32_t)x1[1], (uint32_t)x1[2], (uint32_t)x1[3]};
+  auto process = [&](const Slice& L, int g) {
     uint32_t a[8], b[8];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      // codes of channels 8i + (0, 2, 4, 6) and 8i + (1, 3, 5, 7)
-      a[2 * i] = w4[i] & 0x0F0F0F0Fu;
-      a[2 * i + 1] = (w4[i] >> 4) & 0x0F0F0F0Fu;
-      // activations of the same channels: v_perm_b32(hi, lo, sel) picks bytes of lo (0-3) and hi (4-7)
-      b[2 * i] = __builtin_amdgcn_perm(xd[2 * i + 1], xd[2 * i], 0x06040200u);
-      b[2 * i + 1] = __builtin_amdgcn_perm(xd[2 * i + 1], xd[2 * i], 0x07050301u);
+      const uint32_t wi = (uint32_t)L.w[i];
+      const uint32_t lo = (uint32_t)(i < 2 ? L.x0[2 * i] : L.x1[2 * i - 4]);
+      const uint32_t hi = (uint32_t)(i < 2 ? L.x0[2 * i + 1] : L.x1[2 * i - 3]);
+      // activations of channels 8i + (0, 2, 4, 6) and 8i + (1, 3, 5, 7):
+      // v_perm_b32(hi, lo, sel) picks bytes of lo (0-3) and hi (4-7)
+      a[2 * i] = __builtin_amdgcn_perm(hi, lo, 0x06040200u);
+      a[2 * i + 1] = __builtin_amdgcn_perm(hi, lo, 0x07050301u);
+      // codes of the same channels
+      b[2 * i] = wi & 0x0F0F0F0Fu;
+      b[2 * i + 1] = (wi >> 4) & 0x0F0F0F0Fu;
     }
     const i32x4 a0 = {(int)a[0], (int)a[1], (int)a[2], (int)a[3]}, a1 = {(int)a[4], (int)a[5], (int)a[6], (int)a[7]};
     const i32x4 b0 = {(int)b[0], (int)b[1], (int)b[2], (int)b[3]}, b1 = {(int)b[4], (int)b[5], (int)b[6], (int)b[7]};
     i32x4 c = __builtin_amdgcn_mfma_i32_16x16x64_i8(a0, b0, (i32x4){0, 0, 0, 0}, 0, 0, 0);
     c = __builtin_amdgcn_mfma_i32_16x16x64_i8(a1, b1, c, 0, 0, 0);
-    const float4 sc4 = *reinterpret_cast<const float4*>(s_sc + g * 16 + 4 * q);
-    const uint32_t z4 = *reinterpret_cast<const uint32_t*>(s_z + g * 16 + 4 * q);
-    const int xs = s_xs[g * 16 + ln];
-    const float scv[4] = {sc4.x, sc4.y, sc4.z, sc4.w};
+    // groups past G (the unrolled tail) read group G-1's staging and add nothing
+    const bool live = g < G;
+    const int4 xs = *reinterpret_cast<const int4*>(s_xs + (live ? g : G - 1) * 16 + 4 * q);
+    const int z = symmetric ? 8 : (int)((L.z >> (4 * (g & 7))) & 0xFu);
+    const float sc = live ? bf16_bits_to_f32(L.sc) : 0.0f;
+    const int xsv[4] = {xs.x, xs.y, xs.z, xs.w};
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const int zr = (int)((z4 >> (8 * r)) & 0xFFu);
-      acc[r] += scv[r] * (float)(c[r] - zr * xs);
+      acc[r] += sc * (float)(c[r] - z * xsv[r]);
+      // materialize the running sum here: left free, the compiler defers every
+      // group's fold to the end and keeps all the integer tiles alive (spills)
+      asm volatile("" : "+v"(acc[r]));
     }
+  };
+  // groups g = wave + i W, i < NI (unrolled: the waits are exact); P slices in
+  // flight, each refilled with the group P W further on once it is computed
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+    process(Ls[i % P], wave + i * W);
+    if (i + P < NI) load(wave + (i + P) * W, Ls[i % P]);
+    __builtin_amdgcn_sched_barrier(0);
   }
 #pragma unroll
   for (int r = 0; r < 4; ++r) s_red[(wave * 16 + 4 * q + r) * 16 + ln] = acc[r];
   __syncthreads();
-  if (t < 256) {
-    const int n = t >> 4, m = t & 15;
+  for (int e = t; e < 256; e += blockDim.x) {
+    const int m = e >> 4, n = e & 15;
     if (m < M && n0 + n < N) {
       float s = 0.0f;
-      for (int w = 0; w < W; ++w) s += s_red[(w * 16 + n) * 16 + m];
+      for (int w = 0; w < W; ++w) s += s_red[(w * 16 + m) * 16 + n];
       Y[(size_t)m * N + n0 + n] = (uint16_t)f32_to_bf16_bits(s * sx[m]);
     }
   }
 }
+
+namespace {
+
+constexpr int kW4a8MaxNi = 25;       // 400 groups at 16 waves
+using W4a8Kernel = void (*)(const int8_t*, const float*, const int32_t*, int, int, int, const uint32_t*,
+                            const uint16_t*, const uint32_t*, int, uint16_t*);
+
+template <int... I>
+W4a8Kernel w4a8_pick(int ni, std::integer_sequence<int, I...>) {
+  W4a8Kernel k = nullptr;
+  ((ni == I + 2 ? (k = w4a8_gemv_kernel<I + 2>, 0) : 0), ...);
+  return k;
+}
+
+W4a8Kernel w4a8_kernel_for(int ni) { return w4a8_pick(ni, std::make_integer_sequence<int, kW4a8MaxNi - 1>{}); }
+
+}  // namespace
 
 int launch_w4a8_quantize(const uint16_t* X, int M, int K, int8_t* Xq, float* sx, int32_t* xsum,
                          hipStream_t stream) {
@@ -191,7 +243,30 @@ int launch_w4a8_quantize(const uint16_t* X, int M, int K, int8_t* Xq, float* sx,
   return W4_OK;
 }
 
-size_t w4a8_gemv_lds_bytes(int K, int waves) { return (size_t)(K >> 7) * 144 + (size_t)waves * 16 * 16 * 4; }
+// W waves per workgroup and NI = ceil(G / W) groups per wave (2 <= NI <= 25): the
+// most waves (8, 4 or 2) with which one round of resident workgroups covers the
+// ceil(N / 16) row tiles (about 20 resident waves per CU), at least ceil(G / 25).
+// LDS: per group the code sums of the 16 activation rows (int32), plus 16 x 16 fp32
+// sums per wave.
+int w4a8_plan(int K, int N, int cus, int* ni, int* waves, size_t* lds) {
+  const int G = K >> 7;
+  const long long tiles = (N + 15) / 16;
+  int w = 2;
+  for (int cand : {8, 4}) {
+    if (tiles <= (long long)cus * (20 / cand)) {
+      w = cand;
+      break;
+    }
+  }
+  w = std::max(std::min(w, G), (G + kW4a8MaxNi - 1) / kW4a8MaxNi);
+  const int n = std::max(2, (G + w - 1) / w);
+  const size_t bytes = (size_t)G * 64 + (size_t)w * 16 * 16 * 4;
+  if (w > 16 || n > kW4a8MaxNi || bytes > 64 * 1024) return W4_ERR_UNSUPPORTED;
+  if (ni) *ni = n;
+  if (waves) *waves = w;
+  if (lds) *lds = bytes;
+  return W4_OK;
+}
 
 int launch_w4a8_gemv(const int8_t* Xq, const float* sx, const int32_t* xsum, int M, int K, int N,
                      const uint32_t* qweight, const uint16_t* scales, const uint32_t* qzeros, int symmetric,
@@ -199,17 +274,17 @@ int launch_w4a8_gemv(const int8_t* Xq, const float* sx, const int32_t* xsum, int
   if (M == 0 || N == 0) return W4_OK;
   // 32-bit buffer offsets: packed weights N K / 2 and activations M K below 2^31
   if ((long long)N * K / 2 >= (1LL << 31) || (long long)M * K >= (1LL << 31)) return W4_ERR_SHAPE;
-  const int G = K >> 7;
-  const int waves = G <= 32 ? 4 : 8;
-  const size_t lds = w4a8_gemv_lds_bytes(K, waves);
-  if (lds > 64 * 1024) return W4_ERR_UNSUPPORTED;
+  int ni = 0, waves = 0;
+  size_t lds = 0;
+  int cus = 256, dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) !=
+                                               hipSuccess || cus < 1)
+    cus = 256;
+  const int st = w4a8_plan(K, N, cus, &ni, &waves, &lds);
+  if (st != W4_OK) return st;
   const dim3 grid((unsigned)((N + 15) / 16));
-  if (waves == 4)
-    hipLaunchKernelGGL(w4a8_gemv_kernel<4>, grid, dim3(256), lds, stream, Xq, sx, xsum, M, K, N, qweight, scales,
-                       qzeros, symmetric, Y);
-  else
-    hipLaunchKernelGGL(w4a8_gemv_kernel<8>, grid, dim3(512), lds, stream, Xq, sx, xsum, M, K, N, qweight, scales,
-                       qzeros, symmetric, Y);
+  hipLaunchKernelGGL(w4a8_kernel_for(ni), grid, dim3(waves * 64), lds, stream, Xq, sx, xsum, M, K, N, qweight, scales,
+                     qzeros, symmetric, Y);
   W4_CHECK_LAUNCH();
   return W4_OK;
 }

@@ -176,6 +176,44 @@ def linear(X_bf16: np.ndarray, W_hat: np.ndarray) -> np.ndarray:
     return bf16_to_f32(X_bf16).astype(np.float64) @ np.asarray(W_hat, dtype=np.float64).T
 
 
+# --------------------------------------------------------------------------- per-channel clipping
+
+def clip_search_per_channel(X_bf16, W_bf16, s, ratios, symmetric=False, rows=None):
+    """Stock per-output-channel clipping: a shrink ratio per (output channel, group).
+
+    [AWQ-W4 card] "Clipping granularity" and the comparability caveat: the d = 0
+    arm searches a clipping threshold per output channel, where each channel's
+    loss is its own; the look-ahead arm replaces it with one global ratio.
+    Reading: for row n, group g and every ratio r of the grid,
+      w_hat = dequantize(Q(clip_r(v))) of that group alone (quantize_rtn with clip r),
+      e = v - w_hat with v = W diag(s) (fp32 values, difference in fp64),
+      L[g][n][r] = sum_t (sum_{k in g} x'_tk e_k)^2 with x' = bf16(X / s), the
+      deployed activations (IEEE fp32 division, then RNE to bf16);
+    best[n][g] = the first ratio index with the least loss.
+    rows: optional subset of output channels (the result covers only those).
+    Returns (L float64 [G][len(rows)][R], best int64 [len(rows)][G]).
+    """
+    W_bf16 = np.asarray(W_bf16, dtype=np.uint16)
+    if rows is not None:
+        W_bf16 = W_bf16[np.asarray(rows)]
+    N, K = W_bf16.shape
+    G = K // GROUP
+    s32 = np.asarray(s, dtype=np.float32)
+    xs = bf16_to_f32(f32_to_bf16(bf16_to_f32(X_bf16) / s32[None, :])).astype(np.float64)   # [T][K]
+    v = (bf16_to_f32(W_bf16) * s32[None, :]).astype(np.float64)                               # [N][K]
+    R = len(ratios)
+    L = np.zeros((G, N, R))
+    for ir, r in enumerate(ratios):
+        qw, sc, qz = quantize_pack(W_bf16, s32, float(np.float32(r)), symmetric)
+        e = v - dequantize(qw, sc, qz, K, symmetric).astype(np.float64)
+        for g in range(G):
+            sl = slice(GROUP * g, GROUP * (g + 1))
+            P = xs[:, sl] @ e[:, sl].T                        # [T][N] partial outputs of group g
+            L[g, :, ir] = (P * P).sum(axis=0)
+    best = np.argmin(L, axis=2).T                               # first minimum
+    return L, best
+
+
 # --------------------------------------------------------------------------- W4A8 decode
 
 INT8_MAX = 127       # symmetric int8 activation codes in [-127, 127] (reading)

@@ -453,7 +453,53 @@ def check_w4a8_linear_reduces_to_dequant_matmul():
         assert np.array_equal(y1[0], 0.5 * 127 * Wh[:, 200])
 
 
+def check_clip_channel_bruteforce():
+    """Per-channel clipping losses and choices: the scalar restatement agrees to
+    1e-10 on K=256, N=3, T=6 with a non-trivial s, both quantizer forms."""
+    X, W = small_case(6, 256, 3, 53)
+    rng = np.random.default_rng(53)
+    s = np.exp(rng.standard_normal(256) * 0.5).astype(np.float32)
+    ratios = O.shrink_grid()
+    Xr = O.bf16_to_f32(X).astype(np.float64).tolist()
+    Wr = O.bf16_to_f32(W).astype(np.float64).tolist()
+    for sym in (False, True):
+        Ls, bs = S.per_channel_clip_losses(Xr, Wr, s.astype(np.float64).tolist(), ratios.tolist(), sym)
+        L, best = O.clip_search_per_channel(X, W, s, ratios, sym)
+        assert np.allclose(L, np.array(Ls), rtol=1e-10, atol=0), sym
+        assert np.array_equal(best, np.array(bs)), sym
+
+
+def check_clip_channel_special_cases():
+    """One-hot deployed activations (x' = unit vectors) make each loss the plain
+    squared quantization error of the group; scaling X by 2 scales every loss by 4
+    exactly with the same choices; a row subset is the same slice of the full
+    result; an all-zero weight row has zero loss everywhere and picks ratio 0."""
+    K, N = 256, 4
+    W = _rand_w(N=N, K=K, seed=59)
+    W[2] = 0
+    s = np.exp2(np.random.default_rng(59).integers(-2, 3, size=K)).astype(np.float32)
+    X = round_to_bf16_bits(np.diag(s))                     # bf16(X / s) = identity exactly
+    ratios = O.shrink_grid()
+    for sym in (False, True):
+        L, best = O.clip_search_per_channel(X, W, s, ratios, sym)
+        v = O.bf16_to_f32(W).astype(np.float64) * s.astype(np.float64)
+        for j, r in enumerate(ratios):
+            qw, sc, qz = O.quantize_pack(W, s, float(r), sym)
+            e = v - O.dequantize(qw, sc, qz, K, sym)
+            sq = (e.reshape(N, 2, 128) ** 2).sum(axis=2)   # [N][G]
+            assert np.allclose(L[:, :, j], sq.T, rtol=1e-12, atol=0), (sym, j)
+        assert not L[:, 2, :].any() and not best[2].any()
+        X2, W2 = small_case(5, K, N, 61)
+        La, ba = O.clip_search_per_channel(X2, W2, s, ratios, sym)
+        Xd = round_to_bf16_bits(O.bf16_to_f32(X2) * np.float32(2))
+        Lb, bb = O.clip_search_per_channel(Xd, W2, s, ratios, sym)
+        assert np.array_equal(Lb, 4 * La) and np.array_equal(ba, bb)
+        Lr, br = O.clip_search_per_channel(X2, W2, s, ratios, sym, rows=[3, 1])
+        assert np.array_equal(Lr, La[:, [3, 1], :]) and np.array_equal(br, ba[[3, 1]])
+
+
 ALL_CHECKS = [
+    check_clip_channel_bruteforce, check_clip_channel_special_cases,
     check_w4a8_activation_codes, check_w4a8_linear_reduces_to_dequant_matmul,
     check_division_ties,
     check_bf16_golden, check_bf16_against_torch, check_worked_groups, check_pack_golden,

@@ -108,3 +108,28 @@ def search(X_rows, W_rows, alphas, ratios, symmetric=False):
     lr = [loss(X_rows, W_rows, s_star, r, symmetric, Y_ref) for r in ratios]
     ir = min(range(len(lr)), key=lambda i: (lr[i], i))
     return la, lr, ia, ir
+
+
+def per_channel_clip_losses(X_rows, W_rows, s, ratios, symmetric=False):
+    """Per (group g, output channel n, ratio index j): the squared partial output
+    error of group g over the tokens, sum_t (sum_{k in g} x'[t][k] e[n][k])^2 with
+    x' = bf16(fp32(x / s)) and e = fp32(w s) - w_hat(ratio j); and per (n, g) the
+    first ratio index of least loss.  Returns (L[g][n][j], best[n][g])."""
+    T, N, K = len(X_rows), len(W_rows), len(W_rows[0])
+    xs = [[round_bf16(f32(X_rows[t][k] / s[k])) for k in range(K)] for t in range(T)]
+    v = [[f32(W_rows[n][k] * s[k]) for k in range(K)] for n in range(N)]
+    G = K // 128
+    L = [[[0.0] * len(ratios) for _ in range(N)] for _ in range(G)]
+    for j, r in enumerate(ratios):
+        what = quantize_dequant(W_rows, s, r, symmetric)
+        for n in range(N):
+            for g in range(G):
+                tot = 0.0
+                for t in range(T):
+                    p = 0.0
+                    for k in range(128 * g, 128 * g + 128):
+                        p += xs[t][k] * (v[n][k] - what[n][k])
+                    tot += p * p
+                L[g][n][j] = tot
+    best = [[min(range(len(ratios)), key=lambda j: (L[g][n][j], j)) for g in range(G)] for n in range(N)]
+    return L, best

@@ -58,6 +58,14 @@ MUTANTS = {
     "w4a8_no_act_scale": ("return y * np.asarray(sx, dtype=np.float64)[:, None]", "return y"),
     "w4a8_group_sum_shifted": ("xsum = xq.astype(np.int64).reshape(M, K // GROUP, GROUP).sum(axis=2)",
                                "xsum = np.roll(xq.astype(np.int64), 1, axis=1).reshape(M, K // GROUP, GROUP).sum(axis=2)"),
+    "clip_loss_x_times_s": ("bf16_to_f32(f32_to_bf16(bf16_to_f32(X_bf16) / s32[None, :]))",
+                            "bf16_to_f32(f32_to_bf16(bf16_to_f32(X_bf16) * s32[None, :]))"),
+    "clip_loss_v_unscaled": ("v = (bf16_to_f32(W_bf16) * s32[None, :])", "v = (bf16_to_f32(W_bf16) * 1)"),
+    "clip_loss_abs": ("L[g, :, ir] = (P * P).sum(axis=0)", "L[g, :, ir] = np.abs(P).sum(axis=0)"),
+    "clip_loss_half_group": ("sl = slice(GROUP * g, GROUP * (g + 1))", "sl = slice(GROUP * g, GROUP * g + 64)"),
+    "clip_loss_x_transposed_tokens": ("P = xs[:, sl] @ e[:, sl].T", "P = xs[::-1, sl][:, ::-1] @ e[:, sl].T"),
+    "clip_best_last": ("best = np.argmin(L, axis=2).T", "best = (L.shape[2] - 1 - np.argmin(L[:, :, ::-1], axis=2)).T"),
+    "clip_best_max": ("best = np.argmin(L, axis=2).T", "best = np.argmax(L, axis=2).T"),
     "clip_after_scale_choice": ("        absmax = np.abs(v).max(axis=2, keepdims=True)\n    if symmetric:",
                                 "    if symmetric:"),
 }

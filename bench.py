@@ -350,6 +350,32 @@ def rows_search(torch, w4, wl, reps):
     return rows
 
 
+def rows_clip(torch, w4, wl, reps):
+    """Per-output-channel clipping search at the search workload's full size: T=4096
+    calibration tokens, K=2048, N=6144, the 10-ratio grid, s = s(alpha*) from the
+    two-phase search (untimed).  Algorithmic work: the Gram matrices (2 T K 128
+    flops) and e^T H_g e for every (channel, group, ratio) (2 N K R 128 flops)."""
+    rows = []
+    Xn, Wn = wl.awq_calibration()
+    X, W = to_dev_bf16(torch, Xn), to_dev_bf16(torch, Wn)
+    res = w4.awq_search(X, W, [i / 20 for i in range(20)], [1 - j / 20 for j in range(10)])
+    s = res["s"]
+    ratios = torch.tensor([1 - j / 20 for j in range(10)], dtype=torch.float32, device="cuda")
+    T, K = X.shape
+    N = W.shape[0]
+    R = ratios.numel()
+    flops = 2 * T * K * 128 + 2 * N * K * R * 128
+    for sym in (False, True):
+        L, best = w4.awq_clip_search(X, W, ratios, s=s, symmetric=sym)
+        ws = torch.empty(64 << 20, dtype=torch.uint8, device="cuda")
+        ms = time_events(torch, lambda: w4.awq_clip_search(X, W, ratios, s=s, symmetric=sym, losses=L, best=best,
+                                                          workspace=ws), reps)
+        hist = torch.bincount(best.flatten().long(), minlength=R).tolist()
+        rows.append(row_gemm(f"per-channel clip search T={T} K={K} N={N} R={R} {'sym' if sym else 'asym'}",
+                             flops, ms, {"choice_histogram": hist}))
+    return rows
+
+
 def rows_convert(torch, w4, wl, reps):
     """Streaming data-free symmetric conversion of a synthetic 3-shard checkpoint
     (8 hidden-2048 blocks, 0.87 GB of bf16) written to a temporary directory."""
@@ -416,7 +442,7 @@ def main(argv=None):
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
     ap.add_argument("--step-only", action="store_true", help="measure only the decode-sweep step")
     ap.add_argument("--only", default="", help="comma list of extra rows to measure "
-                    "(sweeps,w4a8,large,prefill,gemv2048,search,convert); default all")
+                    "(sweeps,w4a8,large,prefill,gemv2048,search,clip,convert); default all")
     ap.add_argument("--blocks", type=int, default=28)
     ap.add_argument("--skip-step", action="store_true",
                     help="profiling aid: skip the decode-sweep step (value is null) and run only --only rows")
@@ -506,7 +532,7 @@ def main(argv=None):
         torch.cuda.empty_cache()
 
     want = set(x for x in args.only.split(",") if x) or {"sweeps", "w4a8", "large", "prefill", "gemv2048",
-                                                         "search", "convert"}
+                                                         "search", "clip", "convert"}
     if not args.step_only:
         rows = []
         if "sweeps" in want and packed:
@@ -538,7 +564,7 @@ def main(argv=None):
         torch.cuda.empty_cache()
         reps = max(5, args.steps)
         for name, fn in (("large", rows_large), ("prefill", rows_prefill), ("gemv2048", rows_gemv2048),
-                         ("search", rows_search), ("convert", rows_convert)):
+                         ("search", rows_search), ("clip", rows_clip), ("convert", rows_convert)):
             if name in want:
                 log(f"rows: {name}")
                 rows += fn(torch, w4, wl, reps)

@@ -187,6 +187,37 @@ int awq_grid_loss(const uint16_t* X, int T, int K, int N, const uint16_t* W,
                   size_t* workspace_bytes, void* stream);
 
 /*
+ * awq_clip_search -- stock per-output-channel clipping: a shrink ratio per
+ * (output channel, group).  [AWQ-W4 card] "Clipping granularity" and the caveat
+ * under the perplexity table: the d = 0 arm searches the clipping threshold per
+ * output channel, each channel scored on its own error (the look-ahead arm's one
+ * global ratio is awq_grid_loss / awq_search).  For channel n, group g, ratio j:
+ *   v = fp32(W[n][k] s[k]) over the 128 channels k of g;
+ *   w_hat = the dequantized RTN of v clamped to +-ratios[j] * absmax(v), exactly
+ *           as awq_quantize_pack with clip ratios[j];  e = v - w_hat;
+ *   losses[g][n][j] = sum_t (sum_{k in g} x'[t][k] e[k])^2,
+ *                     x' = bf16(X[t][k] / s[k]) (the deployed activations);
+ *   best[n][g] = the first j with the least losses[g][n][j].
+ * The loss is formed as e^T H_g e with the Gram matrix H_g = X'_g^T X'_g (fp32
+ * accumulation of exact bf16 products) and bf16 hi + lo splits of e and H_g on
+ * the matrix cores: relative error of order 2^-16 of e^T |H_g| e, so ratios whose
+ * losses differ by less than that may be chosen either way.
+ *
+ *   X [T][K] bf16 calibration activations, T >= 0 (T = 0: every loss is 0).
+ *   W [N][K] bf16 unquantized weight.  s [K] fp32 (every s[k] > 0) or NULL (= 1).
+ *   ratios [R] fp32 device, 1 <= R <= 64 (else W4_ERR_VALUE); a ratio >= 1 means
+ *   no clipping.
+ *   losses [G][N][R] fp32 device out, or NULL (not written); G = K / 128.
+ *   best [N][G] uint8 device out.
+ *   workspace: size query as in w4a16_gemm (workspace == NULL and workspace_bytes
+ *   != NULL); the size depends on (T, K) and is about 16 MiB + 64 KiB per group.
+ * Deterministic: fixed summation orders, bit-identical from run to run.
+ */
+int awq_clip_search(const uint16_t* X, int T, int K, int N, const uint16_t* W, const float* s,
+                    const float* ratios, int R, int symmetric, int group_size, float* losses,
+                    uint8_t* best, void* workspace, size_t* workspace_bytes, void* stream);
+
+/*
  * awq_search -- the two-phase search of [AWQ-W4 card] "Search": every alpha in
  * `alphas` scored at r = 1, keep the first minimum alpha*; then every ratio in
  * `ratios` scored at s(alpha*), keep the first minimum r*.

@@ -28,7 +28,8 @@ def declared_functions():
 
 def test_header_declares_the_boundary():
     names = declared_functions()
-    for n in ("awq_quantize_pack", "w4a16_gemv", "w4a16_gemm", "awq_grid_loss", "awq_search", "w4_status_string"):
+    for n in ("awq_quantize_pack", "w4a16_gemv", "w4a16_gemm", "awq_grid_loss", "awq_search", "awq_clip_search",
+              "w4_status_string"):
         assert n in names, names
 
 
@@ -152,6 +153,40 @@ def test_search_validation(lib):
     badr = (D * 1)(0.0)
     assert f(A, 64, 256, 8, A, al, 20, badr, 1, 0, 128, None, None, None, None, None, ctypes.byref(sz), None) == -7
     assert f(A, 64, 256, 8, A, None, 20, ra, 10, 0, 128, None, None, None, None, None, ctypes.byref(sz), None) == -1
+
+
+def test_clip_search_validation(lib):
+    sz = ctypes.c_size_t(0)
+    f = lib.awq_clip_search
+    assert f(None, 4096, 2048, 6144, None, None, None, 10, 0, 128, None, None, None, ctypes.byref(sz), None) == 0
+    G = 2048 // 128
+    assert sz.value >= G * 65536 and sz.value <= 64 * 2**20
+    big = sz.value
+    assert f(None, 64, 2048, 6144, None, None, None, 10, 0, 128, None, None, None, ctypes.byref(sz), None) == 0
+    assert sz.value < big                                    # Gram partials scale with the token slices
+    ok = ctypes.c_size_t(big)
+    args = lambda **k: [k.get("X", A), k.get("T", 64), k.get("K", 2048), k.get("N", 64), k.get("W", A),
+                        k.get("s", None), k.get("ratios", A), k.get("R", 10), k.get("sym", 0), k.get("gs", 128),
+                        k.get("losses", A), k.get("best", A), k.get("ws", A), ctypes.byref(ok), None]
+    assert f(*args(gs=64)) == -4
+    assert f(*args(K=200)) == -2
+    assert f(*args(T=-1)) == -2
+    assert f(*args(R=0)) == -7
+    assert f(*args(R=65)) == -7
+    assert f(*args(sym=2)) == -7
+    assert f(*args(W=None)) == -1
+    assert f(*args(best=None)) == -1
+    assert f(*args(ratios=None)) == -1
+    assert f(*args(X=None)) == -1
+    assert f(*args(W=MIS)) == -3
+    assert f(*args(s=MIS)) == -3
+    assert f(*args(N=0, W=None, best=None)) == 0              # no-op
+    small = ctypes.c_size_t(16)
+    a = args()
+    a[13] = ctypes.byref(small)
+    assert f(*a) == -5
+    a[13] = None
+    assert f(*a) == -5
 
 
 def test_python_binding_fails_loudly_without_library(monkeypatch, tmp_path):

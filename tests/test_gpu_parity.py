@@ -453,3 +453,111 @@ def test_w4a8_rejects_m17():
     X = np.zeros((17, 256), dtype=np.uint16)
     with pytest.raises(w4.W4Error):
         w4.w4a8_quantize_activations(to_bf16(X))
+
+
+# ----------------------------------------------------------------------------- per-channel clipping
+
+# Error bound of the GPU loss e^T H_g e: e and H_g enter the matrix cores as bf16
+# hi + lo (residue <= 2^-17 of each entry, the lo x lo product dropped: <= 2^-18),
+# H_g and H_g e accumulate in fp32 over at most 256 tokens per slice and 384
+# products; all of it is below 2^-13 of the same expression with every term taken
+# in absolute value, e^T (|X'|^T |X'|) e with |e|.  The test allows 2^-12 of that.
+CLIP_TOL = 2.0 ** -12
+
+
+def _clip_reference(X, W, s, ratios, sym, rows):
+    s32 = np.ones(X.shape[1], np.float32) if s is None else s
+    L, best = O.clip_search_per_channel(X, W, s32, ratios, sym, rows=rows)
+    xs = np.abs(O.bf16_to_f32(O.f32_to_bf16(O.bf16_to_f32(X) / s32[None, :])).astype(np.float64))
+    Wr = W[np.asarray(rows)]
+    v = O.bf16_to_f32(Wr).astype(np.float64) * s32.astype(np.float64)
+    K = X.shape[1]
+    bound = np.zeros_like(L)
+    for j, r in enumerate(ratios):
+        qw, sc, qz = O.quantize_pack(Wr, s32, float(r), sym)
+        e = np.abs(v - O.dequantize(qw, sc, qz, K, sym))
+        for g in range(K // 128):
+            sl = slice(128 * g, 128 * g + 128)
+            bound[g, :, j] = ((xs[:, sl] @ e[:, sl].T) ** 2).sum(axis=0)
+    return L, best, bound
+
+
+def _clip_check(X, W, s, ratios, sym, rows=None, repeat=False):
+    N, K = W.shape
+    rows = list(range(N)) if rows is None else rows
+    args = (to_bf16(X), to_bf16(W), to_f32(ratios))
+    kw = dict(s=None if s is None else to_f32(s), symmetric=sym)
+    L, best = w4.awq_clip_search(*args, **kw)
+    torch.cuda.synchronize()
+    if repeat:
+        L2, best2 = w4.awq_clip_search(*args, **kw)
+        torch.cuda.synchronize()
+        assert torch.equal(L, L2) and torch.equal(best, best2), "clip search not deterministic"
+    got = L.cpu().numpy().astype(np.float64)[:, rows, :]
+    gbest = best.cpu().numpy().astype(np.int64)[rows]
+    want, wbest, bound = _clip_reference(X, W, s, ratios, sym, rows)
+    tol = CLIP_TOL * bound + 1e-30
+    bad = np.abs(got - want) > tol
+    assert not bad.any(), (f"{int(bad.sum())} losses off; worst excess "
+                           f"{np.max((np.abs(got - want) - tol))}, at {np.argwhere(bad)[:4]}")
+    G = K // 128
+    n_idx = np.arange(len(rows))[:, None]
+    g_idx = np.arange(G)[None, :]
+    pick = want[g_idx, n_idx, gbest]             # [rows][G] oracle loss at the GPU's choice
+    low = want[g_idx, n_idx, wbest]
+    slack = tol[g_idx, n_idx, gbest] + tol[g_idx, n_idx, wbest]
+    assert np.all(pick <= low + slack), np.argwhere(pick > low + slack)[:4]
+    return float(np.mean(gbest == wbest))
+
+
+@pytest.mark.parametrize("sym", [False, True])
+@pytest.mark.parametrize("with_s", [False, True])
+def test_clip_search_small(sym, with_s):
+    X, W = wl.awq_calibration(256, 384, 200, seed_block=4)
+    s = O.awq_scales(O.act_mean_abs(X), 0.5) if with_s else None
+    say("clip search small", sym, with_s)
+    agree = _clip_check(X, W, s, O.shrink_grid().astype(np.float32), sym, repeat=True)
+    assert agree >= 0.9, agree
+
+
+@pytest.mark.parametrize("T,K,N", [(77, 128, 37), (1, 256, 5), (130, 1152, 131), (64, 640, 129)])
+def test_clip_search_ragged(T, K, N):
+    X, W = wl.awq_calibration(T, K, N, seed_block=5)
+    s = O.awq_scales(O.act_mean_abs(X), 0.35)
+    ratios = np.array([1.0, 0.9, 0.8, 0.7, 0.6, 0.55, 0.5], dtype=np.float32)
+    for sym in (False, True):
+        say("clip search ragged", T, K, N, sym)
+        _clip_check(X, W, s, ratios, sym)
+
+
+def test_clip_search_degenerate():
+    """No tokens: every loss 0 and ratio 0 chosen; all-zero weight rows: losses 0,
+    ratio 0; a single ratio; N = 0 is a no-op."""
+    X, W = wl.awq_calibration(64, 256, 40, seed_block=6)
+    W = W.copy()
+    W[[0, 17, 39]] = 0
+    ratios = O.shrink_grid().astype(np.float32)
+    say("clip search degenerate")
+    L, best = w4.awq_clip_search(to_bf16(X[:0]), to_bf16(W), to_f32(ratios))
+    torch.cuda.synchronize()
+    assert not L.any() and not best.any()
+    L, best = w4.awq_clip_search(to_bf16(X), to_bf16(W), to_f32(ratios))
+    torch.cuda.synchronize()
+    assert not L[:, [0, 17, 39], :].any() and not best[[0, 17, 39]].any()
+    _clip_check(X, W, None, ratios[:1], False)
+    L, best = w4.awq_clip_search(to_bf16(X), to_bf16(W[:0]), to_f32(ratios))
+    torch.cuda.synchronize()
+    assert L.numel() == 0 and best.numel() == 0
+
+
+@pytest.mark.parametrize("sym", [False, True])
+def test_clip_search_full_size(sym):
+    """4096 calibration tokens, K = 2048, N = 6144 at s(alpha = 0.5); 48 sampled
+    channels (first, last, tile edges, random) against the oracle."""
+    X, W = wl.awq_calibration(seed_block=0)
+    s = O.awq_scales(O.act_mean_abs(X), 0.5)
+    N = W.shape[0]
+    rng = np.random.default_rng(11)
+    rows = sorted(set([0, 31, 32, 127, 128, N - 129, N - 1] + rng.choice(N, 41, replace=False).tolist()))
+    say("clip search full size", sym, X.shape, W.shape)
+    _clip_check(X, W, s, O.shrink_grid().astype(np.float32), sym, rows=rows)

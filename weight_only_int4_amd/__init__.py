@@ -20,7 +20,8 @@ import torch
 __all__ = [
     "W4Error", "library_path", "load_library", "awq_quantize_pack", "w4a16_gemv", "w4a16_gemm",
     "awq_grid_loss", "awq_search", "GROUP_SIZE", "GEMV_MAX_M", "gemv_launcher", "gemm_launcher",
-    "w4a8_quantize_activations", "w4a8_gemv", "w4a8_gemv_launcher", "probe_stream_read", "probe_empty",
+    "w4a8_quantize_activations", "w4a8_gemv", "w4a8_gemv_launcher", "awq_clip_search", "probe_stream_read",
+    "probe_empty",
 ]
 
 GROUP_SIZE = 128
@@ -39,6 +40,7 @@ _SIGNATURES = {
     "w4_probe_empty": ([_vp], _i),
     "w4a8_quantize_activations": ([_vp, _i, _i, _vp, _vp, _vp, _vp], _i),
     "w4a8_gemv": ([_vp, _vp, _vp, _i, _i, _i, _vp, _vp, _vp, _i, _i, _vp, _vp], _i),
+    "awq_clip_search": ([_vp, _i, _i, _i, _vp, _vp, _vp, _i, _i, _i, _vp, _vp, _vp, _sz, _vp], _i),
     "awq_search": ([_vp, _i, _i, _i, _vp, ctypes.POINTER(ctypes.c_double), _i,
                     ctypes.POINTER(ctypes.c_double), _i, _i, _i, ctypes.POINTER(ctypes.c_float),
                     ctypes.POINTER(ctypes.c_int), ctypes.POINTER(ctypes.c_int), _vp, _vp, _sz, _vp], _i),
@@ -271,6 +273,39 @@ def awq_grid_loss(X, W, S, ratios, symmetric: bool = False, Yref=None, losses=No
                              GROUP_SIZE, _ptr(losses), _ptr(ws), None if wsb is None else ctypes.byref(wsb),
                              _stream(dev)))
     return losses
+
+
+def awq_clip_search(X, W, ratios, s=None, symmetric: bool = False, want_losses: bool = True, losses=None,
+                    best=None, workspace=None):
+    """Per-output-channel clipping search.  Returns (losses [G][N][R] fp32 or None,
+    best [N][G] uint8): for channel n and group g, losses over the ratio grid of the
+    group's squared partial-output error over the tokens, and the first ratio index
+    of least loss."""
+    lib = load_library()
+    _need(X, torch.bfloat16, "X", 2)
+    _need(W, torch.bfloat16, "W", 2)
+    _need(ratios, torch.float32, "ratios", 1)
+    if s is not None:
+        _need(s, torch.float32, "s", 1)
+    T, K = X.shape
+    N = W.shape[0]
+    R = ratios.shape[0]
+    G = K // GROUP_SIZE
+    dev = X.device
+    if want_losses and losses is None:
+        losses = torch.empty((G, N, R), dtype=torch.float32, device=dev)
+    if best is None:
+        best = torch.empty((N, G), dtype=torch.uint8, device=dev)
+
+    def q(sz):
+        return lib.awq_clip_search(None, T, K, N, None, None, None, R, int(symmetric), GROUP_SIZE, None, None,
+                                   None, sz, None)
+
+    ws, wsb = _workspace(q, dev, workspace)
+    _check(lib.awq_clip_search(_ptr(X), T, K, N, _ptr(W), _ptr(s), _ptr(ratios), R, int(symmetric), GROUP_SIZE,
+                               _ptr(losses) if want_losses else None, _ptr(best), _ptr(ws),
+                               None if wsb is None else ctypes.byref(wsb), _stream(dev)))
+    return (losses if want_losses else None), best
 
 
 def awq_search(X, W, alphas, ratios, symmetric: bool = False, workspace=None):

@@ -53,6 +53,12 @@ int launch_grid_loss(const uint16_t* X, int T, int K, int N, const uint16_t* W,
                      const uint16_t* Yref, const float* S, const float* ratios, int C,
                      int symmetric, float* losses, void* workspace, hipStream_t stream);
 
+// ---------------------------------------------------------------- per-channel clipping search
+size_t clip_search_workspace_bytes(int T, int K);
+int launch_clip_search(const uint16_t* X, int T, int K, int N, const uint16_t* W, const float* s,
+                       const float* ratios, int R, int symmetric, float* losses, uint8_t* best,
+                       void* workspace, hipStream_t stream);
+
 // Y = bf16(X W^T) with bf16 weights W [N][K] (the unquantized reference output).
 int launch_reference_gemm(const uint16_t* X, int M, int K, int N, const uint16_t* W, uint16_t* Y,
                           hipStream_t stream);

@@ -161,6 +161,28 @@ int awq_grid_loss(const uint16_t* X, int T, int K, int N, const uint16_t* W, con
                           static_cast<hipStream_t>(stream));
 }
 
+int awq_clip_search(const uint16_t* X, int T, int K, int N, const uint16_t* W, const float* s,
+                    const float* ratios, int R, int symmetric, int group_size, float* losses, uint8_t* best,
+                    void* workspace, size_t* workspace_bytes, void* stream) {
+  int st = check_weight_shape(N, K, group_size);
+  if (st) return st;
+  if (T < 0) return W4_ERR_SHAPE;
+  if (symmetric != 0 && symmetric != 1) return W4_ERR_VALUE;
+  if (R < 1 || R > 64) return W4_ERR_VALUE;
+  const size_t need = clip_search_workspace_bytes(T, K);
+  if (!workspace) {
+    if (!workspace_bytes) return W4_ERR_WORKSPACE;
+    *workspace_bytes = need;
+    return W4_OK;
+  }
+  if (!workspace_bytes || *workspace_bytes < need) return W4_ERR_WORKSPACE;
+  if (N == 0) return W4_OK;
+  if ((T > 0 && !X) || !W || !ratios || !best) return W4_ERR_NULL;
+  if (misaligned(X) || misaligned(W) || misaligned(s) || misaligned(workspace)) return W4_ERR_ALIGN;
+  return launch_clip_search(X, T, K, N, W, s, ratios, R, symmetric, losses, best, workspace,
+                            static_cast<hipStream_t>(stream));
+}
+
 }  // extern "C"
 
 namespace {

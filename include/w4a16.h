@@ -205,8 +205,9 @@ int awq_grid_loss(const uint16_t* X, int T, int K, int N, const uint16_t* W,
  *
  *   X [T][K] bf16 calibration activations, T >= 0 (T = 0: every loss is 0).
  *   W [N][K] bf16 unquantized weight.  s [K] fp32 (every s[k] > 0) or NULL (= 1).
- *   ratios [R] fp32 device, 1 <= R <= 64 (else W4_ERR_VALUE); a ratio >= 1 means
- *   no clipping.
+ *   ratios [R] fp32 device, 1 <= R <= 64 (else W4_ERR_VALUE); every ratio must
+ *   lie in (0, 1] (a ratio of 1 means no clipping; the values are read on the
+ *   device and not checked: others give unspecified losses, never a fault).
  *   losses [G][N][R] fp32 device out, or NULL (not written); G = K / 128.
  *   best [N][G] uint8 device out.
  *   workspace: size query as in w4a16_gemm (workspace == NULL and workspace_bytes

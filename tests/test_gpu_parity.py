@@ -550,6 +550,31 @@ def test_clip_search_degenerate():
     assert L.numel() == 0 and best.numel() == 0
 
 
+def test_clip_search_rounding_ties_and_degenerate_groups():
+    """Row 0 holds exact half-integer quotients and their fp32 neighbours at ratio 1
+    (the codes come from the division itself there); rows 1-4 hold constant, zero and
+    single-outlier groups."""
+    sc = 164.0 / 2048.0
+    ties = [(k + 0.5) * sc for k in range(14)]
+    vals = ties + [float(np.nextafter(np.float32(t), np.float32(0))) for t in ties] + \
+        [float(np.nextafter(np.float32(t), np.float32(2))) for t in ties]
+    s = np.ones(256, dtype=np.float32)
+    s[2:2 + len(vals)] = vals
+    Wf = np.zeros((5, 256), dtype=np.float32)
+    Wf[0, 1] = 1.203125
+    Wf[0, 2:2 + len(vals)] = 1.0
+    Wf[0, 128:] = np.linspace(-1, 1, 128, dtype=np.float32)
+    Wf[1, :] = 0.5
+    Wf[2, :128] = -3.0
+    Wf[3, 5] = 100.0
+    W = wl.round_to_bf16_bits(Wf)
+    X = wl.round_to_bf16_bits(np.random.default_rng(12).standard_normal((64, 256)).astype(np.float32))
+    ratios = np.array([1.0, 0.9, 0.5], dtype=np.float32)
+    for sym in (False, True):
+        say("clip search ties and degenerate groups", sym)
+        _clip_check(X, W, s, ratios, sym)
+
+
 @pytest.mark.parametrize("sym", [False, True])
 def test_clip_search_full_size(sym):
     """4096 calibration tokens, K = 2048, N = 6144 at s(alpha = 0.5); 48 sampled

@@ -230,10 +230,20 @@ __global__ __launch_bounds__(256, 2) void clip_loss_kernel(const uint16_t* __res
       }
     }
   }
-  float amax = 0.0f;
 #pragma unroll
-  for (int i = 0; i < 64; ++i) amax = fmaxf(amax, fabsf(v[i]));
-  amax = fmaxf(amax, __shfl_xor(amax, 32, kWave));
+  for (int i = 0; i < 64; ++i) v[i] = __builtin_canonicalizef(v[i]);
+  // group minimum and maximum of v.  Clamping is monotone, so the clipped group's
+  // minimum and maximum are the clamped ones, and its largest magnitude is the larger
+  // magnitude of the two: the per-ratio statistics need no pass over the values.
+  float vmin = v[0], vmax = v[0];
+#pragma unroll
+  for (int i = 1; i < 64; ++i) {
+    vmin = fminf(vmin, v[i]);
+    vmax = fmaxf(vmax, v[i]);
+  }
+  vmin = fminf(vmin, __shfl_xor(vmin, 32, kWave));
+  vmax = fmaxf(vmax, __shfl_xor(vmax, 32, kWave));
+  const float amax = fmaxf(fabsf(vmin), fabsf(vmax));
   __syncthreads();
 
   float best_loss = 0.0f;
@@ -242,50 +252,57 @@ __global__ __launch_bounds__(256, 2) void clip_loss_kernel(const uint16_t* __res
     // compiler-only fence: keeps the LDS operand reads inside the loop (hoisted, the
     // 256 registers of all of H_g's operands would not fit)
     asm volatile("" ::: "memory");
-    const float ratio = ratios[j];
-    const bool clip = ratio < 1.0f;
-    const float t = ratio * amax;
-    auto clamped = [&](float x) { return clip ? fminf(fmaxf(x, -t), t) : x; };
+    // clip threshold t = ratio * absmax >= 0 for ratio > 0; a ratio >= 1 leaves every
+    // value in [-t, t], which is the unclipped group.  med3(x, -t, t) is the clamp.
+    const float t = ratios[j] * amax;
+    auto clamped = [&](float x) { return __builtin_amdgcn_fmed3f(x, -t, t); };
+    const float lo = clamped(vmin), hi = clamped(vmax);
     float sc, z;
     if (SYM) {
-      float am = 0.0f;
-#pragma unroll
-      for (int i = 0; i < 64; ++i) am = fmaxf(am, fabsf(clamped(v[i])));
-      am = fmaxf(am, __shfl_xor(am, 32, kWave));
-      sc = bf16_bits_to_f32(f32_to_bf16_bits(fmaxf(am, 1e-5f) / 7.0f));
-      z = 0.0f;
+      sc = bf16_bits_to_f32(f32_to_bf16_bits(fmaxf(fmaxf(fabsf(lo), fabsf(hi)), 1e-5f) / 7.0f));
+      z = 8.0f;                                        // stored offset: q = d + 8
     } else {
-      float lo = clamped(v[0]), hi = lo;
-#pragma unroll
-      for (int i = 1; i < 64; ++i) {
-        lo = fminf(lo, clamped(v[i]));
-        hi = fmaxf(hi, clamped(v[i]));
-      }
-      lo = fminf(lo, __shfl_xor(lo, 32, kWave));
-      hi = fmaxf(hi, __shfl_xor(hi, 32, kWave));
       sc = bf16_bits_to_f32(f32_to_bf16_bits(fmaxf(hi - lo, 1e-5f) / 15.0f));
       z = fminf(fmaxf(rintf(-lo / sc), 0.0f), 15.0f);
     }
-    // codes as nibbles (q - z + 8 in 0..15 for both forms: asymmetric q - z lies in [-15, 15]
-    // only across groups; within one group with zero z it spans [-z, 15 - z], kept exact
-    // below as the signed integer d = q - z in a byte).
+    // stored codes q in 0..15 (bytes), d = q - z.  The code is rint of the IEEE quotient
+    // c / sc.  The product c * rcp(sc) is within |q0| 2^-22 of that quotient (reciprocal
+    // within 1 ulp, one rounding of the product), so where q0 lies farther than
+    // |q0| 2^-20 from every half-integer both round to the same integer; a lane with
+    // any value closer redoes its codes with the division itself.
+    const float rc = __builtin_amdgcn_rcpf(sc);
+    auto code = [&](float k) {
+      return SYM ? __builtin_amdgcn_fmed3f(k, -8.0f, 7.0f) + 8.0f : __builtin_amdgcn_fmed3f(k + z, 0.0f, 15.0f);
+    };
     uint32_t dq[16];
+    float near = 0.0f;
 #pragma unroll
     for (int w = 0; w < 16; ++w) {
       uint32_t word = 0;
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
-        const float c = clamped(v[4 * w + u]);
-        const float d = SYM ? fminf(fmaxf(rintf(c / sc), -8.0f), 7.0f)
-                            : fminf(fmaxf(rintf(c / sc) + z, 0.0f), 15.0f) - z;
-        word |= ((uint32_t)(int)d & 0xFFu) << (8 * u);
+        const float q0 = clamped(v[4 * w + u]) * rc;
+        const float k = rintf(q0);
+        near = fmaxf(near, fmaf(fabsf(q0), 0x1p-20f, fabsf(q0 - k)));
+        word = __builtin_amdgcn_cvt_pk_u8_f32(code(k), u, word);
       }
       dq[w] = word;
     }
-    // e[m] = v[m] - d[m] sc, fp32 (the same operations in the products and the epilogue)
+    if (near >= 0.5f) {
+#pragma unroll
+      for (int w = 0; w < 16; ++w) {
+        uint32_t word = 0;
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+          word = __builtin_amdgcn_cvt_pk_u8_f32(code(rintf(clamped(v[4 * w + u]) / sc)), u, word);
+        dq[w] = word;
+      }
+    }
+    // e[m] = v[m] - d[m] sc with one rounding (d sc is exact: a small integer times a
+    // bf16 value), the same in the products and in the epilogue
     auto err = [&](int m) {
-      const float d = (float)(int8_t)((dq[m >> 2] >> (8 * (m & 3))) & 0xFFu);
-      return v[m] - d * sc;
+      const float d = (float)((dq[m >> 2] >> (8 * (m & 3))) & 0xFFu) - z;
+      return fmaf(-d, sc, v[m]);
     };
 
     f32x16 acc[4];
@@ -297,15 +314,12 @@ __global__ __launch_bounds__(256, 2) void clip_loss_kernel(const uint16_t* __res
       uint32_t ph[4], pl[4];
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        uint32_t hb[2], lb[2];
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-          const float e = err(8 * st + 2 * q + u);
-          hb[u] = f32_to_bf16_bits(e);
-          lb[u] = f32_to_bf16_bits(e - bf16_bits_to_f32(hb[u]));
-        }
-        ph[q] = hb[0] | (hb[1] << 16);
-        pl[q] = lb[0] | (lb[1] << 16);
+        const float e0 = err(8 * st + 2 * q), e1 = err(8 * st + 2 * q + 1);
+        const bf16x2 hp = {(__bf16)e0, (__bf16)e1};
+        ph[q] = __builtin_bit_cast(uint32_t, hp);
+        const bf16x2 lp = {(__bf16)(e0 - __uint_as_float(ph[q] << 16)),
+                           (__bf16)(e1 - __uint_as_float(ph[q] & 0xFFFF0000u))};
+        pl[q] = __builtin_bit_cast(uint32_t, lp);
       }
       const bf16x8 ehi = __builtin_bit_cast(bf16x8, make_uint4(ph[0], ph[1], ph[2], ph[3]));
       const bf16x8 elo = __builtin_bit_cast(bf16x8, make_uint4(pl[0], pl[1], pl[2], pl[3]));
@@ -327,7 +341,7 @@ __global__ __launch_bounds__(256, 2) void clip_loss_kernel(const uint16_t* __res
     // register m % 16.
     float part = 0.0f;
 #pragma unroll
-    for (int m = 0; m < 64; ++m) part = part + err(m) * acc[m >> 4][m & 15];
+    for (int m = 0; m < 64; ++m) part = fmaf(err(m), acc[m >> 4][m & 15], part);
     const float other = __shfl_xor(part, 32, kWave);
     const float loss = half ? other + part : part + other;   // (lower half) + (upper half) in every lane
     if (j == 0 || loss < best_loss) {

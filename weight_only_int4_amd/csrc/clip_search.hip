@@ -83,6 +83,20 @@ __global__ __launch_bounds__(256) void gram_partial_kernel(const uint16_t* __res
     for (int b = 0; b < 2; ++b) acc[a][b] = f32x16{};
 
   const int bi0 = 2 * (wave >> 1), bj0 = 2 * (wave & 1);
+  // the next chunk's rows are loaded into registers while the current one is multiplied
+  uint4 d[2][2];
+  auto load = [&](int t0) {
+#pragma unroll
+    for (int it = 0; it < 2; ++it)
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int t = t0 + 2 * tp + u;
+        d[it][u] = make_uint4(0u, 0u, 0u, 0u);
+        if (t < t_end)
+          d[it][u] = *reinterpret_cast<const uint4*>(X + (size_t)t * K + (size_t)g * kGroup + 8 * (oc + 8 * it));
+      }
+  };
+  if (t_begin < t_end) load(t_begin);
   for (int t0 = t_begin; t0 < t_end; t0 += kGramChunk) {
     __syncthreads();
 #pragma unroll
@@ -91,10 +105,7 @@ __global__ __launch_bounds__(256) void gram_partial_kernel(const uint16_t* __res
       uint32_t xv[2][4];
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
-        const int t = t0 + 2 * tp + u;
-        uint4 d = make_uint4(0u, 0u, 0u, 0u);
-        if (t < t_end) d = *reinterpret_cast<const uint4*>(X + (size_t)t * K + (size_t)g * kGroup + c8);
-        const uint32_t w[4] = {d.x, d.y, d.z, d.w};
+        const uint32_t w[4] = {d[it][u].x, d[it][u].y, d[it][u].z, d[it][u].w};
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const float lo = __uint_as_float(w[q] << 16) / sv[it][2 * q];
@@ -109,6 +120,7 @@ __global__ __launch_bounds__(256) void gram_partial_kernel(const uint16_t* __res
         *reinterpret_cast<uint32_t*>(&xt[(c8 + i) * kXtStride + 2 * tp]) = pair;
       }
     }
+    if (t0 + kGramChunk < t_end) load(t0 + kGramChunk);
     __syncthreads();
 #pragma unroll
     for (int step = 0; step < kGramChunk / 16; ++step) {
@@ -144,34 +156,49 @@ __global__ __launch_bounds__(256) void gram_partial_kernel(const uint16_t* __res
 // exact fp32 remainder), written as the loss kernel's A operands:
 //   Hperm[g][((rb * 8 + step) * 2 + part) * 64 + lane] = 8 bf16, element jj =
 //   H[out_slot_index(32 rb + lane % 32)][64 (lane / 32) + 8 step + jj].
-// One thread per (g, rb, step, lane): grid G * 2048 / 256.
+// One thread per (g, row, 8-column run), consecutive threads reading consecutive runs:
+// grid G * 2048 / 256.  Row p = out_slot_index(o) for o = 32 rb + i with
+// rb = (p / 16) % 4 and i = (p % 4) + 4 (p / 64) + 8 ((p % 16) / 4).
 __global__ __launch_bounds__(256) void gram_finish_kernel(const float* __restrict__ Hpart, int slices, int G,
                                                           uint4* __restrict__ Hperm) {
   const int idx = blockIdx.x * 256 + threadIdx.x;
   const int g = idx >> 11;
   if (g >= G) return;
-  const int rem = idx & 2047;
-  const int lane = rem & 63;
-  const int step = (rem >> 6) & 7;
-  const int rb = rem >> 9;
-  const int row = out_slot_index(32 * rb + (lane & 31));
-  const int col0 = 64 * (lane >> 5) + 8 * step;
+  const int row = (idx >> 4) & 127;
+  const int run = idx & 15;
+  double acc[8];
+#pragma unroll
+  for (int jj = 0; jj < 8; ++jj) acc[jj] = 0.0;
+  for (int ts = 0; ts < slices; ++ts) {
+    const float4* src =
+        reinterpret_cast<const float4*>(Hpart + ((size_t)ts * G + g) * (kGroup * kGroup) + row * kGroup + 8 * run);
+    const float4 a = src[0], b = src[1];
+    acc[0] += (double)a.x;
+    acc[1] += (double)a.y;
+    acc[2] += (double)a.z;
+    acc[3] += (double)a.w;
+    acc[4] += (double)b.x;
+    acc[5] += (double)b.y;
+    acc[6] += (double)b.z;
+    acc[7] += (double)b.w;
+  }
   uint32_t hi[4], lo[4];
 #pragma unroll
   for (int jj = 0; jj < 8; jj += 2) {
     uint32_t hb[2], lb[2];
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
-      double acc = 0.0;
-      for (int ts = 0; ts < slices; ++ts)
-        acc += (double)Hpart[((size_t)ts * G + g) * (kGroup * kGroup) + row * kGroup + col0 + jj + u];
-      const float h = (float)acc;
+      const float h = (float)acc[jj + u];
       hb[u] = f32_to_bf16_bits(h);
       lb[u] = f32_to_bf16_bits(h - bf16_bits_to_f32(hb[u]));
     }
     hi[jj >> 1] = hb[0] | (hb[1] << 16);
     lo[jj >> 1] = lb[0] | (lb[1] << 16);
   }
+  const int rb = (row >> 4) & 3;
+  const int i = (row & 3) + 4 * (row >> 6) + 8 * ((row & 15) >> 2);
+  const int lane = i + 32 * (run >> 3);
+  const int step = run & 7;
   uint4* dst = Hperm + (size_t)g * (kHpermBytes / 16) + (size_t)((rb * 8 + step) * 2) * 64 + lane;
   dst[0] = make_uint4(hi[0], hi[1], hi[2], hi[3]);
   dst[64] = make_uint4(lo[0], lo[1], lo[2], lo[3]);

@@ -156,8 +156,11 @@ int w4a8_gemv(const int8_t* Xq, const float* sx, const int32_t* xsum, int M, int
  *   workspace (always needed, > 0 bytes): X with every 8-channel run reordered
  *   for the packed-word expansion, the negated group row sums of X (each as
  *   three exact bf16 parts) and, per group and column, the scale with
- *   bf16(128 + z).  Size query as in w4a16_gemv.  The size depends only on
- *   (M, K, N); about 2 M K bytes.
+ *   bf16(128 + z); when the output tiles are too few to fill the chip (small M
+ *   and N), the groups are split among several workgroups per tile and the
+ *   workspace also holds their fp32 partial outputs (splits x M x N x 4 bytes,
+ *   added in split order by a second kernel).  Size query as in w4a16_gemv.  The
+ *   size depends only on (M, K, N); about 2 M K bytes plus the partials.
  */
 int w4a16_gemm(const uint16_t* X, int M, int K, int N, const uint32_t* qweight,
                const uint16_t* scales, const uint32_t* qzeros, int symmetric, int group_size,

@@ -3,6 +3,8 @@
 // counts; model card "Qwen3.6-27B-W4A16": int4 weights, 16-bit activations).
 #include <type_traits>
 
+#include <algorithm>
+
 #include "gemm_core.hpp"
 
 namespace w4 {
@@ -129,13 +131,61 @@ int launch_gemm_prep(const uint16_t* X, size_t x_stride, int M, int K, int mpad,
 }
 
 
+namespace {
+
+// K split for grids too small to fill the chip: as many splits as fit the tiles x
+// splits workgroups into one round of two resident workgroups on each of 256 CUs
+// (at least 2 below a full round), each split at least 4 groups long.  A function
+// of the shape only (the workspace size follows it).
+constexpr long long kSplitSlots = 2 * 256;
+
+int gemm_k_splits(int M, int K, int N) {
+  const long long tiles = (long long)((N + kBN - 1) / kBN) * ((M + kBM - 1) / kBM);
+  const int G = K / kGroup;
+  if (tiles >= kSplitSlots || G < 8) return 1;
+  int s = (int)std::min<long long>(std::max<long long>(2, kSplitSlots / tiles), G / 4);
+  s = std::max(s, 1);
+  const int gps = (G + s - 1) / s;
+  return (G + gps - 1) / gps;          // every split non-empty
+}
+
+// Y[i] = bf16(sum over splits k of ypart[k * stride + i]), fp32 in split order; 4 outputs
+// per thread (stride a multiple of 4).
+__global__ __launch_bounds__(256) void gemm_split_reduce_kernel(const float* ypart, int splits, size_t stride,
+                                                                size_t count, uint16_t* Y) {
+  const size_t i = ((size_t)blockIdx.x * 256 + threadIdx.x) * 4;
+  if (i >= count) return;
+  if (i + 4 <= count) {
+    float4 s = *reinterpret_cast<const float4*>(ypart + i);
+    for (int k = 1; k < splits; ++k) {
+      const float4 v = *reinterpret_cast<const float4*>(ypart + (size_t)k * stride + i);
+      s.x += v.x;
+      s.y += v.y;
+      s.z += v.z;
+      s.w += v.w;
+    }
+    *reinterpret_cast<uint2*>(Y + i) =
+        make_uint2(f32_to_bf16_bits(s.x) | (f32_to_bf16_bits(s.y) << 16), f32_to_bf16_bits(s.z) | (f32_to_bf16_bits(s.w) << 16));
+  } else {
+    for (size_t j = i; j < count; ++j) {
+      float s = ypart[j];
+      for (int k = 1; k < splits; ++k) s += ypart[(size_t)k * stride + j];
+      Y[j] = (uint16_t)f32_to_bf16_bits(s);
+    }
+  }
+}
+
+}  // namespace
+
 // workspace: pair-arranged X [mpad][K] bf16 (rows >= M zero), rsq [G][mpad][4] bf16,
-// szq [G][npad] u32
+// szq [G][npad] u32, and with a K split the fp32 partial outputs [splits][M][N]
 size_t gemm_workspace_bytes(int M, int K, int N) {
   if (M <= 0 || K <= 0 || N <= 0) return 0;
   const size_t mpad = align_up((size_t)M, kBM);
   const size_t G = (size_t)(K / kGroup);
-  return align_up(mpad * K * 2, 256) + align_up(G * mpad * 8, 256) + align_up(G * gemm_npad(N) * 4, 256);
+  const int splits = gemm_k_splits(M, K, N);
+  return align_up(mpad * K * 2, 256) + align_up(G * mpad * 8, 256) + align_up(G * gemm_npad(N) * 4, 256) +
+         (splits > 1 ? (size_t)splits * align_up((size_t)M * N, 64) * 4 : 0);
 }
 
 int launch_gemm(const uint16_t* X, int M, int K, int N, const uint32_t* qweight,
@@ -146,12 +196,15 @@ int launch_gemm(const uint16_t* X, int M, int K, int N, const uint32_t* qweight,
   if (((long long)M + kBM) * K >= (1LL << 31) || (long long)N * K >= (1LL << 33)) return W4_ERR_SHAPE;
   const int mpad = (int)align_up((size_t)M, kBM);
   const int G = K / kGroup;
+  const int splits = gemm_k_splits(M, K, N);
   char* ws = static_cast<char*>(workspace);
   uint16_t* xp = reinterpret_cast<uint16_t*>(ws);
   ws += align_up((size_t)mpad * K * 2, 256);
   uint16_t* rsq = reinterpret_cast<uint16_t*>(ws);
   ws += align_up((size_t)G * mpad * 8, 256);
   uint32_t* szq = reinterpret_cast<uint32_t*>(ws);
+  ws += align_up((size_t)G * gemm_npad(N) * 4, 256);
+  float* ypart = splits > 1 ? reinterpret_cast<float*>(ws) : nullptr;
   int st = launch_gemm_prep(X, 0, M, K, mpad, scales, 0, qzeros, 0, symmetric, N, rsq, 0, szq, 0, xp, 1, stream);
   if (st != W4_OK) return st;
   GemmCoreArgs a{};
@@ -165,11 +218,21 @@ int launch_gemm(const uint16_t* X, int M, int K, int N, const uint32_t* qweight,
   a.mpad = mpad;
   a.npad = gemm_npad(N);
   a.Y = Y;
+  a.ypart = ypart;
+  a.ypart_stride = align_up((size_t)M * N, 64);
+  a.gsplit = splits > 1 ? (G + splits - 1) / splits : 0;
   const long long tiles = (long long)((N + kBN - 1) / kBN) * ((M + kBM - 1) / kBM);
   if (tiles > 0x7FFFFFFFLL) return W4_ERR_SHAPE;
-  const dim3 grid((unsigned)tiles, 1, 1);
+  const dim3 grid((unsigned)tiles, (unsigned)splits, 1);
   hipLaunchKernelGGL((gemm_core_kernel<true, EPI_STORE>), grid, dim3(kGemmWaves * 64), 0, stream, a);
   W4_CHECK_LAUNCH();
+  if (splits > 1) {
+    const size_t count = (size_t)M * N;
+    const size_t blocks = (count + 1023) / 1024;
+    hipLaunchKernelGGL(gemm_split_reduce_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, ypart, splits,
+                       a.ypart_stride, count, Y);
+    W4_CHECK_LAUNCH();
+  }
   return W4_OK;
 }
 

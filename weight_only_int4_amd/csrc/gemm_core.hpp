@@ -68,8 +68,13 @@ struct GemmCoreArgs {
   int mpad, npad;          // M and N rounded up to 128
   // bf16 weights (reference path)
   const uint16_t* W;       // [N][K]
+  // split over K: workgroup (tile, blockIdx.y) covers groups [gsplit y, gsplit (y + 1));
+  // 0 = all groups
+  int gsplit;
   // epilogue
-  uint16_t* Y;             // EPI_STORE: [M][N] bf16
+  uint16_t* Y;             // EPI_STORE: [M][N] bf16 (ypart == NULL)
+  float* ypart;            // EPI_STORE with a K split: fp32 partial sums, split y's [M][N] at y * ypart_stride
+  size_t ypart_stride;
   const uint16_t* Yref;    // EPI_SQDIFF: [M][N] bf16
   float* partials;         // EPI_SQDIFF: [z][tiles]
 };
@@ -154,6 +159,8 @@ __global__ __launch_bounds__(kGemmWaves * 64, GemmSmem<INT4>::kBlocksPerCU) void
   const int m0 = tm * kBM, n0 = tn * kBN;
   const int zc_idx = blockIdx.z;
   const int G = a.K >> 7;
+  const int g0 = a.gsplit ? (int)blockIdx.y * a.gsplit : 0;   // this workgroup's groups: [g0, g0 + Gl)
+  const int Gl = a.gsplit ? min(G - g0, a.gsplit) : G;
   const uint32_t smem_base = (uint32_t)(uintptr_t)smem;   // LDS byte address (low half of the generic one)
 
   // ---- copy sources: wave-uniform bases (without the group term) and per-lane byte offsets ----
@@ -413,13 +420,13 @@ __global__ __launch_bounds__(kGemmWaves * 64, GemmSmem<INT4>::kBlocksPerCU) void
   // g+1, issued during iteration g-1, may stay in flight), barriers -- after which every
   // wave's group-g copies are in LDS and every wave has finished reading group
   // g-1 -- then computes group g while issuing the copies of group g + D into the
-  // stage group g-1 used.  Past the last group the copies repeat group G-1 into
+  // stage group g-1 used.  Past its last group a workgroup's copies repeat that group into
   // that stage, which nothing reads again: every stage issues the same L copies,
   // so the wait count is the same in every iteration.
   static_assert(D == 1 || D == 2, "at most one stage in flight at each wait");
 #pragma unroll
   for (int p = 0; p < D; ++p) {
-    const GroupSrc src = group_src(min(p, G - 1));
+    const GroupSrc src = group_src(g0 + min(p, Gl - 1));
     const uint32_t st = smem_base + p * SM::kStage;
     copies_of_step(std::integral_constant<int, 0>{}, src, st);
     copies_of_step(std::integral_constant<int, 1>{}, src, st);
@@ -444,16 +451,16 @@ __global__ __launch_bounds__(kGemmWaves * 64, GemmSmem<INT4>::kBlocksPerCU) void
     constexpr int s = decltype(sidx)::value;
     wait_vmcnt<kInFlight>();
     lds_barrier();
-    const GroupSrc nsrc = group_src(min(g + D, G - 1));
+    const GroupSrc nsrc = group_src(g0 + min(g + D, Gl - 1));
     compute(s, nsrc, smem_base + ((s + D) % S) * SM::kStage);
   };
 
-  for (int g = 0; g < G; g += S) {
+  for (int g = 0; g < Gl; g += S) {
     iteration(std::integral_constant<int, 0>{}, g);
-    if (g + 1 >= G) break;
+    if (g + 1 >= Gl) break;
     iteration(std::integral_constant<int, 1>{}, g + 1);
     if constexpr (S == 3) {
-      if (g + 2 >= G) break;
+      if (g + 2 >= Gl) break;
       iteration(std::integral_constant<int, 2>{}, g + 2);
     }
   }
@@ -471,7 +478,16 @@ __global__ __launch_bounds__(kGemmWaves * 64, GemmSmem<INT4>::kBlocksPerCU) void
   const int ncol = n0 + col;
   const bool nok = ncol < a.N;
   if constexpr (EPI == EPI_STORE) {
-    if (nok) {
+    if (nok && a.ypart) {
+      float* yp = a.ypart + (size_t)blockIdx.y * a.ypart_stride;
+#pragma unroll
+      for (int bm = 0; bm < 2; ++bm)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int row = m0 + 32 * bm + 8 * (r >> 2) + 4 * h + (r & 3);
+          if (row < a.M) yp[(size_t)row * a.N + ncol] = acc[bm][r];
+        }
+    } else if (nok) {
 #pragma unroll
       for (int bm = 0; bm < 2; ++bm)
 #pragma unroll

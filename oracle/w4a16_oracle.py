@@ -341,3 +341,141 @@ def search(X_bf16, W_bf16, alphas=None, ratios=None, symmetric=False):
                    ratios, symmetric, Y_ref)
     ir = int(np.argmin(lr))
     return dict(alpha_losses=la, ratio_losses=lr, alpha_index=ia, ratio_index=ir, s=s_star)
+
+
+# --------------------------------------------------------------------------- look-ahead block scoring
+#
+# [AWQ-W4 card] details table "Search" and the paragraph under it: the candidate
+# for block i is scored at the output of block i + 1, which runs unquantized; the
+# reference is the same path with block i unquantized too; the last block falls
+# back to its own output.  The block is the base model's decoder block ([AWQ-W4
+# card] "Base model": Qwen3-1.7B, hidden 2048; [q326 page] architecture notes:
+# grouped-query attention with 16 query heads over 8 key/value heads, head size
+# 128, rotary positions with base 10^6, SiLU-gated feed-forward of width 6144).
+# Readings: pre-norm RMSNorm (eps 1e-6) before attention and before the
+# feed-forward, residual adds after each; no biases and no per-head q/k norms
+# (the pages name neither); rotary embedding on the pairs (j, j + 64) of each
+# head at the token's position within its sequence; causal attention within each
+# sequence with scale 1/sqrt(128), query head h reading key/value head
+# h // (n_q / n_kv); every op output is rounded to bf16 ("in bf16"), the
+# arithmetic inside an op is fp64.  The loss is the mean over tokens and hidden
+# units of the squared difference of the two bf16 outputs.
+
+HEAD_DIM = 128
+LINEARS = ("q", "k", "v", "o", "gate", "up", "down")
+RMS_EPS = 1e-6
+ROPE_BASE = 1e6
+
+
+def _bf16_round(x) -> np.ndarray:
+    """fp64 values -> nearest bf16 value (via fp32, as the kernels store), as fp64."""
+    return bf16_to_f32(f32_to_bf16(np.asarray(x, dtype=np.float64).astype(np.float32))).astype(np.float64)
+
+
+def rmsnorm(x, g, eps=RMS_EPS) -> np.ndarray:
+    """x [T][H] and g [H] bf16 values (fp64): bf16(x / sqrt(mean_k x^2 + eps) * g)."""
+    r = 1.0 / np.sqrt(np.mean(x * x, axis=1) + eps)
+    return _bf16_round(x * r[:, None] * g[None, :])
+
+
+def rope_tables(L: int, base: float = ROPE_BASE):
+    """cos and sin [L][64] of position p times base^(-2j/128), fp64."""
+    inv = base ** (-(2.0 * np.arange(HEAD_DIM // 2)) / HEAD_DIM)
+    ang = np.arange(L, dtype=np.float64)[:, None] * inv[None, :]
+    return np.cos(ang), np.sin(ang)
+
+
+def rope_raw(x, B: int, L: int, n_heads: int, base: float = ROPE_BASE) -> np.ndarray:
+    """Rotary embedding of x [B*L][n_heads*128] in fp64: per head, the pair (j, j + 64)
+    at position p (within its sequence) rotates by the angle p * base^(-2j/128)."""
+    c, s = rope_tables(L, base)
+    xr = x.reshape(B, L, n_heads, HEAD_DIM)
+    x1, x2 = xr[..., :64], xr[..., 64:]
+    c, s = c[None, :, None, :], s[None, :, None, :]
+    out = np.concatenate([x1 * c - x2 * s, x2 * c + x1 * s], axis=-1)
+    return out.reshape(B * L, n_heads * HEAD_DIM)
+
+
+def rope(x, B: int, L: int, n_heads: int, base: float = ROPE_BASE) -> np.ndarray:
+    """rope_raw rounded to bf16."""
+    return _bf16_round(rope_raw(x, B, L, n_heads, base))
+
+
+def attention(q, k, v, B: int, L: int, n_q: int, n_kv: int) -> np.ndarray:
+    """attention_raw rounded to bf16."""
+    return _bf16_round(attention_raw(q, k, v, B, L, n_q, n_kv))
+
+
+def attention_raw(q, k, v, B: int, L: int, n_q: int, n_kv: int) -> np.ndarray:
+    """Causal grouped-query attention per sequence in fp64: softmax(q k^T / sqrt(128)) v
+    with query head h reading key/value head h // (n_q / n_kv)."""
+    rep = n_q // n_kv
+    qh = q.reshape(B, L, n_q, HEAD_DIM)
+    kh = k.reshape(B, L, n_kv, HEAD_DIM)
+    vh = v.reshape(B, L, n_kv, HEAD_DIM)
+    out = np.zeros_like(qh)
+    mask = np.triu(np.ones((L, L), dtype=bool), 1)            # key after query
+    for b in range(B):
+        for h in range(n_q):
+            kv = h // rep
+            sc = qh[b, :, h, :] @ kh[b, :, kv, :].T / np.sqrt(HEAD_DIM)
+            sc[mask] = -np.inf
+            sc = sc - sc.max(axis=1, keepdims=True)
+            p = np.exp(sc)
+            p = p / p.sum(axis=1, keepdims=True)
+            out[b, :, h, :] = p @ vh[b, :, kv, :]
+    return out.reshape(B * L, n_q * HEAD_DIM)
+
+
+def silu_mul(g, u) -> np.ndarray:
+    """bf16(silu(g) * u), silu(g) = g / (1 + exp(-g))."""
+    return _bf16_round(g / (1.0 + np.exp(-g)) * u)
+
+
+def block_forward(x_bf16, B: int, L: int, blk: dict, n_q: int, n_kv: int, candidate=None):
+    """One decoder block on x [B*L][H] (uint16 bf16).  blk maps "norm1", "norm2" to
+    bf16 [H] and each name of LINEARS to its bf16 weight [out][in].  candidate =
+    (name, s fp32 [in], packed (qweight, scales, qzeros), symmetric) replaces that
+    linear by its deployed int4 form: input bf16(in / s) against the dequantized
+    codes.  Returns the block output as bf16 bits [B*L][H]."""
+    val = lambda bits: bf16_to_f32(np.asarray(bits, dtype=np.uint16)).astype(np.float64)
+
+    def lin(name, a):
+        if candidate is not None and candidate[0] == name:
+            _, s, (qw, sc, qz), sym = candidate
+            K = a.shape[1]
+            s32 = np.asarray(s, dtype=np.float32)
+            xs = bf16_to_f32(f32_to_bf16(a.astype(np.float32) / s32[None, :])).astype(np.float64)
+            w = dequantize(qw, sc, qz, K, sym).astype(np.float64)
+        else:
+            xs, w = a, val(blk[name])
+        return _bf16_round(xs @ w.T)
+
+    x = val(x_bf16)
+    a = rmsnorm(x, val(blk["norm1"]))
+    q = rope(lin("q", a), B, L, n_q)
+    k = rope(lin("k", a), B, L, n_kv)
+    v = lin("v", a)
+    o = attention(q, k, v, B, L, n_q, n_kv)
+    h = _bf16_round(x + lin("o", o))
+    b2 = rmsnorm(h, val(blk["norm2"]))
+    m = silu_mul(lin("gate", b2), lin("up", b2))
+    y = _bf16_round(h + lin("down", m))
+    return f32_to_bf16(y.astype(np.float32))
+
+
+def lookahead_losses(x_bf16, B, L, blk, nxt, n_q, n_kv, name, S, ratios, symmetric=False):
+    """Look-ahead (d = 1) and block-output (d = 0) losses of C candidates (S[c], ratios[c])
+    for linear `name` of block blk, nxt the next block or None (last block: the d = 1
+    loss falls back to the block's own output).  Returns (d1 [C], d0 [C]) fp64."""
+    val = lambda bits: bf16_to_f32(np.asarray(bits, dtype=np.uint16)).astype(np.float64)
+    ref_i = block_forward(x_bf16, B, L, blk, n_q, n_kv)
+    ref_n = block_forward(ref_i, B, L, nxt, n_q, n_kv) if nxt is not None else ref_i
+    d1, d0 = [], []
+    for c in range(len(ratios)):
+        packed = quantize_pack(blk[name], S[c], float(np.float32(ratios[c])), symmetric)
+        yi = block_forward(x_bf16, B, L, blk, n_q, n_kv, candidate=(name, S[c], packed, symmetric))
+        yn = block_forward(yi, B, L, nxt, n_q, n_kv) if nxt is not None else yi
+        d0.append(float(np.mean((val(yi) - val(ref_i)) ** 2)))
+        d1.append(float(np.mean((val(yn) - val(ref_n)) ** 2)))
+    return np.array(d1), np.array(d0)

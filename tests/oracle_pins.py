@@ -498,7 +498,127 @@ def check_clip_channel_special_cases():
         assert np.array_equal(Lr, La[:, [3, 1], :]) and np.array_equal(br, ba[[3, 1]])
 
 
+# ----------------------------------------------------------------------------- look-ahead block
+
+def _block(rng, H=256, I=384, n_q=2, n_kv=1, std=0.05):
+    w = lambda o, i: round_to_bf16_bits((rng.standard_normal((o, i)) * std).astype(np.float32))
+    g = lambda: round_to_bf16_bits((1 + 0.1 * rng.standard_normal(H)).astype(np.float32))
+    return dict(norm1=g(), norm2=g(), q=w(n_q * 128, H), k=w(n_kv * 128, H), v=w(n_kv * 128, H),
+                o=w(H, n_q * 128), gate=w(I, H), up=w(I, H), down=w(H, I))
+
+
+def check_rope_rotation():
+    """Rotary embedding: position 0 is the identity; each (j, j + 64) pair keeps its
+    length; q.k after rotation depends only on the position difference; the pure-Python
+    rotation agrees; rope() is rope_raw rounded to bf16."""
+    rng = np.random.default_rng(71)
+    B, L, nh = 2, 6, 2
+    x = O.bf16_to_f32(round_to_bf16_bits(rng.standard_normal((B * L, nh * 128)).astype(np.float32)))
+    x = x.astype(np.float64)
+    r = O.rope_raw(x, B, L, nh)
+    xr, rr = x.reshape(B, L, nh, 128), r.reshape(B, L, nh, 128)
+    assert np.array_equal(rr[:, 0], xr[:, 0])
+    assert np.allclose(rr[..., :64] ** 2 + rr[..., 64:] ** 2, xr[..., :64] ** 2 + xr[..., 64:] ** 2, rtol=1e-12)
+    # q at position m, k at n: same vectors placed at every position of a sequence
+    qv, kv = x[0, :128], x[1, :128]
+    seq = np.zeros((1 * L, 2 * 128))
+    seq[:, :128], seq[:, 128:] = qv, kv
+    rs = O.rope_raw(seq, 1, L, 2)
+    dots = np.array([[rs[m, :128] @ rs[n, 128:] for n in range(L)] for m in range(L)])
+    for d in range(-(L - 1), L):
+        diag = np.diagonal(dots, offset=d)
+        assert np.allclose(diag, diag[0], rtol=1e-10, atol=1e-10), d
+    for t in range(L):
+        want = S.rotate_pairs(xr[1, t, 1].tolist(), t)
+        assert np.allclose(rr[1, t, 1], want, rtol=1e-12, atol=1e-12)
+    assert np.array_equal(O.rope(x, B, L, nh), O.bf16_to_f32(O.f32_to_bf16(r.astype(np.float32))).astype(np.float64))
+
+
+def check_attention():
+    """Causal grouped-query attention: the pure-Python loop agrees to 1e-12 (2 query heads
+    over 1 key/value head, and 4 over 2); the first token returns its own value; zero
+    queries average the values seen so far; a key/value head that is all zero gives
+    zero output exactly for the query heads that read it."""
+    rng = np.random.default_rng(73)
+    for n_q, n_kv in ((2, 1), (4, 2)):
+        L = 5
+        q = rng.standard_normal((L, n_q * 128))
+        k = rng.standard_normal((L, n_kv * 128))
+        v = rng.standard_normal((L, n_kv * 128))
+        o = O.attention_raw(q, k, v, 1, L, n_q, n_kv)
+        want = np.array(S.causal_attention(q.tolist(), k.tolist(), v.tolist(), L, n_q, n_kv))
+        assert np.allclose(o, want, rtol=1e-12, atol=1e-12), (n_q, n_kv)
+        rep = n_q // n_kv
+        for h in range(n_q):
+            assert np.allclose(o[0, 128 * h:128 * h + 128], v[0, 128 * (h // rep):128 * (h // rep) + 128], rtol=1e-14)
+        oz = O.attention_raw(np.zeros_like(q), k, v, 1, L, n_q, n_kv)
+        for t in range(L):
+            for h in range(n_q):
+                kv = h // rep
+                assert np.allclose(oz[t, 128 * h:128 * h + 128], v[:t + 1, 128 * kv:128 * kv + 128].mean(axis=0))
+        v2 = v.copy()
+        v2[:, :128] = 0
+        o2 = O.attention_raw(q, k, v2, 1, L, n_q, n_kv)
+        assert not o2[:, :128 * rep].any() and (n_kv == 1 or o2[:, 128 * rep:].all())
+
+
+def check_rmsnorm_and_silu():
+    """RMSNorm of a +-c row with eps 0 is sign * g exactly; of a zero row is zero; silu(0)
+    = 0 and silu(g) * 1 matches g sigmoid(g) closed values."""
+    g = O.bf16_to_f32(round_to_bf16_bits(np.linspace(0.5, 2, 256).astype(np.float32))).astype(np.float64)
+    x = np.where(np.arange(256) % 3 == 0, -3.0, 3.0)[None, :]
+    y = O.rmsnorm(x, g, eps=0.0)
+    assert np.array_equal(y[0], O._bf16_round(np.sign(x[0]) * g))
+    assert not O.rmsnorm(np.zeros((1, 256)), g).any()
+    gv = np.array([0.0, 1.0, -2.0, 4.0])
+    got = O.silu_mul(gv, np.ones(4))
+    want = O._bf16_round(gv / (1 + np.exp(-gv)))
+    assert np.array_equal(got, want) and got[0] == 0.0
+    assert abs(got[1] - 0.7310585786) < 4e-3 and abs(got[2] + 0.2384058440) < 2e-3
+
+
+def check_block_and_lookahead():
+    """Block with zero o- and down-projections returns its input; a candidate whose
+    weights are already on the int4 grid (s = 1, r = 1) reproduces the reference, so
+    both losses are 0; without a next block the d = 1 loss equals the d = 0 loss;
+    a coarser clip gives a larger loss than none on this block."""
+    rng = np.random.default_rng(79)
+    B, L, H = 2, 6, 256
+    blk = _block(rng, H=H)
+    x = round_to_bf16_bits(rng.standard_normal((B * L, H)).astype(np.float32))
+    z = dict(blk)
+    z["o"] = np.zeros_like(blk["o"])
+    z["down"] = np.zeros_like(blk["down"])
+    assert np.array_equal(O.block_forward(x, B, L, z, 2, 1), x)
+    # weights on the grid: codes 0..15 spanning each group, scale 1/64, zero 8
+    for name in ("q", "down"):
+        on = dict(blk)
+        N, K = blk[name].shape
+        codes = rng.integers(0, 16, size=(N, K)).astype(np.float32)
+        codes[:, ::128], codes[:, 1::128] = 0.0, 15.0
+        on[name] = round_to_bf16_bits((codes - 8.0) * np.float32(1 / 64))
+        S1 = np.ones((2, K), np.float32)
+        d1, d0 = O.lookahead_losses(x, B, L, on, blk, 2, 1, name, S1, np.array([1.0, 0.6]))
+        assert d1[0] == 0.0 and d0[0] == 0.0 and d1[1] > 0 and d0[1] > 0, (name, d1, d0)
+    # scale rewrite: per-group powers of two keep the grid, so Q(W diag(s)) diag(1/s) = W
+    on = dict(blk)
+    N, K = blk["up"].shape
+    codes = rng.integers(0, 16, size=(N, K)).astype(np.float32)
+    codes[:, ::128], codes[:, 1::128] = 0.0, 15.0
+    on["up"] = round_to_bf16_bits((codes - 8.0) * np.float32(1 / 64))
+    sg = np.repeat(np.exp2(rng.integers(-2, 3, size=K // 128)).astype(np.float32), 128)
+    d1, d0 = O.lookahead_losses(x, B, L, on, blk, 2, 1, "up", sg[None, :], np.array([1.0]))
+    assert d1[0] == 0.0 and d0[0] == 0.0
+    nxt = _block(rng, H=H)
+    S2 = np.ones((2, H), np.float32)
+    e1, e0 = O.lookahead_losses(x, B, L, blk, None, 2, 1, "gate", S2, np.array([1.0, 0.5]))
+    assert np.array_equal(e1, e0)
+    f1, f0 = O.lookahead_losses(x, B, L, blk, nxt, 2, 1, "gate", S2, np.array([1.0, 0.5]))
+    assert np.array_equal(f0, e0) and f1[1] > f1[0] > 0
+
+
 ALL_CHECKS = [
+    check_rope_rotation, check_attention, check_rmsnorm_and_silu, check_block_and_lookahead,
     check_clip_channel_bruteforce, check_clip_channel_special_cases,
     check_w4a8_activation_codes, check_w4a8_linear_reduces_to_dequant_matmul,
     check_division_ties,

@@ -133,3 +133,40 @@ def per_channel_clip_losses(X_rows, W_rows, s, ratios, symmetric=False):
                 L[g][n][j] = tot
     best = [[min(range(len(ratios)), key=lambda j: (L[g][n][j], j)) for g in range(G)] for n in range(N)]
     return L, best
+
+
+def causal_attention(q, k, v, L, n_q, n_kv, hd=128):
+    """One sequence, pure Python: q [L][n_q*hd], k, v [L][n_kv*hd] (lists of floats).
+    Query head h reads key/value head h // (n_q // n_kv); token t attends to 0..t."""
+    rep = n_q // n_kv
+    out = [[0.0] * (n_q * hd) for _ in range(L)]
+    for t in range(L):
+        for h in range(n_q):
+            kv = h // rep
+            sc = []
+            for j in range(t + 1):
+                d = 0.0
+                for e in range(hd):
+                    d += q[t][h * hd + e] * k[j][kv * hd + e]
+                sc.append(d / math.sqrt(hd))
+            mx = max(sc)
+            ex = [math.exp(x - mx) for x in sc]
+            z = sum(ex)
+            for e in range(hd):
+                acc = 0.0
+                for j in range(t + 1):
+                    acc += ex[j] / z * v[j][kv * hd + e]
+                out[t][h * hd + e] = acc
+    return out
+
+
+def rotate_pairs(x, p, base=1e6, hd=128):
+    """Rotary embedding of one head vector x (list of hd floats) at position p."""
+    half = hd // 2
+    out = [0.0] * hd
+    for j in range(half):
+        a = p * base ** (-(2.0 * j) / hd)
+        c, s = math.cos(a), math.sin(a)
+        out[j] = x[j] * c - x[j + half] * s
+        out[j + half] = x[j + half] * c + x[j] * s
+    return out

@@ -66,6 +66,23 @@ MUTANTS = {
     "clip_loss_x_transposed_tokens": ("P = xs[:, sl] @ e[:, sl].T", "P = xs[::-1, sl][:, ::-1] @ e[:, sl].T"),
     "clip_best_last": ("best = np.argmin(L, axis=2).T", "best = (L.shape[2] - 1 - np.argmin(L[:, :, ::-1], axis=2)).T"),
     "clip_best_max": ("best = np.argmin(L, axis=2).T", "best = np.argmax(L, axis=2).T"),
+    "rope_sign": ("out = np.concatenate([x1 * c - x2 * s, x2 * c + x1 * s], axis=-1)",
+                  "out = np.concatenate([x1 * c + x2 * s, x2 * c + x1 * s], axis=-1)"),
+    "rope_adjacent_pairs": ("x1, x2 = xr[..., :64], xr[..., 64:]", "x1, x2 = xr[..., 0::2], xr[..., 1::2]"),
+    "rope_frequency": ("inv = base ** (-(2.0 * np.arange(HEAD_DIM // 2)) / HEAD_DIM)",
+                       "inv = base ** (-(1.0 * np.arange(HEAD_DIM // 2)) / HEAD_DIM)"),
+    "attention_sees_next_token": ("mask = np.triu(np.ones((L, L), dtype=bool), 1)",
+                                  "mask = np.triu(np.ones((L, L), dtype=bool), 2)"),
+    "attention_gqa_interleaved": ("            kv = h // rep\n            sc = qh", "            kv = h % n_kv\n            sc = qh"),
+    "attention_scale": ("sc = qh[b, :, h, :] @ kh[b, :, kv, :].T / np.sqrt(HEAD_DIM)",
+                        "sc = qh[b, :, h, :] @ kh[b, :, kv, :].T / HEAD_DIM"),
+    "rmsnorm_mean_abs": ("r = 1.0 / np.sqrt(np.mean(x * x, axis=1) + eps)", "r = 1.0 / np.sqrt(np.mean(np.abs(x), axis=1) + eps)"),
+    "silu_is_sigmoid": ("return _bf16_round(g / (1.0 + np.exp(-g)) * u)", "return _bf16_round(1.0 / (1.0 + np.exp(-g)) * u)"),
+    "block_no_attention_residual": ('h = _bf16_round(x + lin("o", o))', 'h = _bf16_round(lin("o", o))'),
+    "candidate_input_times_s": ("xs = bf16_to_f32(f32_to_bf16(a.astype(np.float32) / s32[None, :])).astype(np.float64)",
+                                "xs = bf16_to_f32(f32_to_bf16(a.astype(np.float32) * s32[None, :])).astype(np.float64)"),
+    "lookahead_next_on_input": ("yn = block_forward(yi, B, L, nxt, n_q, n_kv) if nxt is not None else yi",
+                                "yn = block_forward(x_bf16, B, L, nxt, n_q, n_kv) if nxt is not None else yi"),
     "clip_after_scale_choice": ("        absmax = np.abs(v).max(axis=2, keepdims=True)\n    if symmetric:",
                                 "    if symmetric:"),
 }

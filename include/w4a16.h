@@ -244,6 +244,65 @@ int awq_search(const uint16_t* X, int T, int K, int N, const uint16_t* W,
                void* stream);
 
 /*
+ * One decoder block's weights (all bf16, device pointers, [out][in] row-major):
+ * the base model's block ([AWQ-W4 card] "Base model": Qwen3-1.7B, hidden 2048;
+ * [q326 page] architecture notes: grouped-query attention, head size 128,
+ * rotary positions with base 10^6, SiLU-gated feed-forward).
+ *   norm1 [H], wq [128 n_q][H], wk [128 n_kv][H], wv [128 n_kv][H], wo [H][128 n_q],
+ *   norm2 [H], wgate [I][H], wup [I][H], wdown [H][I].
+ */
+typedef struct w4_block {
+  const uint16_t* norm1;
+  const uint16_t* wq;
+  const uint16_t* wk;
+  const uint16_t* wv;
+  const uint16_t* wo;
+  const uint16_t* norm2;
+  const uint16_t* wgate;
+  const uint16_t* wup;
+  const uint16_t* wdown;
+} w4_block;
+
+/*
+ * w4_block_forward -- Y = block(X) for B sequences of L tokens, X and Y [B L][H] bf16.
+ *   a = rmsnorm(x) * norm1 (eps 1e-6); q, k, v = a Wq^T, a Wk^T, a Wv^T; rotary
+ *   embedding of q and k on the pairs (j, j + 64) of each head at the token's
+ *   position in its sequence; o = causal softmax(q k^T / sqrt(128)) v per sequence,
+ *   query head h reading key/value head h / (n_q / n_kv); h1 = x + o Wo^T;
+ *   b = rmsnorm(h1) * norm2; y = h1 + (silu(b Wg^T) * (b Wu^T)) Wd^T.  No biases,
+ *   no per-head q/k norms.  Every op computes in fp32 and stores bf16 (nearest
+ *   even); the linears run on the matrix cores.
+ *   H and I multiples of 128; n_kv >= 1 divides n_q; B, L >= 1.
+ *   Workspace: size query as in w4a16_gemm (about 2 B L (5 H + 3 I + 2 128 n_q +
+ *   2 128 n_kv) bytes).
+ */
+int w4_block_forward(const uint16_t* X, int B, int L, int hidden, int n_q, int n_kv, int inter,
+                     const w4_block* blk, uint16_t* Y, void* workspace, size_t* workspace_bytes,
+                     void* stream);
+
+/*
+ * awq_lookahead_loss -- look-ahead (d = 1) scoring of C candidates for one linear of
+ * block `blk`.  [AWQ-W4 card] "Search" and the paragraph under it: the candidate
+ * weights go into this block, the MSE is taken at the output of the next block
+ * `next`, which runs unquantized; the reference is the same path with this block
+ * unquantized; with next == NULL (the last block) the loss is taken at this
+ * block's own output.  Candidate c replaces linear `linear` (0..6: q, k, v, o,
+ * gate, up, down) by its deployed form: input bf16(a / S[c]) against the int4
+ * codes Q(W diag(S[c]), ratios[c]) (awq_quantize_pack, symmetric or not).
+ *   losses[c] = mean over the B L tokens and H outputs of (y_c - y_ref)^2, both
+ *   bf16 outputs of the scored block, fp64 sum in a fixed order, stored fp32.
+ *   losses_d0[c] (or NULL) = the same at this block's output (d = 0).
+ *   X [B L][H] bf16: the input of this block.  S [C][K] fp32 device (K the
+ *   linear's input size), ratios [C] fp32 device in (0, 1].  Blocks as in
+ *   w4_block_forward.  Workspace: size query; it depends on the shape and on
+ *   `linear`.  Candidates run one after another on `stream`.
+ */
+int awq_lookahead_loss(const uint16_t* X, int B, int L, int hidden, int n_q, int n_kv, int inter,
+                       const w4_block* blk, const w4_block* next, int linear, const float* S,
+                       const float* ratios, int C, int symmetric, int group_size, float* losses,
+                       float* losses_d0, void* workspace, size_t* workspace_bytes, void* stream);
+
+/*
  * Measurement helpers (not part of the method): the yardsticks the kernels
  * above are measured against on the same device.
  *

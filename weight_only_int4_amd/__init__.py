@@ -20,8 +20,8 @@ import torch
 __all__ = [
     "W4Error", "library_path", "load_library", "awq_quantize_pack", "w4a16_gemv", "w4a16_gemm",
     "awq_grid_loss", "awq_search", "GROUP_SIZE", "GEMV_MAX_M", "gemv_launcher", "gemm_launcher",
-    "w4a8_quantize_activations", "w4a8_gemv", "w4a8_gemv_launcher", "awq_clip_search", "probe_stream_read",
-    "probe_empty",
+    "w4a8_quantize_activations", "w4a8_gemv", "w4a8_gemv_launcher", "awq_clip_search", "block_forward",
+    "awq_lookahead_loss", "BLOCK_LINEARS", "probe_stream_read", "probe_empty",
 ]
 
 GROUP_SIZE = 128
@@ -30,6 +30,17 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB = None
 
 _vp, _i, _f, _sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.POINTER(ctypes.c_size_t)
+
+BLOCK_LINEARS = ("q", "k", "v", "o", "gate", "up", "down")
+_BLOCK_FIELDS = ("norm1", "wq", "wk", "wv", "wo", "norm2", "wgate", "wup", "wdown")
+
+
+class _Block(ctypes.Structure):
+    """struct w4_block: device pointers of one decoder block's bf16 weights."""
+    _fields_ = [(f, ctypes.c_void_p) for f in _BLOCK_FIELDS]
+
+
+_bp = ctypes.POINTER(_Block)
 _SIGNATURES = {
     "w4_status_string": ([_i], ctypes.c_char_p),
     "awq_quantize_pack": ([_vp, _i, _i, _vp, _f, _i, _i, _vp, _vp, _vp, _vp], _i),
@@ -41,6 +52,9 @@ _SIGNATURES = {
     "w4a8_quantize_activations": ([_vp, _i, _i, _vp, _vp, _vp, _vp], _i),
     "w4a8_gemv": ([_vp, _vp, _vp, _i, _i, _i, _vp, _vp, _vp, _i, _i, _vp, _vp], _i),
     "awq_clip_search": ([_vp, _i, _i, _i, _vp, _vp, _vp, _i, _i, _i, _vp, _vp, _vp, _sz, _vp], _i),
+    "w4_block_forward": ([_vp, _i, _i, _i, _i, _i, _i, _bp, _vp, _vp, _sz, _vp], _i),
+    "awq_lookahead_loss": ([_vp, _i, _i, _i, _i, _i, _i, _bp, _bp, _i, _vp, _vp, _i, _i, _i, _vp, _vp, _vp, _sz, _vp],
+                           _i),
     "awq_search": ([_vp, _i, _i, _i, _vp, ctypes.POINTER(ctypes.c_double), _i,
                     ctypes.POINTER(ctypes.c_double), _i, _i, _i, ctypes.POINTER(ctypes.c_float),
                     ctypes.POINTER(ctypes.c_int), ctypes.POINTER(ctypes.c_int), _vp, _vp, _sz, _vp], _i),
@@ -306,6 +320,71 @@ def awq_clip_search(X, W, ratios, s=None, symmetric: bool = False, want_losses: 
                                _ptr(losses) if want_losses else None, _ptr(best), _ptr(ws),
                                None if wsb is None else ctypes.byref(wsb), _stream(dev)))
     return (losses if want_losses else None), best
+
+
+def _block_struct(blk, H, n_q, n_kv, I):
+    """blk: dict with "norm1", "norm2" (bf16 [H]) and q, k, v, o, gate, up, down (bf16 [out][in])."""
+    shapes = {"norm1": (H,), "norm2": (H,), "q": (128 * n_q, H), "k": (128 * n_kv, H), "v": (128 * n_kv, H),
+              "o": (H, 128 * n_q), "gate": (I, H), "up": (I, H), "down": (H, I)}
+    for name, shape in shapes.items():
+        _need(blk[name], torch.bfloat16, name)
+        if tuple(blk[name].shape) != shape:
+            raise ValueError(f"{name} must have shape {shape}, got {tuple(blk[name].shape)}")
+    keys = ("norm1", "q", "k", "v", "o", "norm2", "gate", "up", "down")
+    return _Block(*[blk[k].data_ptr() for k in keys])
+
+
+def block_forward(X, B: int, L: int, blk, n_q: int, n_kv: int, Y=None, workspace=None):
+    """Y [B L][H] bf16 = decoder block(X) (see include/w4a16.h, w4_block_forward)."""
+    lib = load_library()
+    _need(X, torch.bfloat16, "X", 2)
+    T, H = X.shape
+    if T != B * L:
+        raise ValueError("X must have B * L rows")
+    I = blk["gate"].shape[0]
+    b = _block_struct(blk, H, n_q, n_kv, I)
+    if Y is None:
+        Y = torch.empty_like(X)
+
+    def q(sz):
+        return lib.w4_block_forward(None, B, L, H, n_q, n_kv, I, None, None, None, sz, None)
+
+    ws, wsb = _workspace(q, X.device, workspace)
+    _check(lib.w4_block_forward(_ptr(X), B, L, H, n_q, n_kv, I, ctypes.byref(b), _ptr(Y), _ptr(ws),
+                                None if wsb is None else ctypes.byref(wsb), _stream(X.device)))
+    return Y
+
+
+def awq_lookahead_loss(X, B: int, L: int, blk, nxt, n_q: int, n_kv: int, linear, S, ratios,
+                       symmetric: bool = False, want_d0: bool = True, workspace=None):
+    """Look-ahead (d = 1) losses [C] of candidates (S[c], ratios[c]) for one linear of
+    block blk scored after block nxt (None: the last block, scored at its own output),
+    and the block-output (d = 0) losses [C] (or None)."""
+    lib = load_library()
+    _need(X, torch.bfloat16, "X", 2)
+    _need(S, torch.float32, "S", 2)
+    _need(ratios, torch.float32, "ratios", 1)
+    T, H = X.shape
+    if T != B * L:
+        raise ValueError("X must have B * L rows")
+    I = blk["gate"].shape[0]
+    li = BLOCK_LINEARS.index(linear) if isinstance(linear, str) else int(linear)
+    b = _block_struct(blk, H, n_q, n_kv, I)
+    nb = None if nxt is None else _block_struct(nxt, H, n_q, n_kv, I)
+    C = S.shape[0]
+    losses = torch.empty(C, dtype=torch.float32, device=X.device)
+    d0 = torch.empty(C, dtype=torch.float32, device=X.device) if want_d0 else None
+
+    def q(sz):
+        return lib.awq_lookahead_loss(None, B, L, H, n_q, n_kv, I, None, None, li, None, None, C, int(symmetric),
+                                      GROUP_SIZE, None, None, None, sz, None)
+
+    ws, wsb = _workspace(q, X.device, workspace)
+    _check(lib.awq_lookahead_loss(_ptr(X), B, L, H, n_q, n_kv, I, ctypes.byref(b),
+                                  None if nb is None else ctypes.byref(nb), li, _ptr(S), _ptr(ratios), C,
+                                  int(symmetric), GROUP_SIZE, _ptr(losses), _ptr(d0), _ptr(ws),
+                                  None if wsb is None else ctypes.byref(wsb), _stream(X.device)))
+    return losses, d0
 
 
 def awq_search(X, W, alphas, ratios, symmetric: bool = False, workspace=None):

@@ -1,0 +1,533 @@
+// Look-ahead block scoring, model card "rebuttal_w4g128_awq_w2", details table row
+// "Search" and the paragraph under it: a candidate for a linear of block i is scored
+// at the output of block i + 1, which runs unquantized; the reference runs block i
+// unquantized too; the last block is scored at its own output.  The block is the
+// base model's decoder block (same card, "Base model": Qwen3-1.7B, hidden 2048;
+// model page "qwen3-1.7b_q326_channel", architecture notes: grouped-query attention
+// with 16 query heads over 8 key/value heads of size 128, rotary positions with base
+// 10^6, SiLU-gated feed-forward of width 6144).
+//
+// Readings fixed here: pre-norm RMSNorm (eps 1e-6) before attention and before the
+// feed-forward, residual adds after each, no biases and no per-head q/k norms;
+// rotary embedding on the pairs (j, j + 64) of each head at the token's position in
+// its sequence; causal attention within each of B sequences of L tokens, scale
+// 1/sqrt(128), query head h reading key/value head h / (n_q / n_kv); every op output
+// is stored in bf16 (round to nearest even) and computed in fp32.
+//
+// Block forward, all on the caller's stream:
+//   a = rmsnorm(x, g1); q, k, v = a Wq^T, a Wk^T, a Wv^T; q, k = rope(q), rope(k);
+//   o = attention(q, k, v); h = x + o Wo^T; b = rmsnorm(h, g2);
+//   m = silu(b Wg^T) * (b Wu^T); y = h + m Wd^T.
+// The linears run on the MFMA core with bf16 weights; a candidate linear runs as
+// deployed: bf16(input / s) against its int4 codes Q(W diag(s), r) on the int4 GEMM.
+#include <math.h>
+
+#include <algorithm>
+
+#include "internal.hpp"
+
+#pragma clang fp contract(off)
+
+namespace w4 {
+
+namespace {
+
+constexpr int kHd = 128;              // head size
+constexpr float kEps = 1e-6f;
+constexpr double kRopeBase = 1e6;
+
+// ---------------------------------------------------------------------------------------
+// y = bf16((x * r) * g), r = 1 / sqrt(mean(x^2) + eps): one wave per row, fp32 sums in a
+// fixed order (lane-strided, then a butterfly).
+__global__ __launch_bounds__(256) void rmsnorm_kernel(const uint16_t* __restrict__ X, int T, int H,
+                                                      const uint16_t* __restrict__ g, uint16_t* __restrict__ Y) {
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (row >= T) return;
+  const uint16_t* x = X + (size_t)row * H;
+  float ss = 0.0f;
+  for (int c = lane * 8; c < H; c += 512) {
+    const uint4 v = *reinterpret_cast<const uint4*>(x + c);
+    const uint32_t d[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const float a = __uint_as_float(d[q] << 16), b = __uint_as_float(d[q] & 0xFFFF0000u);
+      ss = ss + a * a;
+      ss = ss + b * b;
+    }
+  }
+  ss = wave_sum(ss);
+  const float r = 1.0f / sqrtf(ss / (float)H + kEps);
+  for (int c = lane * 8; c < H; c += 512) {
+    const uint4 v = *reinterpret_cast<const uint4*>(x + c);
+    const uint4 gv = *reinterpret_cast<const uint4*>(g + c);
+    const uint32_t d[4] = {v.x, v.y, v.z, v.w};
+    const uint32_t e[4] = {gv.x, gv.y, gv.z, gv.w};
+    uint32_t o[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const float lo = (__uint_as_float(d[q] << 16) * r) * __uint_as_float(e[q] << 16);
+      const float hi = (__uint_as_float(d[q] & 0xFFFF0000u) * r) * __uint_as_float(e[q] & 0xFFFF0000u);
+      o[q] = f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
+    }
+    *reinterpret_cast<uint4*>(Y + (size_t)row * H + c) = make_uint4(o[0], o[1], o[2], o[3]);
+  }
+}
+
+// cos / sin [L][64] of p * base^(-2j/128), in fp64, stored fp32.
+__global__ __launch_bounds__(256) void rope_table_kernel(int L, float* cs, float* sn) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i >= L * 64) return;
+  const int p = i >> 6, j = i & 63;
+  const double ang = (double)p * pow(kRopeBase, -(2.0 * j) / kHd);
+  cs[i] = (float)cos(ang);
+  sn[i] = (float)sin(ang);
+}
+
+// In place on x [T][nh * 128] (T = B L, token t at position t % L): per head, pair
+// (j, j + 64) -> (x1 c - x2 s, x2 c + x1 s), bf16.  One thread per (token, head, j).
+__global__ __launch_bounds__(256) void rope_kernel(uint16_t* __restrict__ x, long long items, int nh, int L,
+                                                   const float* __restrict__ cs, const float* __restrict__ sn) {
+  const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (i >= items) return;
+  const int j = (int)(i & 63);
+  const long long th = i >> 6;                 // token * nh + head
+  const int t = (int)(th / nh);
+  const int p = t % L;
+  uint16_t* base = x + th * kHd;
+  const float x1 = bf16_bits_to_f32(base[j]), x2 = bf16_bits_to_f32(base[j + 64]);
+  const float c = cs[p * 64 + j], s = sn[p * 64 + j];
+  base[j] = (uint16_t)f32_to_bf16_bits(x1 * c - x2 * s);
+  base[j + 64] = (uint16_t)f32_to_bf16_bits(x2 * c + x1 * s);
+}
+
+// Causal grouped-query attention.  Workgroup (query block of 64, query head, sequence),
+// 256 threads: 4 lanes per query, lane part u owns dims 32 u .. 32 u + 31 of q and of
+// the output.  Keys and values of the query head's key/value head go through LDS in
+// chunks of 32 keys (fp32; part u of a key at float offset 36 u, so the four parts'
+// 16-byte reads fall in different banks); each query keeps an online softmax
+// (running max and sum) in fp32.
+constexpr int kAttnQ = 64, kAttnK = 32, kAttnRow = 4 * 36;
+__global__ __launch_bounds__(256) void attention_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ Kx,
+                                                        const uint16_t* __restrict__ V, int L, int n_q, int n_kv,
+                                                        uint16_t* __restrict__ O) {
+  __shared__ __align__(16) float ks[kAttnK * kAttnRow];
+  __shared__ __align__(16) float vs[kAttnK * kAttnRow];
+  const int qb = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int kvh = h / (n_q / n_kv);
+  const int tid = threadIdx.x;
+  const int qi = tid >> 2, u = tid & 3;
+  const int t = qb * kAttnQ + qi;                    // query position in the sequence
+  const bool live = t < L;
+  const size_t qstride = (size_t)n_q * kHd, kstride = (size_t)n_kv * kHd;
+  const size_t tok0 = (size_t)b * L;
+  float q[32], o[32];
+  {
+    const uint16_t* qp = Q + (tok0 + (live ? t : 0)) * qstride + (size_t)h * kHd + 32 * u;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const uint4 v = *reinterpret_cast<const uint4*>(qp + 8 * c);
+      const uint32_t d[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        q[8 * c + 2 * e] = __uint_as_float(d[e] << 16);
+        q[8 * c + 2 * e + 1] = __uint_as_float(d[e] & 0xFFFF0000u);
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < 32; ++e) o[e] = 0.0f;
+  }
+  const float scale = 1.0f / sqrtf((float)kHd);
+  float mx = -INFINITY, sum = 0.0f;
+  const int kend = min(L, (qb + 1) * kAttnQ);        // keys this block needs: 0 .. kend-1
+  for (int k0 = 0; k0 < kend; k0 += kAttnK) {
+    __syncthreads();
+    // stage 32 keys x 128 dims of k and v: thread -> (key tid / 8, 16 dims at 16 (tid % 8))
+    {
+      const int kj = tid >> 3, part = tid & 7;
+      const int key = k0 + kj;
+      const bool ok = key < kend;
+      const size_t src = (tok0 + (ok ? key : 0)) * kstride + (size_t)kvh * kHd + 16 * part;
+      float* kd = &ks[kj * kAttnRow + 36 * (part >> 1) + 16 * (part & 1)];
+      float* vd = &vs[kj * kAttnRow + 36 * (part >> 1) + 16 * (part & 1)];
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        const uint4 kv4 = *reinterpret_cast<const uint4*>(Kx + src + 8 * c);
+        const uint4 vv4 = *reinterpret_cast<const uint4*>(V + src + 8 * c);
+        const uint32_t dk[4] = {kv4.x, kv4.y, kv4.z, kv4.w};
+        const uint32_t dv[4] = {vv4.x, vv4.y, vv4.z, vv4.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          kd[8 * c + 2 * e] = __uint_as_float(dk[e] << 16);
+          kd[8 * c + 2 * e + 1] = __uint_as_float(dk[e] & 0xFFFF0000u);
+          vd[8 * c + 2 * e] = __uint_as_float(dv[e] << 16);
+          vd[8 * c + 2 * e + 1] = __uint_as_float(dv[e] & 0xFFFF0000u);
+        }
+      }
+    }
+    __syncthreads();
+    const int nk = min(kAttnK, kend - k0);
+    for (int kj = 0; kj < nk; ++kj) {
+      const int key = k0 + kj;
+      const float* kr = &ks[kj * kAttnRow + 36 * u];
+      float d = 0.0f;
+#pragma unroll
+      for (int e = 0; e < 32; ++e) d = fmaf(q[e], kr[e], d);
+      // the 4 parts of a query sit in consecutive lanes: (0+1) + (2+3), the same in all four
+      d = d + __shfl_xor(d, 1, kWave);
+      d = d + __shfl_xor(d, 2, kWave);
+      if (!live || key > t) continue;                // causal: keys after the query are skipped
+      const float sc = d * scale;
+      const float mnew = fmaxf(mx, sc);
+      const float corr = expf(mx - mnew);            // 0 for the first key (mx = -inf)
+      const float p = expf(sc - mnew);
+      sum = sum * corr + p;
+      const float* vr = &vs[kj * kAttnRow + 36 * u];
+#pragma unroll
+      for (int e = 0; e < 32; ++e) o[e] = fmaf(p, vr[e], o[e] * corr);
+      mx = mnew;
+    }
+  }
+  if (!live) return;
+  const float inv = 1.0f / sum;
+  uint16_t* op = O + (tok0 + t) * qstride + (size_t)h * kHd + 32 * u;
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    uint32_t w[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      w[e] = f32_to_bf16_bits(o[8 * c + 2 * e] * inv) | (f32_to_bf16_bits(o[8 * c + 2 * e + 1] * inv) << 16);
+    *reinterpret_cast<uint4*>(op + 8 * c) = make_uint4(w[0], w[1], w[2], w[3]);
+  }
+}
+
+// Elementwise over n bf16 values (n % 8 == 0), 8 per thread.
+enum { EW_ADD = 0, EW_SILU_MUL = 1 };
+template <int OP>
+__global__ __launch_bounds__(256) void elementwise_kernel(const uint16_t* __restrict__ A, const uint16_t* __restrict__ B,
+                                                          size_t n, uint16_t* __restrict__ Y) {
+  const size_t i = ((size_t)blockIdx.x * 256 + threadIdx.x) * 8;
+  if (i >= n) return;
+  const uint4 av = *reinterpret_cast<const uint4*>(A + i);
+  const uint4 bv = *reinterpret_cast<const uint4*>(B + i);
+  const uint32_t a[4] = {av.x, av.y, av.z, av.w};
+  const uint32_t b[4] = {bv.x, bv.y, bv.z, bv.w};
+  uint32_t o[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    float r[2];
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const float x = e ? __uint_as_float(a[q] & 0xFFFF0000u) : __uint_as_float(a[q] << 16);
+      const float y = e ? __uint_as_float(b[q] & 0xFFFF0000u) : __uint_as_float(b[q] << 16);
+      r[e] = OP == EW_ADD ? x + y : x / (1.0f + expf(-x)) * y;
+    }
+    o[q] = f32_to_bf16_bits(r[0]) | (f32_to_bf16_bits(r[1]) << 16);
+  }
+  *reinterpret_cast<uint4*>(Y + i) = make_uint4(o[0], o[1], o[2], o[3]);
+}
+
+// Y[t][k] = bf16(X[t][k] / s[k]) (IEEE division), 8 per thread, K % 8 == 0.
+__global__ __launch_bounds__(256) void divide_columns_kernel(const uint16_t* __restrict__ X, size_t n, int K,
+                                                             const float* __restrict__ s, uint16_t* __restrict__ Y) {
+  const size_t i = ((size_t)blockIdx.x * 256 + threadIdx.x) * 8;
+  if (i >= n) return;
+  const int k0 = (int)(i % (size_t)K);
+  const uint4 v = *reinterpret_cast<const uint4*>(X + i);
+  const uint32_t d[4] = {v.x, v.y, v.z, v.w};
+  uint32_t o[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const float lo = __uint_as_float(d[q] << 16) / s[k0 + 2 * q];
+    const float hi = __uint_as_float(d[q] & 0xFFFF0000u) / s[k0 + 2 * q + 1];
+    o[q] = f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
+  }
+  *reinterpret_cast<uint4*>(Y + i) = make_uint4(o[0], o[1], o[2], o[3]);
+}
+
+// part[blk] = sum over this block's elements of (a - b)^2 in fp64 (fixed order);
+// 2048 elements per 256-thread block.
+__global__ __launch_bounds__(256) void sqdiff_partial_kernel(const uint16_t* __restrict__ A,
+                                                             const uint16_t* __restrict__ B, size_t n,
+                                                             double* __restrict__ part) {
+  __shared__ double red[256];
+  const size_t i = ((size_t)blockIdx.x * 256 + threadIdx.x) * 8;
+  double s = 0.0;
+  if (i < n) {
+    const uint4 av = *reinterpret_cast<const uint4*>(A + i);
+    const uint4 bv = *reinterpret_cast<const uint4*>(B + i);
+    const uint32_t a[4] = {av.x, av.y, av.z, av.w};
+    const uint32_t b[4] = {bv.x, bv.y, bv.z, bv.w};
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const double d0 = (double)__uint_as_float(a[q] << 16) - (double)__uint_as_float(b[q] << 16);
+      const double d1 = (double)__uint_as_float(a[q] & 0xFFFF0000u) - (double)__uint_as_float(b[q] & 0xFFFF0000u);
+      s += d0 * d0;
+      s += d1 * d1;
+    }
+  }
+  red[threadIdx.x] = s;
+  __syncthreads();
+  for (int w = 128; w > 0; w >>= 1) {
+    if ((int)threadIdx.x < w) red[threadIdx.x] += red[threadIdx.x + w];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) part[blockIdx.x] = red[0];
+}
+
+// out[0] = sum of part[0 .. nparts) (fp64, lane-strided then butterfly) / count.
+__global__ __launch_bounds__(64) void mean_finish_kernel(const double* __restrict__ part, long long nparts,
+                                                         double count, float* __restrict__ out) {
+  double s = 0.0;
+  for (long long i = threadIdx.x; i < nparts; i += 64) s += part[i];
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) s += __shfl_xor(s, off, 64);
+  if (threadIdx.x == 0) out[0] = (float)(s / count);
+}
+
+// ---------------------------------------------------------------------------------------
+// host side
+
+struct Dims {
+  int B, L, T, H, nq, nkv, I, QD, KD;      // T = B L, QD = 128 nq, KD = 128 nkv
+};
+
+// (K, N) of linear i: q k v o gate up down
+inline void linear_shape(const Dims& d, int i, int& K, int& N) {
+  static const int kin[7] = {0, 0, 0, 1, 0, 0, 2};  // 0: H, 1: QD, 2: I
+  const int in = kin[i];
+  K = in == 0 ? d.H : in == 1 ? d.QD : d.I;
+  N = i == 0 ? d.QD : (i == 1 || i == 2) ? d.KD : (i == 3 || i == 6) ? d.H : d.I;
+}
+
+struct BlockLayout {
+  size_t a, q, k, v, o, p, h, b2, gt, up, m, dn;      // per-op outputs
+  size_t cs, sn;                                      // rope tables
+  size_t total;
+};
+
+BlockLayout block_layout(const Dims& d, size_t& off) {
+  BlockLayout l{};
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off = align_up(off + bytes, 256);
+    return o;
+  };
+  const size_t T = (size_t)d.T;
+  l.a = take(T * d.H * 2);
+  l.q = take(T * d.QD * 2);
+  l.k = take(T * d.KD * 2);
+  l.v = take(T * d.KD * 2);
+  l.o = take(T * d.QD * 2);
+  l.p = take(T * d.H * 2);
+  l.h = take(T * d.H * 2);
+  l.b2 = take(T * d.H * 2);
+  l.gt = take(T * d.I * 2);
+  l.up = take(T * d.I * 2);
+  l.m = take(T * d.I * 2);
+  l.dn = take(T * d.H * 2);
+  l.cs = take((size_t)d.L * 64 * 4);
+  l.sn = take((size_t)d.L * 64 * 4);
+  l.total = off;
+  return l;
+}
+
+// The deployed int4 form of one linear: codes, scales, zeros and the scaled input.
+struct Candidate {
+  int linear;
+  const float* s;               // [K]
+  const uint32_t* qweight;
+  const uint16_t* scales;
+  const uint32_t* qzeros;       // NULL when symmetric
+  int symmetric;
+  uint16_t* xs;                 // [T][K] scratch for bf16(input / s)
+  void* gemm_ws;                // launch_gemm workspace
+};
+
+int ew_launch(int op, const uint16_t* A, const uint16_t* B, size_t n, uint16_t* Y, hipStream_t st) {
+  const size_t blocks = (n / 8 + 255) / 256;
+  if (op == EW_ADD)
+    hipLaunchKernelGGL(elementwise_kernel<EW_ADD>, dim3((unsigned)blocks), dim3(256), 0, st, A, B, n, Y);
+  else
+    hipLaunchKernelGGL(elementwise_kernel<EW_SILU_MUL>, dim3((unsigned)blocks), dim3(256), 0, st, A, B, n, Y);
+  W4_CHECK_LAUNCH();
+  return W4_OK;
+}
+
+// One linear: Y [T][N] = bf16(X W^T), or the candidate's deployed int4 form.
+int run_linear(const Dims& d, int i, const uint16_t* X, const uint16_t* W, const Candidate* cand, uint16_t* Y,
+               hipStream_t st) {
+  int K, N;
+  linear_shape(d, i, K, N);
+  if (cand && cand->linear == i) {
+    const size_t n = (size_t)d.T * K;
+    hipLaunchKernelGGL(divide_columns_kernel, dim3((unsigned)((n / 8 + 255) / 256)), dim3(256), 0, st, X, n, K,
+                       cand->s, cand->xs);
+    W4_CHECK_LAUNCH();
+    return launch_gemm(cand->xs, d.T, K, N, cand->qweight, cand->scales, cand->qzeros, cand->symmetric, Y,
+                       cand->gemm_ws, st);
+  }
+  return launch_reference_gemm(X, d.T, K, N, W, Y, st);
+}
+
+int run_block(const Dims& d, const w4_block& blk, const uint16_t* X, uint16_t* Y, const Candidate* cand,
+              char* ws, const BlockLayout& l, hipStream_t st) {
+  auto buf = [&](size_t off) { return reinterpret_cast<uint16_t*>(ws + off); };
+  const size_t T = (size_t)d.T;
+  const unsigned nrow = (unsigned)((d.T + 3) / 4);
+  int rc;
+  hipLaunchKernelGGL(rmsnorm_kernel, dim3(nrow), dim3(256), 0, st, X, d.T, d.H, blk.norm1, buf(l.a));
+  W4_CHECK_LAUNCH();
+  if ((rc = run_linear(d, 0, buf(l.a), blk.wq, cand, buf(l.q), st))) return rc;
+  if ((rc = run_linear(d, 1, buf(l.a), blk.wk, cand, buf(l.k), st))) return rc;
+  if ((rc = run_linear(d, 2, buf(l.a), blk.wv, cand, buf(l.v), st))) return rc;
+  const float* cs = reinterpret_cast<const float*>(ws + l.cs);
+  const float* sn = reinterpret_cast<const float*>(ws + l.sn);
+  const long long qi = (long long)T * d.nq * 64, ki = (long long)T * d.nkv * 64;
+  hipLaunchKernelGGL(rope_kernel, dim3((unsigned)((qi + 255) / 256)), dim3(256), 0, st, buf(l.q), qi, d.nq, d.L, cs, sn);
+  W4_CHECK_LAUNCH();
+  hipLaunchKernelGGL(rope_kernel, dim3((unsigned)((ki + 255) / 256)), dim3(256), 0, st, buf(l.k), ki, d.nkv, d.L, cs, sn);
+  W4_CHECK_LAUNCH();
+  hipLaunchKernelGGL(attention_kernel, dim3((unsigned)((d.L + kAttnQ - 1) / kAttnQ), (unsigned)d.nq, (unsigned)d.B),
+                     dim3(256), 0, st, buf(l.q), buf(l.k), buf(l.v), d.L, d.nq, d.nkv, buf(l.o));
+  W4_CHECK_LAUNCH();
+  if ((rc = run_linear(d, 3, buf(l.o), blk.wo, cand, buf(l.p), st))) return rc;
+  if ((rc = ew_launch(EW_ADD, X, buf(l.p), T * d.H, buf(l.h), st))) return rc;
+  hipLaunchKernelGGL(rmsnorm_kernel, dim3(nrow), dim3(256), 0, st, buf(l.h), d.T, d.H, blk.norm2, buf(l.b2));
+  W4_CHECK_LAUNCH();
+  if ((rc = run_linear(d, 4, buf(l.b2), blk.wgate, cand, buf(l.gt), st))) return rc;
+  if ((rc = run_linear(d, 5, buf(l.b2), blk.wup, cand, buf(l.up), st))) return rc;
+  if ((rc = ew_launch(EW_SILU_MUL, buf(l.gt), buf(l.up), T * d.I, buf(l.m), st))) return rc;
+  if ((rc = run_linear(d, 6, buf(l.m), blk.wdown, cand, buf(l.dn), st))) return rc;
+  return ew_launch(EW_ADD, buf(l.h), buf(l.dn), T * d.H, Y, st);
+}
+
+int rope_tables(const Dims& d, char* ws, const BlockLayout& l, hipStream_t st) {
+  hipLaunchKernelGGL(rope_table_kernel, dim3((unsigned)((d.L * 64 + 255) / 256)), dim3(256), 0, st, d.L,
+                     reinterpret_cast<float*>(ws + l.cs), reinterpret_cast<float*>(ws + l.sn));
+  W4_CHECK_LAUNCH();
+  return W4_OK;
+}
+
+Dims make_dims(int B, int L, int H, int nq, int nkv, int I) {
+  Dims d{};
+  d.B = B;
+  d.L = L;
+  d.T = B * L;
+  d.H = H;
+  d.nq = nq;
+  d.nkv = nkv;
+  d.I = I;
+  d.QD = nq * kHd;
+  d.KD = nkv * kHd;
+  return d;
+}
+
+struct LookLayout {
+  BlockLayout blk;
+  size_t yref_i, yref_n, yc_i, yc_n, xs, qw, sc, qz, gemm, part, total;
+  size_t nparts;
+};
+
+LookLayout look_layout(const Dims& d, int linear) {
+  LookLayout l{};
+  size_t off = 0;
+  l.blk = block_layout(d, off);
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off = align_up(off + bytes, 256);
+    return o;
+  };
+  int K, N;
+  linear_shape(d, linear, K, N);
+  const size_t T = (size_t)d.T;
+  l.yref_i = take(T * d.H * 2);
+  l.yref_n = take(T * d.H * 2);
+  l.yc_i = take(T * d.H * 2);
+  l.yc_n = take(T * d.H * 2);
+  l.xs = take(T * K * 2);
+  l.qw = take((size_t)N * (K / 8) * 4);
+  l.sc = take((size_t)N * (K / kGroup) * 2);
+  l.qz = take((size_t)N * ((K / kGroup + 7) / 8) * 4);
+  l.gemm = take(gemm_workspace_bytes(d.T, K, N));
+  l.nparts = (T * d.H + 2047) / 2048;
+  l.part = take(l.nparts * 8);
+  l.total = off;
+  return l;
+}
+
+}  // namespace
+
+size_t block_forward_workspace_bytes(int B, int L, int H, int nq, int nkv, int I) {
+  size_t off = 0;
+  return block_layout(make_dims(B, L, H, nq, nkv, I), off).total;
+}
+
+int launch_block_forward(const uint16_t* X, int B, int L, int H, int nq, int nkv, int I, const w4_block& blk,
+                         uint16_t* Y, void* workspace, hipStream_t stream) {
+  const Dims d = make_dims(B, L, H, nq, nkv, I);
+  size_t off = 0;
+  const BlockLayout l = block_layout(d, off);
+  char* ws = static_cast<char*>(workspace);
+  int rc = rope_tables(d, ws, l, stream);
+  if (rc) return rc;
+  return run_block(d, blk, X, Y, nullptr, ws, l, stream);
+}
+
+size_t lookahead_workspace_bytes(int B, int L, int H, int nq, int nkv, int I, int linear) {
+  return look_layout(make_dims(B, L, H, nq, nkv, I), linear).total;
+}
+
+int launch_lookahead_loss(const uint16_t* X, int B, int L, int H, int nq, int nkv, int I, const w4_block& blk,
+                          const w4_block* next, int linear, const float* S, const float* ratios, int C,
+                          int symmetric, float* losses, float* losses_d0, void* workspace, hipStream_t stream) {
+  const Dims d = make_dims(B, L, H, nq, nkv, I);
+  const LookLayout l = look_layout(d, linear);
+  char* ws = static_cast<char*>(workspace);
+  auto buf = [&](size_t off) { return reinterpret_cast<uint16_t*>(ws + off); };
+  int rc = rope_tables(d, ws, l.blk, stream);
+  if (rc) return rc;
+  // reference path
+  if ((rc = run_block(d, blk, X, buf(l.yref_i), nullptr, ws, l.blk, stream))) return rc;
+  if (next && (rc = run_block(d, *next, buf(l.yref_i), buf(l.yref_n), nullptr, ws, l.blk, stream))) return rc;
+  const uint16_t* ref_n = next ? buf(l.yref_n) : buf(l.yref_i);
+  int K, N;
+  linear_shape(d, linear, K, N);
+  const uint16_t* Wl[7] = {blk.wq, blk.wk, blk.wv, blk.wo, blk.wgate, blk.wup, blk.wdown};
+  double* part = reinterpret_cast<double*>(ws + l.part);
+  const size_t n = (size_t)d.T * d.H;
+  const unsigned pblocks = (unsigned)l.nparts;
+  for (int c = 0; c < C; ++c) {
+    QuantArgs q{};
+    q.W = Wl[linear];
+    q.N = N;
+    q.K = K;
+    q.s = S + (size_t)c * K;
+    q.ratios = ratios + c;
+    q.symmetric = symmetric;
+    q.qweight = reinterpret_cast<uint32_t*>(ws + l.qw);
+    q.scales = buf(l.sc);
+    q.qzeros = symmetric ? nullptr : reinterpret_cast<uint32_t*>(ws + l.qz);
+    if ((rc = launch_quantize_pack(q, 1, stream))) return rc;
+    Candidate cand{linear, S + (size_t)c * K, q.qweight, q.scales, q.qzeros, symmetric, buf(l.xs), ws + l.gemm};
+    if ((rc = run_block(d, blk, X, buf(l.yc_i), &cand, ws, l.blk, stream))) return rc;
+    if (next && (rc = run_block(d, *next, buf(l.yc_i), buf(l.yc_n), nullptr, ws, l.blk, stream))) return rc;
+    const uint16_t* yc_n = next ? buf(l.yc_n) : buf(l.yc_i);
+    hipLaunchKernelGGL(sqdiff_partial_kernel, dim3(pblocks), dim3(256), 0, stream, yc_n, ref_n, n, part);
+    W4_CHECK_LAUNCH();
+    hipLaunchKernelGGL(mean_finish_kernel, dim3(1), dim3(64), 0, stream, part, (long long)l.nparts, (double)n,
+                       losses + c);
+    W4_CHECK_LAUNCH();
+    if (losses_d0) {
+      hipLaunchKernelGGL(sqdiff_partial_kernel, dim3(pblocks), dim3(256), 0, stream, buf(l.yc_i), buf(l.yref_i), n,
+                         part);
+      W4_CHECK_LAUNCH();
+      hipLaunchKernelGGL(mean_finish_kernel, dim3(1), dim3(64), 0, stream, part, (long long)l.nparts, (double)n,
+                         losses_d0 + c);
+      W4_CHECK_LAUNCH();
+    }
+  }
+  return W4_OK;
+}
+
+}  // namespace w4

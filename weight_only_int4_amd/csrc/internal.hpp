@@ -59,6 +59,15 @@ int launch_clip_search(const uint16_t* X, int T, int K, int N, const uint16_t* W
                        const float* ratios, int R, int symmetric, float* losses, uint8_t* best,
                        void* workspace, hipStream_t stream);
 
+// ---------------------------------------------------------------- decoder block / look-ahead loss
+size_t block_forward_workspace_bytes(int B, int L, int H, int nq, int nkv, int I);
+int launch_block_forward(const uint16_t* X, int B, int L, int H, int nq, int nkv, int I, const w4_block& blk,
+                         uint16_t* Y, void* workspace, hipStream_t stream);
+size_t lookahead_workspace_bytes(int B, int L, int H, int nq, int nkv, int I, int linear);
+int launch_lookahead_loss(const uint16_t* X, int B, int L, int H, int nq, int nkv, int I, const w4_block& blk,
+                          const w4_block* next, int linear, const float* S, const float* ratios, int C,
+                          int symmetric, float* losses, float* losses_d0, void* workspace, hipStream_t stream);
+
 // Y = bf16(X W^T) with bf16 weights W [N][K] (the unquantized reference output).
 int launch_reference_gemm(const uint16_t* X, int M, int K, int N, const uint16_t* W, uint16_t* Y,
                           hipStream_t stream);

@@ -4,6 +4,7 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <algorithm>
 #include <vector>
 
 #include "internal.hpp"
@@ -181,6 +182,65 @@ int awq_clip_search(const uint16_t* X, int T, int K, int N, const uint16_t* W, c
   if (misaligned(X) || misaligned(W) || misaligned(s) || misaligned(workspace)) return W4_ERR_ALIGN;
   return launch_clip_search(X, T, K, N, W, s, ratios, R, symmetric, losses, best, workspace,
                             static_cast<hipStream_t>(stream));
+}
+
+namespace {
+int check_block_shape(int B, int L, int H, int nq, int nkv, int I) {
+  if (B < 1 || L < 1 || H < kGroup || H % kGroup || I < kGroup || I % kGroup || nkv < 1 || nq < nkv || nq % nkv)
+    return W4_ERR_SHAPE;
+  const long long T = (long long)B * L;
+  const long long wide = std::max<long long>(std::max<long long>(H, I), 128LL * nq);
+  if ((T + 64) * wide >= (1LL << 31) || (long long)I * H >= (1LL << 31) || 128LL * nq * H >= (1LL << 31) ||
+      L > 65535LL * 64 || nq > 65535 || B > 65535)
+    return W4_ERR_SHAPE;
+  return W4_OK;
+}
+bool block_null(const w4_block* b) {
+  return !b || !b->norm1 || !b->wq || !b->wk || !b->wv || !b->wo || !b->norm2 || !b->wgate || !b->wup || !b->wdown;
+}
+bool block_misaligned(const w4_block* b) {
+  return misaligned(b->norm1) || misaligned(b->wq) || misaligned(b->wk) || misaligned(b->wv) || misaligned(b->wo) ||
+         misaligned(b->norm2) || misaligned(b->wgate) || misaligned(b->wup) || misaligned(b->wdown);
+}
+}  // namespace
+
+int w4_block_forward(const uint16_t* X, int B, int L, int hidden, int n_q, int n_kv, int inter,
+                     const w4_block* blk, uint16_t* Y, void* workspace, size_t* workspace_bytes, void* stream) {
+  int st = check_block_shape(B, L, hidden, n_q, n_kv, inter);
+  if (st) return st;
+  const size_t need = block_forward_workspace_bytes(B, L, hidden, n_q, n_kv, inter);
+  if (!workspace) {
+    if (!workspace_bytes) return W4_ERR_WORKSPACE;
+    *workspace_bytes = need;
+    return W4_OK;
+  }
+  if (!workspace_bytes || *workspace_bytes < need) return W4_ERR_WORKSPACE;
+  if (!X || !Y || block_null(blk)) return W4_ERR_NULL;
+  if (misaligned(X) || misaligned(Y) || misaligned(workspace) || block_misaligned(blk)) return W4_ERR_ALIGN;
+  return launch_block_forward(X, B, L, hidden, n_q, n_kv, inter, *blk, Y, workspace, static_cast<hipStream_t>(stream));
+}
+
+int awq_lookahead_loss(const uint16_t* X, int B, int L, int hidden, int n_q, int n_kv, int inter,
+                       const w4_block* blk, const w4_block* next, int linear, const float* S,
+                       const float* ratios, int C, int symmetric, int group_size, float* losses,
+                       float* losses_d0, void* workspace, size_t* workspace_bytes, void* stream) {
+  if (group_size != kGroup) return W4_ERR_UNSUPPORTED;
+  int st = check_block_shape(B, L, hidden, n_q, n_kv, inter);
+  if (st) return st;
+  if (linear < 0 || linear > 6 || C < 0 || (symmetric != 0 && symmetric != 1)) return W4_ERR_VALUE;
+  const size_t need = lookahead_workspace_bytes(B, L, hidden, n_q, n_kv, inter, linear);
+  if (!workspace) {
+    if (!workspace_bytes) return W4_ERR_WORKSPACE;
+    *workspace_bytes = need;
+    return W4_OK;
+  }
+  if (!workspace_bytes || *workspace_bytes < need) return W4_ERR_WORKSPACE;
+  if (C == 0) return W4_OK;
+  if (!X || !S || !ratios || !losses || block_null(blk) || (next && block_null(next))) return W4_ERR_NULL;
+  if (misaligned(X) || misaligned(workspace) || block_misaligned(blk) || (next && block_misaligned(next)))
+    return W4_ERR_ALIGN;
+  return launch_lookahead_loss(X, B, L, hidden, n_q, n_kv, inter, *blk, next, linear, S, ratios, C, symmetric,
+                               losses, losses_d0, workspace, static_cast<hipStream_t>(stream));
 }
 
 }  // extern "C"

@@ -37,7 +37,7 @@ from __future__ import annotations
 import numpy as np
 
 # workload ids used in the seed entropy
-GEMV_2048, DECODE_SWEEP, PREFILL, LARGE_SYM, AWQ_SEARCH, CHECKPOINT = 1, 2, 3, 4, 5, 6
+GEMV_2048, DECODE_SWEEP, PREFILL, LARGE_SYM, AWQ_SEARCH, CHECKPOINT, LOOKAHEAD = 1, 2, 3, 4, 5, 6, 7
 
 # (name, K, N) of one hidden-2048 decoder block, in execution order
 BLOCK_LINEARS = (
@@ -141,6 +141,32 @@ def small_case(M: int, K: int, N: int, seed: int, w_std: float = 0.02, x_std: fl
     W = normal_bf16(rng, (N, K), w_std)
     X = normal_bf16(rng, (M, K), x_std)
     return X, W
+
+
+# ----------------------------------------------------------------------------- look-ahead block
+
+# block shape of the base model: hidden 2048, 16 query / 8 key-value heads of 128, FFN 6144
+QWEN_BLOCK = dict(H=2048, I=6144, n_q=16, n_kv=8)
+LOOKAHEAD_B, LOOKAHEAD_L = 8, 512            # 4096 calibration tokens as 8 sequences of 512
+
+
+def synthetic_block(H: int = 2048, I: int = 6144, n_q: int = 16, n_kv: int = 8, seed: int = 0,
+                    w_std: float = 0.02) -> dict:
+    """bf16 weights of one decoder block: norm1, norm2 ~ N(1, 0.1) [H]; q [128 n_q][H],
+    k, v [128 n_kv][H], o [H][128 n_q], gate, up [I][H], down [H][I] ~ N(0, w_std)."""
+    rng = np.random.default_rng(np.random.SeedSequence([0, LOOKAHEAD, seed, H, I, n_q, n_kv]))
+    shapes = dict(q=(128 * n_q, H), k=(128 * n_kv, H), v=(128 * n_kv, H), o=(H, 128 * n_q),
+                  gate=(I, H), up=(I, H), down=(H, I))
+    blk = {"norm1": round_to_bf16_bits((1 + 0.1 * rng.standard_normal(H)).astype(np.float32)),
+           "norm2": round_to_bf16_bits((1 + 0.1 * rng.standard_normal(H)).astype(np.float32))}
+    for name, shape in shapes.items():
+        blk[name] = normal_bf16(rng, shape, w_std)
+    return blk
+
+
+def block_input(T: int, H: int = 2048, seed: int = 0) -> np.ndarray:
+    """Hidden states entering a block: [T][H] bf16 ~ N(0, 1)."""
+    return normal_bf16(np.random.default_rng(np.random.SeedSequence([0, LOOKAHEAD, 1000 + seed, T, H])), (T, H), 1.0)
 
 
 # ----------------------------------------------------------------------------- sharded checkpoint

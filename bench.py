@@ -376,6 +376,53 @@ def rows_clip(torch, w4, wl, reps):
     return rows
 
 
+def block_flops(T, B, L, H, I, n_q, n_kv):
+    """Algorithmic flops of one decoder-block forward: the seven linears (2 T per weight)
+    and causal attention (q k^T and p v over the L (L + 1) / 2 visible pairs per head)."""
+    params = H * 128 * n_q * 2 + 2 * H * 128 * n_kv + 3 * H * I
+    return 2 * T * params + 2 * 2 * B * n_q * (L * (L + 1) // 2) * 128
+
+
+def rows_lookahead(torch, w4, wl, reps):
+    """Look-ahead (d = 1) scoring at the base model's block shape: 8 sequences x 512
+    tokens, hidden 2048, 16 / 8 heads, FFN 6144.  Each candidate runs the scored block
+    with the candidate linear and the next block (two block forwards)."""
+    rows = []
+    shp = wl.QWEN_BLOCK
+    H, I, n_q, n_kv = shp["H"], shp["I"], shp["n_q"], shp["n_kv"]
+    B, L = wl.LOOKAHEAD_B, wl.LOOKAHEAD_L
+    T = B * L
+    dev = lambda b: {k: to_dev_bf16(torch, v) for k, v in b.items()}
+    blk, nxt = dev(wl.synthetic_block(H, I, n_q, n_kv, 0)), dev(wl.synthetic_block(H, I, n_q, n_kv, 1))
+    X = to_dev_bf16(torch, wl.block_input(T, H, 0))
+    f_blk = block_flops(T, B, L, H, I, n_q, n_kv)
+    ws = torch.empty(1, dtype=torch.uint8, device="cuda")
+    Y = w4.block_forward(X, B, L, blk, n_q, n_kv)
+    ms = time_events(torch, lambda: w4.block_forward(X, B, L, blk, n_q, n_kv, Y=Y), reps)
+    rows.append(row_gemm(f"decoder block forward T={T} (B={B} L={L}) H={H} I={I} heads {n_q}/{n_kv}", f_blk, ms))
+    C = 10
+    S = torch.ones((C, 2048), dtype=torch.float32, device="cuda")
+    ratios = torch.tensor([1 - j / 20 for j in range(C)], dtype=torch.float32, device="cuda")
+    w4.awq_lookahead_loss(X, B, L, blk, nxt, n_q, n_kv, "gate", S, ratios)
+    t0 = time.perf_counter()
+    n = 2
+    for _ in range(n):
+        l1, _ = w4.awq_lookahead_loss(X, B, L, blk, nxt, n_q, n_kv, "gate", S, ratios)
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / n
+    rows.append(row_gemm(f"look-ahead losses, gate, {C} candidates + reference (two blocks each)",
+                         (C + 1) * 2 * f_blk, ms, {"ms_per_candidate": round(ms / (C + 1), 3)}))
+    res = w4.awq_search_lookahead(X, B, L, blk, nxt, n_q, n_kv, "gate", [i / 20 for i in range(20)],
+                                  [1 - j / 20 for j in range(10)])
+    t0 = time.perf_counter()
+    res = w4.awq_search_lookahead(X, B, L, blk, nxt, n_q, n_kv, "gate", [i / 20 for i in range(20)],
+                                  [1 - j / 20 for j in range(10)])
+    ms = (time.perf_counter() - t0) * 1e3
+    rows.append(row_gemm("look-ahead two-phase search, gate (20 alpha + 10 ratio + reference)", 31 * 2 * f_blk, ms,
+                         {"alpha_index": res["alpha_index"], "ratio_index": res["ratio_index"]}))
+    return rows
+
+
 def rows_convert(torch, w4, wl, reps):
     """Streaming data-free symmetric conversion of a synthetic 3-shard checkpoint
     (8 hidden-2048 blocks, 0.87 GB of bf16) written to a temporary directory."""
@@ -442,7 +489,7 @@ def main(argv=None):
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
     ap.add_argument("--step-only", action="store_true", help="measure only the decode-sweep step")
     ap.add_argument("--only", default="", help="comma list of extra rows to measure "
-                    "(sweeps,w4a8,large,prefill,gemv2048,search,clip,convert); default all")
+                    "(sweeps,w4a8,large,prefill,gemv2048,search,clip,lookahead,convert); default all")
     ap.add_argument("--blocks", type=int, default=28)
     ap.add_argument("--skip-step", action="store_true",
                     help="profiling aid: skip the decode-sweep step (value is null) and run only --only rows")
@@ -532,7 +579,7 @@ def main(argv=None):
         torch.cuda.empty_cache()
 
     want = set(x for x in args.only.split(",") if x) or {"sweeps", "w4a8", "large", "prefill", "gemv2048",
-                                                         "search", "clip", "convert"}
+                                                         "search", "clip", "lookahead", "convert"}
     if not args.step_only:
         rows = []
         if "sweeps" in want and packed:
@@ -564,7 +611,8 @@ def main(argv=None):
         torch.cuda.empty_cache()
         reps = max(5, args.steps)
         for name, fn in (("large", rows_large), ("prefill", rows_prefill), ("gemv2048", rows_gemv2048),
-                         ("search", rows_search), ("clip", rows_clip), ("convert", rows_convert)):
+                         ("search", rows_search), ("clip", rows_clip), ("lookahead", rows_lookahead),
+                         ("convert", rows_convert)):
             if name in want:
                 log(f"rows: {name}")
                 rows += fn(torch, w4, wl, reps)

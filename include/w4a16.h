@@ -303,6 +303,25 @@ int awq_lookahead_loss(const uint16_t* X, int B, int L, int hidden, int n_q, int
                        float* losses_d0, void* workspace, size_t* workspace_bytes, void* stream);
 
 /*
+ * awq_search_lookahead -- the two-phase search of [AWQ-W4 card] "Search" scored
+ * with the look-ahead loss of awq_lookahead_loss: m_k = mean_t |a[t][k]| of the
+ * linear's input a in the reference pass (device, fp64, fixed order), s(alpha) as in
+ * awq_search (host fp64, stored fp32); every alpha at r = 1, first minimum alpha*;
+ * then every ratio at s(alpha*), first minimum r*.
+ *   alphas [n_alpha], ratios [n_ratio]: host fp64 (1 <= n <= 64 each; alphas in
+ *   [0, 16], ratios in (0, 1]).  losses_out [n_alpha + n_ratio]: host fp32 out
+ *   (d = 1 losses).  alpha_index, ratio_index: host int out.  s_out [K] fp32
+ *   device out: s(alpha*).  Workspace as in awq_search (NULL workspace and NULL
+ *   workspace_bytes: the call allocates and frees its own).  Synchronizes
+ *   `stream` (three times).
+ */
+int awq_search_lookahead(const uint16_t* X, int B, int L, int hidden, int n_q, int n_kv, int inter,
+                         const w4_block* blk, const w4_block* next, int linear, const double* alphas,
+                         int n_alpha, const double* ratios, int n_ratio, int symmetric, int group_size,
+                         float* losses_out, int* alpha_index, int* ratio_index, float* s_out,
+                         void* workspace, size_t* workspace_bytes, void* stream);
+
+/*
  * Measurement helpers (not part of the method): the yardsticks the kernels
  * above are measured against on the same device.
  *

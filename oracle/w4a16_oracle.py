@@ -432,15 +432,18 @@ def silu_mul(g, u) -> np.ndarray:
     return _bf16_round(g / (1.0 + np.exp(-g)) * u)
 
 
-def block_forward(x_bf16, B: int, L: int, blk: dict, n_q: int, n_kv: int, candidate=None):
+def block_forward(x_bf16, B: int, L: int, blk: dict, n_q: int, n_kv: int, candidate=None, inputs=None):
     """One decoder block on x [B*L][H] (uint16 bf16).  blk maps "norm1", "norm2" to
     bf16 [H] and each name of LINEARS to its bf16 weight [out][in].  candidate =
     (name, s fp32 [in], packed (qweight, scales, qzeros), symmetric) replaces that
     linear by its deployed int4 form: input bf16(in / s) against the dequantized
-    codes.  Returns the block output as bf16 bits [B*L][H]."""
+    codes.  Returns the block output as bf16 bits [B*L][H]; a dict passed as
+    `inputs` receives each linear's input (bf16 values, fp64)."""
     val = lambda bits: bf16_to_f32(np.asarray(bits, dtype=np.uint16)).astype(np.float64)
 
     def lin(name, a):
+        if inputs is not None:
+            inputs[name] = a
         if candidate is not None and candidate[0] == name:
             _, s, (qw, sc, qz), sym = candidate
             K = a.shape[1]
@@ -479,3 +482,23 @@ def lookahead_losses(x_bf16, B, L, blk, nxt, n_q, n_kv, name, S, ratios, symmetr
         d0.append(float(np.mean((val(yi) - val(ref_i)) ** 2)))
         d1.append(float(np.mean((val(yn) - val(ref_n)) ** 2)))
     return np.array(d1), np.array(d0)
+
+
+def search_lookahead(x_bf16, B, L, blk, nxt, n_q, n_kv, name, alphas=None, ratios=None, symmetric=False):
+    """Two-phase search of [AWQ-W4 card] "Search" with the look-ahead loss: the
+    statistic m = mean |input of the linear| over the tokens of the reference pass,
+    every alpha at r = 1 (first minimum alpha*), then every ratio at s(alpha*).
+    Returns dict(alpha_losses, ratio_losses, alpha_index, ratio_index, s)."""
+    alphas = alpha_grid() if alphas is None else np.asarray(alphas, dtype=np.float64)
+    ratios = shrink_grid() if ratios is None else np.asarray(ratios, dtype=np.float64)
+    ins = {}
+    block_forward(x_bf16, B, L, blk, n_q, n_kv, inputs=ins)
+    m = np.abs(ins[name]).mean(axis=0)
+    S = np.stack([awq_scales(m, a) for a in alphas])
+    la, _ = lookahead_losses(x_bf16, B, L, blk, nxt, n_q, n_kv, name, S, np.ones(len(alphas)), symmetric)
+    ia = int(np.argmin(la))
+    s_star = S[ia]
+    lr, _ = lookahead_losses(x_bf16, B, L, blk, nxt, n_q, n_kv, name,
+                             np.broadcast_to(s_star, (len(ratios), s_star.size)), ratios, symmetric)
+    ir = int(np.argmin(lr))
+    return dict(alpha_losses=la, ratio_losses=lr, alpha_index=ia, ratio_index=ir, s=s_star)

@@ -617,8 +617,26 @@ def check_block_and_lookahead():
     assert np.array_equal(f0, e0) and f1[1] > f1[0] > 0
 
 
+def check_search_lookahead_statistic_and_ties():
+    """The look-ahead search takes m from the linear's own input (for gate: the second
+    RMSNorm's output) and keeps the first of equal minima: with equal-magnitude inputs
+    every alpha gives the same s, so all alpha losses tie and alpha 0 is chosen."""
+    rng = np.random.default_rng(83)
+    B, L, H = 1, 8, 256
+    blk = _block(rng, H=H)
+    blk["norm2"] = round_to_bf16_bits(np.ones(H, np.float32))
+    x = round_to_bf16_bits(np.where(rng.random((B * L, H)) < 0.5, -1.0, 1.0).astype(np.float32))
+    blk["o"] = np.zeros_like(blk["o"])              # h = x, so the gate input is rmsnorm(x) = x
+    ins = {}
+    O.block_forward(x, B, L, blk, 2, 1, inputs=ins)
+    assert np.array_equal(ins["gate"], O.bf16_to_f32(x).astype(np.float64))
+    res = O.search_lookahead(x, B, L, blk, None, 2, 1, "gate", alphas=[0.0, 0.3, 0.7], ratios=[1.0, 0.9])
+    assert np.all(res["alpha_losses"] == res["alpha_losses"][0]) and res["alpha_index"] == 0
+    assert np.array_equal(res["s"], np.ones(H, np.float32))
+
+
 ALL_CHECKS = [
-    check_rope_rotation, check_attention, check_rmsnorm_and_silu, check_block_and_lookahead,
+    check_search_lookahead_statistic_and_ties, check_rope_rotation, check_attention, check_rmsnorm_and_silu, check_block_and_lookahead,
     check_clip_channel_bruteforce, check_clip_channel_special_cases,
     check_w4a8_activation_codes, check_w4a8_linear_reduces_to_dequant_matmul,
     check_division_ties,

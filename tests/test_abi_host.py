@@ -29,7 +29,7 @@ def declared_functions():
 def test_header_declares_the_boundary():
     names = declared_functions()
     for n in ("awq_quantize_pack", "w4a16_gemv", "w4a16_gemm", "awq_grid_loss", "awq_search", "awq_clip_search",
-              "w4_status_string"):
+              "w4_block_forward", "awq_lookahead_loss", "awq_search_lookahead", "w4_status_string"):
         assert n in names, names
 
 
@@ -187,6 +187,50 @@ def test_clip_search_validation(lib):
     assert f(*a) == -5
     a[13] = None
     assert f(*a) == -5
+
+
+_Blk = w4._Block          # struct w4_block as the binding declares it
+
+
+def test_block_and_lookahead_validation(lib):
+    sz = ctypes.c_size_t(0)
+    blk = _Blk(*([0x10000] * 9))
+    bad = _Blk(*([0x10000] * 8 + [0]))
+    mis = _Blk(*([0x10000] * 8 + [0x10004]))
+    f = lib.w4_block_forward
+    assert f(None, 8, 512, 2048, 16, 8, 6144, None, None, None, ctypes.byref(sz), None) == 0
+    assert sz.value > 2 * 4096 * (5 * 2048 + 3 * 6144) * 2 // 2
+    ok = ctypes.c_size_t(sz.value)
+    assert f(A, 8, 512, 2000, 16, 8, 6144, ctypes.byref(blk), A, A, ctypes.byref(ok), None) == -2   # H % 128
+    assert f(A, 8, 512, 2048, 16, 6, 6144, ctypes.byref(blk), A, A, ctypes.byref(ok), None) == -2   # n_kv !| n_q
+    assert f(A, 0, 512, 2048, 16, 8, 6144, ctypes.byref(blk), A, A, ctypes.byref(ok), None) == -2
+    assert f(A, 8, 512, 2048, 16, 8, 6144, ctypes.byref(bad), A, A, ctypes.byref(ok), None) == -1
+    assert f(A, 8, 512, 2048, 16, 8, 6144, ctypes.byref(mis), A, A, ctypes.byref(ok), None) == -3
+    assert f(A, 8, 512, 2048, 16, 8, 6144, ctypes.byref(blk), A, A, ctypes.byref(ctypes.c_size_t(16)), None) == -5
+    g = lib.awq_lookahead_loss
+    assert g(None, 8, 512, 2048, 16, 8, 6144, None, None, 6, None, None, 10, 0, 128, None, None, None,
+             ctypes.byref(sz), None) == 0
+    ok = ctypes.c_size_t(sz.value)
+    args = lambda **k: [k.get("X", A), 8, 512, 2048, 16, 8, 6144, ctypes.byref(k.get("blk", blk)), k.get("nxt", None),
+                        k.get("lin", 6), k.get("S", A), A, 10, k.get("sym", 0), k.get("gs", 128), A, None, A,
+                        ctypes.byref(ok), None]
+    assert g(*args(lin=7)) == -7
+    assert g(*args(sym=2)) == -7
+    assert g(*args(gs=64)) == -4
+    assert g(*args(S=None)) == -1
+    assert g(*args(blk=bad)) == -1
+    assert g(*args(nxt=ctypes.byref(bad))) == -1
+    assert g(*args(X=MIS)) == -3
+    h = lib.awq_search_lookahead
+    D = ctypes.c_double
+    al = (D * 20)(*[i / 20 for i in range(20)])
+    ra = (D * 10)(*[1 - j / 20 for j in range(10)])
+    assert h(None, 8, 512, 2048, 16, 8, 6144, None, None, 0, al, 20, ra, 10, 0, 128, None, None, None, None, None,
+             ctypes.byref(sz), None) == 0
+    assert sz.value > ok.value // 2
+    badr = (D * 1)(1.5)
+    assert h(A, 8, 512, 2048, 16, 8, 6144, ctypes.byref(blk), None, 0, al, 20, badr, 1, 0, 128, None, None, None, None,
+             None, ctypes.byref(sz), None) == -7
 
 
 def test_python_binding_fails_loudly_without_library(monkeypatch, tmp_path):

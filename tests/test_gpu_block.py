@@ -150,3 +150,24 @@ def test_lookahead_qwen_shape():
         n1, n0 = _noise(x, B, L, blk, nxt, n_q, n_kv)
         _losses_ok(l1.cpu().numpy().astype(np.float64), o1, n1)
         _losses_ok(l0.cpu().numpy().astype(np.float64), o0, n0)
+
+
+def test_search_lookahead_small():
+    """Two-phase search of the gate projection scored after the next block: every alpha
+    and ratio loss within its bar of the oracle's, the chosen alpha valid, and, when
+    it is the oracle's, s(alpha*) within 1e-3 and the chosen ratio valid.  (The
+    statistic is taken over the linear's input as each side computes it in its own
+    reference pass, whose rare bf16 rounding flips move m by about 2^-8 / T.)"""
+    H, I, n_q, n_kv, B, L = 256, 384, 2, 1, 2, 40
+    blk, x = _block_case(H, I, n_q, n_kv, B, L, 21)
+    nxt = synthetic_block(H, I, n_q, n_kv, 22)
+    alphas, ratios = [0.0, 0.25, 0.5, 0.75], [1.0, 0.9, 0.8]
+    say("search lookahead")
+    res = w4.awq_search_lookahead(to_bf16(x), B, L, _dev(blk), _dev(nxt), n_q, n_kv, "gate", alphas, ratios)
+    ref = O.search_lookahead(x, B, L, blk, nxt, n_q, n_kv, "gate", alphas, ratios)
+    n1, _ = _noise(x, B, L, blk, nxt, n_q, n_kv)
+    la, oa = np.array(res["alpha_losses"], np.float64), ref["alpha_losses"]
+    _losses_ok(la, oa, n1)
+    if res["alpha_index"] == ref["alpha_index"]:
+        assert np.allclose(res["s"].cpu().numpy(), ref["s"], rtol=1e-3, atol=0)
+        _losses_ok(np.array(res["ratio_losses"], np.float64), ref["ratio_losses"], n1)

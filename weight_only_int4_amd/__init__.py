@@ -21,7 +21,7 @@ __all__ = [
     "W4Error", "library_path", "load_library", "awq_quantize_pack", "w4a16_gemv", "w4a16_gemm",
     "awq_grid_loss", "awq_search", "GROUP_SIZE", "GEMV_MAX_M", "gemv_launcher", "gemm_launcher",
     "w4a8_quantize_activations", "w4a8_gemv", "w4a8_gemv_launcher", "awq_clip_search", "block_forward",
-    "awq_lookahead_loss", "BLOCK_LINEARS", "probe_stream_read", "probe_empty",
+    "awq_lookahead_loss", "awq_search_lookahead", "BLOCK_LINEARS", "probe_stream_read", "probe_empty",
 ]
 
 GROUP_SIZE = 128
@@ -55,6 +55,9 @@ _SIGNATURES = {
     "w4_block_forward": ([_vp, _i, _i, _i, _i, _i, _i, _bp, _vp, _vp, _sz, _vp], _i),
     "awq_lookahead_loss": ([_vp, _i, _i, _i, _i, _i, _i, _bp, _bp, _i, _vp, _vp, _i, _i, _i, _vp, _vp, _vp, _sz, _vp],
                            _i),
+    "awq_search_lookahead": ([_vp, _i, _i, _i, _i, _i, _i, _bp, _bp, _i, ctypes.POINTER(ctypes.c_double), _i,
+                              ctypes.POINTER(ctypes.c_double), _i, _i, _i, ctypes.POINTER(ctypes.c_float),
+                              ctypes.POINTER(ctypes.c_int), ctypes.POINTER(ctypes.c_int), _vp, _vp, _sz, _vp], _i),
     "awq_search": ([_vp, _i, _i, _i, _vp, ctypes.POINTER(ctypes.c_double), _i,
                     ctypes.POINTER(ctypes.c_double), _i, _i, _i, ctypes.POINTER(ctypes.c_float),
                     ctypes.POINTER(ctypes.c_int), ctypes.POINTER(ctypes.c_int), _vp, _vp, _sz, _vp], _i),
@@ -385,6 +388,41 @@ def awq_lookahead_loss(X, B: int, L: int, blk, nxt, n_q: int, n_kv: int, linear,
                                   int(symmetric), GROUP_SIZE, _ptr(losses), _ptr(d0), _ptr(ws),
                                   None if wsb is None else ctypes.byref(wsb), _stream(X.device)))
     return losses, d0
+
+
+def awq_search_lookahead(X, B: int, L: int, blk, nxt, n_q: int, n_kv: int, linear, alphas, ratios,
+                         symmetric: bool = False, workspace=None):
+    """Two-phase AWQ search of one linear of block blk scored after block nxt (None:
+    the last block).  Returns dict(alpha_losses, ratio_losses, alpha_index,
+    ratio_index, s).  Synchronizes."""
+    lib = load_library()
+    _need(X, torch.bfloat16, "X", 2)
+    T, H = X.shape
+    if T != B * L:
+        raise ValueError("X must have B * L rows")
+    I = blk["gate"].shape[0]
+    li = BLOCK_LINEARS.index(linear) if isinstance(linear, str) else int(linear)
+    b = _block_struct(blk, H, n_q, n_kv, I)
+    nb = None if nxt is None else _block_struct(nxt, H, n_q, n_kv, I)
+    K = blk[BLOCK_LINEARS[li]].shape[1]
+    a = (ctypes.c_double * len(alphas))(*[float(x) for x in alphas])
+    r = (ctypes.c_double * len(ratios))(*[float(x) for x in ratios])
+    out = (ctypes.c_float * (len(alphas) + len(ratios)))()
+    ia, ir = ctypes.c_int(-1), ctypes.c_int(-1)
+    s_out = torch.empty(K, dtype=torch.float32, device=X.device)
+
+    def q(sz):
+        return lib.awq_search_lookahead(None, B, L, H, n_q, n_kv, I, None, None, li, a, len(alphas), r, len(ratios),
+                                        int(symmetric), GROUP_SIZE, None, None, None, None, None, sz, None)
+
+    ws, wsb = _workspace(q, X.device, workspace)
+    _check(lib.awq_search_lookahead(_ptr(X), B, L, H, n_q, n_kv, I, ctypes.byref(b),
+                                    None if nb is None else ctypes.byref(nb), li, a, len(alphas), r, len(ratios),
+                                    int(symmetric), GROUP_SIZE, out, ctypes.byref(ia), ctypes.byref(ir), _ptr(s_out),
+                                    _ptr(ws), None if wsb is None else ctypes.byref(wsb), _stream(X.device)))
+    vals = list(out)
+    return dict(alpha_losses=vals[: len(alphas)], ratio_losses=vals[len(alphas):], alpha_index=ia.value,
+                ratio_index=ir.value, s=s_out)
 
 
 def awq_search(X, W, alphas, ratios, symmetric: bool = False, workspace=None):

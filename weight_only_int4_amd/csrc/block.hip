@@ -478,18 +478,46 @@ size_t lookahead_workspace_bytes(int B, int L, int H, int nq, int nkv, int I, in
   return look_layout(make_dims(B, L, H, nq, nkv, I), linear).total;
 }
 
-int launch_lookahead_loss(const uint16_t* X, int B, int L, int H, int nq, int nkv, int I, const w4_block& blk,
-                          const w4_block* next, int linear, const float* S, const float* ratios, int C,
-                          int symmetric, float* losses, float* losses_d0, void* workspace, hipStream_t stream) {
+int lookahead_input_size(int H, int nq, int I, int linear) {
+  Dims d = make_dims(1, 1, H, nq, 1, I);
+  int K, N;
+  linear_shape(d, linear, K, N);
+  return K;
+}
+
+// Reference path: block `blk` (its output kept), then `next` when given.  With m not
+// NULL, mean |input| of linear `linear` over the tokens is written to m[0 .. K) (m
+// holds (1 + ceil(T / 64)) K doubles, the rest per-chunk partial sums).
+int launch_lookahead_reference(const uint16_t* X, int B, int L, int H, int nq, int nkv, int I, const w4_block& blk,
+                               const w4_block* next, int linear, double* m, void* workspace, hipStream_t stream) {
   const Dims d = make_dims(B, L, H, nq, nkv, I);
   const LookLayout l = look_layout(d, linear);
   char* ws = static_cast<char*>(workspace);
   auto buf = [&](size_t off) { return reinterpret_cast<uint16_t*>(ws + off); };
   int rc = rope_tables(d, ws, l.blk, stream);
   if (rc) return rc;
-  // reference path
   if ((rc = run_block(d, blk, X, buf(l.yref_i), nullptr, ws, l.blk, stream))) return rc;
+  if (m) {
+    // the block buffers still hold this block's activations: the linear's input
+    const size_t in[7] = {l.blk.a, l.blk.a, l.blk.a, l.blk.o, l.blk.b2, l.blk.b2, l.blk.m};
+    int K, N;
+    linear_shape(d, linear, K, N);
+    if ((rc = launch_act_mean_abs(buf(in[linear]), d.T, K, m, stream))) return rc;
+  }
   if (next && (rc = run_block(d, *next, buf(l.yref_i), buf(l.yref_n), nullptr, ws, l.blk, stream))) return rc;
+  return W4_OK;
+}
+
+// Candidates against the reference outputs left in the workspace by
+// launch_lookahead_reference (same shape, blocks and linear).
+int launch_lookahead_candidates(const uint16_t* X, int B, int L, int H, int nq, int nkv, int I, const w4_block& blk,
+                                const w4_block* next, int linear, const float* S, const float* ratios, int C,
+                                int symmetric, float* losses, float* losses_d0, void* workspace,
+                                hipStream_t stream) {
+  const Dims d = make_dims(B, L, H, nq, nkv, I);
+  const LookLayout l = look_layout(d, linear);
+  char* ws = static_cast<char*>(workspace);
+  auto buf = [&](size_t off) { return reinterpret_cast<uint16_t*>(ws + off); };
   const uint16_t* ref_n = next ? buf(l.yref_n) : buf(l.yref_i);
   int K, N;
   linear_shape(d, linear, K, N);
@@ -497,6 +525,7 @@ int launch_lookahead_loss(const uint16_t* X, int B, int L, int H, int nq, int nk
   double* part = reinterpret_cast<double*>(ws + l.part);
   const size_t n = (size_t)d.T * d.H;
   const unsigned pblocks = (unsigned)l.nparts;
+  int rc;
   for (int c = 0; c < C; ++c) {
     QuantArgs q{};
     q.W = Wl[linear];
@@ -528,6 +557,15 @@ int launch_lookahead_loss(const uint16_t* X, int B, int L, int H, int nq, int nk
     }
   }
   return W4_OK;
+}
+
+int launch_lookahead_loss(const uint16_t* X, int B, int L, int H, int nq, int nkv, int I, const w4_block& blk,
+                          const w4_block* next, int linear, const float* S, const float* ratios, int C,
+                          int symmetric, float* losses, float* losses_d0, void* workspace, hipStream_t stream) {
+  int rc = launch_lookahead_reference(X, B, L, H, nq, nkv, I, blk, next, linear, nullptr, workspace, stream);
+  if (rc) return rc;
+  return launch_lookahead_candidates(X, B, L, H, nq, nkv, I, blk, next, linear, S, ratios, C, symmetric, losses,
+                                     losses_d0, workspace, stream);
 }
 
 }  // namespace w4

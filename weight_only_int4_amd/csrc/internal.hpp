@@ -67,6 +67,13 @@ size_t lookahead_workspace_bytes(int B, int L, int H, int nq, int nkv, int I, in
 int launch_lookahead_loss(const uint16_t* X, int B, int L, int H, int nq, int nkv, int I, const w4_block& blk,
                           const w4_block* next, int linear, const float* S, const float* ratios, int C,
                           int symmetric, float* losses, float* losses_d0, void* workspace, hipStream_t stream);
+int lookahead_input_size(int H, int nq, int I, int linear);
+int launch_lookahead_reference(const uint16_t* X, int B, int L, int H, int nq, int nkv, int I, const w4_block& blk,
+                               const w4_block* next, int linear, double* m, void* workspace, hipStream_t stream);
+int launch_lookahead_candidates(const uint16_t* X, int B, int L, int H, int nq, int nkv, int I, const w4_block& blk,
+                                const w4_block* next, int linear, const float* S, const float* ratios, int C,
+                                int symmetric, float* losses, float* losses_d0, void* workspace,
+                                hipStream_t stream);
 
 // Y = bf16(X W^T) with bf16 weights W [N][K] (the unquantized reference output).
 int launch_reference_gemm(const uint16_t* X, int M, int K, int N, const uint16_t* W, uint16_t* Y,

@@ -274,6 +274,24 @@ SearchLayout search_layout(int T, int K, int N, int C) {
   return L;
 }
 
+// s(alpha)_k = max(m_k^alpha, 1e-4) / sqrt(max_j p_j min_j p_j) on the host in fp64,
+// stored fp32: row i of S for alphas[i].
+void alpha_scales(const std::vector<double>& m, const double* alphas, int n_alpha, std::vector<float>& S) {
+  const int K = (int)m.size();
+  std::vector<double> p(K);
+  for (int i = 0; i < n_alpha; ++i) {
+    double pmax = 0.0, pmin = INFINITY;
+    for (int k = 0; k < K; ++k) {
+      const double v = pow(m[k], alphas[i]);
+      p[k] = v > 1e-4 ? v : 1e-4;
+      pmax = p[k] > pmax ? p[k] : pmax;
+      pmin = p[k] < pmin ? p[k] : pmin;
+    }
+    const double d = sqrt(pmax * pmin);
+    for (int k = 0; k < K; ++k) S[(size_t)i * K + k] = (float)(p[k] / d);
+  }
+}
+
 int first_argmin(const std::vector<float>& v) {
   int best = 0;
   for (int i = 1; i < (int)v.size(); ++i)
@@ -301,20 +319,8 @@ int search_impl(const uint16_t* X, int T, int K, int N, const uint16_t* W, const
   if (hipMemcpyAsync(m.data(), dm, (size_t)K * 8, hipMemcpyDeviceToHost, stream) != hipSuccess) return W4_ERR_HIP;
   if (hipStreamSynchronize(stream) != hipSuccess) return W4_ERR_HIP;
 
-  // s(alpha) on the host in fp64, stored fp32
   std::vector<float> S((size_t)C * K), R(C, 1.0f);
-  std::vector<double> p(K);
-  for (int i = 0; i < n_alpha; ++i) {
-    double pmax = 0.0, pmin = INFINITY;
-    for (int k = 0; k < K; ++k) {
-      const double v = pow(m[k], alphas[i]);
-      p[k] = v > 1e-4 ? v : 1e-4;
-      pmax = p[k] > pmax ? p[k] : pmax;
-      pmin = p[k] < pmin ? p[k] : pmin;
-    }
-    const double d = sqrt(pmax * pmin);
-    for (int k = 0; k < K; ++k) S[(size_t)i * K + k] = (float)(p[k] / d);
-  }
+  alpha_scales(m, alphas, n_alpha, S);
   if (hipMemcpyAsync(dS, S.data(), (size_t)n_alpha * K * 4, hipMemcpyHostToDevice, stream) != hipSuccess ||
       hipMemcpyAsync(dR, R.data(), (size_t)n_alpha * 4, hipMemcpyHostToDevice, stream) != hipSuccess)
     return W4_ERR_HIP;
@@ -382,6 +388,126 @@ extern "C" int awq_search(const uint16_t* X, int T, int K, int N, const uint16_t
   if (hipMalloc(&own, L.total) != hipSuccess) return W4_ERR_HIP;
   st = search_impl(X, T, K, N, W, alphas, n_alpha, ratios, n_ratio, symmetric, losses_out, alpha_index,
                    ratio_index, s_out, static_cast<char*>(own), L, s);
+  const hipError_t fe = hipFree(own);
+  if (st == W4_OK && fe != hipSuccess) st = W4_ERR_HIP;
+  return st;
+}
+
+namespace {
+
+struct LookSearchLayout {
+  size_t look, S, R, L, m, total;
+};
+
+LookSearchLayout look_search_layout(int B, int L, int H, int nq, int nkv, int I, int linear, int C) {
+  LookSearchLayout l{};
+  const int K = lookahead_input_size(H, nq, I, linear);
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off = align_up(off + bytes, 256);
+    return o;
+  };
+  l.look = take(lookahead_workspace_bytes(B, L, H, nq, nkv, I, linear));
+  l.S = take((size_t)C * K * 4);
+  l.R = take((size_t)C * 4);
+  l.L = take((size_t)C * 4);
+  l.m = take((size_t)(1 + ((long long)B * L + kActRows - 1) / kActRows) * K * 8);
+  l.total = off;
+  return l;
+}
+
+int look_search_impl(const uint16_t* X, int B, int L, int H, int nq, int nkv, int I, const w4_block& blk,
+                     const w4_block* next, int linear, const double* alphas, int n_alpha, const double* ratios,
+                     int n_ratio, int symmetric, float* losses_out, int* alpha_index, int* ratio_index,
+                     float* s_out, char* ws, const LookSearchLayout& l, hipStream_t stream) {
+  const int K = lookahead_input_size(H, nq, I, linear);
+  const int C = std::max(n_alpha, n_ratio);
+  void* lw = ws + l.look;
+  float* dS = reinterpret_cast<float*>(ws + l.S);
+  float* dR = reinterpret_cast<float*>(ws + l.R);
+  float* dL = reinterpret_cast<float*>(ws + l.L);
+  double* dm = reinterpret_cast<double*>(ws + l.m);
+  int st = launch_lookahead_reference(X, B, L, H, nq, nkv, I, blk, next, linear, dm, lw, stream);
+  if (st) return st;
+  std::vector<double> m(K);
+  if (hipMemcpyAsync(m.data(), dm, (size_t)K * 8, hipMemcpyDeviceToHost, stream) != hipSuccess ||
+      hipStreamSynchronize(stream) != hipSuccess)
+    return W4_ERR_HIP;
+  std::vector<float> S((size_t)C * K), R(C, 1.0f);
+  alpha_scales(m, alphas, n_alpha, S);
+  if (hipMemcpyAsync(dS, S.data(), (size_t)n_alpha * K * 4, hipMemcpyHostToDevice, stream) != hipSuccess ||
+      hipMemcpyAsync(dR, R.data(), (size_t)n_alpha * 4, hipMemcpyHostToDevice, stream) != hipSuccess)
+    return W4_ERR_HIP;
+  st = launch_lookahead_candidates(X, B, L, H, nq, nkv, I, blk, next, linear, dS, dR, n_alpha, symmetric, dL,
+                                   nullptr, lw, stream);
+  if (st) return st;
+  std::vector<float> la(n_alpha);
+  if (hipMemcpyAsync(la.data(), dL, (size_t)n_alpha * 4, hipMemcpyDeviceToHost, stream) != hipSuccess ||
+      hipStreamSynchronize(stream) != hipSuccess)
+    return W4_ERR_HIP;
+  const int ia = first_argmin(la);
+  const std::vector<float> s_star(S.begin() + (size_t)ia * K, S.begin() + (size_t)(ia + 1) * K);
+  for (int j = 0; j < n_ratio; ++j) {
+    memcpy(&S[(size_t)j * K], s_star.data(), (size_t)K * 4);
+    R[j] = (float)ratios[j];
+  }
+  if (hipMemcpyAsync(dS, S.data(), (size_t)n_ratio * K * 4, hipMemcpyHostToDevice, stream) != hipSuccess ||
+      hipMemcpyAsync(dR, R.data(), (size_t)n_ratio * 4, hipMemcpyHostToDevice, stream) != hipSuccess)
+    return W4_ERR_HIP;
+  st = launch_lookahead_candidates(X, B, L, H, nq, nkv, I, blk, next, linear, dS, dR, n_ratio, symmetric, dL,
+                                   nullptr, lw, stream);
+  if (st) return st;
+  std::vector<float> lr(n_ratio);
+  if (hipMemcpyAsync(lr.data(), dL, (size_t)n_ratio * 4, hipMemcpyDeviceToHost, stream) != hipSuccess ||
+      hipMemcpyAsync(s_out, dS, (size_t)K * 4, hipMemcpyDeviceToDevice, stream) != hipSuccess ||
+      hipStreamSynchronize(stream) != hipSuccess)
+    return W4_ERR_HIP;
+  memcpy(losses_out, la.data(), (size_t)n_alpha * 4);
+  memcpy(losses_out + n_alpha, lr.data(), (size_t)n_ratio * 4);
+  *alpha_index = ia;
+  *ratio_index = first_argmin(lr);
+  return W4_OK;
+}
+
+}  // namespace
+
+extern "C" int awq_search_lookahead(const uint16_t* X, int B, int L, int hidden, int n_q, int n_kv, int inter,
+                                    const w4_block* blk, const w4_block* next, int linear, const double* alphas,
+                                    int n_alpha, const double* ratios, int n_ratio, int symmetric, int group_size,
+                                    float* losses_out, int* alpha_index, int* ratio_index, float* s_out,
+                                    void* workspace, size_t* workspace_bytes, void* stream) {
+  if (group_size != kGroup) return W4_ERR_UNSUPPORTED;
+  int st = check_block_shape(B, L, hidden, n_q, n_kv, inter);
+  if (st) return st;
+  if (linear < 0 || linear > 6 || (symmetric != 0 && symmetric != 1)) return W4_ERR_VALUE;
+  if (n_alpha < 1 || n_alpha > 64 || n_ratio < 1 || n_ratio > 64) return W4_ERR_VALUE;
+  if (!alphas || !ratios) return W4_ERR_NULL;
+  for (int i = 0; i < n_alpha; ++i)
+    if (!(alphas[i] >= 0.0 && alphas[i] <= 16.0)) return W4_ERR_VALUE;
+  for (int j = 0; j < n_ratio; ++j)
+    if (!(ratios[j] > 0.0 && ratios[j] <= 1.0)) return W4_ERR_VALUE;
+  const LookSearchLayout l =
+      look_search_layout(B, L, hidden, n_q, n_kv, inter, linear, std::max(n_alpha, n_ratio));
+  if (!workspace && workspace_bytes) {
+    *workspace_bytes = l.total;
+    return W4_OK;
+  }
+  if (workspace && (!workspace_bytes || *workspace_bytes < l.total)) return W4_ERR_WORKSPACE;
+  if (!X || !losses_out || !alpha_index || !ratio_index || !s_out || block_null(blk) || (next && block_null(next)))
+    return W4_ERR_NULL;
+  if (misaligned(X) || misaligned(s_out) || misaligned(workspace) || block_misaligned(blk) ||
+      (next && block_misaligned(next)))
+    return W4_ERR_ALIGN;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (workspace)
+    return look_search_impl(X, B, L, hidden, n_q, n_kv, inter, *blk, next, linear, alphas, n_alpha, ratios, n_ratio,
+                            symmetric, losses_out, alpha_index, ratio_index, s_out, static_cast<char*>(workspace), l,
+                            s);
+  void* own = nullptr;
+  if (hipMalloc(&own, l.total) != hipSuccess) return W4_ERR_HIP;
+  st = look_search_impl(X, B, L, hidden, n_q, n_kv, inter, *blk, next, linear, alphas, n_alpha, ratios, n_ratio,
+                        symmetric, losses_out, alpha_index, ratio_index, s_out, static_cast<char*>(own), l, s);
   const hipError_t fe = hipFree(own);
   if (st == W4_OK && fe != hipSuccess) st = W4_ERR_HIP;
   return st;

@@ -370,36 +370,47 @@ int run_linear(const Dims& d, int i, const uint16_t* X, const uint16_t* W, const
   return launch_reference_gemm(X, d.T, K, N, W, Y, st);
 }
 
+// The block from a given stage: 0 = from its input X; 1 = from the attention output
+// o_in (X still needed for the residual); 2 = from the post-attention residual h_in.
 int run_block(const Dims& d, const w4_block& blk, const uint16_t* X, uint16_t* Y, const Candidate* cand,
-              char* ws, const BlockLayout& l, hipStream_t st) {
+              char* ws, const BlockLayout& l, hipStream_t st, int stage = 0, const uint16_t* o_in = nullptr,
+              const uint16_t* h_in = nullptr) {
   auto buf = [&](size_t off) { return reinterpret_cast<uint16_t*>(ws + off); };
   const size_t T = (size_t)d.T;
   const unsigned nrow = (unsigned)((d.T + 3) / 4);
   int rc;
-  hipLaunchKernelGGL(rmsnorm_kernel, dim3(nrow), dim3(256), 0, st, X, d.T, d.H, blk.norm1, buf(l.a));
-  W4_CHECK_LAUNCH();
-  if ((rc = run_linear(d, 0, buf(l.a), blk.wq, cand, buf(l.q), st))) return rc;
-  if ((rc = run_linear(d, 1, buf(l.a), blk.wk, cand, buf(l.k), st))) return rc;
-  if ((rc = run_linear(d, 2, buf(l.a), blk.wv, cand, buf(l.v), st))) return rc;
-  const float* cs = reinterpret_cast<const float*>(ws + l.cs);
-  const float* sn = reinterpret_cast<const float*>(ws + l.sn);
-  const long long qi = (long long)T * d.nq * 64, ki = (long long)T * d.nkv * 64;
-  hipLaunchKernelGGL(rope_kernel, dim3((unsigned)((qi + 255) / 256)), dim3(256), 0, st, buf(l.q), qi, d.nq, d.L, cs, sn);
-  W4_CHECK_LAUNCH();
-  hipLaunchKernelGGL(rope_kernel, dim3((unsigned)((ki + 255) / 256)), dim3(256), 0, st, buf(l.k), ki, d.nkv, d.L, cs, sn);
-  W4_CHECK_LAUNCH();
-  hipLaunchKernelGGL(attention_kernel, dim3((unsigned)((d.L + kAttnQ - 1) / kAttnQ), (unsigned)d.nq, (unsigned)d.B),
-                     dim3(256), 0, st, buf(l.q), buf(l.k), buf(l.v), d.L, d.nq, d.nkv, buf(l.o));
-  W4_CHECK_LAUNCH();
-  if ((rc = run_linear(d, 3, buf(l.o), blk.wo, cand, buf(l.p), st))) return rc;
-  if ((rc = ew_launch(EW_ADD, X, buf(l.p), T * d.H, buf(l.h), st))) return rc;
-  hipLaunchKernelGGL(rmsnorm_kernel, dim3(nrow), dim3(256), 0, st, buf(l.h), d.T, d.H, blk.norm2, buf(l.b2));
+  const uint16_t* o = stage >= 1 ? o_in : buf(l.o);
+  const uint16_t* h = stage >= 2 ? h_in : buf(l.h);
+  if (stage == 0) {
+    hipLaunchKernelGGL(rmsnorm_kernel, dim3(nrow), dim3(256), 0, st, X, d.T, d.H, blk.norm1, buf(l.a));
+    W4_CHECK_LAUNCH();
+    if ((rc = run_linear(d, 0, buf(l.a), blk.wq, cand, buf(l.q), st))) return rc;
+    if ((rc = run_linear(d, 1, buf(l.a), blk.wk, cand, buf(l.k), st))) return rc;
+    if ((rc = run_linear(d, 2, buf(l.a), blk.wv, cand, buf(l.v), st))) return rc;
+    const float* cs = reinterpret_cast<const float*>(ws + l.cs);
+    const float* sn = reinterpret_cast<const float*>(ws + l.sn);
+    const long long qi = (long long)T * d.nq * 64, ki = (long long)T * d.nkv * 64;
+    hipLaunchKernelGGL(rope_kernel, dim3((unsigned)((qi + 255) / 256)), dim3(256), 0, st, buf(l.q), qi, d.nq, d.L, cs,
+                       sn);
+    W4_CHECK_LAUNCH();
+    hipLaunchKernelGGL(rope_kernel, dim3((unsigned)((ki + 255) / 256)), dim3(256), 0, st, buf(l.k), ki, d.nkv, d.L,
+                       cs, sn);
+    W4_CHECK_LAUNCH();
+    hipLaunchKernelGGL(attention_kernel, dim3((unsigned)((d.L + kAttnQ - 1) / kAttnQ), (unsigned)d.nq, (unsigned)d.B),
+                       dim3(256), 0, st, buf(l.q), buf(l.k), buf(l.v), d.L, d.nq, d.nkv, buf(l.o));
+    W4_CHECK_LAUNCH();
+  }
+  if (stage <= 1) {
+    if ((rc = run_linear(d, 3, o, blk.wo, cand, buf(l.p), st))) return rc;
+    if ((rc = ew_launch(EW_ADD, X, buf(l.p), T * d.H, buf(l.h), st))) return rc;
+  }
+  hipLaunchKernelGGL(rmsnorm_kernel, dim3(nrow), dim3(256), 0, st, h, d.T, d.H, blk.norm2, buf(l.b2));
   W4_CHECK_LAUNCH();
   if ((rc = run_linear(d, 4, buf(l.b2), blk.wgate, cand, buf(l.gt), st))) return rc;
   if ((rc = run_linear(d, 5, buf(l.b2), blk.wup, cand, buf(l.up), st))) return rc;
   if ((rc = ew_launch(EW_SILU_MUL, buf(l.gt), buf(l.up), T * d.I, buf(l.m), st))) return rc;
   if ((rc = run_linear(d, 6, buf(l.m), blk.wdown, cand, buf(l.dn), st))) return rc;
-  return ew_launch(EW_ADD, buf(l.h), buf(l.dn), T * d.H, Y, st);
+  return ew_launch(EW_ADD, h, buf(l.dn), T * d.H, Y, st);
 }
 
 int rope_tables(const Dims& d, char* ws, const BlockLayout& l, hipStream_t st) {
@@ -425,7 +436,7 @@ Dims make_dims(int B, int L, int H, int nq, int nkv, int I) {
 
 struct LookLayout {
   BlockLayout blk;
-  size_t yref_i, yref_n, yc_i, yc_n, xs, qw, sc, qz, gemm, part, total;
+  size_t yref_i, yref_n, yc_i, yc_n, oref, href, xs, qw, sc, qz, gemm, part, total;
   size_t nparts;
 };
 
@@ -445,6 +456,8 @@ LookLayout look_layout(const Dims& d, int linear) {
   l.yref_n = take(T * d.H * 2);
   l.yc_i = take(T * d.H * 2);
   l.yc_n = take(T * d.H * 2);
+  l.oref = take(T * d.QD * 2);      // the scored block's reference attention output and
+  l.href = take(T * d.H * 2);       // post-attention residual: candidates start from them
   l.xs = take(T * K * 2);
   l.qw = take((size_t)N * (K / 8) * 4);
   l.sc = take((size_t)N * (K / kGroup) * 2);
@@ -497,6 +510,10 @@ int launch_lookahead_reference(const uint16_t* X, int B, int L, int H, int nq, i
   int rc = rope_tables(d, ws, l.blk, stream);
   if (rc) return rc;
   if ((rc = run_block(d, blk, X, buf(l.yref_i), nullptr, ws, l.blk, stream))) return rc;
+  if (hipMemcpyAsync(buf(l.oref), buf(l.blk.o), (size_t)d.T * d.QD * 2, hipMemcpyDeviceToDevice, stream) !=
+          hipSuccess ||
+      hipMemcpyAsync(buf(l.href), buf(l.blk.h), (size_t)d.T * d.H * 2, hipMemcpyDeviceToDevice, stream) != hipSuccess)
+    return W4_ERR_HIP;
   if (m) {
     // the block buffers still hold this block's activations: the linear's input
     const size_t in[7] = {l.blk.a, l.blk.a, l.blk.a, l.blk.o, l.blk.b2, l.blk.b2, l.blk.m};
@@ -539,7 +556,11 @@ int launch_lookahead_candidates(const uint16_t* X, int B, int L, int H, int nq, 
     q.qzeros = symmetric ? nullptr : reinterpret_cast<uint32_t*>(ws + l.qz);
     if ((rc = launch_quantize_pack(q, 1, stream))) return rc;
     Candidate cand{linear, S + (size_t)c * K, q.qweight, q.scales, q.qzeros, symmetric, buf(l.xs), ws + l.gemm};
-    if ((rc = run_block(d, blk, X, buf(l.yc_i), &cand, ws, l.blk, stream))) return rc;
+    // the block runs from the first op the candidate changes: o from the reference
+    // attention output, gate / up / down from the reference post-attention residual
+    const int stage = linear <= 2 ? 0 : linear == 3 ? 1 : 2;
+    if ((rc = run_block(d, blk, X, buf(l.yc_i), &cand, ws, l.blk, stream, stage, buf(l.oref), buf(l.href))))
+      return rc;
     if (next && (rc = run_block(d, *next, buf(l.yc_i), buf(l.yc_n), nullptr, ws, l.blk, stream))) return rc;
     const uint16_t* yc_n = next ? buf(l.yc_n) : buf(l.yc_i);
     hipLaunchKernelGGL(sqdiff_partial_kernel, dim3(pblocks), dim3(256), 0, stream, yc_n, ref_n, n, part);

@@ -101,104 +101,136 @@ __global__ __launch_bounds__(256) void rope_kernel(uint16_t* __restrict__ x, lon
   base[j + 64] = (uint16_t)f32_to_bf16_bits(x2 * c + x1 * s);
 }
 
-// Causal grouped-query attention.  Workgroup (query block of 64, query head, sequence),
-// 256 threads: 4 lanes per query, lane part u owns dims 32 u .. 32 u + 31 of q and of
-// the output.  Keys and values of the query head's key/value head go through LDS in
-// chunks of 32 keys (fp32; part u of a key at float offset 36 u, so the four parts'
-// 16-byte reads fall in different banks); each query keeps an online softmax
-// (running max and sum) in fp32.
-constexpr int kAttnQ = 64, kAttnK = 32, kAttnRow = 4 * 36;
-__global__ __launch_bounds__(256) void attention_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ Kx,
-                                                        const uint16_t* __restrict__ V, int L, int n_q, int n_kv,
-                                                        uint16_t* __restrict__ O) {
-  __shared__ __align__(16) float ks[kAttnK * kAttnRow];
-  __shared__ __align__(16) float vs[kAttnK * kAttnRow];
-  const int qb = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
-  const int kvh = h / (n_q / n_kv);
+// Causal grouped-query attention on the matrix cores.  Workgroup (block of 128
+// queries, query head, sequence), 4 waves of 32 queries.  Per block of 32 keys a wave
+// computes the transposed scores S^T = K Q^T (8 v_mfma_f32_32x32x16_bf16 over the 128
+// dims: lane (query l % 32, half h) receives the scores of keys (r % 4) + 4 h + 8 (r / 4),
+// r = 0..15), updates its query's running max and sum (the two halves of a query swap
+// their partial max and sum), and accumulates O^T += V^T P^T (8 MFMAs: 4 blocks of 32
+// dims x 2 steps of 16 keys).  The P operand of step s, element j is the lane's own
+// score register 8 s + j, i.e. key j % 4 + 4 h + 16 s + 8 (j / 4); V^T is staged with its
+// keys in that order (key bits 2 and 3 swapped), so no value crosses lanes.  K rows
+// (272 B) and V^T rows (80 B) are padded so that 16 lanes' 16-byte reads hit distinct
+// banks.  Softmax in fp32: p = exp(s / sqrt(128) - m), entering the products as bf16
+// hi + lo (16 bits of p, so rounding p adds no error of its own beyond the output's
+// bf16 rounding), the output divided by the sum.
+constexpr int kFaQ = 128, kFaK = 32, kFaKRow = 136, kFaVRow = 40;   // rows in bf16 elements
+__global__ __launch_bounds__(256) void attention_mfma_kernel(const uint16_t* __restrict__ Q,
+                                                             const uint16_t* __restrict__ Kx,
+                                                             const uint16_t* __restrict__ V, int L, int n_q,
+                                                             int n_kv, uint16_t* __restrict__ O) {
+  __shared__ __align__(16) uint16_t ks[kFaK * kFaKRow];
+  __shared__ __align__(16) uint16_t vt[kHd * kFaVRow];
+  const int qb = blockIdx.x, hq = blockIdx.y, b = blockIdx.z;
+  const int kvh = hq / (n_q / n_kv);
   const int tid = threadIdx.x;
-  const int qi = tid >> 2, u = tid & 3;
-  const int t = qb * kAttnQ + qi;                    // query position in the sequence
-  const bool live = t < L;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int h = lane >> 5, l32 = lane & 31;
   const size_t qstride = (size_t)n_q * kHd, kstride = (size_t)n_kv * kHd;
   const size_t tok0 = (size_t)b * L;
-  float q[32], o[32];
+  const int q0 = qb * kFaQ + wave * 32;                 // this wave's first query
+  const int qpos = q0 + l32;                            // this lane's query
+  const int qmax = min(q0 + 31, L - 1);                 // the wave's last live query
+  bf16x8 qf[8];
   {
-    const uint16_t* qp = Q + (tok0 + (live ? t : 0)) * qstride + (size_t)h * kHd + 32 * u;
+    const uint16_t* qp = Q + (tok0 + min(qpos, L - 1)) * qstride + (size_t)hq * kHd + 8 * h;
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const uint4 v = *reinterpret_cast<const uint4*>(qp + 8 * c);
-      const uint32_t d[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        q[8 * c + 2 * e] = __uint_as_float(d[e] << 16);
-        q[8 * c + 2 * e + 1] = __uint_as_float(d[e] & 0xFFFF0000u);
-      }
-    }
-#pragma unroll
-    for (int e = 0; e < 32; ++e) o[e] = 0.0f;
+    for (int st = 0; st < 8; ++st) qf[st] = *reinterpret_cast<const bf16x8*>(qp + 16 * st);
   }
+  f32x16 acc[4];
+#pragma unroll
+  for (int db = 0; db < 4; ++db) acc[db] = f32x16{};
   const float scale = 1.0f / sqrtf((float)kHd);
   float mx = -INFINITY, sum = 0.0f;
-  const int kend = min(L, (qb + 1) * kAttnQ);        // keys this block needs: 0 .. kend-1
-  for (int k0 = 0; k0 < kend; k0 += kAttnK) {
+  const int kend = min(L, qb * kFaQ + kFaQ);            // keys the workgroup needs: 0 .. kend-1
+  for (int kb = 0; kb < kend; kb += kFaK) {
     __syncthreads();
-    // stage 32 keys x 128 dims of k and v: thread -> (key tid / 8, 16 dims at 16 (tid % 8))
+    // stage: thread -> (key tid / 8, dims 16 (tid % 8) .. +15) of K and of V
     {
       const int kj = tid >> 3, part = tid & 7;
-      const int key = k0 + kj;
-      const bool ok = key < kend;
-      const size_t src = (tok0 + (ok ? key : 0)) * kstride + (size_t)kvh * kHd + 16 * part;
-      float* kd = &ks[kj * kAttnRow + 36 * (part >> 1) + 16 * (part & 1)];
-      float* vd = &vs[kj * kAttnRow + 36 * (part >> 1) + 16 * (part & 1)];
+      const int key = kb + kj;
+      uint4 k0 = make_uint4(0u, 0u, 0u, 0u), k1 = k0, v0 = k0, v1 = k0;
+      if (key < kend) {
+        const size_t src = (tok0 + key) * kstride + (size_t)kvh * kHd + 16 * part;
+        k0 = *reinterpret_cast<const uint4*>(Kx + src);
+        k1 = *reinterpret_cast<const uint4*>(Kx + src + 8);
+        v0 = *reinterpret_cast<const uint4*>(V + src);
+        v1 = *reinterpret_cast<const uint4*>(V + src + 8);
+      }
+      *reinterpret_cast<uint4*>(&ks[kj * kFaKRow + 16 * part]) = k0;
+      *reinterpret_cast<uint4*>(&ks[kj * kFaKRow + 16 * part + 8]) = k1;
+      const int slot = (kj & ~12) | ((kj & 4) << 1) | ((kj & 8) >> 1);    // key bits 2 and 3 swapped
+      const uint32_t w[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
 #pragma unroll
-      for (int c = 0; c < 2; ++c) {
-        const uint4 kv4 = *reinterpret_cast<const uint4*>(Kx + src + 8 * c);
-        const uint4 vv4 = *reinterpret_cast<const uint4*>(V + src + 8 * c);
-        const uint32_t dk[4] = {kv4.x, kv4.y, kv4.z, kv4.w};
-        const uint32_t dv[4] = {vv4.x, vv4.y, vv4.z, vv4.w};
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          kd[8 * c + 2 * e] = __uint_as_float(dk[e] << 16);
-          kd[8 * c + 2 * e + 1] = __uint_as_float(dk[e] & 0xFFFF0000u);
-          vd[8 * c + 2 * e] = __uint_as_float(dv[e] << 16);
-          vd[8 * c + 2 * e + 1] = __uint_as_float(dv[e] & 0xFFFF0000u);
-        }
+      for (int e = 0; e < 8; ++e) {
+        vt[(16 * part + 2 * e) * kFaVRow + slot] = (uint16_t)(w[e] & 0xFFFFu);
+        vt[(16 * part + 2 * e + 1) * kFaVRow + slot] = (uint16_t)(w[e] >> 16);
       }
     }
     __syncthreads();
-    const int nk = min(kAttnK, kend - k0);
-    for (int kj = 0; kj < nk; ++kj) {
-      const int key = k0 + kj;
-      const float* kr = &ks[kj * kAttnRow + 36 * u];
-      float d = 0.0f;
+    if (kb > qmax) continue;                            // every query of this wave precedes these keys
+    f32x16 sc = f32x16{};
 #pragma unroll
-      for (int e = 0; e < 32; ++e) d = fmaf(q[e], kr[e], d);
-      // the 4 parts of a query sit in consecutive lanes: (0+1) + (2+3), the same in all four
-      d = d + __shfl_xor(d, 1, kWave);
-      d = d + __shfl_xor(d, 2, kWave);
-      if (!live || key > t) continue;                // causal: keys after the query are skipped
-      const float sc = d * scale;
-      const float mnew = fmaxf(mx, sc);
-      const float corr = expf(mx - mnew);            // 0 for the first key (mx = -inf)
-      const float p = expf(sc - mnew);
-      sum = sum * corr + p;
-      const float* vr = &vs[kj * kAttnRow + 36 * u];
+    for (int st = 0; st < 8; ++st) {
+      const bf16x8 kf = *reinterpret_cast<const bf16x8*>(&ks[l32 * kFaKRow + 16 * st + 8 * h]);
+      sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[st], sc, 0, 0, 0);
+    }
+    float mloc = -INFINITY;
 #pragma unroll
-      for (int e = 0; e < 32; ++e) o[e] = fmaf(p, vr[e], o[e] * corr);
-      mx = mnew;
+    for (int r = 0; r < 16; ++r) {
+      const int key = kb + (r & 3) + 4 * h + 8 * (r >> 2);
+      const float v = (key <= qpos && key < L) ? sc[r] * scale : -INFINITY;
+      sc[r] = v;
+      mloc = fmaxf(mloc, v);
+    }
+    mloc = fmaxf(mloc, __shfl_xor(mloc, 32, kWave));
+    const float mnew = fmaxf(mx, mloc);                 // finite: key 0 is in every query's first block
+    const float corr = expf(mx - mnew);
+    float lsum = 0.0f;
+    uint32_t pb[8], pl[8];          // p as bf16 hi + lo (the pair carries 16 bits of p)
+#pragma unroll
+    for (int r = 0; r < 16; r += 2) {
+      const float p0 = expf(sc[r] - mnew), p1 = expf(sc[r + 1] - mnew);
+      lsum = lsum + p0;
+      lsum = lsum + p1;
+      const bf16x2 pp = {(__bf16)p0, (__bf16)p1};
+      pb[r >> 1] = __builtin_bit_cast(uint32_t, pp);
+      const bf16x2 pq = {(__bf16)(p0 - __uint_as_float(pb[r >> 1] << 16)),
+                         (__bf16)(p1 - __uint_as_float(pb[r >> 1] & 0xFFFF0000u))};
+      pl[r >> 1] = __builtin_bit_cast(uint32_t, pq);
+    }
+    lsum = lsum + __shfl_xor(lsum, 32, kWave);
+    sum = sum * corr + lsum;
+    mx = mnew;
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[db][r] = acc[db][r] * corr;
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2) {
+      const bf16x8 pf = __builtin_bit_cast(bf16x8, make_uint4(pb[4 * s2], pb[4 * s2 + 1], pb[4 * s2 + 2], pb[4 * s2 + 3]));
+      const bf16x8 pg = __builtin_bit_cast(bf16x8, make_uint4(pl[4 * s2], pl[4 * s2 + 1], pl[4 * s2 + 2], pl[4 * s2 + 3]));
+#pragma unroll
+      for (int db = 0; db < 4; ++db) {
+        const bf16x8 vf = *reinterpret_cast<const bf16x8*>(&vt[(32 * db + l32) * kFaVRow + 16 * s2 + 8 * h]);
+        acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf, acc[db], 0, 0, 0);
+        acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pg, acc[db], 0, 0, 0);
+      }
     }
   }
-  if (!live) return;
+  if (qpos >= L) return;
   const float inv = 1.0f / sum;
-  uint16_t* op = O + (tok0 + t) * qstride + (size_t)h * kHd + 32 * u;
+  uint16_t* op = O + (tok0 + qpos) * qstride + (size_t)hq * kHd;
 #pragma unroll
-  for (int c = 0; c < 4; ++c) {
-    uint32_t w[4];
+  for (int db = 0; db < 4; ++db)
 #pragma unroll
-    for (int e = 0; e < 4; ++e)
-      w[e] = f32_to_bf16_bits(o[8 * c + 2 * e] * inv) | (f32_to_bf16_bits(o[8 * c + 2 * e + 1] * inv) << 16);
-    *reinterpret_cast<uint4*>(op + 8 * c) = make_uint4(w[0], w[1], w[2], w[3]);
-  }
+    for (int i = 0; i < 4; ++i) {
+      const int d0 = 32 * db + 8 * i + 4 * h;          // registers 4 i .. 4 i + 3: dims d0 .. d0 + 3
+      const uint32_t lo = f32_to_bf16_bits(acc[db][4 * i] * inv) | (f32_to_bf16_bits(acc[db][4 * i + 1] * inv) << 16);
+      const uint32_t hi = f32_to_bf16_bits(acc[db][4 * i + 2] * inv) | (f32_to_bf16_bits(acc[db][4 * i + 3] * inv) << 16);
+      *reinterpret_cast<uint2*>(op + d0) = make_uint2(lo, hi);
+    }
 }
 
 // Elementwise over n bf16 values (n % 8 == 0), 8 per thread.
@@ -396,7 +428,7 @@ int run_block(const Dims& d, const w4_block& blk, const uint16_t* X, uint16_t* Y
     hipLaunchKernelGGL(rope_kernel, dim3((unsigned)((ki + 255) / 256)), dim3(256), 0, st, buf(l.k), ki, d.nkv, d.L,
                        cs, sn);
     W4_CHECK_LAUNCH();
-    hipLaunchKernelGGL(attention_kernel, dim3((unsigned)((d.L + kAttnQ - 1) / kAttnQ), (unsigned)d.nq, (unsigned)d.B),
+    hipLaunchKernelGGL(attention_mfma_kernel, dim3((unsigned)((d.L + kFaQ - 1) / kFaQ), (unsigned)d.nq, (unsigned)d.B),
                        dim3(256), 0, st, buf(l.q), buf(l.k), buf(l.v), d.L, d.nq, d.nkv, buf(l.o));
     W4_CHECK_LAUNCH();
   }

@@ -22,11 +22,16 @@
  *   - bf16 values are passed as uint16_t bit patterns.
  *   - Array pointers are DEVICE pointers owned by the caller unless a parameter
  *     says "host".  The library never frees caller memory and never allocates
- *     device memory, except awq_search, which allocates its workspace itself
- *     when the caller passes none (see there).
+ *     device memory, except: awq_search and awq_search_lookahead allocate their
+ *     workspace themselves when the caller passes none (see there); the
+ *     decoder-block calls (w4_block_forward, awq_lookahead_loss,
+ *     awq_search_lookahead) run their unquantized bf16 projections through
+ *     rocBLAS, whose handle (one per device, created on first use, with its own
+ *     device workspace) the library keeps until the process ends.
  *   - `stream` is a hipStream_t (NULL = the default stream).  Work is enqueued
  *     asynchronously on it; results are ready once the stream is synchronized.
- *     awq_search is the one call that synchronizes (it reads losses on the host).
+ *     awq_search and awq_search_lookahead are the calls that synchronize (they
+ *     read losses on the host).
  *   - Arguments are validated on the host before any HIP call; a failing check
  *     returns a negative w4_status and enqueues nothing.  No call aborts or prints.
  *   - Weight layout: W is [N][K] row-major (output channels x input channels,
@@ -271,7 +276,7 @@ typedef struct w4_block {
  *   query head h reading key/value head h / (n_q / n_kv); h1 = x + o Wo^T;
  *   b = rmsnorm(h1) * norm2; y = h1 + (silu(b Wg^T) * (b Wu^T)) Wd^T.  No biases,
  *   no per-head q/k norms.  Every op computes in fp32 and stores bf16 (nearest
- *   even); the linears run on the matrix cores.
+ *   even); the projections are bf16 GEMMs with fp32 accumulation (rocBLAS).
  *   H and I multiples of 128; n_kv >= 1 divides n_q; B, L >= 1.
  *   Workspace: size query as in w4a16_gemm (about 2 B L (5 H + 3 I + 2 128 n_q +
  *   2 128 n_kv) bytes).

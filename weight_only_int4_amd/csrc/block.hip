@@ -18,11 +18,14 @@
 //   a = rmsnorm(x, g1); q, k, v = a Wq^T, a Wk^T, a Wv^T; q, k = rope(q), rope(k);
 //   o = attention(q, k, v); h = x + o Wo^T; b = rmsnorm(h, g2);
 //   m = silu(b Wg^T) * (b Wu^T); y = h + m Wd^T.
-// The linears run on the MFMA core with bf16 weights; a candidate linear runs as
-// deployed: bf16(input / s) against its int4 codes Q(W diag(s), r) on the int4 GEMM.
+// The unquantized projections are plain bf16 GEMMs (rocBLAS, fp32 accumulation); a
+// candidate linear runs as deployed: bf16(input / s) against its int4 codes
+// Q(W diag(s), r) on the library's int4 GEMM.
 #include <math.h>
+#include <rocblas/rocblas.h>
 
 #include <algorithm>
+#include <mutex>
 
 #include "internal.hpp"
 
@@ -386,6 +389,30 @@ int ew_launch(int op, const uint16_t* A, const uint16_t* B, size_t n, uint16_t* 
   return W4_OK;
 }
 
+// rocBLAS handle per device, created on first use and kept for the process.
+rocblas_handle blas_handle() {
+  static rocblas_handle handles[64] = {};
+  static std::mutex mu;
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
+  std::lock_guard<std::mutex> guard(mu);
+  if (!handles[dev] && rocblas_create_handle(&handles[dev]) != rocblas_status_success) handles[dev] = nullptr;
+  return handles[dev];
+}
+
+// Y [T][N] = bf16(X W^T) for bf16 X [T][K] and W [N][K]: a plain library GEMM
+// (column-major view: Y^T = W^T-op(K x N) times X^T), fp32 accumulation.
+int bf16_linear(const uint16_t* X, int T, int K, int N, const uint16_t* W, uint16_t* Y, hipStream_t st) {
+  rocblas_handle hnd = blas_handle();
+  if (!hnd || rocblas_set_stream(hnd, st) != rocblas_status_success) return W4_ERR_HIP;
+  const float alpha = 1.0f, beta = 0.0f;
+  const rocblas_status rs =
+      rocblas_gemm_ex(hnd, rocblas_operation_transpose, rocblas_operation_none, N, T, K, &alpha, W,
+                      rocblas_datatype_bf16_r, K, X, rocblas_datatype_bf16_r, K, &beta, Y, rocblas_datatype_bf16_r, N,
+                      Y, rocblas_datatype_bf16_r, N, rocblas_datatype_f32_r, rocblas_gemm_algo_standard, 0, 0);
+  return rs == rocblas_status_success ? W4_OK : W4_ERR_HIP;
+}
+
 // One linear: Y [T][N] = bf16(X W^T), or the candidate's deployed int4 form.
 int run_linear(const Dims& d, int i, const uint16_t* X, const uint16_t* W, const Candidate* cand, uint16_t* Y,
                hipStream_t st) {
@@ -399,7 +426,7 @@ int run_linear(const Dims& d, int i, const uint16_t* X, const uint16_t* W, const
     return launch_gemm(cand->xs, d.T, K, N, cand->qweight, cand->scales, cand->qzeros, cand->symmetric, Y,
                        cand->gemm_ws, st);
   }
-  return launch_reference_gemm(X, d.T, K, N, W, Y, st);
+  return bf16_linear(X, d.T, K, N, W, Y, st);
 }
 
 // The block from a given stage: 0 = from its input X; 1 = from the attention output

@@ -33,16 +33,18 @@ __device__ __forceinline__ float row16_sum(float v) {
 }
 
 // One launch, two jobs (grid.z = problem c):
-//  * blocks [0, rs_blocks): one wave per row m < mpad.  Pass i covers channels
-//    512 i .. 512 i + 511: lane l loads 8 consecutive bf16 (16 bytes) at
-//    512 i + 8 l, so the 16 lanes of row r of the wave hold group 4 i + r; each
-//    lane sums its 8 values in fp32 (fixed order), the row adds its 16 lanes, and
-//    lane 16 r writes rsq[g][m] = the negated group sum split into three bf16
-//    parts (exact) and a zero (rows >= M: zeros).  When xp is set every lane also
-//    writes its 8 channels pair-arranged into xp (rows >= M: zeros).  All passes'
-//    loads are issued before the first sum.
-//  * the remaining blocks: one thread per (triple of groups t, column n < npad)
-//    writes szq[g][n] = scale bits | bf16(128 + z) << 16 (0 for n >= N).
+//  * blocks [0, rs_blocks): one wave per (row m < mpad, chunk of 4096 channels).
+//    Pass i covers channels 512 i .. 512 i + 511: lane l loads 8 consecutive bf16
+//    (16 bytes) at 512 i + 8 l, so the 16 lanes of row r of the wave hold group
+//    4 i + r; each lane sums its 8 values in fp32 (fixed order), the row adds its 16
+//    lanes, and lane 16 r writes rsq[g][m] = the negated group sum split into three
+//    bf16 parts (exact) and a zero (rows >= M: zeros).  When xp is set every lane
+//    also writes its 8 channels pair-arranged into xp (rows >= M: zeros).  The
+//    chunk's loads are issued before its first sum.
+//  * the remaining blocks: one thread per (column n < npad, block of 8 groups)
+//    writes szq[g][n] = scale bits | bf16(128 + z) << 16 (0 for n >= N); the 8
+//    zero points of the block are one packed word.
+constexpr int kPrepChunk = 8;                             // passes (4096 channels) per wave
 __global__ __launch_bounds__(256) void gemm_prep_kernel(const uint16_t* X, size_t x_stride, int M, int K, int mpad,
                                                         const uint16_t* scales, size_t sc_stride,
                                                         const uint32_t* qzeros, size_t qz_stride, int symmetric,
@@ -53,62 +55,59 @@ __global__ __launch_bounds__(256) void gemm_prep_kernel(const uint16_t* X, size_
   const int c = blockIdx.z;
   if ((int)blockIdx.x < rs_blocks) {
     const int lane = threadIdx.x & 63;
-    const int m = blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (m >= mpad) return;                                // uniform per wave
     const int passes = (K + 511) >> 9;
+    const int chunks = (passes + kPrepChunk - 1) / kPrepChunk;
+    const long long w = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int m = (int)(w / chunks);
+    if (m >= mpad) return;                                // uniform per wave
+    const int i0 = (int)(w % chunks) * kPrepChunk;
     const uint16_t* xrow = X + (size_t)c * x_stride + (size_t)m * K;
     uint16_t* prow = xp ? xp + (size_t)c * x_stride + (size_t)m * K : nullptr;
-    constexpr int kMaxPasses = 8;                         // 4096 channels per batch of passes
-    for (int i0 = 0; i0 < passes; i0 += kMaxPasses) {
-      uint4 v[kMaxPasses];
+    uint4 v[kPrepChunk];
 #pragma unroll
-      for (int j = 0; j < kMaxPasses; ++j) {
-        const int k = (i0 + j) * 512 + lane * 8;
-        v[j] = (i0 + j < passes && k < K && m < M) ? *reinterpret_cast<const uint4*>(xrow + k)
-                                                     : make_uint4(0u, 0u, 0u, 0u);
+    for (int j = 0; j < kPrepChunk; ++j) {
+      const int k = (i0 + j) * 512 + lane * 8;
+      v[j] = (i0 + j < passes && k < K && m < M) ? *reinterpret_cast<const uint4*>(xrow + k)
+                                                   : make_uint4(0u, 0u, 0u, 0u);
+    }
+#pragma unroll
+    for (int j = 0; j < kPrepChunk; ++j) {
+      const int i = i0 + j;
+      if (i >= passes) break;                             // uniform
+      const int k = i * 512 + lane * 8;
+      const uint32_t d[4] = {v[j].x, v[j].y, v[j].z, v[j].w};
+      float s = 0.0f;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) s += __uint_as_float(d[q] << 16) + __uint_as_float(d[q] & 0xFFFF0000u);
+      if (prow && k < K) {
+        uint32_t e[4];
+        pair_activations(d, e);
+        *reinterpret_cast<uint4*>(prow + k) = make_uint4(e[0], e[1], e[2], e[3]);
       }
-#pragma unroll
-      for (int j = 0; j < kMaxPasses; ++j) {
-        const int i = i0 + j;
-        if (i >= passes) break;                           // uniform
-        const int k = i * 512 + lane * 8;
-        const uint32_t d[4] = {v[j].x, v[j].y, v[j].z, v[j].w};
-        float s = 0.0f;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) s += __uint_as_float(d[q] << 16) + __uint_as_float(d[q] & 0xFFFF0000u);
-        if (prow && k < K) {
-          uint32_t e[4];
-          pair_activations(d, e);
-          *reinterpret_cast<uint4*>(prow + k) = make_uint4(e[0], e[1], e[2], e[3]);
-        }
-        s = row16_sum(s);
-        const int g = 4 * i + (lane >> 4);
-        if ((lane & 15) == 0 && g < G) {
-          uint32_t hi, mid, lo;
-          split3(-s, hi, mid, lo);
-          *reinterpret_cast<uint2*>(rsq + (size_t)c * rsq_stride + ((size_t)g * mpad + m) * 4) =
-              make_uint2(hi | (mid << 16), lo);
-        }
+      s = row16_sum(s);
+      const int g = 4 * i + (lane >> 4);
+      if ((lane & 15) == 0 && g < G) {
+        uint32_t hi, mid, lo;
+        split3(-s, hi, mid, lo);
+        *reinterpret_cast<uint2*>(rsq + (size_t)c * rsq_stride + ((size_t)g * mpad + m) * 4) =
+            make_uint2(hi | (mid << 16), lo);
       }
     }
   } else {
-    const int T3 = (G + 2) / 3;
+    const int GW = (G + 7) >> 3;
     const int npad = gemm_npad(N);
     const long long item = (long long)(blockIdx.x - rs_blocks) * 256 + threadIdx.x;
-    if (item >= (long long)npad * T3) return;
-    const int t = (int)(item / npad);
+    if (item >= (long long)npad * GW) return;
+    const int gw = (int)(item / npad);
     const int n = (int)(item % npad);
-    const int GW = (G + 7) >> 3;
-    for (int jj = 0; jj < 3; ++jj) {
-      const int g = 3 * t + jj;
+    uint32_t zw = 0x88888888u;                            // symmetric: z = 8 for every group
+    if (!symmetric && n < N) zw = qzeros[(size_t)c * qz_stride + (size_t)n * GW + gw];
+    const uint16_t* srow = scales + (size_t)c * sc_stride + (size_t)n * G;
+    for (int jj = 0; jj < 8; ++jj) {
+      const int g = 8 * gw + jj;
       if (g >= G) break;
       uint32_t v = 0;
-      if (n < N) {
-        const uint32_t scb = scales[(size_t)c * sc_stride + (size_t)n * G + g];
-        uint32_t z = 8;
-        if (!symmetric) z = (qzeros[(size_t)c * qz_stride + (size_t)n * GW + (g >> 3)] >> (4 * (g & 7))) & 0xFu;
-        v = scb | ((0x4300u | z) << 16);                      // bf16 0x4300 | z = 128 + z exactly
-      }
+      if (n < N) v = (uint32_t)srow[g] | ((0x4300u | ((zw >> (4 * jj)) & 0xFu)) << 16);   // bf16 0x4300 | z = 128 + z
       szq[(size_t)c * szq_stride + (size_t)g * npad + n] = v;
     }
   }
@@ -118,9 +117,10 @@ int launch_gemm_prep(const uint16_t* X, size_t x_stride, int M, int K, int mpad,
                      size_t sc_stride, const uint32_t* qzeros, size_t qz_stride, int symmetric, int N,
                      uint16_t* rsq, size_t rsq_stride, uint32_t* szq, size_t szq_stride, uint16_t* xp, int C,
                      hipStream_t stream) {
-  const int T3 = ((K >> 7) + 2) / 3;
-  const long long rs_blocks = ((long long)mpad + 3) / 4;
-  const long long sz_blocks = ((long long)gemm_npad(N) * T3 + 255) / 256;
+  const int GW = ((K >> 7) + 7) / 8;
+  const int chunks = (((K + 511) >> 9) + kPrepChunk - 1) / kPrepChunk;
+  const long long rs_blocks = ((long long)mpad * chunks + 3) / 4;
+  const long long sz_blocks = ((long long)gemm_npad(N) * GW + 255) / 256;
   if (rs_blocks + sz_blocks == 0) return W4_OK;
   if (rs_blocks + sz_blocks > 0x7FFFFFFFLL || C > 65535) return W4_ERR_SHAPE;
   hipLaunchKernelGGL(gemm_prep_kernel, dim3((unsigned)(rs_blocks + sz_blocks), 1, (unsigned)C), dim3(256), 0,

@@ -389,13 +389,16 @@ int ew_launch(int op, const uint16_t* A, const uint16_t* B, size_t n, uint16_t* 
   return W4_OK;
 }
 
-// rocBLAS handle per device, created on first use and kept for the process.
-rocblas_handle blas_handle() {
+// rocBLAS handle per device, created on first use and kept for the process.  The
+// handle carries the stream it enqueues on, so setting the stream and enqueueing the
+// GEMM happen under one lock (host threads calling on one device take turns; the GPU
+// work itself stays asynchronous).
+std::mutex blas_mu;
+
+rocblas_handle blas_handle_locked() {
   static rocblas_handle handles[64] = {};
-  static std::mutex mu;
   int dev = -1;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
-  std::lock_guard<std::mutex> guard(mu);
   if (!handles[dev] && rocblas_create_handle(&handles[dev]) != rocblas_status_success) handles[dev] = nullptr;
   return handles[dev];
 }
@@ -403,7 +406,8 @@ rocblas_handle blas_handle() {
 // Y [T][N] = bf16(X W^T) for bf16 X [T][K] and W [N][K]: a plain library GEMM
 // (column-major view: Y^T = W^T-op(K x N) times X^T), fp32 accumulation.
 int bf16_linear(const uint16_t* X, int T, int K, int N, const uint16_t* W, uint16_t* Y, hipStream_t st) {
-  rocblas_handle hnd = blas_handle();
+  std::lock_guard<std::mutex> guard(blas_mu);
+  rocblas_handle hnd = blas_handle_locked();
   if (!hnd || rocblas_set_stream(hnd, st) != rocblas_status_success) return W4_ERR_HIP;
   const float alpha = 1.0f, beta = 0.0f;
   const rocblas_status rs =

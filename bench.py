@@ -207,10 +207,12 @@ def measure_rotation(torch, launches, reps):
 
 
 def fused_sweep_launches(torch, w4, wl, packed, M):
-    """Variant of the sweep with the shared-input linears of a block launched as one
-    GEMV each: q|k|v (N = 4096) and gate|up (N = 12288), their packed rows
-    concatenated along N (contiguous in the N-major layout).  Four launches per
-    block: q|k|v, o, gate|up, down."""
+    """The decode step as a decoder runs it: the linears of a block that read the same
+    activations (q, k, v; gate, up) are one GEMV each over their packed rows stored
+    concatenated along N (contiguous in the N-major layout): q|k|v (N = 4096) and
+    gate|up (N = 12288), with the activation row of the block's first linear of the
+    group.  Four launches per block: q|k|v, o, gate|up, down; the same weight bytes
+    as one launch per linear."""
     by_block = {}
     for b, layer, K, N, qw, sc, qz in packed:
         by_block.setdefault(b, {})[layer] = (K, N, qw, sc, qz)
@@ -539,13 +541,15 @@ def main(argv=None):
         "dtype": "bf16 x int4 (fp32 accumulate)",
         "data": "synthetic (seeded; W ~ N(0,0.02) bf16, X ~ N(0,1) bf16)",
         "config": {"workload": f"decode sweep: {args.blocks} blocks x 7 linears of a hidden-2048 decoder block "
-                               f"(q,k,v,o,gate,up,down), M=1, asymmetric int4 g128, HIP-graph replay"},
+                               f"(q,k,v,o,gate,up,down), M=1, asymmetric int4 g128, the shared-input linears "
+                               f"launched together as a decoder runs them (q|k|v, o, gate|up, down: 4 GEMV "
+                               f"launches per block), HIP-graph replay"},
     }
     packed = []
     if not args.skip_step:
         log("packing decode-sweep weights")
         packed = pack_sweep(torch, w4, wl, args.blocks)
-        sweep = sweep_launches(torch, w4, wl, packed, 1)
+        sweep = fused_sweep_launches(torch, w4, wl, packed, 1)
         step_bytes = sum(l.nbytes for l in sweep)
         graph = capture_graph(torch, sweep)
 
@@ -586,11 +590,11 @@ def main(argv=None):
     if not args.step_only:
         rows = []
         if "sweeps" in want and packed:
-            log("decode sweep M=1, fused shared-input linears")
-            fs = fused_sweep_launches(torch, w4, wl, packed, 1)
+            log("decode sweep M=1, one launch per linear")
+            fs = sweep_launches(torch, w4, wl, packed, 1)
             g = capture_graph(torch, fs)
             ms = time_events(torch, g.replay, max(3, args.steps // 2))
-            rows.append(row_gemv("decode sweep M=1 fused q|k|v and gate|up (graph, variant)",
+            rows.append(row_gemv("decode sweep M=1, one GEMV launch per linear (graph)",
                                  sum(l.nbytes for l in fs), ms, {"launches": len(fs)}))
             del g, fs
             torch.cuda.empty_cache()

@@ -358,6 +358,21 @@ def test_grid_loss_small(sym):
     assert rel.max() <= 2e-3, rel.max()
 
 
+def test_grid_loss_full_size():
+    """The search workload at full size (T=4096, K=2048, N=6144): three candidates in the
+    launch configuration the search uses (alpha 0 and 0.3 at r = 1, alpha 0.3 at r = 0.85)."""
+    X, W = wl.awq_calibration()
+    m = O.act_mean_abs(X)
+    S = np.stack([O.awq_scales(m, 0.0), O.awq_scales(m, 0.3), O.awq_scales(m, 0.3)])
+    ratios = np.array([1.0, 1.0, 0.85], dtype=np.float32)
+    say("grid loss full size", X.shape, W.shape)
+    L = w4.awq_grid_loss(to_bf16(X), to_bf16(W), to_f32(S), to_f32(ratios), False)
+    torch.cuda.synchronize()
+    got = L.cpu().numpy().astype(np.float64)
+    want = O.grid_loss(X, W, S, ratios, False)
+    assert np.max(np.abs(got - want) / want) <= 2e-3, (got, want)
+
+
 def test_grid_loss_given_yref():
     X, W, S = _grid_inputs(200, 256, 130, 2)
     ratios = np.ones(S.shape[0], dtype=np.float32)

@@ -41,19 +41,22 @@ typedef int i32x4 __attribute__((ext_vector_type(4)));
 
 }  // namespace
 
-// One wave per activation row m.  Pass 1: absmax over the row (bf16 -> fp32 is
-// exact).  Pass 2: lane l handles 8 consecutive channels 8 (l + 64 i); the 16
-// lanes of each 16-lane row then cover one 128-channel group, whose code sum
-// lane 16 r writes to xsum.
-__global__ __launch_bounds__(64) void w4a8_quant_act_kernel(const uint16_t* X, int K, int8_t* Xq, float* sx,
-                                                             int32_t* xsum) {
+// One workgroup of 4 waves per activation row m.  Pass 1: absmax over the row (bf16
+// -> fp32 is exact; the waves combine through LDS).  Pass 2: thread t handles the 8
+// consecutive channels 8 (t + 256 i); the 16 lanes of each 16-lane row then cover one
+// 128-channel group, whose code sum the row's first lane writes to xsum.
+constexpr int kActThreads = 256;                        // 4 waves per activation row
+__global__ __launch_bounds__(kActThreads) void w4a8_quant_act_kernel(const uint16_t* X, int K, int8_t* Xq,
+                                                                     float* sx, int32_t* xsum) {
 #pragma clang fp contract(off)
+  __shared__ float wmax[kActThreads / kWave];
   const int m = blockIdx.x;
-  const int lane = threadIdx.x;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
   const int chunks = K >> 3;
   const uint16_t* xr = X + (size_t)m * K;
   float amax = 0.0f;
-  for (int c = lane; c < chunks; c += kWave) {
+  for (int c = tid; c < chunks; c += kActThreads) {
     const uint4 v = *reinterpret_cast<const uint4*>(xr + 8 * c);
     const uint32_t d[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
@@ -62,11 +65,16 @@ __global__ __launch_bounds__(64) void w4a8_quant_act_kernel(const uint16_t* X, i
   }
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off, kWave));
+  if (lane == 0) wmax[tid >> 6] = amax;
+  __syncthreads();
+#pragma unroll
+  for (int w = 0; w < kActThreads / kWave; ++w) amax = fmaxf(amax, wmax[w]);
   const float s = amax > 0.0f ? amax / 127.0f : 1.0f;
-  if (lane == 0) sx[m] = s;
+  if (tid == 0) sx[m] = s;
   const int G = K >> 7;
-  for (int c0 = 0; c0 < chunks; c0 += kWave) {
-    const int c = c0 + lane;
+  // thread t quantizes channels 8 (c0 + t) .. +7; 16 consecutive threads cover one group
+  for (int c0 = 0; c0 < chunks; c0 += kActThreads) {
+    const int c = c0 + tid;
     int part = 0;
     if (c < chunks) {
       const uint4 v = *reinterpret_cast<const uint4*>(xr + 8 * c);
@@ -84,8 +92,8 @@ __global__ __launch_bounds__(64) void w4a8_quant_act_kernel(const uint16_t* X, i
       *reinterpret_cast<uint2*>(Xq + (size_t)m * K + 8 * c) = make_uint2(packed[0], packed[1]);
     }
     part = row16_sum_i(part);
-    const int g = (c0 >> 4) + (lane >> 4);
-    if ((lane & 15) == 0 && g < G) xsum[(size_t)m * G + g] = part;
+    const int g = (c >> 4);
+    if ((lane & 15) == 0 && c < chunks && g < G) xsum[(size_t)m * G + g] = part;
   }
 }
 
@@ -238,7 +246,7 @@ W4a8Kernel w4a8_kernel_for(int ni) { return w4a8_pick(ni, std::make_integer_sequ
 int launch_w4a8_quantize(const uint16_t* X, int M, int K, int8_t* Xq, float* sx, int32_t* xsum,
                          hipStream_t stream) {
   if (M == 0) return W4_OK;
-  hipLaunchKernelGGL(w4a8_quant_act_kernel, dim3((unsigned)M), dim3(64), 0, stream, X, K, Xq, sx, xsum);
+  hipLaunchKernelGGL(w4a8_quant_act_kernel, dim3((unsigned)M), dim3(kActThreads), 0, stream, X, K, Xq, sx, xsum);
   W4_CHECK_LAUNCH();
   return W4_OK;
 }

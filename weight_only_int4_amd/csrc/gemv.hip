@@ -351,7 +351,11 @@ int gemv_blocks_per_cu(int threads) {
 }
 
 // Batches per workgroup: the fewest (1, 2, 4, 8 or 16) with which one round of
-// resident workgroups covers all rows, else 16 (then several rounds).
+// resident workgroups covers all rows.  Otherwise 4, 8 or 16, whichever gives the
+// busiest CU the least work: ceil(workgroups / CUs) x (batches + 2), the 2
+// standing for a workgroup's activation loads (measured at M = 8: K = 5120,
+// N = 17408 takes 8 -- 544 workgroups of 16 batches left 32 CUs a third one --
+// and K = 17408, N = 5120 keeps 16).
 template <int M, bool SYM>
 void launch_m(const GemvArgs& a, const GemvPlan& p, hipStream_t stream) {
   constexpr int R = gemv_rows(M);
@@ -371,8 +375,15 @@ void launch_m(const GemvArgs& a, const GemvPlan& p, hipStream_t stream) {
     go(gemv_instance<M, 4, SYM>(), 4);
   else if (fits(8, gemv_blocks_per_cu<M, 8, SYM>(threads)))
     go(gemv_instance<M, 8, SYM>(), 8);
-  else
-    go(gemv_instance<M, 16, SYM>(), 16);
+  else {
+    auto load = [&](int bpw) { return ((nb + bpw - 1) / bpw * p.splits + cus - 1) / cus * (bpw + 2); };
+    if (load(4) < load(8) && load(4) < load(16))
+      go(gemv_instance<M, 4, SYM>(), 4);
+    else if (load(8) < load(16))
+      go(gemv_instance<M, 8, SYM>(), 8);
+    else
+      go(gemv_instance<M, 16, SYM>(), 16);
+  }
 }
 
 template <int M>

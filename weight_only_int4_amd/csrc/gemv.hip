@@ -350,39 +350,58 @@ int gemv_blocks_per_cu(int threads) {
   return cache[slot];
 }
 
-// Batches per workgroup: the fewest (1, 2, 4, 8 or 16) with which one round of
-// resident workgroups covers all rows.  Otherwise 4, 8 or 16, whichever gives the
-// busiest CU the least work: ceil(workgroups / CUs) x (batches + 2), the 2
-// standing for a workgroup's activation loads (measured at M = 8: K = 5120,
-// N = 17408 takes 8 -- 544 workgroups of 16 batches left 32 CUs a third one --
-// and K = 17408, N = 5120 keeps 16).
+// Batches per workgroup.  Among 1, 2, 3, 4, 5, 6 and 8, those with which one round
+// of resident workgroups covers all rows; the fewest of them, unless another
+// gives the busiest CU at least 10% fewer batches (workgroups land unevenly on
+// the CUs when their count is not a multiple of the CU count: K = 17408,
+// N = 5120, M = 1 takes 5 -- 512 workgroups, two per CU -- over 4, whose 640
+// left half the CUs a third one: 12.1 -> 11.5 us).  When none fits, 4, 8 or 16,
+// whichever gives the busiest CU the least work: ceil(workgroups / CUs) x
+// (batches + 2), the 2 standing for a workgroup's activation loads (measured at
+// M = 8: K = 5120, N = 17408 takes 8 -- 544 workgroups of 16 batches left 32 CUs
+// a third one -- and K = 17408, N = 5120 keeps 16).
 template <int M, bool SYM>
 void launch_m(const GemvArgs& a, const GemvPlan& p, hipStream_t stream) {
   constexpr int R = gemv_rows(M);
   const int threads = p.nw * kWave;
   const long long nb = (a.N + R - 1) / R;
   const long long cus = device_cus();
-  auto go = [&](auto kernel, int bpw) {
-    const unsigned gx = (unsigned)((nb + bpw - 1) / bpw);
-    hipLaunchKernelGGL(kernel, dim3(gx, (unsigned)p.splits), dim3(threads), 0, stream, a);
+  auto wgs = [&](int bpw) { return (nb + bpw - 1) / bpw * p.splits; };
+  auto busiest = [&](int bpw) { return (wgs(bpw) + cus - 1) / cus * bpw; };
+  auto per_cu = [&](int bpw) {
+    switch (bpw) {
+      case 1: return gemv_blocks_per_cu<M, 1, SYM>(threads);
+      case 2: return gemv_blocks_per_cu<M, 2, SYM>(threads);
+      case 3: return gemv_blocks_per_cu<M, 3, SYM>(threads);
+      case 4: return gemv_blocks_per_cu<M, 4, SYM>(threads);
+      case 5: return gemv_blocks_per_cu<M, 5, SYM>(threads);
+      case 6: return gemv_blocks_per_cu<M, 6, SYM>(threads);
+      default: return gemv_blocks_per_cu<M, 8, SYM>(threads);
+    }
   };
-  auto fits = [&](int bpw, int per_cu) { return (nb + bpw - 1) / bpw * p.splits <= cus * per_cu; };
-  if (fits(1, gemv_blocks_per_cu<M, 1, SYM>(threads)))
-    go(gemv_instance<M, 1, SYM>(), 1);
-  else if (fits(2, gemv_blocks_per_cu<M, 2, SYM>(threads)))
-    go(gemv_instance<M, 2, SYM>(), 2);
-  else if (fits(4, gemv_blocks_per_cu<M, 4, SYM>(threads)))
-    go(gemv_instance<M, 4, SYM>(), 4);
-  else if (fits(8, gemv_blocks_per_cu<M, 8, SYM>(threads)))
-    go(gemv_instance<M, 8, SYM>(), 8);
-  else {
-    auto load = [&](int bpw) { return ((nb + bpw - 1) / bpw * p.splits + cus - 1) / cus * (bpw + 2); };
-    if (load(4) < load(8) && load(4) < load(16))
-      go(gemv_instance<M, 4, SYM>(), 4);
-    else if (load(8) < load(16))
-      go(gemv_instance<M, 8, SYM>(), 8);
-    else
-      go(gemv_instance<M, 16, SYM>(), 16);
+  int first = 0, best = 0;
+  for (int b : {1, 2, 3, 4, 5, 6, 8}) {
+    if (wgs(b) > cus * per_cu(b)) continue;
+    if (first == 0)
+      first = best = b;
+    else if (busiest(b) < busiest(best))
+      best = b;
+  }
+  if (first != 0 && 10 * busiest(best) > 9 * busiest(first)) best = first;
+  if (best == 0) {
+    auto load = [&](int bpw) { return (wgs(bpw) + cus - 1) / cus * (bpw + 2); };
+    best = load(4) < load(8) && load(4) < load(16) ? 4 : (load(8) < load(16) ? 8 : 16);
+  }
+  const dim3 grid((unsigned)((nb + best - 1) / best), (unsigned)p.splits);
+  switch (best) {
+    case 1: hipLaunchKernelGGL((gemv_instance<M, 1, SYM>()), grid, dim3(threads), 0, stream, a); break;
+    case 2: hipLaunchKernelGGL((gemv_instance<M, 2, SYM>()), grid, dim3(threads), 0, stream, a); break;
+    case 3: hipLaunchKernelGGL((gemv_instance<M, 3, SYM>()), grid, dim3(threads), 0, stream, a); break;
+    case 4: hipLaunchKernelGGL((gemv_instance<M, 4, SYM>()), grid, dim3(threads), 0, stream, a); break;
+    case 5: hipLaunchKernelGGL((gemv_instance<M, 5, SYM>()), grid, dim3(threads), 0, stream, a); break;
+    case 6: hipLaunchKernelGGL((gemv_instance<M, 6, SYM>()), grid, dim3(threads), 0, stream, a); break;
+    case 8: hipLaunchKernelGGL((gemv_instance<M, 8, SYM>()), grid, dim3(threads), 0, stream, a); break;
+    default: hipLaunchKernelGGL((gemv_instance<M, 16, SYM>()), grid, dim3(threads), 0, stream, a); break;
   }
 }
 

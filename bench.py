@@ -502,8 +502,8 @@ def main(argv=None):
                     help="counter calibration: run only a plain device copy of MIB MiB ten times and exit")
     args = ap.parse_args(argv)
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path (the kernels shard by output rows "
-              "with no exchange; see the sharding notes). Run with --gpus 1.", file=sys.stderr)
+        print("bench.py measures one GPU: the library has no multi-GPU path (the kernels would shard by "
+              "output rows with no exchange). Run with --gpus 1.", file=sys.stderr)
         return 2
 
     import torch

@@ -231,21 +231,23 @@ def test_gemv_large_full_size(shape, M):
     assert _elementwise_ok(y[:, cols], ref) == 0
 
 
-@pytest.mark.parametrize("M,N", [(1, 40000), (2, 40000), (4, 36000), (16, 30000)])
-def test_gemv_tall_random_codes(M, N):
-    """Tall K = 2048 linears: enough rows that every workgroup gets several row
-    batches (and, for the larger M, several rounds of workgroups).  The packed
-    operands are drawn directly (random codes, scales and zero words); oracle on
-    every 16th row."""
-    rng = np.random.default_rng(1000 + M)
-    K = 2048
+@pytest.mark.parametrize("M,K,N", [(1, 2048, 40000), (2, 2048, 40000), (4, 2048, 36000), (16, 2048, 30000),
+                                   (16, 2048, 4104), (8, 2048, 4104), (4, 2048, 8211), (8, 2048, 17942),
+                                   (1, 5120, 25601)])
+def test_gemv_tall_random_codes(M, K, N):
+    """Tall linears: enough rows that every workgroup gets several row batches
+    (and, for the larger M, several rounds of workgroups); the row counts are
+    picked so that the launch plan takes each of its batch counts (2, 3, 4, 5, 6,
+    8, 16 batches per workgroup) for some M.  The packed operands are drawn
+    directly (random codes, scales and zero words); oracle on every 16th row."""
+    rng = np.random.default_rng(1000 + M + N)
     qw = rng.integers(0, 2 ** 32, size=(N, K // 8), dtype=np.uint64).astype(np.uint32)
     sc = O.f32_to_bf16((np.abs(rng.standard_normal((N, K // 128))) * 2e-3 + 1e-4).astype(np.float32))
     qz = rng.integers(0, 2 ** 32, size=(N, (K // 128 + 7) // 8), dtype=np.uint64).astype(np.uint32)
     X = O.f32_to_bf16(rng.standard_normal((M, K)).astype(np.float32))
     rows = np.arange(0, N, 16)
     for sym in (False, True):
-        say("gemv tall", M, N, sym)
+        say("gemv tall", M, K, N, sym)
         Y = w4.w4a16_gemv(to_bf16(X), to_i32(qw), to_bf16(sc), None if sym else to_i32(qz), sym)
         torch.cuda.synchronize()
         y = bf16_values(bits16(Y))[:, rows]

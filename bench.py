@@ -6,8 +6,9 @@ One step is one decode sweep: the seven linears of a hidden-2048 decoder block
 (q 2048->2048, k/v 2048->1024, o 2048->2048, gate/up 2048->6144, down
 6144->2048) for 28 blocks, M = 1 bf16 activation row, asymmetric int4 group-128
 weights resident in HBM (734 MB of packed weights per sweep, more than the
-256 MB Infinity Cache, so every step streams them from HBM).  The step is
-replayed as one HIP graph of 196 GEMV launches.
+256 MB Infinity Cache, so every step streams them from HBM).  The linears that
+read the same activation row run as one GEMV (q|k|v, o, gate|up, down), as a
+decoder runs them: the step is replayed as one HIP graph of 112 GEMV launches.
 
 ``value`` is the sweep's algorithmic bytes (packed weights + bf16 scales +
 packed zeros + X + Y) divided by the wall time per step (TB/s).  The same JSON
@@ -15,7 +16,10 @@ line carries:
   * ``roofline`` of the dominant kernel (the GEMV): algorithmic bytes per launch
     over its average launch duration -- the event-timed graph replay (only GEMV
     launches, back to back on one stream) divided by the launches -- against
-    the 8 TB/s HBM peak;
+    the 8 TB/s HBM peak, with the latency floor: t0, the per-launch time of the
+    smallest GEMV (one row, one group, one output) replayed as a graph of as
+    many launches, and the step's latency-adjusted ceiling
+    sum(bytes / BW) / sum(t0 + bytes / BW), which no kernel of the sweep can beat;
   * ``rows``: every other step of the path measured in the same run (cold-cache
     GEMV on the 27B-shaped linears, decode sweeps at M = 4 and 16, prefill GEMM
     at M = 2048 and the 27B shapes, quantize + pack, the full 30-candidate AWQ
@@ -74,6 +78,28 @@ class Launch:
 
     def __call__(self):
         self.launcher()
+
+
+def latency_floor_us(torch, w4, launches):
+    """Per-launch time (us) of a graph of `launches` launches of the smallest GEMV:
+    M = 1, K = 128, N = 1 (one group, one output, 24 bytes of weights)."""
+    X = torch.zeros((1, GROUP), dtype=torch.bfloat16, device="cuda")
+    qw = torch.zeros((1, GROUP // 8), dtype=torch.int32, device="cuda")
+    sc = torch.ones((1, 1), dtype=torch.bfloat16, device="cuda")
+    qz = torch.zeros((1, 1), dtype=torch.int32, device="cuda")
+    ls = [Launch(w4.gemv_launcher(X, qw, sc, qz, False, torch.empty((1, 1), dtype=torch.bfloat16, device="cuda")),
+                 0, 0) for _ in range(launches)]
+    g = capture_graph(torch, ls)
+    ms = time_events(torch, g.replay, 20)
+    del g, ls
+    return ms * 1e3 / launches
+
+
+def latency_ceiling(t0_us, nbytes):
+    """Fraction of the HBM peak that a launch moving nbytes reaches at best when
+    every launch also costs t0."""
+    ideal_us = nbytes / (HBM_PEAK_GBS * 1e3)
+    return ideal_us / (t0_us + ideal_us)
 
 
 _SPACER = {}
@@ -546,6 +572,7 @@ def main(argv=None):
                                f"launches per block), HIP-graph replay"},
     }
     packed = []
+    t0 = None                       # latency floor per launch (us), measured with the step
     if not args.skip_step:
         log("packing decode-sweep weights")
         packed = pack_sweep(torch, w4, wl, args.blocks)
@@ -581,6 +608,12 @@ def main(argv=None):
                            "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                            "traffic": profiled_traffic(), "avg_launch_us": round(avg_launch_ms * 1e3, 3),
                            "bytes_per_launch": int(avg_bytes)}
+        t0 = latency_floor_us(torch, w4, len(sweep))
+        ideal_us = step_bytes / (HBM_PEAK_GBS * 1e3)
+        ceil_frac = ideal_us / (len(sweep) * t0 + ideal_us)
+        out["roofline"]["latency_floor"] = {"t0_us": round(t0, 3), "ceiling_frac": round(ceil_frac, 4),
+                                            "frac_of_ceiling": round(achieved / HBM_PEAK_GBS / ceil_frac, 4)}
+        log(f"latency floor: t0 {t0:.2f} us per launch, step ceiling {ceil_frac:.3f} of HBM peak")
         del graph, sweep
         torch.cuda.synchronize()
         torch.cuda.empty_cache()
@@ -623,6 +656,13 @@ def main(argv=None):
             if name in want:
                 log(f"rows: {name}")
                 rows += fn(torch, w4, wl, reps)
+        # single-GEMV rows: the best fraction of the HBM peak a launch of that size can
+        # reach when every launch also costs t0
+        gemv_rows = [r for r in rows if r["name"].startswith("gemv") and "bytes" in r]
+        if gemv_rows:
+            t0 = t0 if t0 is not None else latency_floor_us(torch, w4, 112)
+            for r in gemv_rows:
+                r["latency_ceiling_frac"] = round(latency_ceiling(t0, r["bytes"]), 4)
         out["rows"] = rows
         pre = [r for r in rows if r["name"].startswith("gemm prefill")]
         if pre:

@@ -150,7 +150,7 @@ namespace {
 // splits workgroups into one round of two resident workgroups on each of 256 CUs
 // (at least 2 below a full round), each split at least 4 groups long.  A function
 // of the shape only (the workspace size follows it).
-constexpr long long kSplitSlots = 2 * 256;
+constexpr long long kSplitSlots = kCoreSlots;
 
 int gemm_k_splits(int M, int K, int N) {
   const long long tiles = (long long)((N + kBN - 1) / kBN) * ((M + kBM - 1) / kBM);
@@ -237,7 +237,10 @@ int launch_gemm(const uint16_t* X, int M, int K, int N, const uint32_t* qweight,
   const long long tiles = (long long)((N + kBN - 1) / kBN) * ((M + kBM - 1) / kBM);
   if (tiles > 0x7FFFFFFFLL) return W4_ERR_SHAPE;
   const dim3 grid((unsigned)tiles, (unsigned)splits, 1);
-  hipLaunchKernelGGL((gemm_core_kernel<true, EPI_STORE>), grid, dim3(kGemmWaves * 64), 0, stream, a);
+  if (gemm_core_wide(tiles * splits))
+    hipLaunchKernelGGL((gemm_core_kernel<true, EPI_STORE, true>), grid, dim3(kGemmWaves * 64), 0, stream, a);
+  else
+    hipLaunchKernelGGL((gemm_core_kernel<true, EPI_STORE>), grid, dim3(kGemmWaves * 64), 0, stream, a);
   W4_CHECK_LAUNCH();
   if (splits > 1) {
     const size_t count = (size_t)M * N;

@@ -4,12 +4,13 @@
 //
 // Workgroup tile 64 x 128, 4 waves: wave w computes all 64 rows of columns
 // 32 w .. +31 as 2 v_mfma_f32_32x32x16_bf16 blocks, so every packed weight word is
-// expanded once per tile.  Two workgroups share a CU (75 KB of LDS each): while
-// one waits at its per-group barrier the other keeps the matrix cores busy.  One
-// main-loop step covers one 128-channel quantization group.
+// expanded once per tile.  Two or three workgroups share a CU (three stages of
+// 25 KB of LDS each, or two stages for three workgroups): while one waits at its
+// per-group barrier the others keep the matrix cores busy.  One main-loop step
+// covers one 128-channel quantization group.
 //
 // Every operand of a group travels from global memory straight into LDS
-// (global_load_lds: no registers), STAGES groups deep.  These copies are issued
+// (global_load_lds: no registers), one or two groups ahead.  These copies are issued
 // from inline assembly, so the compiler's wait-counter bookkeeping does not see
 // them: it would otherwise wait for every copy in flight, including those of
 // later groups, before each LDS read.  The kernel waits for exactly the copies of
@@ -123,16 +124,21 @@ __device__ __forceinline__ void lds_barrier() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
-// LDS byte layout of one pipeline stage.
-template <bool INT4>
+// LDS byte layout of one pipeline stage.  int4: three stages and two workgroups
+// per CU, or (WIDE) two stages and three workgroups per CU -- more waves to hide
+// latency, one group less of prefetch; the launchers take WIDE when the grid is
+// larger than one round of two workgroups per CU (measured, M = 2048: K = 2048,
+// N = 6144, 1536 tiles, 70.6 -> 66.8 us; K = 6144, N = 2048, 512 tiles, stays on
+// the three-stage kernel, which the wide one would slow from 69.8 to 76.5 us).
+template <bool INT4, bool WIDE = false>
 struct GemmSmem {
   static constexpr int kA = 0;                                   // activations, 16 KB
   static constexpr int kB = kBM * 256;                           // int4: packed words 8 KB; bf16: weights 32 KB
   static constexpr int kS = kB + (INT4 ? kBN * 64 : kBN * 256);  // int4: column words, 128 x 4 B
   static constexpr int kR = kS + (INT4 ? 512 : 0);                // int4: row sums, 64 x 8 B
   static constexpr int kStage = kR + (INT4 ? 512 : 0);
-  static constexpr int kStages = INT4 ? 3 : 2;
-  static constexpr int kBlocksPerCU = INT4 ? 2 : 1;
+  static constexpr int kStages = INT4 && !WIDE ? 3 : 2;
+  static constexpr int kBlocksPerCU = INT4 ? (WIDE ? 3 : 2) : 1;
   // copies issued per stage and wave (each moves 1 KB, or 256 B for the 4-byte
   // one): activations 4 + int4: packed words 2, column words or row sums 1;
   // bf16: weights 8
@@ -142,9 +148,16 @@ struct GemmSmem {
 
 constexpr int kGemmWaves = 4;
 
-template <bool INT4, int EPI>
-__global__ __launch_bounds__(kGemmWaves * 64, GemmSmem<INT4>::kBlocksPerCU) void gemm_core_kernel(GemmCoreArgs a) {
-  using SM = GemmSmem<INT4>;
+// Resident workgroups of the three-stage int4 kernel on 256 CUs; a larger grid
+// takes the WIDE kernel.
+constexpr long long kCoreSlots = 2 * 256;
+inline bool gemm_core_wide(long long workgroups) { return workgroups > kCoreSlots; }
+
+template <bool INT4, int EPI, bool WIDE = false>
+__global__ __launch_bounds__(kGemmWaves * 64, (GemmSmem<INT4, WIDE>::kBlocksPerCU)) void gemm_core_kernel(
+    GemmCoreArgs a) {
+  static_assert(INT4 || !WIDE, "the wide layout is for int4 weights");
+  using SM = GemmSmem<INT4, WIDE>;
   constexpr int S = SM::kStages;
   constexpr int D = S - 1;                 // prefetch distance in groups
   constexpr int L = SM::kCopies;
@@ -295,8 +308,11 @@ __global__ __launch_bounds__(kGemmWaves * 64, GemmSmem<INT4>::kBlocksPerCU) void
 
   const uint32_t nib_mask = opaque_vgpr(0x000F000Fu);
   // int4: what a lane needs of a group besides the activations -- its 8 packed
-  // words, its column word and the row sums of its two row blocks.  Read one group
-  // ahead (see the pipeline below), so no group starts on an LDS round trip.
+  // words, its column word and the row sums of its two row blocks.  Three stages:
+  // read one group ahead (see the pipeline below), so no group starts on an LDS
+  // round trip; two stages (WIDE): read at the start of the group, whose copies
+  // are the only ones complete at its barrier (the third workgroup on the CU
+  // covers the wait).
   struct GroupMisc {
     uint4 wv[2];
     uint32_t szw;
@@ -328,6 +344,7 @@ __global__ __launch_bounds__(kGemmWaves * 64, GemmSmem<INT4>::kBlocksPerCU) void
     for (int bm = 0; bm < 2; ++bm) af[0][bm] = frag(sa, bm, 0);
     if constexpr (INT4) {
       (void)sb;
+      if constexpr (D == 1) read_misc(st, gcur);
       const uint4* wv = gcur.wv;
       // zero-point step operands: k-slots 0..2 (lane half 0) hold the row sum parts
       // against 128 + z three times; every other slot is 0
@@ -346,7 +363,7 @@ __global__ __launch_bounds__(kGemmWaves * 64, GemmSmem<INT4>::kBlocksPerCU) void
 #pragma unroll
           for (int bm = 0; bm < 2; ++bm) af[(j + 1) & 1][bm] = frag(sa, bm, j + 1);
         }
-        if constexpr (j == 4) read_misc(st_next, gnext);
+        if constexpr (j == 4 && D == 2) read_misc(st_next, gnext);
         // keep the reads of step j+1 ahead of the MFMAs of step j (the scheduler
         // would otherwise sink each read next to its use and expose LDS latency)
         __builtin_amdgcn_sched_barrier(0);
@@ -384,7 +401,8 @@ __global__ __launch_bounds__(kGemmWaves * 64, GemmSmem<INT4>::kBlocksPerCU) void
       // this group's scale (columns past N have 0); its fold happens in step 0 of
       // the next group (or after the loop)
       sc_prev = sc_cur;
-      gcur = gnext;
+      if constexpr (D == 2) gcur = gnext;
+      (void)st_next;
     } else {
       bf16x8 bfc = frag(sb, wave, 0), bfn = bfc;
       __builtin_amdgcn_sched_barrier(0);
@@ -438,11 +456,12 @@ __global__ __launch_bounds__(kGemmWaves * 64, GemmSmem<INT4>::kBlocksPerCU) void
     copies_of_step(std::integral_constant<int, 7>{}, src, st);
   }
 
-  // int4: at the barrier of group g the copies still in flight are the
-  // activation copies of group g+1 (its other copies, issued first, are complete:
-  // every wave may read group g+1's GroupMisc during group g)
-  constexpr int kInFlight = INT4 ? 4 : (D - 1) * L;
-  if constexpr (INT4) {
+  // int4, three stages: at the barrier of group g the copies still in flight are
+  // the activation copies of group g+1 (its other copies, issued first, are
+  // complete: every wave may read group g+1's GroupMisc during group g).  Two
+  // stages: none (group g+1's copies are issued after this barrier).
+  constexpr int kInFlight = INT4 ? (D == 2 ? 4 : 0) : (D - 1) * L;
+  if constexpr (INT4 && D == 2) {
     wait_vmcnt<kInFlight>();
     lds_barrier();
     read_misc(smem, gcur);

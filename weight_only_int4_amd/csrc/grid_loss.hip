@@ -196,7 +196,10 @@ int launch_grid_loss(const uint16_t* X, int T, int K, int N, const uint16_t* W, 
   a.partials = part;
   dim3 grid = tile_grid;
   grid.z = (unsigned)C;
-  hipLaunchKernelGGL((gemm_core_kernel<true, EPI_SQDIFF>), grid, dim3(kGemmWaves * 64), 0, stream, a);
+  if (gemm_core_wide((long long)grid.x * grid.y * grid.z))
+    hipLaunchKernelGGL((gemm_core_kernel<true, EPI_SQDIFF, true>), grid, dim3(kGemmWaves * 64), 0, stream, a);
+  else
+    hipLaunchKernelGGL((gemm_core_kernel<true, EPI_SQDIFF>), grid, dim3(kGemmWaves * 64), 0, stream, a);
   W4_CHECK_LAUNCH();
 
   hipLaunchKernelGGL(loss_reduce_kernel, dim3((unsigned)C), dim3(64), 0, stream, part, L.tiles,

@@ -148,10 +148,18 @@ int w4a8_quantize_activations(const uint16_t* X, int M, int K, int8_t* Xq, float
  *   w4a8_quantize_activations; qweight/scales/qzeros as for w4a16_gemv.
  *   M > 16: W4_ERR_UNSUPPORTED; K above 51,200 channels (400 groups, 25 per
  *   wave of a 16-wave workgroup): W4_ERR_UNSUPPORTED.
+ *   workspace / workspace_bytes: as for w4a16_gemv.  When K has at least 64
+ *   groups and N is below 8,192 (fewer than two 16-column tiles per CU of
+ *   256), the groups are split among several workgroups per tile (ranges of at
+ *   least 16 groups, as many as bring the workgroups near two per CU) and the
+ *   workspace holds their fp32 partial sums
+ *   (splits x M x N x 4 bytes, added in split order by a second kernel before
+ *   the sx[m] scaling); otherwise the size is 0 and both may be NULL.  The size
+ *   depends only on (M, K, N).
  */
 int w4a8_gemv(const int8_t* Xq, const float* sx, const int32_t* xsum, int M, int K, int N,
               const uint32_t* qweight, const uint16_t* scales, const uint32_t* qzeros, int symmetric,
-              int group_size, uint16_t* Y, void* stream);
+              int group_size, uint16_t* Y, void* workspace, size_t* workspace_bytes, void* stream);
 
 /*
  * w4a16_gemm -- prefill contraction Y = X W_hat^T for any M >= 1 (intended for

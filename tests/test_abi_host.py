@@ -97,16 +97,28 @@ def test_w4a8_validation(lib):
     assert f(MIS, 1, 256, A, A, A, None) == -3
     assert f(A, 0, 256, A, A, A, None) == 0                         # M = 0: empty
     g = lib.w4a8_gemv
-    assert g(A, A, A, 17, 256, 8, A, A, A, 0, 128, A, None) == -4
-    assert g(A, A, A, 1, 200, 8, A, A, A, 0, 128, A, None) == -2
-    assert g(A, A, A, 1, 256, 8, A, A, A, 0, 64, A, None) == -4
-    assert g(A, A, A, 1, 51328, 8, A, A, A, 0, 128, A, None) == -4   # 401 groups: beyond the unrolled kernels
-    assert g(None, A, A, 1, 256, 8, A, A, A, 0, 128, A, None) == -1
-    assert g(A, A, None, 1, 256, 8, A, A, A, 0, 128, A, None) == -1
-    assert g(A, A, A, 1, 256, 8, A, A, None, 0, 128, A, None) == -1  # asymmetric needs qzeros
-    assert g(A, A, A, 1, 256, 8, A, A, A, 1, 128, A, None) == -1     # symmetric forbids them
-    assert g(MIS, A, A, 1, 256, 8, A, A, A, 0, 128, A, None) == -3
-    assert g(A, A, A, 0, 256, 8, A, A, A, 0, 128, A, None) == 0
+    assert g(A, A, A, 17, 256, 8, A, A, A, 0, 128, A, None, None, None) == -4
+    assert g(A, A, A, 1, 200, 8, A, A, A, 0, 128, A, None, None, None) == -2
+    assert g(A, A, A, 1, 256, 8, A, A, A, 0, 64, A, None, None, None) == -4
+    assert g(A, A, A, 1, 51328, 8, A, A, A, 0, 128, A, None, None, None) == -4   # 401 groups: beyond the unrolled kernels
+    assert g(None, A, A, 1, 256, 8, A, A, A, 0, 128, A, None, None, None) == -1
+    assert g(A, A, None, 1, 256, 8, A, A, A, 0, 128, A, None, None, None) == -1
+    assert g(A, A, A, 1, 256, 8, A, A, None, 0, 128, A, None, None, None) == -1  # asymmetric needs qzeros
+    assert g(A, A, A, 1, 256, 8, A, A, A, 1, 128, A, None, None, None) == -1     # symmetric forbids them
+    assert g(MIS, A, A, 1, 256, 8, A, A, A, 0, 128, A, None, None, None) == -3
+    assert g(A, A, A, 0, 256, 8, A, A, A, 0, 128, A, None, None, None) == 0
+    # K split (at least 64 groups, fewer than 512 column tiles): fp32 partials per split
+    sz = ctypes.c_size_t(0)
+    assert g(None, None, None, 1, 8192, 2048, None, None, None, 0, 128, None, None, ctypes.byref(sz), None) == 0
+    assert sz.value == 4 * 1 * 2048 * 4                  # 64 groups in 4 ranges of 16
+    assert g(None, None, None, 16, 17408, 5120, None, None, None, 1, 128, None, None, ctypes.byref(sz), None) == 0
+    assert sz.value == 2 * 16 * 5120 * 4                 # 136 groups in 2 ranges of 68
+    for K, N in ((5120, 17408), (6144, 2048), (8064, 64)):   # enough tiles, or under 64 groups: no split
+        assert g(None, None, None, 4, K, N, None, None, None, 0, 128, None, None, ctypes.byref(sz), None) == 0
+        assert sz.value == 0
+    assert g(A, A, A, 1, 8192, 2048, A, A, A, 0, 128, A, None, None, None) == -5
+    small = ctypes.c_size_t(4 * 2048 * 4 - 1)
+    assert g(A, A, A, 1, 8192, 2048, A, A, A, 0, 128, A, A, ctypes.byref(small), None) == -5
 
 
 def test_gemm_size_query(lib):

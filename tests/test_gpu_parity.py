@@ -428,7 +428,7 @@ def test_w4a8_quantize_activations_bit_exact(M, K):
 
 
 @pytest.mark.parametrize("M,K,N", [(1, 2048, 300), (4, 2048, 129), (16, 2048, 64), (7, 128, 33), (2, 6144, 17),
-                                   (16, 17408, 40), (1, 5120, 1000), (9, 4224, 31), (3, 51200, 20)])
+                                   (16, 17408, 40), (1, 5120, 1000), (9, 4224, 31), (3, 51200, 20), (5, 9344, 100)])
 @pytest.mark.parametrize("sym", [False, True])
 def test_w4a8_gemv(M, K, N, sym):
     say("w4a8 gemv", M, K, N, sym)

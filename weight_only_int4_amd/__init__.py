@@ -50,7 +50,7 @@ _SIGNATURES = {
     "w4_probe_stream_read": ([_vp, ctypes.c_size_t, _i, _i, _i, _vp, _vp], _i),
     "w4_probe_empty": ([_vp], _i),
     "w4a8_quantize_activations": ([_vp, _i, _i, _vp, _vp, _vp, _vp], _i),
-    "w4a8_gemv": ([_vp, _vp, _vp, _i, _i, _i, _vp, _vp, _vp, _i, _i, _vp, _vp], _i),
+    "w4a8_gemv": ([_vp, _vp, _vp, _i, _i, _i, _vp, _vp, _vp, _i, _i, _vp, _vp, _sz, _vp], _i),
     "awq_clip_search": ([_vp, _i, _i, _i, _vp, _vp, _vp, _i, _i, _i, _vp, _vp, _vp, _sz, _vp], _i),
     "w4_block_forward": ([_vp, _i, _i, _i, _i, _i, _i, _bp, _vp, _vp, _sz, _vp], _i),
     "awq_lookahead_loss": ([_vp, _i, _i, _i, _i, _i, _i, _bp, _bp, _i, _vp, _vp, _i, _i, _i, _vp, _vp, _vp, _sz, _vp],
@@ -216,19 +216,29 @@ def _w4a8_args(Xq, sx, xsum, qweight, scales, qzeros, symmetric):
     return M, K, N
 
 
-def w4a8_gemv(Xq, sx, xsum, qweight, scales, qzeros=None, symmetric: bool = False, Y=None):
+def _w4a8_workspace(lib, M, K, N, symmetric, device, workspace):
+    def q(sz):
+        return lib.w4a8_gemv(None, None, None, M, K, N, None, None, None, int(symmetric), GROUP_SIZE, None, None,
+                             sz, None)
+
+    return _workspace(q, device, workspace)
+
+
+def w4a8_gemv(Xq, sx, xsum, qweight, scales, qzeros=None, symmetric: bool = False, Y=None, workspace=None):
     """W4A8 decode GEMV: Y [M][N] bf16 from int8 activations (w4a8_quantize_activations)."""
     lib = load_library()
     M, K, N = _w4a8_args(Xq, sx, xsum, qweight, scales, qzeros, symmetric)
     dev = Xq.device
     if Y is None:
         Y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    ws, wsb = _w4a8_workspace(lib, M, K, N, symmetric, dev, workspace)
     _check(lib.w4a8_gemv(_ptr(Xq), _ptr(sx), _ptr(xsum), M, K, N, _ptr(qweight), _ptr(scales),
-                         _ptr(None if symmetric else qzeros), int(symmetric), GROUP_SIZE, _ptr(Y), _stream(dev)))
+                         _ptr(None if symmetric else qzeros), int(symmetric), GROUP_SIZE, _ptr(Y), _ptr(ws),
+                         None if wsb is None else ctypes.byref(wsb), _stream(dev)))
     return Y
 
 
-def w4a8_gemv_launcher(Xq, sx, xsum, qweight, scales, qzeros, symmetric: bool, Y):
+def w4a8_gemv_launcher(Xq, sx, xsum, qweight, scales, qzeros, symmetric: bool, Y, workspace=None):
     """As gemv_launcher, for w4a8_gemv."""
     lib = load_library()
     M, K, N = _w4a8_args(Xq, sx, xsum, qweight, scales, qzeros, symmetric)
@@ -236,14 +246,16 @@ def w4a8_gemv_launcher(Xq, sx, xsum, qweight, scales, qzeros, symmetric: bool, Y
     if tuple(Y.shape) != (M, N):
         raise ValueError("Y must be [M][N]")
     qz = None if symmetric else qzeros
-    args = (_ptr(Xq), _ptr(sx), _ptr(xsum), M, K, N, _ptr(qweight), _ptr(scales), _ptr(qz), int(symmetric),
-            GROUP_SIZE, _ptr(Y))
     dev = Xq.device
+    ws, wsb = _w4a8_workspace(lib, M, K, N, symmetric, dev, workspace)
+    args = (_ptr(Xq), _ptr(sx), _ptr(xsum), M, K, N, _ptr(qweight), _ptr(scales), _ptr(qz), int(symmetric),
+            GROUP_SIZE, _ptr(Y), _ptr(ws), None if wsb is None else ctypes.byref(wsb))
 
     def launch():
         _check(lib.w4a8_gemv(*args, _stream(dev)))
 
-    launch.tensors = (Xq, sx, xsum, qweight, scales, qz, Y)
+    launch.tensors = (Xq, sx, xsum, qweight, scales, qz, Y, ws)
+    launch.workspace_size = wsb
     return launch
 
 

@@ -39,7 +39,8 @@ int launch_w4a8_quantize(const uint16_t* X, int M, int K, int8_t* Xq, float* sx,
 int w4a8_plan(int K, int N, int cus, int* ni, int* waves, size_t* lds);   // W4_ERR_UNSUPPORTED when K is too long
 int launch_w4a8_gemv(const int8_t* Xq, const float* sx, const int32_t* xsum, int M, int K, int N,
                      const uint32_t* qweight, const uint16_t* scales, const uint32_t* qzeros, int symmetric,
-                     uint16_t* Y, hipStream_t stream);
+                     uint16_t* Y, void* workspace, hipStream_t stream);
+size_t w4a8_workspace_bytes(int M, int K, int N);   // fp32 partials of a K split (0 without one)
 
 // ---------------------------------------------------------------- GEMM (MFMA)
 size_t gemm_workspace_bytes(int M, int K, int N);

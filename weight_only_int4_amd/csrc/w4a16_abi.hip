@@ -104,18 +104,24 @@ int w4a8_quantize_activations(const uint16_t* X, int M, int K, int8_t* Xq, float
 
 int w4a8_gemv(const int8_t* Xq, const float* sx, const int32_t* xsum, int M, int K, int N,
               const uint32_t* qweight, const uint16_t* scales, const uint32_t* qzeros, int symmetric,
-              int group_size, uint16_t* Y, void* stream) {
+              int group_size, uint16_t* Y, void* workspace, size_t* workspace_bytes, void* stream) {
   int st = check_weight_shape(N, K, group_size);
   if (st) return st;
   if (M < 0) return W4_ERR_SHAPE;
   if (M > W4_GEMV_MAX_M) return W4_ERR_UNSUPPORTED;
   if (w4a8_plan(K, N, 256, nullptr, nullptr, nullptr) != W4_OK) return W4_ERR_UNSUPPORTED;
+  const size_t need = w4a8_workspace_bytes(M, K, N);
+  if (!workspace && workspace_bytes) {
+    *workspace_bytes = need;
+    return W4_OK;
+  }
+  if (need > 0 && (!workspace || !workspace_bytes || *workspace_bytes < need)) return W4_ERR_WORKSPACE;
   if (M == 0 || N == 0) return W4_OK;
   if (!Xq || !sx || !xsum || !Y) return W4_ERR_NULL;
   st = check_packed(qweight, scales, qzeros, symmetric);
   if (st) return st;
-  if (misaligned(Xq) || misaligned(Y)) return W4_ERR_ALIGN;
-  return launch_w4a8_gemv(Xq, sx, xsum, M, K, N, qweight, scales, qzeros, symmetric, Y,
+  if (misaligned(Xq) || misaligned(Y) || misaligned(workspace)) return W4_ERR_ALIGN;
+  return launch_w4a8_gemv(Xq, sx, xsum, M, K, N, qweight, scales, qzeros, symmetric, Y, workspace,
                           static_cast<hipStream_t>(stream));
 }
 

@@ -97,8 +97,9 @@ __global__ __launch_bounds__(kActThreads) void w4a8_quant_act_kernel(const uint1
   }
 }
 
-// Workgroup: 16 output channels n0 .. n0+15 and all of K; its W waves take the
-// groups g = w, w + W, ..., w + (NI - 1) W in turn.  Per group, lane l (row index
+// Workgroup: 16 output channels n0 .. n0+15 and all of K, or with a K split
+// (grid.y > 1) the range of gsplit groups starting at g0 = blockIdx.y gsplit; its
+// W waves take the groups g = g0 + w, g0 + w + W, ..., g0 + w + (NI - 1) W in turn.  Per group, lane l (row index
 // l % 16, quarter q = l / 16) holds the 32 int8 activations of row m = l % 16 at
 // channels 128 g + 32 q .. +31 (two 16-byte loads) and the 32 codes of output
 // channel n0 + l % 16 at the same channels (one 16-byte load), plus that
@@ -110,15 +111,20 @@ __global__ __launch_bounds__(kActThreads) void w4a8_quant_act_kernel(const uint1
 // unrolled with four in flight.  The activation code sums of every group are
 // staged in LDS once per workgroup; the zero-point and scale fold is one
 // subtract-multiply-add per output per group; the W waves' fp32 sums meet in
-// LDS at the end, are added in wave order and scaled by sx[m].
+// LDS at the end, are added in wave order and scaled by sx[m] -- or, with a K
+// split, stored unscaled as the split's fp32 partial, which w4a8_split_reduce
+// adds in split order before scaling.
 template <int NI>
 __global__ __launch_bounds__(1024) void w4a8_gemv_kernel(const int8_t* Xq, const float* sx, const int32_t* xsum,
                                                          int M, int K, int N, const uint32_t* qweight,
                                                          const uint16_t* scales, const uint32_t* qzeros,
-                                                         int symmetric, uint16_t* Y) {
+                                                         int symmetric, uint16_t* Y, int gsplit, float* part) {
 #pragma clang fp contract(off)
   extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
   const int G = K >> 7;
+  // this workgroup's groups: [g0, g1) (grid.y splits K when gsplit > 0)
+  const int g0 = gsplit ? (int)blockIdx.y * gsplit : 0;
+  const int g1 = gsplit ? min(G, g0 + gsplit) : G;
   const int GW = (G + 7) >> 3;
   const int t = threadIdx.x;
   const int lane = t & 63;
@@ -149,9 +155,9 @@ __global__ __launch_bounds__(1024) void w4a8_gemv_kernel(const int8_t* Xq, const
   };
   // this lane's codes, activations, scale and zero word of group g: the lane part
   // of every offset is fixed, the group part is wave-uniform and goes in the
-  // scalar offset; groups past G (the unrolled tail) re-read group G-1
+  // scalar offset; groups past g1 (the unrolled tail) re-read group g1-1
   auto load = [&](int g, Slice& L) {
-    const int gc = min(g, G - 1);
+    const int gc = min(g, g1 - 1);
     L.w = __builtin_bit_cast(i32x4, __builtin_amdgcn_raw_buffer_load_b128(rw, wbase, gc * 64, 0));
     L.x0 = __builtin_bit_cast(i32x4, __builtin_amdgcn_raw_buffer_load_b128(rx, xbase, gc * 128, 0));
     L.x1 = __builtin_bit_cast(i32x4, __builtin_amdgcn_raw_buffer_load_b128(rx, xbase + 16u, gc * 128, 0));
@@ -162,7 +168,7 @@ __global__ __launch_bounds__(1024) void w4a8_gemv_kernel(const int8_t* Xq, const
   constexpr int P = NI < 4 ? NI : 4;
   Slice Ls[P];
 #pragma unroll
-  for (int i = 0; i < P; ++i) load(wave + i * W, Ls[i]);
+  for (int i = 0; i < P; ++i) load(g0 + wave + i * W, Ls[i]);
   __builtin_amdgcn_sched_barrier(0);
 
   for (int e = t; e < G * 16; e += blockDim.x) {
@@ -191,9 +197,9 @@ __global__ __launch_bounds__(1024) void w4a8_gemv_kernel(const int8_t* Xq, const
     const i32x4 b0 = {(int)b[0], (int)b[1], (int)b[2], (int)b[3]}, b1 = {(int)b[4], (int)b[5], (int)b[6], (int)b[7]};
     i32x4 c = __builtin_amdgcn_mfma_i32_16x16x64_i8(a0, b0, (i32x4){0, 0, 0, 0}, 0, 0, 0);
     c = __builtin_amdgcn_mfma_i32_16x16x64_i8(a1, b1, c, 0, 0, 0);
-    // groups past G (the unrolled tail) read group G-1's staging and add nothing
-    const bool live = g < G;
-    const int4 xs = *reinterpret_cast<const int4*>(s_xs + (live ? g : G - 1) * 16 + 4 * q);
+    // groups past g1 (the unrolled tail) read group g1-1's staging and add nothing
+    const bool live = g < g1;
+    const int4 xs = *reinterpret_cast<const int4*>(s_xs + (live ? g : g1 - 1) * 16 + 4 * q);
     const int z = symmetric ? 8 : (int)((L.z >> (4 * (g & 7))) & 0xFu);
     const float sc = live ? bf16_bits_to_f32(L.sc) : 0.0f;
     const int xsv[4] = {xs.x, xs.y, xs.z, xs.w};
@@ -209,8 +215,8 @@ __global__ __launch_bounds__(1024) void w4a8_gemv_kernel(const int8_t* Xq, const
   // flight, each refilled with the group P W further on once it is computed
 #pragma unroll
   for (int i = 0; i < NI; ++i) {
-    process(Ls[i % P], wave + i * W);
-    if (i + P < NI) load(wave + (i + P) * W, Ls[i % P]);
+    process(Ls[i % P], g0 + wave + i * W);
+    if (i + P < NI) load(g0 + wave + (i + P) * W, Ls[i % P]);
     __builtin_amdgcn_sched_barrier(0);
   }
 #pragma unroll
@@ -221,7 +227,10 @@ __global__ __launch_bounds__(1024) void w4a8_gemv_kernel(const int8_t* Xq, const
     if (m < M && n0 + n < N) {
       float s = 0.0f;
       for (int w = 0; w < W; ++w) s += s_red[(w * 16 + m) * 16 + n];
-      Y[(size_t)m * N + n0 + n] = (uint16_t)f32_to_bf16_bits(s * sx[m]);
+      if (part)
+        part[((size_t)blockIdx.y * M + m) * N + n0 + n] = s;
+      else
+        Y[(size_t)m * N + n0 + n] = (uint16_t)f32_to_bf16_bits(s * sx[m]);
     }
   }
 }
@@ -230,7 +239,18 @@ namespace {
 
 constexpr int kW4a8MaxNi = 25;       // 400 groups at 16 waves
 using W4a8Kernel = void (*)(const int8_t*, const float*, const int32_t*, int, int, int, const uint32_t*,
-                            const uint16_t*, const uint32_t*, int, uint16_t*);
+                            const uint16_t*, const uint32_t*, int, uint16_t*, int, float*);
+
+// Y[m][n] = bf16(sx[m] * sum over splits k of part[k][m][n]), fp32 in split order.
+__global__ __launch_bounds__(256) void w4a8_split_reduce(const float* part, int splits, int M, int N,
+                                                         const float* sx, uint16_t* Y) {
+  const size_t MN = (size_t)M * N;
+  const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= MN) return;
+  float s = 0.0f;
+  for (int k = 0; k < splits; ++k) s += part[(size_t)k * MN + i];
+  Y[i] = (uint16_t)f32_to_bf16_bits(s * sx[i / N]);
+}
 
 template <int... I>
 W4a8Kernel w4a8_pick(int ni, std::integer_sequence<int, I...>) {
@@ -251,14 +271,39 @@ int launch_w4a8_quantize(const uint16_t* X, int M, int K, int8_t* Xq, float* sx,
   return W4_OK;
 }
 
-// W waves per workgroup and NI = ceil(G / W) groups per wave (2 <= NI <= 25): the
-// most waves (8, 4 or 2) with which one round of resident workgroups covers the
-// ceil(N / 16) row tiles (about 20 resident waves per CU), at least ceil(G / 25).
-// LDS: per group the code sums of the 16 activation rows (int32), plus 16 x 16 fp32
-// sums per wave.
-int w4a8_plan(int K, int N, int cus, int* ni, int* waves, size_t* lds) {
+// K split, a function of the shape only (the workspace size follows it): when K
+// has at least 64 groups and the ceil(N / 16) column tiles are fewer than two per
+// CU of 256, the groups are split into ranges of at least 16 so that the tiles x
+// splits workgroups come near two per CU (K = 17408, N = 5120 takes 2: 20.1 ->
+// 19.4 us at M = 1, 32.9 -> 30.2 us at M = 16).  Shorter K keeps one workgroup
+// per tile: the second kernel's launch costs more than the split saves there (the
+// decode sweep's K = 6144 down projection in 3 splits made the sweep 4% slower).
+int w4a8_k_splits(int K, int N) {
   const int G = K >> 7;
   const long long tiles = (N + 15) / 16;
+  if (G < 64 || tiles >= 2 * 256) return 1;
+  const int s = (int)std::min<long long>((2 * 256 + tiles - 1) / tiles, G / 16);
+  const int gs = (G + s - 1) / s;
+  return (G + gs - 1) / gs;          // every split non-empty
+}
+
+size_t w4a8_workspace_bytes(int M, int K, int N) {
+  if (M <= 0 || N <= 0 || K <= 0) return 0;
+  const int s = w4a8_k_splits(K, N);
+  return s > 1 ? (size_t)s * M * N * sizeof(float) : 0;
+}
+
+// W waves per workgroup and NI = ceil(Gs / W) groups per wave (2 <= NI <= 25), Gs
+// the groups of one split: the most waves (8, 4 or 2) with which one round of
+// resident workgroups covers the ceil(N / 16) column tiles times the splits (about
+// 20 resident waves per CU), at least ceil(Gs / 25).  LDS: per group of K the code
+// sums of the 16 activation rows (int32), plus 16 x 16 fp32 sums per wave.
+int w4a8_plan(int K, int N, int cus, int* ni, int* waves, size_t* lds) {
+  const int GK = K >> 7;
+  if (GK > kW4a8MaxNi * 16) return W4_ERR_UNSUPPORTED;   // 400 groups: the limit without a split
+  const int splits = w4a8_k_splits(K, N);
+  const int G = (GK + splits - 1) / splits;
+  const long long tiles = (N + 15) / 16 * splits;
   int w = 2;
   for (int cand : {8, 4}) {
     if (tiles <= (long long)cus * (20 / cand)) {
@@ -268,7 +313,7 @@ int w4a8_plan(int K, int N, int cus, int* ni, int* waves, size_t* lds) {
   }
   w = std::max(std::min(w, G), (G + kW4a8MaxNi - 1) / kW4a8MaxNi);
   const int n = std::max(2, (G + w - 1) / w);
-  const size_t bytes = (size_t)G * 64 + (size_t)w * 16 * 16 * 4;
+  const size_t bytes = (size_t)GK * 64 + (size_t)w * 16 * 16 * 4;
   if (w > 16 || n > kW4a8MaxNi || bytes > 64 * 1024) return W4_ERR_UNSUPPORTED;
   if (ni) *ni = n;
   if (waves) *waves = w;
@@ -278,7 +323,7 @@ int w4a8_plan(int K, int N, int cus, int* ni, int* waves, size_t* lds) {
 
 int launch_w4a8_gemv(const int8_t* Xq, const float* sx, const int32_t* xsum, int M, int K, int N,
                      const uint32_t* qweight, const uint16_t* scales, const uint32_t* qzeros, int symmetric,
-                     uint16_t* Y, hipStream_t stream) {
+                     uint16_t* Y, void* workspace, hipStream_t stream) {
   if (M == 0 || N == 0) return W4_OK;
   // 32-bit buffer offsets: packed weights N K / 2 and activations M K below 2^31
   if ((long long)N * K / 2 >= (1LL << 31) || (long long)M * K >= (1LL << 31)) return W4_ERR_SHAPE;
@@ -290,10 +335,20 @@ int launch_w4a8_gemv(const int8_t* Xq, const float* sx, const int32_t* xsum, int
     cus = 256;
   const int st = w4a8_plan(K, N, cus, &ni, &waves, &lds);
   if (st != W4_OK) return st;
-  const dim3 grid((unsigned)((N + 15) / 16));
+  const int splits = w4a8_k_splits(K, N);
+  const int G = K >> 7;
+  const int gsplit = splits > 1 ? (G + splits - 1) / splits : 0;
+  float* part = splits > 1 ? static_cast<float*>(workspace) : nullptr;
+  const dim3 grid((unsigned)((N + 15) / 16), (unsigned)splits);
   hipLaunchKernelGGL(w4a8_kernel_for(ni), grid, dim3(waves * 64), lds, stream, Xq, sx, xsum, M, K, N, qweight, scales,
-                     qzeros, symmetric, Y);
+                     qzeros, symmetric, Y, gsplit, part);
   W4_CHECK_LAUNCH();
+  if (splits > 1) {
+    const size_t MN = (size_t)M * N;
+    hipLaunchKernelGGL(w4a8_split_reduce, dim3((unsigned)((MN + 255) / 256)), dim3(256), 0, stream, part, splits, M,
+                       N, sx, Y);
+    W4_CHECK_LAUNCH();
+  }
   return W4_OK;
 }
 

@@ -288,6 +288,21 @@ def test_gemm_shapes(M, K, N, sym):
     assert _elementwise_ok(y, ref) == 0
 
 
+@pytest.mark.parametrize("M,N", [(2048, 2048), (2048, 2056), (2050, 2048)])
+def test_gemm_core_layout_boundary(M, N):
+    """Either side of the grid size at which the MFMA core switches from three
+    stages and two workgroups per CU to two stages and three: 512 tiles of 64 x 128
+    (three stages) and 544 / 528 tiles (two stages) with a ragged column or row
+    tail; K = 640 (five groups: both stage parities and an odd count).  Oracle on
+    every 16th row."""
+    X, W = wl.small_case(M, 640, N, 51)
+    rows = np.arange(0, M, 16)
+    say("gemm core layout", M, N)
+    y, ref = _gemm_case(X, W, False, rows)
+    _fro_ok(y, ref)
+    assert _elementwise_ok(y, ref) == 0
+
+
 def test_gemm_one_hot_and_zero():
     _, W = wl.small_case(1, 384, 160, 9)
     qw, sc, qz = _packed(W, False)
@@ -428,7 +443,8 @@ def test_w4a8_quantize_activations_bit_exact(M, K):
 
 
 @pytest.mark.parametrize("M,K,N", [(1, 2048, 300), (4, 2048, 129), (16, 2048, 64), (7, 128, 33), (2, 6144, 17),
-                                   (16, 17408, 40), (1, 5120, 1000), (9, 4224, 31), (3, 51200, 20), (5, 9344, 100)])
+                                   (16, 17408, 40), (1, 5120, 1000), (9, 4224, 31), (3, 51200, 20), (5, 9344, 100),
+                                   (3, 8064, 40), (3, 8192, 40)])
 @pytest.mark.parametrize("sym", [False, True])
 def test_w4a8_gemv(M, K, N, sym):
     say("w4a8 gemv", M, K, N, sym)

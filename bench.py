@@ -16,9 +16,9 @@ line carries:
   * ``roofline`` of the dominant kernel (the GEMV): algorithmic bytes per launch
     over its average launch duration -- the event-timed graph replay (only GEMV
     launches, back to back on one stream) divided by the launches -- against
-    the 8 TB/s HBM peak, with the latency floor: t0, the per-launch time of the
-    smallest GEMV (one row, one group, one output) replayed as a graph of as
-    many launches, and the step's latency-adjusted ceiling
+    the 8 TB/s HBM peak, with the latency floor: t0, the per-launch time of an
+    empty kernel replayed as a graph of as many launches, and the step's
+    latency-adjusted ceiling
     sum(bytes / BW) / sum(t0 + bytes / BW), which no kernel of the sweep can beat;
   * ``rows``: every other step of the path measured in the same run (cold-cache
     GEMV on the 27B-shaped linears, decode sweeps at M = 4 and 16, prefill GEMM
@@ -81,14 +81,10 @@ class Launch:
 
 
 def latency_floor_us(torch, w4, launches):
-    """Per-launch time (us) of a graph of `launches` launches of the smallest GEMV:
-    M = 1, K = 128, N = 1 (one group, one output, 24 bytes of weights)."""
-    X = torch.zeros((1, GROUP), dtype=torch.bfloat16, device="cuda")
-    qw = torch.zeros((1, GROUP // 8), dtype=torch.int32, device="cuda")
-    sc = torch.ones((1, 1), dtype=torch.bfloat16, device="cuda")
-    qz = torch.zeros((1, 1), dtype=torch.int32, device="cuda")
-    ls = [Launch(w4.gemv_launcher(X, qw, sc, qz, False, torch.empty((1, 1), dtype=torch.bfloat16, device="cuda")),
-                 0, 0) for _ in range(launches)]
+    """Per-launch time (us) of a graph of `launches` launches of an empty kernel
+    (one 64-thread workgroup; a kernel of its own, so that profiles of the GEMV
+    keep only real GEMV dispatches)."""
+    ls = [Launch(lambda: w4.probe_empty(), 0, 0) for _ in range(launches)]
     g = capture_graph(torch, ls)
     ms = time_events(torch, g.replay, 20)
     del g, ls

@@ -209,8 +209,8 @@ __global__ __launch_bounds__(gemv_max_waves(M) * 64) void gemv_kernel(GemvArgs a
     for (int i = 0; i < WPL; ++i) {
       pair_activations(xr[m][i], xp[m][i]);
 #pragma unroll
-      for (int q = 0; q < 4; ++q)
-        xs[m] += __uint_as_float(xr[m][i][q] << 16) + __uint_as_float(xr[m][i][q] & 0xFFFF0000u);
+      for (int q = 0; q < 4; ++q)   // the pair's sum: one dot product with (1, 1) (exact products, fp32 sums)
+        xs[m] = dot2_bf16(xr[m][i][q], 0x3F803F80u, xs[m]);
     }
   }
   // symmetric: the zero-point term -(128 + 8) sum_k x_k is the same for every row

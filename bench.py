@@ -228,13 +228,14 @@ def measure_rotation(torch, launches, reps):
     return ms
 
 
-def fused_sweep_launches(torch, w4, wl, packed, M):
+def fused_sweep_launches(torch, w4, wl, packed, M, w4a8=False):
     """The decode step as a decoder runs it: the linears of a block that read the same
     activations (q, k, v; gate, up) are one GEMV each over their packed rows stored
     concatenated along N (contiguous in the N-major layout): q|k|v (N = 4096) and
     gate|up (N = 12288), with the activation row of the block's first linear of the
     group.  Four launches per block: q|k|v, o, gate|up, down; the same weight bytes
-    as one launch per linear."""
+    as one launch per linear.  w4a8: the same launches on the W4A8 path (activations
+    quantized up front, as for w4a8_sweep_launches)."""
     by_block = {}
     for b, layer, K, N, qw, sc, qz in packed:
         by_block.setdefault(b, {})[layer] = (K, N, qw, sc, qz)
@@ -249,8 +250,14 @@ def fused_sweep_launches(torch, w4, wl, packed, M):
             qz = torch.cat([L[i][4] for i in group], 0)
             X = to_dev_bf16(torch, wl.decode_act(b, group[0], M))
             Y = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
-            launches.append(Launch(w4.gemv_launcher(X, qw, sc, qz, False, Y), gemv_bytes(M, K, N, False),
-                                   2 * M * K * N))
+            if w4a8:
+                Xq, sx, xs = w4.w4a8_quantize_activations(X)
+                launches.append(Launch(w4.w4a8_gemv_launcher(Xq, sx, xs, qw, sc, qz, False, Y),
+                                       packed_bytes(N, K, False) + M * K + M * 4 + M * (K // GROUP) * 4 + M * N * 2,
+                                       2 * M * K * N))
+            else:
+                launches.append(Launch(w4.gemv_launcher(X, qw, sc, qz, False, Y), gemv_bytes(M, K, N, False),
+                                       2 * M * K * N))
     torch.cuda.synchronize()
     return launches
 
@@ -634,6 +641,12 @@ def main(argv=None):
             ms = time_events(torch, g.replay, max(3, args.steps // 2))
             rows.append(row_gemv(f"W4A8 decode sweep M={M} (graph)", sum(l.nbytes for l in sw), ms))
             del g, sw
+            sw = fused_sweep_launches(torch, w4, wl, packed, M, w4a8=True)
+            g = capture_graph(torch, sw)
+            ms = time_events(torch, g.replay, max(3, args.steps // 2))
+            rows.append(row_gemv(f"W4A8 decode sweep M={M}, shared-input linears fused (graph)",
+                                 sum(l.nbytes for l in sw), ms, {"launches": len(sw)}))
+            del g, sw
             torch.cuda.empty_cache()
         for M in ((4, 16) if "sweeps" in want and packed else ()):
             log(f"decode sweep M={M}")
@@ -641,6 +654,12 @@ def main(argv=None):
             g = capture_graph(torch, sw)
             ms = time_events(torch, g.replay, max(3, args.steps // 2))
             rows.append(row_gemv(f"decode sweep M={M} (graph)", sum(l.nbytes for l in sw), ms))
+            del g, sw
+            sw = fused_sweep_launches(torch, w4, wl, packed, M)
+            g = capture_graph(torch, sw)
+            ms = time_events(torch, g.replay, max(3, args.steps // 2))
+            rows.append(row_gemv(f"decode sweep M={M}, shared-input linears fused (graph)",
+                                 sum(l.nbytes for l in sw), ms, {"launches": len(sw)}))
             del g, sw
             torch.cuda.empty_cache()
         del packed

@@ -635,6 +635,51 @@ def check_search_lookahead_statistic_and_ties():
     assert np.array_equal(res["s"], np.ones(H, np.float32))
 
 
+def check_block_scalar_restatement():
+    """The oracle's block, op by op, against the pure-Python token loop of
+    tests/scalar_reference.py on a tiny block (H = 128, feed-forward 256, two query
+    heads over one key/value head, two sequences of three tokens): bit-identical
+    outputs, with every linear unquantized and with the gate projection replaced
+    by its deployed int4 candidate (non-trivial s and a clip ratio).  The first
+    token of each sequence is scaled by 2^-10, so its mean square (about 1e-6) is
+    of the order of the norm's epsilon and the epsilon reading shows in the output;
+    the weights of the two norms differ, and the gate and up weights differ, so the
+    norm each op reads and the projection that carries the SiLU are visible."""
+    rng = np.random.default_rng(97)
+    B, L, H, I, n_q, n_kv = 2, 3, 128, 256, 2, 1
+    blk = _block(rng, H=H, I=I, n_q=n_q, n_kv=n_kv, std=0.08)
+    x = rng.standard_normal((B * L, H)).astype(np.float32)
+    x[0::L] *= np.float32(2.0 ** -10)
+    x = round_to_bf16_bits(x)
+    val = lambda b: O.bf16_to_f32(b).astype(np.float64)
+    sblk = {k: (val(v).tolist()) for k, v in blk.items()}
+    s = np.exp(rng.standard_normal(H) * 0.4).astype(np.float32)
+    packed = O.quantize_pack(blk["gate"], s, 0.9, False)
+    what = S.quantize_dequant(sblk["gate"], s.astype(np.float64).tolist(), 0.9, False)
+    for cand in (None, ("gate", s, packed, False)):
+        y = val(O.block_forward(x, B, L, blk, n_q, n_kv, candidate=cand))
+        for b in range(B):
+            rows = val(x[b * L:(b + 1) * L]).tolist()
+            sc = None if cand is None else ("gate", s.astype(np.float64).tolist(), what)
+            want = np.array(S.block_tokens(rows, sblk, n_q, n_kv, candidate=sc))
+            got = y[b * L:(b + 1) * L]
+            assert np.array_equal(got, want), (cand is None, b, np.argwhere(got != want)[:4])
+
+
+def check_rmsnorm_epsilon_closed_form():
+    """RMSNorm of a constant row c with unit weight is bf16(c / sqrt(c^2 + eps)):
+    with c = 2^-10 (mean square 2^-20, about 1e-6) and c = 2^-7, eps = 1e-6 (the
+    reading; the pages name no value) gives the closed values below, which any
+    other eps of the same order misses."""
+    g = np.ones(256)
+    for c in (2.0 ** -10, 2.0 ** -7):
+        y = O.rmsnorm(np.full((1, 256), c), g)
+        want = S.rb(c / np.sqrt(c * c + 1e-6))
+        assert np.all(y == want), (c, y[0, 0], want)
+    y = O.rmsnorm(np.full((1, 256), 2.0 ** -10), g)
+    assert abs(y[0, 0] - 0.6987) < 4e-3
+
+
 ALL_CHECKS = [
     check_search_lookahead_statistic_and_ties, check_rope_rotation, check_attention, check_rmsnorm_and_silu, check_block_and_lookahead,
     check_clip_channel_bruteforce, check_clip_channel_special_cases,
@@ -647,4 +692,5 @@ ALL_CHECKS = [
     check_act_stat_closed_form, check_scales_closed_form, check_rewrite_identity,
     check_alpha_zero_is_rtn, check_loss_closed_form_reference, check_bruteforce_search,
     check_bruteforce_quantizer_random,
+    check_rmsnorm_epsilon_closed_form, check_block_scalar_restatement,
 ]

@@ -170,3 +170,70 @@ def rotate_pairs(x, p, base=1e6, hd=128):
         out[j] = x[j] * c - x[j + half] * s
         out[j + half] = x[j + half] * c + x[j] * s
     return out
+
+
+# ----------------------------------------------------------------------------- one decoder block
+#
+# The block of the look-ahead scoring (model card "rebuttal_w4g128_awq_w2",
+# "Search" row and the paragraph under the details table; model page
+# "qwen3-1.7b_q326_channel", "Model Architecture": grouped-query attention,
+# rotary positions with base 10^6, SiLU-gated feed-forward), restated token by
+# token with the readings the oracle takes where the pages are silent:
+# pre-norm RMSNorm with eps 1e-6 and a per-channel weight before attention and
+# before the feed-forward, the second norm reading the post-attention residual;
+# SiLU on the gate projection, multiplied by the up projection; residual adds
+# after attention and after the feed-forward; every op output rounded to bf16
+# (through fp32, as the GPU stores it).
+
+RMS_EPS_READING = 1e-6
+
+
+def rb(x: float) -> float:
+    """An op output as stored: fp64 value -> fp32 -> bf16 (nearest even both times)."""
+    return round_bf16(f32(x))
+
+
+def rms_row(x: list[float], g: list[float]) -> list[float]:
+    ms = sum(v * v for v in x) / len(x)
+    r = 1.0 / math.sqrt(ms + RMS_EPS_READING)
+    return [rb(x[c] * r * g[c]) for c in range(len(x))]
+
+
+def matvec(W: list[list[float]], a: list[float]) -> list[float]:
+    """One token through a linear with weight W [out][in]: rounded outputs."""
+    return [rb(sum(W[o][c] * a[c] for c in range(len(a)))) for o in range(len(W))]
+
+
+def block_tokens(x_rows, blk, n_q, n_kv, candidate=None):
+    """One sequence x [L][H] (bf16 values) through the block.  blk holds "norm1",
+    "norm2" ([H] values) and "q", "k", "v", "o", "gate", "up", "down" (weights
+    [out][in] as lists of values).  candidate = (name, s, W_hat) runs that
+    linear in its deployed form: input bf16(fp32(a / s)) against the dequantized
+    weights W_hat (values).  Returns the block output [L][H] (values)."""
+    L = len(x_rows)
+
+    def lin(name, a):
+        if candidate is not None and candidate[0] == name:
+            _, s, what = candidate
+            xs = [round_bf16(f32(a[c] / s[c])) for c in range(len(a))]
+            return matvec(what, xs)
+        return matvec(blk[name], a)
+
+    a = [rms_row(x, blk["norm1"]) for x in x_rows]
+    q, k, v = [], [], []
+    for t in range(L):
+        qt, kt = lin("q", a[t]), lin("k", a[t])
+        q.append([rb(e) for h in range(n_q) for e in rotate_pairs(qt[128 * h:128 * h + 128], t)])
+        k.append([rb(e) for h in range(n_kv) for e in rotate_pairs(kt[128 * h:128 * h + 128], t)])
+        v.append(lin("v", a[t]))
+    att = [[rb(e) for e in row] for row in causal_attention(q, k, v, L, n_q, n_kv)]
+    out = []
+    for t in range(L):
+        ot = lin("o", att[t])
+        h1 = [rb(x_rows[t][c] + ot[c]) for c in range(len(ot))]
+        b = rms_row(h1, blk["norm2"])
+        gt, ut = lin("gate", b), lin("up", b)
+        m = [rb(gt[i] / (1.0 + math.exp(-gt[i])) * ut[i]) for i in range(len(gt))]
+        dt = lin("down", m)
+        out.append([rb(h1[c] + dt[c]) for c in range(len(dt))])
+    return out

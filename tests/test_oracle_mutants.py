@@ -85,6 +85,17 @@ MUTANTS = {
                                 "yn = block_forward(x_bf16, B, L, nxt, n_q, n_kv) if nxt is not None else yi"),
     "clip_after_scale_choice": ("        absmax = np.abs(v).max(axis=2, keepdims=True)\n    if symmetric:",
                                 "    if symmetric:"),
+    "gate_up_swapped": ('m = silu_mul(lin("gate", b2), lin("up", b2))', 'm = silu_mul(lin("up", b2), lin("gate", b2))'),
+    "norm2_on_input": ('b2 = rmsnorm(h, val(blk["norm2"]))', 'b2 = rmsnorm(x, val(blk["norm2"]))'),
+    "norm2_weight_is_norm1": ('b2 = rmsnorm(h, val(blk["norm2"]))', 'b2 = rmsnorm(h, val(blk["norm1"]))'),
+    "rms_eps_1e-5": ("RMS_EPS = 1e-6", "RMS_EPS = 1e-5"),
+    "rms_eps_zero": ("RMS_EPS = 1e-6", "RMS_EPS = 0.0"),
+    "rope_on_values": ('v = lin("v", a)', 'v = rope(lin("v", a), B, L, n_kv)'),
+    "rope_missing_on_keys": ('k = rope(lin("k", a), B, L, n_kv)', 'k = lin("k", a)'),
+    "final_residual_from_input": ('y = _bf16_round(h + lin("down", m))', 'y = _bf16_round(x + lin("down", m))'),
+    "queries_from_block_input": ('q = rope(lin("q", a), B, L, n_q)', 'q = rope(lin("q", x), B, L, n_q)'),
+    "candidate_unrounded_input": ("xs = bf16_to_f32(f32_to_bf16(a.astype(np.float32) / s32[None, :])).astype(np.float64)",
+                                  "xs = a / s32[None, :].astype(np.float64)"),
 }
 
 

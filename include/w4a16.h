@@ -294,6 +294,24 @@ int w4_block_forward(const uint16_t* X, int B, int L, int hidden, int n_q, int n
                      void* stream);
 
 /*
+ * w4_block_forward_quantized -- w4_block_forward with linear `linear` (0..6: q, k,
+ * v, o, gate, up, down) in its deployed int4 form.  [AWQ-W4 card] scale-rewrite
+ * paragraph: the rewrite prev_op /= s, W *= s runs as the input bf16(a / s) (IEEE
+ * fp32 division, rounded to nearest even) against the packed weights of
+ * Q(W diag(s)) on the int4 GEMM (w4a16_gemm), exactly as awq_lookahead_loss scores
+ * a candidate; every other op as in w4_block_forward.
+ *   s [K] fp32 device (K the linear's input size, every s[k] > 0).  qweight,
+ *   scales, qzeros: the linear's packed weights [N][K/8], [N][K/128],
+ *   [N][ceil(K/1024)] as written by awq_quantize_pack (qzeros NULL iff
+ *   symmetric).  X, Y, blk, shapes and the workspace size query as in
+ *   w4_block_forward; the size also depends on `linear`.
+ */
+int w4_block_forward_quantized(const uint16_t* X, int B, int L, int hidden, int n_q, int n_kv, int inter,
+                               const w4_block* blk, int linear, const float* s, const uint32_t* qweight,
+                               const uint16_t* scales, const uint32_t* qzeros, int symmetric, int group_size,
+                               uint16_t* Y, void* workspace, size_t* workspace_bytes, void* stream);
+
+/*
  * awq_lookahead_loss -- look-ahead (d = 1) scoring of C candidates for one linear of
  * block `blk`.  [AWQ-W4 card] "Search" and the paragraph under it: the candidate
  * weights go into this block, the MSE is taken at the output of the next block

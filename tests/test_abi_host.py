@@ -245,6 +245,32 @@ def test_block_and_lookahead_validation(lib):
              None, ctypes.byref(sz), None) == -7
 
 
+def test_block_forward_quantized_validation(lib):
+    sz = ctypes.c_size_t(0)
+    blk = _Blk(*([0x10000] * 9))
+    bad = _Blk(*([0x10000] * 8 + [0]))
+    f = lib.w4_block_forward_quantized
+    assert f(None, 8, 512, 2048, 16, 8, 6144, None, 6, None, None, None, None, 0, 128, None, None, ctypes.byref(sz),
+             None) == 0
+    base = ctypes.c_size_t(0)
+    assert lib.w4_block_forward(None, 8, 512, 2048, 16, 8, 6144, None, None, None, ctypes.byref(base), None) == 0
+    assert sz.value > base.value + 2 * 4096 * 6144      # plus bf16(a / s) of the down projection's input
+    ok = ctypes.c_size_t(sz.value)
+    args = lambda **k: [k.get("X", A), 8, 512, 2048, 16, 8, 6144, ctypes.byref(k.get("blk", blk)), k.get("lin", 6),
+                        k.get("s", A), k.get("qw", A), A, k.get("qz", A), k.get("sym", 0), k.get("gs", 128),
+                        k.get("Y", A), A, ctypes.byref(k.get("ws", ok)), None]
+    assert f(*args(lin=-1)) == -7
+    assert f(*args(sym=3)) == -7
+    assert f(*args(gs=32)) == -4
+    assert f(*args(s=None)) == -1
+    assert f(*args(qw=None)) == -1
+    assert f(*args(sym=1)) == -1                 # qzeros must be NULL when symmetric
+    assert f(*args(qz=None)) == -1
+    assert f(*args(blk=bad)) == -1
+    assert f(*args(Y=MIS)) == -3
+    assert f(*args(ws=ctypes.c_size_t(64))) == -5
+
+
 def test_python_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(w4, "_LIB", None)
     monkeypatch.setattr(w4, "_HERE", str(tmp_path))

@@ -21,7 +21,7 @@ __all__ = [
     "W4Error", "library_path", "load_library", "awq_quantize_pack", "w4a16_gemv", "w4a16_gemm",
     "awq_grid_loss", "awq_search", "GROUP_SIZE", "GEMV_MAX_M", "gemv_launcher", "gemm_launcher",
     "w4a8_quantize_activations", "w4a8_gemv", "w4a8_gemv_launcher", "awq_clip_search", "block_forward",
-    "awq_lookahead_loss", "awq_search_lookahead", "BLOCK_LINEARS", "probe_stream_read", "probe_empty",
+    "block_forward_quantized", "awq_lookahead_loss", "awq_search_lookahead", "BLOCK_LINEARS", "probe_stream_read", "probe_empty",
 ]
 
 GROUP_SIZE = 128
@@ -53,6 +53,8 @@ _SIGNATURES = {
     "w4a8_gemv": ([_vp, _vp, _vp, _i, _i, _i, _vp, _vp, _vp, _i, _i, _vp, _vp, _sz, _vp], _i),
     "awq_clip_search": ([_vp, _i, _i, _i, _vp, _vp, _vp, _i, _i, _i, _vp, _vp, _vp, _sz, _vp], _i),
     "w4_block_forward": ([_vp, _i, _i, _i, _i, _i, _i, _bp, _vp, _vp, _sz, _vp], _i),
+    "w4_block_forward_quantized": ([_vp, _i, _i, _i, _i, _i, _i, _bp, _i, _vp, _vp, _vp, _vp, _i, _i, _vp, _vp, _sz,
+                                    _vp], _i),
     "awq_lookahead_loss": ([_vp, _i, _i, _i, _i, _i, _i, _bp, _bp, _i, _vp, _vp, _i, _i, _i, _vp, _vp, _vp, _sz, _vp],
                            _i),
     "awq_search_lookahead": ([_vp, _i, _i, _i, _i, _i, _i, _bp, _bp, _i, ctypes.POINTER(ctypes.c_double), _i,
@@ -367,6 +369,38 @@ def block_forward(X, B: int, L: int, blk, n_q: int, n_kv: int, Y=None, workspace
     ws, wsb = _workspace(q, X.device, workspace)
     _check(lib.w4_block_forward(_ptr(X), B, L, H, n_q, n_kv, I, ctypes.byref(b), _ptr(Y), _ptr(ws),
                                 None if wsb is None else ctypes.byref(wsb), _stream(X.device)))
+    return Y
+
+
+def block_forward_quantized(X, B: int, L: int, blk, n_q: int, n_kv: int, linear, s, qweight, scales, qzeros=None,
+                            symmetric: bool = False, Y=None, workspace=None):
+    """Y [B L][H] bf16 = decoder block(X) with linear `linear` in its deployed int4 form:
+    input bf16(a / s) against the packed weights of Q(W diag(s)) (see include/w4a16.h,
+    w4_block_forward_quantized)."""
+    lib = load_library()
+    _need(X, torch.bfloat16, "X", 2)
+    _need(s, torch.float32, "s", 1)
+    T, H = X.shape
+    if T != B * L:
+        raise ValueError("X must have B * L rows")
+    I = blk["gate"].shape[0]
+    li = BLOCK_LINEARS.index(linear) if isinstance(linear, str) else int(linear)
+    b = _block_struct(blk, H, n_q, n_kv, I)
+    K = blk[BLOCK_LINEARS[li]].shape[1]
+    if s.shape[0] != K or qweight.shape[1] * 8 != K:
+        raise ValueError("s must have the linear's input size K and qweight K/8 columns")
+    qz = None if symmetric else qzeros
+    if Y is None:
+        Y = torch.empty_like(X)
+
+    def q(sz):
+        return lib.w4_block_forward_quantized(None, B, L, H, n_q, n_kv, I, None, li, None, None, None, None,
+                                              int(symmetric), GROUP_SIZE, None, None, sz, None)
+
+    ws, wsb = _workspace(q, X.device, workspace)
+    _check(lib.w4_block_forward_quantized(_ptr(X), B, L, H, n_q, n_kv, I, ctypes.byref(b), li, _ptr(s),
+                                          _ptr(qweight), _ptr(scales), _ptr(qz), int(symmetric), GROUP_SIZE, _ptr(Y),
+                                          _ptr(ws), None if wsb is None else ctypes.byref(wsb), _stream(X.device)))
     return Y
 
 

@@ -550,6 +550,39 @@ int launch_block_forward(const uint16_t* X, int B, int L, int H, int nq, int nkv
   return run_block(d, blk, X, Y, nullptr, ws, l, stream);
 }
 
+// Block layout, then the candidate's scaled input bf16(a / s) and the int4 GEMM's workspace.
+size_t block_quantized_layout(const Dims& d, int linear, size_t& xs, size_t& gemm) {
+  size_t off = 0;
+  block_layout(d, off);
+  int K, N;
+  linear_shape(d, linear, K, N);
+  xs = off;
+  off = align_up(off + (size_t)d.T * K * 2, 256);
+  gemm = off;
+  return align_up(off + gemm_workspace_bytes(d.T, K, N), 256);
+}
+
+size_t block_quantized_workspace_bytes(int B, int L, int H, int nq, int nkv, int I, int linear) {
+  size_t xs, gemm;
+  return block_quantized_layout(make_dims(B, L, H, nq, nkv, I), linear, xs, gemm);
+}
+
+int launch_block_forward_quantized(const uint16_t* X, int B, int L, int H, int nq, int nkv, int I,
+                                   const w4_block& blk, int linear, const float* s, const uint32_t* qweight,
+                                   const uint16_t* scales, const uint32_t* qzeros, int symmetric, uint16_t* Y,
+                                   void* workspace, hipStream_t stream) {
+  const Dims d = make_dims(B, L, H, nq, nkv, I);
+  size_t off = 0;
+  const BlockLayout l = block_layout(d, off);
+  size_t xs, gemm;
+  block_quantized_layout(d, linear, xs, gemm);
+  char* ws = static_cast<char*>(workspace);
+  int rc = rope_tables(d, ws, l, stream);
+  if (rc) return rc;
+  Candidate cand{linear, s, qweight, scales, qzeros, symmetric, reinterpret_cast<uint16_t*>(ws + xs), ws + gemm};
+  return run_block(d, blk, X, Y, &cand, ws, l, stream);
+}
+
 size_t lookahead_workspace_bytes(int B, int L, int H, int nq, int nkv, int I, int linear) {
   return look_layout(make_dims(B, L, H, nq, nkv, I), linear).total;
 }

@@ -64,6 +64,11 @@ int launch_clip_search(const uint16_t* X, int T, int K, int N, const uint16_t* W
 size_t block_forward_workspace_bytes(int B, int L, int H, int nq, int nkv, int I);
 int launch_block_forward(const uint16_t* X, int B, int L, int H, int nq, int nkv, int I, const w4_block& blk,
                          uint16_t* Y, void* workspace, hipStream_t stream);
+size_t block_quantized_workspace_bytes(int B, int L, int H, int nq, int nkv, int I, int linear);
+int launch_block_forward_quantized(const uint16_t* X, int B, int L, int H, int nq, int nkv, int I,
+                                   const w4_block& blk, int linear, const float* s, const uint32_t* qweight,
+                                   const uint16_t* scales, const uint32_t* qzeros, int symmetric, uint16_t* Y,
+                                   void* workspace, hipStream_t stream);
 size_t lookahead_workspace_bytes(int B, int L, int H, int nq, int nkv, int I, int linear);
 int launch_lookahead_loss(const uint16_t* X, int B, int L, int H, int nq, int nkv, int I, const w4_block& blk,
                           const w4_block* next, int linear, const float* S, const float* ratios, int C,

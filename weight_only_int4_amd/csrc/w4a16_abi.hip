@@ -226,6 +226,30 @@ int w4_block_forward(const uint16_t* X, int B, int L, int hidden, int n_q, int n
   return launch_block_forward(X, B, L, hidden, n_q, n_kv, inter, *blk, Y, workspace, static_cast<hipStream_t>(stream));
 }
 
+int w4_block_forward_quantized(const uint16_t* X, int B, int L, int hidden, int n_q, int n_kv, int inter,
+                               const w4_block* blk, int linear, const float* s, const uint32_t* qweight,
+                               const uint16_t* scales, const uint32_t* qzeros, int symmetric, int group_size,
+                               uint16_t* Y, void* workspace, size_t* workspace_bytes, void* stream) {
+  if (group_size != kGroup) return W4_ERR_UNSUPPORTED;
+  int st = check_block_shape(B, L, hidden, n_q, n_kv, inter);
+  if (st) return st;
+  if (linear < 0 || linear > 6 || (symmetric != 0 && symmetric != 1)) return W4_ERR_VALUE;
+  const size_t need = block_quantized_workspace_bytes(B, L, hidden, n_q, n_kv, inter, linear);
+  if (!workspace) {
+    if (!workspace_bytes) return W4_ERR_WORKSPACE;
+    *workspace_bytes = need;
+    return W4_OK;
+  }
+  if (!workspace_bytes || *workspace_bytes < need) return W4_ERR_WORKSPACE;
+  if (!X || !Y || !s || block_null(blk)) return W4_ERR_NULL;
+  st = check_packed(qweight, scales, qzeros, symmetric);
+  if (st) return st;
+  if (misaligned(X) || misaligned(Y) || misaligned(s) || misaligned(workspace) || block_misaligned(blk))
+    return W4_ERR_ALIGN;
+  return launch_block_forward_quantized(X, B, L, hidden, n_q, n_kv, inter, *blk, linear, s, qweight, scales, qzeros,
+                                        symmetric, Y, workspace, static_cast<hipStream_t>(stream));
+}
+
 int awq_lookahead_loss(const uint16_t* X, int B, int L, int hidden, int n_q, int n_kv, int inter,
                        const w4_block* blk, const w4_block* next, int linear, const float* S,
                        const float* ratios, int C, int symmetric, int group_size, float* losses,

@@ -28,6 +28,8 @@
 //    one wave per row the results are stored at once; otherwise every wave parks
 //    its per-row sums in LDS and the workgroup adds them in wave order after the
 //    last batch (one barrier per workgroup).
+#include <atomic>
+
 #include "internal.hpp"
 
 namespace w4 {
@@ -318,16 +320,19 @@ GemvPlan plan_gemv(int M, int K) {
   return p;
 }
 
+// Per-device and per-instantiation caches of launch-plan queries.  Host threads
+// may launch concurrently: the slots are atomics, and a slot filled twice by
+// racing first calls gets the same value both times.
 int device_cus() {
-  static int cus[64] = {0};
+  static std::atomic<int> cus[64];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (cus[dev] == 0) {
-    int n = 0;
+  int n = cus[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
     if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 1) n = 256;
-    cus[dev] = n;
+    cus[dev].store(n, std::memory_order_relaxed);
   }
-  return cus[dev];
+  return n;
 }
 
 template <int M, int BPW, bool SYM>
@@ -338,16 +343,16 @@ constexpr auto gemv_instance() {
 // Resident workgroups per CU of one instantiation at a block size (cached).
 template <int M, int BPW, bool SYM>
 int gemv_blocks_per_cu(int threads) {
-  static int cache[17] = {0};
+  static std::atomic<int> cache[17];
   const int slot = threads / kWave;
-  if (cache[slot] == 0) {
-    int nblk = 0;
+  int nblk = cache[slot].load(std::memory_order_relaxed);
+  if (nblk == 0) {
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nblk, gemv_instance<M, BPW, SYM>(), threads, 0) != hipSuccess ||
         nblk < 1)
       nblk = 1;
-    cache[slot] = nblk;
+    cache[slot].store(nblk, std::memory_order_relaxed);
   }
-  return cache[slot];
+  return nblk;
 }
 
 // Batches per workgroup.  Among 1, 2, 3, 4, 5, 6 and 8, those with which one round

@@ -66,11 +66,14 @@ typedef enum {
   W4_ERR_UNSUPPORTED = -4,  /* group_size != 128, gemv with M > 16, ...                  */
   W4_ERR_WORKSPACE = -5,    /* workspace missing or smaller than the size query returns  */
   W4_ERR_HIP = -6,          /* a HIP runtime call failed                                 */
-  W4_ERR_VALUE = -7         /* a scalar argument is out of range (clip ratio, grid size) */
+  W4_ERR_VALUE = -7,        /* a scalar argument is out of range (clip ratio, grid size) */
+  W4_ERR_SCRATCH = -8       /* the problem needs more than the library's static scratch  */
 } w4_status;
 
 #define W4_GROUP_SIZE 128
 #define W4_GEMV_MAX_M 16
+/* Size of the static device scratch array of w4a16_gemv_noalloc (per device). */
+#define W4_GEMV_SCRATCH_BYTES (8u << 20)
 
 /* Human-readable name of a status code (static storage; never NULL). */
 const char* w4_status_string(int status);
@@ -122,6 +125,25 @@ int awq_quantize_pack(const uint16_t* W, int N, int K, const float* s, float cli
 int w4a16_gemv(const uint16_t* X, int M, int K, int N, const uint32_t* qweight,
                const uint16_t* scales, const uint32_t* qzeros, int symmetric, int group_size,
                uint16_t* Y, void* workspace, size_t* workspace_bytes, void* stream);
+
+/*
+ * w4a16_gemv_noalloc -- w4a16_gemv for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation).  Same arguments minus the workspace, same kernels, bit-identical
+ * results.  The fp32 partial sums of a K split (the workspace of w4a16_gemv) live
+ * in a static device array of W4_GEMV_SCRATCH_BYTES (8 MiB), one per device, held
+ * until the process ends; its device address is fetched once per device, on the
+ * first call there.  Nothing is allocated or freed.
+ *   Problems whose split partials exceed the array (w4a16_gemv's size query above
+ *   8 MiB, e.g. M = 16 at K = 17408 with N > 43,690) return W4_ERR_SCRATCH and
+ *   enqueue nothing; every other argument is checked as in w4a16_gemv.
+ *   All calls on one device share its array: calls whose executions overlap on
+ *   one device (concurrent streams, or host threads on different streams) race
+ *   and must be serialized by the caller.  Calls on one stream never overlap.
+ */
+int w4a16_gemv_noalloc(const uint16_t* X, int M, int K, int N, const uint32_t* qweight,
+                       const uint16_t* scales, const uint32_t* qzeros, int symmetric, int group_size,
+                       uint16_t* Y, void* stream);
 
 /*
  * w4a8_quantize_activations -- per-row symmetric int8 quantization of decode

@@ -39,7 +39,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_status_strings(lib):
-    for code in range(0, -8, -1):
+    for code in range(0, -9, -1):
         s = lib.w4_status_string(code).decode()
         assert s.startswith("W4_"), s
     assert lib.w4_status_string(-99).decode() == "W4_ERR_UNKNOWN"
@@ -85,6 +85,24 @@ def test_gemv_validation_and_size_query(lib):
     assert f(A, 1, 256, 8, A, A, None, 0, 128, A, None, None, None) == -1
     assert f(MIS, 1, 256, 8, A, A, A, 0, 128, A, None, None, None) == -3
     assert f(A, 0, 256, 8, A, A, A, 0, 128, A, None, None, None) == 0      # M = 0: empty
+
+
+def test_gemv_noalloc_validation(lib):
+    f = lib.w4a16_gemv_noalloc
+    assert f(A, 17, 256, 8, A, A, A, 0, 128, A, None) == -4
+    assert f(A, 1, 200, 8, A, A, A, 0, 128, A, None) == -2
+    assert f(A, 1, 256, 8, A, A, A, 0, 32, A, None) == -4
+    assert f(None, 1, 256, 8, A, A, A, 0, 128, A, None) == -1
+    assert f(A, 1, 256, 8, A, A, None, 0, 128, A, None) == -1
+    assert f(A, 1, 256, 8, A, A, A, 1, 128, A, None) == -1          # qzeros must be NULL when symmetric
+    assert f(MIS, 1, 256, 8, A, A, A, 0, 128, A, None) == -3
+    assert f(A, 0, 256, 8, A, A, A, 0, 128, A, None) == 0           # M = 0: empty, no HIP call
+    # split partials above the 8 MiB static array: rejected before any HIP call
+    sz = ctypes.c_size_t(0)
+    assert lib.w4a16_gemv(None, 16, 17408, 50000, None, None, None, 1, 128, None, None, ctypes.byref(sz), None) == 0
+    assert sz.value > 8 << 20
+    assert f(A, 16, 17408, 50000, A, A, None, 1, 128, A, None) == -8
+    assert lib.w4_status_string(-8).decode().startswith("W4_ERR_SCRATCH")
 
 
 def test_w4a8_validation(lib):

@@ -18,7 +18,7 @@ import os
 import torch
 
 __all__ = [
-    "W4Error", "library_path", "load_library", "awq_quantize_pack", "w4a16_gemv", "w4a16_gemm",
+    "W4Error", "library_path", "load_library", "awq_quantize_pack", "w4a16_gemv", "w4a16_gemv_noalloc", "w4a16_gemm",
     "awq_grid_loss", "awq_search", "GROUP_SIZE", "GEMV_MAX_M", "gemv_launcher", "gemm_launcher",
     "w4a8_quantize_activations", "w4a8_gemv", "w4a8_gemv_launcher", "awq_clip_search", "block_forward",
     "block_forward_quantized", "awq_lookahead_loss", "awq_search_lookahead", "BLOCK_LINEARS", "probe_stream_read", "probe_empty",
@@ -46,6 +46,7 @@ _SIGNATURES = {
     "awq_quantize_pack": ([_vp, _i, _i, _vp, _f, _i, _i, _vp, _vp, _vp, _vp], _i),
     "w4a16_gemv": ([_vp, _i, _i, _i, _vp, _vp, _vp, _i, _i, _vp, _vp, _sz, _vp], _i),
     "w4a16_gemm": ([_vp, _i, _i, _i, _vp, _vp, _vp, _i, _i, _vp, _vp, _sz, _vp], _i),
+    "w4a16_gemv_noalloc": ([_vp, _i, _i, _i, _vp, _vp, _vp, _i, _i, _vp, _vp], _i),
     "awq_grid_loss": ([_vp, _i, _i, _i, _vp, _vp, _vp, _vp, _i, _i, _i, _vp, _vp, _sz, _vp], _i),
     "w4_probe_stream_read": ([_vp, ctypes.c_size_t, _i, _i, _i, _vp, _vp], _i),
     "w4_probe_empty": ([_vp], _i),
@@ -186,6 +187,21 @@ def w4a16_gemv(X, qweight, scales, qzeros=None, symmetric: bool = False, Y=None,
     ws, wsb = _workspace(q, dev, workspace)
     _check(lib.w4a16_gemv(_ptr(X), M, K, N, _ptr(qweight), _ptr(scales), _ptr(qz), int(symmetric), GROUP_SIZE,
                           _ptr(Y), _ptr(ws), None if wsb is None else ctypes.byref(wsb), _stream(dev)))
+    return Y
+
+
+def w4a16_gemv_noalloc(X, qweight, scales, qzeros, symmetric: bool, Y):
+    """Decode GEMV into the caller's Y [M][N] bf16 without any device allocation: the
+    K-split partial sums use the library's static scratch array (see include/w4a16.h,
+    w4a16_gemv_noalloc; calls overlapping on one device race)."""
+    lib = load_library()
+    M, K, N = _packed_shapes(X, qweight, scales, qzeros, symmetric)
+    _need(Y, torch.bfloat16, "Y", 2)
+    if tuple(Y.shape) != (M, N):
+        raise ValueError(f"Y must have shape {(M, N)}")
+    qz = None if symmetric else qzeros
+    _check(lib.w4a16_gemv_noalloc(_ptr(X), M, K, N, _ptr(qweight), _ptr(scales), _ptr(qz), int(symmetric), GROUP_SIZE,
+                                  _ptr(Y), _stream(X.device)))
     return Y
 
 

@@ -44,6 +44,7 @@ const char* w4_status_string(int status) {
     case W4_ERR_WORKSPACE: return "W4_ERR_WORKSPACE: workspace missing or too small";
     case W4_ERR_HIP: return "W4_ERR_HIP: a HIP runtime call failed";
     case W4_ERR_VALUE: return "W4_ERR_VALUE: scalar argument out of range";
+    case W4_ERR_SCRATCH: return "W4_ERR_SCRATCH: the problem needs more than the static scratch array holds";
     default: return "W4_ERR_UNKNOWN";
   }
 }

@@ -23,11 +23,8 @@
  *   - Array pointers are DEVICE pointers owned by the caller unless a parameter
  *     says "host".  The library never frees caller memory and never allocates
  *     device memory, except: awq_search and awq_search_lookahead allocate their
- *     workspace themselves when the caller passes none (see there); the
- *     decoder-block calls (w4_block_forward, awq_lookahead_loss,
- *     awq_search_lookahead) run their unquantized bf16 projections through
- *     rocBLAS, whose handle (one per device, created on first use, with its own
- *     device workspace) the library keeps until the process ends.
+ *     workspace themselves when the caller passes none (see there).  Every
+ *     kernel is the library's own; it links nothing beyond the HIP runtime.
  *   - `stream` is a hipStream_t (NULL = the default stream).  Work is enqueued
  *     asynchronously on it; results are ready once the stream is synchronized.
  *     awq_search and awq_search_lookahead are the calls that synchronize (they
@@ -202,6 +199,18 @@ int w4a16_gemm(const uint16_t* X, int M, int K, int N, const uint32_t* qweight,
                uint16_t* Y, void* workspace, size_t* workspace_bytes, void* stream);
 
 /*
+ * w4_bf16_linear -- the unquantized linear Y = bf16(X W^T) (fp32 accumulation,
+ * rounded to nearest even), on the library's bf16 matrix-core kernel.
+ * [AWQ-W4 card] scale-rewrite paragraph and the paragraph under the details
+ * table: the losses of the search compare against the linear in original
+ * precision (awq_grid_loss computes its Yref with this kernel; the decoder-block
+ * calls run their unquantized projections on it).
+ *   X [M][K] bf16, W [N][K] bf16 (K contiguous), Y [M][N] bf16 out (device).
+ *   K a positive multiple of 64 (else W4_ERR_SHAPE); 2 M K and 2 N K below 2^32.
+ */
+int w4_bf16_linear(const uint16_t* X, int M, int K, int N, const uint16_t* W, uint16_t* Y, void* stream);
+
+/*
  * awq_grid_loss -- losses of C fake-quant candidates of one linear.
  * [AWQ-W4 card] scale-rewrite paragraph: a candidate (s, r) is simulated by
  * swapping the weight for Q(W diag(s)) diag(1/s), i.e. by feeding X diag(1/s)
@@ -306,7 +315,8 @@ typedef struct w4_block {
  *   query head h reading key/value head h / (n_q / n_kv); h1 = x + o Wo^T;
  *   b = rmsnorm(h1) * norm2; y = h1 + (silu(b Wg^T) * (b Wu^T)) Wd^T.  No biases,
  *   no per-head q/k norms.  Every op computes in fp32 and stores bf16 (nearest
- *   even); the projections are bf16 GEMMs with fp32 accumulation (rocBLAS).
+ *   even); the projections are bf16 GEMMs with fp32 accumulation (w4_bf16_linear's
+ *   kernel).
  *   H and I multiples of 128; n_kv >= 1 divides n_q; B, L >= 1.
  *   Workspace: size query as in w4a16_gemm (about 2 B L (5 H + 3 I + 2 128 n_q +
  *   2 128 n_kv) bytes).

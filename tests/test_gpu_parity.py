@@ -370,6 +370,43 @@ def test_gemm_deterministic_and_overwrites():
     assert np.array_equal(bits16(Y1), bits16(Y2))
 
 
+# ----------------------------------------------------------------------------- unquantized bf16 linear
+
+@pytest.mark.parametrize("M,K,N", [(1, 64, 1), (130, 192, 257), (64, 2048, 128), (257, 6144, 200), (1000, 128, 129),
+                                   (2, 4096, 3000)])
+def test_bf16_linear_shapes(M, K, N):
+    """Y = bf16(X W^T): within half a bf16 ulp of the fp64 value plus the fp32
+    accumulation slack, ragged tiles on both sides."""
+    X, W = wl.small_case(M, K, N, 61)
+    say("bf16 linear", M, K, N)
+    Y = w4.bf16_linear(to_bf16(X), to_bf16(W))
+    torch.cuda.synchronize()
+    y = bf16_values(bits16(Y))
+    ref = O.linear(X, O.bf16_to_f32(W))
+    _fro_ok(y, ref)
+    assert _elementwise_ok(y, ref) == 0
+
+
+@pytest.mark.parametrize("M,K,N", [(4096, 2048, 6144), (4096, 6144, 2048), (4096, 2048, 1024)])
+def test_bf16_linear_full_size(M, K, N):
+    """The search's reference output (T=4096, K=2048, N=6144) and the decoder block's
+    down and k/v projections at 8 x 512 tokens; oracle on every 16th row; bit-identical rerun."""
+    rng = np.random.default_rng(M + K + N)
+    X = wl.round_to_bf16_bits(rng.standard_normal((M, K)).astype(np.float32))
+    W = wl.round_to_bf16_bits((rng.standard_normal((N, K)) * 0.02).astype(np.float32))
+    say("bf16 linear full", M, K, N)
+    Xd, Wd = to_bf16(X), to_bf16(W)
+    Y = w4.bf16_linear(Xd, Wd)
+    Y2 = w4.bf16_linear(Xd, Wd)
+    torch.cuda.synchronize()
+    assert torch.equal(Y, Y2)
+    rows = np.arange(0, M, 16)
+    y = bf16_values(bits16(Y))[rows]
+    ref = O.linear(X[rows], O.bf16_to_f32(W))
+    _fro_ok(y, ref)
+    assert _elementwise_ok(y, ref) == 0
+
+
 # ----------------------------------------------------------------------------- grid loss
 
 def _grid_inputs(T, K, N, seed):

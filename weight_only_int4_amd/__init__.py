@@ -18,7 +18,7 @@ import os
 import torch
 
 __all__ = [
-    "W4Error", "library_path", "load_library", "awq_quantize_pack", "w4a16_gemv", "w4a16_gemv_noalloc", "w4a16_gemm",
+    "W4Error", "library_path", "load_library", "awq_quantize_pack", "w4a16_gemv", "w4a16_gemv_noalloc", "w4a16_gemm", "bf16_linear",
     "awq_grid_loss", "awq_search", "GROUP_SIZE", "GEMV_MAX_M", "gemv_launcher", "gemm_launcher",
     "w4a8_quantize_activations", "w4a8_gemv", "w4a8_gemv_launcher", "awq_clip_search", "block_forward",
     "block_forward_quantized", "awq_lookahead_loss", "awq_search_lookahead", "BLOCK_LINEARS", "probe_stream_read", "probe_empty",
@@ -47,6 +47,7 @@ _SIGNATURES = {
     "w4a16_gemv": ([_vp, _i, _i, _i, _vp, _vp, _vp, _i, _i, _vp, _vp, _sz, _vp], _i),
     "w4a16_gemm": ([_vp, _i, _i, _i, _vp, _vp, _vp, _i, _i, _vp, _vp, _sz, _vp], _i),
     "w4a16_gemv_noalloc": ([_vp, _i, _i, _i, _vp, _vp, _vp, _i, _i, _vp, _vp], _i),
+    "w4_bf16_linear": ([_vp, _i, _i, _i, _vp, _vp, _vp], _i),
     "awq_grid_loss": ([_vp, _i, _i, _i, _vp, _vp, _vp, _vp, _i, _i, _i, _vp, _vp, _sz, _vp], _i),
     "w4_probe_stream_read": ([_vp, ctypes.c_size_t, _i, _i, _i, _vp, _vp], _i),
     "w4_probe_empty": ([_vp], _i),
@@ -202,6 +203,21 @@ def w4a16_gemv_noalloc(X, qweight, scales, qzeros, symmetric: bool, Y):
     qz = None if symmetric else qzeros
     _check(lib.w4a16_gemv_noalloc(_ptr(X), M, K, N, _ptr(qweight), _ptr(scales), _ptr(qz), int(symmetric), GROUP_SIZE,
                                   _ptr(Y), _stream(X.device)))
+    return Y
+
+
+def bf16_linear(X, W, Y=None):
+    """Unquantized linear Y [M][N] = bf16(X [M][K] W [N][K]^T) on the library's bf16 kernel."""
+    lib = load_library()
+    _need(X, torch.bfloat16, "X", 2)
+    _need(W, torch.bfloat16, "W", 2)
+    M, K = X.shape
+    N = W.shape[0]
+    if W.shape[1] != K:
+        raise ValueError("W must be [N][K] for X [M][K]")
+    if Y is None:
+        Y = torch.empty((M, N), dtype=torch.bfloat16, device=X.device)
+    _check(lib.w4_bf16_linear(_ptr(X), M, K, N, _ptr(W), _ptr(Y), _stream(X.device)))
     return Y
 
 

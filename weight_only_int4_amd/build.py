@@ -38,9 +38,8 @@ HIPCC_FLAGS = [
 ]
 
 
-# rocBLAS serves the plain bf16 projections of the decoder-block path
-ROCM_LIB = "/opt/rocm/lib"
-LINK_LIBS = [f"-L{ROCM_LIB}", f"-Wl,-rpath,{ROCM_LIB}", "-lrocblas"]
+# the library links nothing beyond the HIP runtime
+LINK_LIBS: list[str] = []
 
 
 def hipcc() -> str:

@@ -18,14 +18,13 @@
 //   a = rmsnorm(x, g1); q, k, v = a Wq^T, a Wk^T, a Wv^T; q, k = rope(q), rope(k);
 //   o = attention(q, k, v); h = x + o Wo^T; b = rmsnorm(h, g2);
 //   m = silu(b Wg^T) * (b Wu^T); y = h + m Wd^T.
-// The unquantized projections are plain bf16 GEMMs (rocBLAS, fp32 accumulation); a
-// candidate linear runs as deployed: bf16(input / s) against its int4 codes
-// Q(W diag(s), r) on the library's int4 GEMM.
+// The unquantized projections run on the library's bf16 MFMA kernel (fp32
+// accumulation; q, k, v as one launch and gate, up as one launch, since each group
+// reads the same input); a candidate linear runs as deployed: bf16(input / s)
+// against its int4 codes Q(W diag(s), r) on the library's int4 GEMM.
 #include <math.h>
-#include <rocblas/rocblas.h>
 
 #include <algorithm>
-#include <mutex>
 
 #include "internal.hpp"
 
@@ -389,32 +388,9 @@ int ew_launch(int op, const uint16_t* A, const uint16_t* B, size_t n, uint16_t* 
   return W4_OK;
 }
 
-// rocBLAS handle per device, created on first use and kept for the process.  The
-// handle carries the stream it enqueues on, so setting the stream and enqueueing the
-// GEMM happen under one lock (host threads calling on one device take turns; the GPU
-// work itself stays asynchronous).
-std::mutex blas_mu;
-
-rocblas_handle blas_handle_locked() {
-  static rocblas_handle handles[64] = {};
-  int dev = -1;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
-  if (!handles[dev] && rocblas_create_handle(&handles[dev]) != rocblas_status_success) handles[dev] = nullptr;
-  return handles[dev];
-}
-
-// Y [T][N] = bf16(X W^T) for bf16 X [T][K] and W [N][K]: a plain library GEMM
-// (column-major view: Y^T = W^T-op(K x N) times X^T), fp32 accumulation.
+// Y [T][N] = bf16(X W^T) for bf16 X [T][K] and W [N][K] (the unquantized projections).
 int bf16_linear(const uint16_t* X, int T, int K, int N, const uint16_t* W, uint16_t* Y, hipStream_t st) {
-  std::lock_guard<std::mutex> guard(blas_mu);
-  rocblas_handle hnd = blas_handle_locked();
-  if (!hnd || rocblas_set_stream(hnd, st) != rocblas_status_success) return W4_ERR_HIP;
-  const float alpha = 1.0f, beta = 0.0f;
-  const rocblas_status rs =
-      rocblas_gemm_ex(hnd, rocblas_operation_transpose, rocblas_operation_none, N, T, K, &alpha, W,
-                      rocblas_datatype_bf16_r, K, X, rocblas_datatype_bf16_r, K, &beta, Y, rocblas_datatype_bf16_r, N,
-                      Y, rocblas_datatype_bf16_r, N, rocblas_datatype_f32_r, rocblas_gemm_algo_standard, 0, 0);
-  return rs == rocblas_status_success ? W4_OK : W4_ERR_HIP;
+  return launch_bf16_gemm(X, T, K, N, W, Y, st);
 }
 
 // One linear: Y [T][N] = bf16(X W^T), or the candidate's deployed int4 form.
@@ -447,9 +423,16 @@ int run_block(const Dims& d, const w4_block& blk, const uint16_t* X, uint16_t* Y
   if (stage == 0) {
     hipLaunchKernelGGL(rmsnorm_kernel, dim3(nrow), dim3(256), 0, st, X, d.T, d.H, blk.norm1, buf(l.a));
     W4_CHECK_LAUNCH();
-    if ((rc = run_linear(d, 0, buf(l.a), blk.wq, cand, buf(l.q), st))) return rc;
-    if ((rc = run_linear(d, 1, buf(l.a), blk.wk, cand, buf(l.k), st))) return rc;
-    if ((rc = run_linear(d, 2, buf(l.a), blk.wv, cand, buf(l.v), st))) return rc;
+    if (cand && cand->linear <= 2) {
+      if ((rc = run_linear(d, 0, buf(l.a), blk.wq, cand, buf(l.q), st))) return rc;
+      if ((rc = run_linear(d, 1, buf(l.a), blk.wk, cand, buf(l.k), st))) return rc;
+      if ((rc = run_linear(d, 2, buf(l.a), blk.wv, cand, buf(l.v), st))) return rc;
+    } else {      // q, k and v read the same normalized input: one launch
+      const uint16_t* Ws[3] = {blk.wq, blk.wk, blk.wv};
+      const int Ns[3] = {d.QD, d.KD, d.KD};
+      uint16_t* Ys[3] = {buf(l.q), buf(l.k), buf(l.v)};
+      if ((rc = launch_bf16_gemm_multi(buf(l.a), d.T, d.H, 3, Ws, Ns, Ys, st))) return rc;
+    }
     const float* cs = reinterpret_cast<const float*>(ws + l.cs);
     const float* sn = reinterpret_cast<const float*>(ws + l.sn);
     const long long qi = (long long)T * d.nq * 64, ki = (long long)T * d.nkv * 64;
@@ -464,16 +447,32 @@ int run_block(const Dims& d, const w4_block& blk, const uint16_t* X, uint16_t* Y
     W4_CHECK_LAUNCH();
   }
   if (stage <= 1) {
-    if ((rc = run_linear(d, 3, o, blk.wo, cand, buf(l.p), st))) return rc;
-    if ((rc = ew_launch(EW_ADD, X, buf(l.p), T * d.H, buf(l.h), st))) return rc;
+    if (cand && cand->linear == 3) {
+      if ((rc = run_linear(d, 3, o, blk.wo, cand, buf(l.p), st))) return rc;
+      if ((rc = ew_launch(EW_ADD, X, buf(l.p), T * d.H, buf(l.h), st))) return rc;
+    } else {      // h = x + o Wo^T: the residual added in the GEMM's epilogue
+      uint16_t* hy = buf(l.h);
+      if ((rc = launch_bf16_gemm_multi(o, d.T, d.QD, 1, &blk.wo, &d.H, &hy, st, &X))) return rc;
+    }
   }
   hipLaunchKernelGGL(rmsnorm_kernel, dim3(nrow), dim3(256), 0, st, h, d.T, d.H, blk.norm2, buf(l.b2));
   W4_CHECK_LAUNCH();
-  if ((rc = run_linear(d, 4, buf(l.b2), blk.wgate, cand, buf(l.gt), st))) return rc;
-  if ((rc = run_linear(d, 5, buf(l.b2), blk.wup, cand, buf(l.up), st))) return rc;
+  if (cand && (cand->linear == 4 || cand->linear == 5)) {
+    if ((rc = run_linear(d, 4, buf(l.b2), blk.wgate, cand, buf(l.gt), st))) return rc;
+    if ((rc = run_linear(d, 5, buf(l.b2), blk.wup, cand, buf(l.up), st))) return rc;
+  } else {        // gate and up read the same normalized input: one launch
+    const uint16_t* Ws[2] = {blk.wgate, blk.wup};
+    const int Ns[2] = {d.I, d.I};
+    uint16_t* Ys[2] = {buf(l.gt), buf(l.up)};
+    if ((rc = launch_bf16_gemm_multi(buf(l.b2), d.T, d.H, 2, Ws, Ns, Ys, st))) return rc;
+  }
   if ((rc = ew_launch(EW_SILU_MUL, buf(l.gt), buf(l.up), T * d.I, buf(l.m), st))) return rc;
-  if ((rc = run_linear(d, 6, buf(l.m), blk.wdown, cand, buf(l.dn), st))) return rc;
-  return ew_launch(EW_ADD, h, buf(l.dn), T * d.H, Y, st);
+  if (cand && cand->linear == 6) {
+    if ((rc = run_linear(d, 6, buf(l.m), blk.wdown, cand, buf(l.dn), st))) return rc;
+    return ew_launch(EW_ADD, h, buf(l.dn), T * d.H, Y, st);
+  }
+  // y = h + m Wd^T: the residual added in the GEMM's epilogue
+  return launch_bf16_gemm_multi(buf(l.m), d.T, d.I, 1, &blk.wdown, &d.H, &Y, st, &h);
 }
 
 int rope_tables(const Dims& d, char* ws, const BlockLayout& l, hipStream_t st) {

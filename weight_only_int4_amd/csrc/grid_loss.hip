@@ -210,20 +210,7 @@ int launch_grid_loss(const uint16_t* X, int T, int K, int N, const uint16_t* W, 
 
 int launch_reference_gemm(const uint16_t* X, int M, int K, int N, const uint16_t* W, uint16_t* Y,
                           hipStream_t stream) {
-  // 32-bit per-lane byte offsets in the MFMA core: 2 M K and 2 N K below 2^32
-  if ((long long)M * K >= (1LL << 31) || (long long)N * K >= (1LL << 31)) return W4_ERR_SHAPE;
-  GemmCoreArgs r{};
-  r.X = X;
-  r.M = M;
-  r.K = K;
-  r.N = N;
-  r.W = W;
-  r.Y = Y;
-  const long long tiles = (long long)((N + kBN - 1) / kBN) * ((M + kBM - 1) / kBM);
-  if (tiles > 0x7FFFFFFFLL) return W4_ERR_SHAPE;
-  hipLaunchKernelGGL((gemm_core_kernel<false, EPI_STORE>), dim3((unsigned)tiles), dim3(kGemmWaves * 64), 0, stream, r);
-  W4_CHECK_LAUNCH();
-  return W4_OK;
+  return launch_bf16_gemm(X, M, K, N, W, Y, stream);
 }
 
 int launch_act_mean_abs(const uint16_t* X, int T, int K, double* m, hipStream_t stream) {

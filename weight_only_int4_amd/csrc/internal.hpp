@@ -81,6 +81,14 @@ int launch_lookahead_candidates(const uint16_t* X, int B, int L, int H, int nq, 
                                 int symmetric, float* losses, float* losses_d0, void* workspace,
                                 hipStream_t stream);
 
+// Y = bf16(X W^T) with bf16 weights W [N][K] on the library's bf16 MFMA kernel
+// (K a multiple of 64).
+int launch_bf16_gemm(const uint16_t* X, int M, int K, int N, const uint16_t* W, uint16_t* Y, hipStream_t stream);
+// One launch for up to three weights W[s] [N[s]][K] reading the same X: Y[s] = bf16(X W[s]^T),
+// or bf16(R[s] + bf16(X W[s]^T)) with residuals R (NULL: none; R[s] NULL: none for s).
+int launch_bf16_gemm_multi(const uint16_t* X, int M, int K, int nseg, const uint16_t* const* W, const int* N,
+                           uint16_t* const* Y, hipStream_t stream, const uint16_t* const* R = nullptr);
+
 // Y = bf16(X W^T) with bf16 weights W [N][K] (the unquantized reference output).
 int launch_reference_gemm(const uint16_t* X, int M, int K, int N, const uint16_t* W, uint16_t* Y,
                           hipStream_t stream);

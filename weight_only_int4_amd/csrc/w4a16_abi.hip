@@ -147,6 +147,15 @@ int w4a16_gemm(const uint16_t* X, int M, int K, int N, const uint32_t* qweight, 
                      static_cast<hipStream_t>(stream));
 }
 
+int w4_bf16_linear(const uint16_t* X, int M, int K, int N, const uint16_t* W, uint16_t* Y, void* stream) {
+  if (M < 0 || N < 0 || K <= 0 || K % 64 || (long long)M * K >= (1LL << 31) || (long long)N * K >= (1LL << 31))
+    return W4_ERR_SHAPE;
+  if (M == 0 || N == 0) return W4_OK;
+  if (!X || !W || !Y) return W4_ERR_NULL;
+  if (misaligned(X) || misaligned(W) || misaligned(Y)) return W4_ERR_ALIGN;
+  return launch_bf16_gemm(X, M, K, N, W, Y, static_cast<hipStream_t>(stream));
+}
+
 int awq_grid_loss(const uint16_t* X, int T, int K, int N, const uint16_t* W, const uint16_t* Yref,
                   const float* S, const float* ratios, int C, int symmetric, int group_size, float* losses,
                   void* workspace, size_t* workspace_bytes, void* stream) {

@@ -43,6 +43,8 @@ struct GemvArgs {
   uint16_t* Y;
   float* partial;       // [splits][M][N] when splits > 1
   int wps;              // packed words per split (multiple of WPL)
+  int nwk;              // waves covering one slab's channel range
+  int rw;               // slabs per workgroup (one group of nwk waves each)
 };
 
 // Raw buffer resource over [base, base + bytes) (gfx9 word 3: untyped, range
@@ -142,12 +144,13 @@ __global__ __launch_bounds__(gemv_max_waves(M) * 64) void gemv_kernel(GemvArgs a
   constexpr int V = R * M;
   constexpr int VP = pow2_ceil(V);
   constexpr int LOGV = ilog2(VP);
-  __shared__ float red[BPW * R * M][16];    // per-row sums of every wave when nw > 1
+  __shared__ float red[16][BPW * R * M];    // per-row sums of every wave when nwk > 1
 
-  const int t = threadIdx.x;
-  const int lane = t & (kWave - 1);
+  const int lane = threadIdx.x & (kWave - 1);
+  const int nw = a.nwk;
+  const int slab = threadIdx.x / (nw * kWave);       // this wave's slab within the workgroup
+  const int t = threadIdx.x - slab * nw * kWave;     // thread index within the slab's waves
   const int wave = t >> 6;
-  const int nw = blockDim.x >> 6;
   const int words = a.K >> 3;
   const int G = a.K >> 7;
   const int GW = (G + 7) >> 3;
@@ -166,7 +169,7 @@ __global__ __launch_bounds__(gemv_max_waves(M) * 64) void gemv_kernel(GemvArgs a
   const auto rs = make_rsrc(a.scales, (uint32_t)a.N * srow);
   const auto rz = make_rsrc(SYM ? static_cast<const void*>(a.scales) : a.qzeros, SYM ? 0u : (uint32_t)a.N * zrow);
   const auto rx = make_rsrc(a.X, (uint32_t)(M * a.K) * 2u);
-  const int n_first = blockIdx.x * BPW * R;   // first row of the slab
+  const int n_first = (blockIdx.x * a.rw + slab) * BPW * R;   // first row of the slab
 
   struct Batch {
     uint32_t w[R][WPL];
@@ -261,7 +264,7 @@ __global__ __launch_bounds__(gemv_max_waves(M) * 64) void gemv_kernel(GemvArgs a
       const int n = n_first + rloc;
       if (writer && n < a.N) store(m, n, part[0]);
     } else if (writer) {
-      red[rloc * M + m][wave] = part[0];
+      red[slab * nw + wave][rloc * M + m] = part[0];
     }
   };
 
@@ -274,12 +277,14 @@ __global__ __launch_bounds__(gemv_max_waves(M) * 64) void gemv_kernel(GemvArgs a
 
   if (nw > 1) {
     __syncthreads();
-    for (int e = t; e < BPW * R * M; e += blockDim.x) {
-      const int n = n_first + e / M;
+    constexpr int E = BPW * R * M;
+    for (int e = threadIdx.x; e < a.rw * E; e += blockDim.x) {
+      const int sl = e / E, i = e - sl * E;
+      const int n = (blockIdx.x * a.rw + sl) * BPW * R + i / M;
       if (n < a.N) {
         float s = 0.0f;
-        for (int w = 0; w < nw; ++w) s += red[e][w];
-        store(e % M, n, s);
+        for (int w = 0; w < nw; ++w) s += red[sl * nw + w][i];
+        store(i % M, n, s);
       }
     }
   }
@@ -306,6 +311,13 @@ constexpr int gemv_nb(int M) { return 2; }
 struct GemvPlan {
   int wpl, nw, splits, wps;
 };
+
+// Waves per workgroup the launch aims for when one slab needs fewer: slabs of
+// a workgroup share its dispatch (a K = 2048 GEMV is one wave per slab).
+#ifndef W4_GEMV_WG_WAVES
+#define W4_GEMV_WG_WAVES 4
+#endif
+constexpr int kGemvWgWaves = W4_GEMV_WG_WAVES;
 
 // K split into `splits` ranges of wps words, each covered by nw waves.
 GemvPlan plan_gemv(int M, int K) {
@@ -366,12 +378,16 @@ int gemv_blocks_per_cu(int threads) {
 // M = 8: K = 5120, N = 17408 takes 8 -- 544 workgroups of 16 batches left 32 CUs
 // a third one -- and K = 17408, N = 5120 keeps 16).
 template <int M, bool SYM>
-void launch_m(const GemvArgs& a, const GemvPlan& p, hipStream_t stream) {
+void launch_m(GemvArgs a, const GemvPlan& p, hipStream_t stream) {
   constexpr int R = gemv_rows(M);
-  const int threads = p.nw * kWave;
+  // slabs per workgroup: several slabs share a workgroup when one slab needs few waves
+  const int rw = p.nw >= kGemvWgWaves ? 1 : kGemvWgWaves / p.nw;
+  a.nwk = p.nw;
+  a.rw = rw;
+  const int threads = p.nw * rw * kWave;
   const long long nb = (a.N + R - 1) / R;
   const long long cus = device_cus();
-  auto wgs = [&](int bpw) { return (nb + bpw - 1) / bpw * p.splits; };
+  auto wgs = [&](int bpw) { return ((nb + bpw - 1) / bpw + rw - 1) / rw * p.splits; };
   auto busiest = [&](int bpw) { return (wgs(bpw) + cus - 1) / cus * bpw; };
   auto per_cu = [&](int bpw) {
     switch (bpw) {
@@ -397,7 +413,7 @@ void launch_m(const GemvArgs& a, const GemvPlan& p, hipStream_t stream) {
     auto load = [&](int bpw) { return (wgs(bpw) + cus - 1) / cus * (bpw + 2); };
     best = load(4) < load(8) && load(4) < load(16) ? 4 : (load(8) < load(16) ? 8 : 16);
   }
-  const dim3 grid((unsigned)((nb + best - 1) / best), (unsigned)p.splits);
+  const dim3 grid((unsigned)(((nb + best - 1) / best + rw - 1) / rw), (unsigned)p.splits);
   switch (best) {
     case 1: hipLaunchKernelGGL((gemv_instance<M, 1, SYM>()), grid, dim3(threads), 0, stream, a); break;
     case 2: hipLaunchKernelGGL((gemv_instance<M, 2, SYM>()), grid, dim3(threads), 0, stream, a); break;

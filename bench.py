@@ -485,32 +485,145 @@ def rows_convert(torch, w4, wl, reps):
 
 # ----------------------------------------------------------------------------- CPU baseline
 
-def cpu_baseline(wl, budget_s=12.0):
-    """The oracle (dequantize + fp64 linear) over the sweep's linears in block order,
-    until budget_s of CPU time is spent; TB/s of algorithmic bytes."""
-    from oracle import w4a16_oracle as O
+def _cpu_threads():
+    """(threads BLAS uses, os.cpu_count(), CPUs this process may run on)."""
     try:
         from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        blas = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
     except Exception:
-        threads = 1
-    done_bytes, spent, n = 0, 0.0, 0
+        blas = 1
+    try:
+        aff = len(os.sched_getaffinity(0))
+    except Exception:
+        aff = os.cpu_count() or 1
+    return int(blas), int(os.cpu_count() or 1), int(aff)
+
+
+def _cpu_timed(fn, budget_s):
+    """Calls fn() until budget_s of wall time is spent (at least once); (calls, seconds)."""
+    n, spent = 0, 0.0
+    while n == 0 or spent < budget_s:
+        t0 = time.perf_counter()
+        fn()
+        spent += time.perf_counter() - t0
+        n += 1
+    return n, spent
+
+
+def cpu_baseline(wl, gpu_rows=None, budget_s=8.0):
+    """The CPU oracle on bounded samples of the workloads, on this host's cores.
+
+    value: the decode sweep's metric -- oracle dequantize + fp64 linear over the 14
+    linears of the sweep's first two blocks (M = 1), repeated for budget_s; TB/s of
+    algorithmic bytes.  rows: the other steps of the path, each on a sample of its
+    own workload, with the GPU row of the same workload when this run measured it:
+    quantize + pack (NumPy elementwise, one thread), dequantize, the prefill fp64
+    contraction (BLAS, multithreaded) and the AWQ search (reference output plus three
+    candidates of the 30, each a quantize + dequantize + fp64 contraction)."""
+    from oracle import w4a16_oracle as O
+    blas, ncpu, aff = _cpu_threads()
+    gpu = {r["name"]: r for r in (gpu_rows or [])}
+    # decode sweep GEMV (the metric)
     cache = {}
-    while spent < budget_s:
-        for b in range(2):
-            for layer, (_, K, N) in enumerate(wl.BLOCK_LINEARS):
-                if (b, layer) not in cache:
-                    W = wl.decode_weight(b, layer)
-                    cache[(b, layer)] = (wl.decode_act(b, layer, 1), O.quantize_pack(W))
-                X, (qw, sc, qz) = cache[(b, layer)]
-                t0 = time.perf_counter()
-                O.linear(X, O.dequantize(qw, sc, qz, K, False))
-                spent += time.perf_counter() - t0
-                done_bytes += gemv_bytes(1, K, N, False)
-                n += 1
-    return {"value": round(done_bytes / spent / 1e12, 6), "unit": "TB/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"{n} GEMVs over the 14 linears of the first 2 blocks of the decode sweep (M=1), repeated: "
-                      f"oracle dequantize + fp64 linear, {spent:.1f} s of CPU time"}
+    for b in range(2):
+        for layer, (_, K, N) in enumerate(wl.BLOCK_LINEARS):
+            cache[(b, layer)] = (K, N, wl.decode_act(b, layer, 1), O.quantize_pack(wl.decode_weight(b, layer)))
+    done = {"bytes": 0, "n": 0}
+
+    def sweep_pass():
+        for K, N, X, (qw, sc, qz) in cache.values():
+            O.linear(X, O.dequantize(qw, sc, qz, K, False))
+            done["bytes"] += gemv_bytes(1, K, N, False)
+            done["n"] += 1
+    _, spent = _cpu_timed(sweep_pass, budget_s)
+    out = {"value": round(done["bytes"] / spent / 1e12, 6), "unit": "TB/s", "cores": blas, "kind": "oracle",
+           "sample": f"{done['n']} GEMVs over the 14 linears of the first 2 blocks of the decode sweep (M=1), "
+                     f"repeated: oracle dequantize + fp64 linear, {spent:.1f} s",
+           "cpu_count": ncpu, "affinity_cpus": aff, "blas_threads": blas}
+    rows = []
+    # quantize + pack and dequantize: one 27B-shaped symmetric linear, a slice of 2048 rows
+    K, N = wl.LARGE_SHAPES[0]
+    W = wl.large_weight(0)[:2048]
+    n, t = _cpu_timed(lambda: O.quantize_pack(W, None, 1.0, True), 1.0)
+    nb = W.size * 2 + packed_bytes(W.shape[0], K, True)
+    row = {"name": f"oracle quantize_pack sym K={K}, {W.shape[0]} of N={N} rows", "GB/s": round(nb * n / t / 1e9, 3),
+           "threads": 1, "seconds": round(t, 2)}
+    g = [r for r in gpu.values() if r["name"].startswith(f"quantize_pack sym K={K}")]
+    if g:
+        row["gpu_GB/s"] = g[0]["GB/s"]
+        row["gpu_speedup"] = round(g[0]["GB/s"] / row["GB/s"], 1)
+    rows.append(row)
+    qw, sc, _ = O.quantize_pack(W, None, 1.0, True)
+    n, t = _cpu_timed(lambda: O.dequantize(qw, sc, None, K, True), 1.0)
+    rows.append({"name": f"oracle dequantize sym K={K}, {W.shape[0]} rows",
+                 "GB/s": round(packed_bytes(W.shape[0], K, True) * n / t / 1e9, 3), "threads": 1,
+                 "seconds": round(t, 2)})
+    # prefill contraction: the first prefill shape, all 2048 rows, fp64 (BLAS)
+    X, Wp = wl.prefill(0)
+    Kp, Np = wl.PREFILL_SHAPES[0]
+    qp = O.quantize_pack(Wp)
+    What = O.dequantize(*qp, Kp, False)
+    n, t = _cpu_timed(lambda: O.linear(X, What), 1.0)
+    fl = 2 * X.shape[0] * Kp * Np
+    row = {"name": f"oracle fp64 linear M={X.shape[0]} K={Kp} N={Np}", "GFLOP/s": round(fl * n / t / 1e9, 2),
+           "threads": blas, "seconds": round(t, 2)}
+    g = [r for r in gpu.values() if r["name"].startswith(f"gemm prefill M={X.shape[0]} K={Kp} N={Np}")]
+    if g:
+        row["gpu_TFLOP/s"] = g[0]["TFLOP/s"]
+        row["gpu_speedup"] = round(g[0]["TFLOP/s"] * 1e3 / row["GFLOP/s"], 1)
+    rows.append(row)
+    del X, Wp, What
+    # AWQ search: reference output and 3 of the 30 candidates; scaled to the full search
+    Xs, Ws = wl.awq_calibration()
+    t0 = time.perf_counter()
+    m = O.act_mean_abs(Xs)
+    Yref = O.reference_output(Xs, Ws)
+    for a in (0.0, 0.25, 0.5):
+        O.candidate_loss(Xs, Ws, O.awq_scales(m, a), 1.0, False, Yref)
+    t = time.perf_counter() - t0
+    full_s = t / 4 * 31
+    row = {"name": "oracle AWQ search T=4096 K=2048 N=6144: reference + 3 of 30 candidates",
+           "seconds": round(t, 2), "threads": blas, "full_search_estimate_s": round(full_s, 1)}
+    g = [r for r in gpu.values() if r["name"].startswith("awq_search T=4096")]
+    if g:
+        row["gpu_ms"] = g[0]["us"] / 1e3
+        row["gpu_speedup"] = round(full_s * 1e3 / row["gpu_ms"], 1)
+    rows.append(row)
+    out["rows"] = rows
+    return out
+
+
+def trace_summary(trace_dir):
+    """Kernel durations inside the timed region of a rocprofv3 kernel trace of this
+    script (--kernel-trace --output-format csv): the dispatches that start after the
+    first launch of the empty probe kernel ends and end before the second starts.
+    Prints one JSON line per kernel name: dispatches, mean / median / min duration
+    (us) and the region's wall time."""
+    import csv
+    import glob
+    path = sorted(glob.glob(os.path.join(trace_dir, "**", "*kernel_trace.csv"), recursive=True))
+    if not path:
+        print(f"no kernel_trace.csv under {trace_dir}", file=sys.stderr)
+        return 2
+    rows = list(csv.DictReader(open(path[0])))
+    rows.sort(key=lambda r: int(r["Start_Timestamp"]))
+    marks = [r for r in rows if "empty_kernel" in r["Kernel_Name"]][:2]
+    if len(marks) < 2:
+        print("the trace holds no timed-region markers", file=sys.stderr)
+        return 2
+    lo, hi = int(marks[0]["End_Timestamp"]), int(marks[1]["Start_Timestamp"])
+    inside = [r for r in rows if int(r["Start_Timestamp"]) >= lo and int(r["End_Timestamp"]) <= hi]
+    by = {}
+    for r in inside:
+        by.setdefault(r["Kernel_Name"], []).append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    first = min(int(r["Start_Timestamp"]) for r in inside)
+    last = max(int(r["End_Timestamp"]) for r in inside)
+    for name, d in sorted(by.items(), key=lambda kv: -sum(kv[1])):
+        d = sorted(d)
+        print(json.dumps({"kernel": name, "dispatches": len(d), "mean_us": round(sum(d) / len(d), 3),
+                          "median_us": round(d[len(d) // 2], 3), "min_us": round(d[0], 3),
+                          "sum_us": round(sum(d), 1), "region_us": round((last - first) / 1e3, 1)}))
+    return 0
 
 
 # ----------------------------------------------------------------------------- main
@@ -527,9 +640,14 @@ def main(argv=None):
     ap.add_argument("--blocks", type=int, default=28)
     ap.add_argument("--skip-step", action="store_true",
                     help="profiling aid: skip the decode-sweep step (value is null) and run only --only rows")
+    ap.add_argument("--trace-summary", default="", metavar="DIR",
+                    help="print the kernel durations inside the timed step of a rocprofv3 kernel trace "
+                         "of this script written under DIR, and exit (no GPU)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="counter calibration: run only a plain device copy of MIB MiB ten times and exit")
     args = ap.parse_args(argv)
+    if args.trace_summary:
+        return trace_summary(args.trace_summary)
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: the library has no multi-GPU path (the kernels would shard by "
               "output rows with no exchange). Run with --gpus 1.", file=sys.stderr)
@@ -587,10 +705,14 @@ def main(argv=None):
             graph.replay()
         torch.cuda.synchronize()
         s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        # the first two launches of the empty probe kernel in the run bracket the timed
+        # region, so that a kernel trace of this run can be cut to it (--trace-summary)
+        w4.probe_empty()
         s.record()
         for _ in range(args.steps):
             graph.replay()
         e.record()
+        w4.probe_empty()
         torch.cuda.synchronize()
         ms_step = s.elapsed_time(e) / args.steps
         value = step_bytes / (ms_step * 1e-3) / 1e12
@@ -685,7 +807,7 @@ def main(argv=None):
             out["prefill_gemm_frac"] = [r["frac"] for r in pre]
     if not args.no_cpu:
         log("cpu baseline (oracle)")
-        out["cpu_baseline"] = cpu_baseline(wl)
+        out["cpu_baseline"] = cpu_baseline(wl, out.get("rows"))
     print(json.dumps(out), flush=True)
     return 0
 

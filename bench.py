@@ -756,7 +756,7 @@ def main(argv=None):
                                  sum(l.nbytes for l in fs), ms, {"launches": len(fs)}))
             del g, fs
             torch.cuda.empty_cache()
-        for M in ((1, 4, 16) if "w4a8" in want and packed else ()):
+        for M in ((1, 4, 8, 16) if "w4a8" in want and packed else ()):
             log(f"W4A8 decode sweep M={M}")
             sw = w4a8_sweep_launches(torch, w4, wl, packed, M)
             g = capture_graph(torch, sw)
@@ -770,7 +770,7 @@ def main(argv=None):
                                  sum(l.nbytes for l in sw), ms, {"launches": len(sw)}))
             del g, sw
             torch.cuda.empty_cache()
-        for M in ((4, 16) if "sweeps" in want and packed else ()):
+        for M in ((4, 8, 16) if "sweeps" in want and packed else ()):
             log(f"decode sweep M={M}")
             sw = sweep_launches(torch, w4, wl, packed, M)
             g = capture_graph(torch, sw)

@@ -22,9 +22,10 @@
  *   - bf16 values are passed as uint16_t bit patterns.
  *   - Array pointers are DEVICE pointers owned by the caller unless a parameter
  *     says "host".  The library never frees caller memory and never allocates
- *     device memory, except: awq_search and awq_search_lookahead allocate their
- *     workspace themselves when the caller passes none (see there).  Every
- *     kernel is the library's own; it links nothing beyond the HIP runtime.
+ *     device memory: scratch space comes in through a caller workspace (with a
+ *     size query), or, for w4a16_gemv_noalloc, from one static array per device
+ *     that exists while the library is loaded.  Every kernel is the library's
+ *     own; it links nothing beyond the HIP runtime.
  *   - `stream` is a hipStream_t (NULL = the default stream).  Work is enqueued
  *     asynchronously on it; results are ready once the stream is synchronized.
  *     awq_search and awq_search_lookahead are the calls that synchronize (they
@@ -278,8 +279,8 @@ int awq_clip_search(const uint16_t* X, int T, int K, int N, const uint16_t* W, c
  *   alpha_index, ratio_index: host int out.   s_out [K] fp32 device out: s(alpha*).
  *   workspace / workspace_bytes: as awq_grid_loss with C = max(n_alpha, n_ratio) plus
  *   the statistic; workspace == NULL and workspace_bytes != NULL -> size query.
- *   workspace == NULL and workspace_bytes == NULL -> the call allocates and frees
- *   its own workspace.  Synchronizes `stream` (twice).
+ *   The workspace is required: W4_ERR_WORKSPACE when it is NULL (without a size
+ *   query) or smaller than the query's answer.  Synchronizes `stream` (twice).
  */
 int awq_search(const uint16_t* X, int T, int K, int N, const uint16_t* W,
                const double* alphas, int n_alpha, const double* ratios, int n_ratio,
@@ -374,9 +375,8 @@ int awq_lookahead_loss(const uint16_t* X, int B, int L, int hidden, int n_q, int
  *   alphas [n_alpha], ratios [n_ratio]: host fp64 (1 <= n <= 64 each; alphas in
  *   [0, 16], ratios in (0, 1]).  losses_out [n_alpha + n_ratio]: host fp32 out
  *   (d = 1 losses).  alpha_index, ratio_index: host int out.  s_out [K] fp32
- *   device out: s(alpha*).  Workspace as in awq_search (NULL workspace and NULL
- *   workspace_bytes: the call allocates and frees its own).  Synchronizes
- *   `stream` (three times).
+ *   device out: s(alpha*).  Workspace as in awq_search (size query, then
+ *   required).  Synchronizes `stream` (three times).
  */
 int awq_search_lookahead(const uint16_t* X, int B, int L, int hidden, int n_q, int n_kv, int inter,
                          const w4_block* blk, const w4_block* next, int linear, const double* alphas,

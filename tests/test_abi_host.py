@@ -183,6 +183,13 @@ def test_search_validation(lib):
     badr = (D * 1)(0.0)
     assert f(A, 64, 256, 8, A, al, 20, badr, 1, 0, 128, None, None, None, None, None, ctypes.byref(sz), None) == -7
     assert f(A, 64, 256, 8, A, None, 20, ra, 10, 0, 128, None, None, None, None, None, ctypes.byref(sz), None) == -1
+    # the workspace is required: the library allocates nothing of its own
+    lo, ia, ir = (ctypes.c_float * 30)(), ctypes.c_int(0), ctypes.c_int(0)
+    outs = (lo, ctypes.byref(ia), ctypes.byref(ir), A)
+    assert f(A, 64, 256, 8, A, al, 20, ra, 10, 0, 128, *outs, None, None, None) == -5
+    assert f(A, 64, 256, 8, A, al, 20, ra, 10, 0, 128, None, None, None, None, None, ctypes.byref(sz), None) == 0
+    small = ctypes.c_size_t(sz.value - 1)
+    assert f(A, 64, 256, 8, A, al, 20, ra, 10, 0, 128, *outs, A, ctypes.byref(small), None) == -5
 
 
 def test_clip_search_validation(lib):
@@ -261,6 +268,9 @@ def test_block_and_lookahead_validation(lib):
     badr = (D * 1)(1.5)
     assert h(A, 8, 512, 2048, 16, 8, 6144, ctypes.byref(blk), None, 0, al, 20, badr, 1, 0, 128, None, None, None, None,
              None, ctypes.byref(sz), None) == -7
+    lo, ia, ir = (ctypes.c_float * 30)(), ctypes.c_int(0), ctypes.c_int(0)
+    assert h(A, 8, 512, 2048, 16, 8, 6144, ctypes.byref(blk), None, 0, al, 20, ra, 10, 0, 128, lo, ctypes.byref(ia),
+             ctypes.byref(ir), A, None, None, None) == -5
 
 
 def test_block_forward_quantized_validation(lib):

@@ -418,19 +418,11 @@ extern "C" int awq_search(const uint16_t* X, int T, int K, int N, const uint16_t
     *workspace_bytes = L.total;
     return W4_OK;
   }
-  if (workspace && (!workspace_bytes || *workspace_bytes < L.total)) return W4_ERR_WORKSPACE;
+  if (!workspace || !workspace_bytes || *workspace_bytes < L.total) return W4_ERR_WORKSPACE;
   if (!X || !W || !losses_out || !alpha_index || !ratio_index || !s_out) return W4_ERR_NULL;
   if (misaligned(X) || misaligned(W) || misaligned(s_out) || misaligned(workspace)) return W4_ERR_ALIGN;
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  if (workspace) return search_impl(X, T, K, N, W, alphas, n_alpha, ratios, n_ratio, symmetric, losses_out,
-                                    alpha_index, ratio_index, s_out, static_cast<char*>(workspace), L, s);
-  void* own = nullptr;
-  if (hipMalloc(&own, L.total) != hipSuccess) return W4_ERR_HIP;
-  st = search_impl(X, T, K, N, W, alphas, n_alpha, ratios, n_ratio, symmetric, losses_out, alpha_index,
-                   ratio_index, s_out, static_cast<char*>(own), L, s);
-  const hipError_t fe = hipFree(own);
-  if (st == W4_OK && fe != hipSuccess) st = W4_ERR_HIP;
-  return st;
+  return search_impl(X, T, K, N, W, alphas, n_alpha, ratios, n_ratio, symmetric, losses_out, alpha_index,
+                     ratio_index, s_out, static_cast<char*>(workspace), L, static_cast<hipStream_t>(stream));
 }
 
 namespace {
@@ -533,22 +525,13 @@ extern "C" int awq_search_lookahead(const uint16_t* X, int B, int L, int hidden,
     *workspace_bytes = l.total;
     return W4_OK;
   }
-  if (workspace && (!workspace_bytes || *workspace_bytes < l.total)) return W4_ERR_WORKSPACE;
+  if (!workspace || !workspace_bytes || *workspace_bytes < l.total) return W4_ERR_WORKSPACE;
   if (!X || !losses_out || !alpha_index || !ratio_index || !s_out || block_null(blk) || (next && block_null(next)))
     return W4_ERR_NULL;
   if (misaligned(X) || misaligned(s_out) || misaligned(workspace) || block_misaligned(blk) ||
       (next && block_misaligned(next)))
     return W4_ERR_ALIGN;
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  if (workspace)
-    return look_search_impl(X, B, L, hidden, n_q, n_kv, inter, *blk, next, linear, alphas, n_alpha, ratios, n_ratio,
-                            symmetric, losses_out, alpha_index, ratio_index, s_out, static_cast<char*>(workspace), l,
-                            s);
-  void* own = nullptr;
-  if (hipMalloc(&own, l.total) != hipSuccess) return W4_ERR_HIP;
-  st = look_search_impl(X, B, L, hidden, n_q, n_kv, inter, *blk, next, linear, alphas, n_alpha, ratios, n_ratio,
-                        symmetric, losses_out, alpha_index, ratio_index, s_out, static_cast<char*>(own), l, s);
-  const hipError_t fe = hipFree(own);
-  if (st == W4_OK && fe != hipSuccess) st = W4_ERR_HIP;
-  return st;
+  return look_search_impl(X, B, L, hidden, n_q, n_kv, inter, *blk, next, linear, alphas, n_alpha, ratios, n_ratio,
+                          symmetric, losses_out, alpha_index, ratio_index, s_out, static_cast<char*>(workspace), l,
+                          static_cast<hipStream_t>(stream));
 }

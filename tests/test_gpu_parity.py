@@ -233,13 +233,18 @@ def test_gemv_large_full_size(shape, M):
 
 @pytest.mark.parametrize("M,K,N", [(1, 2048, 40000), (2, 2048, 40000), (4, 2048, 36000), (16, 2048, 30000),
                                    (16, 2048, 4104), (8, 2048, 4104), (4, 2048, 8211), (8, 2048, 17942),
-                                   (1, 5120, 25601)])
+                                   (1, 5120, 25601), (3, 2048, 36000), (5, 4096, 4104), (12, 8192, 1000),
+                                   (6, 6144, 4100), (10, 2048, 2000)])
 def test_gemv_tall_random_codes(M, K, N):
     """Tall linears: enough rows that every workgroup gets several row batches
     (and, for the larger M, several rounds of workgroups); the row counts are
-    picked so that the launch plan takes each of its batch counts (2, 3, 4, 5, 6,
-    8, 16 batches per workgroup) for some M.  The packed operands are drawn
-    directly (random codes, scales and zero words); oracle on every 16th row."""
+    picked so that the launch plans take each of their batch counts for some M,
+    on both forms of the GEMV: the VALU form (2, 3, 4, 5, 6, 8, 16 row batches per
+    workgroup) and the matrix-core form (1 to 8 column blocks per slab; 2 groups per
+    wave up to K = 4096 and 4 above, with a K split at K = 8192; entered at M = 3
+    on a 36.9 MB weight, at M = 5 from N = 4096 and at M = 10 otherwise).  The
+    packed operands are drawn directly (random codes, scales and zero words);
+    oracle on every 16th row."""
     rng = np.random.default_rng(1000 + M + N)
     qw = rng.integers(0, 2 ** 32, size=(N, K // 8), dtype=np.uint64).astype(np.uint32)
     sc = O.f32_to_bf16((np.abs(rng.standard_normal((N, K // 128))) * 2e-3 + 1e-4).astype(np.float32))
@@ -256,11 +261,14 @@ def test_gemv_tall_random_codes(M, K, N):
         assert _elementwise_ok(y, ref) == 0
 
 
-@pytest.mark.parametrize("M,K,N", [(1, 33792, 96), (16, 17408, 200), (1, 2048, 4096), (4, 6144, 2048)])
+@pytest.mark.parametrize("M,K,N", [(1, 33792, 96), (16, 17408, 200), (1, 2048, 4096), (4, 6144, 2048),
+                                   (12, 2048, 4096), (16, 256, 300)])
 def test_gemv_deterministic_and_overwrites(M, K, N):
     """Y prefilled with NaN is fully overwritten and two calls agree bit for bit, on
-    the direct store (K = 2048), the cross-wave LDS sum (K = 6144) and the K split
-    with its second reduction kernel (K = 33792 at M = 1, K = 17408 at M = 16)."""
+    the direct store (K = 2048 at M = 1; the matrix-core form with one wave per
+    slab at K = 256), the cross-wave LDS sums (K = 6144 at M = 4; the matrix-core
+    form at K = 2048, M = 12) and the K split with its second reduction kernel
+    (K = 33792 at M = 1, K = 17408 at M = 16)."""
     X, W = wl.small_case(M, K, N, 91)
     qw, sc, qz = _packed(W, False)
     args = (to_bf16(X), to_i32(qw), to_bf16(sc), to_i32(qz), False)

@@ -65,6 +65,28 @@ __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
                                          __builtin_bit_cast(bf16x2, b), c, false);
 }
 
+// Raw buffer resource over [base, base + bytes) (gfx9 word 3: untyped, range
+// checked).  A load whose byte offset is >= bytes returns 0 and touches no memory.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+// Lane offset that keeps every load out of range: all buffers here are smaller than
+// 2^31 bytes, so row offset + kOob neither wraps nor lands in range.
+constexpr uint32_t kOob = 0x80000000u;
+
+// permlane32 swap of (x, y): lanes 0-31 end up with (x, x of lane + 32), lanes 32-63
+// with (y of lane - 32, y); the sum of the pair is x summed over lanes l, l + 32 in
+// the lower half and y summed over them in the upper half.  permlane16 likewise
+// for lanes 16 apart (even 16-lane rows keep x, odd rows y).
+__device__ __forceinline__ float swap_sum32(float x, float y) {
+  const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(y), false, false);
+  return __uint_as_float(p[0]) + __uint_as_float(p[1]);
+}
+__device__ __forceinline__ float swap_sum16(float x, float y) {
+  const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(y), false, false);
+  return __uint_as_float(p[0]) + __uint_as_float(p[1]);
+}
+
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, kWave);

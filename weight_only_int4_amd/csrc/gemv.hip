@@ -47,15 +47,6 @@ struct GemvArgs {
   int rw;               // slabs per workgroup (one group of nwk waves each)
 };
 
-// Raw buffer resource over [base, base + bytes) (gfx9 word 3: untyped, range
-// checked).  A load whose byte offset is >= bytes returns 0 and touches no memory.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
-}
-// Lane offset that keeps every load out of range: all buffers here are smaller than
-// 2^31 bytes, so row offset + kOob neither wraps nor lands in range.
-constexpr uint32_t kOob = 0x80000000u;
-
 template <int WPL>
 __device__ __forceinline__ void load_words(__amdgpu_buffer_rsrc_t r, uint32_t off, uint32_t* w) {
   if constexpr (WPL == 4) {
@@ -73,19 +64,6 @@ template <int CTRL>
 __device__ __forceinline__ float dpp(float v) {
   return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, true));
 }
-// permlane32 swap of (x, y): lanes 0-31 end up with (x, x of lane + 32), lanes 32-63
-// with (y of lane - 32, y); the sum of the pair is x summed over lanes l, l + 32 in
-// the lower half and y summed over them in the upper half.  permlane16 likewise
-// for lanes 16 apart (even 16-lane rows keep x, odd rows y).
-__device__ __forceinline__ float swap_sum32(float x, float y) {
-  const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(y), false, false);
-  return __uint_as_float(p[0]) + __uint_as_float(p[1]);
-}
-__device__ __forceinline__ float swap_sum16(float x, float y) {
-  const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(y), false, false);
-  return __uint_as_float(p[0]) + __uint_as_float(p[1]);
-}
-
 // keep + the partner's `send`, partners paired by lane bit B:
 //   B = 3, 2: the mirrors l <-> 15 - l, l <-> 7 - l inside each 16-lane row;
 //   B = 1, 0: l ^ 2, l ^ 1 (quad permutations).
@@ -438,6 +416,7 @@ void launch_sym(const GemvArgs& a, const GemvPlan& p, bool symmetric, hipStream_
 
 size_t gemv_workspace_bytes(int M, int K, int N) {
   if (M <= 0 || N <= 0 || K <= 0) return 0;
+  if (gemv_use_mfma(M, K, N)) return gemv_mfma_workspace_bytes(M, K, N);
   const GemvPlan p = plan_gemv(M, K);
   return p.splits > 1 ? (size_t)p.splits * M * N * sizeof(float) : 0;
 }
@@ -446,6 +425,8 @@ int launch_gemv(const uint16_t* X, int M, int K, int N, const uint32_t* qweight,
                 const uint16_t* scales, const uint32_t* qzeros, int symmetric, uint16_t* Y,
                 void* workspace, hipStream_t stream) {
   if (M == 0 || N == 0) return W4_OK;
+  if (M <= W4_GEMV_MAX_M && gemv_use_mfma(M, K, N))
+    return launch_gemv_mfma(X, M, K, N, qweight, scales, qzeros, symmetric, Y, workspace, stream);
   // buffer loads take 32-bit byte offsets: every operand below 2^31 bytes
   // (packed words N K / 2, activations 2 M K)
   if ((long long)N * K / 2 >= (1LL << 31) || 2LL * M * K >= (1LL << 31)) return W4_ERR_SHAPE;
@@ -473,11 +454,15 @@ int launch_gemv(const uint16_t* X, int M, int K, int N, const uint32_t* qweight,
   }
   W4_CHECK_LAUNCH();
   if (p.splits > 1) {
-    const size_t MN = (size_t)M * N;
-    hipLaunchKernelGGL(gemv_split_reduce, dim3((unsigned)((MN + 255) / 256)), dim3(256), 0, stream,
-                       static_cast<const float*>(workspace), p.splits, MN, Y);
-    W4_CHECK_LAUNCH();
+    return launch_gemv_split_reduce(static_cast<const float*>(workspace), p.splits, (size_t)M * N, Y, stream);
   }
+  return W4_OK;
+}
+
+int launch_gemv_split_reduce(const float* partial, int splits, size_t MN, uint16_t* Y, hipStream_t stream) {
+  hipLaunchKernelGGL(gemv_split_reduce, dim3((unsigned)((MN + 255) / 256)), dim3(256), 0, stream, partial, splits,
+                     MN, Y);
+  W4_CHECK_LAUNCH();
   return W4_OK;
 }
 

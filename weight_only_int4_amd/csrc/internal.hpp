@@ -28,10 +28,19 @@ struct QuantArgs {
 int launch_quantize_pack(const QuantArgs& a, int C, hipStream_t stream);
 
 // ---------------------------------------------------------------- GEMV (M <= 16)
+// Whether a decode GEMV of this shape runs on the matrix cores (gemv_mfma.hip)
+// instead of the vector ALUs (gemv.hip).
+bool gemv_use_mfma(int M, int K, int N);
 size_t gemv_workspace_bytes(int M, int K, int N);
 int launch_gemv(const uint16_t* X, int M, int K, int N, const uint32_t* qweight,
                 const uint16_t* scales, const uint32_t* qzeros, int symmetric, uint16_t* Y,
                 void* workspace, hipStream_t stream);
+size_t gemv_mfma_workspace_bytes(int M, int K, int N);
+int launch_gemv_mfma(const uint16_t* X, int M, int K, int N, const uint32_t* qweight,
+                     const uint16_t* scales, const uint32_t* qzeros, int symmetric, uint16_t* Y,
+                     void* workspace, hipStream_t stream);
+// Y[i] = bf16(sum over k < splits of partial[k * MN + i]), in split order.
+int launch_gemv_split_reduce(const float* partial, int splits, size_t MN, uint16_t* Y, hipStream_t stream);
 
 // ---------------------------------------------------------------- W4A8 decode (M <= 16)
 int launch_w4a8_quantize(const uint16_t* X, int M, int K, int8_t* Xq, float* sx, int32_t* xsum,

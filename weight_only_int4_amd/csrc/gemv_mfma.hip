@@ -87,7 +87,11 @@ __global__ __launch_bounds__(max_waves(KT) * 64) void gemv_mfma_kernel(MfmaArgs 
   const auto rsc = make_rsrc(a.scales, (uint32_t)a.N * srow);
   const auto rzp = make_rsrc(SYM ? static_cast<const void*>(a.scales) : a.qzeros, SYM ? 0u : (uint32_t)a.N * zrow);
   const auto rx = make_rsrc(a.X, (uint32_t)a.M * (uint32_t)a.K * 2u);
-  const int n_first = ((int)blockIdx.x * a.rw + slab) * bpw * kBlockCols;
+  // slab S of TS takes the blocks S, S + TS, S + 2 TS, ... (block b of the slab starts
+  // at column n_first + b * n_step), so that the blocks spread evenly over the slabs
+  const int TS = (int)gridDim.x * a.rw;
+  const int n_first = ((int)blockIdx.x * a.rw + slab) * kBlockCols;
+  const int n_step = TS * kBlockCols;
 
   // byte offsets inside one row of each array; out of range for groups past the split
   uint32_t kw[KT], ks[KT];
@@ -124,13 +128,13 @@ __global__ __launch_bounds__(max_waves(KT) * 64) void gemv_mfma_kernel(MfmaArgs 
     uint32_t z;
   };
   // Block b of the slab (past N: nothing read).  Packed words: lanes 4 c .. 4 c + 3
-  // read the 64 bytes of column n_first + 16 b + c in one group, so that every four
+  // read the 64 bytes of column n_first + b n_step + c in one group, so that every four
   // consecutive lanes hit one cache line; the lanes trade them into the operand
   // layout before use (see process).  Scale and zero word: this lane's own column
-  // n_first + 16 b + j.  The row offsets are computed per load, not kept per block.
+  // n_first + b n_step + j.  The row offsets are computed per load, not kept per block.
   auto load = [&](int b, Batch& B) {
-    const uint32_t n = (uint32_t)min(n_first + b * kBlockCols + j, a.N);
-    const uint32_t nw = (uint32_t)min(n_first + b * kBlockCols + (lane >> 2), a.N);
+    const uint32_t n = (uint32_t)min(n_first + b * n_step + j, a.N);
+    const uint32_t nw = (uint32_t)min(n_first + b * n_step + (lane >> 2), a.N);
     const uint32_t ow = opaque_vgpr(nw * wrow), os = opaque_vgpr(n * srow);
 #pragma unroll
     for (int t = 0; t < KT; ++t) {
@@ -209,7 +213,7 @@ __global__ __launch_bounds__(max_waves(KT) * 64) void gemv_mfma_kernel(MfmaArgs 
       for (int i = 0; i < 4; ++i) acc[i] = fmaf(sc, tile[i], acc[i]);
     }
     if (a.nwk == 1) {
-      const int n = n_first + b * kBlockCols + j;
+      const int n = n_first + b * n_step + j;
 #pragma unroll
       for (int i = 0; i < 4; ++i)
         if (4 * q + i < a.M && n < a.N) store(4 * q + i, n, acc[i]);
@@ -236,7 +240,7 @@ __global__ __launch_bounds__(max_waves(KT) * 64) void gemv_mfma_kernel(MfmaArgs 
       const int sl = e / E, r = e - sl * E;
       const int b = r / (a.M * kBlockCols), r2 = r - b * (a.M * kBlockCols);
       const int m = r2 / kBlockCols, c = r2 - m * kBlockCols;
-      const int n = ((int)blockIdx.x * a.rw + sl) * bpw * kBlockCols + b * kBlockCols + c;
+      const int n = ((int)blockIdx.x * a.rw + sl) * kBlockCols + b * n_step + c;
       if (n < a.N) {
         const int src = c + 16 * (m >> 2);
         float s = 0.0f;
@@ -304,11 +308,9 @@ int device_cu_count() {
   return n;
 }
 
-// Blocks per slab: among 1, 2, 3, 4, 6 and 8 (as far as the partial tiles fit in
-// LDS), those with which one round of resident workgroups covers all blocks; the
-// fewest of them, unless another gives the busiest CU at least 10% fewer blocks.
-// When none fits, the one that gives the busiest CU the least work, counting two
-// blocks' worth per workgroup for its activation loads.
+// Blocks per slab: the fewest (1 to 8) with which one round of resident
+// workgroups covers every block (the slabs take the blocks round-robin, so each
+// holds that many or one less); when no count fits one round, the largest.
 template <int KT, bool SYM>
 void launch_kt(MfmaArgs a, const MfmaPlan& p, hipStream_t stream) {
   const int rw = p.nwk >= kWgWaves ? 1 : kWgWaves / p.nwk;
@@ -320,15 +322,15 @@ void launch_kt(MfmaArgs a, const MfmaPlan& p, hipStream_t stream) {
   const long long cus = device_cu_count();
   const int qm = (a.M + 3) / 4;
   auto lds = [&](int bpw) { return p.nwk > 1 ? (size_t)rw * p.nwk * bpw * qm * 16 * sizeof(f32x4) : (size_t)0; };
-  auto wgs = [&](int bpw) { return ((nb + bpw - 1) / bpw + rw - 1) / rw * p.splits; };
-  auto busiest = [&](int bpw) { return (wgs(bpw) + cus - 1) / cus * bpw; };
   auto by_regs = [&](int bpw) {
     switch (bpw) {
       case 1: return mfma_blocks_per_cu<KT, clamp_bpw(KT, SYM, 1), SYM>(threads);
       case 2: return mfma_blocks_per_cu<KT, clamp_bpw(KT, SYM, 2), SYM>(threads);
       case 3: return mfma_blocks_per_cu<KT, clamp_bpw(KT, SYM, 3), SYM>(threads);
       case 4: return mfma_blocks_per_cu<KT, clamp_bpw(KT, SYM, 4), SYM>(threads);
+      case 5: return mfma_blocks_per_cu<KT, clamp_bpw(KT, SYM, 5), SYM>(threads);
       case 6: return mfma_blocks_per_cu<KT, clamp_bpw(KT, SYM, 6), SYM>(threads);
+      case 7: return mfma_blocks_per_cu<KT, clamp_bpw(KT, SYM, 7), SYM>(threads);
       default: return mfma_blocks_per_cu<KT, clamp_bpw(KT, SYM, 8), SYM>(threads);
     }
   };
@@ -337,19 +339,12 @@ void launch_kt(MfmaArgs a, const MfmaPlan& p, hipStream_t stream) {
     const long long r = by_regs(bpw);
     return l ? std::min<long long>(r, (long long)(kLdsPerCu / l)) : r;
   };
-  auto load_cost = [&](int bpw) { return (wgs(bpw) + cus * per_cu(bpw) - 1) / (cus * per_cu(bpw)) * (bpw + 2); };
-  int first = 0, best = 0, least = 0;
-  for (int b : {1, 2, 3, 4, 6, 8}) {
-    if (b > max_bpw(KT, SYM) || lds(b) > kMaxLds || per_cu(b) < 1) continue;
-    if (least == 0 || load_cost(b) < load_cost(least)) least = b;
-    if (wgs(b) > cus * per_cu(b)) continue;
-    if (first == 0)
-      first = best = b;
-    else if (busiest(b) < busiest(best))
-      best = b;
+  auto wgs = [&](int bpw) { return ((nb + bpw - 1) / bpw + rw - 1) / rw * p.splits; };
+  int best = 1;
+  for (int b = 1; b <= max_bpw(KT, SYM) && lds(b) <= kMaxLds; ++b) {
+    best = b;
+    if (wgs(b) <= cus * per_cu(b)) break;
   }
-  if (first != 0 && 10 * busiest(best) > 9 * busiest(first)) best = first;
-  if (best == 0) best = least;
   const dim3 grid((unsigned)(((nb + best - 1) / best + rw - 1) / rw), (unsigned)p.splits);
   const size_t sh = lds(best);
   switch (best) {
@@ -357,7 +352,9 @@ void launch_kt(MfmaArgs a, const MfmaPlan& p, hipStream_t stream) {
     case 2: hipLaunchKernelGGL((gemv_mfma_kernel<KT, clamp_bpw(KT, SYM, 2), SYM>), grid, dim3(threads), sh, stream, a); break;
     case 3: hipLaunchKernelGGL((gemv_mfma_kernel<KT, clamp_bpw(KT, SYM, 3), SYM>), grid, dim3(threads), sh, stream, a); break;
     case 4: hipLaunchKernelGGL((gemv_mfma_kernel<KT, clamp_bpw(KT, SYM, 4), SYM>), grid, dim3(threads), sh, stream, a); break;
+    case 5: hipLaunchKernelGGL((gemv_mfma_kernel<KT, clamp_bpw(KT, SYM, 5), SYM>), grid, dim3(threads), sh, stream, a); break;
     case 6: hipLaunchKernelGGL((gemv_mfma_kernel<KT, clamp_bpw(KT, SYM, 6), SYM>), grid, dim3(threads), sh, stream, a); break;
+    case 7: hipLaunchKernelGGL((gemv_mfma_kernel<KT, clamp_bpw(KT, SYM, 7), SYM>), grid, dim3(threads), sh, stream, a); break;
     default: hipLaunchKernelGGL((gemv_mfma_kernel<KT, clamp_bpw(KT, SYM, 8), SYM>), grid, dim3(threads), sh, stream, a); break;
   }
 }

@@ -238,9 +238,9 @@ int launch_gemm(const uint16_t* X, int M, int K, int N, const uint32_t* qweight,
   if (tiles > 0x7FFFFFFFLL) return W4_ERR_SHAPE;
   const dim3 grid((unsigned)tiles, (unsigned)splits, 1);
   if (gemm_core_wide(tiles * splits))
-    hipLaunchKernelGGL((gemm_core_kernel<true, EPI_STORE, true>), grid, dim3(kGemmWaves * 64), 0, stream, a);
+    hipLaunchKernelGGL((gemm_core_kernel<EPI_STORE, true>), grid, dim3(kGemmWaves * 64), 0, stream, a);
   else
-    hipLaunchKernelGGL((gemm_core_kernel<true, EPI_STORE>), grid, dim3(kGemmWaves * 64), 0, stream, a);
+    hipLaunchKernelGGL((gemm_core_kernel<EPI_STORE>), grid, dim3(kGemmWaves * 64), 0, stream, a);
   W4_CHECK_LAUNCH();
   if (splits > 1) {
     const size_t count = (size_t)M * N;

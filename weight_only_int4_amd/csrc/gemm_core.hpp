@@ -1,6 +1,6 @@
 // MFMA core of the W4A16 prefill contraction, shared by w4a16_gemm and the AWQ
-// grid loss.  Y = X W_hat^T with X bf16 [M][K] and W_hat given either as packed
-// int4 groups (q - z) * sc or, for the unquantized reference, as bf16 [N][K].
+// grid loss.  Y = X W_hat^T with X bf16 [M][K] and W_hat given as packed int4
+// groups (q - z) * sc.
 //
 // Workgroup tile 64 x 128, 4 waves: wave w computes all 64 rows of columns
 // 32 w .. +31 as 2 v_mfma_f32_32x32x16_bf16 blocks, so every packed weight word is
@@ -55,11 +55,9 @@ constexpr int kBN = 128;
 enum { EPI_STORE = 0, EPI_SQDIFF = 1 };
 
 struct GemmCoreArgs {
-  const uint16_t* X;       // [M][K] bf16 (+ z * x_stride); int4 weights: pair-arranged, rows up to M
-                           // rounded to 128 readable
+  const uint16_t* X;       // [M][K] bf16 (+ z * x_stride), pair-arranged, rows up to M rounded to 128 readable
   size_t x_stride;
   int M, K, N;
-  // int4 weights
   const uint32_t* qweight; // [N][K/8] (+ z * qw_stride)
   size_t qw_stride;
   const uint16_t* rsq;     // [K/128][mpad][4] bf16: -(group row sum of X) as hi, mid, lo, 0 (+ z * rsq_stride)
@@ -67,8 +65,6 @@ struct GemmCoreArgs {
   const uint32_t* szq;     // [K/128][npad]: scale bits | bf16(128 + z) << 16, 0 for columns >= N (+ z * szq_stride)
   size_t szq_stride;
   int mpad, npad;          // M and N rounded up to 128
-  // bf16 weights (reference path)
-  const uint16_t* W;       // [N][K]
   // split over K: workgroup (tile, blockIdx.y) covers groups [gsplit y, gsplit (y + 1));
   // 0 = all groups
   int gsplit;
@@ -130,34 +126,32 @@ __device__ __forceinline__ void lds_barrier() {
 // larger than one round of two workgroups per CU (measured, M = 2048: K = 2048,
 // N = 6144, 1536 tiles, 70.6 -> 66.8 us; K = 6144, N = 2048, 512 tiles, stays on
 // the three-stage kernel, which the wide one would slow from 69.8 to 76.5 us).
-template <bool INT4, bool WIDE = false>
+template <bool WIDE = false>
 struct GemmSmem {
-  static constexpr int kA = 0;                                   // activations, 16 KB
-  static constexpr int kB = kBM * 256;                           // int4: packed words 8 KB; bf16: weights 32 KB
-  static constexpr int kS = kB + (INT4 ? kBN * 64 : kBN * 256);  // int4: column words, 128 x 4 B
-  static constexpr int kR = kS + (INT4 ? 512 : 0);                // int4: row sums, 64 x 8 B
-  static constexpr int kStage = kR + (INT4 ? 512 : 0);
-  static constexpr int kStages = INT4 && !WIDE ? 3 : 2;
-  static constexpr int kBlocksPerCU = INT4 ? (WIDE ? 3 : 2) : 1;
+  static constexpr int kA = 0;                     // activations, 16 KB
+  static constexpr int kB = kBM * 256;             // packed words, 8 KB
+  static constexpr int kS = kB + kBN * 64;         // column words, 128 x 4 B
+  static constexpr int kR = kS + 512;              // row sums, 64 x 8 B
+  static constexpr int kStage = kR + 512;
+  static constexpr int kStages = WIDE ? 2 : 3;
+  static constexpr int kBlocksPerCU = WIDE ? 3 : 2;
   // copies issued per stage and wave (each moves 1 KB, or 256 B for the 4-byte
-  // one): activations 4 + int4: packed words 2, column words or row sums 1;
-  // bf16: weights 8
-  static constexpr int kCopies = INT4 ? 7 : 12;
+  // one): activations 4, packed words 2, column words or row sums 1
+  static constexpr int kCopies = 7;
   static_assert(kStage * kStages * kBlocksPerCU <= 160 * 1024, "LDS");
 };
 
 constexpr int kGemmWaves = 4;
 
-// Resident workgroups of the three-stage int4 kernel on 256 CUs; a larger grid
+// Resident workgroups of the three-stage kernel on 256 CUs; a larger grid
 // takes the WIDE kernel.
 constexpr long long kCoreSlots = 2 * 256;
 inline bool gemm_core_wide(long long workgroups) { return workgroups > kCoreSlots; }
 
-template <bool INT4, int EPI, bool WIDE = false>
-__global__ __launch_bounds__(kGemmWaves * 64, (GemmSmem<INT4, WIDE>::kBlocksPerCU)) void gemm_core_kernel(
+template <int EPI, bool WIDE = false>
+__global__ __launch_bounds__(kGemmWaves * 64, (GemmSmem<WIDE>::kBlocksPerCU)) void gemm_core_kernel(
     GemmCoreArgs a) {
-  static_assert(INT4 || !WIDE, "the wide layout is for int4 weights");
-  using SM = GemmSmem<INT4, WIDE>;
+  using SM = GemmSmem<WIDE>;
   constexpr int S = SM::kStages;
   constexpr int D = S - 1;                 // prefetch distance in groups
   constexpr int L = SM::kCopies;
@@ -177,35 +171,23 @@ __global__ __launch_bounds__(kGemmWaves * 64, (GemmSmem<INT4, WIDE>::kBlocksPerC
   const uint32_t smem_base = (uint32_t)(uintptr_t)smem;   // LDS byte address (low half of the generic one)
 
   // ---- copy sources: wave-uniform bases (without the group term) and per-lane byte offsets ----
-  // 256-byte-row tiles (activations; bf16 weights): copy i of wave w fills rows
-  // 4 u .. 4 u + 3 with u = w + 4 i; lane -> row 4 u + lane / 16, stored chunk
-  // lane % 16 holding logical chunk (lane % 16) ^ (row & 15), and row & 15 =
-  // 4 w + lane / 16 for every i.  int4: X has rows up to M rounded to 64 (the
-  // prologue pads them), so copy i is copy 0 moved by 16 rows and one offset
-  // serves all four (< 2 mpad K).  bf16: rows past M (columns past N) read the
-  // last valid one: their finite results are never stored or scored.
+  // Activations: copy i of wave w fills rows 4 u .. 4 u + 3 with u = w + 4 i;
+  // lane -> row 4 u + lane / 16, stored chunk lane % 16 holding logical chunk
+  // (lane % 16) ^ (row & 15), and row & 15 = 4 w + lane / 16 for every i.  X has
+  // rows up to M rounded to 64 (the prologue pads them), so copy i is copy 0
+  // moved by 16 rows and one offset serves all four (< 2 mpad K).
   const unsigned char* abase = reinterpret_cast<const unsigned char*>(a.X + (size_t)zc_idx * a.x_stride);
   const int arow = 4 * wave + (lane >> 4);
   const uint32_t achunk = (uint32_t)(((lane & 15) ^ (arow & 15)) * 8);
-  uint32_t aoff[INT4 ? 1 : 4];
-  if constexpr (INT4) {
-    aoff[0] = ((uint32_t)(m0 + arow) * (uint32_t)a.K + achunk) * 2u;
-  } else {
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      aoff[i] = ((uint32_t)min(m0 + arow + 16 * i, a.M - 1) * (uint32_t)a.K + achunk) * 2u;
-  }
-  // weights.  int4: copy u (of 2) of wave w fills LDS chunks 64 (2 w + u) + lane:
+  const uint32_t aoff = ((uint32_t)(m0 + arow) * (uint32_t)a.K + achunk) * 2u;
+  // Packed words: copy u (of 2) of wave w fills LDS chunks 64 (2 w + u) + lane:
   // column (64 (2 w + u) + lane) / 4, stored chunk lane % 4 holding logical chunk
   // (lane % 4) ^ ((col >> 2) & 3) (LDS serves a 16-byte read 16 lanes at a time
   // over 64 banks: 16 consecutive columns then hit 16 distinct 16-byte bank
-  // groups); offsets < N K / 2.  bf16: like the activations, 128 rows = columns
-  // n, 8 copies per wave (rows 4 (w + 4 i) ..); offsets < 2 N K.  Columns past N
-  // read column N-1.
-  const unsigned char* wbase;
-  uint32_t woff[INT4 ? 2 : 8];
-  if constexpr (INT4) {
-    wbase = reinterpret_cast<const unsigned char*>(a.qweight + (size_t)zc_idx * a.qw_stride);
+  // groups); offsets < N K / 2.  Columns past N read column N-1.
+  const unsigned char* wbase = reinterpret_cast<const unsigned char*>(a.qweight + (size_t)zc_idx * a.qw_stride);
+  uint32_t woff[2];
+  {
     const uint32_t words = (uint32_t)(a.K >> 3);
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
@@ -214,74 +196,53 @@ __global__ __launch_bounds__(kGemmWaves * 64, (GemmSmem<INT4, WIDE>::kBlocksPerC
       const int chunk = (p & 3) ^ ((col >> 2) & 3);
       woff[u] = (uint32_t)min(n0 + col, a.N - 1) * words * 4u + (uint32_t)chunk * 16u;
     }
-  } else {
-    wbase = reinterpret_cast<const unsigned char*>(a.W);
-#pragma unroll
-    for (int i = 0; i < 8; ++i)
-      woff[i] = ((uint32_t)min(n0 + arow + 16 * i, a.N - 1) * (uint32_t)a.K + achunk) * 2u;
   }
-  // int4, 4-byte copies: waves 0, 1 copy the column words of columns 64 w .. +63;
+  // 4-byte copies: waves 0, 1 copy the column words of columns 64 w .. +63;
   // waves 2, 3 copy the row sums of rows 32 (w - 2) .. +31 (8 bytes each, 4 per lane)
-  const unsigned char* mbase = nullptr;
-  uint32_t mdst = 0;
-  if constexpr (INT4) {
-    if (wave < 2) {
-      mbase = reinterpret_cast<const unsigned char*>(a.szq + (size_t)zc_idx * a.szq_stride + n0 + 64 * wave);
-      mdst = SM::kS + wave * 256;
-    } else {
-      mbase = reinterpret_cast<const unsigned char*>(a.rsq + (size_t)zc_idx * a.rsq_stride +
-                                                     (size_t)(m0 + 32 * (wave - 2)) * 4);
-      mdst = SM::kR + (wave - 2) * 256;
-    }
+  const unsigned char* mbase;
+  uint32_t mdst;
+  if (wave < 2) {
+    mbase = reinterpret_cast<const unsigned char*>(a.szq + (size_t)zc_idx * a.szq_stride + n0 + 64 * wave);
+    mdst = SM::kS + wave * 256;
+  } else {
+    mbase = reinterpret_cast<const unsigned char*>(a.rsq + (size_t)zc_idx * a.rsq_stride +
+                                                   (size_t)(m0 + 32 * (wave - 2)) * 4);
+    mdst = SM::kR + (wave - 2) * 256;
   }
 
   // Sources of one group's copies: wave-uniform base addresses.
   struct GroupSrc {
     const unsigned char* a;   // activations
-    const unsigned char* w;   // packed words (int4) / weights (bf16)
-    const unsigned char* m;   // row sums or column words (int4)
+    const unsigned char* w;   // packed words
+    const unsigned char* m;   // row sums or column words
   };
   auto group_src = [&](int g) {
     GroupSrc r;
     r.a = abase + (size_t)g * 256;
-    r.w = wbase + (size_t)g * (INT4 ? 64 : 256);
-    r.m = INT4 ? mbase + (size_t)g * (wave < 2 ? (size_t)a.npad * 4 : (size_t)a.mpad * 8) : nullptr;
+    r.w = wbase + (size_t)g * 64;
+    r.m = mbase + (size_t)g * (wave < 2 ? (size_t)a.npad * 4 : (size_t)a.mpad * 8);
     return r;
   };
-  // copy k (0 .. L-1) of a group into the stage at LDS byte address st.  int4: 0-3
-  // activations, 4-5 packed words, 6 column words / row sums; bf16: 0-3
-  // activations, 4-11 weights.
+  // copy k (0 .. L-1) of a group into the stage at LDS byte address st: 0-3
+  // activations, 4-5 packed words, 6 column words / row sums
   auto copy_piece = [&](auto kidx, const GroupSrc& src, uint32_t st) {
     constexpr int k = decltype(kidx)::value;
-    if constexpr (k < 4) {
-      if constexpr (INT4)
-        lds_copy16(aoff[0], src.a + (size_t)k * 32 * a.K, st + SM::kA + (wave + 4 * k) * 1024);
-      else
-        lds_copy16(aoff[k], src.a, st + SM::kA + (wave + 4 * k) * 1024);
-    } else if constexpr (INT4) {
-      if constexpr (k < 6)
-        lds_copy16(woff[k - 4], src.w, st + SM::kB + (2 * wave + k - 4) * 1024);
-      else
-        lds_copy4(4u * (uint32_t)lane, src.m, st + mdst);
-    } else {
-      lds_copy16(woff[k - 4], src.w, st + SM::kB + (wave + 4 * (k - 4)) * 1024);
-    }
+    if constexpr (k < 4)
+      lds_copy16(aoff, src.a + (size_t)k * 32 * a.K, st + SM::kA + (wave + 4 * k) * 1024);
+    else if constexpr (k < 6)
+      lds_copy16(woff[k - 4], src.w, st + SM::kB + (2 * wave + k - 4) * 1024);
+    else
+      lds_copy4(4u * (uint32_t)lane, src.m, st + mdst);
   };
-  // the copies that go with MFMA step j of the group being computed.  int4: the
-  // packed words and the column words / row sums first (steps 0-2), so that they
-  // can be waited for one group earlier than the activations (steps 3-6); bf16:
-  // two per step from step 4 on
+  // the copies that go with MFMA step j of the group being computed: the packed
+  // words and the column words / row sums first (steps 0-2), so that they can be
+  // waited for one group earlier than the activations (steps 3-6)
   auto copies_of_step = [&](auto jidx, const GroupSrc& src, uint32_t st) {
     constexpr int j = decltype(jidx)::value;
-    if constexpr (INT4) {
-      if constexpr (j < L) copy_piece(std::integral_constant<int, j < 3 ? j + 4 : j - 3>{}, src, st);
-    } else {
-      if constexpr (j < L) copy_piece(std::integral_constant<int, j>{}, src, st);
-      if constexpr (j >= 4 && j + 4 < L) copy_piece(std::integral_constant<int, j + 4>{}, src, st);
-    }
+    if constexpr (j < L) copy_piece(std::integral_constant<int, j < 3 ? j + 4 : j - 3>{}, src, st);
   };
 
-  // fragment reads of a 256-byte-row tile (activations; bf16 weights): row
+  // fragment reads of the activation tile: row
   // 32 rb + l32 (rb = 32-row block), logical chunk 8h + j at stored chunk
   // (8h + j) ^ (l32 & 15), i.e. byte (l32 * 256 + ((8h ^ (l32 & 15)) * 16)) ^ (16 j)
   // + 8192 rb: one XOR per step, the rest immediate offsets
@@ -297,7 +258,7 @@ __global__ __launch_bounds__(kGemmWaves * 64, (GemmSmem<INT4, WIDE>::kBlocksPerC
   for (int bm = 0; bm < 2; ++bm)
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[bm][r] = 0.0f;
-  // int4: per-group products of the last group computed and its scale, folded
+  // per-group products of the last group computed and its scale, folded
   // into acc at the start of the next group (0 * 0 before the first)
   f32x16 tmp[2];
 #pragma unroll
@@ -307,7 +268,7 @@ __global__ __launch_bounds__(kGemmWaves * 64, (GemmSmem<INT4, WIDE>::kBlocksPerC
   float sc_prev = 0.0f;
 
   const uint32_t nib_mask = opaque_vgpr(0x000F000Fu);
-  // int4: what a lane needs of a group besides the activations -- its 8 packed
+  // what a lane needs of a group besides the activations -- its 8 packed
   // words, its column word and the row sums of its two row blocks.  Three stages:
   // read one group ahead (see the pipeline below), so no group starts on an LDS
   // round trip; two stages (WIDE): read at the start of the group, whose copies
@@ -329,21 +290,19 @@ __global__ __launch_bounds__(kGemmWaves * 64, (GemmSmem<INT4, WIDE>::kBlocksPerC
   GroupMisc gcur{}, gnext{};
   // Computes the group in stage s; between its MFMA steps it issues the copies of
   // the group described by nsrc into the stage at LDS byte address nst.  The
-  // activation fragments of step j+1 are read before the MFMAs of step j.  int4:
-  // uses gcur and, during step 4, reads the next group's GroupMisc (stage s+1)
-  // into gnext.
+  // activation fragments of step j+1 are read before the MFMAs of step j.  Uses
+  // gcur and, during step 4, reads the next group's GroupMisc (stage s+1) into
+  // gnext.
   auto compute = [&](int s, const GroupSrc& nsrc, uint32_t nst) {
     const unsigned char* st = smem + s * SM::kStage;
     const unsigned char* sa = st + SM::kA;
-    const unsigned char* sb = st + SM::kB;
     // recomputed per group: hoisted out of the loop, the eight per-step
     // addresses would stay live in registers for the whole kernel
     fb = opaque_vgpr(fbase);
     bf16x8 af[2][2];
 #pragma unroll
     for (int bm = 0; bm < 2; ++bm) af[0][bm] = frag(sa, bm, 0);
-    if constexpr (INT4) {
-      (void)sb;
+    {
       if constexpr (D == 1) read_misc(st, gcur);
       const uint4* wv = gcur.wv;
       // zero-point step operands: k-slots 0..2 (lane half 0) hold the row sum parts
@@ -403,33 +362,6 @@ __global__ __launch_bounds__(kGemmWaves * 64, (GemmSmem<INT4, WIDE>::kBlocksPerC
       sc_prev = sc_cur;
       if constexpr (D == 2) gcur = gnext;
       (void)st_next;
-    } else {
-      bf16x8 bfc = frag(sb, wave, 0), bfn = bfc;
-      __builtin_amdgcn_sched_barrier(0);
-      auto step = [&](auto jidx) {
-        constexpr int j = decltype(jidx)::value;
-        if constexpr (j < 7) {
-#pragma unroll
-          for (int bm = 0; bm < 2; ++bm) af[(j + 1) & 1][bm] = frag(sa, bm, j + 1);
-          bfn = frag(sb, wave, j + 1);
-        }
-        __builtin_amdgcn_sched_barrier(0);
-        const bf16x8 bf = bfc;
-        copies_of_step(jidx, nsrc, nst);
-#pragma unroll
-        for (int bm = 0; bm < 2; ++bm)
-          acc[bm] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[j & 1][bm], bf, acc[bm], 0, 0, 0);
-        bfc = bfn;
-        __builtin_amdgcn_sched_barrier(0);
-      };
-      step(std::integral_constant<int, 0>{});
-      step(std::integral_constant<int, 1>{});
-      step(std::integral_constant<int, 2>{});
-      step(std::integral_constant<int, 3>{});
-      step(std::integral_constant<int, 4>{});
-      step(std::integral_constant<int, 5>{});
-      step(std::integral_constant<int, 6>{});
-      step(std::integral_constant<int, 7>{});
     }
   };
 
@@ -456,12 +388,12 @@ __global__ __launch_bounds__(kGemmWaves * 64, (GemmSmem<INT4, WIDE>::kBlocksPerC
     copies_of_step(std::integral_constant<int, 7>{}, src, st);
   }
 
-  // int4, three stages: at the barrier of group g the copies still in flight are
+  // Three stages: at the barrier of group g the copies still in flight are
   // the activation copies of group g+1 (its other copies, issued first, are
   // complete: every wave may read group g+1's GroupMisc during group g).  Two
   // stages: none (group g+1's copies are issued after this barrier).
-  constexpr int kInFlight = INT4 ? (D == 2 ? 4 : 0) : (D - 1) * L;
-  if constexpr (INT4 && D == 2) {
+  constexpr int kInFlight = D == 2 ? 4 : 0;
+  if constexpr (D == 2) {
     wait_vmcnt<kInFlight>();
     lds_barrier();
     read_misc(smem, gcur);
@@ -485,12 +417,10 @@ __global__ __launch_bounds__(kGemmWaves * 64, (GemmSmem<INT4, WIDE>::kBlocksPerC
   }
   // the repeated copies of the last iterations must land before LDS is reused or released
   wait_vmcnt<0>();
-  if constexpr (INT4) {
 #pragma unroll
-    for (int bm = 0; bm < 2; ++bm)
+  for (int bm = 0; bm < 2; ++bm)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) acc[bm][r] = fmaf(sc_prev, tmp[bm][r], acc[bm][r]);
-  }
+    for (int r = 0; r < 16; ++r) acc[bm][r] = fmaf(sc_prev, tmp[bm][r], acc[bm][r]);
 
   // epilogue.  Output layout of a 32x32 block: lane holds column l32 and rows
   // 8*i + 4*h + j for register 4*i + j.

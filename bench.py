@@ -137,7 +137,7 @@ def profiled_traffic():
         text = open(os.path.join(ROOT, "profiles", "gemv_decode_sweep_M1.md")).read()
         vals = dict(re.findall(r"^(\w+): (\S+)$", text, flags=re.M))
         h = hashlib.sha256()
-        for f in ("gemv.hip", "common.hpp", "internal.hpp"):
+        for f in ("gemv.hip", "gemv_mfma.hip", "common.hpp"):
             with open(os.path.join(ROOT, "weight_only_int4_amd", "csrc", f), "rb") as fh:
                 h.update(fh.read())
         if vals.get("gemv_source_sha256_16") != h.hexdigest()[:16]:

@@ -176,13 +176,13 @@ int w4a8_quantize_activations(const uint16_t* X, int M, int K, int8_t* Xq, float
  *   (splits x M x N x 4 bytes, added in split order by a second kernel before
  *   the sx[m] scaling); otherwise the size is 0 and both may be NULL.  The size
  *   depends only on (M, K, N).
- *   When to prefer it over w4a16_gemv (measured on MI355X, graph-replayed
- *   GEMV launches, the W4A8 activations quantized beforehand as the previous op
- *   would emit them): only for the narrow decode-block linears (K = 2048 / 6144,
- *   N <= 12288) at M >= 8 -- about even at M = 8, 16% faster at M = 16; W4A16 is
- *   faster at M <= 4 (1.5x at M = 1) and on the 27B-shaped linears at every M
- *   measured (cold, W4A8 at M = 16: 26 / 30 us; W4A16 at M = 8: 16 / 18 us),
- *   and it keeps 16-bit activations.
+ *   Measured against w4a16_gemv on MI355X (graph-replayed GEMV launches, the
+ *   W4A8 activations quantized beforehand as the previous op would emit them):
+ *   w4a16_gemv is faster at every M measured -- on the decode-block linears by
+ *   1.5x at M = 1, 1.2x at M = 4 and 8, 1.1x at M = 16, and on the 27B-shaped
+ *   linears cold (W4A8 at M = 16: 26 / 30 us; W4A16 at M = 8: 14 / 17 us) -- and
+ *   keeps 16-bit activations; W4A8 remains for stacks that need the int8
+ *   activation path.
  */
 int w4a8_gemv(const int8_t* Xq, const float* sx, const int32_t* xsum, int M, int K, int N,
               const uint32_t* qweight, const uint16_t* scales, const uint32_t* qzeros, int symmetric,

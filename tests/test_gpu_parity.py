@@ -234,16 +234,16 @@ def test_gemv_large_full_size(shape, M):
 @pytest.mark.parametrize("M,K,N", [(1, 2048, 40000), (2, 2048, 40000), (4, 2048, 36000), (16, 2048, 30000),
                                    (16, 2048, 4104), (8, 2048, 4104), (4, 2048, 8211), (8, 2048, 17942),
                                    (1, 5120, 25601), (3, 2048, 36000), (5, 4096, 4104), (12, 8192, 1000),
-                                   (6, 6144, 4100), (10, 2048, 2000)])
+                                   (6, 6144, 4100), (10, 2048, 2000), (16, 4096, 600)])
 def test_gemv_tall_random_codes(M, K, N):
     """Tall linears: enough rows that every workgroup gets several row batches
-    (and, for the larger M, several rounds of workgroups); the row counts are
-    picked so that the launch plans take each of their batch counts for some M,
-    on both forms of the GEMV: the VALU form (2, 3, 4, 5, 6, 8, 16 row batches per
-    workgroup) and the matrix-core form (1 to 8 column blocks per slab; 2 groups per
-    wave up to K = 4096 and 4 above, with a K split at K = 8192; entered at M = 3
-    on a 36.9 MB weight, at M = 5 from N = 4096 and at M = 10 otherwise).  The
-    packed operands are drawn directly (random codes, scales and zero words);
+    (and, for the larger M, several rounds of workgroups), on both forms of the
+    GEMV: the VALU form (M <= 4 on narrow outputs; several row-batch counts per
+    workgroup) and the matrix-core form (1 to 8 column blocks per slab; 2 groups
+    per wave up to K = 4096 and 4 above, with a K split at K = 8192; entered at
+    M = 3 from N = 4096 and at M = 5 otherwise; K = 4096 at M = 16 takes more than
+    64 KB of LDS per workgroup).  The packed operands are drawn directly (random
+    codes, scales and zero words);
     oracle on every 16th row."""
     rng = np.random.default_rng(1000 + M + N)
     qw = rng.integers(0, 2 ** 32, size=(N, K // 8), dtype=np.uint64).astype(np.uint32)

@@ -1,10 +1,13 @@
-// Decode contraction Y = X W_hat^T for 1 <= M <= 16 rows (W4A16 GEMV).
+// Decode contraction Y = X W_hat^T for 1 <= M <= 16 rows (W4A16 GEMV): the
+// launcher, the vector-ALU form for the smallest batches (M <= 4; which form runs
+// is gemv_use_mfma's measured rule, the matrix-core form being gemv_mfma.hip) and
+// the reduction of K-split partials both forms share.
 //
 // Model card "GLM-5.2-QSRT-Fruit-Instruct", "Reproducible runtime": decode
 // batches of at most 16 rows take their own path; model card
 // "Qwen3.6-27B-W4A16", opening paragraph: int4 weights, 16-bit activations.
 //
-// Design (CDNA4, wave64, VALU):
+// Design of the vector-ALU form (CDNA4, wave64):
 //  * A workgroup owns a contiguous slab of output rows (BPW batches of R rows)
 //    and a range of input channels (all of K unless K is split over
 //    grid.y).  Its waves split the channel range: every lane holds WPL packed
@@ -438,19 +441,7 @@ int launch_gemv(const uint16_t* X, int M, int K, int N, const uint32_t* qweight,
     case 2: launch_sym<2>(a, p, sym, stream); break;
     case 3: launch_sym<3>(a, p, sym, stream); break;
     case 4: launch_sym<4>(a, p, sym, stream); break;
-    case 5: launch_sym<5>(a, p, sym, stream); break;
-    case 6: launch_sym<6>(a, p, sym, stream); break;
-    case 7: launch_sym<7>(a, p, sym, stream); break;
-    case 8: launch_sym<8>(a, p, sym, stream); break;
-    case 9: launch_sym<9>(a, p, sym, stream); break;
-    case 10: launch_sym<10>(a, p, sym, stream); break;
-    case 11: launch_sym<11>(a, p, sym, stream); break;
-    case 12: launch_sym<12>(a, p, sym, stream); break;
-    case 13: launch_sym<13>(a, p, sym, stream); break;
-    case 14: launch_sym<14>(a, p, sym, stream); break;
-    case 15: launch_sym<15>(a, p, sym, stream); break;
-    case 16: launch_sym<16>(a, p, sym, stream); break;
-    default: return W4_ERR_UNSUPPORTED;
+    default: return W4_ERR_UNSUPPORTED;   // M >= 5 always takes the matrix-core form
   }
   W4_CHECK_LAUNCH();
   if (p.splits > 1) {

@@ -24,7 +24,8 @@
 //    of 16 columns of its slab; its activations (64 bytes per lane and group) and
 //    the group row sums of X stay in registers for the whole slab.  nwk waves
 //    cover the groups of a split; rw slabs share a workgroup.
-//  * Per block and group: the zero-point term -(128 + z) rowsum_g(x) is the
+//  * Per block and group: the zero-point term -(128 + z) rowsum_g(x) (the row
+//    sums also taken on the matrix cores, against a B of ones) is the
 //    initial accumulator of the group's tile, four MFMAs add the exact products
 //    x (128 + q) (bf16 integers below 2^8 times bf16 activations: exact in fp32),
 //    and acc += sc * tile folds the group into the block's result.
@@ -68,10 +69,13 @@ template <int KT, int BPW, bool SYM>
 __global__ __launch_bounds__(max_waves(KT) * 64) void gemv_mfma_kernel(MfmaArgs a) {
   constexpr int NB = 2;            // blocks in flight
   constexpr int bpw = BPW;
-  // partial tiles when nwk > 1: [rw * nwk][BPW][qm * 16] for the lanes that hold
-  // rows below M (lane quarters q < qm = ceil(M / 4))
-  extern __shared__ f32x4 red[];
+  // Dynamic LDS: per wave a staging area for one group of its activation rows
+  // ([4 qm rows][256 bytes], qm = ceil(M / 4)), then, when nwk > 1, the partial
+  // tiles [rw * nwk][BPW][qm * 16] of the lanes that hold rows below M (lane
+  // quarters q < qm).
+  extern __shared__ f32x4 lds_dyn[];
   const int qm = (a.M + 3) >> 2;
+  f32x4* red = lds_dyn + (size_t)(blockDim.x >> 6) * qm * 4 * 16;
 
   const int lane = threadIdx.x & (kWave - 1);
   const int wid = threadIdx.x >> 6;
@@ -104,19 +108,24 @@ __global__ __launch_bounds__(max_waves(KT) * 64) void gemv_mfma_kernel(MfmaArgs 
   static_assert(8 % KT == 0, "the wave's groups share one zero word");
   const uint32_t kz = g0 < gend ? (uint32_t)(g0 >> 3) * 4u : kOob;
 
-  // Prologue: the activations of the wave's groups (row j, channels 32 q .. 32 q + 31
-  // of each group; only the lanes of rows below M load), then the first NB blocks,
-  // all issued before anything waits.
+  // Prologue: the activations of the wave's groups, then the first NB blocks, all
+  // issued before anything waits.  Activations are read row-contiguously (load u
+  // of a group: rows 4 u .. 4 u + 3, sixteen lanes of 16 bytes per row, only the
+  // first qm loads and only rows below M) and later rearranged through LDS into
+  // the operand layout.
+  const int xr_row = lane >> 4, xr_chunk = lane & 15;
   uint32_t xr[KT][4][4] = {};
-  if (j < a.M) {
 #pragma unroll
-    for (int t = 0; t < KT; ++t) {
-      const uint32_t xo = g0 + t < gend ? ((uint32_t)j * (uint32_t)a.K + (uint32_t)(g0 + t) * 128u) * 2u + 64u * q
-                                        : kOob;
+  for (int t = 0; t < KT; ++t) {
 #pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        const auto v = __builtin_amdgcn_raw_buffer_load_b128(rx, xo + 16u * s, 0, 0);
-        xr[t][s][0] = v[0]; xr[t][s][1] = v[1]; xr[t][s][2] = v[2]; xr[t][s][3] = v[3];
+    for (int u = 0; u < 4; ++u) {
+      const int r = 4 * u + xr_row;
+      if (u < qm && r < a.M) {
+        const uint32_t xo = g0 + t < gend ? ((uint32_t)r * (uint32_t)a.K + (uint32_t)(g0 + t) * 128u +
+                                             8u * (uint32_t)xr_chunk) * 2u
+                                          : kOob;
+        const auto v = __builtin_amdgcn_raw_buffer_load_b128(rx, xo, 0, 0);
+        xr[t][u][0] = v[0]; xr[t][u][1] = v[1]; xr[t][u][2] = v[2]; xr[t][u][3] = v[3];
       }
     }
   }
@@ -149,30 +158,42 @@ __global__ __launch_bounds__(max_waves(KT) * 64) void gemv_mfma_kernel(MfmaArgs 
     if (i < BPW) load(i, B[i]);
   __builtin_amdgcn_sched_barrier(0);
 
-  // A operands and row sums.  The sum of row j over the lane's 32 channels comes
-  // from dot products with (1, 1) (exact products, fp32 sums); the two lane swaps
-  // add the four quarters in the same order in all four lanes of row j; each lane
-  // then fetches the sums of its output rows 4 q .. 4 q + 3.
+  // A operands and row sums.  Per group the wave writes its activation rows to its
+  // LDS staging area (16-byte chunk c of row r at r * 256 + ((c ^ r) & 15) * 16, so
+  // that the reads below hit 16 distinct bank groups) and reads back, for lane
+  // (j, q) and step s, chunk 4 q + s of row j (rows past M repeat row M - 1: their
+  // outputs are never stored).  The group sums of the rows come from the matrix
+  // cores: the group's four A operands against a B of bf16 ones put
+  // sum_k x[r][k] (exact products, fp32 sums) in every column of the tile, so each
+  // lane receives the sums of its own output rows 4 q .. 4 q + 3 in place.
+  uint4* xs = reinterpret_cast<uint4*>(lds_dyn + (size_t)wid * qm * 4 * 16);
+  const int jr = min(j, a.M - 1);
   bf16x8 xa[KT][4];
   f32x4 zx[KT];        // -(128 + z) row sums (symmetric: z = 8), or the plain row sums
+  const bf16x8 ones = __builtin_bit_cast(bf16x8, make_uint4(0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u));
 #pragma unroll
   for (int t = 0; t < KT; ++t) {
-    float p = 0.0f;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int r = 4 * u + xr_row;
+      if (u < qm) xs[r * 16 + ((xr_chunk ^ r) & 15)] = make_uint4(xr[t][u][0], xr[t][u][1], xr[t][u][2], xr[t][u][3]);
+    }
+    uint32_t xq[4][4];
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const uint4 v = xs[jr * 16 + (((4 * q + s) ^ jr) & 15)];
+      xq[s][0] = v.x; xq[s][1] = v.y; xq[s][2] = v.z; xq[s][3] = v.w;
+    }
+    f32x4 r = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       uint32_t e[4];
-      pair_activations(xr[t][s], e);
+      pair_activations(xq[s], e);
       xa[t][s] = __builtin_bit_cast(bf16x8, make_uint4(e[0], e[1], e[2], e[3]));
-#pragma unroll
-      for (int d = 0; d < 4; ++d) p = dot2_bf16(xr[t][s][d], 0x3F803F80u, p);
+      r = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa[t][s], ones, r, 0, 0, 0);
     }
-    p = swap_sum32(p, p);
-    p = swap_sum16(p, p);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float r = __shfl(p, 4 * q + i, kWave);
-      zx[t][i] = SYM ? -136.0f * r : r;
-    }
+    for (int i = 0; i < 4; ++i) zx[t][i] = SYM ? -136.0f * r[i] : r[i];
   }
   const uint32_t nib_mask = opaque_vgpr(0x000F000Fu);
   // operand lane j + 16 q takes the words of column j, chunk q from lane 4 j + q
@@ -271,14 +292,32 @@ MfmaPlan plan_mfma(int K) {
 // Waves per workgroup the launch aims for when one slab needs fewer.
 constexpr int kWgWaves = 4;
 constexpr size_t kLdsPerCu = 160 * 1024;
-constexpr size_t kMaxLds = 64 * 1024;
+constexpr size_t kMaxLds = kLdsPerCu;
+constexpr size_t kDefaultLds = 64 * 1024;   // dynamic LDS a launch may take without raising the limit
+
+// Allows an instantiation more than 64 KB of dynamic LDS (once per device).
+template <int KT, int BPW, bool SYM>
+bool allow_large_lds() {
+  static std::atomic<int> state[64];       // 0 not yet, 1 done, -1 failed
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return false;
+  int st = state[dev].load(std::memory_order_relaxed);
+  if (st == 0) {
+    st = hipFuncSetAttribute(reinterpret_cast<const void*>(gemv_mfma_kernel<KT, BPW, SYM>),
+                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLdsPerCu) == hipSuccess
+             ? 1
+             : -1;
+    state[dev].store(st, std::memory_order_relaxed);
+  }
+  return st == 1;
+}
 
 // Resident workgroups per CU of one instantiation at a block size, from its
 // registers alone (cached per block size); the LDS of the partial tiles is
 // applied on top by the caller.
 // Largest blocks per slab an instantiation takes: with four asymmetric groups per
-// wave, more than three blocks would spill registers.
-constexpr int max_bpw(int kt, bool sym) { return kt == 4 && !sym ? 3 : 8; }
+// wave, more than two blocks would spill registers.
+constexpr int max_bpw(int kt, bool sym) { return kt == 4 && !sym ? 2 : 8; }
 constexpr int clamp_bpw(int kt, bool sym, int b) { return b < max_bpw(kt, sym) ? b : max_bpw(kt, sym); }
 
 template <int KT, int BPW, bool SYM>
@@ -312,7 +351,7 @@ int device_cu_count() {
 // workgroups covers every block (the slabs take the blocks round-robin, so each
 // holds that many or one less); when no count fits one round, the largest.
 template <int KT, bool SYM>
-void launch_kt(MfmaArgs a, const MfmaPlan& p, hipStream_t stream) {
+int launch_kt(MfmaArgs a, const MfmaPlan& p, hipStream_t stream) {
   const int rw = p.nwk >= kWgWaves ? 1 : kWgWaves / p.nwk;
   a.nwk = p.nwk;
   a.rw = rw;
@@ -321,7 +360,10 @@ void launch_kt(MfmaArgs a, const MfmaPlan& p, hipStream_t stream) {
   const long long nb = (a.N + kBlockCols - 1) / kBlockCols;
   const long long cus = device_cu_count();
   const int qm = (a.M + 3) / 4;
-  auto lds = [&](int bpw) { return p.nwk > 1 ? (size_t)rw * p.nwk * bpw * qm * 16 * sizeof(f32x4) : (size_t)0; };
+  auto lds = [&](int bpw) {
+    const size_t xs = (size_t)rw * p.nwk * qm * 4 * 256;
+    return xs + (p.nwk > 1 ? (size_t)rw * p.nwk * bpw * qm * 16 * sizeof(f32x4) : (size_t)0);
+  };
   auto by_regs = [&](int bpw) {
     switch (bpw) {
       case 1: return mfma_blocks_per_cu<KT, clamp_bpw(KT, SYM, 1), SYM>(threads);
@@ -347,31 +389,36 @@ void launch_kt(MfmaArgs a, const MfmaPlan& p, hipStream_t stream) {
   }
   const dim3 grid((unsigned)(((nb + best - 1) / best + rw - 1) / rw), (unsigned)p.splits);
   const size_t sh = lds(best);
+  auto go = [&](auto kernel, auto allow) {
+    if (sh > kDefaultLds && !allow()) return W4_ERR_HIP;
+    hipLaunchKernelGGL(kernel, grid, dim3(threads), sh, stream, a);
+    return W4_OK;
+  };
   switch (best) {
-    case 1: hipLaunchKernelGGL((gemv_mfma_kernel<KT, clamp_bpw(KT, SYM, 1), SYM>), grid, dim3(threads), sh, stream, a); break;
-    case 2: hipLaunchKernelGGL((gemv_mfma_kernel<KT, clamp_bpw(KT, SYM, 2), SYM>), grid, dim3(threads), sh, stream, a); break;
-    case 3: hipLaunchKernelGGL((gemv_mfma_kernel<KT, clamp_bpw(KT, SYM, 3), SYM>), grid, dim3(threads), sh, stream, a); break;
-    case 4: hipLaunchKernelGGL((gemv_mfma_kernel<KT, clamp_bpw(KT, SYM, 4), SYM>), grid, dim3(threads), sh, stream, a); break;
-    case 5: hipLaunchKernelGGL((gemv_mfma_kernel<KT, clamp_bpw(KT, SYM, 5), SYM>), grid, dim3(threads), sh, stream, a); break;
-    case 6: hipLaunchKernelGGL((gemv_mfma_kernel<KT, clamp_bpw(KT, SYM, 6), SYM>), grid, dim3(threads), sh, stream, a); break;
-    case 7: hipLaunchKernelGGL((gemv_mfma_kernel<KT, clamp_bpw(KT, SYM, 7), SYM>), grid, dim3(threads), sh, stream, a); break;
-    default: hipLaunchKernelGGL((gemv_mfma_kernel<KT, clamp_bpw(KT, SYM, 8), SYM>), grid, dim3(threads), sh, stream, a); break;
+    case 1: return go(gemv_mfma_kernel<KT, clamp_bpw(KT, SYM, 1), SYM>, allow_large_lds<KT, clamp_bpw(KT, SYM, 1), SYM>);
+    case 2: return go(gemv_mfma_kernel<KT, clamp_bpw(KT, SYM, 2), SYM>, allow_large_lds<KT, clamp_bpw(KT, SYM, 2), SYM>);
+    case 3: return go(gemv_mfma_kernel<KT, clamp_bpw(KT, SYM, 3), SYM>, allow_large_lds<KT, clamp_bpw(KT, SYM, 3), SYM>);
+    case 4: return go(gemv_mfma_kernel<KT, clamp_bpw(KT, SYM, 4), SYM>, allow_large_lds<KT, clamp_bpw(KT, SYM, 4), SYM>);
+    case 5: return go(gemv_mfma_kernel<KT, clamp_bpw(KT, SYM, 5), SYM>, allow_large_lds<KT, clamp_bpw(KT, SYM, 5), SYM>);
+    case 6: return go(gemv_mfma_kernel<KT, clamp_bpw(KT, SYM, 6), SYM>, allow_large_lds<KT, clamp_bpw(KT, SYM, 6), SYM>);
+    case 7: return go(gemv_mfma_kernel<KT, clamp_bpw(KT, SYM, 7), SYM>, allow_large_lds<KT, clamp_bpw(KT, SYM, 7), SYM>);
+    default: return go(gemv_mfma_kernel<KT, clamp_bpw(KT, SYM, 8), SYM>, allow_large_lds<KT, clamp_bpw(KT, SYM, 8), SYM>);
   }
 }
 
 }  // namespace
 
-// Which form runs a decode GEMV.  Measured on MI355X (kernel time per call, VALU
-// form / MFMA form, asymmetric K = 2048 and K = 6144 linears with warm caches,
-// symmetric 27B-shaped ones): the MFMA form wins from M = 3 on the 27B shapes
-// (K = 5120, N = 17408: 15.6 / 13.6 us at M = 3..4, 31.2 / 14.4 at M = 8), from
-// M = 5 at N >= 4096 (K = 2048, N = 12288: 8.1 / 7.3 us at M = 5), and only from
-// M = 10 or so at N = 2048 (K = 2048: 4.5 / 4.8 us at M = 8, 6.7 / 5.1 at M = 12),
-// where its 128 column blocks leave most of the chip idle.
+// Which form runs a decode GEMV.  Measured on MI355X (kernel time per call,
+// VALU form / MFMA form, asymmetric decode-block linears with warm caches and the
+// symmetric 27B-shaped ones): K = 2048, N = 4096: 4.4 / 4.1 us at M = 3; K = 2048,
+// N = 12288: 6.8 / 6.4 at M = 3; K = 5120, N = 17408: 15.6 / 12.1 at M = 3;
+// K = 17408, N = 5120: 23.2 / 16.4 at M = 3 but 11.6 / 16.4 at M = 2 (the K split's
+// second launch); K = 6144, N = 2048: 5.4 / 5.9 at M = 3, 6.2 / 5.9 at M = 4;
+// K = 2048, N = 2048: 3.7 / 4.0 at M = 4, 4.4 / 4.1 at M = 6, 4.8 / 4.0 at M = 8.
 bool gemv_use_mfma(int M, int K, int N) {
-  if (M >= 10) return true;
-  if (M >= 3 && (long long)N * K / 2 >= (16LL << 20)) return true;
-  return M >= 5 && N >= 4096;
+  if (M >= 5) return true;
+  if (M >= 3 && N >= 4096) return true;
+  return M == 4 && (long long)N * K / 2 >= (4LL << 20);
 }
 
 size_t gemv_mfma_workspace_bytes(int M, int K, int N) {
@@ -390,17 +437,12 @@ int launch_gemv_mfma(const uint16_t* X, int M, int K, int N, const uint32_t* qwe
   const MfmaPlan p = plan_mfma(K);
   MfmaArgs a{X, M, K, N, qweight, scales, qzeros, Y, p.splits > 1 ? static_cast<float*>(workspace) : nullptr,
              p.gs, p.nwk, 1};
-  if (p.kt == 2) {
-    if (symmetric)
-      launch_kt<2, true>(a, p, stream);
-    else
-      launch_kt<2, false>(a, p, stream);
-  } else {
-    if (symmetric)
-      launch_kt<4, true>(a, p, stream);
-    else
-      launch_kt<4, false>(a, p, stream);
-  }
+  int st;
+  if (p.kt == 2)
+    st = symmetric ? launch_kt<2, true>(a, p, stream) : launch_kt<2, false>(a, p, stream);
+  else
+    st = symmetric ? launch_kt<4, true>(a, p, stream) : launch_kt<4, false>(a, p, stream);
+  if (st) return st;
   W4_CHECK_LAUNCH();
   if (p.splits > 1) {
     return launch_gemv_split_reduce(static_cast<const float*>(workspace), p.splits, (size_t)M * N, Y, stream);

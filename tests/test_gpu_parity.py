@@ -112,6 +112,36 @@ def test_quantize_division_ties():
     _assert_quant_equal(W, s)
 
 
+def test_quantize_near_ties():
+    """Quotients a few dozen ulps from half-integers, in groups of known scale (an
+    anchor fixes sc = 5/64 exactly): codes equal to the IEEE-division oracle's on
+    either side of every half-integer, whichever way the kernel takes them."""
+    c = 5.0 / 64.0
+    vals = []
+    for k in range(7):
+        t = np.float32((k + 0.5) * c)
+        for d in (12, 16, 20, 24, 32, 64):
+            up, dn = t, t
+            for _ in range(d):
+                up = np.nextafter(up, np.float32(8))
+                dn = np.nextafter(dn, np.float32(0))
+            vals += [float(up), float(dn)]
+    for sym in (False, True):
+        G = (len(vals) + 125) // 126
+        s = np.ones(128 * G, dtype=np.float32)
+        Wf = np.zeros(128 * G, dtype=np.float32)
+        for g in range(G):
+            chunk = vals[126 * g:126 * (g + 1)]
+            # anchors: symmetric absmax 7c (sc = c); asymmetric min 0, max 15c (sc = c, z = 0)
+            Wf[128 * g] = 7.0 * c if sym else 15.0 * c
+            Wf[128 * g + 1] = 0.0
+            s[128 * g + 2:128 * g + 2 + len(chunk)] = chunk
+            Wf[128 * g + 2:128 * g + 2 + len(chunk)] = 1.0
+        W = wl.round_to_bf16_bits(Wf)[None, :]
+        say("near ties", sym)
+        _assert_quant_equal(W, s, sym=sym)
+
+
 def test_quantize_degenerate_groups():
     """Constant and all-zero groups hit the 1e-5 range floor; a lone outlier clamps."""
     W = np.zeros((4, 256), dtype=np.float32)

@@ -36,8 +36,8 @@
 // live k-slots: hi, mid, lo times 128 + z, all products exact), then accumulate
 // the exact integer-weight products sum_k x (128 + q) on top: the tile holds
 // sum_k x (q - z).  It is folded into the output accumulator with one FMA,
-// acc += sc * tmp, block by block between the first MFMAs of the next group (so
-// the matrix cores do not drain at group boundaries).
+// acc += sc * tmp, at the start of the next group, while that group's LDS reads
+// of packed words, column words and row sums are in flight.
 // The k-slots of the MFMA are assigned so that lane half h, step j covers
 // channels 64h + 8j .. 64h + 8j + 7 of the group: each lane's 8 words of a group
 // are contiguous.
@@ -304,6 +304,13 @@ __global__ __launch_bounds__(kGemmWaves * 64, (GemmSmem<WIDE>::kBlocksPerCU)) vo
     for (int bm = 0; bm < 2; ++bm) af[0][bm] = frag(sa, bm, 0);
     {
       if constexpr (D == 1) read_misc(st, gcur);
+      // fold the previous group's blocks, acc += sc_prev * tmp, while the reads
+      // above are in flight (two stages: this group's misc words arrive from LDS now)
+#pragma unroll
+      for (int bm = 0; bm < 2; ++bm)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[bm][r] = fmaf(sc_prev, tmp[bm][r], acc[bm][r]);
+      __builtin_amdgcn_sched_barrier(0);
       const uint4* wv = gcur.wv;
       // zero-point step operands: k-slots 0..2 (lane half 0) hold the row sum parts
       // against 128 + z three times; every other slot is 0
@@ -333,16 +340,10 @@ __global__ __launch_bounds__(kGemmWaves * 64, (GemmSmem<WIDE>::kBlocksPerCU)) vo
             bf16x8, make_uint4(nibble_pair_m(word, 0, nib_mask), nibble_pair_m(word, 1, nib_mask),
                                nibble_pair_m(word, 2, nib_mask), nibble_pair_m(word, 3, nib_mask)));
         if constexpr (j == 0) {
+          // start this group's blocks with their zero-point terms
 #pragma unroll
-          for (int bm = 0; bm < 2; ++bm) {
-            // fold the previous group's block first: acc += sc_prev * tmp (fenced
-            // from the MFMA that overwrites tmp, so both never need registers at
-            // once), then start this group's block with its zero-point term
-#pragma unroll
-            for (int r = 0; r < 16; ++r) acc[bm][r] = fmaf(sc_prev, tmp[bm][r], acc[bm][r]);
-            __builtin_amdgcn_sched_barrier(0);
+          for (int bm = 0; bm < 2; ++bm)
             tmp[bm] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(za[bm], zb, f32x16{}, 0, 0, 0);
-          }
         }
 #pragma unroll
         for (int bm = 0; bm < 2; ++bm)

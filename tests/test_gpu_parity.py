@@ -203,7 +203,9 @@ def test_gemv_all_m(M, sym):
 
 @pytest.mark.parametrize("M,K,N", [(1, 128, 1), (1, 384, 37), (3, 1152, 129), (8, 6144, 200), (16, 17408, 70),
                                    (5, 5120, 64), (1, 17408, 33), (9, 8320, 17), (2, 16384, 8), (4, 24576, 5),
-                                   (1, 4096, 77), (1, 5120, 65), (1, 8192, 9), (1, 9216, 40), (1, 33792, 12)])
+                                   (1, 4096, 77), (1, 5120, 65), (1, 8192, 9), (1, 9216, 40), (1, 33792, 12),
+                                   (5, 128, 1), (16, 128, 17), (7, 256, 33), (12, 384, 5), (6, 640, 4100),
+                                   (16, 8192, 3), (3, 1024, 4097)])
 def test_gemv_ragged(M, K, N):
     say("gemv ragged", M, K, N)
     X, W = wl.small_case(M, K, N, 21)

@@ -1,14 +1,15 @@
 // Decode contraction Y = X W_hat^T on the matrix cores, for the larger decode
-// batches (W4A16 GEMV, MFMA form; the launcher in gemv.hip picks it from
-// kGemvMfmaMinM rows on).
+// batches (W4A16 GEMV, MFMA form; gemv_use_mfma below is the measured rule by which
+// the launcher in gemv.hip picks it over the VALU form).
 //
 // Model card "GLM-5.2-QSRT-Fruit-Instruct", "Reproducible runtime": decode
 // batches of at most 16 rows take their own path.  The VALU form (gemv.hip)
 // spends M dot products on every unpacked weight pair, so from a few rows on it is
 // bound by vector ALU work instead of memory.  Here one v_mfma_f32_16x16x32_bf16
 // multiplies a block of 16 columns x 32 channels of unpacked weights with all 16
-// activation rows (rows past M read as zeros): the per-weight VALU work -- the
-// unpacking and the per-group fold -- no longer grows with M.
+// activation rows (rows past M are don't-care rows whose outputs are never
+// stored): the per-weight VALU work -- the unpacking and the per-group fold -- no
+// longer grows with M.
 //
 // Design (CDNA4, wave64):
 //  * MFMA operands: A = activations (16 rows x 32 k-slots), B = unpacked weights
@@ -16,22 +17,24 @@
 //    of A and column j of B in k-slots 8 q .. 8 q + 7, and column j, rows
 //    4 q .. 4 q + 3 of D.  In step s (0..3) of a 128-channel group, lane quarter q
 //    takes the group's packed word 4 q + s (channels 32 q + 8 s .. + 7) as its B
-//    slots, so each lane reads the 16 contiguous bytes of its column's words
-//    4 q .. 4 q + 3 once per group; its A slots in step s are the same 8 channels
-//    of row j, pair-arranged as (x0,x4)(x1,x5)(x2,x6)(x3,x7) to match the order in
-//    which a word unpacks.
+//    slots; its A slots in step s are the same 8 channels of row j, pair-arranged
+//    as (x0,x4)(x1,x5)(x2,x6)(x3,x7) to match the order in which a word unpacks.
+//  * Memory access: both operands are read so that every four consecutive lanes
+//    hit one cache line, then rearranged -- the packed words (lanes 4 c .. 4 c + 3:
+//    the 64 bytes of column c in a group) with ds_bpermute, the activations (16
+//    lanes per 256-byte row, rows below M only) through a per-wave LDS staging area.
 //  * A wave owns KT consecutive groups of one K split and streams the BPW blocks
-//    of 16 columns of its slab; its activations (64 bytes per lane and group) and
-//    the group row sums of X stay in registers for the whole slab.  nwk waves
-//    cover the groups of a split; rw slabs share a workgroup.
+//    of 16 columns of its slab; its A operands and the group row sums of X stay
+//    in registers for the whole slab.  nwk waves cover the groups of a split; rw
+//    slabs share a workgroup.
 //  * Per block and group: the zero-point term -(128 + z) rowsum_g(x) (the row
 //    sums also taken on the matrix cores, against a B of ones) is the
 //    initial accumulator of the group's tile, four MFMAs add the exact products
 //    x (128 + q) (bf16 integers below 2^8 times bf16 activations: exact in fp32),
 //    and acc += sc * tile folds the group into the block's result.
 //  * Loads are buffer loads (an out-of-range offset returns 0 and touches no
-//    memory): rows of X past M, columns past N and groups past the split read
-//    zeros, whose tiles are 0 and whose scales are 0.
+//    memory): columns past N and groups past the split read zeros, whose tiles
+//    are 0 and whose scales are 0.
 //  * The nwk partial tiles of a block meet in LDS and are added in wave order;
 //    with a K split the fp32 sums go to the workspace and gemv_split_reduce adds
 //    the splits in order.  Every sum has a fixed order: results are

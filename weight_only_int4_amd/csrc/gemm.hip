@@ -108,12 +108,24 @@ __global__ __launch_bounds__(256) void gemm_prep_kernel(const uint16_t* X, size_
     if (!symmetric && n < N) zw = qzeros[(size_t)c * qz_stride + (size_t)n * GW + gw];
     const uint16_t* srow = scales + (size_t)c * sc_stride + (size_t)n * G;
     // all eight scale loads are issued before the first store (one memory round
-    // trip per thread, not eight)
+    // trip per thread, not eight); a full block of 8 groups in a 16-byte aligned
+    // row is one 16-byte load
     uint32_t sv[8];
+    const uint16_t* sblk = srow + 8 * gw;
+    if (n < N && 8 * gw + 8 <= G && (reinterpret_cast<uintptr_t>(sblk) & 15) == 0) {
+      const uint4 v = *reinterpret_cast<const uint4*>(sblk);
+      const uint32_t d[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
-    for (int jj = 0; jj < 8; ++jj) {
-      const int g = 8 * gw + jj;
-      sv[jj] = (n < N && g < G) ? (uint32_t)srow[g] : 0u;
+      for (int jj = 0; jj < 4; ++jj) {
+        sv[2 * jj] = d[jj] & 0xFFFFu;
+        sv[2 * jj + 1] = d[jj] >> 16;
+      }
+    } else {
+#pragma unroll
+      for (int jj = 0; jj < 8; ++jj) {
+        const int g = 8 * gw + jj;
+        sv[jj] = (n < N && g < G) ? (uint32_t)srow[g] : 0u;
+      }
     }
 #pragma unroll
     for (int jj = 0; jj < 8; ++jj) {

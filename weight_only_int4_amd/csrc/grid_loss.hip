@@ -90,8 +90,18 @@ __global__ __launch_bounds__(64) void loss_reduce_kernel(const float* partials, 
                                                          float* losses) {
   const int c = blockIdx.x;
   const int lane = threadIdx.x;
+  // loads issued 16 at a time, added in the same ascending order
+  const float* pc = partials + (size_t)c * tiles;
   double s = 0.0;
-  for (int t = lane; t < tiles; t += 64) s += (double)partials[(size_t)c * tiles + t];
+  int t = lane;
+  for (; t + 64 * 15 < tiles; t += 64 * 16) {
+    float v[16];
+#pragma unroll
+    for (int u = 0; u < 16; ++u) v[u] = pc[t + 64 * u];
+#pragma unroll
+    for (int u = 0; u < 16; ++u) s += (double)v[u];
+  }
+  for (; t < tiles; t += 64) s += (double)pc[t];
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) s += __shfl_xor(s, off, 64);
   if (lane == 0) losses[c] = (float)(s * inv_count);
@@ -104,8 +114,17 @@ __global__ __launch_bounds__(256) void act_abs_partial_kernel(const uint16_t* X,
   if (k >= K) return;
   const int t0 = blockIdx.y * rows;
   const int t1 = min(t0 + rows, T);
+  // loads issued 8 at a time, added in the same ascending order
   double s = 0.0;
-  for (int t = t0; t < t1; ++t) s += (double)fabsf(bf16_bits_to_f32(X[(size_t)t * K + k]));
+  int t = t0;
+  for (; t + 7 < t1; t += 8) {
+    uint32_t v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = X[(size_t)(t + u) * K + k];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) s += (double)fabsf(bf16_bits_to_f32(v[u]));
+  }
+  for (; t < t1; ++t) s += (double)fabsf(bf16_bits_to_f32(X[(size_t)t * K + k]));
   partial[(size_t)blockIdx.y * K + k] = s;
 }
 
@@ -113,8 +132,17 @@ __global__ __launch_bounds__(256) void act_abs_finish_kernel(const double* parti
                                                              double* m) {
   const int k = blockIdx.x * 256 + threadIdx.x;
   if (k >= K) return;
+  // loads issued 8 at a time, added in the same ascending order
   double s = 0.0;
-  for (int c = 0; c < chunks; ++c) s += partial[(size_t)c * K + k];
+  int c = 0;
+  for (; c + 7 < chunks; c += 8) {
+    double v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = partial[(size_t)(c + u) * K + k];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) s += v[u];
+  }
+  for (; c < chunks; ++c) s += partial[(size_t)c * K + k];
   m[k] = s / (double)T;
 }
 

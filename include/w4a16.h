@@ -105,17 +105,21 @@ int awq_quantize_pack(const uint16_t* W, int N, int K, const float* s, float cli
 
 /*
  * w4a16_gemv -- decode contraction Y = X W_hat^T for 1 <= M <= 16 rows, bf16
- * activations, int4 weights dequantized in registers; one wavefront reduction
- * per output.  [QSRT card] "Reproducible runtime": decode batches of at most 16
- * rows take their own path; [27B card] activations stay 16-bit.
+ * activations, int4 weights unpacked in registers.  The smallest batches take
+ * one wavefront dot-product reduction per output; larger ones (from M = 5, or
+ * earlier on wide or large weights, by a fixed rule of the shape) take 16x16x32
+ * bf16 matrix-core products over all rows at once.  [QSRT card] "Reproducible
+ * runtime": decode batches of at most 16 rows take their own path; [27B card]
+ * activations stay 16-bit.
  *
  *   X [M][K] bf16.  qweight/scales/qzeros as produced by awq_quantize_pack
  *   (qzeros NULL iff symmetric).  Y [M][N] bf16 out: fp32 accumulation, each
  *   128-group summed with exact integer weights (q - z) and scaled once, rounded
  *   to nearest even at the store.
  *   M > 16 returns W4_ERR_UNSUPPORTED (no silent fallback: use w4a16_gemm).
- *   workspace / workspace_bytes: K-split partial sums for shapes whose
- *   activations do not fit one workgroup's registers (size 0 for most shapes).
+ *   workspace / workspace_bytes: fp32 K-split partial sums for long K (the
+ *   wavefront form above K = 32768 at M <= 2 and K = 16384 at M = 3, 4; the
+ *   matrix-core form above K = 6144); size 0 for shorter K.
  *   Size query: workspace == NULL with workspace_bytes != NULL writes the size
  *   needed and returns W4_OK without enqueuing work.  To run a shape whose size
  *   is 0, pass workspace == NULL and workspace_bytes == NULL.

@@ -398,16 +398,27 @@ def test_gemm_large_full_size(shape, M):
     assert _elementwise_ok(y, ref) == 0
 
 
-def test_gemm_deterministic_and_overwrites():
-    X, W = wl.small_case(300, 1024, 300, 5)
+@pytest.mark.parametrize("M,K,N", [(300, 1024, 300), (64, 17408, 256)])
+def test_gemm_deterministic_and_overwrites(M, K, N):
+    """Y prefilled with NaN is fully overwritten and two calls agree bit for bit:
+    a 2-way K split (300 x 1024 x 300) and a 34-way one (two column tiles of
+    136 groups), both through the split reduction; the second also against the
+    oracle."""
+    X, W = wl.small_case(M, K, N, 5)
     qw, sc, qz = _packed(W, False)
     args = (to_bf16(X), to_i32(qw), to_bf16(sc), to_i32(qz), False)
-    Y1 = torch.full((300, 300), float("nan"), dtype=torch.bfloat16, device="cuda")
+    say("gemm determinism", M, K, N)
+    Y1 = torch.full((M, N), float("nan"), dtype=torch.bfloat16, device="cuda")
     w4.w4a16_gemm(*args, Y=Y1)
     Y2 = w4.w4a16_gemm(*args)
     torch.cuda.synchronize()
     assert not torch.isnan(Y1.float()).any()
     assert np.array_equal(bits16(Y1), bits16(Y2))
+    if M == 64:
+        y = bf16_values(bits16(Y1))
+        ref = O.linear(X, O.dequantize(qw, sc, qz, K, False))
+        _fro_ok(y, ref)
+        assert _elementwise_ok(y, ref) == 0
 
 
 # ----------------------------------------------------------------------------- unquantized bf16 linear
@@ -607,6 +618,24 @@ def test_w4a8_gemv_large_full_size(shape, M):
     ref = O.w4a8_linear(oq, osx, qw[cols], sc[cols], None, W.shape[1], True)
     _fro_ok(y[:, cols], ref)
     assert _elementwise_ok(y[:, cols], ref) == 0
+
+
+@pytest.mark.parametrize("M,K,N", [(1, 2048, 300), (16, 17408, 40), (3, 51200, 20)])
+def test_w4a8_gemv_deterministic_and_overwrites(M, K, N):
+    """Y prefilled with NaN is fully overwritten and two calls agree bit for bit:
+    one workgroup per 16-channel tile (K = 2048) and the split over K with the
+    fp32 partials added in split order (K = 17408 and 51200 on narrow N)."""
+    say("w4a8 determinism", M, K, N)
+    X, W = wl.small_case(M, K, N, 43)
+    qw, sc, qz = _packed(W, False)
+    gq, gsx, gxs, _, _, _ = _w4a8_inputs(X)
+    args = (gq, gsx, gxs, to_i32(qw), to_bf16(sc), to_i32(qz), False)
+    Y1 = torch.full((M, N), float("nan"), dtype=torch.bfloat16, device="cuda")
+    w4.w4a8_gemv(*args, Y=Y1)
+    Y2 = w4.w4a8_gemv(*args)
+    torch.cuda.synchronize()
+    assert not torch.isnan(Y1.float()).any()
+    assert np.array_equal(bits16(Y1), bits16(Y2))
 
 
 def test_w4a8_rejects_m17():

@@ -19,13 +19,17 @@
 //   o = attention(q, k, v); h = x + o Wo^T; b = rmsnorm(h, g2);
 //   m = silu(b Wg^T) * (b Wu^T); y = h + m Wd^T.
 // The unquantized projections run on the library's bf16 MFMA kernel (fp32
-// accumulation; q, k, v as one launch and gate, up as one launch, since each group
-// reads the same input); a candidate linear runs as deployed: bf16(input / s)
-// against its int4 codes Q(W diag(s), r) on the library's int4 GEMM.
+// accumulation; q, k, v as one launch with the rotary embedding of q and k in its
+// epilogue, and gate, up as one launch storing silu(gate) up, since each group reads
+// the same input; the epilogues compute exactly what the standalone rope and
+// elementwise kernels do); a candidate linear runs as deployed: bf16(input / s)
+// against its int4 codes Q(W diag(s), r) on the library's int4 GEMM, with the
+// standalone kernels around it.
 #include <math.h>
 
 #include <algorithm>
 
+#include "block_ops.hpp"
 #include "internal.hpp"
 
 #pragma clang fp contract(off)
@@ -99,8 +103,10 @@ __global__ __launch_bounds__(256) void rope_kernel(uint16_t* __restrict__ x, lon
   uint16_t* base = x + th * kHd;
   const float x1 = bf16_bits_to_f32(base[j]), x2 = bf16_bits_to_f32(base[j + 64]);
   const float c = cs[p * 64 + j], s = sn[p * 64 + j];
-  base[j] = (uint16_t)f32_to_bf16_bits(x1 * c - x2 * s);
-  base[j + 64] = (uint16_t)f32_to_bf16_bits(x2 * c + x1 * s);
+  float y1, y2;
+  rope_rotate(x1, x2, c, s, y1, y2);
+  base[j] = (uint16_t)f32_to_bf16_bits(y1);
+  base[j + 64] = (uint16_t)f32_to_bf16_bits(y2);
 }
 
 // Causal grouped-query attention on the matrix cores.  Workgroup (block of 128
@@ -254,7 +260,7 @@ __global__ __launch_bounds__(256) void elementwise_kernel(const uint16_t* __rest
     for (int e = 0; e < 2; ++e) {
       const float x = e ? __uint_as_float(a[q] & 0xFFFF0000u) : __uint_as_float(a[q] << 16);
       const float y = e ? __uint_as_float(b[q] & 0xFFFF0000u) : __uint_as_float(b[q] << 16);
-      r[e] = OP == EW_ADD ? x + y : x / (1.0f + expf(-x)) * y;
+      r[e] = OP == EW_ADD ? x + y : silu_mul_f32(x, y);
     }
     o[q] = f32_to_bf16_bits(r[0]) | (f32_to_bf16_bits(r[1]) << 16);
   }
@@ -433,25 +439,25 @@ int run_block(const Dims& d, const w4_block& blk, const uint16_t* X, uint16_t* Y
   if (stage == 0) {
     hipLaunchKernelGGL(rmsnorm_kernel, dim3(nrow), dim3(256), 0, st, X, d.T, d.H, blk.norm1, buf(l.a));
     W4_CHECK_LAUNCH();
+    const float* cs = reinterpret_cast<const float*>(ws + l.cs);
+    const float* sn = reinterpret_cast<const float*>(ws + l.sn);
     if (cand && cand->linear <= 2) {
       if ((rc = run_linear(d, 0, buf(l.a), blk.wq, cand, buf(l.q), st))) return rc;
       if ((rc = run_linear(d, 1, buf(l.a), blk.wk, cand, buf(l.k), st))) return rc;
       if ((rc = run_linear(d, 2, buf(l.a), blk.wv, cand, buf(l.v), st))) return rc;
-    } else {      // q, k and v read the same normalized input: one launch
+      const long long qi = (long long)T * d.nq * 64, ki = (long long)T * d.nkv * 64;
+      hipLaunchKernelGGL(rope_kernel, dim3((unsigned)((qi + 255) / 256)), dim3(256), 0, st, buf(l.q), qi, d.nq, d.L,
+                         cs, sn);
+      W4_CHECK_LAUNCH();
+      hipLaunchKernelGGL(rope_kernel, dim3((unsigned)((ki + 255) / 256)), dim3(256), 0, st, buf(l.k), ki, d.nkv,
+                         d.L, cs, sn);
+      W4_CHECK_LAUNCH();
+    } else {      // q, k and v read the same normalized input: one launch, q and k rotated in its epilogue
       const uint16_t* Ws[3] = {blk.wq, blk.wk, blk.wv};
       const int Ns[3] = {d.QD, d.KD, d.KD};
       uint16_t* Ys[3] = {buf(l.q), buf(l.k), buf(l.v)};
-      if ((rc = launch_bf16_gemm_multi(buf(l.a), d.T, d.H, 3, Ws, Ns, Ys, st))) return rc;
+      if ((rc = launch_bf16_gemm_rope(buf(l.a), d.T, d.H, 3, Ws, Ns, Ys, 0x3, cs, sn, d.L, st))) return rc;
     }
-    const float* cs = reinterpret_cast<const float*>(ws + l.cs);
-    const float* sn = reinterpret_cast<const float*>(ws + l.sn);
-    const long long qi = (long long)T * d.nq * 64, ki = (long long)T * d.nkv * 64;
-    hipLaunchKernelGGL(rope_kernel, dim3((unsigned)((qi + 255) / 256)), dim3(256), 0, st, buf(l.q), qi, d.nq, d.L, cs,
-                       sn);
-    W4_CHECK_LAUNCH();
-    hipLaunchKernelGGL(rope_kernel, dim3((unsigned)((ki + 255) / 256)), dim3(256), 0, st, buf(l.k), ki, d.nkv, d.L,
-                       cs, sn);
-    W4_CHECK_LAUNCH();
     hipLaunchKernelGGL(attention_mfma_kernel, dim3((unsigned)((d.L + kFaQ - 1) / kFaQ), (unsigned)d.nq, (unsigned)d.B),
                        dim3(256), 0, st, buf(l.q), buf(l.k), buf(l.v), d.L, d.nq, d.nkv, buf(l.o));
     W4_CHECK_LAUNCH();
@@ -470,13 +476,10 @@ int run_block(const Dims& d, const w4_block& blk, const uint16_t* X, uint16_t* Y
   if (cand && (cand->linear == 4 || cand->linear == 5)) {
     if ((rc = run_linear(d, 4, buf(l.b2), blk.wgate, cand, buf(l.gt), st))) return rc;
     if ((rc = run_linear(d, 5, buf(l.b2), blk.wup, cand, buf(l.up), st))) return rc;
-  } else {        // gate and up read the same normalized input: one launch
-    const uint16_t* Ws[2] = {blk.wgate, blk.wup};
-    const int Ns[2] = {d.I, d.I};
-    uint16_t* Ys[2] = {buf(l.gt), buf(l.up)};
-    if ((rc = launch_bf16_gemm_multi(buf(l.b2), d.T, d.H, 2, Ws, Ns, Ys, st))) return rc;
+    if ((rc = ew_launch(EW_SILU_MUL, buf(l.gt), buf(l.up), T * d.I, buf(l.m), st))) return rc;
+  } else {        // gate and up read the same normalized input: one launch, silu(gate) up in its epilogue
+    if ((rc = launch_bf16_glu(buf(l.b2), d.T, d.H, d.I, blk.wgate, blk.wup, buf(l.m), st))) return rc;
   }
-  if ((rc = ew_launch(EW_SILU_MUL, buf(l.gt), buf(l.up), T * d.I, buf(l.m), st))) return rc;
   if (cand && cand->linear == 6) {
     if ((rc = run_linear(d, 6, buf(l.m), blk.wdown, cand, buf(l.dn), st))) return rc;
     return ew_launch(EW_ADD, h, buf(l.dn), T * d.H, Y, st);

@@ -10,13 +10,23 @@
 // same X (the q, k, v projections; gate and up): their output tiles are laid
 // side by side along N, each tile belonging to one weight.  A segment may add a
 // residual R [M][N] in its epilogue: Y = bf16(R + bf16(X W^T)), the same roundings
-// as a separate add of the rounded product.  Workgroup tile 128 x 128, four waves of 64 x 64
+// as a separate add of the rounded product.  Two more epilogues fuse the decoder
+// block's elementwise steps (model card "qwen3-1.7b_q326_channel", "Model
+// Architecture"), with the arithmetic of the standalone kernels (block_ops.hpp):
+//  * GLU: a tile covers 64 columns of the gate weight and the same 64 columns of
+//    the up weight (W rows 0-63 and 64-127 of the stage); the gate waves hand their
+//    bf16 values to the up waves through LDS, which store bf16(silu(gate) up);
+//  * RoPE: on the segments it is asked for (q, k: 128-column tiles are heads), the
+//    two waves holding dims j and j + 64 of the same rows trade their bf16 values
+//    through LDS and store the rotated pair (position = row % L).
+// Workgroup tile 128 x 128, four waves of 64 x 64
 // (2 x 2 blocks of v_mfma_f32_32x32x16_bf16, fp32 accumulation), K in stages of
 // 64 channels: per stage and workgroup 16 KB of X and 16 KB of W travel from
 // global memory straight into LDS (global_load_lds_dwordx4, no registers), S
 // stages deep.  Inside a 128-byte LDS row the 16-byte chunk c is stored at
 // position c ^ ((row >> 1) & 7): a 16-lane pass of fragment reads (16 rows, one
 // chunk each) then covers all 64 banks once.
+#include "block_ops.hpp"
 #include "gemm_core.hpp"
 
 namespace w4 {
@@ -57,7 +67,11 @@ __device__ __forceinline__ int swz(int r) { return kB16K == 64 ? (r >> 1) & 7 : 
 
 // Up to three weights reading the same X: segment s has W[s] [N[s]][K] and writes
 // Y[s] [M][N[s]] (plus R[s] [M][N[s]] when not NULL); its 128-column tiles are
-// tiles t0[s] .. t0[s + 1] - 1 along N.
+// tiles t0[s] .. t0[s + 1] - 1 along N.  GLU: one segment, W[0] the gate and W[1]
+// the up weight, 64-column tiles.  RoPE: segments whose bit is set in rope_mask
+// are rotated with the tables cs, sn [L][64].
+enum { B16_PLAIN = 0, B16_GLU = 1, B16_ROPE = 2 };
+
 struct B16Args {
   const uint16_t* X;
   int M, K;
@@ -67,10 +81,16 @@ struct B16Args {
   const uint16_t* R[3];
   int N[3];
   int t0[4];
+  const float* cs;
+  const float* sn;
+  int L;
+  int rope_mask;
 };
 
-template <int S>
+template <int S, int MODE>
 __global__ __launch_bounds__(kB16Waves * 64, kB16Blocks) void bf16_gemm_kernel(B16Args g) {
+  constexpr int kTN = MODE == B16_GLU ? kB16N / 2 : kB16N;   // output columns per tile
+  static_assert(MODE != B16_GLU || kB16CW % 2 == 0, "gate and up copies split evenly");
   constexpr int D = S - 1;                 // stages in flight ahead of the one computed
   __shared__ __attribute__((aligned(1024))) unsigned char smem[S * kB16Stage];
   const int tid = threadIdx.x;
@@ -87,7 +107,7 @@ __global__ __launch_bounds__(kB16Waves * 64, kB16Blocks) void bf16_gemm_kernel(B
   uint16_t* __restrict__ Y = g.Y[seg];
   const uint16_t* __restrict__ R = g.R[seg];
   const int N = g.N[seg];
-  const int m0 = tm * kB16M, n0 = (tn - g.t0[seg]) * kB16N;
+  const int m0 = tm * kB16M, n0 = (tn - g.t0[seg]) * kTN;
   const int KT = K / kB16K;
   const uint32_t smem_base = (uint32_t)(uintptr_t)smem;
 
@@ -107,10 +127,13 @@ __global__ __launch_bounds__(kB16Waves * 64, kB16Blocks) void bf16_gemm_kernel(B
   for (int u = 0; u < kB16CW; ++u) {
     const int r = kB16RowsPerCopy * (wave + kB16Waves * u) + lane / kB16Chunks;
     const int c = (lane % kB16Chunks) ^ swz(r);
-    woff[u] = ((uint32_t)min(n0 + r, N - 1) * (uint32_t)K + (uint32_t)(8 * c)) * 2u;
+    // GLU: stage rows 0-63 (copies u < kB16CW / 2) are gate rows n0 .., 64-127 up rows n0 ..
+    const int wr = MODE == B16_GLU ? (r & (kTN - 1)) : r;
+    woff[u] = ((uint32_t)min(n0 + wr, N - 1) * (uint32_t)K + (uint32_t)(8 * c)) * 2u;
   }
   const unsigned char* xb = reinterpret_cast<const unsigned char*>(X);
   const unsigned char* wb = reinterpret_cast<const unsigned char*>(W);
+  const unsigned char* wb2 = reinterpret_cast<const unsigned char*>(g.W[1]);
   auto issue = [&](int kt, int stage) {
     const unsigned char* xs = xb + (size_t)kt * (kB16K * 2);
     const unsigned char* ws = wb + (size_t)kt * (kB16K * 2);
@@ -118,7 +141,11 @@ __global__ __launch_bounds__(kB16Waves * 64, kB16Blocks) void bf16_gemm_kernel(B
 #pragma unroll
     for (int u = 0; u < kB16CX; ++u) lds_copy16(xoff[u], xs, st + (wave + kB16Waves * u) * 1024);
 #pragma unroll
-    for (int u = 0; u < kB16CW; ++u) lds_copy16(woff[u], ws, st + kB16XPart + (wave + kB16Waves * u) * 1024);
+    for (int u = 0; u < kB16CW; ++u) {
+      const unsigned char* wsrc =
+          MODE == B16_GLU && u >= kB16CW / 2 ? wb2 + (size_t)kt * (kB16K * 2) : ws;
+      lds_copy16(woff[u], wsrc, st + kB16XPart + (wave + kB16Waves * u) * 1024);
+    }
   };
 
   // fragment reads: row (or column) 32 b + l32 of this wave's quarter, logical chunk
@@ -176,6 +203,62 @@ __global__ __launch_bounds__(kB16Waves * 64, kB16Blocks) void bf16_gemm_kernel(B
   }
   wait_vmcnt<0>();
 
+  // Fused elementwise step.  The two waves of a row half (wn = 0, 1) hold partner
+  // values at the same lane and register: columns c and 64 + c of the tile (RoPE:
+  // dims j and j + 64 of a head) or gate and up of column c (GLU).  Each hands its
+  // bf16-rounded values over through LDS (the stage buffers, free after the
+  // barrier), pairs of registers per 4-byte word.
+  if constexpr (MODE != B16_PLAIN) {
+    if (MODE == B16_GLU || ((g.rope_mask >> seg) & 1)) {      // uniform per workgroup
+      uint32_t* xw = reinterpret_cast<uint32_t*>(smem);
+      auto slot = [&](int w_n, int i, int jn, int rp) {
+        return ((((wm * 2 + w_n) * 2 + i) * 2 + jn) * 8 + rp) * 64 + lane;
+      };
+      static_assert(kB16M / 64 * 2 * 2 * 2 * 8 * 64 * 4 <= S * kB16Stage, "exchange fits the stages");
+      lds_barrier();                          // every wave is past its last fragment read
+      if (MODE == B16_ROPE || wn == 0) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+          for (int jn = 0; jn < 2; ++jn)
+#pragma unroll
+            for (int rp = 0; rp < 8; ++rp)
+              xw[slot(wn, i, jn, rp)] =
+                  f32_to_bf16_bits(acc[i][jn][2 * rp]) | (f32_to_bf16_bits(acc[i][jn][2 * rp + 1]) << 16);
+      }
+      lds_barrier();
+      if (MODE == B16_GLU && wn == 0) return;  // the up waves store
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int jn = 0; jn < 2; ++jn)
+#pragma unroll
+          for (int rp = 0; rp < 8; ++rp) {
+            const uint32_t pw = xw[slot(MODE == B16_GLU ? 0 : 1 - wn, i, jn, rp)];
+#pragma unroll
+            for (int e = 0; e < 2; ++e) {
+              const int r = 2 * rp + e;
+              const float own = bf16_bits_to_f32(f32_to_bf16_bits(acc[i][jn][r]));
+              const float other = bf16_bits_to_f32(e ? pw >> 16 : pw & 0xFFFFu);
+              if constexpr (MODE == B16_GLU) {
+                acc[i][jn][r] = silu_mul_f32(other, own);
+              } else {
+                const int row = m0 + 64 * wm + 32 * i + 8 * (r >> 2) + 4 * h + (r & 3);
+                const int j = 32 * jn + l32;
+                const int p = row % g.L;
+                const float c = g.cs[p * 64 + j], sv = g.sn[p * 64 + j];
+                float y1, y2;
+                if (wn == 0)
+                  rope_rotate(own, other, c, sv, y1, y2);
+                else
+                  rope_rotate(other, own, c, sv, y1, y2);
+                acc[i][jn][r] = wn == 0 ? y1 : y2;
+              }
+            }
+          }
+    }
+  }
+
   // Epilogue.  A lane holds column l32 and rows 8 i + 4 h + jj (register 4 i + jj)
   // of a block.  Neighbouring lanes (columns c, c + 1) trade values so that the
   // even lane holds both columns of the even registers' rows and the odd lane of
@@ -184,7 +267,7 @@ __global__ __launch_bounds__(kB16Waves * 64, kB16Blocks) void bf16_gemm_kernel(B
   const bool pair_ok = (N & 1) == 0;       // 4-byte aligned pairs; otherwise one bf16 per store
 #pragma unroll
   for (int jn = 0; jn < 2; ++jn) {
-    const int col = n0 + 64 * wn + 32 * jn + l32;
+    const int col = n0 + (MODE == B16_GLU ? 0 : 64 * wn) + 32 * jn + l32;
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
@@ -223,10 +306,23 @@ __global__ __launch_bounds__(kB16Waves * 64, kB16Blocks) void bf16_gemm_kernel(B
 
 }  // namespace
 
-int launch_bf16_gemm_multi(const uint16_t* X, int M, int K, int nseg, const uint16_t* const* W, const int* N,
-                           uint16_t* const* Y, hipStream_t stream, const uint16_t* const* R) {
+namespace {
+
+template <int MODE>
+int launch_b16(const B16Args& g, long long tiles, hipStream_t stream) {
+  if (tiles == 0) return W4_OK;
+  if (tiles > 0x7FFFFFFFLL) return W4_ERR_SHAPE;
+  hipLaunchKernelGGL((bf16_gemm_kernel<W4_BF16_GEMM_STAGES, MODE>), dim3((unsigned)tiles), dim3(kB16Waves * 64), 0,
+                     stream, g);
+  W4_CHECK_LAUNCH();
+  return W4_OK;
+}
+
+// Arguments of a launch over nseg weights reading X; the tile count through `tiles`.
+int b16_args(const uint16_t* X, int M, int K, int nseg, const uint16_t* const* W, const int* N, uint16_t* const* Y,
+             const uint16_t* const* R, B16Args& g, long long& tiles) {
   if (nseg < 1 || nseg > 3 || K <= 0 || K % kB16K) return W4_ERR_SHAPE;
-  B16Args g{};
+  g = B16Args{};
   g.X = X;
   g.M = M;
   g.K = K;
@@ -249,13 +345,46 @@ int launch_bf16_gemm_multi(const uint16_t* X, int M, int K, int nseg, const uint
     g.R[s] = nullptr;
     g.N[s] = 0;
   }
-  const long long tiles = (long long)((M + kB16M - 1) / kB16M) * t;
-  if (tiles == 0) return W4_OK;
-  if (tiles > 0x7FFFFFFFLL) return W4_ERR_SHAPE;
-  hipLaunchKernelGGL(bf16_gemm_kernel<W4_BF16_GEMM_STAGES>, dim3((unsigned)tiles), dim3(kB16Waves * 64), 0, stream,
-                     g);
-  W4_CHECK_LAUNCH();
+  tiles = (long long)((M + kB16M - 1) / kB16M) * t;
   return W4_OK;
+}
+
+}  // namespace
+
+int launch_bf16_gemm_multi(const uint16_t* X, int M, int K, int nseg, const uint16_t* const* W, const int* N,
+                           uint16_t* const* Y, hipStream_t stream, const uint16_t* const* R) {
+  B16Args g;
+  long long tiles = 0;
+  if (int st = b16_args(X, M, K, nseg, W, N, Y, R, g, tiles)) return st;
+  return launch_b16<B16_PLAIN>(g, tiles, stream);
+}
+
+int launch_bf16_gemm_rope(const uint16_t* X, int M, int K, int nseg, const uint16_t* const* W, const int* N,
+                          uint16_t* const* Y, int rope_mask, const float* cs, const float* sn, int L,
+                          hipStream_t stream) {
+  B16Args g;
+  long long tiles = 0;
+  if (int st = b16_args(X, M, K, nseg, W, N, Y, nullptr, g, tiles)) return st;
+  if (L < 1) return W4_ERR_SHAPE;
+  for (int s = 0; s < nseg; ++s)
+    if (((rope_mask >> s) & 1) && N[s] % 128) return W4_ERR_SHAPE;     // whole heads per tile
+  g.cs = cs;
+  g.sn = sn;
+  g.L = L;
+  g.rope_mask = rope_mask;
+  return launch_b16<B16_ROPE>(g, tiles, stream);
+}
+
+int launch_bf16_glu(const uint16_t* X, int M, int K, int N, const uint16_t* Wg, const uint16_t* Wu, uint16_t* Y,
+                    hipStream_t stream) {
+  B16Args g;
+  long long tiles = 0;
+  if (int st = b16_args(X, M, K, 1, &Wg, &N, &Y, nullptr, g, tiles)) return st;
+  g.W[1] = Wu;
+  const long long t = (N + kB16N / 2 - 1) / (kB16N / 2);
+  for (int s = 1; s < 4; ++s) g.t0[s] = (int)t;
+  tiles = (long long)((M + kB16M - 1) / kB16M) * t;
+  return launch_b16<B16_GLU>(g, tiles, stream);
 }
 
 int launch_bf16_gemm(const uint16_t* X, int M, int K, int N, const uint16_t* W, uint16_t* Y, hipStream_t stream) {

@@ -97,6 +97,15 @@ int launch_bf16_gemm(const uint16_t* X, int M, int K, int N, const uint16_t* W, 
 // or bf16(R[s] + bf16(X W[s]^T)) with residuals R (NULL: none; R[s] NULL: none for s).
 int launch_bf16_gemm_multi(const uint16_t* X, int M, int K, int nseg, const uint16_t* const* W, const int* N,
                            uint16_t* const* Y, hipStream_t stream, const uint16_t* const* R = nullptr);
+// As launch_bf16_gemm_multi without residuals; the segments whose bit is set in
+// rope_mask (N[s] a multiple of the head size 128) get the rotary embedding of row
+// position row % L from the tables cs, sn [L][64], as the standalone rope kernel.
+int launch_bf16_gemm_rope(const uint16_t* X, int M, int K, int nseg, const uint16_t* const* W, const int* N,
+                          uint16_t* const* Y, int rope_mask, const float* cs, const float* sn, int L,
+                          hipStream_t stream);
+// Y = bf16(silu(bf16(X Wg^T)) bf16(X Wu^T)) [M][N] in one launch (gate and up [N][K]).
+int launch_bf16_glu(const uint16_t* X, int M, int K, int N, const uint16_t* Wg, const uint16_t* Wu, uint16_t* Y,
+                    hipStream_t stream);
 
 // Y = bf16(X W^T) with bf16 weights W [N][K] (the unquantized reference output).
 int launch_reference_gemm(const uint16_t* X, int M, int K, int N, const uint16_t* W, uint16_t* Y,

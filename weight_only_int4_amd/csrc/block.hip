@@ -129,7 +129,17 @@ __global__ __launch_bounds__(256) void attention_mfma_kernel(const uint16_t* __r
                                                              int n_kv, uint16_t* __restrict__ O) {
   __shared__ __align__(16) uint16_t ks[kFaK * kFaKRow];
   __shared__ __align__(16) uint16_t vt[kHd * kFaVRow];
-  const int qb = blockIdx.x, hq = blockIdx.y, b = blockIdx.z;
+  // Workgroup -> (query block, head, sequence).  A query block's work grows with its
+  // index (causal), and workgroups go to the 8 XCDs round-robin, so the blocks are
+  // ordered by rank, every rank over all heads and sequences: the heavier half first
+  // in decreasing order, then the lighter half in increasing order (4 blocks: 3, 2,
+  // 0, 1), so that a CU's first and second workgroup tend to pair heavy with light.
+  const int nqb = (int)gridDim.x, nhs = (int)(gridDim.y * gridDim.z);
+  const int wg = (int)(blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z));
+  const int rank = wg / nhs, hs = wg - rank * nhs;
+  const int half = (nqb + 1) / 2;
+  const int qb = rank < half ? nqb - 1 - rank : rank - half;
+  const int hq = hs % n_q, b = hs / n_q;
   const int kvh = hq / (n_q / n_kv);
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -152,20 +162,25 @@ __global__ __launch_bounds__(256) void attention_mfma_kernel(const uint16_t* __r
   const float scale = 1.0f / sqrtf((float)kHd);
   float mx = -INFINITY, sum = 0.0f;
   const int kend = min(L, qb * kFaQ + kFaQ);            // keys the workgroup needs: 0 .. kend-1
+  // staging: thread -> (key tid / 8, dims 16 (tid % 8) .. +15) of K and of V; the
+  // next key block is loaded into registers while the current one is computed
+  const int kj = tid >> 3, part = tid & 7;
+  uint4 k0, k1, v0, v1;
+  auto load_kv = [&](int kb) {
+    const int key = kb + kj;
+    k0 = make_uint4(0u, 0u, 0u, 0u), k1 = k0, v0 = k0, v1 = k0;
+    if (key < kend) {
+      const size_t src = (tok0 + key) * kstride + (size_t)kvh * kHd + 16 * part;
+      k0 = *reinterpret_cast<const uint4*>(Kx + src);
+      k1 = *reinterpret_cast<const uint4*>(Kx + src + 8);
+      v0 = *reinterpret_cast<const uint4*>(V + src);
+      v1 = *reinterpret_cast<const uint4*>(V + src + 8);
+    }
+  };
+  load_kv(0);
   for (int kb = 0; kb < kend; kb += kFaK) {
     __syncthreads();
-    // stage: thread -> (key tid / 8, dims 16 (tid % 8) .. +15) of K and of V
     {
-      const int kj = tid >> 3, part = tid & 7;
-      const int key = kb + kj;
-      uint4 k0 = make_uint4(0u, 0u, 0u, 0u), k1 = k0, v0 = k0, v1 = k0;
-      if (key < kend) {
-        const size_t src = (tok0 + key) * kstride + (size_t)kvh * kHd + 16 * part;
-        k0 = *reinterpret_cast<const uint4*>(Kx + src);
-        k1 = *reinterpret_cast<const uint4*>(Kx + src + 8);
-        v0 = *reinterpret_cast<const uint4*>(V + src);
-        v1 = *reinterpret_cast<const uint4*>(V + src + 8);
-      }
       *reinterpret_cast<uint4*>(&ks[kj * kFaKRow + 16 * part]) = k0;
       *reinterpret_cast<uint4*>(&ks[kj * kFaKRow + 16 * part + 8]) = k1;
       const int slot = (kj & ~12) | ((kj & 4) << 1) | ((kj & 8) >> 1);    // key bits 2 and 3 swapped
@@ -177,6 +192,7 @@ __global__ __launch_bounds__(256) void attention_mfma_kernel(const uint16_t* __r
       }
     }
     __syncthreads();
+    if (kb + kFaK < kend) load_kv(kb + kFaK);
     if (kb > qmax) continue;                            // every query of this wave precedes these keys
     f32x16 sc = f32x16{};
 #pragma unroll

@@ -205,57 +205,56 @@ __global__ __launch_bounds__(kB16Waves * 64, kB16Blocks) void bf16_gemm_kernel(B
 
   // Fused elementwise step.  The two waves of a row half (wn = 0, 1) hold partner
   // values at the same lane and register: columns c and 64 + c of the tile (RoPE:
-  // dims j and j + 64 of a head) or gate and up of column c (GLU).  Each hands its
-  // bf16-rounded values over through LDS (the stage buffers, free after the
-  // barrier), pairs of registers per 4-byte word.
+  // dims j and j + 64 of a head) or gate and up of column c (GLU).  Each hands all
+  // its bf16-rounded values over through LDS (the stage buffers, free after the
+  // barrier; pairs of registers per 4-byte word), then wave wn finishes the 32-row
+  // block i = wn for both partners: RoPE rotates the pair and stores both dims, GLU
+  // stores silu(gate) up.  Afterwards register block acc[s] holds the values for
+  // row block rb(s) and column half ch(s) below.
+  bool fused = false;
   if constexpr (MODE != B16_PLAIN) {
     if (MODE == B16_GLU || ((g.rope_mask >> seg) & 1)) {      // uniform per workgroup
+      fused = true;
       uint32_t* xw = reinterpret_cast<uint32_t*>(smem);
       auto slot = [&](int w_n, int i, int jn, int rp) {
         return ((((wm * 2 + w_n) * 2 + i) * 2 + jn) * 8 + rp) * 64 + lane;
       };
       static_assert(kB16M / 64 * 2 * 2 * 2 * 8 * 64 * 4 <= S * kB16Stage, "exchange fits the stages");
       lds_barrier();                          // every wave is past its last fragment read
-      if (MODE == B16_ROPE || wn == 0) {
-#pragma unroll
-        for (int i = 0; i < 2; ++i)
-#pragma unroll
-          for (int jn = 0; jn < 2; ++jn)
-#pragma unroll
-            for (int rp = 0; rp < 8; ++rp)
-              xw[slot(wn, i, jn, rp)] =
-                  f32_to_bf16_bits(acc[i][jn][2 * rp]) | (f32_to_bf16_bits(acc[i][jn][2 * rp + 1]) << 16);
-      }
-      lds_barrier();
-      if (MODE == B16_GLU && wn == 0) return;  // the up waves store
 #pragma unroll
       for (int i = 0; i < 2; ++i)
 #pragma unroll
         for (int jn = 0; jn < 2; ++jn)
 #pragma unroll
-          for (int rp = 0; rp < 8; ++rp) {
-            const uint32_t pw = xw[slot(MODE == B16_GLU ? 0 : 1 - wn, i, jn, rp)];
+          for (int rp = 0; rp < 8; ++rp)
+            xw[slot(wn, i, jn, rp)] =
+                f32_to_bf16_bits(acc[i][jn][2 * rp]) | (f32_to_bf16_bits(acc[i][jn][2 * rp + 1]) << 16);
+      lds_barrier();
 #pragma unroll
-            for (int e = 0; e < 2; ++e) {
-              const int r = 2 * rp + e;
-              const float own = bf16_bits_to_f32(f32_to_bf16_bits(acc[i][jn][r]));
-              const float other = bf16_bits_to_f32(e ? pw >> 16 : pw & 0xFFFFu);
-              if constexpr (MODE == B16_GLU) {
-                acc[i][jn][r] = silu_mul_f32(other, own);
-              } else {
-                const int row = m0 + 64 * wm + 32 * i + 8 * (r >> 2) + 4 * h + (r & 3);
-                const int j = 32 * jn + l32;
-                const int p = row % g.L;
-                const float c = g.cs[p * 64 + j], sv = g.sn[p * 64 + j];
-                float y1, y2;
-                if (wn == 0)
-                  rope_rotate(own, other, c, sv, y1, y2);
-                else
-                  rope_rotate(other, own, c, sv, y1, y2);
-                acc[i][jn][r] = wn == 0 ? y1 : y2;
-              }
+      for (int jn = 0; jn < 2; ++jn)
+#pragma unroll
+        for (int rp = 0; rp < 8; ++rp) {
+          const uint32_t pw = xw[slot(1 - wn, wn, jn, rp)];    // the partner's row block i = wn
+#pragma unroll
+          for (int e = 0; e < 2; ++e) {
+            const int r = 2 * rp + e;
+            const float own = bf16_bits_to_f32(f32_to_bf16_bits(wn ? acc[1][jn][r] : acc[0][jn][r]));
+            const float other = bf16_bits_to_f32(e ? pw >> 16 : pw & 0xFFFFu);
+            const float lo = wn ? other : own;      // column c (dim j) or gate
+            const float hi = wn ? own : other;      // column 64 + c (dim j + 64) or up
+            if constexpr (MODE == B16_GLU) {
+              acc[0][jn][r] = silu_mul_f32(lo, hi);
+            } else {
+              const int row = m0 + 64 * wm + 32 * wn + 8 * (r >> 2) + 4 * h + (r & 3);
+              const int j = 32 * jn + l32;
+              const int p = row % g.L;
+              float y1, y2;
+              rope_rotate(lo, hi, g.cs[p * 64 + j], g.sn[p * 64 + j], y1, y2);
+              acc[0][jn][r] = y1;
+              acc[1][jn][r] = y2;
             }
           }
+        }
     }
   }
 
@@ -265,17 +264,21 @@ __global__ __launch_bounds__(kB16Waves * 64, kB16Blocks) void bf16_gemm_kernel(B
   // the odd registers' rows: one 4-byte store of a bf16 pair per two values.
   const bool odd = l32 & 1;
   const bool pair_ok = (N & 1) == 0;       // 4-byte aligned pairs; otherwise one bf16 per store
+  // register block s: row block rb and column half ch (GLU tiles have no column half)
 #pragma unroll
   for (int jn = 0; jn < 2; ++jn) {
-    const int col = n0 + (MODE == B16_GLU ? 0 : 64 * wn) + 32 * jn + l32;
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int sb = 0; sb < 2; ++sb) {
+      if (MODE == B16_GLU && sb == 1) continue;
+      const int rblk = fused ? wn : sb;
+      const int ch = MODE == B16_GLU ? 0 : (fused ? sb : wn);
+      const int col = n0 + 64 * ch + 32 * jn + l32;
 #pragma unroll
       for (int r = 0; r < 16; r += 2) {
-        const float v0 = acc[i][jn][r], v1 = acc[i][jn][r + 1];
+        const float v0 = acc[sb][jn][r], v1 = acc[sb][jn][r + 1];
         const float send = odd ? v0 : v1;
         const float recv = __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(send), 0xB1, 0xF, 0xF, true));
-        const int row0 = m0 + 64 * wm + 32 * i + 8 * (r >> 2) + 4 * h + (r & 3);   // register r + 1: row0 + 1
+        const int row0 = m0 + 64 * wm + 32 * rblk + 8 * (r >> 2) + 4 * h + (r & 3);   // register r + 1: row0 + 1
         if (pair_ok) {
           const int row = odd ? row0 + 1 : row0;
           const int c0 = col & ~1;
@@ -301,6 +304,7 @@ __global__ __launch_bounds__(kB16Waves * 64, kB16Blocks) void bf16_gemm_kernel(B
           if (row0 + 1 < M) put(row0 + 1, v1);
         }
       }
+    }
   }
 }
 

@@ -14,11 +14,13 @@
 // block's elementwise steps (model card "qwen3-1.7b_q326_channel", "Model
 // Architecture"), with the arithmetic of the standalone kernels (block_ops.hpp):
 //  * GLU: a tile covers 64 columns of the gate weight and the same 64 columns of
-//    the up weight (W rows 0-63 and 64-127 of the stage); the gate waves hand their
-//    bf16 values to the up waves through LDS, which store bf16(silu(gate) up);
+//    the up weight (W rows 0-63 and 64-127 of the stage) and stores
+//    bf16(silu(gate) up);
 //  * RoPE: on the segments it is asked for (q, k: 128-column tiles are heads), the
-//    two waves holding dims j and j + 64 of the same rows trade their bf16 values
-//    through LDS and store the rotated pair (position = row % L).
+//    tile stores the rotated pairs of dims (j, j + 64) at position row % L.
+// In both, the two waves of a row half hold partner values at the same lane and
+// register; they trade their bf16 values through LDS and each finishes one 32-row
+// block for both partners.
 // Workgroup tile 128 x 128, four waves of 64 x 64
 // (2 x 2 blocks of v_mfma_f32_32x32x16_bf16, fp32 accumulation), K in stages of
 // 64 channels: per stage and workgroup 16 KB of X and 16 KB of W travel from

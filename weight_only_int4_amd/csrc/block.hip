@@ -114,8 +114,10 @@ __global__ __launch_bounds__(256) void rope_kernel(uint16_t* __restrict__ x, lon
 // computes the transposed scores S^T = K Q^T (8 v_mfma_f32_32x32x16_bf16 over the 128
 // dims: lane (query l % 32, half h) receives the scores of keys (r % 4) + 4 h + 8 (r / 4),
 // r = 0..15), updates its query's running max and sum (the two halves of a query swap
-// their partial max and sum), and accumulates O^T += V^T P^T (8 MFMAs: 4 blocks of 32
-// dims x 2 steps of 16 keys).  The P operand of step s, element j is the lane's own
+// their partial max and sum), and accumulates O^T += V^T P^T (16 MFMAs: 4 blocks of 32
+// dims x 2 steps of 16 keys x p as bf16 hi and lo).  The next key block's K and V
+// are loaded into registers while the current one is computed.  The P operand of
+// step s, element j is the lane's own
 // score register 8 s + j, i.e. key j % 4 + 4 h + 16 s + 8 (j / 4); V^T is staged with its
 // keys in that order (key bits 2 and 3 swapped), so no value crosses lanes.  K rows
 // (272 B) and V^T rows (80 B) are padded so that 16 lanes' 16-byte reads hit distinct

@@ -15,8 +15,8 @@
 //    matching activations in registers as bf16 pairs (x_j, x_j+4) and their fp32
 //    sum.
 //  * Each wave streams its slice of every row of the slab: per row and lane one
-//    16/8/4-byte load of packed words, one 2-byte scale load and (asymmetric) one
-//    4-byte zero-word load.  These are buffer loads: an offset past the end of
+//    16-byte load of packed words (WPL = 4 words, 32 channels), one 2-byte scale
+//    load and (asymmetric) one 4-byte zero-word load.  These are buffer loads: an offset past the end of
 //    the buffer returns 0 without a memory access, so lanes past the channel
 //    range and rows past N need neither branches nor clamped re-reads.  The
 //    batch loop is unrolled (BPW is a template parameter): straight-line code in
@@ -52,15 +52,9 @@ struct GemvArgs {
 
 template <int WPL>
 __device__ __forceinline__ void load_words(__amdgpu_buffer_rsrc_t r, uint32_t off, uint32_t* w) {
-  if constexpr (WPL == 4) {
-    const auto v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
-    w[0] = v[0]; w[1] = v[1]; w[2] = v[2]; w[3] = v[3];
-  } else if constexpr (WPL == 2) {
-    const auto v = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
-    w[0] = v[0]; w[1] = v[1];
-  } else {
-    w[0] = __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
-  }
+  static_assert(WPL == 4, "one 16-byte load of four packed words per lane and row");
+  const auto v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+  w[0] = v[0]; w[1] = v[1]; w[2] = v[2]; w[3] = v[3];
 }
 
 template <int CTRL>
@@ -283,10 +277,11 @@ __global__ __launch_bounds__(256) void gemv_split_reduce(const float* partial, i
 
 namespace {
 
-// Words per lane, rows per batch and batches in flight for M activation rows
-// (the activations of one lane take 4 M WPL registers: 16 to 128).
-constexpr int gemv_wpl(int M) { return M <= 4 ? 4 : 2; }
-constexpr int gemv_rows(int M) { return M <= 8 ? 2 : 1; }
+// Words per lane, rows per batch and batches in flight of the vector-ALU form,
+// which serves M <= 4 (the activations of one lane take 16 M registers).
+constexpr int kGemvMaxM = 4;
+constexpr int gemv_wpl(int M) { return 4; }
+constexpr int gemv_rows(int M) { return 2; }
 constexpr int gemv_nb(int M) { return 2; }
 
 struct GemvPlan {
@@ -330,6 +325,7 @@ int device_cus() {
 
 template <int M, int BPW, bool SYM>
 constexpr auto gemv_instance() {
+  static_assert(M >= 1 && M <= kGemvMaxM, "larger batches take the matrix-core form");
   return gemv_kernel<M, gemv_wpl(M), gemv_rows(M), BPW, gemv_nb(M), SYM>;
 }
 

@@ -49,11 +49,12 @@ __global__ __launch_bounds__(256) void gemm_prep_kernel(const uint16_t* X, size_
                                                         const uint16_t* scales, size_t sc_stride,
                                                         const uint32_t* qzeros, size_t qz_stride, int symmetric,
                                                         int N, uint16_t* rsq, size_t rsq_stride, uint32_t* szq,
-                                                        size_t szq_stride, uint16_t* xp, int rs_blocks) {
+                                                        size_t szq_stride, uint16_t* xp, int rs_blocks, int rs_c) {
 #pragma clang fp contract(off)
   const int G = K >> 7;
   const int c = blockIdx.z;
   if ((int)blockIdx.x < rs_blocks) {
+    if (c >= rs_c) return;                                // problems that share the first one's X
     const int lane = threadIdx.x & 63;
     const int passes = (K + 511) >> 9;
     const int chunks = (passes + kPrepChunk - 1) / kPrepChunk;
@@ -141,7 +142,7 @@ __global__ __launch_bounds__(256) void gemm_prep_kernel(const uint16_t* X, size_
 int launch_gemm_prep(const uint16_t* X, size_t x_stride, int M, int K, int mpad, const uint16_t* scales,
                      size_t sc_stride, const uint32_t* qzeros, size_t qz_stride, int symmetric, int N,
                      uint16_t* rsq, size_t rsq_stride, uint32_t* szq, size_t szq_stride, uint16_t* xp, int C,
-                     hipStream_t stream) {
+                     hipStream_t stream, int rs_c) {
   const int GW = ((K >> 7) + 7) / 8;
   const int chunks = (((K + 511) >> 9) + kPrepChunk - 1) / kPrepChunk;
   const long long rs_blocks = ((long long)mpad * chunks + 3) / 4;
@@ -150,7 +151,7 @@ int launch_gemm_prep(const uint16_t* X, size_t x_stride, int M, int K, int mpad,
   if (rs_blocks + sz_blocks > 0x7FFFFFFFLL || C > 65535) return W4_ERR_SHAPE;
   hipLaunchKernelGGL(gemm_prep_kernel, dim3((unsigned)(rs_blocks + sz_blocks), 1, (unsigned)C), dim3(256), 0,
                      stream, X, x_stride, M, K, mpad, scales, sc_stride, symmetric ? nullptr : qzeros, qz_stride,
-                     symmetric, N, rsq, rsq_stride, szq, szq_stride, xp, (int)rs_blocks);
+                     symmetric, N, rsq, rsq_stride, szq, szq_stride, xp, (int)rs_blocks, rs_c < 0 ? C : rs_c);
   W4_CHECK_LAUNCH();
   return W4_OK;
 }

@@ -514,11 +514,12 @@ __global__ __launch_bounds__(kGemmWaves * 64, (GemmSmem<WIDE>::kBlocksPerCU)) vo
 //   symmetric); 0 for columns >= N.
 // When xp is not NULL it also writes X[c] pair-arranged (every 8-channel run as
 // (x0,x4)(x1,x5)(x2,x6)(x3,x7)) into xp[c] ([mpad][K], same strides as X; rows
-// M .. mpad-1 zero).
+// M .. mpad-1 zero).  Only the first rs_c problems (all when negative) get row sums
+// and arranged rows: the others share the first one's activations.
 __host__ __device__ inline int gemm_npad(int N) { return (N + kBN - 1) / kBN * kBN; }
 int launch_gemm_prep(const uint16_t* X, size_t x_stride, int M, int K, int mpad, const uint16_t* scales,
                      size_t sc_stride, const uint32_t* qzeros, size_t qz_stride, int symmetric, int N,
                      uint16_t* rsq, size_t rsq_stride, uint32_t* szq, size_t szq_stride, uint16_t* xp, int C,
-                     hipStream_t stream);
+                     hipStream_t stream, int rs_c = -1);
 
 }  // namespace w4

@@ -155,7 +155,7 @@ size_t grid_loss_workspace_bytes(int T, int K, int N, int C, bool need_yref) {
 
 int launch_grid_loss(const uint16_t* X, int T, int K, int N, const uint16_t* W, const uint16_t* Yref,
                      const float* S, const float* ratios, int C, int symmetric, float* losses,
-                     void* workspace, hipStream_t stream) {
+                     void* workspace, hipStream_t stream, bool shared_s) {
   if (C == 0) return W4_OK;
   // 32-bit per-lane byte offsets in the MFMA core: 2 tpad K and 2 N K (bf16 reference weights) below 2^32
   if (((long long)T + kBM) * K >= (1LL << 31) || (long long)N * K >= (1LL << 31)) return W4_ERR_SHAPE;
@@ -198,24 +198,26 @@ int launch_grid_loss(const uint16_t* X, int T, int K, int N, const uint16_t* W, 
   if (st != W4_OK) return st;
 
   const size_t chunks = (size_t)L.mpad * (K / 8);
-  hipLaunchKernelGGL(scale_activations_kernel, dim3((unsigned)((chunks + 255) / 256), 1, (unsigned)C), dim3(256), 0,
+  // one scaled copy of X per candidate, or one for all when they share s
+  const int CX = shared_s ? 1 : C;
+  hipLaunchKernelGGL(scale_activations_kernel, dim3((unsigned)((chunks + 255) / 256), 1, (unsigned)CX), dim3(256), 0,
                      stream, X, T, L.mpad, K, S, xs);
   W4_CHECK_LAUNCH();
   st = launch_gemm_prep(xs, (size_t)L.mpad * K, T, K, L.mpad, sc, q.sc_stride, symmetric ? nullptr : qz,
                         q.qz_stride, symmetric, N, rsq, (size_t)L.G * L.mpad * 4, szq, (size_t)L.G * L.npad, nullptr,
-                        C, stream);
+                        C, stream, CX);
   if (st != W4_OK) return st;
 
   GemmCoreArgs a{};
   a.X = xs;
-  a.x_stride = (size_t)L.mpad * K;
+  a.x_stride = shared_s ? 0 : (size_t)L.mpad * K;
   a.M = T;
   a.K = K;
   a.N = N;
   a.qweight = qw;
   a.qw_stride = q.qw_stride;
   a.rsq = rsq;
-  a.rsq_stride = (size_t)L.G * L.mpad * 4;
+  a.rsq_stride = shared_s ? 0 : (size_t)L.G * L.mpad * 4;
   a.szq = szq;
   a.szq_stride = (size_t)L.G * L.npad;
   a.mpad = L.mpad;

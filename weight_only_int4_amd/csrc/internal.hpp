@@ -59,9 +59,12 @@ int launch_gemm(const uint16_t* X, int M, int K, int N, const uint32_t* qweight,
 
 // ---------------------------------------------------------------- grid loss
 size_t grid_loss_workspace_bytes(int T, int K, int N, int C, bool need_yref);
+// shared_s: every row of S is the same (the ratio phase of the search, at s(alpha*)):
+// the scaled activations and their row sums are formed once for all candidates.
 int launch_grid_loss(const uint16_t* X, int T, int K, int N, const uint16_t* W,
                      const uint16_t* Yref, const float* S, const float* ratios, int C,
-                     int symmetric, float* losses, void* workspace, hipStream_t stream);
+                     int symmetric, float* losses, void* workspace, hipStream_t stream,
+                     bool shared_s = false);
 
 // ---------------------------------------------------------------- per-channel clipping search
 size_t clip_search_workspace_bytes(int T, int K);

@@ -381,7 +381,7 @@ int search_impl(const uint16_t* X, int T, int K, int N, const uint16_t* W, const
   if (hipMemcpyAsync(dS, S.data(), (size_t)n_ratio * K * 4, hipMemcpyHostToDevice, stream) != hipSuccess ||
       hipMemcpyAsync(dR, R.data(), (size_t)n_ratio * 4, hipMemcpyHostToDevice, stream) != hipSuccess)
     return W4_ERR_HIP;
-  st = launch_grid_loss(X, T, K, N, W, yref, dS, dR, n_ratio, symmetric, dL, grid_ws, stream);
+  st = launch_grid_loss(X, T, K, N, W, yref, dS, dR, n_ratio, symmetric, dL, grid_ws, stream, true);
   if (st) return st;
   std::vector<float> lr(n_ratio);
   if (hipMemcpyAsync(lr.data(), dL, (size_t)n_ratio * 4, hipMemcpyDeviceToHost, stream) != hipSuccess ||

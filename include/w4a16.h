@@ -117,6 +117,9 @@ int awq_quantize_pack(const uint16_t* W, int N, int K, const float* s, float cli
  *   128-group summed with exact integer weights (q - z) and scaled once, rounded
  *   to nearest even at the store.
  *   M > 16 returns W4_ERR_UNSUPPORTED (no silent fallback: use w4a16_gemm).
+ *   W4_ERR_SHAPE (from the size query too) when N K / 2 >= 2^31 or 32 K >= 2^31:
+ *   the kernels address the packed weights and the activation rows with 32-bit
+ *   byte offsets.
  *   workspace / workspace_bytes: fp32 K-split partial sums for long K (the
  *   wavefront form above K = 32768 at M <= 2 and K = 16384 at M = 3, 4; the
  *   matrix-core form above K = 6144); size 0 for shorter K.
@@ -205,6 +208,9 @@ int w4a8_gemv(const int8_t* Xq, const float* sx, const int32_t* xsum, int M, int
  *   workspace also holds their fp32 partial outputs (splits x M x N x 4 bytes,
  *   added in split order by a second kernel).  Size query as in w4a16_gemv.  The
  *   size depends only on (M, K, N); about 2 M K bytes plus the partials.
+ *   W4_ERR_SHAPE (from the size query too) when (M + 64) K >= 2^31 or
+ *   N K >= 2^33 (32-bit byte offsets into the arranged activations and the
+ *   packed weights).
  */
 int w4a16_gemm(const uint16_t* X, int M, int K, int N, const uint32_t* qweight,
                const uint16_t* scales, const uint32_t* qzeros, int symmetric, int group_size,

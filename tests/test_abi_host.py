@@ -87,6 +87,21 @@ def test_gemv_validation_and_size_query(lib):
     assert f(A, 0, 256, 8, A, A, A, 0, 128, A, None, None, None) == 0      # M = 0: empty
 
 
+def test_gemv_size_limits(lib):
+    """32-bit buffer offsets: N K / 2 < 2^31 and 32 K < 2^31, checked by the size
+    query and by the call (before any HIP call), for both decode forms."""
+    sz = ctypes.c_size_t(123)
+    f = lib.w4a16_gemv
+    for M in (1, 16):
+        # the largest N at K = 2048 (packed weights 2^31 - 1024 bytes), then one more
+        assert f(None, M, 2048, (1 << 21) - 1, None, None, None, 1, 128, None, None, ctypes.byref(sz), None) == 0
+        assert f(None, M, 2048, 1 << 21, None, None, None, 1, 128, None, None, ctypes.byref(sz), None) == -2
+        assert f(A, M, 2048, 1 << 21, A, A, None, 1, 128, A, None, None, None) == -2
+        assert lib.w4a16_gemv_noalloc(A, M, 2048, 1 << 21, A, A, None, 1, 128, A, None) == -2
+    assert f(None, 1, 1 << 26, 1, None, None, None, 1, 128, None, None, ctypes.byref(sz), None) == -2   # 32 K = 2^31
+    assert f(None, 1, (1 << 26) - 128, 1, None, None, None, 1, 128, None, None, ctypes.byref(sz), None) == 0
+
+
 def test_gemv_noalloc_validation(lib):
     f = lib.w4a16_gemv_noalloc
     assert f(A, 17, 256, 8, A, A, A, 0, 128, A, None) == -4
@@ -154,6 +169,15 @@ def test_gemm_size_query(lib):
     assert f(A, 200, 384, 8, A, A, A, 0, 128, A, A, ctypes.byref(small), None) == -5
     ok = ctypes.c_size_t(need)
     assert f(A, 200, 384, 8, A, A, A, 0, 128, MIS, A, ctypes.byref(ok), None) == -3
+    # 32-bit offsets: (M + 64) K < 2^31 (arranged activations) and N K < 2^33 (packed weights),
+    # from the size query and the call alike
+    K = 2048
+    assert f(None, (1 << 20) - 65, K, 64, None, None, None, 0, 128, None, None, ctypes.byref(sz), None) == 0
+    assert f(None, (1 << 20) - 64, K, 64, None, None, None, 0, 128, None, None, ctypes.byref(sz), None) == -2
+    big = ctypes.c_size_t(1 << 40)
+    assert f(A, (1 << 20) - 64, K, 64, A, A, A, 0, 128, A, A, ctypes.byref(big), None) == -2
+    assert f(None, 64, K, (1 << 22) - 1, None, None, None, 0, 128, None, None, ctypes.byref(sz), None) == 0
+    assert f(None, 64, K, 1 << 22, None, None, None, 0, 128, None, None, ctypes.byref(sz), None) == -2
 
 
 def test_grid_loss_validation(lib):

@@ -214,12 +214,18 @@ size_t gemm_workspace_bytes(int M, int K, int N) {
          (splits > 1 ? (size_t)splits * align_up((size_t)M * N, 64) * 4 : 0);
 }
 
+// 32-bit per-lane byte offsets in the core: the arranged activations (2 x (M + 64) x K
+// bytes) and the packed weights (N K / 2 bytes) below 2^32.
+int gemm_check_size(int M, int K, int N) {
+  if (((long long)M + kBM) * K >= (1LL << 31) || (long long)N * K >= (1LL << 33)) return W4_ERR_SHAPE;
+  return W4_OK;
+}
+
 int launch_gemm(const uint16_t* X, int M, int K, int N, const uint32_t* qweight,
                 const uint16_t* scales, const uint32_t* qzeros, int symmetric, uint16_t* Y,
                 void* workspace, hipStream_t stream) {
   if (M == 0 || N == 0) return W4_OK;
-  // 32-bit per-lane byte offsets in the kernel: 2 mpad K and N K / 2 below 2^32
-  if (((long long)M + kBM) * K >= (1LL << 31) || (long long)N * K >= (1LL << 33)) return W4_ERR_SHAPE;
+  if (int st = gemm_check_size(M, K, N)) return st;
   const int mpad = (int)align_up((size_t)M, kBM);
   const int G = K / kGroup;
   const int splits = gemm_k_splits(M, K, N);

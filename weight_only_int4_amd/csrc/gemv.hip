@@ -413,6 +413,15 @@ void launch_sym(const GemvArgs& a, const GemvPlan& p, bool symmetric, hipStream_
 
 }  // namespace
 
+// The kernels' buffer loads take 32-bit byte offsets: the packed weights (N K / 2
+// bytes) and the 16 activation rows either form addresses (2 x 16 x K bytes) stay
+// below 2^31.
+int gemv_check_size(int M, int K, int N) {
+  (void)M;
+  if ((long long)N * K / 2 >= (1LL << 31) || 2LL * W4_GEMV_MAX_M * K >= (1LL << 31)) return W4_ERR_SHAPE;
+  return W4_OK;
+}
+
 size_t gemv_workspace_bytes(int M, int K, int N) {
   if (M <= 0 || N <= 0 || K <= 0) return 0;
   if (gemv_use_mfma(M, K, N)) return gemv_mfma_workspace_bytes(M, K, N);
@@ -426,9 +435,7 @@ int launch_gemv(const uint16_t* X, int M, int K, int N, const uint32_t* qweight,
   if (M == 0 || N == 0) return W4_OK;
   if (M <= W4_GEMV_MAX_M && gemv_use_mfma(M, K, N))
     return launch_gemv_mfma(X, M, K, N, qweight, scales, qzeros, symmetric, Y, workspace, stream);
-  // buffer loads take 32-bit byte offsets: every operand below 2^31 bytes
-  // (packed words N K / 2, activations 2 M K)
-  if ((long long)N * K / 2 >= (1LL << 31) || 2LL * M * K >= (1LL << 31)) return W4_ERR_SHAPE;
+  if (int st = gemv_check_size(M, K, N)) return st;
   const GemvPlan p = plan_gemv(M, K);
   GemvArgs a{X, K, N, qweight, scales, qzeros, Y, p.splits > 1 ? static_cast<float*>(workspace) : nullptr, p.wps};
   const bool sym = symmetric != 0;

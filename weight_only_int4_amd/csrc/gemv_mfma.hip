@@ -434,9 +434,7 @@ int launch_gemv_mfma(const uint16_t* X, int M, int K, int N, const uint32_t* qwe
                      const uint32_t* qzeros, int symmetric, uint16_t* Y, void* workspace, hipStream_t stream) {
   if (M == 0 || N == 0) return W4_OK;
   if (M > kBlockCols) return W4_ERR_UNSUPPORTED;
-  // buffer loads take 32-bit byte offsets: activations (16 rows addressed) and
-  // packed words below 2^31 bytes
-  if ((long long)N * K / 2 >= (1LL << 31) || 2LL * kBlockCols * K >= (1LL << 31)) return W4_ERR_SHAPE;
+  if (int st = gemv_check_size(M, K, N)) return st;
   const MfmaPlan p = plan_mfma(K);
   MfmaArgs a{X, M, K, N, qweight, scales, qzeros, Y, p.splits > 1 ? static_cast<float*>(workspace) : nullptr,
              p.gs, p.nwk, 1};

@@ -49,6 +49,7 @@ extern "C" int w4a16_gemv_noalloc(const uint16_t* X, int M, int K, int N, const 
   if (group_size != kGroup) return W4_ERR_UNSUPPORTED;
   if (N < 0 || K <= 0 || K % kGroup != 0 || M < 0) return W4_ERR_SHAPE;
   if (M > W4_GEMV_MAX_M) return W4_ERR_UNSUPPORTED;
+  if (int st = gemv_check_size(M, K, N)) return st;
   if (gemv_workspace_bytes(M, K, N) > kScratchBytes) return W4_ERR_SCRATCH;
   if (!X || !Y) return W4_ERR_NULL;
   if (symmetric != 0 && symmetric != 1) return W4_ERR_VALUE;

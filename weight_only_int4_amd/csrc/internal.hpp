@@ -31,6 +31,10 @@ int launch_quantize_pack(const QuantArgs& a, int C, hipStream_t stream);
 // Whether a decode GEMV of this shape runs on the matrix cores (gemv_mfma.hip)
 // instead of the vector ALUs (gemv.hip).
 bool gemv_use_mfma(int M, int K, int N);
+// W4_ERR_SHAPE when a GEMV or GEMM of this shape would exceed the kernels' 32-bit
+// buffer offsets (checked by the entry points before their size queries, too).
+int gemv_check_size(int M, int K, int N);
+int gemm_check_size(int M, int K, int N);
 size_t gemv_workspace_bytes(int M, int K, int N);
 int launch_gemv(const uint16_t* X, int M, int K, int N, const uint32_t* qweight,
                 const uint16_t* scales, const uint32_t* qzeros, int symmetric, uint16_t* Y,

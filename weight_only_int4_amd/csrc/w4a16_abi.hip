@@ -79,6 +79,7 @@ int w4a16_gemv(const uint16_t* X, int M, int K, int N, const uint32_t* qweight, 
   if (st) return st;
   if (M < 0) return W4_ERR_SHAPE;
   if (M > W4_GEMV_MAX_M) return W4_ERR_UNSUPPORTED;
+  if ((st = gemv_check_size(M, K, N))) return st;
   const size_t need = gemv_workspace_bytes(M, K, N);
   if (!workspace && workspace_bytes) {
     *workspace_bytes = need;
@@ -132,6 +133,7 @@ int w4a16_gemm(const uint16_t* X, int M, int K, int N, const uint32_t* qweight, 
   int st = check_weight_shape(N, K, group_size);
   if (st) return st;
   if (M < 0) return W4_ERR_SHAPE;
+  if ((st = gemm_check_size(M, K, N))) return st;
   const size_t need = gemm_workspace_bytes(M, K, N);
   if (!workspace) {
     if (!workspace_bytes) return need ? W4_ERR_WORKSPACE : W4_OK;

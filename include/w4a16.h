@@ -243,6 +243,9 @@ int w4_bf16_linear(const uint16_t* X, int M, int K, int N, const uint16_t* W, ui
  *   S [C][K] fp32 (row c = s_c, every s_c[k] > 0).  ratios [C] fp32 in (0, 1].
  *   losses [C] fp32 out (device).  Workspace size query as in w4a16_gemm; it
  *   depends on (T, K, N, C) and on whether Yref is NULL.
+ *   W4_ERR_SHAPE (from the size query too) when (T + 64) K >= 2^31, N K >= 2^31
+ *   or C > 65535.  awq_search applies the same limits with C = max(n_alpha,
+ *   n_ratio); w4a8_gemv those of w4a16_gemv.
  * The per-tile partial sums are reduced in a fixed order: results are
  * bit-identical from run to run.
  */

@@ -102,6 +102,29 @@ def test_gemv_size_limits(lib):
     assert f(None, 1, (1 << 26) - 128, 1, None, None, None, 1, 128, None, None, ctypes.byref(sz), None) == 0
 
 
+def test_grid_loss_search_w4a8_size_limits(lib):
+    sz = ctypes.c_size_t(123)
+    g = lib.awq_grid_loss
+    # (T + 64) K < 2^31 at K = 2048; N K < 2^31; C <= 65535 -- size query and call alike
+    assert g(None, (1 << 20) - 65, 2048, 64, None, None, None, None, 1, 0, 128, None, None, ctypes.byref(sz), None) == 0
+    assert g(None, (1 << 20) - 64, 2048, 64, None, None, None, None, 1, 0, 128, None, None, ctypes.byref(sz), None) == -2
+    assert g(None, 64, 2048, 1 << 20, None, None, None, None, 1, 0, 128, None, None, ctypes.byref(sz), None) == -2
+    assert g(None, 64, 2048, 64, None, None, None, None, 65536, 0, 128, None, None, ctypes.byref(sz), None) == -2
+    big = ctypes.c_size_t(1 << 40)
+    assert g(A, (1 << 20) - 64, 2048, 64, A, None, A, A, 1, 0, 128, A, A, ctypes.byref(big), None) == -2
+    al = (ctypes.c_double * 2)(0.0, 0.5)
+    ra = (ctypes.c_double * 2)(1.0, 0.9)
+    s = lib.awq_search
+    assert s(None, 64, 2048, 1 << 20, None, al, 2, ra, 2, 0, 128, None, None, None, None, None,
+             ctypes.byref(sz), None) == -2
+    assert s(None, 64, 2048, 64, None, al, 2, ra, 2, 0, 128, None, None, None, None, None,
+             ctypes.byref(sz), None) == 0
+    w = lib.w4a8_gemv
+    assert w(None, None, None, 1, 2048, 1 << 21, None, None, None, 1, 128, None, None, ctypes.byref(sz), None) == -2
+    assert w(None, None, None, 1, 2048, (1 << 21) - 1, None, None, None, 1, 128, None, None, ctypes.byref(sz),
+             None) == 0
+
+
 def test_gemv_noalloc_validation(lib):
     f = lib.w4a16_gemv_noalloc
     assert f(A, 17, 256, 8, A, A, A, 0, 128, A, None) == -4

@@ -148,6 +148,14 @@ __global__ __launch_bounds__(256) void act_abs_finish_kernel(const double* parti
 
 }  // namespace
 
+// 32-bit per-lane byte offsets in the cores: the scaled activations (2 x (T + 64) x K
+// bytes) and the bf16 reference weights (2 N K bytes) below 2^32; C candidates on
+// grid.z.
+int grid_loss_check_size(int T, int K, int N, int C) {
+  if (((long long)T + kBM) * K >= (1LL << 31) || (long long)N * K >= (1LL << 31) || C > 65535) return W4_ERR_SHAPE;
+  return W4_OK;
+}
+
 size_t grid_loss_workspace_bytes(int T, int K, int N, int C, bool need_yref) {
   if (T <= 0 || K <= 0 || N <= 0 || C <= 0) return 0;
   return loss_layout(T, K, N, C, need_yref).total;
@@ -157,12 +165,10 @@ int launch_grid_loss(const uint16_t* X, int T, int K, int N, const uint16_t* W, 
                      const float* S, const float* ratios, int C, int symmetric, float* losses,
                      void* workspace, hipStream_t stream, bool shared_s) {
   if (C == 0) return W4_OK;
-  // 32-bit per-lane byte offsets in the MFMA core: 2 tpad K and 2 N K (bf16 reference weights) below 2^32
-  if (((long long)T + kBM) * K >= (1LL << 31) || (long long)N * K >= (1LL << 31)) return W4_ERR_SHAPE;
+  if (int st = grid_loss_check_size(T, K, N, C)) return st;
   const LossLayout L = loss_layout(T, K, N, C, Yref == nullptr);
   char* ws = static_cast<char*>(workspace);
   const dim3 tile_grid((unsigned)L.tiles, 1, 1);
-  if (C > 65535) return W4_ERR_SHAPE;
 
   if (Yref == nullptr) {
     uint16_t* yref = reinterpret_cast<uint16_t*>(ws + L.yref);

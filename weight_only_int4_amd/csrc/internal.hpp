@@ -62,6 +62,7 @@ int launch_gemm(const uint16_t* X, int M, int K, int N, const uint32_t* qweight,
                 void* workspace, hipStream_t stream);
 
 // ---------------------------------------------------------------- grid loss
+int grid_loss_check_size(int T, int K, int N, int C);
 size_t grid_loss_workspace_bytes(int T, int K, int N, int C, bool need_yref);
 // shared_s: every row of S is the same (the ratio phase of the search, at s(alpha*)):
 // the scaled activations and their row sums are formed once for all candidates.

@@ -112,6 +112,7 @@ int w4a8_gemv(const int8_t* Xq, const float* sx, const int32_t* xsum, int M, int
   if (M < 0) return W4_ERR_SHAPE;
   if (M > W4_GEMV_MAX_M) return W4_ERR_UNSUPPORTED;
   if (w4a8_plan(K, N, 256, nullptr, nullptr, nullptr) != W4_OK) return W4_ERR_UNSUPPORTED;
+  if ((st = gemv_check_size(M, K, N))) return st;
   const size_t need = w4a8_workspace_bytes(M, K, N);
   if (!workspace && workspace_bytes) {
     *workspace_bytes = need;
@@ -164,6 +165,7 @@ int awq_grid_loss(const uint16_t* X, int T, int K, int N, const uint16_t* W, con
   int st = check_weight_shape(N, K, group_size);
   if (st) return st;
   if (T <= 0 || N <= 0 || C < 0) return W4_ERR_SHAPE;
+  if ((st = grid_loss_check_size(T, K, N, C))) return st;
   if (symmetric != 0 && symmetric != 1) return W4_ERR_VALUE;
   const size_t need = grid_loss_workspace_bytes(T, K, N, C, Yref == nullptr);
   if (!workspace) {
@@ -415,6 +417,7 @@ extern "C" int awq_search(const uint16_t* X, int T, int K, int N, const uint16_t
   for (int j = 0; j < n_ratio; ++j)
     if (!(ratios[j] > 0.0 && ratios[j] <= 1.0)) return W4_ERR_VALUE;
   const int C = n_alpha > n_ratio ? n_alpha : n_ratio;
+  if ((st = grid_loss_check_size(T, K, N, C))) return st;
   const SearchLayout L = search_layout(T, K, N, C);
   if (!workspace && workspace_bytes) {
     *workspace_bytes = L.total;

@@ -293,37 +293,26 @@ __global__ __launch_bounds__(256, 2) void clip_loss_kernel(const uint16_t* __res
       z = fminf(fmaxf(rintf(-lo / sc), 0.0f), 15.0f);
     }
     // stored codes q in 0..15 (bytes), d = q - z.  The code is rint of the IEEE quotient
-    // c / sc.  The product c * rcp(sc) is within |q0| 2^-22 of that quotient (reciprocal
-    // within 1 ulp, one rounding of the product), so where q0 lies farther than
-    // |q0| 2^-20 from every half-integer both round to the same integer; a lane with
-    // any value closer redoes its codes with the division itself.
-    const float rc = __builtin_amdgcn_rcpf(sc);
+    // c / sc, obtained exactly from the correctly rounded reciprocal 1 / sc with one FMA
+    // correction (Markstein's division: q0 = c rsc, q = q0 + (c - sc q0) rsc), which
+    // equals the IEEE quotient for every bf16 divisor (the same exhaustive check as the
+    // quantizer's).
+    const float rsc = 1.0f / sc;
     auto code = [&](float k) {
       return SYM ? __builtin_amdgcn_fmed3f(k, -8.0f, 7.0f) + 8.0f : __builtin_amdgcn_fmed3f(k + z, 0.0f, 15.0f);
     };
     uint32_t dq[16];
-    float near = 0.0f;
 #pragma unroll
     for (int w = 0; w < 16; ++w) {
       uint32_t word = 0;
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
-        const float q0 = clamped(v[4 * w + u]) * rc;
-        const float k = rintf(q0);
-        near = fmaxf(near, fmaf(fabsf(q0), 0x1p-20f, fabsf(q0 - k)));
+        const float c = clamped(v[4 * w + u]);
+        const float q0 = c * rsc;
+        const float k = rintf(fmaf(fmaf(-sc, q0, c), rsc, q0));
         word = __builtin_amdgcn_cvt_pk_u8_f32(code(k), u, word);
       }
       dq[w] = word;
-    }
-    if (near >= 0.5f) {
-#pragma unroll
-      for (int w = 0; w < 16; ++w) {
-        uint32_t word = 0;
-#pragma unroll
-        for (int u = 0; u < 4; ++u)
-          word = __builtin_amdgcn_cvt_pk_u8_f32(code(rintf(clamped(v[4 * w + u]) / sc)), u, word);
-        dq[w] = word;
-      }
     }
     // e[m] = v[m] - d[m] sc with one rounding (d sc is exact: a small integer times a
     // bf16 value), the same in the products and in the epilogue

@@ -1,6 +1,6 @@
-"""The quantization kernel takes its codes from v / scale computed as
-fma(fma(-scale, q0, v), 1/scale, q0) with q0 = v * (1/scale); this must equal the
-IEEE quotient that the oracle divides with.  Checked exhaustively (every bf16 scale
+"""The quantization and clip-search kernels take their codes from v / scale
+computed as fma(fma(-scale, q0, v), 1/scale, q0) with q0 = v * (1/scale); this must
+equal the IEEE quotient that the oracle divides with.  Checked exhaustively (every bf16 scale
 significand x every fp32 significand) by a small C program compiled here."""
 import os
 import shutil

@@ -41,11 +41,13 @@ typedef int i32x4 __attribute__((ext_vector_type(4)));
 
 }  // namespace
 
-// One workgroup of 4 waves per activation row m.  Pass 1: absmax over the row (bf16
+// One workgroup of 16 waves per activation row m.  Pass 1: absmax over the row (bf16
 // -> fp32 is exact; the waves combine through LDS).  Pass 2: thread t handles the 8
-// consecutive channels 8 (t + 256 i); the 16 lanes of each 16-lane row then cover one
-// 128-channel group, whose code sum the row's first lane writes to xsum.
-constexpr int kActThreads = 256;                        // 4 waves per activation row
+// consecutive channels 8 (t + 1024 i); the 16 lanes of each 16-lane row then cover one
+// 128-channel group, whose code sum the row's first lane writes to xsum.  Both passes
+// load four chunks per thread before using them (K = 17408: 7.1 -> 5.4 us per call
+// against four waves per row and one load at a time).
+constexpr int kActThreads = 1024;                       // 16 waves per activation row
 __global__ __launch_bounds__(kActThreads) void w4a8_quant_act_kernel(const uint16_t* X, int K, int8_t* Xq,
                                                                      float* sx, int32_t* xsum) {
 #pragma clang fp contract(off)
@@ -55,13 +57,24 @@ __global__ __launch_bounds__(kActThreads) void w4a8_quant_act_kernel(const uint1
   const int lane = tid & 63;
   const int chunks = K >> 3;
   const uint16_t* xr = X + (size_t)m * K;
+  // both passes issue their loads four chunks at a time (one memory round trip per
+  // four chunks instead of one per chunk)
+  constexpr int kU = 4;
   float amax = 0.0f;
-  for (int c = tid; c < chunks; c += kActThreads) {
-    const uint4 v = *reinterpret_cast<const uint4*>(xr + 8 * c);
-    const uint32_t d[4] = {v.x, v.y, v.z, v.w};
+  for (int c0 = tid; c0 < chunks; c0 += kU * kActThreads) {
+    uint4 v[kU];
 #pragma unroll
-    for (int q = 0; q < 4; ++q)
-      amax = fmaxf(amax, fmaxf(fabsf(__uint_as_float(d[q] << 16)), fabsf(__uint_as_float(d[q] & 0xFFFF0000u))));
+    for (int u = 0; u < kU; ++u) {
+      const int c = c0 + u * kActThreads;
+      v[u] = c < chunks ? *reinterpret_cast<const uint4*>(xr + 8 * c) : make_uint4(0u, 0u, 0u, 0u);
+    }
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const uint32_t d[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        amax = fmaxf(amax, fmaxf(fabsf(__uint_as_float(d[q] << 16)), fabsf(__uint_as_float(d[q] & 0xFFFF0000u))));
+    }
   }
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off, kWave));
@@ -73,27 +86,35 @@ __global__ __launch_bounds__(kActThreads) void w4a8_quant_act_kernel(const uint1
   if (tid == 0) sx[m] = s;
   const int G = K >> 7;
   // thread t quantizes channels 8 (c0 + t) .. +7; 16 consecutive threads cover one group
-  for (int c0 = 0; c0 < chunks; c0 += kActThreads) {
-    const int c = c0 + tid;
-    int part = 0;
-    if (c < chunks) {
-      const uint4 v = *reinterpret_cast<const uint4*>(xr + 8 * c);
-      const uint32_t d[4] = {v.x, v.y, v.z, v.w};
-      uint32_t packed[2] = {0u, 0u};
+  for (int cb = 0; cb < chunks; cb += kU * kActThreads) {
+    uint4 vv[kU];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const uint32_t b = (e & 1) ? (d[e >> 1] & 0xFFFF0000u) : (d[e >> 1] << 16);
-        float q = __builtin_rintf(__uint_as_float(b) / s);
-        q = fminf(fmaxf(q, -127.0f), 127.0f);
-        const int qi = (int)q;
-        part += qi;
-        packed[e >> 2] |= ((uint32_t)qi & 0xFFu) << (8 * (e & 3));
-      }
-      *reinterpret_cast<uint2*>(Xq + (size_t)m * K + 8 * c) = make_uint2(packed[0], packed[1]);
+    for (int u = 0; u < kU; ++u) {
+      const int c = cb + u * kActThreads + tid;
+      vv[u] = c < chunks ? *reinterpret_cast<const uint4*>(xr + 8 * c) : make_uint4(0u, 0u, 0u, 0u);
     }
-    part = row16_sum_i(part);
-    const int g = (c >> 4);
-    if ((lane & 15) == 0 && c < chunks && g < G) xsum[(size_t)m * G + g] = part;
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const int c = cb + u * kActThreads + tid;
+      int part = 0;
+      if (c < chunks) {
+        const uint32_t d[4] = {vv[u].x, vv[u].y, vv[u].z, vv[u].w};
+        uint32_t packed[2] = {0u, 0u};
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const uint32_t b = (e & 1) ? (d[e >> 1] & 0xFFFF0000u) : (d[e >> 1] << 16);
+          float q = __builtin_rintf(__uint_as_float(b) / s);
+          q = fminf(fmaxf(q, -127.0f), 127.0f);
+          const int qi = (int)q;
+          part += qi;
+          packed[e >> 2] |= ((uint32_t)qi & 0xFFu) << (8 * (e & 3));
+        }
+        *reinterpret_cast<uint2*>(Xq + (size_t)m * K + 8 * c) = make_uint2(packed[0], packed[1]);
+      }
+      part = row16_sum_i(part);
+      const int g = (c >> 4);
+      if ((lane & 15) == 0 && c < chunks && g < G) xsum[(size_t)m * G + g] = part;
+    }
   }
 }
 

@@ -282,10 +282,41 @@ def row_gemm(name, flops, ms, extra=None):
     return d
 
 
+def stream_read_sweep(torch, w4, nbytes, reps, min_bytes=640 << 20):
+    """Cold plain read of nbytes: a graph of launches of the streaming-read probe, launch i
+    reading slice i of a buffer larger than the Infinity Cache, for every unroll depth,
+    load kind and grid size; returns (best ms per launch, its settings, all settings' us)."""
+    nbytes = (nbytes + 255) // 256 * 256
+    copies = max(2, -(-min_bytes // nbytes))
+    buf = torch.empty(copies * nbytes // 4, dtype=torch.int32, device="cuda")
+    buf.fill_(1)
+    sink = torch.empty(8192 * 256, dtype=torch.int32, device="cuda")
+    table, best = {}, None
+    for unroll in (1, 2, 4, 8):
+        for nt in (False, True):
+            for blocks in (256, 512, 1024, 2048, 4096, 8192):
+                ls = [Launch(lambda sl=buf[i * nbytes // 4:(i + 1) * nbytes // 4], u=unroll, n=nt, b=blocks:
+                             w4.probe_stream_read(sl, unroll=u, nontemporal=n, blocks=b, sink=sink), nbytes, 0)
+                      for i in range(copies)]
+                ms = measure_rotation(torch, ls, reps)
+                key = f"u{unroll}{'nt' if nt else ''}b{blocks}"
+                table[key] = round(ms * 1e3, 2)
+                if best is None or ms < best[0]:
+                    best = (ms, {"unroll": unroll, "nontemporal": nt, "blocks": blocks})
+    del buf, sink
+    torch.cuda.empty_cache()
+    return best[0], best[1], table
+
+
 def rows_large(torch, w4, wl, reps):
     rows = []
     # 27B-shaped symmetric linears: cold-cache GEMV at M = 1, 8 and GEMM at M = 64, 512
     for si, (K, N) in enumerate(wl.LARGE_SHAPES):
+        # yardstick: the best cold plain read of the M = 1 GEMV's bytes
+        read_bytes = gemv_bytes(1, K, N, True)
+        read_ms, read_cfg, read_table = stream_read_sweep(torch, w4, read_bytes, max(2, reps // 4))
+        rows.append(row_gemv(f"plain read cold {read_bytes} B (best of {len(read_table)} settings)", read_bytes,
+                             read_ms, {"settings": read_cfg, "us_by_setting": read_table}))
         W = to_dev_bf16(torch, wl.large_weight(si))
         # quantize + pack (HBM-bound read of bf16 W and write of the packed form)
         qw, sc, _ = w4.awq_quantize_pack(W, symmetric=True)
@@ -299,7 +330,8 @@ def rows_large(torch, w4, wl, reps):
                                    lambda m, k, n: 2 * m * k * n)
             ms = measure_rotation(torch, ls, max(2, reps // 4))
             rows.append(row_gemv(f"gemv cold M={M} K={K} N={N} sym", ls[0].nbytes, ms,
-                                 {"cache": f"cold ({len(ls)} rotating copies)"}))
+                                 {"cache": f"cold ({len(ls)} rotating copies)",
+                                  "of_best_plain_read": round(read_ms / ms, 4) if M == 1 else None}))
             del ls
         for M in (1, 16):
             X = to_dev_bf16(torch, wl.large_act(si, M))

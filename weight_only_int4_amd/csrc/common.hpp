@@ -70,6 +70,9 @@ __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
 }
+// Cache-policy operand of the raw buffer loads: 0 = default, kLoadNt = the
+// non-temporal (streaming) hint, for weights that one launch reads once.
+constexpr int kLoadNt = 2;
 // Lane offset that keeps every load out of range: all buffers here are smaller than
 // 2^31 bytes, so row offset + kOob neither wraps nor lands in range.
 constexpr uint32_t kOob = 0x80000000u;

@@ -68,7 +68,7 @@ struct MfmaArgs {
   int rw;               // slabs per workgroup
 };
 
-template <int KT, int BPW, bool SYM>
+template <int KT, int BPW, bool SYM, bool NT>
 __global__ __launch_bounds__(max_waves(KT) * 64) void gemv_mfma_kernel(MfmaArgs a) {
   constexpr int NB = 2;            // blocks in flight
   constexpr int bpw = BPW;
@@ -150,7 +150,7 @@ __global__ __launch_bounds__(max_waves(KT) * 64) void gemv_mfma_kernel(MfmaArgs 
     const uint32_t ow = opaque_vgpr(nw * wrow), os = opaque_vgpr(n * srow);
 #pragma unroll
     for (int t = 0; t < KT; ++t) {
-      B.w[t] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rwt, ow + kw[t], 0, 0));
+      B.w[t] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rwt, ow + kw[t], 0, NT ? kLoadNt : 0));
       B.sc[t] = __builtin_amdgcn_raw_buffer_load_b16(rsc, os + ks[t], 0, 0);
     }
     if constexpr (!SYM) B.z = __builtin_amdgcn_raw_buffer_load_b32(rzp, n * zrow + kz, 0, 0);
@@ -299,14 +299,14 @@ constexpr size_t kMaxLds = kLdsPerCu;
 constexpr size_t kDefaultLds = 64 * 1024;   // dynamic LDS a launch may take without raising the limit
 
 // Allows an instantiation more than 64 KB of dynamic LDS (once per device).
-template <int KT, int BPW, bool SYM>
+template <int KT, int BPW, bool SYM, bool NT>
 bool allow_large_lds() {
   static std::atomic<int> state[64];       // 0 not yet, 1 done, -1 failed
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return false;
   int st = state[dev].load(std::memory_order_relaxed);
   if (st == 0) {
-    st = hipFuncSetAttribute(reinterpret_cast<const void*>(gemv_mfma_kernel<KT, BPW, SYM>),
+    st = hipFuncSetAttribute(reinterpret_cast<const void*>(gemv_mfma_kernel<KT, BPW, SYM, NT>),
                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLdsPerCu) == hipSuccess
              ? 1
              : -1;
@@ -323,13 +323,13 @@ bool allow_large_lds() {
 constexpr int max_bpw(int kt, bool sym) { return kt == 4 && !sym ? 2 : 8; }
 constexpr int clamp_bpw(int kt, bool sym, int b) { return b < max_bpw(kt, sym) ? b : max_bpw(kt, sym); }
 
-template <int KT, int BPW, bool SYM>
+template <int KT, int BPW, bool SYM, bool NT>
 int mfma_blocks_per_cu(int threads) {
   static std::atomic<int> cache[kMaxWavesAny + 1];
   const int slot = threads / kWave;
   int nblk = cache[slot].load(std::memory_order_relaxed);
   if (nblk == 0) {
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nblk, gemv_mfma_kernel<KT, BPW, SYM>, threads, 0) !=
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nblk, gemv_mfma_kernel<KT, BPW, SYM, NT>, threads, 0) !=
             hipSuccess ||
         nblk < 1)
       nblk = 1;
@@ -353,7 +353,7 @@ int device_cu_count() {
 // Blocks per slab: the fewest (1 to 8) with which one round of resident
 // workgroups covers every block (the slabs take the blocks round-robin, so each
 // holds that many or one less); when no count fits one round, the largest.
-template <int KT, bool SYM>
+template <int KT, bool SYM, bool NT>
 int launch_kt(MfmaArgs a, const MfmaPlan& p, hipStream_t stream) {
   const int rw = p.nwk >= kWgWaves ? 1 : kWgWaves / p.nwk;
   a.nwk = p.nwk;
@@ -369,14 +369,14 @@ int launch_kt(MfmaArgs a, const MfmaPlan& p, hipStream_t stream) {
   };
   auto by_regs = [&](int bpw) {
     switch (bpw) {
-      case 1: return mfma_blocks_per_cu<KT, clamp_bpw(KT, SYM, 1), SYM>(threads);
-      case 2: return mfma_blocks_per_cu<KT, clamp_bpw(KT, SYM, 2), SYM>(threads);
-      case 3: return mfma_blocks_per_cu<KT, clamp_bpw(KT, SYM, 3), SYM>(threads);
-      case 4: return mfma_blocks_per_cu<KT, clamp_bpw(KT, SYM, 4), SYM>(threads);
-      case 5: return mfma_blocks_per_cu<KT, clamp_bpw(KT, SYM, 5), SYM>(threads);
-      case 6: return mfma_blocks_per_cu<KT, clamp_bpw(KT, SYM, 6), SYM>(threads);
-      case 7: return mfma_blocks_per_cu<KT, clamp_bpw(KT, SYM, 7), SYM>(threads);
-      default: return mfma_blocks_per_cu<KT, clamp_bpw(KT, SYM, 8), SYM>(threads);
+      case 1: return mfma_blocks_per_cu<KT, clamp_bpw(KT, SYM, 1), SYM, NT>(threads);
+      case 2: return mfma_blocks_per_cu<KT, clamp_bpw(KT, SYM, 2), SYM, NT>(threads);
+      case 3: return mfma_blocks_per_cu<KT, clamp_bpw(KT, SYM, 3), SYM, NT>(threads);
+      case 4: return mfma_blocks_per_cu<KT, clamp_bpw(KT, SYM, 4), SYM, NT>(threads);
+      case 5: return mfma_blocks_per_cu<KT, clamp_bpw(KT, SYM, 5), SYM, NT>(threads);
+      case 6: return mfma_blocks_per_cu<KT, clamp_bpw(KT, SYM, 6), SYM, NT>(threads);
+      case 7: return mfma_blocks_per_cu<KT, clamp_bpw(KT, SYM, 7), SYM, NT>(threads);
+      default: return mfma_blocks_per_cu<KT, clamp_bpw(KT, SYM, 8), SYM, NT>(threads);
     }
   };
   auto per_cu = [&](int bpw) {
@@ -398,14 +398,14 @@ int launch_kt(MfmaArgs a, const MfmaPlan& p, hipStream_t stream) {
     return W4_OK;
   };
   switch (best) {
-    case 1: return go(gemv_mfma_kernel<KT, clamp_bpw(KT, SYM, 1), SYM>, allow_large_lds<KT, clamp_bpw(KT, SYM, 1), SYM>);
-    case 2: return go(gemv_mfma_kernel<KT, clamp_bpw(KT, SYM, 2), SYM>, allow_large_lds<KT, clamp_bpw(KT, SYM, 2), SYM>);
-    case 3: return go(gemv_mfma_kernel<KT, clamp_bpw(KT, SYM, 3), SYM>, allow_large_lds<KT, clamp_bpw(KT, SYM, 3), SYM>);
-    case 4: return go(gemv_mfma_kernel<KT, clamp_bpw(KT, SYM, 4), SYM>, allow_large_lds<KT, clamp_bpw(KT, SYM, 4), SYM>);
-    case 5: return go(gemv_mfma_kernel<KT, clamp_bpw(KT, SYM, 5), SYM>, allow_large_lds<KT, clamp_bpw(KT, SYM, 5), SYM>);
-    case 6: return go(gemv_mfma_kernel<KT, clamp_bpw(KT, SYM, 6), SYM>, allow_large_lds<KT, clamp_bpw(KT, SYM, 6), SYM>);
-    case 7: return go(gemv_mfma_kernel<KT, clamp_bpw(KT, SYM, 7), SYM>, allow_large_lds<KT, clamp_bpw(KT, SYM, 7), SYM>);
-    default: return go(gemv_mfma_kernel<KT, clamp_bpw(KT, SYM, 8), SYM>, allow_large_lds<KT, clamp_bpw(KT, SYM, 8), SYM>);
+    case 1: return go(gemv_mfma_kernel<KT, clamp_bpw(KT, SYM, 1), SYM, NT>, allow_large_lds<KT, clamp_bpw(KT, SYM, 1), SYM, NT>);
+    case 2: return go(gemv_mfma_kernel<KT, clamp_bpw(KT, SYM, 2), SYM, NT>, allow_large_lds<KT, clamp_bpw(KT, SYM, 2), SYM, NT>);
+    case 3: return go(gemv_mfma_kernel<KT, clamp_bpw(KT, SYM, 3), SYM, NT>, allow_large_lds<KT, clamp_bpw(KT, SYM, 3), SYM, NT>);
+    case 4: return go(gemv_mfma_kernel<KT, clamp_bpw(KT, SYM, 4), SYM, NT>, allow_large_lds<KT, clamp_bpw(KT, SYM, 4), SYM, NT>);
+    case 5: return go(gemv_mfma_kernel<KT, clamp_bpw(KT, SYM, 5), SYM, NT>, allow_large_lds<KT, clamp_bpw(KT, SYM, 5), SYM, NT>);
+    case 6: return go(gemv_mfma_kernel<KT, clamp_bpw(KT, SYM, 6), SYM, NT>, allow_large_lds<KT, clamp_bpw(KT, SYM, 6), SYM, NT>);
+    case 7: return go(gemv_mfma_kernel<KT, clamp_bpw(KT, SYM, 7), SYM, NT>, allow_large_lds<KT, clamp_bpw(KT, SYM, 7), SYM, NT>);
+    default: return go(gemv_mfma_kernel<KT, clamp_bpw(KT, SYM, 8), SYM, NT>, allow_large_lds<KT, clamp_bpw(KT, SYM, 8), SYM, NT>);
   }
 }
 
@@ -424,6 +424,12 @@ bool gemv_use_mfma(int M, int K, int N) {
   return M == 4 && (long long)N * K / 2 >= (4LL << 20);
 }
 
+// Packed weights up to this size take the non-temporal hint (a measured rule).
+// Cold at M = 8: 8 MB 5.93 -> 5.65 us, 16 and 24 MB unchanged, 20 MB (K = 5120)
+// 9.3 -> 9.7 us, 30-45 MB 6-17% slower; the decode sweep's linears (2-12.6 MB)
+// 7% faster at M = 3-16.
+constexpr long long kMfmaNtMaxBytes = 16LL << 20;
+
 size_t gemv_mfma_workspace_bytes(int M, int K, int N) {
   if (M <= 0 || N <= 0 || K <= 0) return 0;
   const MfmaPlan p = plan_mfma(K);
@@ -438,11 +444,14 @@ int launch_gemv_mfma(const uint16_t* X, int M, int K, int N, const uint32_t* qwe
   const MfmaPlan p = plan_mfma(K);
   MfmaArgs a{X, M, K, N, qweight, scales, qzeros, Y, p.splits > 1 ? static_cast<float*>(workspace) : nullptr,
              p.gs, p.nwk, 1};
+  const bool nt = (long long)N * K / 2 <= kMfmaNtMaxBytes;
   int st;
   if (p.kt == 2)
-    st = symmetric ? launch_kt<2, true>(a, p, stream) : launch_kt<2, false>(a, p, stream);
+    st = symmetric ? (nt ? launch_kt<2, true, true>(a, p, stream) : launch_kt<2, true, false>(a, p, stream))
+                   : (nt ? launch_kt<2, false, true>(a, p, stream) : launch_kt<2, false, false>(a, p, stream));
   else
-    st = symmetric ? launch_kt<4, true>(a, p, stream) : launch_kt<4, false>(a, p, stream);
+    st = symmetric ? (nt ? launch_kt<4, true, true>(a, p, stream) : launch_kt<4, true, false>(a, p, stream))
+                   : (nt ? launch_kt<4, false, true>(a, p, stream) : launch_kt<4, false, false>(a, p, stream));
   if (st) return st;
   W4_CHECK_LAUNCH();
   if (p.splits > 1) {

@@ -53,7 +53,7 @@ struct GemvArgs {
 // The packed words are read once per launch, each wave load covering whole cache
 // lines, so they take the non-temporal hint (measured: decode sweep 3.96 -> 3.69 us
 // per launch at M = 1, 4.82 -> 4.41 at M = 2; cold 27B shapes at M = 1 11.5 -> 10.9
-// and 11.8 -> 11.2 us).
+// and 11.8 -> 11.2 us); so do the scales (sweep 3.68 -> 3.59 us, cold unchanged).
 template <int WPL>
 __device__ __forceinline__ void load_words(__amdgpu_buffer_rsrc_t r, uint32_t off, uint32_t* w) {
   static_assert(WPL == 4, "one 16-byte load of four packed words per lane and row");
@@ -161,7 +161,7 @@ __global__ __launch_bounds__(gemv_max_waves(M) * 64) void gemv_kernel(GemvArgs a
     for (int r = 0; r < R; ++r) {
       const uint32_t row = (uint32_t)min(n_first + i * R + r, a.N);
       load_words<WPL>(rw, row * wrow + kw, B.w[r]);
-      B.sc[r] = __builtin_amdgcn_raw_buffer_load_b16(rs, row * srow + ks, 0, 0);
+      B.sc[r] = __builtin_amdgcn_raw_buffer_load_b16(rs, row * srow + ks, 0, kLoadNt);
       if constexpr (!SYM) B.z[r] = __builtin_amdgcn_raw_buffer_load_b32(rz, row * zrow + kz, 0, 0);
     }
   };

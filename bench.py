@@ -19,7 +19,9 @@ line carries:
     the 8 TB/s HBM peak, with the latency floor: t0, the per-launch time of an
     empty kernel replayed as a graph of as many launches, and the step's
     latency-adjusted ceiling
-    sum(bytes / BW) / sum(t0 + bytes / BW), which no kernel of the sweep can beat;
+    sum(bytes / BW) / sum(t0 + bytes / BW), which no kernel of the sweep can beat,
+    and the plain-read yardstick: the best of 40 settings of a streaming-read probe
+    replayed as a graph with the step's launch sizes and order, over the same bytes;
   * ``rows``: every other step of the path measured in the same run (cold-cache
     GEMV on the 27B-shaped linears, decode sweeps at M = 4 and 16, prefill GEMM
     at M = 2048 and the 27B shapes, quantize + pack, the full 30-candidate AWQ
@@ -306,6 +308,36 @@ def stream_read_sweep(torch, w4, nbytes, reps, min_bytes=640 << 20):
     del buf, sink
     torch.cuda.empty_cache()
     return best[0], best[1], table
+
+
+def plain_read_step(torch, w4, sizes, reps=10):
+    """Yardstick for the decode step: one graph of plain streaming reads with the step's
+    launch sizes in its order, each over a buffer of its own (nothing cached from the previous
+    replay once the step exceeds the Infinity Cache), for every probe unroll depth, load kind and
+    grid size; returns (best ms per step, its settings)."""
+    sizes = [(n + 255) // 256 * 256 for n in sizes]
+    offs = [0]
+    for n in sizes:
+        offs.append(offs[-1] + n)
+    buf = torch.empty(offs[-1] // 4, dtype=torch.int32, device="cuda")
+    buf.fill_(1)
+    sink = torch.empty(4096 * 256, dtype=torch.int32, device="cuda")
+    best = None
+    for unroll in (1, 2, 4, 8):
+        for nt in (False, True):
+            for blocks in (256, 512, 1024, 2048, 4096):
+                ls = [Launch(lambda sl=buf[offs[i] // 4:offs[i + 1] // 4], u=unroll, n=nt, b=blocks:
+                             w4.probe_stream_read(sl, unroll=u, nontemporal=n, blocks=b, sink=sink), sizes[i], 0)
+                      for i in range(len(sizes))]
+                g = capture_graph(torch, ls)
+                g.replay()
+                ms = min(time_events(torch, g.replay, reps) for _ in range(2))
+                del g, ls
+                if best is None or ms < best[0]:
+                    best = (ms, {"unroll": unroll, "nontemporal": nt, "blocks": blocks})
+    del buf, sink
+    torch.cuda.empty_cache()
+    return best
 
 
 def rows_large(torch, w4, wl, reps):
@@ -771,6 +803,12 @@ def main(argv=None):
         out["roofline"]["latency_floor"] = {"t0_us": round(t0, 3), "ceiling_frac": round(ceil_frac, 4),
                                             "frac_of_ceiling": round(achieved / HBM_PEAK_GBS / ceil_frac, 4)}
         log(f"latency floor: t0 {t0:.2f} us per launch, step ceiling {ceil_frac:.3f} of HBM peak")
+        read_ms, read_cfg = plain_read_step(torch, w4, [l.nbytes for l in sweep])
+        out["roofline"]["plain_read_step"] = {
+            "us_per_launch": round(read_ms * 1e3 / len(sweep), 3), "settings": read_cfg,
+            "frac": round(step_bytes / (read_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "gemv_of_read": round(read_ms / ms_step, 4)}
+        log(f"plain read of the step's bytes in the same launches: {read_ms * 1e3:.1f} us per step")
         del graph, sweep
         torch.cuda.synchronize()
         torch.cuda.empty_cache()

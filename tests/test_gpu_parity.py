@@ -363,6 +363,21 @@ def test_gemm_core_layout_boundary(M, N):
     assert _elementwise_ok(y, ref) == 0
 
 
+@pytest.mark.parametrize("M,N", [(1024, 4096), (1025, 4096), (1024, 3968), (2048, 6144)])
+def test_gemm_row_tail_and_rounds(M, N):
+    """The MFMA core at 512 tiles of 64 x 128 (one round of two workgroups per CU,
+    three stages), 544 with a one-row tail (two stages), 496 (three stages, a short
+    round) and the prefill width (1536 tiles, two stages); K = 640 (five groups:
+    every stage of the ring and an odd count).  Oracle on every 8th row and the
+    last one."""
+    X, W = wl.small_case(M, 640, N, 57)
+    rows = np.unique(np.concatenate([np.arange(0, M, 8), [M - 1]]))
+    say("gemm tall boundary", M, N)
+    y, ref = _gemm_case(X, W, False, rows)
+    _fro_ok(y, ref)
+    assert _elementwise_ok(y, ref) == 0
+
+
 def test_gemm_one_hot_and_zero():
     _, W = wl.small_case(1, 384, 160, 9)
     qw, sc, qz = _packed(W, False)

@@ -310,11 +310,11 @@ def stream_read_sweep(torch, w4, nbytes, reps, min_bytes=640 << 20):
     return best[0], best[1], table
 
 
-def plain_read_step(torch, w4, sizes, reps=10):
+def plain_read_step(torch, w4, sizes, reps=10, settings=None):
     """Yardstick for the decode step: one graph of plain streaming reads with the step's
     launch sizes in its order, each over a buffer of its own (nothing cached from the previous
     replay once the step exceeds the Infinity Cache), for every probe unroll depth, load kind and
-    grid size; returns (best ms per step, its settings)."""
+    grid size (or only the given settings); returns (best ms per step, its settings)."""
     sizes = [(n + 255) // 256 * 256 for n in sizes]
     offs = [0]
     for n in sizes:
@@ -323,18 +323,20 @@ def plain_read_step(torch, w4, sizes, reps=10):
     buf.fill_(1)
     sink = torch.empty(4096 * 256, dtype=torch.int32, device="cuda")
     best = None
-    for unroll in (1, 2, 4, 8):
-        for nt in (False, True):
-            for blocks in (256, 512, 1024, 2048, 4096):
-                ls = [Launch(lambda sl=buf[offs[i] // 4:offs[i + 1] // 4], u=unroll, n=nt, b=blocks:
-                             w4.probe_stream_read(sl, unroll=u, nontemporal=n, blocks=b, sink=sink), sizes[i], 0)
-                      for i in range(len(sizes))]
-                g = capture_graph(torch, ls)
-                g.replay()
-                ms = min(time_events(torch, g.replay, reps) for _ in range(2))
-                del g, ls
-                if best is None or ms < best[0]:
-                    best = (ms, {"unroll": unroll, "nontemporal": nt, "blocks": blocks})
+    if settings is None:
+        settings = [{"unroll": u, "nontemporal": nt, "blocks": b}
+                    for u in (1, 2, 4, 8) for nt in (False, True) for b in (256, 512, 1024, 2048, 4096)]
+    for cfg in settings:
+        ls = [Launch(lambda sl=buf[offs[i] // 4:offs[i + 1] // 4], u=cfg["unroll"], n=cfg["nontemporal"],
+                     b=cfg["blocks"]: w4.probe_stream_read(sl, unroll=u, nontemporal=n, blocks=b, sink=sink),
+                     sizes[i], 0)
+              for i in range(len(sizes))]
+        g = capture_graph(torch, ls)
+        g.replay()
+        ms = min(time_events(torch, g.replay, reps) for _ in range(2))
+        del g, ls
+        if best is None or ms < best[0]:
+            best = (ms, dict(cfg))
     del buf, sink
     torch.cuda.empty_cache()
     return best
@@ -758,6 +760,7 @@ def main(argv=None):
     }
     packed = []
     t0 = None                       # latency floor per launch (us), measured with the step
+    read_cfg = None                 # best plain-read setting for the step's launches
     if not args.skip_step:
         log("packing decode-sweep weights")
         packed = pack_sweep(torch, w4, wl, args.blocks)
@@ -850,8 +853,13 @@ def main(argv=None):
             sw = fused_sweep_launches(torch, w4, wl, packed, M)
             g = capture_graph(torch, sw)
             ms = time_events(torch, g.replay, max(3, args.steps // 2))
+            extra = {"launches": len(sw)}
+            if read_cfg is not None:
+                # the same bytes read plainly in the same launches (the step's best setting)
+                rms, _ = plain_read_step(torch, w4, [l.nbytes for l in sw], settings=[read_cfg])
+                extra.update({"plain_read_us": round(rms * 1e3, 1), "of_plain_read": round(rms / ms, 4)})
             rows.append(row_gemv(f"decode sweep M={M}, shared-input linears fused (graph)",
-                                 sum(l.nbytes for l in sw), ms, {"launches": len(sw)}))
+                                 sum(l.nbytes for l in sw), ms, extra))
             del g, sw
             torch.cuda.empty_cache()
         del packed

@@ -508,17 +508,20 @@ def rows_lookahead(torch, w4, wl, reps):
     torch.cuda.synchronize()
     ms = (time.perf_counter() - t0) * 1e3 / n
     # a gate candidate reruns the feed-forward half of the scored block (the attention
-    # half is the reference's) and the whole next block
-    f_cand = 2 * T * 3 * H * I + f_blk
+    # half is the reference's) and the whole next block; of the feed-forward half only
+    # gate and down change with the candidate (the up projection runs once per call)
+    f_cand = 2 * T * 2 * H * I + f_blk
+    f_up = 2 * T * H * I
     rows.append(row_gemm(f"look-ahead losses, gate, {C} candidates (feed-forward half + next block each) + reference",
-                         C * f_cand + 2 * f_blk, ms, {"ms_per_candidate_with_reference_share": round(ms / C, 3)}))
+                         C * f_cand + 2 * f_blk + f_up, ms, {"ms_per_candidate_with_reference_share": round(ms / C, 3)}))
     res = w4.awq_search_lookahead(X, B, L, blk, nxt, n_q, n_kv, "gate", [i / 20 for i in range(20)],
                                   [1 - j / 20 for j in range(10)])
     t0 = time.perf_counter()
     res = w4.awq_search_lookahead(X, B, L, blk, nxt, n_q, n_kv, "gate", [i / 20 for i in range(20)],
                                   [1 - j / 20 for j in range(10)])
     ms = (time.perf_counter() - t0) * 1e3
-    rows.append(row_gemm("look-ahead two-phase search, gate (20 alpha + 10 ratio + reference)", 30 * f_cand + 2 * f_blk, ms,
+    rows.append(row_gemm("look-ahead two-phase search, gate (20 alpha + 10 ratio + reference)",
+                         30 * f_cand + 2 * f_blk + 2 * f_up, ms,
                          {"alpha_index": res["alpha_index"], "ratio_index": res["ratio_index"]}))
     return rows
 

@@ -530,6 +530,7 @@ Dims make_dims(int B, int L, int H, int nq, int nkv, int I) {
 struct LookLayout {
   BlockLayout blk;
   size_t yref_i, yref_n, yc_i, yc_n, oref, href, xs, qw, sc, qz, gemm, part, total;
+  size_t b2ref, ffix;   // feed-forward candidates: the normalized residual and the operand no candidate changes
   size_t nparts;
 };
 
@@ -558,6 +559,8 @@ LookLayout look_layout(const Dims& d, int linear) {
   l.gemm = take(gemm_workspace_bytes(d.T, K, N));
   l.nparts = (T * d.H + 2047) / 2048;
   l.part = take(l.nparts * 8);
+  l.b2ref = take(linear >= 4 ? T * d.H * 2 : 0);
+  l.ffix = take(linear >= 4 ? T * d.I * 2 : 0);
   l.total = off;
   return l;
 }
@@ -651,6 +654,31 @@ int launch_lookahead_reference(const uint16_t* X, int B, int L, int H, int nq, i
   return W4_OK;
 }
 
+// The feed-forward half of the block for a candidate of gate, up or down, from the
+// reference post-attention residual h: what run_block does from its third stage,
+// with the normalized residual b2 = rmsnorm(h) and the operand the candidate does not
+// change (up for a gate candidate, gate for an up candidate, silu(gate) up for a
+// down candidate) taken as computed once for all candidates.
+int run_ffn_candidate(const Dims& d, const w4_block& blk, const uint16_t* h, const uint16_t* b2,
+                      const uint16_t* fixed, const Candidate& cand, uint16_t* Y, char* ws, const BlockLayout& l,
+                      hipStream_t st) {
+  auto buf = [&](size_t off) { return reinterpret_cast<uint16_t*>(ws + off); };
+  const size_t T = (size_t)d.T;
+  int rc;
+  if (cand.linear == 6) {
+    if ((rc = run_linear(d, 6, fixed, blk.wdown, &cand, buf(l.dn), st))) return rc;
+    return ew_launch(EW_ADD, h, buf(l.dn), T * d.H, Y, st);
+  }
+  if (cand.linear == 4) {
+    if ((rc = run_linear(d, 4, b2, blk.wgate, &cand, buf(l.gt), st))) return rc;
+    if ((rc = ew_launch(EW_SILU_MUL, buf(l.gt), fixed, T * d.I, buf(l.m), st))) return rc;
+  } else {
+    if ((rc = run_linear(d, 5, b2, blk.wup, &cand, buf(l.up), st))) return rc;
+    if ((rc = ew_launch(EW_SILU_MUL, fixed, buf(l.up), T * d.I, buf(l.m), st))) return rc;
+  }
+  return launch_bf16_gemm_multi(buf(l.m), d.T, d.I, 1, &blk.wdown, &d.H, &Y, st, &h);
+}
+
 // Candidates against the reference outputs left in the workspace by
 // launch_lookahead_reference (same shape, blocks and linear).
 int launch_lookahead_candidates(const uint16_t* X, int B, int L, int H, int nq, int nkv, int I, const w4_block& blk,
@@ -669,6 +697,21 @@ int launch_lookahead_candidates(const uint16_t* X, int B, int L, int H, int nq, 
   const size_t n = (size_t)d.T * d.H;
   const unsigned pblocks = (unsigned)l.nparts;
   int rc;
+  // the block runs from the first op the candidate changes: o from the reference
+  // attention output, gate / up / down from the reference post-attention residual
+  const int stage = linear <= 2 ? 0 : linear == 3 ? 1 : 2;
+  if (stage == 2) {
+    // what no feed-forward candidate changes, once: rmsnorm of the residual, then up
+    // (gate candidates), gate (up candidates) or silu(gate) up (down candidates)
+    hipLaunchKernelGGL(rmsnorm_kernel, dim3((unsigned)((d.T + 3) / 4)), dim3(256), 0, stream, buf(l.href), d.T, d.H,
+                       blk.norm2, buf(l.b2ref));
+    W4_CHECK_LAUNCH();
+    if (linear == 4 && (rc = bf16_linear(buf(l.b2ref), d.T, d.H, d.I, blk.wup, buf(l.ffix), stream))) return rc;
+    if (linear == 5 && (rc = bf16_linear(buf(l.b2ref), d.T, d.H, d.I, blk.wgate, buf(l.ffix), stream))) return rc;
+    if (linear == 6 &&
+        (rc = launch_bf16_glu(buf(l.b2ref), d.T, d.H, d.I, blk.wgate, blk.wup, buf(l.ffix), stream)))
+      return rc;
+  }
   for (int c = 0; c < C; ++c) {
     QuantArgs q{};
     q.W = Wl[linear];
@@ -682,11 +725,11 @@ int launch_lookahead_candidates(const uint16_t* X, int B, int L, int H, int nq, 
     q.qzeros = symmetric ? nullptr : reinterpret_cast<uint32_t*>(ws + l.qz);
     if ((rc = launch_quantize_pack(q, 1, stream))) return rc;
     Candidate cand{linear, S + (size_t)c * K, q.qweight, q.scales, q.qzeros, symmetric, buf(l.xs), ws + l.gemm};
-    // the block runs from the first op the candidate changes: o from the reference
-    // attention output, gate / up / down from the reference post-attention residual
-    const int stage = linear <= 2 ? 0 : linear == 3 ? 1 : 2;
-    if ((rc = run_block(d, blk, X, buf(l.yc_i), &cand, ws, l.blk, stream, stage, buf(l.oref), buf(l.href))))
-      return rc;
+    if (stage == 2)
+      rc = run_ffn_candidate(d, blk, buf(l.href), buf(l.b2ref), buf(l.ffix), cand, buf(l.yc_i), ws, l.blk, stream);
+    else
+      rc = run_block(d, blk, X, buf(l.yc_i), &cand, ws, l.blk, stream, stage, buf(l.oref), buf(l.href));
+    if (rc) return rc;
     if (next && (rc = run_block(d, *next, buf(l.yc_i), buf(l.yc_n), nullptr, ws, l.blk, stream))) return rc;
     const uint16_t* yc_n = next ? buf(l.yc_n) : buf(l.yc_i);
     hipLaunchKernelGGL(sqdiff_partial_kernel, dim3(pblocks), dim3(256), 0, stream, yc_n, ref_n, n, part);

@@ -631,7 +631,8 @@ int lookahead_input_size(int H, int nq, int I, int linear) {
 // NULL, mean |input| of linear `linear` over the tokens is written to m[0 .. K) (m
 // holds (1 + ceil(T / 64)) K doubles, the rest per-chunk partial sums).
 int launch_lookahead_reference(const uint16_t* X, int B, int L, int H, int nq, int nkv, int I, const w4_block& blk,
-                               const w4_block* next, int linear, double* m, void* workspace, hipStream_t stream) {
+                               const w4_block* next, int linear, double* m, void* workspace, hipStream_t stream,
+                               double* m_host, hipEvent_t m_ready) {
   const Dims d = make_dims(B, L, H, nq, nkv, I);
   const LookLayout l = look_layout(d, linear);
   char* ws = static_cast<char*>(workspace);
@@ -649,6 +650,10 @@ int launch_lookahead_reference(const uint16_t* X, int B, int L, int H, int nq, i
     int K, N;
     linear_shape(d, linear, K, N);
     if ((rc = launch_act_mean_abs(buf(in[linear]), d.T, K, m, stream))) return rc;
+    if (m_host && m_ready &&
+        (hipMemcpyAsync(m_host, m, (size_t)K * 8, hipMemcpyDeviceToHost, stream) != hipSuccess ||
+         hipEventRecord(m_ready, stream) != hipSuccess))
+      return W4_ERR_HIP;
   }
   if (next && (rc = run_block(d, *next, buf(l.yref_i), buf(l.yref_n), nullptr, ws, l.blk, stream))) return rc;
   return W4_OK;

@@ -91,8 +91,11 @@ int launch_lookahead_loss(const uint16_t* X, int B, int L, int H, int nq, int nk
                           const w4_block* next, int linear, const float* S, const float* ratios, int C,
                           int symmetric, float* losses, float* losses_d0, void* workspace, hipStream_t stream);
 int lookahead_input_size(int H, int nq, int I, int linear);
+// With m_host and m_ready set (and m), the statistic is also copied to m_host (K doubles)
+// and m_ready recorded right after it, before the next block is enqueued.
 int launch_lookahead_reference(const uint16_t* X, int B, int L, int H, int nq, int nkv, int I, const w4_block& blk,
-                               const w4_block* next, int linear, double* m, void* workspace, hipStream_t stream);
+                               const w4_block* next, int linear, double* m, void* workspace, hipStream_t stream,
+                               double* m_host = nullptr, hipEvent_t m_ready = nullptr);
 int launch_lookahead_candidates(const uint16_t* X, int B, int L, int H, int nq, int nkv, int I, const w4_block& blk,
                                 const w4_block* next, int linear, const float* S, const float* ratios, int C,
                                 int symmetric, float* losses, float* losses_d0, void* workspace,

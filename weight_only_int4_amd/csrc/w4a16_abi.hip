@@ -336,6 +336,17 @@ void alpha_scales(const std::vector<double>& m, const double* alphas, int n_alph
   }
 }
 
+// An event recorded on a stream, destroyed with its scope.
+struct ScopedEvent {
+  hipEvent_t ev = nullptr;
+  ScopedEvent() {
+    if (hipEventCreateWithFlags(&ev, hipEventDisableTiming) != hipSuccess) ev = nullptr;
+  }
+  ~ScopedEvent() {
+    if (ev) (void)hipEventDestroy(ev);
+  }
+};
+
 int first_argmin(const std::vector<float>& v) {
   int best = 0;
   for (int i = 1; i < (int)v.size(); ++i)
@@ -356,12 +367,16 @@ int search_impl(const uint16_t* X, int T, int K, int N, const uint16_t* W, const
 
   int st = launch_act_mean_abs(X, T, K, dm, stream);
   if (st) return st;
-  // Y_ref = bf16(X W^T) once for both phases, through the bf16-weight MFMA path
+  std::vector<double> m(K);
+  ScopedEvent m_ready;
+  if (!m_ready.ev || hipMemcpyAsync(m.data(), dm, (size_t)K * 8, hipMemcpyDeviceToHost, stream) != hipSuccess ||
+      hipEventRecord(m_ready.ev, stream) != hipSuccess)
+    return W4_ERR_HIP;
+  // Y_ref = bf16(X W^T) once for both phases, through the bf16-weight MFMA path; it
+  // runs while the host computes s(alpha) from the statistic
   st = launch_reference_gemm(X, T, K, N, W, yref, stream);
   if (st) return st;
-  std::vector<double> m(K);
-  if (hipMemcpyAsync(m.data(), dm, (size_t)K * 8, hipMemcpyDeviceToHost, stream) != hipSuccess) return W4_ERR_HIP;
-  if (hipStreamSynchronize(stream) != hipSuccess) return W4_ERR_HIP;
+  if (hipEventSynchronize(m_ready.ev) != hipSuccess) return W4_ERR_HIP;
 
   std::vector<float> S((size_t)C * K), R(C, 1.0f);
   alpha_scales(m, alphas, n_alpha, S);
@@ -465,12 +480,15 @@ int look_search_impl(const uint16_t* X, int B, int L, int H, int nq, int nkv, in
   float* dR = reinterpret_cast<float*>(ws + l.R);
   float* dL = reinterpret_cast<float*>(ws + l.L);
   double* dm = reinterpret_cast<double*>(ws + l.m);
-  int st = launch_lookahead_reference(X, B, L, H, nq, nkv, I, blk, next, linear, dm, lw, stream);
-  if (st) return st;
+  // the statistic reaches the host right after block i; the host computes s(alpha)
+  // while block i + 1 of the reference runs
   std::vector<double> m(K);
-  if (hipMemcpyAsync(m.data(), dm, (size_t)K * 8, hipMemcpyDeviceToHost, stream) != hipSuccess ||
-      hipStreamSynchronize(stream) != hipSuccess)
-    return W4_ERR_HIP;
+  ScopedEvent m_ready;
+  if (!m_ready.ev) return W4_ERR_HIP;
+  int st = launch_lookahead_reference(X, B, L, H, nq, nkv, I, blk, next, linear, dm, lw, stream, m.data(),
+                                      m_ready.ev);
+  if (st) return st;
+  if (hipEventSynchronize(m_ready.ev) != hipSuccess) return W4_ERR_HIP;
   std::vector<float> S((size_t)C * K), R(C, 1.0f);
   alpha_scales(m, alphas, n_alpha, S);
   if (hipMemcpyAsync(dS, S.data(), (size_t)n_alpha * K * 4, hipMemcpyHostToDevice, stream) != hipSuccess ||

@@ -5,6 +5,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <thread>
 #include <vector>
 
 #include "internal.hpp"
@@ -322,18 +323,34 @@ SearchLayout search_layout(int T, int K, int N, int C) {
 // stored fp32: row i of S for alphas[i].
 void alpha_scales(const std::vector<double>& m, const double* alphas, int n_alpha, std::vector<float>& S) {
   const int K = (int)m.size();
-  std::vector<double> p(K);
-  for (int i = 0; i < n_alpha; ++i) {
-    double pmax = 0.0, pmin = INFINITY;
-    for (int k = 0; k < K; ++k) {
-      const double v = pow(m[k], alphas[i]);
-      p[k] = v > 1e-4 ? v : 1e-4;
-      pmax = p[k] > pmax ? p[k] : pmax;
-      pmin = p[k] < pmin ? p[k] : pmin;
+  // row i of S from alpha i alone: the rows are independent, so host threads take
+  // interleaved rows (same arithmetic per row, whichever thread computes it)
+  auto rows = [&](int first, int step) {
+    std::vector<double> p(K);
+    for (int i = first; i < n_alpha; i += step) {
+      double pmax = 0.0, pmin = INFINITY;
+      for (int k = 0; k < K; ++k) {
+        const double v = pow(m[k], alphas[i]);
+        p[k] = v > 1e-4 ? v : 1e-4;
+        pmax = p[k] > pmax ? p[k] : pmax;
+        pmin = p[k] < pmin ? p[k] : pmin;
+      }
+      const double d = sqrt(pmax * pmin);
+      for (int k = 0; k < K; ++k) S[(size_t)i * K + k] = (float)(p[k] / d);
     }
-    const double d = sqrt(pmax * pmin);
-    for (int k = 0; k < K; ++k) S[(size_t)i * K + k] = (float)(p[k] / d);
+  };
+  const unsigned hw = std::thread::hardware_concurrency();
+  const int nt = std::max(1, std::min({n_alpha, 8, (int)(hw > 1 ? hw / 2 : 1)}));
+  std::vector<std::thread> pool;
+  int started = 1;                     // threads running (this one included)
+  try {
+    for (; started < nt; ++started) pool.emplace_back(rows, started, nt);
+  } catch (...) {
+    // a thread that could not start leaves its rows to this one
   }
+  rows(0, nt);
+  for (int t = started; t < nt; ++t) rows(t, nt);
+  for (auto& th : pool) th.join();
 }
 
 // An event recorded on a stream, destroyed with its scope.

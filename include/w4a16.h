@@ -196,18 +196,24 @@ int w4a8_gemv(const int8_t* Xq, const float* sx, const int32_t* xsum, int M, int
               int group_size, uint16_t* Y, void* workspace, size_t* workspace_bytes, void* stream);
 
 /*
- * w4a16_gemm -- prefill contraction Y = X W_hat^T for any M >= 1 (intended for
- * M >= 64), on MFMA bf16 matrix cores with LDS-staged activation tiles.
- * [QSRT card] "Reproducible runtime": W4A16 serves prefill row counts.
- * Same operands and rounding as w4a16_gemv.
- *   workspace (always needed, > 0 bytes): X with every 8-channel run reordered
- *   for the packed-word expansion, the negated group row sums of X (each as
- *   three exact bf16 parts) and, per group and column, the scale with
- *   bf16(128 + z); when the output tiles are too few to fill the chip (small M
- *   and N), the groups are split among several workgroups per tile and the
- *   workspace also holds their fp32 partial outputs (splits x M x N x 4 bytes,
- *   added in split order by a second kernel).  Size query as in w4a16_gemv.  The
- *   size depends only on (M, K, N); about 2 M K bytes plus the partials.
+ * w4a16_gemm -- prefill contraction Y = X W_hat^T for any M >= 1, on MFMA bf16
+ * matrix cores.  [QSRT card] "Reproducible runtime": W4A16 serves prefill row
+ * counts.  Same operands and rounding as w4a16_gemv.  Two forms, chosen by shape:
+ *   - M <= 48 (with N K / 2 < 2^31 and 2 M K < 2^31): one pass over the packed
+ *     weights, each wave holding all M activation rows of one group in
+ *     registers; no workspace when K <= 2048 (16 groups, one workgroup's waves),
+ *     else the groups are split into ranges of at most 16 whose fp32 partial
+ *     outputs (splits x M x N x 4 bytes) a second kernel adds in split order.
+ *   - larger M: tiles of 64 x 128 outputs with LDS-staged activations; the
+ *     workspace (always > 0 bytes) holds X with every 8-channel run reordered
+ *     for the packed-word expansion, the negated group row sums of X (each as
+ *     three exact bf16 parts) and, per group and column, the scale with
+ *     bf16(128 + z); when the output tiles are too few to fill the chip, the
+ *     groups are split among several workgroups per tile and the workspace also
+ *     holds their fp32 partial outputs (splits x M x N x 4 bytes, added in split
+ *     order by a second kernel); about 2 M K bytes plus the partials.
+ *   Size query as in w4a16_gemv (when the size is 0, pass workspace == NULL and
+ *   workspace_bytes == NULL).  The size depends only on (M, K, N).
  *   W4_ERR_SHAPE (from the size query too) when (M + 64) K >= 2^31 or
  *   N K >= 2^33 (32-bit byte offsets into the arranged activations and the
  *   packed weights).

@@ -203,6 +203,28 @@ def test_gemm_size_query(lib):
     assert f(None, 64, K, 1 << 22, None, None, None, 0, 128, None, None, ctypes.byref(sz), None) == -2
 
 
+def test_gemm_short_m_workspace(lib):
+    """Row counts up to 48 take the one-pass form: no workspace while K fits one
+    workgroup's 16 waves (one group each), else fp32 partials for the group
+    ranges only; 49 rows and more take the tiled core and its workspace."""
+    sz = ctypes.c_size_t(7)
+    f = lib.w4a16_gemm
+    for M, K in ((1, 2048), (48, 2048), (17, 128)):
+        assert f(None, M, K, 300, None, None, None, 0, 128, None, None, ctypes.byref(sz), None) == 0
+        assert sz.value == 0, (M, K)
+    # 40 groups: 3 ranges; 136 groups: 9 ranges; 17 groups: 2 ranges
+    for M, K, N, splits in ((48, 5120, 17408, 3), (33, 17408, 5120, 9), (16, 2176, 96, 2)):
+        assert f(None, M, K, N, None, None, None, 1, 128, None, None, ctypes.byref(sz), None) == 0
+        assert sz.value == splits * M * N * 4, (M, K, N)
+    # 49 rows: the core's arranged activations (rows rounded to 64), row sums, column
+    # words and, with 3 column tiles, the fp32 partials of a 4-way K split (M N
+    # rounded up to 64 elements)
+    assert f(None, 49, 2048, 300, None, None, None, 1, 128, None, None, ctypes.byref(sz), None) == 0
+    assert sz.value == 64 * 2048 * 2 + 16 * 64 * 8 + 16 * 384 * 4 + 4 * 14720 * 4
+    # a zero-byte workspace is not required; a nonzero one is
+    assert f(A, 48, 5120, 17408, A, A, None, 1, 128, A, None, None, None) == -5
+
+
 def test_grid_loss_validation(lib):
     sz = ctypes.c_size_t(0)
     f = lib.awq_grid_loss

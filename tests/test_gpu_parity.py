@@ -401,8 +401,40 @@ def test_gemm_prefill_full_size(shape):
     assert _elementwise_ok(y, ref) == 0
 
 
+@pytest.mark.parametrize("M,K,N,sym", [(1, 128, 1, False), (5, 384, 70, True), (16, 4096, 64, False),
+                                       (17, 2048, 300, False), (31, 640, 129, True), (33, 17408, 40, False),
+                                       (48, 2176, 257, True), (40, 33792, 24, True), (48, 128, 16, False),
+                                       (47, 2304, 1000, False), (48, 2048, 17, True), (49, 2048, 130, False)])
+def test_gemm_short_m(M, K, N, sym):
+    """The one-pass form for up to 48 rows: one to three row blocks with a ragged
+    row tail, ragged column tails, a single group, K within one workgroup's 16
+    groups (no split), K splits with a short last range (17 groups: 16 + 1; 18: 16 +
+    2; 264: 17 ranges), and 49 rows on the tiled core beside it."""
+    say("gemm short M", M, K, N, sym)
+    X, W = wl.small_case(M, K, N, 77)
+    y, ref = _gemm_case(X, W, sym)
+    _fro_ok(y, ref)
+    assert _elementwise_ok(y, ref) == 0
+
+
+@pytest.mark.parametrize("M,K,N", [(48, 4096, 300), (20, 2048, 33)])
+def test_gemm_short_m_deterministic_and_overwrites(M, K, N):
+    """Y prefilled with NaN is fully overwritten and two calls agree bit for bit,
+    through the split reduction (32 groups: 2 ranges) and without a split."""
+    X, W = wl.small_case(M, K, N, 5)
+    qw, sc, qz = _packed(W, False)
+    args = (to_bf16(X), to_i32(qw), to_bf16(sc), to_i32(qz), False)
+    say("gemm short M determinism", M, K, N)
+    Y1 = torch.full((M, N), float("nan"), dtype=torch.bfloat16, device="cuda")
+    w4.w4a16_gemm(*args, Y=Y1)
+    Y2 = w4.w4a16_gemm(*args)
+    torch.cuda.synchronize()
+    assert not torch.isnan(Y1.float()).any()
+    assert np.array_equal(bits16(Y1), bits16(Y2))
+
+
 @pytest.mark.parametrize("shape", [0, 1])
-@pytest.mark.parametrize("M", [64, 512])
+@pytest.mark.parametrize("M", [48, 64, 512])
 def test_gemm_large_full_size(shape, M):
     W = wl.large_weight(shape)
     X = wl.large_act(shape, M)

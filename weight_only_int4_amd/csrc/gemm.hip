@@ -207,6 +207,7 @@ __global__ __launch_bounds__(256) void gemm_split_reduce_kernel(const float* ypa
 // szq [G][npad] u32, and with a K split the fp32 partial outputs [splits][M][N]
 size_t gemm_workspace_bytes(int M, int K, int N) {
   if (M <= 0 || K <= 0 || N <= 0) return 0;
+  if (gemm_use_skinny(M, K, N)) return gemm_skinny_workspace_bytes(M, K, N);
   const size_t mpad = align_up((size_t)M, kBM);
   const size_t G = (size_t)(K / kGroup);
   const int splits = gemm_k_splits(M, K, N);
@@ -226,6 +227,8 @@ int launch_gemm(const uint16_t* X, int M, int K, int N, const uint32_t* qweight,
                 void* workspace, hipStream_t stream) {
   if (M == 0 || N == 0) return W4_OK;
   if (int st = gemm_check_size(M, K, N)) return st;
+  if (gemm_use_skinny(M, K, N))
+    return launch_gemm_skinny(X, M, K, N, qweight, scales, qzeros, symmetric, Y, workspace, stream);
   const int mpad = (int)align_up((size_t)M, kBM);
   const int G = K / kGroup;
   const int splits = gemm_k_splits(M, K, N);

@@ -56,6 +56,14 @@ int launch_w4a8_gemv(const int8_t* Xq, const float* sx, const int32_t* xsum, int
 size_t w4a8_workspace_bytes(int M, int K, int N);   // fp32 partials of a K split (0 without one)
 
 // ---------------------------------------------------------------- GEMM (MFMA)
+// Row counts up to kSkinnyMaxM take the one-pass kernel of gemm_skinny.hip (when its
+// 32-bit buffer offsets cover the shape); larger ones the tiled core.
+constexpr int kSkinnyMaxM = 48;
+bool gemm_use_skinny(int M, int K, int N);
+size_t gemm_skinny_workspace_bytes(int M, int K, int N);
+int launch_gemm_skinny(const uint16_t* X, int M, int K, int N, const uint32_t* qweight,
+                       const uint16_t* scales, const uint32_t* qzeros, int symmetric, uint16_t* Y,
+                       void* workspace, hipStream_t stream);
 size_t gemm_workspace_bytes(int M, int K, int N);
 int launch_gemm(const uint16_t* X, int M, int K, int N, const uint32_t* qweight,
                 const uint16_t* scales, const uint32_t* qzeros, int symmetric, uint16_t* Y,

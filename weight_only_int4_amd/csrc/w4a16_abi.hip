@@ -137,12 +137,11 @@ int w4a16_gemm(const uint16_t* X, int M, int K, int N, const uint32_t* qweight, 
   if (M < 0) return W4_ERR_SHAPE;
   if ((st = gemm_check_size(M, K, N))) return st;
   const size_t need = gemm_workspace_bytes(M, K, N);
-  if (!workspace) {
-    if (!workspace_bytes) return need ? W4_ERR_WORKSPACE : W4_OK;
+  if (!workspace && workspace_bytes) {
     *workspace_bytes = need;
     return W4_OK;
   }
-  if (!workspace_bytes || *workspace_bytes < need) return W4_ERR_WORKSPACE;
+  if (need > 0 && (!workspace || !workspace_bytes || *workspace_bytes < need)) return W4_ERR_WORKSPACE;
   if (!X || !Y) return W4_ERR_NULL;
   st = check_packed(qweight, scales, qzeros, symmetric);
   if (st) return st;

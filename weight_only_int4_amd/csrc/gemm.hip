@@ -175,32 +175,6 @@ int gemm_k_splits(int M, int K, int N) {
   return (G + gps - 1) / gps;          // every split non-empty
 }
 
-// Y[i] = bf16(sum over splits k of ypart[k * stride + i]), fp32 in split order; 4 outputs
-// per thread (stride a multiple of 4).
-__global__ __launch_bounds__(256) void gemm_split_reduce_kernel(const float* ypart, int splits, size_t stride,
-                                                                size_t count, uint16_t* Y) {
-  const size_t i = ((size_t)blockIdx.x * 256 + threadIdx.x) * 4;
-  if (i >= count) return;
-  if (i + 4 <= count) {
-    float4 s = *reinterpret_cast<const float4*>(ypart + i);
-    for (int k = 1; k < splits; ++k) {
-      const float4 v = *reinterpret_cast<const float4*>(ypart + (size_t)k * stride + i);
-      s.x += v.x;
-      s.y += v.y;
-      s.z += v.z;
-      s.w += v.w;
-    }
-    *reinterpret_cast<uint2*>(Y + i) =
-        make_uint2(f32_to_bf16_bits(s.x) | (f32_to_bf16_bits(s.y) << 16), f32_to_bf16_bits(s.z) | (f32_to_bf16_bits(s.w) << 16));
-  } else {
-    for (size_t j = i; j < count; ++j) {
-      float s = ypart[j];
-      for (int k = 1; k < splits; ++k) s += ypart[(size_t)k * stride + j];
-      Y[j] = (uint16_t)f32_to_bf16_bits(s);
-    }
-  }
-}
-
 }  // namespace
 
 // workspace: pair-arranged X [mpad][K] bf16 (rows >= M zero), rsq [G][mpad][4] bf16,
@@ -264,13 +238,7 @@ int launch_gemm(const uint16_t* X, int M, int K, int N, const uint32_t* qweight,
   else
     hipLaunchKernelGGL((gemm_core_kernel<EPI_STORE>), grid, dim3(kGemmWaves * 64), 0, stream, a);
   W4_CHECK_LAUNCH();
-  if (splits > 1) {
-    const size_t count = (size_t)M * N;
-    const size_t blocks = (count + 1023) / 1024;
-    hipLaunchKernelGGL(gemm_split_reduce_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, ypart, splits,
-                       a.ypart_stride, count, Y);
-    W4_CHECK_LAUNCH();
-  }
+  if (splits > 1) return launch_split_reduce(ypart, splits, a.ypart_stride, (size_t)M * N, Y, stream);
   return W4_OK;
 }
 

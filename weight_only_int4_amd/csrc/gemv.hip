@@ -269,14 +269,49 @@ __global__ __launch_bounds__(gemv_max_waves(M) * 64) void gemv_kernel(GemvArgs a
   }
 }
 
-// Y[m][n] = bf16(sum over splits of partial[s][m][n]), splits in order.
-__global__ __launch_bounds__(256) void gemv_split_reduce(const float* partial, int splits, size_t MN,
-                                                         uint16_t* Y) {
-  const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
-  if (i >= MN) return;
-  float s = 0.0f;
-  for (int k = 0; k < splits; ++k) s += partial[(size_t)k * MN + i];
-  Y[i] = (uint16_t)f32_to_bf16_bits(s);
+// Y[i] = bf16(sum over splits k of partial[k * stride + i]) for i < count, fp32 in
+// split order.  Four outputs per thread; the loads of up to eight splits are issued
+// before their adds (a dependent load per split made the kernel one memory round
+// trip per split long).
+constexpr int kReduceBatch = 8;
+__global__ __launch_bounds__(256) void split_reduce_kernel(const float* partial, int splits, size_t stride,
+                                                           size_t count, uint16_t* Y) {
+  const size_t i = ((size_t)blockIdx.x * 256 + threadIdx.x) * 4;
+  if (i >= count) return;
+  if (i + 4 <= count && (stride & 3) == 0) {
+    float4 s = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    for (int k0 = 0; k0 < splits; k0 += kReduceBatch) {
+      float4 v[kReduceBatch];
+#pragma unroll
+      for (int u = 0; u < kReduceBatch; ++u)
+        if (k0 + u < splits) v[u] = *reinterpret_cast<const float4*>(partial + (size_t)(k0 + u) * stride + i);
+#pragma unroll
+      for (int u = 0; u < kReduceBatch; ++u)
+        if (k0 + u < splits) {
+          s.x = k0 + u == 0 ? v[u].x : s.x + v[u].x;
+          s.y = k0 + u == 0 ? v[u].y : s.y + v[u].y;
+          s.z = k0 + u == 0 ? v[u].z : s.z + v[u].z;
+          s.w = k0 + u == 0 ? v[u].w : s.w + v[u].w;
+        }
+    }
+    *reinterpret_cast<uint2*>(Y + i) = make_uint2(f32_to_bf16_bits(s.x) | (f32_to_bf16_bits(s.y) << 16),
+                                                  f32_to_bf16_bits(s.z) | (f32_to_bf16_bits(s.w) << 16));
+  } else {
+    const size_t e = count - i < 4 ? count - i : 4;
+    for (size_t j = 0; j < e; ++j) {
+      float s = 0.0f;
+      for (int k0 = 0; k0 < splits; k0 += kReduceBatch) {
+        float v[kReduceBatch];
+#pragma unroll
+        for (int u = 0; u < kReduceBatch; ++u)
+          if (k0 + u < splits) v[u] = partial[(size_t)(k0 + u) * stride + i + j];
+#pragma unroll
+        for (int u = 0; u < kReduceBatch; ++u)
+          if (k0 + u < splits) s = k0 + u == 0 ? v[u] : s + v[u];
+      }
+      Y[i + j] = (uint16_t)f32_to_bf16_bits(s);
+    }
+  }
 }
 
 namespace {
@@ -457,11 +492,18 @@ int launch_gemv(const uint16_t* X, int M, int K, int N, const uint32_t* qweight,
   return W4_OK;
 }
 
-int launch_gemv_split_reduce(const float* partial, int splits, size_t MN, uint16_t* Y, hipStream_t stream) {
-  hipLaunchKernelGGL(gemv_split_reduce, dim3((unsigned)((MN + 255) / 256)), dim3(256), 0, stream, partial, splits,
-                     MN, Y);
+int launch_split_reduce(const float* partial, int splits, size_t stride, size_t count, uint16_t* Y,
+                        hipStream_t stream) {
+  const size_t blocks = (count + 1023) / 1024;
+  if (blocks > 0x7FFFFFFFu) return W4_ERR_SHAPE;
+  hipLaunchKernelGGL(split_reduce_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, partial, splits, stride, count,
+                     Y);
   W4_CHECK_LAUNCH();
   return W4_OK;
+}
+
+int launch_gemv_split_reduce(const float* partial, int splits, size_t MN, uint16_t* Y, hipStream_t stream) {
+  return launch_split_reduce(partial, splits, MN, MN, Y, stream);
 }
 
 }  // namespace w4

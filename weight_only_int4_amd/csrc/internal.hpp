@@ -43,7 +43,10 @@ size_t gemv_mfma_workspace_bytes(int M, int K, int N);
 int launch_gemv_mfma(const uint16_t* X, int M, int K, int N, const uint32_t* qweight,
                      const uint16_t* scales, const uint32_t* qzeros, int symmetric, uint16_t* Y,
                      void* workspace, hipStream_t stream);
-// Y[i] = bf16(sum over k < splits of partial[k * MN + i]), in split order.
+// Y[i] = bf16(sum over k < splits of partial[k * stride + i]) for i < count, in split order.
+int launch_split_reduce(const float* partial, int splits, size_t stride, size_t count, uint16_t* Y,
+                        hipStream_t stream);
+// The same with stride = count = MN.
 int launch_gemv_split_reduce(const float* partial, int splits, size_t MN, uint16_t* Y, hipStream_t stream);
 
 // ---------------------------------------------------------------- W4A8 decode (M <= 16)

@@ -344,7 +344,7 @@ def plain_read_step(torch, w4, sizes, reps=10, settings=None):
 
 def rows_large(torch, w4, wl, reps):
     rows = []
-    # 27B-shaped symmetric linears: cold-cache GEMV at M = 1, 8 and GEMM at M = 16, 48, 64, 512
+    # 27B-shaped symmetric linears: cold-cache GEMV at M = 1, 8 and GEMM at M = 16, 32, 48, 64, 512
     for si, (K, N) in enumerate(wl.LARGE_SHAPES):
         # yardstick: the best cold plain read of the M = 1 GEMV's bytes
         read_bytes = gemv_bytes(1, K, N, True)
@@ -380,8 +380,8 @@ def rows_large(torch, w4, wl, reps):
             rows.append(row_gemv(f"W4A8 gemv cold M={M} K={K} N={N} sym", nbytes, ms,
                                  {"cache": f"cold ({len(ls)} rotating copies)"}))
             del ls
-        # M = 16, 48: the one-pass form (rows <= 48); M = 64, 512: the tiled core
-        for M in (16, 48, 64, 512):
+        # M = 16: the decode GEMV's kernels; M = 32, 48: the one-pass form; M = 64, 512: the tiled core
+        for M in (16, 32, 48, 64, 512):
             X = to_dev_bf16(torch, wl.large_act(si, M))
             Y = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
             ms = time_events(torch, w4.gemm_launcher(X, qw, sc, None, True, Y), reps)

@@ -199,7 +199,9 @@ int w4a8_gemv(const int8_t* Xq, const float* sx, const int32_t* xsum, int M, int
  * w4a16_gemm -- prefill contraction Y = X W_hat^T for any M >= 1, on MFMA bf16
  * matrix cores.  [QSRT card] "Reproducible runtime": W4A16 serves prefill row
  * counts.  Same operands and rounding as w4a16_gemv.  Two forms, chosen by shape:
- *   - M <= 48 (with N K / 2 < 2^31 and 2 M K < 2^31): one pass over the packed
+ *   - M <= 16: the kernels of w4a16_gemv (its workspace and size limits); measured
+ *     faster than the one-pass form below at every such M.
+ *   - 17 <= M <= 48 (with N K / 2 < 2^31 and 2 M K < 2^31): one pass over the packed
  *     weights, each wave holding all M activation rows of one group in
  *     registers; no workspace when K <= 2048 (16 groups, one workgroup's waves),
  *     else the groups are split into ranges of at most 16 whose fp32 partial

@@ -204,16 +204,23 @@ def test_gemm_size_query(lib):
 
 
 def test_gemm_short_m_workspace(lib):
-    """Row counts up to 48 take the one-pass form: no workspace while K fits one
-    workgroup's 16 waves (one group each), else fp32 partials for the group
-    ranges only; 49 rows and more take the tiled core and its workspace."""
+    """Up to 16 rows the GEMM takes the decode GEMV's kernels and workspace; 17-48
+    rows the one-pass form: no workspace while K fits one workgroup's 16 waves (one
+    group each), else fp32 partials for the group ranges only; 49 rows and more the
+    tiled core and its workspace."""
     sz = ctypes.c_size_t(7)
     f = lib.w4a16_gemm
-    for M, K in ((1, 2048), (48, 2048), (17, 128)):
+    g = lib.w4a16_gemv
+    gz = ctypes.c_size_t(7)
+    for M, K, N in ((1, 2048, 300), (16, 17408, 5120), (8, 33792, 64)):
+        assert f(None, M, K, N, None, None, None, 1, 128, None, None, ctypes.byref(sz), None) == 0
+        assert g(None, M, K, N, None, None, None, 1, 128, None, None, ctypes.byref(gz), None) == 0
+        assert sz.value == gz.value, (M, K, N)
+    for M, K in ((48, 2048), (17, 128)):
         assert f(None, M, K, 300, None, None, None, 0, 128, None, None, ctypes.byref(sz), None) == 0
         assert sz.value == 0, (M, K)
     # 40 groups: 3 ranges; 136 groups: 9 ranges; 17 groups: 2 ranges
-    for M, K, N, splits in ((48, 5120, 17408, 3), (33, 17408, 5120, 9), (16, 2176, 96, 2)):
+    for M, K, N, splits in ((48, 5120, 17408, 3), (33, 17408, 5120, 9), (17, 2176, 96, 2)):
         assert f(None, M, K, N, None, None, None, 1, 128, None, None, ctypes.byref(sz), None) == 0
         assert sz.value == splits * M * N * 4, (M, K, N)
     # 49 rows: the core's arranged activations (rows rounded to 64), row sums, column

@@ -177,10 +177,17 @@ int gemm_k_splits(int M, int K, int N) {
 
 }  // namespace
 
+// Up to 16 rows the decode GEMV's kernels serve the GEMM too: measured on MI355X
+// (graphs of launches over weight copies larger than the Infinity Cache, M = 4, 8,
+// 16 on the decode-block and 27B-shaped linears), they were faster than the
+// one-pass form by up to 3.6 us or equal (K = 2048, N = 12288 at M = 16: 8.6 / 8.5 us).
+bool gemm_use_gemv(int M, int K, int N) { return M <= W4_GEMV_MAX_M && gemv_check_size(M, K, N) == W4_OK; }
+
 // workspace: pair-arranged X [mpad][K] bf16 (rows >= M zero), rsq [G][mpad][4] bf16,
 // szq [G][npad] u32, and with a K split the fp32 partial outputs [splits][M][N]
 size_t gemm_workspace_bytes(int M, int K, int N) {
   if (M <= 0 || K <= 0 || N <= 0) return 0;
+  if (gemm_use_gemv(M, K, N)) return gemv_workspace_bytes(M, K, N);
   if (gemm_use_skinny(M, K, N)) return gemm_skinny_workspace_bytes(M, K, N);
   const size_t mpad = align_up((size_t)M, kBM);
   const size_t G = (size_t)(K / kGroup);
@@ -201,6 +208,7 @@ int launch_gemm(const uint16_t* X, int M, int K, int N, const uint32_t* qweight,
                 void* workspace, hipStream_t stream) {
   if (M == 0 || N == 0) return W4_OK;
   if (int st = gemm_check_size(M, K, N)) return st;
+  if (gemm_use_gemv(M, K, N)) return launch_gemv(X, M, K, N, qweight, scales, qzeros, symmetric, Y, workspace, stream);
   if (gemm_use_skinny(M, K, N))
     return launch_gemm_skinny(X, M, K, N, qweight, scales, qzeros, symmetric, Y, workspace, stream);
   const int mpad = (int)align_up((size_t)M, kBM);

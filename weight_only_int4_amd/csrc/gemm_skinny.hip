@@ -1,4 +1,4 @@
-// Contraction Y = X W_hat^T for short activation blocks (1 <= M <= 48 rows) on the
+// Contraction Y = X W_hat^T for short activation blocks (17 <= M <= 48 rows) on the
 // matrix cores, in one pass over the packed weights and without a prologue.
 //
 // Model card "GLM-5.2-QSRT-Fruit-Instruct", "Reproducible runtime": W4A16 serves
@@ -290,7 +290,7 @@ int launch_rb(const SkinnyArgs& a, const SkinnyPlan& p, hipStream_t stream) {
 }  // namespace
 
 bool gemm_use_skinny(int M, int K, int N) {
-  return M >= 1 && M <= kSkinnyMaxM && (long long)N * K / 2 < (1LL << 31) && 2LL * M * K < (1LL << 31);
+  return M > W4_GEMV_MAX_M && M <= kSkinnyMaxM && (long long)N * K / 2 < (1LL << 31) && 2LL * M * K < (1LL << 31);
 }
 
 size_t gemm_skinny_workspace_bytes(int M, int K, int N) {
@@ -311,8 +311,7 @@ int launch_gemm_skinny(const uint16_t* X, int M, int K, int N, const uint32_t* q
   const int rb = (M + 15) / 16;
   const bool sym = symmetric != 0;
   int st;
-  switch (rb) {
-    case 1: st = sym ? launch_rb<1, true>(a, p, stream) : launch_rb<1, false>(a, p, stream); break;
+  switch (rb) {   // 17 to 48 rows: two or three row blocks
     case 2: st = sym ? launch_rb<2, true>(a, p, stream) : launch_rb<2, false>(a, p, stream); break;
     default: st = sym ? launch_rb<3, true>(a, p, stream) : launch_rb<3, false>(a, p, stream); break;
   }

@@ -59,8 +59,10 @@ int launch_w4a8_gemv(const int8_t* Xq, const float* sx, const int32_t* xsum, int
 size_t w4a8_workspace_bytes(int M, int K, int N);   // fp32 partials of a K split (0 without one)
 
 // ---------------------------------------------------------------- GEMM (MFMA)
-// Row counts up to kSkinnyMaxM take the one-pass kernel of gemm_skinny.hip (when its
-// 32-bit buffer offsets cover the shape); larger ones the tiled core.
+// Which kernels serve w4a16_gemm: up to 16 rows the decode GEMV's (gemm_use_gemv), up
+// to kSkinnyMaxM rows the one-pass kernel of gemm_skinny.hip (when the 32-bit buffer
+// offsets of either cover the shape), else the tiled core.
+bool gemm_use_gemv(int M, int K, int N);
 constexpr int kSkinnyMaxM = 48;
 bool gemm_use_skinny(int M, int K, int N);
 size_t gemm_skinny_workspace_bytes(int M, int K, int N);

@@ -11,7 +11,7 @@
 // Design (CDNA4, wave64, v_mfma_f32_16x16x32_bf16):
 //  * A workgroup is 16 waves.  Wave w owns one 128-channel group g (of its K
 //    split) and holds all M activation rows of that group in registers as MFMA
-//    A operands (RB = ceil(M / 16) row blocks x 4 steps of 32 channels), with the
+//    A operands (RB = ceil(M / 16) = 2 or 3 row blocks x 4 steps of 32 channels), with the
 //    rows' group sums (taken on the matrix cores against a B of bf16 ones).
 //  * The workgroup streams a set of 16-column blocks.  Per block every wave
 //    unpacks its group's 16 x 128 codes once (one packed word per lane and step,
@@ -39,7 +39,7 @@ namespace {
 // Waves per workgroup = groups per K split (four per SIMD, at most 128 registers).
 // Above 48 rows the activation operands and row sums (80 registers) leave too few
 // for the rest, and 12 waves per workgroup measured slower than the tiled core.
-constexpr int sk_waves(int) { return 16; }
+constexpr int kSkWaves = 16;
 constexpr int kSkCols = 16;         // columns per block
 
 struct SkinnyArgs {
@@ -55,8 +55,8 @@ struct SkinnyArgs {
 };
 
 template <int RB, bool SYM>
-__global__ __launch_bounds__(sk_waves(RB) * kWave) void gemm_skinny_kernel(SkinnyArgs a) {
-  constexpr int NW = sk_waves(RB);
+__global__ __launch_bounds__(kSkWaves * kWave) void gemm_skinny_kernel(SkinnyArgs a) {
+  constexpr int NW = kSkWaves;
   // red[slot][wave][rb][i][lane]: element i of lane's tile of row block rb
   extern __shared__ float red[];
   const int lane = threadIdx.x & (kWave - 1);
@@ -250,11 +250,10 @@ int sk_cu_count() {
 // blocks per workgroup: the fewest (rounded up to even) with which one workgroup
 // per CU covers every block of every split, so that all workgroups run in one
 // round.
-SkinnyPlan plan_skinny(int M, int K, int N, int cus) {
+SkinnyPlan plan_skinny(int K, int N, int cus) {
   SkinnyPlan p;
   const int G = K / kGroup;
-  const int nw = sk_waves((M + 15) / 16);
-  p.splits = (G + nw - 1) / nw;
+  p.splits = (G + kSkWaves - 1) / kSkWaves;
   p.gs = (G + p.splits - 1) / p.splits;
   p.splits = (G + p.gs - 1) / p.gs;
   const long long nb = (N + kSkCols - 1) / kSkCols;
@@ -267,7 +266,7 @@ SkinnyPlan plan_skinny(int M, int K, int N, int cus) {
 
 template <int RB, bool SYM>
 int launch_rb(const SkinnyArgs& a, const SkinnyPlan& p, hipStream_t stream) {
-  const size_t lds = 2 * (size_t)sk_waves(RB) * RB * 4 * kWave * sizeof(float);
+  const size_t lds = 2 * (size_t)kSkWaves * RB * 4 * kWave * sizeof(float);
   static std::atomic<int> state[64];       // 0 not yet, 1 done, -1 failed (per device)
   if (lds > 64 * 1024) {
     int dev = 0;
@@ -282,7 +281,7 @@ int launch_rb(const SkinnyArgs& a, const SkinnyPlan& p, hipStream_t stream) {
     }
     if (st != 1) return W4_ERR_HIP;
   }
-  hipLaunchKernelGGL((gemm_skinny_kernel<RB, SYM>), dim3((unsigned)p.gx, (unsigned)p.splits), dim3(sk_waves(RB) * kWave), lds,
+  hipLaunchKernelGGL((gemm_skinny_kernel<RB, SYM>), dim3((unsigned)p.gx, (unsigned)p.splits), dim3(kSkWaves * kWave), lds,
                      stream, a);
   return W4_OK;
 }
@@ -295,7 +294,7 @@ bool gemm_use_skinny(int M, int K, int N) {
 
 size_t gemm_skinny_workspace_bytes(int M, int K, int N) {
   if (M <= 0 || N <= 0 || K <= 0) return 0;
-  const SkinnyPlan p = plan_skinny(M, K, N, 256);
+  const SkinnyPlan p = plan_skinny(K, N, 256);
   return p.splits > 1 ? (size_t)p.splits * M * N * sizeof(float) : 0;
 }
 
@@ -303,9 +302,9 @@ int launch_gemm_skinny(const uint16_t* X, int M, int K, int N, const uint32_t* q
                        const uint32_t* qzeros, int symmetric, uint16_t* Y, void* workspace, hipStream_t stream) {
   if (M == 0 || N == 0) return W4_OK;
   if (!gemm_use_skinny(M, K, N)) return W4_ERR_UNSUPPORTED;
-  // the split count is a function of M and K alone, so the workspace size query
-  // (made without a device) and the launch agree
-  const SkinnyPlan p = plan_skinny(M, K, N, sk_cu_count());
+  // the split count is a function of K alone, so the workspace size query (made
+  // without a device) and the launch agree
+  const SkinnyPlan p = plan_skinny(K, N, sk_cu_count());
   SkinnyArgs a{X, M, K, N, qweight, scales, qzeros, Y, p.splits > 1 ? static_cast<float*>(workspace) : nullptr,
                p.gs, p.nblk};
   const int rb = (M + 15) / 16;

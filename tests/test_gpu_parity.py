@@ -205,7 +205,7 @@ def test_gemv_all_m(M, sym):
                                    (5, 5120, 64), (1, 17408, 33), (9, 8320, 17), (2, 16384, 8), (4, 24576, 5),
                                    (1, 4096, 77), (1, 5120, 65), (1, 8192, 9), (1, 9216, 40), (1, 33792, 12),
                                    (5, 128, 1), (16, 128, 17), (7, 256, 33), (12, 384, 5), (6, 640, 4100),
-                                   (16, 8192, 3), (3, 1024, 4097)])
+                                   (16, 8192, 3), (3, 1024, 4097), (3, 17408, 37)])
 def test_gemv_ragged(M, K, N):
     say("gemv ragged", M, K, N)
     X, W = wl.small_case(M, K, N, 21)
@@ -404,12 +404,14 @@ def test_gemm_prefill_full_size(shape):
 @pytest.mark.parametrize("M,K,N,sym", [(1, 128, 1, False), (5, 384, 70, True), (16, 4096, 64, False),
                                        (17, 2048, 300, False), (31, 640, 129, True), (33, 17408, 40, False),
                                        (48, 2176, 257, True), (40, 33792, 24, True), (48, 128, 16, False),
-                                       (47, 2304, 1000, False), (48, 2048, 17, True), (49, 2048, 130, False)])
+                                       (47, 2304, 1000, False), (48, 2048, 17, True), (49, 2048, 130, False),
+                                       (17, 2304, 33, False)])
 def test_gemm_short_m(M, K, N, sym):
     """The one-pass form for up to 48 rows: one to three row blocks with a ragged
     row tail, ragged column tails, a single group, K within one workgroup's 16
     groups (no split), K splits with a short last range (17 groups: 16 + 1; 18: 16 +
-    2; 264: 17 ranges), and 49 rows on the tiled core beside it."""
+    2; 264: 17 ranges; 17 x 33 outputs, a count the split reduction cannot take
+    four at a time), and 49 rows on the tiled core beside it."""
     say("gemm short M", M, K, N, sym)
     X, W = wl.small_case(M, K, N, 77)
     y, ref = _gemm_case(X, W, sym)

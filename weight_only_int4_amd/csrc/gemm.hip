@@ -33,7 +33,7 @@ __device__ __forceinline__ float row16_sum(float v) {
 }
 
 // One launch, two jobs (grid.z = problem c):
-//  * blocks [0, rs_blocks): one wave per (row m < mpad, chunk of 4096 channels).
+//  * blocks [0, rs_blocks): one wave per (row m < mpad, chunk of CH passes).
 //    Pass i covers channels 512 i .. 512 i + 511: lane l loads 8 consecutive bf16
 //    (16 bytes) at 512 i + 8 l, so the 16 lanes of row r of the wave hold group
 //    4 i + r; each lane sums its 8 values in fp32 (fixed order), the row adds its 16
@@ -44,7 +44,9 @@ __device__ __forceinline__ float row16_sum(float v) {
 //  * the remaining blocks: one thread per (column n < npad, block of 8 groups)
 //    writes szq[g][n] = scale bits | bf16(128 + z) << 16 (0 for n >= N); the 8
 //    zero points of the block are one packed word.
-constexpr int kPrepChunk = 8;                             // passes (4096 channels) per wave
+// Passes (512 channels each) per wave: CH = 8 (4096 channels), or CH = 2 when that
+// would leave fewer than four waves per CU (few rows; see launch_gemm_prep).
+template <int CH>
 __global__ __launch_bounds__(256) void gemm_prep_kernel(const uint16_t* X, size_t x_stride, int M, int K, int mpad,
                                                         const uint16_t* scales, size_t sc_stride,
                                                         const uint32_t* qzeros, size_t qz_stride, int symmetric,
@@ -57,22 +59,22 @@ __global__ __launch_bounds__(256) void gemm_prep_kernel(const uint16_t* X, size_
     if (c >= rs_c) return;                                // problems that share the first one's X
     const int lane = threadIdx.x & 63;
     const int passes = (K + 511) >> 9;
-    const int chunks = (passes + kPrepChunk - 1) / kPrepChunk;
+    const int chunks = (passes + CH - 1) / CH;
     const long long w = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
     const int m = (int)(w / chunks);
     if (m >= mpad) return;                                // uniform per wave
-    const int i0 = (int)(w % chunks) * kPrepChunk;
+    const int i0 = (int)(w % chunks) * CH;
     const uint16_t* xrow = X + (size_t)c * x_stride + (size_t)m * K;
     uint16_t* prow = xp ? xp + (size_t)c * x_stride + (size_t)m * K : nullptr;
-    uint4 v[kPrepChunk];
+    uint4 v[CH];
 #pragma unroll
-    for (int j = 0; j < kPrepChunk; ++j) {
+    for (int j = 0; j < CH; ++j) {
       const int k = (i0 + j) * 512 + lane * 8;
       v[j] = (i0 + j < passes && k < K && m < M) ? *reinterpret_cast<const uint4*>(xrow + k)
                                                    : make_uint4(0u, 0u, 0u, 0u);
     }
 #pragma unroll
-    for (int j = 0; j < kPrepChunk; ++j) {
+    for (int j = 0; j < CH; ++j) {
       const int i = i0 + j;
       if (i >= passes) break;                             // uniform
       const int k = i * 512 + lane * 8;
@@ -144,14 +146,21 @@ int launch_gemm_prep(const uint16_t* X, size_t x_stride, int M, int K, int mpad,
                      uint16_t* rsq, size_t rsq_stride, uint32_t* szq, size_t szq_stride, uint16_t* xp, int C,
                      hipStream_t stream, int rs_c) {
   const int GW = ((K >> 7) + 7) / 8;
-  const int chunks = (((K + 511) >> 9) + kPrepChunk - 1) / kPrepChunk;
+  const int passes = (K + 511) >> 9;
+  // short chunks when long ones would leave fewer than four waves per CU (measured on
+  // the 27B shapes at M = 64: 30.6 / 29.9 -> 29.4 / 28.9 us per GEMM; at M = 2048,
+  // K = 6144 the long chunks stay 0.6 us faster)
+  const bool few = (long long)mpad * ((passes + 7) / 8) < 4 * 256;
+  const int ch = few ? 2 : 8;
+  const int chunks = (passes + ch - 1) / ch;
   const long long rs_blocks = ((long long)mpad * chunks + 3) / 4;
   const long long sz_blocks = ((long long)gemm_npad(N) * GW + 255) / 256;
   if (rs_blocks + sz_blocks == 0) return W4_OK;
   if (rs_blocks + sz_blocks > 0x7FFFFFFFLL || C > 65535) return W4_ERR_SHAPE;
-  hipLaunchKernelGGL(gemm_prep_kernel, dim3((unsigned)(rs_blocks + sz_blocks), 1, (unsigned)C), dim3(256), 0,
-                     stream, X, x_stride, M, K, mpad, scales, sc_stride, symmetric ? nullptr : qzeros, qz_stride,
-                     symmetric, N, rsq, rsq_stride, szq, szq_stride, xp, (int)rs_blocks, rs_c < 0 ? C : rs_c);
+  hipLaunchKernelGGL(few ? gemm_prep_kernel<2> : gemm_prep_kernel<8>, dim3((unsigned)(rs_blocks + sz_blocks), 1,
+                     (unsigned)C), dim3(256), 0, stream, X, x_stride, M, K, mpad, scales, sc_stride,
+                     symmetric ? nullptr : qzeros, qz_stride, symmetric, N, rsq, rsq_stride, szq, szq_stride, xp,
+                     (int)rs_blocks, rs_c < 0 ? C : rs_c);
   W4_CHECK_LAUNCH();
   return W4_OK;
 }
